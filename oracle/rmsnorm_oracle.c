@@ -161,7 +161,8 @@ int oracle_rmsnorm_bwd(const double* x, const double* w, const double* dy, int64
  * contributions" reduced in a "fixed aggregation order" ("WS1 C4 (#270)
  * closeout evidence", opening note and "Acceptance map"); the order below is
  * this project's reading of that, written out plainly:
- *   c[l][j] = fl32(dy * fl32(x * rstd))            one value per logical row
+ *   c[l][j] = fl32(fl32(dy * x) * rstd)    one value per logical row; dy*x
+ *       of two bf16 values is exact in FP32, so c is dy*x*rstd rounded once
  *   block b holds logical rows 64b .. 64b+63; slot s = l - 64b
  *   stream w (0..7) folds slots w, w+8, ..., w+56 in ascending order,
  *       starting from +0.0; a slot the accumulation does not hold adds +0.0
@@ -214,8 +215,8 @@ int oracle_cdo_v1_dweight_f32(const uint16_t* x, const uint16_t* dy, const float
                     int64_t p = inv[l];
                     float xv = bf16_bits_to_float(x[p * H + j]);
                     float dyv = bf16_bits_to_float(dy[p * H + j]);
-                    float xhat = xv * rstd[p];
-                    float c = dyv * xhat;
+                    float prod = dyv * xv; /* exact: two 8-bit significands */
+                    float c = prod * rstd[p];
                     acc = acc + c;
                 }
                 q[w] = acc;

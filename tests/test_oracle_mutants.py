@@ -34,8 +34,9 @@ MUTANTS = {
                                    "P[b] = ((((((q[0] + q[1]) + q[2]) + q[3]) + q[4]) + q[5]) + q[6]) + q[7];"),
     "cdo_left_fold_over_blocks": ("dweight[j] = nb > 0 ? cdo_tree(P, nb, 0, npad) : 0.0f;",
                                   "{ float a = 0.0f; for (int64_t b = 0; b < nb; ++b) a = a + P[b]; dweight[j] = a; }"),
-    "cdo_contribution_fused": ("float c = dyv * xhat;\n                    acc = acc + c;",
-                               "acc = fmaf(dyv, xhat, acc);"),
+    "cdo_contribution_fused": ("float c = prod * rstd[p];\n                    acc = acc + c;",
+                               "acc = fmaf(prod, rstd[p], acc);"),
+    "cdo_contribution_x_rstd_first": ("float c = prod * rstd[p];", "float c = dyv * (xv * rstd[p]);"),
 }
 
 
