@@ -1,0 +1,155 @@
+/*
+ * rmsnorm_bi.h -- C-ABI of the batch-invariant RMSNorm library for AMD
+ * MI355X (gfx950): forward, backward dx, and a dweight that is bitwise
+ * identical however the same logical rows reach it (one B=N call, N
+ * singleton B=1 calls, chunked-prefill pieces, left/right padding, permuted
+ * samples).
+ *
+ * What is computed.  RMSNorm is the operator whose "dx/dweight" gradients are
+ * a required adapter in "[WS1 Closeout][Backward] Reusable gradient-invariance
+ * harness and operator adapters" (section "Required adapters"):
+ *     rstd = 1/sqrt(mean_j x_j^2 + eps),   y_j = x_j * rstd * w_j
+ *     dx_j = rstd*(dy_j w_j - x_j rstd^2 * (sum_k dy_k w_k x_k) / H)
+ *     dweight_j = sum over logical rows of dy_j x_j rstd.
+ * The invariance requirement is that section's "Acceptance criteria"
+ * (Batch/Chunk gradient invariance is bitwise after logical aggregation).
+ * "WS1 C4 (#270) closeout evidence", section "Historical finding -- RMSNorm
+ * dweight is not chunk/batch decomposable", traces the failure this library
+ * removes to a dweight fold whose shape follows the physical row count; here
+ * dweight is reduced from per-logical-row FP32 contributions in one canonical
+ * order (CDO-v1) that depends only on the logical row index and on nothing
+ * else:
+ *     c = fl32(fl32(dy*x)*rstd)  (dy*x of two bf16 values is exact)
+ *     block b = logical rows 64b..64b+63; stream w = slot mod 8 folds its
+ *     8 slots in ascending order from +0.0; block partial
+ *     P[b] = ((q0+q1)+(q2+q3))+((q4+q5)+(q6+q7)); dweight = perfect
+ *     pairwise tree over P[0..2^ceil(log2 nb)) with +0.0 leaves past nb.
+ *
+ * Conventions for every entry point.
+ *   - Tensors are contiguous and row-major.  bf16 tensors are passed as raw
+ *     16-bit patterns (rmsnorm_bf16).  x, dy, y, dx, w must be 16-byte
+ *     aligned and hidden % 8 == 0 (each row is a whole number of 16-byte
+ *     vectors); rstd and dweight must be 4-byte aligned.
+ *   - Pointers to tensors are DEVICE pointers owned by the caller.  The
+ *     library never frees them and never allocates inside rmsnorm_fwd,
+ *     rmsnorm_bwd_dx, rmsnorm_dw_contrib or rmsnorm_dw_finalize; only the
+ *     *_create functions allocate.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; no call synchronises the device
+ *     except the create and destroy functions where stated.
+ *   - Outputs must not alias inputs.
+ *   - A layout of NULL means the identity map: physical row p is logical row
+ *     p and there is no padding.
+ *   - Every function returns an int status (RMSNORM_OK = 0, negative on
+ *     error); nothing is enqueued when an error is returned by a check.  The
+ *     message of the last error on the calling thread is rmsnorm_last_error().
+ *     There is no fallback path: unsupported inputs are refused.
+ *   - rows == 0 is a successful no-op.
+ *   - An accumulator and the layouts used with it must be driven from one
+ *     host thread at a time; separate accumulators are independent.
+ */
+#ifndef RMSNORM_BI_H
+#define RMSNORM_BI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t rmsnorm_bf16;
+
+/* Opaque per-call physical->logical plan (host copy + device copy). */
+typedef struct rmsnorm_layout rmsnorm_layout;
+/* Opaque canonical dweight accumulator for one logical row multiset. */
+typedef struct rmsnorm_dw_acc rmsnorm_dw_acc;
+
+#define RMSNORM_OK 0
+#define RMSNORM_EINVAL (-1)       /* null pointer, negative size, eps < 0 or NaN, aliasing */
+#define RMSNORM_EUNSUPPORTED (-2) /* hidden % 8 != 0, hidden > max, misaligned pointer, rows > 2^31-1 */
+#define RMSNORM_ELAYOUT (-3)      /* bad row map, or rows / n_logical do not match */
+#define RMSNORM_ECOVERAGE (-4)    /* a logical row contributed twice, or missing at finalize */
+#define RMSNORM_ESTATE (-5)       /* contribution after finalize without reset */
+#define RMSNORM_EHIP (-6)         /* HIP runtime error (message attached) */
+
+/* Largest supported hidden size. */
+int rmsnorm_max_hidden(void);
+
+/* Forward.  x[rows][hidden] -> y[rows][hidden] (bf16, rounded to nearest
+ * even) and rstd[rows] (FP32, kept for the backward).  With a layout, rows
+ * mapped to -1 are padding: they are not read and get y = 0, rstd = 0.
+ * layout->rows must equal rows.  The result of a row depends only on that
+ * row's values (never on its position, the row count or the layout). */
+int rmsnorm_fwd(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y, float* rstd,
+                int64_t rows, int64_t hidden, float eps, const rmsnorm_layout* layout,
+                void* stream);
+
+/* Backward dx from the forward's rstd.  dx[rows][hidden] (bf16); padding
+ * rows get dx = 0 without being read.  If acc is non-NULL the dweight
+ * contributions of this call's logical rows are folded into acc in the same
+ * pass over x and dy (one read of each).  With acc, the layout's n_logical
+ * (or rows, for a NULL layout) must equal the accumulator's n_logical, and
+ * every logical row may contribute at most once before finalize
+ * (RMSNORM_ECOVERAGE otherwise, checked on the host before any launch). */
+int rmsnorm_bwd_dx(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
+                   const float* rstd, rmsnorm_bf16* dx, int64_t rows, int64_t hidden,
+                   const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, void* stream);
+
+/* dweight contributions only (no dx): same accumulation as rmsnorm_bwd_dx
+ * with an accumulator; rstd is an input (any FP32 values). */
+int rmsnorm_dw_contrib(const rmsnorm_bf16* x, const rmsnorm_bf16* dy, const float* rstd,
+                       int64_t rows, int64_t hidden, const rmsnorm_layout* layout,
+                       rmsnorm_dw_acc* acc, void* stream);
+
+/* dweight[hidden] (FP32) of everything contributed since create/reset.  Every
+ * logical row 0..n_logical-1 must have contributed exactly once
+ * (RMSNORM_ECOVERAGE otherwise).  After finalize the accumulator refuses
+ * further contributions until rmsnorm_dw_acc_reset.  Calling finalize again
+ * without reset recomputes the same value.  The accumulator's buffers are
+ * read by kernels enqueued here; do not destroy or reset it before `stream`
+ * has passed them if they are then reused from another stream. */
+int rmsnorm_dw_finalize(rmsnorm_dw_acc* acc, float* dweight, void* stream);
+
+/* Plan for one call: row_logical_host[rows] (HOST memory, int32) maps each
+ * physical row to its canonical logical index in [0, n_logical), or -1 for a
+ * padding row; each logical index may appear at most once.  The plan is
+ * validated (RMSNORM_ELAYOUT on a bad map), built on the host and copied to
+ * the device on `stream`; the function waits for that copy, so the host
+ * array may be freed on return.  The layout owns its device memory. */
+int rmsnorm_layout_create(rmsnorm_layout** out, const int32_t* row_logical_host, int64_t rows,
+                          int64_t n_logical, void* stream);
+
+/* Frees a layout (waits for the device to finish with it).  NULL is a no-op. */
+int rmsnorm_layout_destroy(rmsnorm_layout* layout);
+
+/* Host-only validation and statistics of a row map, without creating a
+ * layout or touching the GPU: stats[0] = blocks touched, stats[1] = blocks
+ * held completely, stats[2] = blocks held in part (their rows are spilled),
+ * stats[3] = padding rows, stats[4] = real rows. */
+int rmsnorm_layout_check(const int32_t* row_logical_host, int64_t rows, int64_t n_logical,
+                         int64_t stats[5]);
+
+/* Accumulator for n_logical logical rows of width hidden.  Allocates device
+ * memory: block partials (ceil(n_logical/64)*hidden FP32), spill rows for
+ * blocks that arrive in pieces (n_logical*hidden FP32) and a small scratch
+ * for the cross-block tree, plus a pinned host staging buffer. */
+int rmsnorm_dw_acc_create(rmsnorm_dw_acc** out, int64_t n_logical, int64_t hidden, void* stream);
+
+/* Forget all contributions (host bookkeeping only; nothing is enqueued). */
+int rmsnorm_dw_acc_reset(rmsnorm_dw_acc* acc, void* stream);
+
+/* Frees an accumulator (waits for the device).  NULL is a no-op. */
+int rmsnorm_dw_acc_destroy(rmsnorm_dw_acc* acc);
+
+/* Message of the last error on this thread ("" if none). */
+const char* rmsnorm_last_error(void);
+
+/* Provenance: target, canonical-order version and kernel variants, e.g.
+ * "hip gfx950; cdo=v1 R=64 S=8 tree=pairwise; ...".  Static string. */
+const char* rmsnorm_backend_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_BI_H */

@@ -1,0 +1,172 @@
+"""Gradient adapters over the HIP library, and their logical inputs.
+
+``GRADIENT_ADAPTERS`` is the registry the harness enumerates ("[WS1
+Closeout][Backward] Reusable gradient-invariance harness and operator
+adapters", Required adapters: RMSNorm dx/dweight; "WS1 C4 (#270) closeout
+evidence", status table: rms_norm and qk_norm).  Stable gradient names:
+``rms_norm`` -> dx, dweight (plus forward y, rstd); ``qk_norm`` -> dq, dk,
+dweight_q, dweight_k (plus yq, yk, rstd_q, rstd_k).
+
+An adapter runs the operator on each call's *physical* rows: real rows are
+gathered from the logical tensors, padding rows are filled with a NaN
+pattern (the operator must not read them), every call goes through the C-ABI
+with its own layout, and one accumulator per norm collects dweight for the
+whole cell.  Outputs are restored to logical order through the row map.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+from . import binding, inputs
+from .harness import GradientAdapter
+from .layouts import Cell
+
+PAD_POISON_BITS = 0x7FC1   # a quiet NaN in bf16: never read, never visible
+
+
+@dataclasses.dataclass
+class NormInputs:
+    """Logical inputs of one norm: x, dy [n_logical, hidden] and w [hidden]
+    (bf16 device tensors), eps, and the loss definition they come from."""
+    name: str
+    workload: inputs.Workload
+    x: torch.Tensor
+    w: torch.Tensor
+    dy: torch.Tensor
+    eps: float
+    active_token_denominator: int
+    loss_reduction: str = "mean_over_active_tokens"
+
+
+def make_inputs(wl: inputs.Workload, device="cuda", gen_device=None) -> NormInputs:
+    """Generate a workload's logical inputs (on ``gen_device``, default the
+    target device) and place them on ``device``."""
+    g = device if gen_device is None else gen_device
+    x = inputs.gen_x(wl, device=g).to(device)
+    w = inputs.gen_w(wl, device=g).to(device)
+    dy = inputs.gen_dy(wl, device=g).to(device)
+    return NormInputs(wl.name, wl, x, w, dy, wl.eps, inputs.n_active(wl))
+
+
+@dataclasses.dataclass
+class QkInputs:
+    name: str
+    q: NormInputs
+    k: NormInputs
+
+    @property
+    def active_token_denominator(self) -> int:
+        return self.q.active_token_denominator
+
+    loss_reduction: str = "mean_over_active_tokens"
+
+
+@dataclasses.dataclass
+class PairCell:
+    """The same token layout seen by the Q and the K norm."""
+    name: str
+    q: Cell
+    k: Cell
+
+    @property
+    def calls(self):
+        return self.q.calls
+
+    @property
+    def call_shapes(self):
+        return self.q.call_shapes
+
+
+def _poisoned(rows: int, hidden: int, device) -> torch.Tensor:
+    t = torch.full((rows, hidden), PAD_POISON_BITS, dtype=torch.int16, device=device)
+    return t.view(torch.bfloat16)
+
+
+class RmsNormAdapter(GradientAdapter):
+    name = "rms_norm"
+    grad_names = ("dx", "dweight")
+    forward_names = ("y", "rstd")
+    aggregation_order = "CDO-v1"
+
+    def run_cell(self, cell: Cell, data: NormInputs) -> Dict[str, np.ndarray]:
+        out = self.run_norm(cell, data)
+        return {"dx": out["dx"], "dweight": out["dweight"], "y": out["y"], "rstd": out["rstd"],
+                "pad_rows_clean": out["pad_rows_clean"]}
+
+    def run_norm(self, cell: Cell, data: NormInputs) -> Dict[str, np.ndarray]:
+        x, w, dy = data.x, data.w, data.dy
+        T, H = x.shape
+        dev = x.device
+        acc = binding.DwAccumulator(T, H)
+        y_l = torch.zeros_like(x)
+        dx_l = torch.zeros_like(x)
+        rstd_l = torch.zeros(T, dtype=torch.float32, device=dev)
+        pads_clean = True
+        layouts: List[binding.Layout] = []
+        for call in cell.calls:
+            self.call_log.append((cell.name, call.name, call.rows))
+            if call.row_logical is None:
+                assert call.rows == T
+                y, rstd = binding.fwd(x, w, data.eps)
+                dx = binding.bwd(x, w, dy, rstd, acc=acc)
+                y_l.copy_(y)
+                dx_l.copy_(dx)
+                rstd_l.copy_(rstd)
+                continue
+            rl = torch.from_numpy(call.row_logical.astype(np.int64)).to(dev)
+            real = rl >= 0
+            xc = _poisoned(call.rows, H, dev)
+            dyc = _poisoned(call.rows, H, dev)
+            xc[real] = x[rl[real]]
+            dyc[real] = dy[rl[real]]
+            layout = binding.Layout(call.row_logical, T)
+            layouts.append(layout)
+            y, rstd = binding.fwd(xc, w, data.eps, layout)
+            dx = binding.bwd(xc, w, dyc, rstd, layout, acc)
+            y_l[rl[real]] = y[real]
+            dx_l[rl[real]] = dx[real]
+            rstd_l[rl[real]] = rstd[real]
+            if bool((~real).any()):
+                pad = ~real
+                pads_clean &= bool((y[pad].view(torch.int16) == 0).all())
+                pads_clean &= bool((dx[pad].view(torch.int16) == 0).all())
+                pads_clean &= bool((rstd[pad] == 0).all())
+        dweight = acc.finalize()
+        torch.cuda.synchronize()
+        res = {
+            "dx": dx_l.view(torch.int16).cpu().numpy().view(np.uint16),
+            "y": y_l.view(torch.int16).cpu().numpy().view(np.uint16),
+            "rstd": rstd_l.cpu().numpy(),
+            "dweight": dweight.cpu().numpy(),
+            "pad_rows_clean": np.array([pads_clean]),
+        }
+        for lay in layouts:
+            lay.close()
+        acc.close()
+        return res
+
+    def provenance(self) -> dict:
+        return {"backend": binding.rmsnorm_backend_info(), "library": binding.library_path()}
+
+
+class QkNormAdapter(RmsNormAdapter):
+    name = "qk_norm"
+    grad_names = ("dq", "dk", "dweight_q", "dweight_k")
+    forward_names = ("yq", "yk", "rstd_q", "rstd_k")
+
+    def run_cell(self, cell: PairCell, data: QkInputs) -> Dict[str, np.ndarray]:
+        q = self.run_norm(cell.q, data.q)
+        k = self.run_norm(cell.k, data.k)
+        return {"dq": q["dx"], "dk": k["dx"], "dweight_q": q["dweight"], "dweight_k": k["dweight"],
+                "yq": q["y"], "yk": k["y"], "rstd_q": q["rstd"], "rstd_k": k["rstd"],
+                "pad_rows_clean": np.array([bool(q["pad_rows_clean"][0] and k["pad_rows_clean"][0])])}
+
+
+GRADIENT_ADAPTERS = {
+    "rms_norm": RmsNormAdapter,
+    "qk_norm": QkNormAdapter,
+}

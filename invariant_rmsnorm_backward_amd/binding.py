@@ -1,0 +1,251 @@
+"""Thin ctypes binding of the C-ABI in ``include/rmsnorm_bi.h``.
+
+The functions named like the C entry points take exactly the C arguments
+(device pointers as ints, sizes, a stream handle as int); they only marshal.
+The small helpers below them (``fwd``, ``bwd``, ``Layout``, ``DwAccumulator``)
+allocate outputs with torch (device memory only) and call those entry points.
+Every computation runs in the HIP library; if the library is missing this
+module raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "librmsnorm_bi.so")
+
+OK, EINVAL, EUNSUPPORTED, ELAYOUT, ECOVERAGE, ESTATE, EHIP = 0, -1, -2, -3, -4, -5, -6
+STATUS_NAMES = {OK: "OK", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", ELAYOUT: "ELAYOUT",
+                ECOVERAGE: "ECOVERAGE", ESTATE: "ESTATE", EHIP: "EHIP"}
+
+EXPORTED = ("rmsnorm_max_hidden", "rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_contrib",
+            "rmsnorm_dw_finalize", "rmsnorm_layout_create", "rmsnorm_layout_destroy",
+            "rmsnorm_layout_check", "rmsnorm_dw_acc_create", "rmsnorm_dw_acc_reset",
+            "rmsnorm_dw_acc_destroy", "rmsnorm_last_error", "rmsnorm_backend_info")
+
+
+class RmsNormError(RuntimeError):
+    def __init__(self, code: int, func: str, message: str):
+        super().__init__(f"{func} -> {STATUS_NAMES.get(code, code)}: {message}")
+        self.code = code
+        self.func = func
+        self.message = message
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                           "(run __graft_entry__.build() or python -m invariant_rmsnorm_backward_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "rmsnorm_max_hidden": ([], I32),
+        "rmsnorm_fwd": ([P, P, P, P, I64, I64, ctypes.c_float, P, P], I32),
+        "rmsnorm_bwd_dx": ([P, P, P, P, P, I64, I64, P, P, P], I32),
+        "rmsnorm_dw_contrib": ([P, P, P, I64, I64, P, P, P], I32),
+        "rmsnorm_dw_finalize": ([P, P, P], I32),
+        "rmsnorm_layout_create": ([PP, P, I64, I64, P], I32),
+        "rmsnorm_layout_destroy": ([P], I32),
+        "rmsnorm_layout_check": ([P, I64, I64, ctypes.POINTER(ctypes.c_int64)], I32),
+        "rmsnorm_dw_acc_create": ([PP, I64, I64, P], I32),
+        "rmsnorm_dw_acc_reset": ([P, P], I32),
+        "rmsnorm_dw_acc_destroy": ([P], I32),
+        "rmsnorm_last_error": ([], ctypes.c_char_p),
+        "rmsnorm_backend_info": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, func: str):
+    if rc != OK:
+        raise RmsNormError(rc, func, rmsnorm_last_error())
+
+
+# ------------------------------------------------------------ C entry points
+def rmsnorm_max_hidden() -> int:
+    return load().rmsnorm_max_hidden()
+
+
+def rmsnorm_last_error() -> str:
+    return load().rmsnorm_last_error().decode()
+
+
+def rmsnorm_backend_info() -> str:
+    return load().rmsnorm_backend_info().decode()
+
+
+def rmsnorm_fwd(x: int, w: int, y: int, rstd: int, rows: int, hidden: int, eps: float,
+                layout: Optional[int], stream: Optional[int]) -> None:
+    _check(load().rmsnorm_fwd(x, w, y, rstd, rows, hidden, eps, layout, stream), "rmsnorm_fwd")
+
+
+def rmsnorm_bwd_dx(x: int, w: int, dy: int, rstd: int, dx: int, rows: int, hidden: int,
+                   layout: Optional[int], acc: Optional[int], stream: Optional[int]) -> None:
+    _check(load().rmsnorm_bwd_dx(x, w, dy, rstd, dx, rows, hidden, layout, acc, stream),
+           "rmsnorm_bwd_dx")
+
+
+def rmsnorm_dw_contrib(x: int, dy: int, rstd: int, rows: int, hidden: int,
+                       layout: Optional[int], acc: Optional[int], stream: Optional[int]) -> None:
+    _check(load().rmsnorm_dw_contrib(x, dy, rstd, rows, hidden, layout, acc, stream),
+           "rmsnorm_dw_contrib")
+
+
+def rmsnorm_dw_finalize(acc: Optional[int], dweight: int, stream: Optional[int]) -> None:
+    _check(load().rmsnorm_dw_finalize(acc, dweight, stream), "rmsnorm_dw_finalize")
+
+
+def rmsnorm_layout_create(row_logical: np.ndarray, n_logical: int, stream: Optional[int]) -> int:
+    rl = np.ascontiguousarray(row_logical, dtype=np.int32)
+    out = ctypes.c_void_p()
+    _check(load().rmsnorm_layout_create(ctypes.byref(out), rl.ctypes.data_as(ctypes.c_void_p),
+                                        rl.size, n_logical, stream), "rmsnorm_layout_create")
+    return out.value
+
+
+def rmsnorm_layout_destroy(layout: Optional[int]) -> None:
+    _check(load().rmsnorm_layout_destroy(layout), "rmsnorm_layout_destroy")
+
+
+def rmsnorm_layout_check(row_logical: np.ndarray, n_logical: int) -> dict:
+    rl = np.ascontiguousarray(row_logical, dtype=np.int32)
+    stats = (ctypes.c_int64 * 5)()
+    _check(load().rmsnorm_layout_check(rl.ctypes.data_as(ctypes.c_void_p), rl.size, n_logical,
+                                       stats), "rmsnorm_layout_check")
+    keys = ("blocks", "complete_blocks", "partial_blocks", "pad_rows", "real_rows")
+    return dict(zip(keys, list(stats)))
+
+
+def rmsnorm_dw_acc_create(n_logical: int, hidden: int, stream: Optional[int]) -> int:
+    out = ctypes.c_void_p()
+    _check(load().rmsnorm_dw_acc_create(ctypes.byref(out), n_logical, hidden, stream),
+           "rmsnorm_dw_acc_create")
+    return out.value
+
+
+def rmsnorm_dw_acc_reset(acc: Optional[int], stream: Optional[int]) -> None:
+    _check(load().rmsnorm_dw_acc_reset(acc, stream), "rmsnorm_dw_acc_reset")
+
+
+def rmsnorm_dw_acc_destroy(acc: Optional[int]) -> None:
+    _check(load().rmsnorm_dw_acc_destroy(acc), "rmsnorm_dw_acc_destroy")
+
+
+# ------------------------------------------------------------------ helpers
+def current_stream() -> int:
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+class Layout:
+    """Owns a device layout (plan) built from a host row map."""
+
+    def __init__(self, row_logical: np.ndarray, n_logical: int, stream: Optional[int] = None):
+        self.row_logical = np.ascontiguousarray(row_logical, dtype=np.int32)
+        self.rows = int(self.row_logical.size)
+        self.n_logical = int(n_logical)
+        self.handle = rmsnorm_layout_create(self.row_logical, self.n_logical,
+                                            current_stream() if stream is None else stream)
+
+    def close(self):
+        if self.handle:
+            rmsnorm_layout_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class DwAccumulator:
+    """Owns a canonical dweight accumulator."""
+
+    def __init__(self, n_logical: int, hidden: int, stream: Optional[int] = None):
+        self.n_logical = int(n_logical)
+        self.hidden = int(hidden)
+        self.handle = rmsnorm_dw_acc_create(self.n_logical, self.hidden,
+                                            current_stream() if stream is None else stream)
+
+    def reset(self, stream: Optional[int] = None):
+        rmsnorm_dw_acc_reset(self.handle, current_stream() if stream is None else stream)
+
+    def finalize(self, dweight=None, stream: Optional[int] = None):
+        import torch
+        if dweight is None:
+            dweight = torch.empty(self.hidden, dtype=torch.float32, device="cuda")
+        rmsnorm_dw_finalize(self.handle, dweight.data_ptr(),
+                            current_stream() if stream is None else stream)
+        return dweight
+
+    def close(self):
+        if self.handle:
+            rmsnorm_dw_acc_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _handle(obj) -> Optional[int]:
+    return None if obj is None else obj.handle
+
+
+def fwd(x, w, eps: float, layout: Optional[Layout] = None, y=None, rstd=None,
+        stream: Optional[int] = None) -> Tuple:
+    """y, rstd = RMSNorm forward of bf16 ``x[rows, hidden]`` (device tensors)."""
+    import torch
+    rows, hidden = x.shape
+    y = torch.empty_like(x) if y is None else y
+    rstd = torch.empty(rows, dtype=torch.float32, device=x.device) if rstd is None else rstd
+    rmsnorm_fwd(x.data_ptr(), w.data_ptr(), y.data_ptr(), rstd.data_ptr(), rows, hidden,
+                float(eps), _handle(layout), current_stream() if stream is None else stream)
+    return y, rstd
+
+
+def bwd(x, w, dy, rstd, layout: Optional[Layout] = None, acc: Optional[DwAccumulator] = None,
+        dx=None, stream: Optional[int] = None):
+    """dx of bf16 ``x``; with ``acc`` the dweight contributions are folded in."""
+    import torch
+    rows, hidden = x.shape
+    dx = torch.empty_like(x) if dx is None else dx
+    rmsnorm_bwd_dx(x.data_ptr(), w.data_ptr(), dy.data_ptr(), rstd.data_ptr(), dx.data_ptr(),
+                   rows, hidden, _handle(layout), _handle(acc),
+                   current_stream() if stream is None else stream)
+    return dx
+
+
+def dw_contrib(x, dy, rstd, acc: DwAccumulator, layout: Optional[Layout] = None,
+               stream: Optional[int] = None) -> None:
+    rows, hidden = x.shape
+    rmsnorm_dw_contrib(x.data_ptr(), dy.data_ptr(), rstd.data_ptr(), rows, hidden,
+                       _handle(layout), acc.handle, current_stream() if stream is None else stream)

@@ -1,0 +1,353 @@
+// abi.cpp -- the C-ABI of include/rmsnorm_bi.h: argument checks, layouts,
+// accumulators and kernel launches.  Every check runs on the host before
+// anything is enqueued; there is no fallback path.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/rmsnorm_bi.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(RMSNORM_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int check_hidden(int64_t hidden) {
+  if (hidden <= 0) return fail(RMSNORM_EINVAL, "hidden must be positive");
+  if (hidden % 8 != 0)
+    return fail(RMSNORM_EUNSUPPORTED, "hidden must be a multiple of 8 (16-byte bf16 vectors)");
+  if (hidden > rbi::kMaxHidden)
+    return fail(RMSNORM_EUNSUPPORTED,
+                "hidden " + std::to_string(hidden) + " exceeds the maximum " +
+                    std::to_string(rbi::kMaxHidden));
+  return RMSNORM_OK;
+}
+
+int check_rows(int64_t rows) {
+  if (rows < 0) return fail(RMSNORM_EINVAL, "rows must be non-negative");
+  if (rows > INT32_MAX) return fail(RMSNORM_EUNSUPPORTED, "rows must be below 2^31");
+  return RMSNORM_OK;
+}
+
+int check_tensor(const void* p, const char* name, size_t align) {
+  if (p == nullptr) return fail(RMSNORM_EINVAL, std::string(name) + " is NULL");
+  if (!aligned(p, align))
+    return fail(RMSNORM_EUNSUPPORTED,
+                std::string(name) + " is not " + std::to_string(align) + "-byte aligned");
+  return RMSNORM_OK;
+}
+
+}  // namespace
+
+struct rmsnorm_layout {
+  rbi::PlanHost host;
+  void* d_mem = nullptr;
+  rbi::PlanDev dev;
+};
+
+struct rmsnorm_dw_acc {
+  rbi::AccHost host;
+  float* d_P = nullptr;
+  float* d_S = nullptr;
+  float* d_tmp = nullptr;
+  int32_t* d_spilled = nullptr;
+  int32_t* h_spilled = nullptr;   // pinned staging for the spilled-block list
+  hipEvent_t staged = nullptr;
+  bool staging_pending = false;
+};
+
+extern "C" {
+
+int rmsnorm_max_hidden(void) { return rbi::kMaxHidden; }
+
+const char* rmsnorm_last_error(void) { return g_err.c_str(); }
+
+const char* rmsnorm_backend_info(void) {
+  return "hip gfx950; cdo=v1 R=64 S=8 (hidden<=5120) or S=4 (hidden>5120), "
+         "contribution fl32(fl32(dy*x)*rstd), streams fold ascending from +0.0, "
+         "stream tree pairwise, block tree pairwise with +0.0 padding; no atomics; "
+         "fwd=wave_per_row|lanes_per_row bwd=fused dx+dW, one workgroup per 64-row block; "
+         "max_hidden=10240";
+}
+
+int rmsnorm_fwd(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y, float* rstd,
+                int64_t rows, int64_t hidden, float eps, const rmsnorm_layout* layout,
+                void* stream) {
+  int rc;
+  if ((rc = check_rows(rows)) || (rc = check_hidden(hidden))) return rc;
+  if (!(eps >= 0.0f) || std::isinf(eps)) return fail(RMSNORM_EINVAL, "eps must be finite and >= 0");
+  if (layout != nullptr && layout->host.rows != rows)
+    return fail(RMSNORM_ELAYOUT, "layout rows (" + std::to_string(layout->host.rows) +
+                                     ") differ from rows (" + std::to_string(rows) + ")");
+  if (rows == 0) return RMSNORM_OK;
+  if ((rc = check_tensor(x, "x", 16)) || (rc = check_tensor(w, "w", 16)) ||
+      (rc = check_tensor(y, "y", 16)) || (rc = check_tensor(rstd, "rstd", 4)))
+    return rc;
+  const size_t nbytes = static_cast<size_t>(rows) * hidden * 2;
+  if (overlaps(y, nbytes, x, nbytes) || overlaps(y, nbytes, w, hidden * 2) ||
+      overlaps(rstd, rows * 4, x, nbytes) || overlaps(rstd, rows * 4, y, nbytes))
+    return fail(RMSNORM_EINVAL, "outputs must not alias inputs or each other");
+  rbi::FwdArgs a{x, w, y, rstd, rows, static_cast<int32_t>(hidden), eps,
+                 layout ? layout->dev.row_logical : nullptr};
+  hipError_t e = rbi::launch_fwd(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rmsnorm_fwd launch");
+  return RMSNORM_OK;
+}
+
+static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
+                      const float* rstd, rmsnorm_bf16* dx, int64_t rows, int64_t hidden,
+                      const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, void* stream,
+                      bool with_dx) {
+  int rc;
+  if ((rc = check_rows(rows)) || (rc = check_hidden(hidden))) return rc;
+  if (layout != nullptr && layout->host.rows != rows)
+    return fail(RMSNORM_ELAYOUT, "layout rows (" + std::to_string(layout->host.rows) +
+                                     ") differ from rows (" + std::to_string(rows) + ")");
+  if (acc != nullptr) {
+    if (acc->host.hidden != hidden)
+      return fail(RMSNORM_EINVAL, "accumulator hidden (" + std::to_string(acc->host.hidden) +
+                                      ") differs from hidden (" + std::to_string(hidden) + ")");
+    if (acc->host.finalized)
+      return fail(RMSNORM_ESTATE, "accumulator already finalized; call rmsnorm_dw_acc_reset first");
+  }
+  if (rows > 0) {
+    if ((rc = check_tensor(x, "x", 16)) || (rc = check_tensor(dy, "dy", 16)) ||
+        (rc = check_tensor(rstd, "rstd", 4)))
+      return rc;
+    if (with_dx) {
+      if ((rc = check_tensor(w, "w", 16)) || (rc = check_tensor(dx, "dx", 16))) return rc;
+      const size_t nbytes = static_cast<size_t>(rows) * hidden * 2;
+      if (overlaps(dx, nbytes, x, nbytes) || overlaps(dx, nbytes, dy, nbytes) ||
+          overlaps(dx, nbytes, w, hidden * 2) || overlaps(dx, nbytes, rstd, rows * 4))
+        return fail(RMSNORM_EINVAL, "dx must not alias an input");
+    }
+  }
+  if (acc != nullptr) {
+    std::string err;
+    rc = acc->host.register_call(layout ? &layout->host : nullptr, rows, &err);
+    if (rc != RMSNORM_OK) return fail(rc, err);
+  }
+  if (rows == 0) return RMSNORM_OK;
+
+  rbi::BwdArgs a{};
+  a.x = x;
+  a.w = w;
+  a.dy = dy;
+  a.rstd = rstd;
+  a.dx = with_dx ? dx : nullptr;
+  a.P = acc ? acc->d_P : nullptr;
+  a.S = acc ? acc->d_S : nullptr;
+  a.rows = rows;
+  a.hidden = static_cast<int32_t>(hidden);
+  if (layout != nullptr) {
+    a.plan = layout->dev;
+  } else {
+    a.plan.n_items = static_cast<int32_t>(rbi::num_blocks(rows));
+    a.plan.n_pad = 0;
+  }
+  hipError_t e = rbi::launch_bwd(a, with_dx, acc != nullptr, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rmsnorm backward launch");
+  return RMSNORM_OK;
+}
+
+int rmsnorm_bwd_dx(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
+                   const float* rstd, rmsnorm_bf16* dx, int64_t rows, int64_t hidden,
+                   const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, void* stream) {
+  return bwd_common(x, w, dy, rstd, dx, rows, hidden, layout, acc, stream, true);
+}
+
+int rmsnorm_dw_contrib(const rmsnorm_bf16* x, const rmsnorm_bf16* dy, const float* rstd,
+                       int64_t rows, int64_t hidden, const rmsnorm_layout* layout,
+                       rmsnorm_dw_acc* acc, void* stream) {
+  if (acc == nullptr) return fail(RMSNORM_EINVAL, "rmsnorm_dw_contrib needs an accumulator");
+  return bwd_common(x, nullptr, dy, rstd, nullptr, rows, hidden, layout, acc, stream, false);
+}
+
+int rmsnorm_dw_finalize(rmsnorm_dw_acc* acc, float* dweight, void* stream) {
+  if (acc == nullptr) return fail(RMSNORM_EINVAL, "accumulator is NULL");
+  int rc;
+  if ((rc = check_tensor(dweight, "dweight", 4))) return rc;
+  std::vector<int32_t> spilled;
+  std::string err;
+  rc = acc->host.prepare_finalize(&spilled, &err);
+  if (rc != RMSNORM_OK) return fail(rc, err);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int32_t H = static_cast<int32_t>(acc->host.hidden);
+  hipError_t e;
+  if (!spilled.empty()) {
+    if (acc->staging_pending) {
+      if ((e = hipEventSynchronize(acc->staged)) != hipSuccess) return hip_fail(e, "staging wait");
+      acc->staging_pending = false;
+    }
+    std::memcpy(acc->h_spilled, spilled.data(), spilled.size() * sizeof(int32_t));
+    if ((e = hipMemcpyAsync(acc->d_spilled, acc->h_spilled, spilled.size() * sizeof(int32_t),
+                            hipMemcpyHostToDevice, st)) != hipSuccess)
+      return hip_fail(e, "spilled-block list upload");
+    if ((e = hipEventRecord(acc->staged, st)) != hipSuccess) return hip_fail(e, "event record");
+    acc->staging_pending = true;
+    if ((e = rbi::launch_rebuild(acc->d_S, acc->d_P, acc->d_spilled,
+                                 static_cast<int32_t>(spilled.size()), acc->host.n_logical, H,
+                                 st)) != hipSuccess)
+      return hip_fail(e, "spilled-block rebuild");
+  }
+  if ((e = rbi::launch_tree(acc->d_P, acc->host.nb, acc->d_tmp, dweight, H, st)) != hipSuccess)
+    return hip_fail(e, "block tree");
+  acc->host.finalized = true;
+  return RMSNORM_OK;
+}
+
+int rmsnorm_layout_check(const int32_t* row_logical_host, int64_t rows, int64_t n_logical,
+                         int64_t stats[5]) {
+  rbi::PlanHost plan;
+  std::string err;
+  int rc = rbi::build_plan(row_logical_host, rows, n_logical, &plan, &err);
+  if (rc != RMSNORM_OK) return fail(rc, err);
+  if (stats) {
+    stats[0] = plan.n_items();
+    stats[1] = plan.n_complete;
+    stats[2] = plan.n_partial;
+    stats[3] = static_cast<int64_t>(plan.pad_rows.size());
+    stats[4] = static_cast<int64_t>(plan.logical_rows.size());
+  }
+  return RMSNORM_OK;
+}
+
+int rmsnorm_layout_create(rmsnorm_layout** out, const int32_t* row_logical_host, int64_t rows,
+                          int64_t n_logical, void* stream) {
+  if (out == nullptr) return fail(RMSNORM_EINVAL, "out is NULL");
+  *out = nullptr;
+  auto* L = new rmsnorm_layout();
+  std::string err;
+  int rc = rbi::build_plan(row_logical_host, rows, n_logical, &L->host, &err);
+  if (rc != RMSNORM_OK) {
+    delete L;
+    return fail(rc, err);
+  }
+  const rbi::PlanHost& P = L->host;
+  const size_t n_info = P.item_info.size(), n_slot = P.slot_phys.size(),
+               n_pad = P.pad_rows.size(), n_rl = P.row_logical.size();
+  std::vector<int32_t> staging;
+  staging.reserve(n_info + n_slot + n_pad + n_rl + 4);
+  staging.insert(staging.end(), P.item_info.begin(), P.item_info.end());
+  staging.insert(staging.end(), P.slot_phys.begin(), P.slot_phys.end());
+  staging.insert(staging.end(), P.pad_rows.begin(), P.pad_rows.end());
+  staging.insert(staging.end(), P.row_logical.begin(), P.row_logical.end());
+  staging.push_back(0);  // never allocate zero bytes
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMalloc(&L->d_mem, staging.size() * sizeof(int32_t));
+  if (e != hipSuccess) {
+    delete L;
+    return hip_fail(e, "layout allocation");
+  }
+  e = hipMemcpyAsync(L->d_mem, staging.data(), staging.size() * sizeof(int32_t),
+                     hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) {
+    (void)hipFree(L->d_mem);
+    delete L;
+    return hip_fail(e, "layout upload");
+  }
+  int32_t* base = static_cast<int32_t*>(L->d_mem);
+  L->dev.item_info = base;
+  L->dev.slot_phys = base + n_info;
+  L->dev.pad_rows = base + n_info + n_slot;
+  L->dev.row_logical = base + n_info + n_slot + n_pad;
+  L->dev.n_items = static_cast<int32_t>(n_info);
+  L->dev.n_pad = static_cast<int32_t>(n_pad);
+  *out = L;
+  return RMSNORM_OK;
+}
+
+int rmsnorm_layout_destroy(rmsnorm_layout* layout) {
+  if (layout == nullptr) return RMSNORM_OK;
+  hipError_t e = hipFree(layout->d_mem);  // hipFree waits for the device
+  delete layout;
+  if (e != hipSuccess) return hip_fail(e, "layout free");
+  return RMSNORM_OK;
+}
+
+int rmsnorm_dw_acc_create(rmsnorm_dw_acc** out, int64_t n_logical, int64_t hidden, void* stream) {
+  (void)stream;
+  if (out == nullptr) return fail(RMSNORM_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc;
+  if ((rc = check_hidden(hidden))) return rc;
+  if (n_logical < 0) return fail(RMSNORM_EINVAL, "n_logical must be non-negative");
+  if (n_logical > INT32_MAX) return fail(RMSNORM_EUNSUPPORTED, "n_logical must be below 2^31");
+  auto* A = new rmsnorm_dw_acc();
+  A->host.init(n_logical, hidden);
+  const int64_t nb = A->host.nb;
+  const size_t H = static_cast<size_t>(hidden);
+  hipError_t e = hipSuccess;
+  auto cleanup = [&](const char* what) {
+    if (A->d_P) (void)hipFree(A->d_P);
+    if (A->d_S) (void)hipFree(A->d_S);
+    if (A->d_tmp) (void)hipFree(A->d_tmp);
+    if (A->d_spilled) (void)hipFree(A->d_spilled);
+    if (A->h_spilled) (void)hipHostFree(A->h_spilled);
+    if (A->staged) (void)hipEventDestroy(A->staged);
+    delete A;
+    return hip_fail(e, what);
+  };
+  if ((e = hipMalloc(&A->d_P, std::max<size_t>(1, nb * H) * sizeof(float))) != hipSuccess)
+    return cleanup("block partial allocation");
+  if ((e = hipMalloc(&A->d_S, std::max<size_t>(1, n_logical * H) * sizeof(float))) != hipSuccess)
+    return cleanup("spill allocation");
+  if ((e = hipMalloc(&A->d_tmp, std::max<size_t>(1, rbi::tree_scratch_rows(nb) * H) *
+                                    sizeof(float))) != hipSuccess)
+    return cleanup("tree scratch allocation");
+  if ((e = hipMalloc(&A->d_spilled, std::max<size_t>(1, nb) * sizeof(int32_t))) != hipSuccess)
+    return cleanup("spill list allocation");
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&A->h_spilled),
+                         std::max<size_t>(1, nb) * sizeof(int32_t), hipHostMallocDefault)) !=
+      hipSuccess)
+    return cleanup("pinned staging allocation");
+  if ((e = hipEventCreateWithFlags(&A->staged, hipEventDisableTiming)) != hipSuccess)
+    return cleanup("event creation");
+  *out = A;
+  return RMSNORM_OK;
+}
+
+int rmsnorm_dw_acc_reset(rmsnorm_dw_acc* acc, void* stream) {
+  (void)stream;
+  if (acc == nullptr) return fail(RMSNORM_EINVAL, "accumulator is NULL");
+  acc->host.reset();
+  return RMSNORM_OK;
+}
+
+int rmsnorm_dw_acc_destroy(rmsnorm_dw_acc* acc) {
+  if (acc == nullptr) return RMSNORM_OK;
+  hipError_t e = hipDeviceSynchronize();
+  (void)hipFree(acc->d_P);
+  (void)hipFree(acc->d_S);
+  (void)hipFree(acc->d_tmp);
+  (void)hipFree(acc->d_spilled);
+  (void)hipHostFree(acc->h_spilled);
+  (void)hipEventDestroy(acc->staged);
+  delete acc;
+  if (e != hipSuccess) return hip_fail(e, "accumulator destroy");
+  return RMSNORM_OK;
+}
+
+}  // extern "C"

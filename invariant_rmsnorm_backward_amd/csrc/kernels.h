@@ -1,0 +1,68 @@
+// kernels.h -- launchers of the gfx950 kernels (internal C++ interface used
+// by the C-ABI layer).  Kernel variants are chosen from `hidden` alone, never
+// from the row count or the layout, so a row's results cannot depend on how
+// many rows share its call.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rbi {
+
+constexpr int kMaxHidden = 10240;
+// Canonical-order parameter that depends on the hidden size: the number of
+// in-block fold streams (8 up to this width, 4 above it).
+constexpr int kEightStreamMaxHidden = 5120;
+
+inline int cdo_streams(int hidden) { return hidden <= kEightStreamMaxHidden ? 8 : 4; }
+
+// Physical->logical plan as the kernels see it (device pointers).
+struct PlanDev {
+  const int32_t* item_info = nullptr;  // nullptr: identity map, item = block
+  const int32_t* slot_phys = nullptr;  // [n_items * 64]
+  const int32_t* pad_rows = nullptr;   // [n_pad]
+  const int32_t* row_logical = nullptr;
+  int32_t n_items = 0;
+  int32_t n_pad = 0;
+};
+
+struct FwdArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  uint16_t* y;
+  float* rstd;
+  int64_t rows;
+  int32_t hidden;
+  float eps;
+  const int32_t* row_logical;  // nullptr: no padding
+};
+
+struct BwdArgs {
+  const uint16_t* x;
+  const uint16_t* w;   // needed for dx
+  const uint16_t* dy;
+  const float* rstd;
+  uint16_t* dx;        // nullptr when only dweight contributions are wanted
+  float* P;            // block partials [nb][hidden]
+  float* S;            // spill rows [n_logical][hidden]
+  int64_t rows;
+  int32_t hidden;
+  PlanDev plan;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// with_dx: write dx (and zero padding rows); with_dw: fold dweight contributions.
+hipError_t launch_bwd(const BwdArgs& a, bool with_dx, bool with_dw, hipStream_t stream);
+// Rebuild the partials of spilled blocks from their spill rows.
+hipError_t launch_rebuild(const float* S, float* P, const int32_t* blocks, int32_t n_blocks,
+                          int64_t n_logical, int32_t hidden, hipStream_t stream);
+// dweight = pairwise tree over P[0..nb); tmp needs ceil(nb/32) * hidden floats.
+hipError_t launch_tree(const float* P, int64_t nb, float* tmp, float* dweight, int32_t hidden,
+                       hipStream_t stream);
+int64_t tree_scratch_rows(int64_t nb);
+
+bool hidden_supported(int hidden);
+const char* fwd_variant(int hidden);
+const char* bwd_variant(int hidden);
+
+}  // namespace rbi

@@ -1,0 +1,646 @@
+// kernels.hip -- gfx950 kernels of batch-invariant RMSNorm.
+//
+// Forward: one wavefront per row (hidden >= 512, or any hidden that is not a
+// power of two below 512) or one group of hidden/8 lanes per row (hidden in
+// {8..256}); 16-byte bf16 loads, FP32 math, an xor-butterfly sum of squares.
+//
+// Backward: one workgroup of 8 wavefronts per canonical block of 64 logical
+// rows.  The dweight order (CDO-v1, following "WS1 C4 (#270) closeout
+// evidence": parameter gradients from logical-row FP32 contributions reduced
+// in a fixed order) is laid onto the hardware: each fold stream is a
+// wavefront (or a pair of wavefronts when hidden > 5120) that walks its
+// slots w, w+S, ... in ascending order and keeps the running FP32 sums in
+// registers, so x and dy are read from HBM once for dx and dweight together.
+// The streams meet in LDS for the fixed in-block tree and the block partial
+// goes to HBM; a separate pass reduces the partials with a perfect pairwise
+// tree.  Blocks that a call holds only in part write their rows'
+// contributions to a spill area instead, and the finalize step folds them in
+// exactly the same order.  No atomics anywhere: every sum has one owner.
+#include "kernels.h"
+
+#include "device_math.h"
+#include "plan.h"
+
+namespace rbi {
+
+// ----------------------------------------------------------------- forward
+template <int V>
+__global__ __launch_bounds__(256) void fwd_wide_kernel(FwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int H = a.hidden;
+  const int nchunk = H >> 3;
+  uint4 wv[V];
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    const int q = k * 64 + lane;
+    wv[k] = (k < V - 1 || q < nchunk) ? load16(a.w + q * 8) : make_uint4(0, 0, 0, 0);
+  }
+  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < a.rows; row += (int64_t)gridDim.x * 4) {
+    uint16_t* yr = a.y + row * H;
+    if (a.row_logical != nullptr && a.row_logical[row] < 0) {
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const int q = k * 64 + lane;
+        if (k < V - 1 || q < nchunk) store16(yr + q * 8, make_uint4(0, 0, 0, 0));
+      }
+      if (lane == 0) a.rstd[row] = 0.0f;
+      continue;
+    }
+    const uint16_t* xr = a.x + row * H;
+    uint4 xv[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const int q = k * 64 + lane;
+      xv[k] = (k < V - 1 || q < nchunk) ? load16(xr + q * 8) : make_uint4(0, 0, 0, 0);
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      float f[8];
+      unpack8(xv[k], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+    }
+    ss = wave_sum(ss);
+    const float r = rsqrtf(ss / (float)H + a.eps);
+#pragma unroll
+    for (int k = 0; k < V; ++k) launder(xv[k]);
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const int q = k * 64 + lane;
+      if (k < V - 1 || q < nchunk) {
+        float f[8], g[8], o[8];
+        unpack8(xv[k], f);
+        unpack8(wv[k], g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (f[e] * r) * g[e];
+        store16(yr + q * 8, pack8(o));
+      }
+    }
+    if (lane == 0) a.rstd[row] = r;
+  }
+}
+
+// hidden = 8L with L lanes per row (L in 1..32, a power of two).
+template <int L>
+__global__ __launch_bounds__(256) void fwd_small_kernel(FwdArgs a) {
+  constexpr int H = 8 * L;
+  constexpr int GROUPS = 256 / L;
+  const int g = threadIdx.x / L;
+  const int sub = threadIdx.x % L;
+  float wf[8];
+  unpack8(load16(a.w + sub * 8), wf);
+  for (int64_t base = (int64_t)blockIdx.x * GROUPS; base < a.rows;
+       base += (int64_t)gridDim.x * GROUPS) {
+    const int64_t row = base + g;
+    const bool valid = row < a.rows;
+    const bool pad = valid && a.row_logical != nullptr && a.row_logical[row] < 0;
+    uint4 xv = make_uint4(0, 0, 0, 0);
+    if (valid && !pad) xv = load16(a.x + row * H + sub * 8);
+    float f[8];
+    unpack8(xv, f);
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+    ss = group_sum<L>(ss);
+    const float r = rsqrtf(ss / (float)H + a.eps);
+    if (valid) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = pad ? 0.0f : (f[e] * r) * wf[e];
+      store16(a.y + row * H + sub * 8, pack8(o));
+      if (sub == 0) a.rstd[row] = pad ? 0.0f : r;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- backward
+__device__ __forceinline__ int slot_row(const BwdArgs& a, int item, int blk, int s) {
+  if (a.plan.item_info != nullptr) return a.plan.slot_phys[(int64_t)item * kBlockRows + s];
+  const int64_t r = (int64_t)blk * kBlockRows + s;
+  return r < a.rows ? (int)r : -1;
+}
+
+// Wide rows: V chunks of 8 columns per lane, TW wavefronts per row, S = 8/TW
+// streams; the workgroup is 8 wavefronts.  Chunk q of the row held by lane
+// `lane` of wave-half `half` at step k is q = (half*V + k)*64 + lane.  FULL
+// means hidden == 512*V*TW exactly, so no lane needs a bounds mask.
+template <int V, int TW, bool FULL>
+struct WideShape {
+  static constexpr int S = 8 / TW;                 // fold streams
+  static constexpr int SLOTS = kBlockRows / S;     // slots per stream
+  static constexpr int COLS = 512 * V * TW;        // columns the workgroup covers
+  static constexpr int NTILE = (V * TW + 1) / 2;   // 1024-column tiles of the stream tree
+};
+
+// One canonical block: the stream's slots in ascending order.  COMPLETE: the
+// call holds every present row of the block, so the contributions are folded
+// in registers; otherwise they are written to the spill rows.
+template <int V, int TW, bool FULL, bool DX, bool DW, bool COMPLETE>
+__device__ __forceinline__ void bwd_wide_block(const BwdArgs& a, int item, int blk,
+                                               const float* w_s, float* dot_s,
+                                               float (&acc)[DW ? V * 8 : 1]) {
+  using Sh = WideShape<V, TW, FULL>;
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6;
+  const int lane = tid & 63;
+  const int stream = wv / TW;
+  const int half = wv % TW;
+  const int H = FULL ? Sh::COLS : a.hidden;
+  const int nchunk = H >> 3;
+  const int base = half * V * 512 + lane * 8;      // this lane's first column
+  auto in_row = [&](int k) { return FULL || (half * V + k) * 64 + lane < nchunk; };
+
+  for (int i = 0; i < Sh::SLOTS; ++i) {
+    const int s = stream + Sh::S * i;
+    const int p = slot_row(a, item, blk, s);   // uniform over the wavefront
+    uint4 xv[V], dv[V];
+    float r = 0.0f;
+    float dot = 0.0f;
+    if (p >= 0) {
+      const uint16_t* xr = a.x + (int64_t)p * H + base;
+      const uint16_t* dr = a.dy + (int64_t)p * H + base;
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        xv[k] = in_row(k) ? load16(xr + k * 512) : make_uint4(0, 0, 0, 0);
+        dv[k] = in_row(k) ? load16(dr + k * 512) : make_uint4(0, 0, 0, 0);
+      }
+      r = a.rstd[p];
+      float* srow = COMPLETE ? nullptr : a.S + ((int64_t)blk * kBlockRows + s) * H + base;
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        float xf[8], df[8];
+        unpack8(xv[k], xf);
+        unpack8(dv[k], df);
+        float c[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pr = df[e] * xf[e];          // exact: two bf16 significands
+          if (DX) dot = fmaf(pr, w_s[base + k * 512 + e], dot);
+          c[e] = pr * r;                           // the row's contribution, rounded once
+          if (DW && COMPLETE) acc[k * 8 + e] = acc[k * 8 + e] + c[e];
+        }
+        if (DW && !COMPLETE && in_row(k)) {
+          store_f4(srow + k * 512, c[0], c[1], c[2], c[3]);
+          store_f4(srow + k * 512 + 4, c[4], c[5], c[6], c[7]);
+        }
+      }
+      if (DX && TW == 1) dot = wave_sum(dot);
+    }
+    if (DX) {
+      if (TW > 1) {
+        dot = wave_sum(dot);
+        if (lane == 0) dot_s[(i & 1) * 8 + wv] = dot;
+        __syncthreads();
+        dot = dot_s[(i & 1) * 8 + stream * TW] + dot_s[(i & 1) * 8 + stream * TW + 1];
+      }
+      if (p >= 0) {
+        const float kk = ((r * r) * r) * (dot / (float)H);
+        uint16_t* xo = a.dx + (int64_t)p * H + base;
+        compiler_fence();
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          launder(xv[k]);
+          launder(dv[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          if (in_row(k)) {
+            float xf[8], df[8], o[8];
+            unpack8(xv[k], xf);
+            unpack8(dv[k], df);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float g = df[e] * w_s[base + k * 512 + e];
+              o[e] = fmaf(-xf[e], kk, r * g);
+            }
+            store16(xo + k * 512, pack8(o));
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int V, int TW, bool FULL, bool DX, bool DW>
+__global__ __launch_bounds__(512) void bwd_wide_kernel(BwdArgs a) {
+  using Sh = WideShape<V, TW, FULL>;
+  constexpr int S = Sh::S;
+  __shared__ float w_s[DX ? Sh::COLS : 1];
+  __shared__ float tile_s[DW ? S * 1024 : 1];
+  __shared__ float dot_s[(DX && TW > 1) ? 2 * 8 : 1];
+
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6;
+  const int lane = tid & 63;
+  const int stream = wv / TW;
+  const int half = wv % TW;
+  const int H = FULL ? Sh::COLS : a.hidden;
+  const int nchunk = H >> 3;
+  const int item = blockIdx.x;
+
+  if (item >= a.plan.n_items) {
+    // padding rows: dx = 0, nothing read (one row per wavefront)
+    if (DX) {
+      const int idx = (item - a.plan.n_items) * 8 + wv;
+      if (idx < a.plan.n_pad) {
+        uint16_t* d = a.dx + (int64_t)a.plan.pad_rows[idx] * H;
+        for (int q = lane; q < nchunk; q += 64) store16(d + q * 8, make_uint4(0, 0, 0, 0));
+      }
+    }
+    return;
+  }
+
+  if (DX) {
+    // w as FP32 in LDS; columns past hidden hold 0 so masked lanes read zeros
+    for (int q = tid; q < Sh::COLS / 8; q += 512) {
+      float f[8];
+      unpack8(q < nchunk ? load16(a.w + q * 8) : make_uint4(0, 0, 0, 0), f);
+      store_f4(&w_s[q * 8], f[0], f[1], f[2], f[3]);
+      store_f4(&w_s[q * 8 + 4], f[4], f[5], f[6], f[7]);
+    }
+    __syncthreads();
+  }
+
+  int blk;
+  bool complete;
+  if (a.plan.item_info != nullptr) {
+    const int info = a.plan.item_info[item];
+    complete = info >= 0;
+    blk = complete ? info : ~info;
+  } else {
+    blk = item;
+    complete = true;
+  }
+
+  float acc[DW ? V * 8 : 1];
+#pragma unroll
+  for (int i = 0; i < (DW ? V * 8 : 1); ++i) acc[i] = 0.0f;
+
+  if (!DW || complete) {
+    bwd_wide_block<V, TW, FULL, DX, DW, true>(a, item, blk, w_s, dot_s, acc);
+  } else {
+    bwd_wide_block<V, TW, FULL, DX, DW, false>(a, item, blk, w_s, dot_s, acc);
+    return;
+  }
+
+  if (DW) {
+    // In-block stream tree, 1024 columns at a time: every stream stores its
+    // sums for the tile, then each thread reduces its columns.
+    float* Pb = a.P + (int64_t)blk * H;
+#pragma unroll
+    for (int t = 0; t < Sh::NTILE; ++t) {
+      if (t > 0) __syncthreads();
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const int K = half * V + k;   // 512-column chunk index within the row
+        if ((K >> 1) == t) {
+          float* dst = &tile_s[stream * 1024 + ((K & 1) * 64 + lane) * 8];
+          store_f4(dst, acc[k * 8 + 0], acc[k * 8 + 1], acc[k * 8 + 2], acc[k * 8 + 3]);
+          store_f4(dst + 4, acc[k * 8 + 4], acc[k * 8 + 5], acc[k * 8 + 6], acc[k * 8 + 7]);
+        }
+      }
+      __syncthreads();
+      for (int c = tid; c < 1024; c += 512) {
+        const int col = t * 1024 + c;
+        if (col < H) {
+          float v;
+          if (S == 8) {
+            float q[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w) q[w] = tile_s[(w % S) * 1024 + c];
+            v = stream_tree8(q);
+          } else {
+            const float q0 = tile_s[0 * 1024 + c], q1 = tile_s[1 * 1024 + c];
+            const float q2 = tile_s[(2 % S) * 1024 + c], q3 = tile_s[(3 % S) * 1024 + c];
+            v = (q0 + q1) + (q2 + q3);
+          }
+          Pb[col] = v;
+        }
+      }
+    }
+  }
+}
+
+// Small rows: hidden = 8L (L in 1..32), one group of L lanes per row; the
+// 64 slots' contributions go through LDS and 8 streams fold them there.
+template <int L, bool DX, bool DW>
+__global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
+  constexpr int H = 8 * L;
+  constexpr int GROUPS = 256 / L;
+  constexpr int ITERS = (kBlockRows + GROUPS - 1) / GROUPS;
+  __shared__ float c_s[DW ? kBlockRows * H : 1];
+  __shared__ float q_s[DW ? 8 * H : 1];
+  const int tid = threadIdx.x;
+  const int g = tid / L;
+  const int sub = tid % L;
+  const int item = blockIdx.x;
+
+  if (item >= a.plan.n_items) {
+    if (DX) {
+      const int idx = (item - a.plan.n_items) * GROUPS + g;
+      if (idx < a.plan.n_pad)
+        store16(a.dx + (int64_t)a.plan.pad_rows[idx] * H + sub * 8, make_uint4(0, 0, 0, 0));
+    }
+    return;
+  }
+  float wf[8];
+  if (DX) unpack8(load16(a.w + sub * 8), wf);
+
+  int blk;
+  bool complete;
+  if (a.plan.item_info != nullptr) {
+    const int info = a.plan.item_info[item];
+    complete = info >= 0;
+    blk = complete ? info : ~info;
+  } else {
+    blk = item;
+    complete = true;
+  }
+
+  for (int it = 0; it < ITERS; ++it) {
+    const int s = g + it * GROUPS;
+    const int p = s < kBlockRows ? slot_row(a, item, blk, s) : -1;
+    uint4 xv = make_uint4(0, 0, 0, 0), dv = make_uint4(0, 0, 0, 0);
+    float r = 0.0f;
+    if (p >= 0) {
+      xv = load16(a.x + (int64_t)p * H + sub * 8);
+      dv = load16(a.dy + (int64_t)p * H + sub * 8);
+      r = a.rstd[p];
+    }
+    float xf[8], df[8], pr[8];
+    unpack8(xv, xf);
+    unpack8(dv, df);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pr[e] = df[e] * xf[e];
+    if (DX) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = fmaf(pr[e], wf[e], dot);
+      dot = group_sum<L>(dot);
+      if (p >= 0) {
+        const float kk = ((r * r) * r) * (dot / (float)H);
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(-xf[e], kk, r * (df[e] * wf[e]));
+        store16(a.dx + (int64_t)p * H + sub * 8, pack8(o));
+      }
+    }
+    if (DW) {
+      float c[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c[e] = pr[e] * r;   // +0.0 for slots this call lacks
+      if (complete) {
+        if (s < kBlockRows) {
+          store_f4(&c_s[s * H + sub * 8], c[0], c[1], c[2], c[3]);
+          store_f4(&c_s[s * H + sub * 8 + 4], c[4], c[5], c[6], c[7]);
+        }
+      } else if (p >= 0) {
+        float* srow = a.S + ((int64_t)blk * kBlockRows + s) * H + sub * 8;
+        store_f4(srow, c[0], c[1], c[2], c[3]);
+        store_f4(srow + 4, c[4], c[5], c[6], c[7]);
+      }
+    }
+  }
+  if (DW && complete) {
+    __syncthreads();
+    for (int idx = tid; idx < 8 * H; idx += 256) {
+      const int w = idx / H, j = idx % H;
+      float q = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kSlotsPerStream; ++i) q = q + c_s[(w + 8 * i) * H + j];
+      q_s[w * H + j] = q;
+    }
+    __syncthreads();
+    for (int j = tid; j < H; j += 256) {
+      float q[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) q[w] = q_s[w * H + j];
+      a.P[(int64_t)blk * H + j] = stream_tree8(q);
+    }
+  }
+}
+
+// ----------------------------------------------------------------- finalize
+// Partials of spilled blocks, folded from their spill rows in the same order
+// as the backward kernel folds complete blocks.
+__global__ __launch_bounds__(256) void rebuild_kernel(const float* __restrict__ S,
+                                                      float* __restrict__ P,
+                                                      const int32_t* __restrict__ blocks,
+                                                      int64_t T, int H, int streams) {
+  const int b = blocks[blockIdx.x];
+  const int j = blockIdx.y * 256 + threadIdx.x;
+  if (j >= H) return;
+  float q[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    float acc = 0.0f;
+    if (w < streams) {
+      for (int s = w; s < kBlockRows; s += streams) {
+        const int64_t l = (int64_t)b * kBlockRows + s;
+        if (l < T) acc = acc + S[l * H + j];
+      }
+    }
+    q[w] = acc;
+  }
+  P[(int64_t)b * H + j] = streams == 8 ? stream_tree8(q) : (q[0] + q[1]) + (q[2] + q[3]);
+}
+
+// One level group of the cross-block tree: out[g] = perfect pairwise tree over
+// in[g*G .. g*G+G) with +0.0 past n_in.
+template <int G>
+__global__ __launch_bounds__(256) void tree_kernel(const float* __restrict__ in, int64_t n_in,
+                                                   float* __restrict__ out, int H) {
+  const int j = blockIdx.y * 256 + threadIdx.x;
+  const int64_t g = blockIdx.x;
+  if (j >= H) return;
+  float v[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int64_t idx = g * G + i;
+    v[i] = idx < n_in ? in[idx * H + j] : 0.0f;
+  }
+#pragma unroll
+  for (int st = 1; st < G; st *= 2)
+#pragma unroll
+    for (int i = 0; i < G; i += 2 * st) v[i] = v[i] + v[i + st];
+  out[g * H + j] = v[0];
+}
+
+__global__ void fill_zero_kernel(float* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+// ----------------------------------------------------------------- dispatch
+static int small_lanes(int hidden) {
+  switch (hidden) {
+    case 8: return 1;
+    case 16: return 2;
+    case 32: return 4;
+    case 64: return 8;
+    case 128: return 16;
+    case 256: return 32;
+    default: return 0;
+  }
+}
+
+bool hidden_supported(int hidden) {
+  return hidden > 0 && hidden % 8 == 0 && hidden <= kMaxHidden;
+}
+
+static int wide_tw(int hidden) { return hidden <= kEightStreamMaxHidden ? 1 : 2; }
+static int wide_v(int hidden) {
+  const int per = 512 * wide_tw(hidden);
+  return (hidden + per - 1) / per;
+}
+
+const char* fwd_variant(int hidden) {
+  return small_lanes(hidden) ? "fwd_small(lanes_per_row=hidden/8)" : "fwd_wide(wave_per_row)";
+}
+const char* bwd_variant(int hidden) {
+  if (small_lanes(hidden)) return "bwd_small(lds_fold, streams=8)";
+  return wide_tw(hidden) == 1 ? "bwd_wide(wave_per_row, streams=8)"
+                              : "bwd_wide(two_waves_per_row, streams=4)";
+}
+
+static int grid_cap() { return 256 * 16; }
+
+template <int V>
+static void fwd_wide_go(const FwdArgs& a, hipStream_t st) {
+  int64_t g = (a.rows + 3) / 4;
+  if (g > grid_cap()) g = grid_cap();
+  fwd_wide_kernel<V><<<dim3((unsigned)g), dim3(256), 0, st>>>(a);
+}
+template <int L>
+static void fwd_small_go(const FwdArgs& a, hipStream_t st) {
+  constexpr int GROUPS = 256 / L;
+  int64_t g = (a.rows + GROUPS - 1) / GROUPS;
+  if (g > grid_cap()) g = grid_cap();
+  fwd_small_kernel<L><<<dim3((unsigned)g), dim3(256), 0, st>>>(a);
+}
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
+  if (a.rows == 0) return hipSuccess;
+  switch (small_lanes(a.hidden)) {
+    case 1: fwd_small_go<1>(a, st); return hipGetLastError();
+    case 2: fwd_small_go<2>(a, st); return hipGetLastError();
+    case 4: fwd_small_go<4>(a, st); return hipGetLastError();
+    case 8: fwd_small_go<8>(a, st); return hipGetLastError();
+    case 16: fwd_small_go<16>(a, st); return hipGetLastError();
+    case 32: fwd_small_go<32>(a, st); return hipGetLastError();
+    default: break;
+  }
+  const int V = (a.hidden + 511) / 512;
+  switch (V) {
+#define RBI_FWD(v) case v: fwd_wide_go<v>(a, st); break;
+    RBI_FWD(1) RBI_FWD(2) RBI_FWD(3) RBI_FWD(4) RBI_FWD(5) RBI_FWD(6) RBI_FWD(7) RBI_FWD(8)
+    RBI_FWD(9) RBI_FWD(10) RBI_FWD(11) RBI_FWD(12) RBI_FWD(13) RBI_FWD(14) RBI_FWD(15)
+    RBI_FWD(16) RBI_FWD(17) RBI_FWD(18) RBI_FWD(19) RBI_FWD(20)
+#undef RBI_FWD
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int V, int TW, bool FULL>
+static void bwd_wide_go2(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+  const int pad_groups = dx ? (a.plan.n_pad + 7) / 8 : 0;
+  const dim3 grid((unsigned)(a.plan.n_items + pad_groups)), block(512);
+  if (dx && dw) bwd_wide_kernel<V, TW, FULL, true, true><<<grid, block, 0, st>>>(a);
+  else if (dx) bwd_wide_kernel<V, TW, FULL, true, false><<<grid, block, 0, st>>>(a);
+  else bwd_wide_kernel<V, TW, FULL, false, true><<<grid, block, 0, st>>>(a);
+}
+template <int V, int TW>
+static void bwd_wide_go(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+  if (a.hidden == 512 * V * TW) bwd_wide_go2<V, TW, true>(a, dx, dw, st);
+  else bwd_wide_go2<V, TW, false>(a, dx, dw, st);
+}
+template <int L>
+static void bwd_small_go(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+  constexpr int GROUPS = 256 / L;
+  const int pad_groups = dx ? (a.plan.n_pad + GROUPS - 1) / GROUPS : 0;
+  const dim3 grid((unsigned)(a.plan.n_items + pad_groups)), block(256);
+  if (dx && dw) bwd_small_kernel<L, true, true><<<grid, block, 0, st>>>(a);
+  else if (dx) bwd_small_kernel<L, true, false><<<grid, block, 0, st>>>(a);
+  else bwd_small_kernel<L, false, true><<<grid, block, 0, st>>>(a);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+  const int pads = dx ? a.plan.n_pad : 0;
+  if (a.plan.n_items + pads == 0) return hipSuccess;
+  switch (small_lanes(a.hidden)) {
+    case 1: bwd_small_go<1>(a, dx, dw, st); return hipGetLastError();
+    case 2: bwd_small_go<2>(a, dx, dw, st); return hipGetLastError();
+    case 4: bwd_small_go<4>(a, dx, dw, st); return hipGetLastError();
+    case 8: bwd_small_go<8>(a, dx, dw, st); return hipGetLastError();
+    case 16: bwd_small_go<16>(a, dx, dw, st); return hipGetLastError();
+    case 32: bwd_small_go<32>(a, dx, dw, st); return hipGetLastError();
+    default: break;
+  }
+  const int tw = wide_tw(a.hidden), V = wide_v(a.hidden);
+  if (tw == 1) {
+    switch (V) {
+#define RBI_BWD1(v) case v: bwd_wide_go<v, 1>(a, dx, dw, st); break;
+      RBI_BWD1(1) RBI_BWD1(2) RBI_BWD1(3) RBI_BWD1(4) RBI_BWD1(5)
+      RBI_BWD1(6) RBI_BWD1(7) RBI_BWD1(8) RBI_BWD1(9) RBI_BWD1(10)
+#undef RBI_BWD1
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (V) {
+#define RBI_BWD2(v) case v: bwd_wide_go<v, 2>(a, dx, dw, st); break;
+      RBI_BWD2(6) RBI_BWD2(7) RBI_BWD2(8) RBI_BWD2(9) RBI_BWD2(10)
+#undef RBI_BWD2
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rebuild(const float* S, float* P, const int32_t* blocks, int32_t n_blocks,
+                          int64_t n_logical, int32_t hidden, hipStream_t st) {
+  if (n_blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)n_blocks, (unsigned)((hidden + 255) / 256));
+  rebuild_kernel<<<grid, dim3(256), 0, st>>>(S, P, blocks, n_logical, hidden,
+                                              cdo_streams(hidden));
+  return hipGetLastError();
+}
+
+constexpr int kTreeGroup = 32;
+
+int64_t tree_scratch_rows(int64_t nb) {
+  const int64_t a = (nb + kTreeGroup - 1) / kTreeGroup;
+  const int64_t b = (a + kTreeGroup - 1) / kTreeGroup;
+  return a + b;
+}
+
+hipError_t launch_tree(const float* P, int64_t nb, float* tmp, float* dweight, int32_t hidden,
+                       hipStream_t st) {
+  const unsigned gx = (unsigned)((hidden + 255) / 256);
+  if (nb == 0) {
+    fill_zero_kernel<<<dim3((unsigned)((hidden + 255) / 256)), dim3(256), 0, st>>>(dweight, hidden);
+    return hipGetLastError();
+  }
+  // ping-pong between two scratch regions sized for the first two levels
+  const int64_t rows_a = (nb + kTreeGroup - 1) / kTreeGroup;
+  float* buf[2] = {tmp, tmp + rows_a * hidden};
+  const float* in = P;
+  int64_t n = nb;
+  int which = 0;
+  while (true) {
+    const int64_t groups = (n + kTreeGroup - 1) / kTreeGroup;
+    float* out = groups == 1 ? dweight : buf[which];
+    tree_kernel<kTreeGroup><<<dim3((unsigned)groups, gx), dim3(256), 0, st>>>(in, n, out, hidden);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (groups == 1) break;
+    in = out;
+    n = groups;
+    which ^= 1;
+  }
+  return hipSuccess;
+}
+
+}  // namespace rbi

@@ -1,0 +1,144 @@
+// plan.cpp -- host-side layout plans and accumulator bookkeeping (no HIP).
+#include "plan.h"
+
+#include <algorithm>
+#include <cstring>
+
+namespace rbi {
+
+int build_plan(const int32_t* row_logical, int64_t rows, int64_t n_logical, PlanHost* out,
+               std::string* err) {
+  if (rows < 0 || n_logical < 0) {
+    *err = "rows and n_logical must be non-negative";
+    return kEInval;
+  }
+  if (rows > 0 && row_logical == nullptr) {
+    *err = "row_logical is NULL";
+    return kEInval;
+  }
+  if (rows > INT32_MAX || n_logical > INT32_MAX) {
+    *err = "rows and n_logical must be below 2^31";
+    return kEUnsupported;
+  }
+  const int64_t nb = num_blocks(n_logical);
+  std::vector<uint8_t> seen(static_cast<size_t>(n_logical), 0);
+  std::vector<int32_t> in_call(static_cast<size_t>(nb), 0);  // rows of block in this call
+  int64_t n_real = 0;
+  for (int64_t p = 0; p < rows; ++p) {
+    const int32_t l = row_logical[p];
+    if (l == -1) continue;
+    if (l < 0 || l >= n_logical) {
+      *err = "row_logical[" + std::to_string(p) + "] = " + std::to_string(l) +
+             " is outside [-1, n_logical = " + std::to_string(n_logical) + ")";
+      return kELayout;
+    }
+    if (seen[l]) {
+      *err = "logical row " + std::to_string(l) + " appears twice (second at physical row " +
+             std::to_string(p) + ")";
+      return kELayout;
+    }
+    seen[l] = 1;
+    in_call[l / kBlockRows] += 1;
+    ++n_real;
+  }
+
+  PlanHost& P = *out;
+  P = PlanHost();
+  P.rows = rows;
+  P.n_logical = n_logical;
+  P.row_logical.assign(row_logical, row_logical + rows);
+  P.logical_rows.reserve(static_cast<size_t>(n_real));
+
+  // Items in ascending block order.
+  std::vector<int32_t> item_of_block(static_cast<size_t>(nb), -1);
+  for (int64_t b = 0; b < nb; ++b) {
+    if (in_call[b] == 0) continue;
+    const int64_t present = std::min<int64_t>(kBlockRows, n_logical - b * kBlockRows);
+    const bool complete = in_call[b] == present;
+    item_of_block[b] = static_cast<int32_t>(P.item_info.size());
+    P.item_info.push_back(complete ? static_cast<int32_t>(b) : ~static_cast<int32_t>(b));
+    if (complete) ++P.n_complete; else ++P.n_partial;
+  }
+  P.slot_phys.assign(P.item_info.size() * kBlockRows, -1);
+  for (int64_t p = 0; p < rows; ++p) {
+    const int32_t l = row_logical[p];
+    if (l < 0) {
+      P.pad_rows.push_back(static_cast<int32_t>(p));
+      continue;
+    }
+    const int32_t item = item_of_block[l / kBlockRows];
+    P.slot_phys[static_cast<size_t>(item) * kBlockRows + (l % kBlockRows)] = static_cast<int32_t>(p);
+    P.logical_rows.push_back(l);
+  }
+  return kOk;
+}
+
+void AccHost::init(int64_t T, int64_t H) {
+  n_logical = T;
+  hidden = H;
+  nb = num_blocks(T);
+  covered.assign(static_cast<size_t>(T), 0);
+  block_state.assign(static_cast<size_t>(nb), kBlockNone);
+  finalized = false;
+}
+
+void AccHost::reset() {
+  std::fill(covered.begin(), covered.end(), 0);
+  std::fill(block_state.begin(), block_state.end(), kBlockNone);
+  finalized = false;
+}
+
+int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err) {
+  if (finalized) {
+    *err = "accumulator already finalized; call rmsnorm_dw_acc_reset first";
+    return kEState;
+  }
+  if (plan == nullptr) {
+    if (rows != n_logical) {
+      *err = "identity layout with an accumulator needs rows (" + std::to_string(rows) +
+             ") == n_logical (" + std::to_string(n_logical) + ")";
+      return kELayout;
+    }
+    for (int64_t l = 0; l < rows; ++l) {
+      if (covered[l]) {
+        *err = "logical row " + std::to_string(l) + " already contributed";
+        return kECoverage;
+      }
+    }
+    std::memset(covered.data(), 1, covered.size());
+    std::fill(block_state.begin(), block_state.end(), kBlockDirect);
+    return kOk;
+  }
+  if (plan->n_logical != n_logical) {
+    *err = "layout n_logical (" + std::to_string(plan->n_logical) +
+           ") differs from the accumulator's (" + std::to_string(n_logical) + ")";
+    return kELayout;
+  }
+  for (int32_t l : plan->logical_rows) {
+    if (covered[l]) {
+      *err = "logical row " + std::to_string(l) + " already contributed";
+      return kECoverage;
+    }
+  }
+  for (int32_t l : plan->logical_rows) covered[l] = 1;
+  for (int32_t info : plan->item_info) {
+    if (info >= 0) block_state[info] = kBlockDirect;
+    else block_state[~info] = kBlockSpilled;
+  }
+  return kOk;
+}
+
+int AccHost::prepare_finalize(std::vector<int32_t>* spilled, std::string* err) const {
+  for (int64_t l = 0; l < n_logical; ++l) {
+    if (covered[l] != 1) {
+      *err = "logical row " + std::to_string(l) + " has not contributed";
+      return kECoverage;
+    }
+  }
+  spilled->clear();
+  for (int64_t b = 0; b < nb; ++b)
+    if (block_state[b] == kBlockSpilled) spilled->push_back(static_cast<int32_t>(b));
+  return kOk;
+}
+
+}  // namespace rbi

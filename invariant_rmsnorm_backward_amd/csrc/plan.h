@@ -1,0 +1,75 @@
+// plan.h -- host-side layout plans and dweight-accumulator bookkeeping.
+//
+// Pure C++ (no HIP calls), so every check here runs on a machine without a
+// GPU.  A plan turns a call's physical->logical row map into the work list
+// of the backward kernel: one item per canonical block of 64 logical rows
+// that the call touches, with the physical row of each of its 64 slots and
+// whether the call holds every present row of the block (then the kernel
+// folds the block completely; otherwise it spills the rows' contributions
+// for the finalize step).  The accumulator bookkeeping enforces that every
+// logical row contributes exactly once ("[WS1 Closeout][Backward] Reusable
+// gradient-invariance harness and operator adapters", Acceptance criteria:
+// B1 and BN use the same sample set and a fixed aggregation order).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace rbi {
+
+constexpr int kBlockRows = 64;   // logical rows per canonical block
+constexpr int kStreams = 8;      // in-block fold streams
+constexpr int kSlotsPerStream = kBlockRows / kStreams;
+
+enum Status : int {
+  kOk = 0,
+  kEInval = -1,
+  kEUnsupported = -2,
+  kELayout = -3,
+  kECoverage = -4,
+  kEState = -5,
+  kEHip = -6,
+};
+
+inline int64_t num_blocks(int64_t n_logical) { return (n_logical + kBlockRows - 1) / kBlockRows; }
+
+struct PlanHost {
+  int64_t rows = 0;
+  int64_t n_logical = 0;
+  std::vector<int32_t> row_logical;  // [rows], -1 = padding
+  std::vector<int32_t> item_info;    // [n_items]: block id if complete, ~block id if partial
+  std::vector<int32_t> slot_phys;    // [n_items * 64]: physical row or -1
+  std::vector<int32_t> pad_rows;     // physical rows mapped to -1
+  std::vector<int32_t> logical_rows; // real rows' logical ids (for coverage accounting)
+  int64_t n_complete = 0;
+  int64_t n_partial = 0;
+  int64_t n_items() const { return static_cast<int64_t>(item_info.size()); }
+};
+
+// Validates the map and builds the plan.  Returns kOk or kELayout / kEInval
+// with a message in *err.
+int build_plan(const int32_t* row_logical, int64_t rows, int64_t n_logical, PlanHost* out,
+               std::string* err);
+
+enum BlockState : uint8_t { kBlockNone = 0, kBlockDirect = 1, kBlockSpilled = 2 };
+
+struct AccHost {
+  int64_t n_logical = 0;
+  int64_t hidden = 0;
+  int64_t nb = 0;
+  std::vector<uint8_t> covered;       // per logical row: contributions so far (0/1)
+  std::vector<uint8_t> block_state;   // per block: BlockState
+  bool finalized = false;
+
+  void init(int64_t T, int64_t H);
+  void reset();
+  // Registers one call.  plan == nullptr means the identity map over `rows`
+  // rows (all blocks complete).  Checks everything before changing state.
+  int register_call(const PlanHost* plan, int64_t rows, std::string* err);
+  // Checks that every logical row contributed exactly once and lists the
+  // spilled blocks in ascending order.
+  int prepare_finalize(std::vector<int32_t>* spilled, std::string* err) const;
+};
+
+}  // namespace rbi

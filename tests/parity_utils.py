@@ -1,0 +1,62 @@
+"""Shared helpers of the GPU parity tests (imports the oracle: test-only)."""
+import numpy as np
+import torch
+
+import oracle
+from invariant_rmsnorm_backward_amd import adapters, inputs, layouts
+
+
+def make_data(wl: inputs.Workload) -> adapters.NormInputs:
+    """Logical inputs generated on the CPU, copied to the GPU."""
+    return adapters.make_inputs(wl, device="cuda", gen_device="cpu")
+
+
+def oracle_reference(wl: inputs.Workload) -> dict:
+    """FP64 oracle outputs in logical order, from CPU-generated inputs."""
+    xb = inputs.bf16_bits(inputs.gen_x(wl))
+    wb = inputs.bf16_bits(inputs.gen_w(wl))
+    dyb = inputs.bf16_bits(inputs.gen_dy(wl))
+    y, rstd = oracle.rmsnorm_fwd_bf16(xb, wb, wl.eps)
+    dx, dw, _ = oracle.rmsnorm_bwd_bf16(xb, wb, dyb, wl.eps)
+    return {"y": y, "rstd": rstd, "dx": dx, "dweight": dw}
+
+
+def standard_cells(wl: inputs.Workload, chunk: int):
+    """Every layout family for one logical multiset."""
+    T = wl.n_tokens
+    rev = list(range(wl.n_samples))[::-1]
+    return [
+        layouts.full(wl),
+        layouts.chunked_packed(wl, chunk=chunk, name="BN/chunked"),
+        layouts.chunked_per_sample(wl, chunk=chunk, name="BN/chunked_per_sample"),
+        layouts.singleton_aggregate(wl),
+        layouts.singleton_aggregate(wl, order=rev, name="B1-singleton_aggregate/reversed_calls"),
+        layouts.padded(wl, T + 37, "right"),
+        layouts.padded(wl, T + 37, "left"),
+        layouts.permuted(wl),
+        layouts.permuted(wl, perm=rev, name="BN/permuted_reverse"),
+    ]
+
+
+def qk_cells(wq, wk, chunk):
+    cq = standard_cells(wq, chunk)
+    ck = standard_cells(wk, chunk)
+    return [adapters.PairCell(a.name, a, b) for a, b in zip(cq, ck)]
+
+
+def bf16_ulp_fraction(got_bits: np.ndarray, ref64: np.ndarray) -> float:
+    """Fraction of bf16 outputs within one bf16 ulp of the FP64 reference."""
+    g = (got_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    r = ref64.astype(np.float64)
+    ulp = np.abs(r) * 2.0 ** -7
+    return float(np.mean(np.abs(g - r) <= np.maximum(ulp, 1e-30)))
+
+
+def physical_rstd(rstd_logical: np.ndarray, call) -> torch.Tensor:
+    """rstd for one call's physical rows (padding rows get NaN: never read)."""
+    if call.row_logical is None:
+        return torch.from_numpy(rstd_logical.astype(np.float32)).cuda()
+    rl = call.row_logical.astype(np.int64)
+    out = np.full(call.rows, np.nan, dtype=np.float32)
+    out[rl >= 0] = rstd_logical[rl[rl >= 0]]
+    return torch.from_numpy(out).cuda()

@@ -1,0 +1,123 @@
+"""The C-ABI library loads, exports every declared symbol, and its host-side
+checks work without a GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from invariant_rmsnorm_backward_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmsnorm_bi.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rmsnorm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_contrib", "rmsnorm_dw_finalize"):
+        assert n in names
+    assert sorted(binding.EXPORTED) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_backend_info_names_the_order(lib):
+    info = binding.rmsnorm_backend_info()
+    assert "gfx950" in info and "cdo=v1" in info and "no atomics" in info
+    assert binding.rmsnorm_max_hidden() >= 8192
+
+
+def test_layout_check_stats_and_errors(lib):
+    # hidden-independent plan: 59 rows padded to 80, permuted samples
+    rl = np.full(80, -1, dtype=np.int32)
+    rl[10:69] = np.random.default_rng(0).permutation(59)
+    st = binding.rmsnorm_layout_check(rl, 59)
+    assert st == {"blocks": 1, "complete_blocks": 1, "partial_blocks": 0, "pad_rows": 21,
+                  "real_rows": 59}
+    # a chunk holding rows 60..129 of 200: blocks 0 and 2 in part, block 1 whole
+    st = binding.rmsnorm_layout_check(np.arange(60, 130, dtype=np.int32), 200)
+    assert st["blocks"] == 3 and st["partial_blocks"] == 2 and st["complete_blocks"] == 1
+    st = binding.rmsnorm_layout_check(np.arange(64, 128, dtype=np.int32), 200)
+    assert st["complete_blocks"] == 1 and st["partial_blocks"] == 0
+    # the last block is complete when it holds every present row (T = 70)
+    st = binding.rmsnorm_layout_check(np.arange(64, 70, dtype=np.int32), 70)
+    assert st["complete_blocks"] == 1
+    for bad, code in (([0, 0], binding.ELAYOUT), ([0, 5], binding.ELAYOUT),
+                      ([-2, 1], binding.ELAYOUT)):
+        with pytest.raises(binding.RmsNormError) as ei:
+            binding.rmsnorm_layout_check(np.array(bad, dtype=np.int32), 5)
+        assert ei.value.code == code
+        assert "logical" in ei.value.message or "outside" in ei.value.message
+
+
+def test_argument_errors_are_refused_before_any_launch(lib):
+    A = 1 << 20  # a fake, aligned address: never dereferenced because checks fail first
+    cases = [
+        (dict(hidden=12), binding.EUNSUPPORTED),
+        (dict(hidden=0), binding.EINVAL),
+        (dict(hidden=binding.rmsnorm_max_hidden() + 8), binding.EUNSUPPORTED),
+        (dict(rows=-1), binding.EINVAL),
+        (dict(eps=-1.0), binding.EINVAL),
+        (dict(eps=float("nan")), binding.EINVAL),
+        (dict(x=0), binding.EINVAL),
+        (dict(x=A + 2), binding.EUNSUPPORTED),
+        (dict(y=A), binding.EINVAL),                   # y aliases x
+    ]
+    for over, code in cases:
+        args = dict(x=A, w=A + 4096 * 1024, y=A + 8192 * 1024, rstd=A + 12288 * 1024, rows=4,
+                    hidden=4096, eps=1e-6)
+        args.update(over)
+        with pytest.raises(binding.RmsNormError) as ei:
+            binding.rmsnorm_fwd(args["x"], args["w"], args["y"], args["rstd"], args["rows"],
+                                args["hidden"], args["eps"], None, None)
+        assert ei.value.code == code, (over, ei.value)
+    with pytest.raises(binding.RmsNormError) as ei:
+        binding.rmsnorm_dw_contrib(A, A, A, 4, 4096, None, None, None)
+    assert ei.value.code == binding.EINVAL
+    with pytest.raises(binding.RmsNormError) as ei:
+        binding.rmsnorm_dw_finalize(None, A, None)
+    assert ei.value.code == binding.EINVAL
+
+
+def test_no_atomics_and_no_fallbacks_in_the_library_sources():
+    csrc = os.path.join(ROOT, "invariant_rmsnorm_backward_amd", "csrc")
+    for name in os.listdir(csrc):
+        text = open(os.path.join(csrc, name)).read()
+        code = re.sub(r"//.*", "", re.sub(r"/\*.*?\*/", "", text, flags=re.S))
+        assert not re.search(r"\batomic\w*\s*\(|__atomic|std::atomic|__hip_atomic", code), name
+        assert "__CUDA" not in code and "cuda_runtime" not in code, name
+        assert "__HIP_PLATFORM" not in code, name
+    # variant selection keys on the hidden size only
+    k = open(os.path.join(csrc, "kernels.hip")).read()
+    for fn in ("small_lanes", "wide_tw", "wide_v"):
+        sig = re.search(rf"static int {fn}\(([^)]*)\)", k).group(1)
+        assert sig.strip() == "int hidden", fn
+
+
+def test_product_code_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "invariant_rmsnorm_backward_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "liboracle" not in text, f

@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path against the FP64 oracle, and bitwise invariance
+across every layout of the same logical rows.  Sizes span several 64-row
+blocks and a ragged tail, and every kernel variant (lane groups, one
+wavefront per row with and without lane masks, two wavefronts per row)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from invariant_rmsnorm_backward_amd import adapters, binding, contract, harness, inputs, layouts
+from tests import parity_utils as pu
+
+pytestmark = pytest.mark.gpu
+CONTRACT = contract.load_contract()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the gpu tests need an MI355X"
+    binding.load()
+
+
+def _run(op, cells, data, ref, name):
+    print(f"[parity] {name}: {len(cells)} cells", flush=True)
+    rep = harness.assert_gradient_batch_invariant(op, cells, CONTRACT, data=data, reference=ref,
+                                                  raise_on_red=False)
+    if not rep.strict:
+        print(rep.to_json()[:4000], flush=True)
+    assert rep.strict, rep.first_failure
+    return rep
+
+
+def _check_call_log(adapter_calls, cells):
+    by_cell = {}
+    for cname, _, rows in adapter_calls:
+        by_cell.setdefault(cname, []).append(rows)
+    for c in cells:
+        assert by_cell[c.name] == c.call_shapes, c.name
+    assert len(by_cell["BN/full"]) == 1
+
+
+WIDE_CASES = {
+    # name: (base workload, hidden, lengths, chunk)
+    "h4096": (inputs.workload_h4096, 4096, [300, 257, 150], 100),
+    "h8192": (inputs.workload_h8192, 8192, [130, 333, 61], 128),
+    "h5120": (inputs.workload_h5120, 5120, [200, 100, 50, 30, 77], 64),
+    "h512": (inputs.workload_h4096, 512, [70, 45, 129], 50),
+    "h1000_masked": (inputs.workload_h4096, 1000, [70, 45], 33),
+    "h2048": (inputs.workload_h4096, 2048, [64, 64, 65], 64),
+    "h6144_two_waves": (inputs.workload_h8192, 6144, [99, 30], 40),
+    "h9000_two_waves_masked": (inputs.workload_h8192, 9000, [77, 60], 64),
+    "h40_masked": (inputs.workload_h8, 40, [70, 45, 3], 17),
+    "h16": (inputs.workload_h8, 16, [70, 45, 3], 17),
+    "h128": (inputs.workload_h8, 128, [130, 2, 61], 32),
+    "h256": (inputs.workload_h8, 256, [130, 61], 32),
+}
+
+
+@pytest.mark.parametrize("case", sorted(WIDE_CASES))
+def test_rms_norm_parity_and_invariance(case):
+    base, H, lengths, chunk = WIDE_CASES[case]
+    wl = inputs.scaled(base(), f"{case}_t{sum(lengths)}", hidden=H, lengths=lengths, pad_rows=0)
+    data = pu.make_data(wl)
+    ref = pu.oracle_reference(wl)
+    cells = pu.standard_cells(wl, chunk)
+    ad = adapters.RmsNormAdapter()
+    rep = _run(ad, cells, data, ref, case)
+    _check_call_log(ad.call_log, cells)
+    # diagnostics that are reported, not gated: bf16 outputs within one ulp of FP64
+    out = ad.run_cell(cells[0], data)
+    frac = pu.bf16_ulp_fraction(out["dx"], ref["dx"])
+    print(f"[parity] {case}: dx within 1 bf16 ulp of FP64: {frac:.5f}", flush=True)
+    assert frac > 0.99
+    assert rep.active_token_denominator == inputs.n_active(wl)
+
+
+def test_page_matrix_h8_t59():
+    """The hidden=8, 59-row matrix of the page: every cell bitwise equal."""
+    wl = inputs.workload_h8()
+    data = pu.make_data(wl)
+    ref = pu.oracle_reference(wl)
+    cells = layouts.page_matrix(wl)
+    ad = adapters.RmsNormAdapter()
+    rep = _run(ad, cells, data, ref, "page_matrix_h8")
+    _check_call_log(ad.call_log, cells)
+    names = {c.name for c in rep.cells}
+    assert {"BN/full", "BN/chunked", "B1-singleton_aggregate/full", "BN/padded_right",
+            "BN/padded_left", "BN/permuted"} <= names
+    assert all(v.max_abs == 0.0 for v in rep.invariance_reports)
+
+
+def test_qk_norm_parity_and_invariance():
+    wq = inputs.scaled(inputs.workload_qk("q"), "qk_q_small", lengths=[100, 37, 64])
+    wk = inputs.scaled(inputs.workload_qk("k"), "qk_k_small", lengths=[100, 37, 64])
+    data = adapters.QkInputs("qk_small", pu.make_data(wq), pu.make_data(wk))
+    rq, rk = pu.oracle_reference(wq), pu.oracle_reference(wk)
+    ref = {"dq": rq["dx"], "dk": rk["dx"], "dweight_q": rq["dweight"], "dweight_k": rk["dweight"],
+           "yq": rq["y"], "yk": rk["y"], "rstd_q": rq["rstd"], "rstd_k": rk["rstd"]}
+    _run("qk_norm", pu.qk_cells(wq, wk, 16), data, ref, "qk_norm")
+
+
+def test_masked_padded_permuted_packing_h5120():
+    """25% padding rows between permuted samples, mask density 0.5."""
+    wl = inputs.scaled(inputs.workload_h5120(), "h5120_packed_small", lengths=[200, 100, 50, 30, 77],
+                       pad_rows=150)
+    data = pu.make_data(wl)
+    ref = pu.oracle_reference(wl)
+    cells = [layouts.full(wl), layouts.packed_with_padding(wl), layouts.singleton_aggregate(wl)]
+    rep = _run("rms_norm", cells, data, ref, "h5120_packed")
+    assert rep.cells[1].n_pad_rows == 150
+
+
+def test_inactive_rows_do_not_change_dweight_bits():
+    wl = inputs.scaled(inputs.workload_h5120(), "h5120_inactive", hidden=1024, lengths=[150, 90])
+    data = pu.make_data(wl)
+    s, p, _ = inputs.logical_keys(wl)
+    inactive = torch.from_numpy(~inputs.active_mask(wl, s, p)).cuda()
+    assert bool(inactive.any())
+    ad = adapters.RmsNormAdapter()
+    base = ad.run_cell(layouts.full(wl), data)
+    x2 = data.x.clone()
+    x2[inactive] = (x2[inactive].float() * -3.0 + 0.5).to(torch.bfloat16)
+    data2 = adapters.NormInputs(data.name, wl, x2, data.w, data.dy, data.eps,
+                                data.active_token_denominator)
+    pert = ad.run_cell(layouts.permuted(wl), data2)
+    assert np.array_equal(base["dweight"].view(np.uint32), pert["dweight"].view(np.uint32))
+    act = ~inactive.cpu().numpy()
+    assert np.array_equal(base["dx"][act], pert["dx"][act])
+
+
+@pytest.mark.parametrize("H,lengths", [(8, [59]), (128, [200, 77]), (4096, [130, 70]),
+                                       (5120, [100, 29]), (1000, [64, 1]), (8192, [66, 70]),
+                                       (9000, [40, 41])])
+def test_dweight_is_the_canonical_order_bit_for_bit(H, lengths):
+    """Tree conformance: given the same FP32 rstd, the GPU dweight equals the
+    oracle's FP32 emulation of CDO-v1 bit for bit, for one call and for
+    chunked calls."""
+    wl = inputs.scaled(inputs.workload_h4096(), f"cdo_h{H}", hidden=H, lengths=lengths)
+    xb = inputs.bf16_bits(inputs.gen_x(wl))
+    wb = inputs.bf16_bits(inputs.gen_w(wl))
+    dyb = inputs.bf16_bits(inputs.gen_dy(wl))
+    _, rstd64 = oracle.rmsnorm_fwd_bf16(xb, wb, wl.eps)
+    rstd32 = rstd64.astype(np.float32)
+    want = oracle.cdo_v1_dweight_f32(xb, dyb, rstd32)
+    data = pu.make_data(wl)
+    T = wl.n_logical
+    for cell in (layouts.full(wl), layouts.chunked_packed(wl, chunk=23),
+                 layouts.padded(wl, T + 5, "left")):
+        acc = binding.DwAccumulator(T, H)
+        for call in cell.calls:
+            if call.row_logical is None:
+                xc, dyc, lay = data.x, data.dy, None
+            else:
+                rl = torch.from_numpy(call.row_logical.astype(np.int64)).cuda()
+                real = rl >= 0
+                xc = torch.zeros((call.rows, H), dtype=torch.bfloat16, device="cuda")
+                dyc = torch.zeros_like(xc)
+                xc[real] = data.x[rl[real]]
+                dyc[real] = data.dy[rl[real]]
+                lay = binding.Layout(call.row_logical, T)
+            binding.dw_contrib(xc, dyc, pu.physical_rstd(rstd32, call), acc, lay)
+        got = acc.finalize().cpu().numpy()
+        torch.cuda.synchronize()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (H, cell.name)
+    print(f"[cdo] H={H}: GPU dweight == CDO-v1 emulation bit for bit", flush=True)
+
+
+def test_fused_dweight_equals_dweight_only_path():
+    wl = inputs.scaled(inputs.workload_h4096(), "fused_vs_contrib", lengths=[300, 100])
+    data = pu.make_data(wl)
+    T, H = data.x.shape
+    a1 = binding.DwAccumulator(T, H)
+    y, rstd = binding.fwd(data.x, data.w, data.eps)
+    binding.bwd(data.x, data.w, data.dy, rstd, acc=a1)
+    d1 = a1.finalize().cpu().numpy()
+    a2 = binding.DwAccumulator(T, H)
+    binding.dw_contrib(data.x, data.dy, rstd, a2)
+    d2 = a2.finalize().cpu().numpy()
+    assert np.array_equal(d1.view(np.uint32), d2.view(np.uint32))
+
+
+def test_run_to_run_repeatability():
+    wl = inputs.scaled(inputs.workload_h4096(), "repeat", lengths=[700, 300])
+    data = pu.make_data(wl)
+    ad = adapters.RmsNormAdapter()
+    first = ad.run_cell(layouts.chunked_packed(wl, chunk=97), data)
+    for _ in range(5):
+        again = ad.run_cell(layouts.chunked_packed(wl, chunk=97), data)
+        for k in first:
+            assert np.array_equal(first[k], again[k]), k
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 129])
+def test_small_and_ragged_row_counts(T):
+    wl = inputs.scaled(inputs.workload_h4096(), f"ragged_{T}", hidden=768, lengths=[T])
+    data = pu.make_data(wl)
+    ref = pu.oracle_reference(wl)
+    cells = [layouts.full(wl), layouts.chunked_packed(wl, chunk=7),
+             layouts.padded(wl, T + 64, "right")]
+    _run("rms_norm", cells, data, ref, f"ragged_{T}")
+
+
+def test_zero_rows_and_empty_calls():
+    H = 4096
+    x = torch.zeros((3, H), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(H, dtype=torch.bfloat16, device="cuda")
+    y, rstd = binding.fwd(x, w, 1e-6)
+    torch.cuda.synchronize()
+    want = np.full(3, 1.0 / np.sqrt(np.float64(np.float32(1e-6))))    # eps^-1/2, closed form
+    assert CONTRACT.accuracy_passes(rstd.cpu().numpy(), want, "rstd")
+    assert bool((y.float() == 0).all())
+    # rows == 0 is a successful no-op, with and without an accumulator
+    e = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    binding.fwd(e, w, 1e-6)
+    acc = binding.DwAccumulator(0, H)
+    binding.bwd(e, w, e, torch.empty(0, device="cuda"), acc=acc)
+    dw = acc.finalize()
+    torch.cuda.synchronize()
+    assert bool((dw == 0).all())
+
+
+def test_accumulator_protocol_errors():
+    H, T = 512, 100
+    wl = inputs.scaled(inputs.workload_h4096(), "proto", hidden=H, lengths=[T])
+    data = pu.make_data(wl)
+    y, rstd = binding.fwd(data.x, data.w, data.eps)
+    acc = binding.DwAccumulator(T, H)
+    half = layouts.chunked_packed(wl, sizes=[60, 40]).calls
+    lay0 = binding.Layout(half[0].row_logical, T)
+    binding.dw_contrib(data.x[:60], data.dy[:60], rstd[:60], acc, lay0)
+    with pytest.raises(binding.RmsNormError) as ei:          # the same rows again
+        binding.dw_contrib(data.x[:60], data.dy[:60], rstd[:60], acc, lay0)
+    assert ei.value.code == binding.ECOVERAGE
+    with pytest.raises(binding.RmsNormError) as ei:          # rows 60..99 missing
+        acc.finalize()
+    assert ei.value.code == binding.ECOVERAGE
+    lay1 = binding.Layout(half[1].row_logical, T)
+    with pytest.raises(binding.RmsNormError) as ei:          # layout rows != call rows
+        binding.dw_contrib(data.x[:41], data.dy[:41], rstd[:41], acc, lay1)
+    assert ei.value.code == binding.ELAYOUT
+    binding.dw_contrib(data.x[60:], data.dy[60:], rstd[60:], acc, lay1)
+    d1 = acc.finalize().cpu().numpy()
+    with pytest.raises(binding.RmsNormError) as ei:          # after finalize
+        binding.dw_contrib(data.x[60:], data.dy[60:], rstd[60:], acc, lay1)
+    assert ei.value.code == binding.ESTATE
+    d2 = acc.finalize().cpu().numpy()                        # finalize again: same bits
+    assert np.array_equal(d1.view(np.uint32), d2.view(np.uint32))
+    acc.reset()
+    binding.dw_contrib(data.x, data.dy, rstd, acc)
+    d3 = acc.finalize().cpu().numpy()
+    assert np.array_equal(d1.view(np.uint32), d3.view(np.uint32))
+
+
+def test_generator_cpu_gpu_agree():
+    wl = inputs.scaled(inputs.workload_h5120(), "gen_agree", hidden=1024, lengths=[300, 211])
+    for f in (inputs.gen_x, inputs.gen_dy):
+        a = f(wl, device="cpu")
+        b = f(wl, device="cuda").cpu()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f.__name__
+    assert torch.equal(inputs.gen_w(wl).view(torch.int16),
+                       inputs.gen_w(wl, device="cuda").cpu().view(torch.int16))
