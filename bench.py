@@ -1,0 +1,249 @@
+"""Benchmark: batch-invariant RMSNorm forward + backward on one MI355X.
+
+One step = the whole hot path over one batch: rmsnorm_fwd (y, rstd), then
+rmsnorm_bwd_dx with the canonical dweight accumulator (dx and dweight
+contributions in one pass), then rmsnorm_dw_finalize (dweight), then the
+accumulator reset.  Workload: hidden 4096, 8 samples x 4096 tokens = 32768
+rows, bf16, one B=N call (the identity layout).  Inputs are resident in HBM
+before timing; buffer sets rotate so consecutive steps never reuse data.
+
+value = algorithmic HBM bytes of fwd + bwd per step / step time, in GB/s:
+  fwd = rows*(2H + 4) + rows*2H + 2H        (x, rstd, y, w)
+  bwd = rows*(4H + 4) + rows*2H + 2H + 4H   (x, dy, rstd, dx, w, dweight)
+The roofline entry is the backward kernel alone: its algorithmic bytes over
+its average duration, measured with HIP events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "RMSNorm fwd+bwd achieved HBM GB/s (% of peak) with bitwise B1/BN/chunk invariance"
+PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_traffic_rmsnorm_h4096_t32768.json")
+
+
+def algorithmic_bytes(rows_real: int, rows_phys: int, H: int):
+    fwd = rows_real * (2 * H + 4) + rows_phys * 2 * H + 2 * H
+    bwd = rows_real * (4 * H + 4) + rows_phys * 2 * H + 2 * H + 4 * H
+    return fwd, bwd
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "invariant_rmsnorm_backward_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(bwd_bytes: int):
+    """HBM bytes per backward launch from committed rocprofv3 counters, or
+    None when the kernels changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s: float = 12.0):
+    """The FP64 oracle as it stands, single thread, on the first rows of the
+    same workload until about budget_s seconds of work have been timed."""
+    import oracle
+    from invariant_rmsnorm_backward_amd import inputs
+    import numpy as np
+    chunk = 1024
+    H = wl.hidden
+    wb = inputs.bf16_bits(inputs.gen_w(wl))
+    done, spent, a = 0, 0.0, 0
+    while spent < budget_s and a < wl.n_logical:
+        rows = np.arange(a, min(a + chunk, wl.n_logical))
+        xb = inputs.bf16_bits(inputs.gen_x(wl, rows))
+        dyb = inputs.bf16_bits(inputs.gen_dy(wl, rows))
+        t0 = time.perf_counter()
+        oracle.rmsnorm_fwd_bf16(xb, wb, wl.eps)
+        oracle.rmsnorm_bwd_bf16(xb, wb, dyb, wl.eps)
+        spent += time.perf_counter() - t0
+        done += len(rows)
+        a += chunk
+    f, b = algorithmic_bytes(done, done, H)
+    return {"value": round((f + b) / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {wl.n_logical} rows of {wl.name}, fwd+bwd in FP64 "
+                      f"(single-threaded C), {spent:.1f} s timed, input generation excluded",
+            "rows_per_s": round(done / spent, 1)}
+
+
+def copy_ceiling(torch, nbytes: int, iters: int = 20) -> float:
+    """Device-to-device copy bandwidth (read + write bytes / time), GB/s."""
+    n = nbytes // 2
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=3, help="rotating input/output buffer sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows would shard across GPUs with an all-gather of block partials; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from invariant_rmsnorm_backward_amd import binding, inputs, layouts
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    binding.load()
+    torch.cuda.set_device(0)
+    wl = inputs.workload_h4096()
+    T, H = wl.n_logical, wl.hidden
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    print(f"[bench] generating {wl.name} on the GPU", file=sys.stderr, flush=True)
+    x0 = inputs.gen_x(wl, device="cuda")
+    dy0 = inputs.gen_dy(wl, device="cuda")
+    w = inputs.gen_w(wl, device="cuda")
+    sets = []
+    for _ in range(args.sets):
+        sets.append(dict(x=x0.clone(), dy=dy0.clone(), y=torch.empty_like(x0),
+                         dx=torch.empty_like(x0),
+                         rstd=torch.empty(T, dtype=torch.float32, device="cuda"),
+                         dw=torch.empty(H, dtype=torch.float32, device="cuda")))
+    del x0, dy0
+    acc = binding.DwAccumulator(T, H)
+
+    def step(s):
+        binding.rmsnorm_fwd(s["x"].data_ptr(), w.data_ptr(), s["y"].data_ptr(), s["rstd"].data_ptr(),
+                            T, H, wl.eps, None, sh)
+        binding.rmsnorm_bwd_dx(s["x"].data_ptr(), w.data_ptr(), s["dy"].data_ptr(),
+                               s["rstd"].data_ptr(), s["dx"].data_ptr(), T, H, None, acc.handle, sh)
+        binding.rmsnorm_dw_finalize(acc.handle, s["dw"].data_ptr(), sh)
+        binding.rmsnorm_dw_acc_reset(acc.handle, sh)
+
+    # Invariance check on the benchmark data: B=N vs 8 x B=1 aggregate, bitwise.
+    # The singleton calls use the dx-only and dweight-only kernel instances, so
+    # the fused backward kernel only ever runs at full size in this process.
+    s0 = sets[0]
+    step(s0)
+    ref_dw = s0["dw"].clone()
+    ref_dx = s0["dx"].clone()
+    acc8 = binding.DwAccumulator(T, H)
+    cell = layouts.singleton_aggregate(wl)
+    dx8 = torch.empty_like(s0["dx"])
+    lays = []
+    for call in cell.calls:
+        a, b = int(call.row_logical[0]), int(call.row_logical[-1]) + 1
+        lay = binding.Layout(call.row_logical, T)
+        lays.append(lay)
+        xs, dys = s0["x"][a:b], s0["dy"][a:b]
+        y8, r8 = binding.fwd(xs, w, wl.eps, lay)
+        binding.bwd(xs, w, dys, r8, lay, None, dx=dx8[a:b])
+        binding.dw_contrib(xs, dys, r8, acc8, lay)
+    dw8 = acc8.finalize()
+    torch.cuda.synchronize()
+    inv_ok = bool(torch.equal(dw8.view(torch.int32), ref_dw.view(torch.int32))
+                  and torch.equal(dx8.view(torch.int16), ref_dx.view(torch.int16)))
+    for lay in lays:
+        lay.close()
+    acc8.close()
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        s = sets[i % len(sets)]
+        e = ev[i]
+        e[0].record(stream)
+        binding.rmsnorm_fwd(s["x"].data_ptr(), w.data_ptr(), s["y"].data_ptr(), s["rstd"].data_ptr(),
+                            T, H, wl.eps, None, sh)
+        e[1].record(stream)
+        binding.rmsnorm_bwd_dx(s["x"].data_ptr(), w.data_ptr(), s["dy"].data_ptr(),
+                               s["rstd"].data_ptr(), s["dx"].data_ptr(), T, H, None, acc.handle, sh)
+        e[2].record(stream)
+        binding.rmsnorm_dw_finalize(acc.handle, s["dw"].data_ptr(), sh)
+        e[3].record(stream)
+        binding.rmsnorm_dw_acc_reset(acc.handle, sh)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    fin_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    ms_step = wall / K * 1e3
+    fb, bb = algorithmic_bytes(T, T, H)
+    value = (fb + bb) / (ms_step * 1e-3) / 1e9
+    bwd_avg = float(bwd_ms.mean())
+    achieved = bb / (bwd_avg * 1e-3) / 1e9
+    traffic = measured_traffic(bb)
+
+    copy_gbps = None if args.no_copy else copy_ceiling(torch, 1 << 30)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "hidden": H, "rows": T, "samples": "8 x 4096 tokens",
+                   "layout": "BN/full (one call)", "io_dtype": "bf16", "eps": wl.eps,
+                   "step": "fwd + bwd_dx(fused dweight contributions) + dw_finalize",
+                   "buffer_sets": args.sets},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "bwd_wide_kernel<V=8,TW=1,FULL,DX,DW>",
+                     "algorithmic_bytes_per_launch": bb, "avg_launch_ms": round(bwd_avg, 5)},
+        "cpu_baseline": cpu,
+        "phases_ms": {"fwd": round(float(np.median(fwd_ms)), 5),
+                      "bwd": round(float(np.median(bwd_ms)), 5),
+                      "finalize": round(float(np.median(fin_ms)), 5)},
+        "phases_gbps": {"fwd": round(fb / (float(np.median(fwd_ms)) * 1e-3) / 1e9, 1),
+                        "bwd": round(bb / (float(np.median(bwd_ms)) * 1e-3) / 1e9, 1)},
+        "rows_per_s": round(T / (ms_step * 1e-3), 1),
+        "frac_of_peak": round(value / PEAK_GBPS, 4),
+        "copy_ceiling_gbps": None if copy_gbps is None else round(copy_gbps, 1),
+        "frac_of_copy_ceiling": None if copy_gbps is None else round(value / copy_gbps, 4),
+        "invariance_bn_vs_8xb1_bitwise": inv_ok,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
