@@ -84,10 +84,10 @@ int rmsnorm_max_hidden(void) { return rbi::kMaxHidden; }
 const char* rmsnorm_last_error(void) { return g_err.c_str(); }
 
 const char* rmsnorm_backend_info(void) {
-  return "hip gfx950; cdo=v1 R=64 S=8 (hidden<=5120) or S=4 (hidden>5120), "
+  return "hip gfx950; cdo=v1 R=64 S=4, "
          "contribution fl32(fl32(dy*x)*rstd), streams fold ascending from +0.0, "
          "stream tree pairwise, block tree pairwise with +0.0 padding; no atomics; "
-         "fwd=wave_per_row|lanes_per_row bwd=fused dx+dW, one workgroup per 64-row block; "
+         "fwd=wave_per_row|lanes_per_row bwd=fused dx+dW, one workgroup per 64-row block, nt loads/stores; "
          "max_hidden=10240";
 }
 

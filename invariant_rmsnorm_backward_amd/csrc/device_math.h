@@ -58,6 +58,23 @@ __device__ __forceinline__ void store_f4(float* p, float a, float b, float c, fl
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
+// Streaming (non-temporal) 16-byte global accesses for data touched once:
+// the loads and stores carry the nt cache policy, so a pass over hundreds of
+// MB does not evict what other kernels keep in L2 and the Infinity Cache.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store16_stream(void* p, const uint4& v) {
+  const u32x4_t u = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(u, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_f4_stream(float* p, float a, float b, float c, float d) {
+  const u32x4_t u = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+  __builtin_nontemporal_store(u, reinterpret_cast<u32x4_t*>(p));
+}
+
 // Register "laundering": an empty asm that claims to modify the value.  Used
 // between the two passes over a row so the compiler re-derives FP32 values
 // from the packed bf16 registers instead of keeping 2x as many registers
@@ -79,11 +96,29 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+// Wavefront sum with DPP lane moves inside each 16-lane row, then the four
+// row sums combined in a fixed order from scalar reads.  Every lane returns
+// the same bits: within a row each step adds a lane's value to its partner's
+// (a+b == b+a), and the final combination is computed from uniform values.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = v + dpp_move<0xB1>(v);    // quad_perm [1,0,3,2]: pairs
+  v = v + dpp_move<0x4E>(v);    // quad_perm [2,3,0,1]: quads
+  v = v + dpp_move<0x141>(v);   // row_half_mirror: 8 lanes
+  v = v + dpp_move<0x140>(v);   // row_mirror: 16 lanes
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
 
-// The in-block stream tree of the canonical order: ((q0+q1)+(q2+q3))+((q4+q5)+(q6+q7)).
-__device__ __forceinline__ float stream_tree8(const float (&q)[8]) {
-  return ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+// The in-block stream tree of the canonical order: (q0+q1)+(q2+q3).
+__device__ __forceinline__ float stream_tree4(float q0, float q1, float q2, float q3) {
+  return (q0 + q1) + (q2 + q3);
 }
 
 }  // namespace rbi

@@ -10,11 +10,6 @@
 namespace rbi {
 
 constexpr int kMaxHidden = 10240;
-// Canonical-order parameter that depends on the hidden size: the number of
-// in-block fold streams (8 up to this width, 4 above it).
-constexpr int kEightStreamMaxHidden = 5120;
-
-inline int cdo_streams(int hidden) { return hidden <= kEightStreamMaxHidden ? 8 : 4; }
 
 // Physical->logical plan as the kernels see it (device pointers).
 struct PlanDev {

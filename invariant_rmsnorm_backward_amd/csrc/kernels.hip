@@ -2,14 +2,15 @@
 //
 // Forward: one wavefront per row (hidden >= 512, or any hidden that is not a
 // power of two below 512) or one group of hidden/8 lanes per row (hidden in
-// {8..256}); 16-byte bf16 loads, FP32 math, an xor-butterfly sum of squares.
+// {8..256}); streaming 16-byte bf16 loads and stores, FP32 math, a DPP
+// wavefront sum of squares.
 //
-// Backward: one workgroup of 8 wavefronts per canonical block of 64 logical
-// rows.  The dweight order (CDO-v1, following "WS1 C4 (#270) closeout
-// evidence": parameter gradients from logical-row FP32 contributions reduced
-// in a fixed order) is laid onto the hardware: each fold stream is a
-// wavefront (or a pair of wavefronts when hidden > 5120) that walks its
-// slots w, w+S, ... in ascending order and keeps the running FP32 sums in
+// Backward: one workgroup per canonical block of 64 logical rows.  The
+// dweight order (CDO-v1, following "WS1 C4 (#270) closeout evidence":
+// parameter gradients from logical-row FP32 contributions reduced in a fixed
+// order) is laid onto the hardware: each of the 4 fold streams is one
+// wavefront (hidden <= 1024) or a pair of wavefronts (wider rows) that walks
+// its slots w, w+4, ... in ascending order and keeps the running FP32 sums in
 // registers, so x and dy are read from HBM once for dx and dweight together.
 // The streams meet in LDS for the fixed in-block tree and the block partial
 // goes to HBM; a separate pass reduces the partials with a perfect pairwise
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void fwd_wide_kernel(FwdArgs a) {
 #pragma unroll
       for (int k = 0; k < V; ++k) {
         const int q = k * 64 + lane;
-        if (k < V - 1 || q < nchunk) store16(yr + q * 8, make_uint4(0, 0, 0, 0));
+        if (k < V - 1 || q < nchunk) store16_stream(yr + q * 8, make_uint4(0, 0, 0, 0));
       }
       if (lane == 0) a.rstd[row] = 0.0f;
       continue;
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(256) void fwd_wide_kernel(FwdArgs a) {
 #pragma unroll
     for (int k = 0; k < V; ++k) {
       const int q = k * 64 + lane;
-      xv[k] = (k < V - 1 || q < nchunk) ? load16(xr + q * 8) : make_uint4(0, 0, 0, 0);
+      xv[k] = (k < V - 1 || q < nchunk) ? load16_stream(xr + q * 8) : make_uint4(0, 0, 0, 0);
     }
     float ss = 0.0f;
 #pragma unroll
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void fwd_wide_kernel(FwdArgs a) {
         unpack8(wv[k], g);
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = (f[e] * r) * g[e];
-        store16(yr + q * 8, pack8(o));
+        store16_stream(yr + q * 8, pack8(o));
       }
     }
     if (lane == 0) a.rstd[row] = r;
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(256) void fwd_small_kernel(FwdArgs a) {
     const bool valid = row < a.rows;
     const bool pad = valid && a.row_logical != nullptr && a.row_logical[row] < 0;
     uint4 xv = make_uint4(0, 0, 0, 0);
-    if (valid && !pad) xv = load16(a.x + row * H + sub * 8);
+    if (valid && !pad) xv = load16_stream(a.x + row * H + sub * 8);
     float f[8];
     unpack8(xv, f);
     float ss = 0.0f;
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(256) void fwd_small_kernel(FwdArgs a) {
       float o[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = pad ? 0.0f : (f[e] * r) * wf[e];
-      store16(a.y + row * H + sub * 8, pack8(o));
+      store16_stream(a.y + row * H + sub * 8, pack8(o));
       if (sub == 0) a.rstd[row] = pad ? 0.0f : r;
     }
   }
@@ -122,51 +123,78 @@ __device__ __forceinline__ int slot_row(const BwdArgs& a, int item, int blk, int
   return r < a.rows ? (int)r : -1;
 }
 
-// Wide rows: V chunks of 8 columns per lane, TW wavefronts per row, S = 8/TW
-// streams; the workgroup is 8 wavefronts.  Chunk q of the row held by lane
-// `lane` of wave-half `half` at step k is q = (half*V + k)*64 + lane.  FULL
-// means hidden == 512*V*TW exactly, so no lane needs a bounds mask.
+// Wide rows: V chunks of 8 columns per lane, TW wavefronts per row, 4
+// streams; the workgroup is 4*TW wavefronts.  Chunk q of the row held by
+// lane `lane` of wave-part `half` at step k is q = (half*V + k)*64 + lane.
+// FULL means hidden == 512*V*TW exactly, so no lane needs a bounds mask.
 template <int V, int TW, bool FULL>
 struct WideShape {
-  static constexpr int S = 8 / TW;                 // fold streams
-  static constexpr int SLOTS = kBlockRows / S;     // slots per stream
+  static constexpr int S = kStreams;               // fold streams
+  static constexpr int SLOTS = kSlotsPerStream;    // slots per stream
+  static constexpr int WAVES = S * TW;             // wavefronts per workgroup
+  static constexpr int THREADS = 64 * WAVES;
   static constexpr int COLS = 512 * V * TW;        // columns the workgroup covers
   static constexpr int NTILE = (V * TW + 1) / 2;   // 1024-column tiles of the stream tree
 };
 
 // One canonical block: the stream's slots in ascending order.  COMPLETE: the
 // call holds every present row of the block, so the contributions are folded
-// in registers; otherwise they are written to the spill rows.
+// in registers; otherwise they are written to the spill rows.  When two row
+// buffers fit in registers the loop is software-pipelined: the next slot's
+// row is loaded before the current row's reduction and dx pass.
 template <int V, int TW, bool FULL, bool DX, bool DW, bool COMPLETE>
-__device__ __forceinline__ void bwd_wide_block(const BwdArgs& a, int item, int blk,
-                                               const float* w_s, float* dot_s,
-                                               float (&acc)[DW ? V * 8 : 1]) {
+struct WideBlock {
   using Sh = WideShape<V, TW, FULL>;
-  const int tid = threadIdx.x;
-  const int wv = tid >> 6;
-  const int lane = tid & 63;
-  const int stream = wv / TW;
-  const int half = wv % TW;
-  const int H = FULL ? Sh::COLS : a.hidden;
-  const int nchunk = H >> 3;
-  const int base = half * V * 512 + lane * 8;      // this lane's first column
-  auto in_row = [&](int k) { return FULL || (half * V + k) * 64 + lane < nchunk; };
+  const BwdArgs& a;
+  int item, blk, stream, half, lane, wv, H, nchunk, base;
+  const float* w_s;
+  float* dot_s;
+  float (&acc)[DW ? V * 8 : 1];
+  // Lane j (< SLOTS) holds the physical row of this stream's slot j and its
+  // rstd, loaded once per block; the row loop reads them as scalars, so the
+  // only vector loads in the loop are the row data (in-order waits stay
+  // precise and the next row's loads stay in flight).
+  int slot_p = -1;
+  float slot_r = 0.0f;
 
-  for (int i = 0; i < Sh::SLOTS; ++i) {
+  __device__ __forceinline__ void load_slots() {
+    if (lane < Sh::SLOTS) {
+      slot_p = slot_row(a, item, blk, stream + Sh::S * lane);
+      if (slot_p >= 0) slot_r = a.rstd[slot_p];
+    }
+    // Consume both registers here, before the row loop: the compiler then
+    // waits for these loads once, instead of inserting a full vmcnt(0) wait
+    // inside the loop (which would also wait for the prefetched row).
+    asm volatile("" : "+v"(slot_p), "+v"(slot_r));
+  }
+  __device__ __forceinline__ int row_of(int i) const { return __builtin_amdgcn_readlane(slot_p, i); }
+  __device__ __forceinline__ float rstd_of(int i) const {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(slot_r), i));
+  }
+
+  __device__ __forceinline__ bool in_row(int k) const {
+    return FULL || (half * V + k) * 64 + lane < nchunk;
+  }
+
+  // The loads are issued whether or not the slot is present (an absent slot
+  // reads row 0 and its data is never used): with the same number of memory
+  // operations on every path, the compiler's wait counts stay exact and the
+  // next row's loads remain in flight while the current row is processed.
+  __device__ __forceinline__ void load(int p, uint4 (&xv)[V], uint4 (&dv)[V]) const {
+    const int row = p >= 0 ? p : 0;
+    const uint16_t* xr = a.x + (int64_t)row * H + base;
+    const uint16_t* dr = a.dy + (int64_t)row * H + base;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      xv[k] = in_row(k) ? load16_stream(xr + k * 512) : make_uint4(0, 0, 0, 0);
+      dv[k] = in_row(k) ? load16_stream(dr + k * 512) : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void process(int i, int p, uint4 (&xv)[V], uint4 (&dv)[V], float r) {
     const int s = stream + Sh::S * i;
-    const int p = slot_row(a, item, blk, s);   // uniform over the wavefront
-    uint4 xv[V], dv[V];
-    float r = 0.0f;
     float dot = 0.0f;
     if (p >= 0) {
-      const uint16_t* xr = a.x + (int64_t)p * H + base;
-      const uint16_t* dr = a.dy + (int64_t)p * H + base;
-#pragma unroll
-      for (int k = 0; k < V; ++k) {
-        xv[k] = in_row(k) ? load16(xr + k * 512) : make_uint4(0, 0, 0, 0);
-        dv[k] = in_row(k) ? load16(dr + k * 512) : make_uint4(0, 0, 0, 0);
-      }
-      r = a.rstd[p];
       float* srow = COMPLETE ? nullptr : a.S + ((int64_t)blk * kBlockRows + s) * H + base;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
@@ -182,18 +210,20 @@ __device__ __forceinline__ void bwd_wide_block(const BwdArgs& a, int item, int b
           if (DW && COMPLETE) acc[k * 8 + e] = acc[k * 8 + e] + c[e];
         }
         if (DW && !COMPLETE && in_row(k)) {
-          store_f4(srow + k * 512, c[0], c[1], c[2], c[3]);
-          store_f4(srow + k * 512 + 4, c[4], c[5], c[6], c[7]);
+          store_f4_stream(srow + k * 512, c[0], c[1], c[2], c[3]);
+          store_f4_stream(srow + k * 512 + 4, c[4], c[5], c[6], c[7]);
         }
       }
       if (DX && TW == 1) dot = wave_sum(dot);
     }
     if (DX) {
       if (TW > 1) {
+        // the row's wavefronts exchange their partial dots through LDS
         dot = wave_sum(dot);
-        if (lane == 0) dot_s[(i & 1) * 8 + wv] = dot;
+        if (lane == 0) dot_s[(i & 1) * 16 + wv] = dot;
         __syncthreads();
-        dot = dot_s[(i & 1) * 8 + stream * TW] + dot_s[(i & 1) * 8 + stream * TW + 1];
+        const float* d = &dot_s[(i & 1) * 16 + stream * TW];
+        dot = TW == 2 ? d[0] + d[1] : (d[0] + d[1]) + (d[2 % TW] + d[3 % TW]);
       }
       if (p >= 0) {
         const float kk = ((r * r) * r) * (dot / (float)H);
@@ -215,24 +245,57 @@ __device__ __forceinline__ void bwd_wide_block(const BwdArgs& a, int item, int b
               const float g = df[e] * w_s[base + k * 512 + e];
               o[e] = fmaf(-xf[e], kk, r * g);
             }
-            store16(xo + k * 512, pack8(o));
+            store16_stream(xo + k * 512, pack8(o));
           }
         }
       }
     }
   }
-}
+
+  // Two row buffers fit in the register file only up to 8 chunks per lane
+  // without masks; wider or masked rows are processed one at a time.
+  static constexpr bool PIPE = FULL && V <= 8;
+
+  __device__ __forceinline__ void run() {
+    load_slots();
+    if constexpr (PIPE) run_pipelined();
+    else run_sequential();
+  }
+
+  __device__ __forceinline__ void run_sequential() {
+    for (int i = 0; i < Sh::SLOTS; ++i) {
+      uint4 xv[V], dv[V];
+      const int p = row_of(i);
+      load(p, xv, dv);
+      process(i, p, xv, dv, rstd_of(i));
+    }
+  }
+
+  __device__ __forceinline__ void run_pipelined() {
+    static_assert(Sh::SLOTS % 2 == 0, "slots per stream must be even");
+    uint4 xa[V], da[V], xb[V], db[V];
+    int pa = row_of(0);
+    load(pa, xa, da);
+    for (int i = 0; i < Sh::SLOTS; i += 2) {
+      const int pb = row_of(i + 1);
+      load(pb, xb, db);
+      process(i, pa, xa, da, rstd_of(i));
+      pa = (i + 2 < Sh::SLOTS) ? row_of(i + 2) : -1;
+      load(pa, xa, da);
+      process(i + 1, pb, xb, db, rstd_of(i + 1));
+    }
+  }
+};
 
 template <int V, int TW, bool FULL, bool DX, bool DW>
-__global__ __launch_bounds__(512) void bwd_wide_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
   using Sh = WideShape<V, TW, FULL>;
-  constexpr int S = Sh::S;
   __shared__ float w_s[DX ? Sh::COLS : 1];
-  __shared__ float tile_s[DW ? S * 1024 : 1];
-  __shared__ float dot_s[(DX && TW > 1) ? 2 * 8 : 1];
+  __shared__ float tile_s[DW ? kStreams * 1024 : 1];
+  __shared__ float dot_s[(DX && TW > 1) ? 2 * 16 : 1];
 
   const int tid = threadIdx.x;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
   const int lane = tid & 63;
   const int stream = wv / TW;
   const int half = wv % TW;
@@ -243,10 +306,10 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(BwdArgs a) {
   if (item >= a.plan.n_items) {
     // padding rows: dx = 0, nothing read (one row per wavefront)
     if (DX) {
-      const int idx = (item - a.plan.n_items) * 8 + wv;
+      const int idx = (item - a.plan.n_items) * Sh::WAVES + wv;
       if (idx < a.plan.n_pad) {
         uint16_t* d = a.dx + (int64_t)a.plan.pad_rows[idx] * H;
-        for (int q = lane; q < nchunk; q += 64) store16(d + q * 8, make_uint4(0, 0, 0, 0));
+        for (int q = lane; q < nchunk; q += 64) store16_stream(d + q * 8, make_uint4(0, 0, 0, 0));
       }
     }
     return;
@@ -254,7 +317,7 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(BwdArgs a) {
 
   if (DX) {
     // w as FP32 in LDS; columns past hidden hold 0 so masked lanes read zeros
-    for (int q = tid; q < Sh::COLS / 8; q += 512) {
+    for (int q = tid; q < Sh::COLS / 8; q += Sh::THREADS) {
       float f[8];
       unpack8(q < nchunk ? load16(a.w + q * 8) : make_uint4(0, 0, 0, 0), f);
       store_f4(&w_s[q * 8], f[0], f[1], f[2], f[3]);
@@ -278,10 +341,13 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < (DW ? V * 8 : 1); ++i) acc[i] = 0.0f;
 
+  const int base = half * V * 512 + lane * 8;      // this lane's first column
   if (!DW || complete) {
-    bwd_wide_block<V, TW, FULL, DX, DW, true>(a, item, blk, w_s, dot_s, acc);
+    WideBlock<V, TW, FULL, DX, DW, true>{a, item, blk, stream, half, lane, wv, H, nchunk, base,
+                                         w_s, dot_s, acc}.run();
   } else {
-    bwd_wide_block<V, TW, FULL, DX, DW, false>(a, item, blk, w_s, dot_s, acc);
+    WideBlock<V, TW, FULL, DX, DW, false>{a, item, blk, stream, half, lane, wv, H, nchunk, base,
+                                          w_s, dot_s, acc}.run();
     return;
   }
 
@@ -302,36 +368,24 @@ __global__ __launch_bounds__(512) void bwd_wide_kernel(BwdArgs a) {
         }
       }
       __syncthreads();
-      for (int c = tid; c < 1024; c += 512) {
+      for (int c = tid; c < 1024; c += Sh::THREADS) {
         const int col = t * 1024 + c;
-        if (col < H) {
-          float v;
-          if (S == 8) {
-            float q[8];
-#pragma unroll
-            for (int w = 0; w < 8; ++w) q[w] = tile_s[(w % S) * 1024 + c];
-            v = stream_tree8(q);
-          } else {
-            const float q0 = tile_s[0 * 1024 + c], q1 = tile_s[1 * 1024 + c];
-            const float q2 = tile_s[(2 % S) * 1024 + c], q3 = tile_s[(3 % S) * 1024 + c];
-            v = (q0 + q1) + (q2 + q3);
-          }
-          Pb[col] = v;
-        }
+        if (col < H)
+          Pb[col] = stream_tree4(tile_s[c], tile_s[1024 + c], tile_s[2048 + c], tile_s[3072 + c]);
       }
     }
   }
 }
 
 // Small rows: hidden = 8L (L in 1..32), one group of L lanes per row; the
-// 64 slots' contributions go through LDS and 8 streams fold them there.
+// 64 slots' contributions go through LDS and the 4 streams fold them there.
 template <int L, bool DX, bool DW>
 __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
   constexpr int H = 8 * L;
   constexpr int GROUPS = 256 / L;
   constexpr int ITERS = (kBlockRows + GROUPS - 1) / GROUPS;
   __shared__ float c_s[DW ? kBlockRows * H : 1];
-  __shared__ float q_s[DW ? 8 * H : 1];
+  __shared__ float q_s[DW ? kStreams * H : 1];
   const int tid = threadIdx.x;
   const int g = tid / L;
   const int sub = tid % L;
@@ -341,7 +395,7 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
     if (DX) {
       const int idx = (item - a.plan.n_items) * GROUPS + g;
       if (idx < a.plan.n_pad)
-        store16(a.dx + (int64_t)a.plan.pad_rows[idx] * H + sub * 8, make_uint4(0, 0, 0, 0));
+        store16_stream(a.dx + (int64_t)a.plan.pad_rows[idx] * H + sub * 8, make_uint4(0, 0, 0, 0));
     }
     return;
   }
@@ -365,8 +419,8 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
     uint4 xv = make_uint4(0, 0, 0, 0), dv = make_uint4(0, 0, 0, 0);
     float r = 0.0f;
     if (p >= 0) {
-      xv = load16(a.x + (int64_t)p * H + sub * 8);
-      dv = load16(a.dy + (int64_t)p * H + sub * 8);
+      xv = load16_stream(a.x + (int64_t)p * H + sub * 8);
+      dv = load16_stream(a.dy + (int64_t)p * H + sub * 8);
       r = a.rstd[p];
     }
     float xf[8], df[8], pr[8];
@@ -384,7 +438,7 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = fmaf(-xf[e], kk, r * (df[e] * wf[e]));
-        store16(a.dx + (int64_t)p * H + sub * 8, pack8(o));
+        store16_stream(a.dx + (int64_t)p * H + sub * 8, pack8(o));
       }
     }
     if (DW) {
@@ -398,27 +452,23 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
         }
       } else if (p >= 0) {
         float* srow = a.S + ((int64_t)blk * kBlockRows + s) * H + sub * 8;
-        store_f4(srow, c[0], c[1], c[2], c[3]);
-        store_f4(srow + 4, c[4], c[5], c[6], c[7]);
+        store_f4_stream(srow, c[0], c[1], c[2], c[3]);
+        store_f4_stream(srow + 4, c[4], c[5], c[6], c[7]);
       }
     }
   }
   if (DW && complete) {
     __syncthreads();
-    for (int idx = tid; idx < 8 * H; idx += 256) {
+    for (int idx = tid; idx < kStreams * H; idx += 256) {
       const int w = idx / H, j = idx % H;
       float q = 0.0f;
 #pragma unroll
-      for (int i = 0; i < kSlotsPerStream; ++i) q = q + c_s[(w + 8 * i) * H + j];
+      for (int i = 0; i < kSlotsPerStream; ++i) q = q + c_s[(w + kStreams * i) * H + j];
       q_s[w * H + j] = q;
     }
     __syncthreads();
-    for (int j = tid; j < H; j += 256) {
-      float q[8];
-#pragma unroll
-      for (int w = 0; w < 8; ++w) q[w] = q_s[w * H + j];
-      a.P[(int64_t)blk * H + j] = stream_tree8(q);
-    }
+    for (int j = tid; j < H; j += 256)
+      a.P[(int64_t)blk * H + j] = stream_tree4(q_s[j], q_s[H + j], q_s[2 * H + j], q_s[3 * H + j]);
   }
 }
 
@@ -428,23 +478,21 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
 __global__ __launch_bounds__(256) void rebuild_kernel(const float* __restrict__ S,
                                                       float* __restrict__ P,
                                                       const int32_t* __restrict__ blocks,
-                                                      int64_t T, int H, int streams) {
+                                                      int64_t T, int H) {
   const int b = blocks[blockIdx.x];
   const int j = blockIdx.y * 256 + threadIdx.x;
   if (j >= H) return;
-  float q[8];
+  float q[kStreams];
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
+  for (int w = 0; w < kStreams; ++w) {
     float acc = 0.0f;
-    if (w < streams) {
-      for (int s = w; s < kBlockRows; s += streams) {
-        const int64_t l = (int64_t)b * kBlockRows + s;
-        if (l < T) acc = acc + S[l * H + j];
-      }
+    for (int s = w; s < kBlockRows; s += kStreams) {
+      const int64_t l = (int64_t)b * kBlockRows + s;
+      if (l < T) acc = acc + S[l * H + j];
     }
     q[w] = acc;
   }
-  P[(int64_t)b * H + j] = streams == 8 ? stream_tree8(q) : (q[0] + q[1]) + (q[2] + q[3]);
+  P[(int64_t)b * H + j] = stream_tree4(q[0], q[1], q[2], q[3]);
 }
 
 // One level group of the cross-block tree: out[g] = perfect pairwise tree over
@@ -490,7 +538,8 @@ bool hidden_supported(int hidden) {
   return hidden > 0 && hidden % 8 == 0 && hidden <= kMaxHidden;
 }
 
-static int wide_tw(int hidden) { return hidden <= kEightStreamMaxHidden ? 1 : 2; }
+// Wavefronts per row: one up to 1024 columns, two above.
+static int wide_tw(int hidden) { return hidden <= 1024 ? 1 : 2; }
 static int wide_v(int hidden) {
   const int per = 512 * wide_tw(hidden);
   return (hidden + per - 1) / per;
@@ -500,8 +549,8 @@ const char* fwd_variant(int hidden) {
   return small_lanes(hidden) ? "fwd_small(lanes_per_row=hidden/8)" : "fwd_wide(wave_per_row)";
 }
 const char* bwd_variant(int hidden) {
-  if (small_lanes(hidden)) return "bwd_small(lds_fold, streams=8)";
-  return wide_tw(hidden) == 1 ? "bwd_wide(wave_per_row, streams=8)"
+  if (small_lanes(hidden)) return "bwd_small(lds_fold, streams=4)";
+  return wide_tw(hidden) == 1 ? "bwd_wide(wave_per_row, streams=4)"
                               : "bwd_wide(two_waves_per_row, streams=4)";
 }
 
@@ -546,8 +595,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
 
 template <int V, int TW, bool FULL>
 static void bwd_wide_go2(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
-  const int pad_groups = dx ? (a.plan.n_pad + 7) / 8 : 0;
-  const dim3 grid((unsigned)(a.plan.n_items + pad_groups)), block(512);
+  using Sh = WideShape<V, TW, FULL>;
+  const int pad_groups = dx ? (a.plan.n_pad + Sh::WAVES - 1) / Sh::WAVES : 0;
+  const dim3 grid((unsigned)(a.plan.n_items + pad_groups)), block(Sh::THREADS);
   if (dx && dw) bwd_wide_kernel<V, TW, FULL, true, true><<<grid, block, 0, st>>>(a);
   else if (dx) bwd_wide_kernel<V, TW, FULL, true, false><<<grid, block, 0, st>>>(a);
   else bwd_wide_kernel<V, TW, FULL, false, true><<<grid, block, 0, st>>>(a);
@@ -582,16 +632,15 @@ hipError_t launch_bwd(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
   const int tw = wide_tw(a.hidden), V = wide_v(a.hidden);
   if (tw == 1) {
     switch (V) {
-#define RBI_BWD1(v) case v: bwd_wide_go<v, 1>(a, dx, dw, st); break;
-      RBI_BWD1(1) RBI_BWD1(2) RBI_BWD1(3) RBI_BWD1(4) RBI_BWD1(5)
-      RBI_BWD1(6) RBI_BWD1(7) RBI_BWD1(8) RBI_BWD1(9) RBI_BWD1(10)
-#undef RBI_BWD1
+      case 1: bwd_wide_go<1, 1>(a, dx, dw, st); break;
+      case 2: bwd_wide_go<2, 1>(a, dx, dw, st); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (V) {
 #define RBI_BWD2(v) case v: bwd_wide_go<v, 2>(a, dx, dw, st); break;
-      RBI_BWD2(6) RBI_BWD2(7) RBI_BWD2(8) RBI_BWD2(9) RBI_BWD2(10)
+      RBI_BWD2(2) RBI_BWD2(3) RBI_BWD2(4) RBI_BWD2(5) RBI_BWD2(6)
+      RBI_BWD2(7) RBI_BWD2(8) RBI_BWD2(9) RBI_BWD2(10)
 #undef RBI_BWD2
       default: return hipErrorInvalidValue;
     }
@@ -603,8 +652,7 @@ hipError_t launch_rebuild(const float* S, float* P, const int32_t* blocks, int32
                           int64_t n_logical, int32_t hidden, hipStream_t st) {
   if (n_blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)n_blocks, (unsigned)((hidden + 255) / 256));
-  rebuild_kernel<<<grid, dim3(256), 0, st>>>(S, P, blocks, n_logical, hidden,
-                                              cdo_streams(hidden));
+  rebuild_kernel<<<grid, dim3(256), 0, st>>>(S, P, blocks, n_logical, hidden);
   return hipGetLastError();
 }
 

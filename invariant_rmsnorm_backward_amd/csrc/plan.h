@@ -19,7 +19,7 @@
 namespace rbi {
 
 constexpr int kBlockRows = 64;   // logical rows per canonical block
-constexpr int kStreams = 8;      // in-block fold streams
+constexpr int kStreams = 4;      // in-block fold streams
 constexpr int kSlotsPerStream = kBlockRows / kStreams;
 
 enum Status : int {

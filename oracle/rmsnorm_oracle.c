@@ -164,20 +164,16 @@ int oracle_rmsnorm_bwd(const double* x, const double* w, const double* dy, int64
  *   c[l][j] = fl32(fl32(dy * x) * rstd)    one value per logical row; dy*x
  *       of two bf16 values is exact in FP32, so c is dy*x*rstd rounded once
  *   block b holds logical rows 64b .. 64b+63; slot s = l - 64b
- *   S = 8 fold streams when H <= 5120, S = 4 when H > 5120 (a function of
- *       the row width only)
- *   stream w (0..S-1) folds slots w, w+S, w+2S, ... in ascending order,
+ *   stream w (0..3) folds slots w, w+4, w+8, ..., w+60 in ascending order,
  *       starting from +0.0; a slot the accumulation does not hold adds +0.0
- *   P[b] = ((q0+q1)+(q2+q3)) + ((q4+q5)+(q6+q7))   (S = 8)
- *   P[b] = (q0+q1)+(q2+q3)                         (S = 4)
+ *   P[b] = (q0+q1)+(q2+q3)
  *   dweight = perfect pairwise tree over P[0 .. 2^ceil(log2 nb)),
  *       leaves past nb being +0.0.
  * This emulation exists so the GPU result can be compared bit for bit.
  * ---------------------------------------------------------------------- */
 
 #define CDO_BLOCK 64
-
-static int cdo_streams(int64_t H) { return H <= 5120 ? 8 : 4; }
+#define CDO_STREAMS 4
 
 /* Pairwise tree over leaves[lo .. lo+n), n a power of two, leaves at or past
  * nb counting as +0.0. */
@@ -208,13 +204,12 @@ int oracle_cdo_v1_dweight_f32(const uint16_t* x, const uint16_t* dy, const float
         free(inv);
         return ORACLE_EINVAL;
     }
-    const int S = cdo_streams(H);
     for (int64_t j = 0; j < H; ++j) {
         for (int64_t b = 0; b < nb; ++b) {
-            float q[8];
-            for (int w = 0; w < S; ++w) {
+            float q[CDO_STREAMS];
+            for (int w = 0; w < CDO_STREAMS; ++w) {
                 float acc = 0.0f;
-                for (int s = w; s < CDO_BLOCK; s += S) {
+                for (int s = w; s < CDO_BLOCK; s += CDO_STREAMS) {
                     int64_t l = b * CDO_BLOCK + s;
                     if (l >= n_logical || inv[l] < 0) continue;
                     int64_t p = inv[l];
@@ -226,10 +221,7 @@ int oracle_cdo_v1_dweight_f32(const uint16_t* x, const uint16_t* dy, const float
                 }
                 q[w] = acc;
             }
-            if (S == 8)
-                P[b] = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
-            else
-                P[b] = (q[0] + q[1]) + (q[2] + q[3]);
+            P[b] = (q[0] + q[1]) + (q[2] + q[3]);
         }
         dweight[j] = nb > 0 ? cdo_tree(P, nb, 0, npad) : 0.0f;
     }

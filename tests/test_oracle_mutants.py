@@ -26,18 +26,17 @@ MUTANTS = {
     "pad_rows_read_in_fwd": ("        if (is_pad(row_logical, p)) {\n            for (int64_t j = 0; j < H; ++j) yr[j] = 0.0;",
                              "        if (0) {\n            for (int64_t j = 0; j < H; ++j) yr[j] = 0.0;"),
     "duplicates_accepted": ("        if (inv[l] != -1) return ORACLE_ELAYOUT;\n", ""),
-    "cdo_contiguous_streams": ("for (int s = w; s < CDO_BLOCK; s += S)",
-                               "for (int s = w * (CDO_BLOCK / S); s < (w + 1) * (CDO_BLOCK / S); ++s)"),
-    "cdo_descending_fold": ("for (int s = w; s < CDO_BLOCK; s += S)",
-                            "for (int s = w + CDO_BLOCK - S; s >= 0; s -= S)"),
-    "cdo_sequential_stream_tree": ("P[b] = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));",
-                                   "P[b] = ((((((q[0] + q[1]) + q[2]) + q[3]) + q[4]) + q[5]) + q[6]) + q[7];"),
+    "cdo_contiguous_streams": ("for (int s = w; s < CDO_BLOCK; s += CDO_STREAMS)",
+                               "for (int s = w * 16; s < w * 16 + 16; ++s)"),
+    "cdo_descending_fold": ("for (int s = w; s < CDO_BLOCK; s += CDO_STREAMS)",
+                            "for (int s = w + CDO_BLOCK - CDO_STREAMS; s >= 0; s -= CDO_STREAMS)"),
+    "cdo_sequential_stream_tree": ("P[b] = (q[0] + q[1]) + (q[2] + q[3]);",
+                                   "P[b] = ((q[0] + q[1]) + q[2]) + q[3];"),
     "cdo_left_fold_over_blocks": ("dweight[j] = nb > 0 ? cdo_tree(P, nb, 0, npad) : 0.0f;",
                                   "{ float a = 0.0f; for (int64_t b = 0; b < nb; ++b) a = a + P[b]; dweight[j] = a; }"),
     "cdo_contribution_fused": ("float c = prod * rstd[p];\n                    acc = acc + c;",
                                "acc = fmaf(prod, rstd[p], acc);"),
-    "cdo_streams_always_8": ("static int cdo_streams(int64_t H) { return H <= 5120 ? 8 : 4; }",
-                             "static int cdo_streams(int64_t H) { (void)H; return 8; }"),
+    "cdo_eight_streams": ("#define CDO_STREAMS 4", "#define CDO_STREAMS 8"),
     "cdo_contribution_x_rstd_first": ("float c = prod * rstd[p];", "float c = dyv * (xv * rstd[p]);"),
 }
 
