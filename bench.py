@@ -11,7 +11,10 @@ value = algorithmic HBM bytes of fwd + bwd per step / step time, in GB/s:
   fwd = rows*(2H + 4) + rows*2H + 2H        (x, rstd, y, w)
   bwd = rows*(4H + 4) + rows*2H + 2H + 4H   (x, dy, rstd, dx, w, dweight)
 The roofline entry is the backward kernel alone: its algorithmic bytes over
-its average duration, measured with HIP events on the stream it runs on.
+its average duration, measured with HIP events around K back-to-back
+launches on the stream it runs on; `traffic` is the HBM bytes per launch
+from rocprofv3 FETCH_SIZE/WRITE_SIZE (calibrated on a 1 GiB copy) when the
+committed counters were taken on the current kernel sources, else null.
 """
 from __future__ import annotations
 
@@ -204,13 +207,27 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # The backward kernel alone, back to back on the same stream (the
+    # accumulator reset between launches is host bookkeeping and enqueues
+    # nothing), for the roofline entry.
+    eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eb0.record(stream)
+    for i in range(K):
+        s = sets[i % len(sets)]
+        binding.rmsnorm_bwd_dx(s["x"].data_ptr(), w.data_ptr(), s["dy"].data_ptr(),
+                               s["rstd"].data_ptr(), s["dx"].data_ptr(), T, H, None, acc.handle, sh)
+        binding.rmsnorm_dw_acc_reset(acc.handle, sh)
+    eb1.record(stream)
+    torch.cuda.synchronize()
+    bwd_only_ms = eb0.elapsed_time(eb1) / K
+
     fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     fin_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
     ms_step = wall / K * 1e3
     fb, bb = algorithmic_bytes(T, T, H)
     value = (fb + bb) / (ms_step * 1e-3) / 1e9
-    bwd_avg = float(bwd_ms.mean())
+    bwd_avg = bwd_only_ms
     achieved = bb / (bwd_avg * 1e-3) / 1e9
     traffic = measured_traffic(bb)
 
