@@ -495,25 +495,36 @@ __global__ __launch_bounds__(256) void rebuild_kernel(const float* __restrict__ 
   P[(int64_t)b * H + j] = stream_tree4(q[0], q[1], q[2], q[3]);
 }
 
-// One level group of the cross-block tree: out[g] = perfect pairwise tree over
-// in[g*G .. g*G+G) with +0.0 past n_in.
-template <int G>
-__global__ __launch_bounds__(256) void tree_kernel(const float* __restrict__ in, int64_t n_in,
+// One level of the cross-block tree: out[g] = perfect pairwise tree over the
+// 512 leaves in[g*512 .. g*512+512), +0.0 past n_in.  A workgroup of 8
+// wavefronts covers 64 columns (one per lane): wavefront w reduces the
+// aligned 64-leaf subtree w in registers, and the 8 subtree roots meet in
+// LDS in the same pairwise shape, so the result is the 512-leaf perfect tree.
+constexpr int kTreeLeaves = 512;
+__global__ __launch_bounds__(512) void tree_kernel(const float* __restrict__ in, int64_t n_in,
                                                    float* __restrict__ out, int H) {
-  const int j = blockIdx.y * 256 + threadIdx.x;
+  __shared__ float root_s[8][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = blockIdx.y * 64 + lane;
   const int64_t g = blockIdx.x;
-  if (j >= H) return;
-  float v[G];
+  float v[64];
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
-    const int64_t idx = g * G + i;
-    v[i] = idx < n_in ? in[idx * H + j] : 0.0f;
+  for (int i = 0; i < 64; ++i) {
+    const int64_t idx = g * kTreeLeaves + wv * 64 + i;
+    v[i] = (idx < n_in && j < H) ? in[idx * H + j] : 0.0f;
   }
 #pragma unroll
-  for (int st = 1; st < G; st *= 2)
+  for (int st = 1; st < 64; st *= 2)
 #pragma unroll
-    for (int i = 0; i < G; i += 2 * st) v[i] = v[i] + v[i + st];
-  out[g * H + j] = v[0];
+    for (int i = 0; i < 64; i += 2 * st) v[i] = v[i] + v[i + st];
+  root_s[wv][lane] = v[0];
+  __syncthreads();
+  if (wv == 0 && j < H) {
+    const float r01 = root_s[0][lane] + root_s[1][lane], r23 = root_s[2][lane] + root_s[3][lane];
+    const float r45 = root_s[4][lane] + root_s[5][lane], r67 = root_s[6][lane] + root_s[7][lane];
+    out[g * H + j] = (r01 + r23) + (r45 + r67);
+  }
 }
 
 __global__ void fill_zero_kernel(float* p, int n) {
@@ -656,31 +667,29 @@ hipError_t launch_rebuild(const float* S, float* P, const int32_t* blocks, int32
   return hipGetLastError();
 }
 
-constexpr int kTreeGroup = 32;
-
 int64_t tree_scratch_rows(int64_t nb) {
-  const int64_t a = (nb + kTreeGroup - 1) / kTreeGroup;
-  const int64_t b = (a + kTreeGroup - 1) / kTreeGroup;
+  const int64_t a = (nb + kTreeLeaves - 1) / kTreeLeaves;
+  const int64_t b = (a + kTreeLeaves - 1) / kTreeLeaves;
   return a + b;
 }
 
 hipError_t launch_tree(const float* P, int64_t nb, float* tmp, float* dweight, int32_t hidden,
                        hipStream_t st) {
-  const unsigned gx = (unsigned)((hidden + 255) / 256);
+  const unsigned gy = (unsigned)((hidden + 63) / 64);
   if (nb == 0) {
     fill_zero_kernel<<<dim3((unsigned)((hidden + 255) / 256)), dim3(256), 0, st>>>(dweight, hidden);
     return hipGetLastError();
   }
   // ping-pong between two scratch regions sized for the first two levels
-  const int64_t rows_a = (nb + kTreeGroup - 1) / kTreeGroup;
+  const int64_t rows_a = (nb + kTreeLeaves - 1) / kTreeLeaves;
   float* buf[2] = {tmp, tmp + rows_a * hidden};
   const float* in = P;
   int64_t n = nb;
   int which = 0;
   while (true) {
-    const int64_t groups = (n + kTreeGroup - 1) / kTreeGroup;
+    const int64_t groups = (n + kTreeLeaves - 1) / kTreeLeaves;
     float* out = groups == 1 ? dweight : buf[which];
-    tree_kernel<kTreeGroup><<<dim3((unsigned)groups, gx), dim3(256), 0, st>>>(in, n, out, hidden);
+    tree_kernel<<<dim3((unsigned)groups, gy), dim3(512), 0, st>>>(in, n, out, hidden);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (groups == 1) break;

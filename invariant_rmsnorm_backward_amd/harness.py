@@ -224,9 +224,14 @@ def assert_gradient_batch_invariant(op, configs: Sequence[Cell], contract: Toler
             for t, got in results[c.name].items():
                 want = ref[t]
                 same = contract.invariance_passes(_bits(got), _bits(want))
-                mism = int(np.sum(_bits(got) != _bits(want))) if got.shape == want.shape else -1
-                v = TensorVerdict(op_name, t, "gradient_invariance", c.name, same, same, mism,
-                                  **_drift(got, want, _float_view(got)))
+                if same:   # bitwise equal: every drift statistic is exactly 0
+                    mism, drift = 0, dict(max_abs=0.0, max_rel=0.0, mean_abs=0.0, p99_abs=0.0)
+                else:
+                    mism = int(np.sum(_bits(got) != _bits(want))) if got.shape == want.shape else -1
+                    drift = _drift(got, want, _float_view(got)) if got.shape == want.shape else \
+                        dict(max_abs=float("inf"), max_rel=float("inf"), mean_abs=float("inf"),
+                             p99_abs=float("inf"))
+                v = TensorVerdict(op_name, t, "gradient_invariance", c.name, same, same, mism, **drift)
                 cr.verdicts.append(v)
                 inv.append(v)
                 note(v)

@@ -1,0 +1,148 @@
+"""Full-size workloads in the launch configuration bench.py times.
+
+Every workload runs through the C-ABI on its real shape: bitwise invariance
+across its layouts (B=N, N x B=1 aggregate, chunked prefill in both
+readings, packed with padding/permutation/mask), dweight against the FP64
+oracle over all rows (accumulated in row chunks from CPU-generated inputs),
+and dx / y / rstd against the oracle on sampled rows (row-local, so each
+sampled row is computed alone)."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from invariant_rmsnorm_backward_amd import adapters, binding, contract, harness, inputs, layouts
+from tests import parity_utils as pu
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+CONTRACT = contract.load_contract()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the gpu tests need an MI355X"
+    binding.load()
+
+
+def _log(msg):
+    print(f"[fullsize {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def _oracle_dweight(wl, chunk=8192):
+    """FP64 oracle dweight over all logical rows, accumulated per row chunk."""
+    wb = inputs.bf16_bits(inputs.gen_w(wl))
+    acc = np.zeros(wl.hidden, dtype=np.float64)
+    T = wl.n_logical
+    n_act = inputs.n_active(wl)
+    for a in range(0, T, chunk):
+        rows = np.arange(a, min(a + chunk, T))
+        xb = inputs.bf16_bits(inputs.gen_x(wl, rows))
+        dyb = inputs.bf16_bits(inputs.gen_dy(wl, rows, denominator=n_act))
+        _, dw, _ = oracle.rmsnorm_bwd_bf16(xb, wb, dyb, wl.eps)
+        acc += dw
+        if (a // chunk) % 8 == 0:
+            _log(f"{wl.name}: oracle rows {a + len(rows)}/{T}")
+    return acc
+
+
+def _sample_rows(T, n=200, seed=7):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    pick |= {0, 63, 64, T - 1, T // 2}
+    return np.array(sorted(r for r in pick if 0 <= r < T))
+
+
+def _check_sampled_rows(wl, out, rows):
+    """dx, y, rstd of the sampled logical rows against the oracle."""
+    n_act = inputs.n_active(wl)
+    xb = inputs.bf16_bits(inputs.gen_x(wl, rows))
+    wb = inputs.bf16_bits(inputs.gen_w(wl))
+    dyb = inputs.bf16_bits(inputs.gen_dy(wl, rows, denominator=n_act))
+    y, rstd = oracle.rmsnorm_fwd_bf16(xb, wb, wl.eps)
+    dx, _, _ = oracle.rmsnorm_bwd_bf16(xb, wb, dyb, wl.eps)
+    for name, want in (("dx", dx), ("y", y), ("rstd", rstd)):
+        got = out[name][rows]
+        got = harness.bf16_bits_to_f32(got) if got.dtype == np.uint16 else got
+        assert CONTRACT.accuracy_passes(got, want, name), (wl.name, name)
+    frac = pu.bf16_ulp_fraction(out["dx"][rows], dx)
+    _log(f"{wl.name}: sampled rows {len(rows)}: dx within 1 bf16 ulp {frac:.5f}")
+    assert frac > 0.99
+
+
+def _gpu_data(wl):
+    """Logical inputs generated on the GPU (the CPU/GPU generators agree bit
+    for bit; test_generator_cpu_gpu_agree) -- the oracle side regenerates its
+    rows on the CPU."""
+    return adapters.make_inputs(wl, device="cuda")
+
+
+def _invariance(op, cells, data, name):
+    _log(f"{name}: {len(cells)} cells, calls per cell {[len(c.calls) for c in cells]}")
+    rep = harness.assert_gradient_batch_invariant(op, cells, CONTRACT, data=data, raise_on_red=False)
+    assert rep.strict, rep.first_failure
+    return rep
+
+
+def test_h4096_t32768_bn_vs_singletons_and_chunks():
+    wl = inputs.workload_h4096()
+    data = _gpu_data(wl)
+    cells = [layouts.full(wl), layouts.singleton_aggregate(wl),
+             layouts.chunked_per_sample(wl, chunk=512, name="BN/chunked_512"),
+             layouts.permuted(wl)]
+    ad = adapters.RmsNormAdapter()
+    _invariance(ad, cells, data, wl.name)
+    out = ad.run_cell(cells[0], data)
+    dw = _oracle_dweight(wl)
+    assert CONTRACT.accuracy_passes(out["dweight"], dw, "dweight")
+    _check_sampled_rows(wl, out, _sample_rows(wl.n_logical))
+
+
+def test_h8192_varlen_chunked_prefill():
+    wl = inputs.workload_h8192()
+    _log(f"{wl.name}: T = {wl.n_logical}, lengths {wl.lengths}")
+    data = _gpu_data(wl)
+    cells = [layouts.full(wl), layouts.chunked_packed(wl, chunk=512, name="BN/chunked_512"),
+             layouts.chunked_per_sample(wl, chunk=512, name="BN/chunked_512_per_sample")]
+    ad = adapters.RmsNormAdapter()
+    _invariance(ad, cells, data, wl.name)
+    out = ad.run_cell(cells[0], data)
+    del data
+    dw = _oracle_dweight(wl)
+    assert CONTRACT.accuracy_passes(out["dweight"], dw, "dweight")
+    _check_sampled_rows(wl, out, _sample_rows(wl.n_logical))
+
+
+def test_qk_norm_d128_t16384():
+    wq, wk = inputs.workload_qk("q"), inputs.workload_qk("k")
+    data = adapters.QkInputs("qknorm_d128_t16384", _gpu_data(wq), _gpu_data(wk))
+    cells = [adapters.PairCell(a.name, a, b) for a, b in zip(
+        [layouts.full(wq), layouts.singleton_aggregate(wq),
+         layouts.chunked_packed(wq, chunk=512, name="BN/chunked_512"),
+         layouts.chunked_per_sample(wq, chunk=512, name="BN/chunked_512_per_sample")],
+        [layouts.full(wk), layouts.singleton_aggregate(wk),
+         layouts.chunked_packed(wk, chunk=512, name="BN/chunked_512"),
+         layouts.chunked_per_sample(wk, chunk=512, name="BN/chunked_512_per_sample")])]
+    ad = adapters.QkNormAdapter()
+    _invariance(ad, cells, data, "qknorm_d128_t16384")
+    out = ad.run_cell(cells[0], data)
+    for side, wl, dxk, dwk in (("q", wq, "dq", "dweight_q"), ("k", wk, "dk", "dweight_k")):
+        dw = _oracle_dweight(wl, chunk=65536)
+        assert CONTRACT.accuracy_passes(out[dwk], dw, "dweight"), side
+        _check_sampled_rows(wl, {"dx": out[dxk], "y": out["y" + side], "rstd": out["rstd_" + side]},
+                            _sample_rows(wl.n_logical))
+
+
+def test_h5120_packed_padded_permuted_masked():
+    wl = inputs.workload_h5120()
+    data = _gpu_data(wl)
+    cells = [layouts.full(wl), layouts.packed_with_padding(wl), layouts.singleton_aggregate(wl)]
+    assert cells[1].calls[0].rows == 131072 and cells[1].calls[0].n_pad == 32768
+    ad = adapters.RmsNormAdapter()
+    _invariance(ad, cells, data, wl.name)
+    out = ad.run_cell(cells[0], data)
+    del data
+    dw = _oracle_dweight(wl)
+    assert CONTRACT.accuracy_passes(out["dweight"], dw, "dweight")
+    _check_sampled_rows(wl, out, _sample_rows(wl.n_logical))

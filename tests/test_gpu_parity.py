@@ -130,7 +130,7 @@ def test_inactive_rows_do_not_change_dweight_bits():
 
 @pytest.mark.parametrize("H,lengths", [(8, [59]), (128, [200, 77]), (4096, [130, 70]),
                                        (5120, [100, 29]), (1000, [64, 1]), (8192, [66, 70]),
-                                       (9000, [40, 41])])
+                                       (9000, [40, 41]), (8, [40000]), (16, [70000, 33001])])
 def test_dweight_is_the_canonical_order_bit_for_bit(H, lengths):
     """Tree conformance: given the same FP32 rstd, the GPU dweight equals the
     oracle's FP32 emulation of CDO-v1 bit for bit, for one call and for
