@@ -179,3 +179,27 @@ def gather_physical(logical: np.ndarray, call: Call, pad_value=0) -> np.ndarray:
     out[real] = logical[rl[real]]
     out[~real] = pad_value
     return out
+
+
+def standard_matrix(wl: Workload, chunk: int, pad_extra: int = 37) -> List[Cell]:
+    """Every layout family for one logical multiset: B=N, chunked (both
+    readings), singleton aggregate (in order and reversed), padded right and
+    left, permuted (seeded and reversed), and -- when the workload has padding
+    rows -- the packed layout with padding runs."""
+    T = wl.n_tokens
+    rev = list(range(wl.n_samples))[::-1]
+    cells = [
+        full(wl),
+        chunked_packed(wl, chunk=chunk, name="BN/chunked"),
+        chunked_per_sample(wl, chunk=chunk, name="BN/chunked_per_sample"),
+        singleton_aggregate(wl),
+        singleton_aggregate(wl, order=rev, name="B1-singleton_aggregate/reversed_calls"),
+        padded(wl, T + pad_extra, "right"),
+        padded(wl, T + pad_extra, "left"),
+        permuted(wl),
+        permuted(wl, perm=rev, name="BN/permuted_reverse"),
+    ]
+    if wl.pad_rows:
+        cells.append(packed_with_padding(wl))
+    return cells
+

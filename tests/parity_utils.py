@@ -23,19 +23,7 @@ def oracle_reference(wl: inputs.Workload) -> dict:
 
 def standard_cells(wl: inputs.Workload, chunk: int):
     """Every layout family for one logical multiset."""
-    T = wl.n_tokens
-    rev = list(range(wl.n_samples))[::-1]
-    return [
-        layouts.full(wl),
-        layouts.chunked_packed(wl, chunk=chunk, name="BN/chunked"),
-        layouts.chunked_per_sample(wl, chunk=chunk, name="BN/chunked_per_sample"),
-        layouts.singleton_aggregate(wl),
-        layouts.singleton_aggregate(wl, order=rev, name="B1-singleton_aggregate/reversed_calls"),
-        layouts.padded(wl, T + 37, "right"),
-        layouts.padded(wl, T + 37, "left"),
-        layouts.permuted(wl),
-        layouts.permuted(wl, perm=rev, name="BN/permuted_reverse"),
-    ]
+    return layouts.standard_matrix(wl, chunk)
 
 
 def qk_cells(wq, wk, chunk):

@@ -180,3 +180,14 @@ def test_no_private_thresholds_in_tests():
         if f.startswith("test_gpu") and f.endswith(".py"):
             text = open(os.path.join(here, f)).read()
             assert not re.search(r"assert_allclose|atol\s*=|rtol\s*=", text), f
+
+
+def test_cli_list_and_blocked_hardware_without_gpu(capsys):
+    import torch
+    from invariant_rmsnorm_backward_amd import cli
+    assert cli.main(["list"]) == 0
+    out = capsys.readouterr().out
+    assert "rmsnorm_h8_t59" in out and "BN/chunked: 10 call(s), rows 59" in out
+    if not torch.cuda.is_available():
+        assert cli.main(["sweep", "--workload", "rmsnorm_h8_t59"]) == 1
+        assert "blocked_hardware" in capsys.readouterr().out
