@@ -122,6 +122,14 @@ __device__ __forceinline__ int slot_row(const BwdArgs& a, int item, int blk, int
   const int64_t r = (int64_t)blk * kBlockRows + s;
   return r < a.rows ? (int)r : -1;
 }
+// Same, with the layout kind known at compile time (PLAN: a plan; else the
+// identity map), so each kernel instance has one straight memory sequence.
+template <bool PLAN>
+__device__ __forceinline__ int slot_row_t(const BwdArgs& a, int item, int blk, int s) {
+  if (PLAN) return a.plan.slot_phys[(int64_t)item * kBlockRows + s];
+  const int64_t r = (int64_t)blk * kBlockRows + s;
+  return r < a.rows ? (int)r : -1;
+}
 
 // Wide rows: V chunks of 8 columns per lane, TW wavefronts per row, 4
 // streams; the workgroup is 4*TW wavefronts.  Chunk q of the row held by
@@ -142,7 +150,7 @@ struct WideShape {
 // in registers; otherwise they are written to the spill rows.  When two row
 // buffers fit in registers the loop is software-pipelined: the next slot's
 // row is loaded before the current row's reduction and dx pass.
-template <int V, int TW, bool FULL, bool DX, bool DW, bool COMPLETE>
+template <int V, int TW, bool FULL, bool PLAN, bool DX, bool DW, bool COMPLETE>
 struct WideBlock {
   using Sh = WideShape<V, TW, FULL>;
   const BwdArgs& a;
@@ -158,15 +166,15 @@ struct WideBlock {
   float slot_r = 0.0f;
 
   __device__ __forceinline__ void load_slots() {
-    if (lane < Sh::SLOTS) {
-      slot_p = slot_row(a, item, blk, stream + Sh::S * lane);
-      if (slot_p >= 0) slot_r = a.rstd[slot_p];
-    }
-    // Consume both registers here, before the row loop: the compiler then
-    // waits for these loads once, instead of inserting a full vmcnt(0) wait
-    // inside the loop (which would also wait for the prefetched row).
-    asm volatile("" : "+v"(slot_p), "+v"(slot_r));
+    // every lane loads (lanes past SLOTS repeat a slot): no divergent memory ops
+    slot_p = slot_row_t<PLAN>(a, item, blk, stream + Sh::S * (lane & (Sh::SLOTS - 1)));
+    slot_r = a.rstd[slot_p >= 0 ? slot_p : 0];
   }
+  // Consume both slot registers before the row loop: the compiler then waits
+  // for their loads once, instead of inserting a full vmcnt(0) wait inside
+  // the loop (which would also wait for the prefetched row).  Called after
+  // the first row's loads are issued, so that row is in flight meanwhile.
+  __device__ __forceinline__ void settle_slots() { asm volatile("" : "+v"(slot_p), "+v"(slot_r)); }
   __device__ __forceinline__ int row_of(int i) const { return __builtin_amdgcn_readlane(slot_p, i); }
   __device__ __forceinline__ float rstd_of(int i) const {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(slot_r), i));
@@ -263,6 +271,7 @@ struct WideBlock {
   }
 
   __device__ __forceinline__ void run_sequential() {
+    settle_slots();
     for (int i = 0; i < Sh::SLOTS; ++i) {
       uint4 xv[V], dv[V];
       const int p = row_of(i);
@@ -276,6 +285,7 @@ struct WideBlock {
     uint4 xa[V], da[V], xb[V], db[V];
     int pa = row_of(0);
     load(pa, xa, da);
+    settle_slots();
     for (int i = 0; i < Sh::SLOTS; i += 2) {
       const int pb = row_of(i + 1);
       load(pb, xb, db);
@@ -287,7 +297,7 @@ struct WideBlock {
   }
 };
 
-template <int V, int TW, bool FULL, bool DX, bool DW>
+template <int V, int TW, bool FULL, bool PLAN, bool DX, bool DW>
 __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
   using Sh = WideShape<V, TW, FULL>;
   __shared__ float w_s[DX ? Sh::COLS : 1];
@@ -328,7 +338,7 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
 
   int blk;
   bool complete;
-  if (a.plan.item_info != nullptr) {
+  if (PLAN) {
     const int info = a.plan.item_info[item];
     complete = info >= 0;
     blk = complete ? info : ~info;
@@ -343,11 +353,11 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
 
   const int base = half * V * 512 + lane * 8;      // this lane's first column
   if (!DW || complete) {
-    WideBlock<V, TW, FULL, DX, DW, true>{a, item, blk, stream, half, lane, wv, H, nchunk, base,
-                                         w_s, dot_s, acc}.run();
+    WideBlock<V, TW, FULL, PLAN, DX, DW, true>{a, item, blk, stream, half, lane, wv, H, nchunk,
+                                               base, w_s, dot_s, acc}.run();
   } else {
-    WideBlock<V, TW, FULL, DX, DW, false>{a, item, blk, stream, half, lane, wv, H, nchunk, base,
-                                          w_s, dot_s, acc}.run();
+    WideBlock<V, TW, FULL, PLAN, DX, DW, false>{a, item, blk, stream, half, lane, wv, H, nchunk,
+                                                base, w_s, dot_s, acc}.run();
     return;
   }
 
@@ -604,14 +614,19 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int V, int TW, bool FULL>
-static void bwd_wide_go2(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+template <int V, int TW, bool FULL, bool PLAN>
+static void bwd_wide_go3(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
   using Sh = WideShape<V, TW, FULL>;
   const int pad_groups = dx ? (a.plan.n_pad + Sh::WAVES - 1) / Sh::WAVES : 0;
   const dim3 grid((unsigned)(a.plan.n_items + pad_groups)), block(Sh::THREADS);
-  if (dx && dw) bwd_wide_kernel<V, TW, FULL, true, true><<<grid, block, 0, st>>>(a);
-  else if (dx) bwd_wide_kernel<V, TW, FULL, true, false><<<grid, block, 0, st>>>(a);
-  else bwd_wide_kernel<V, TW, FULL, false, true><<<grid, block, 0, st>>>(a);
+  if (dx && dw) bwd_wide_kernel<V, TW, FULL, PLAN, true, true><<<grid, block, 0, st>>>(a);
+  else if (dx) bwd_wide_kernel<V, TW, FULL, PLAN, true, false><<<grid, block, 0, st>>>(a);
+  else bwd_wide_kernel<V, TW, FULL, PLAN, false, true><<<grid, block, 0, st>>>(a);
+}
+template <int V, int TW, bool FULL>
+static void bwd_wide_go2(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+  if (a.plan.item_info != nullptr) bwd_wide_go3<V, TW, FULL, true>(a, dx, dw, st);
+  else bwd_wide_go3<V, TW, FULL, false>(a, dx, dw, st);
 }
 template <int V, int TW>
 static void bwd_wide_go(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
