@@ -20,10 +20,10 @@
  * order (CDO-v1) that depends only on the logical row index and on nothing
  * else:
  *     c = fl32(fl32(dy*x)*rstd)  (dy*x of two bf16 values is exact)
- *     block b = logical rows 64b..64b+63; stream w = slot mod 8 folds its
- *     8 slots in ascending order from +0.0; block partial
- *     P[b] = ((q0+q1)+(q2+q3))+((q4+q5)+(q6+q7)); dweight = perfect
- *     pairwise tree over P[0..2^ceil(log2 nb)) with +0.0 leaves past nb.
+ *     block b = logical rows 64b..64b+63; stream w = slot mod 4 folds its
+ *     16 slots (w, w+4, ..., w+60) in ascending order from +0.0; block
+ *     partial P[b] = (q0+q1)+(q2+q3); dweight = perfect pairwise tree over
+ *     P[0..2^ceil(log2 nb)) with +0.0 leaves past nb.
  *
  * Conventions for every entry point.
  *   - Tensors are contiguous and row-major.  bf16 tensors are passed as raw

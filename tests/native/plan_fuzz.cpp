@@ -1,0 +1,97 @@
+// Fuzz driver for the host-side plan and accumulator bookkeeping, built with
+// AddressSanitizer + UndefinedBehaviorSanitizer by tests/test_sanitizers.py.
+// Random valid maps must build plans whose slots cover exactly the real rows;
+// invalid maps must be refused; accumulator coverage must catch duplicates
+// and missing rows.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <string>
+#include <vector>
+
+#include "plan.h"
+
+using namespace rbi;
+
+static int fails = 0;
+#define CHECK(c) do { if (!(c)) { std::printf("FAIL %s:%d %s\n", __FILE__, __LINE__, #c); ++fails; } } while (0)
+
+int main() {
+  std::mt19937_64 rng(12345);
+  for (int iter = 0; iter < 3000; ++iter) {
+    const int64_t T = rng() % 700;
+    // a random subset of logical rows, permuted, with random padding interleaved
+    std::vector<int32_t> ids;
+    for (int64_t l = 0; l < T; ++l) if (rng() % 3 != 0) ids.push_back((int32_t)l);
+    std::shuffle(ids.begin(), ids.end(), rng);
+    std::vector<int32_t> rl;
+    for (int32_t l : ids) {
+      while (rng() % 5 == 0) rl.push_back(-1);
+      rl.push_back(l);
+    }
+    PlanHost P;
+    std::string err;
+    int rc = build_plan(rl.data(), (int64_t)rl.size(), T, &P, &err);
+    CHECK(rc == kOk);
+    // every real row appears in exactly one slot, pads in the pad list
+    std::vector<int> seen(rl.size(), 0);
+    for (size_t it = 0; it < P.item_info.size(); ++it) {
+      const int32_t info = P.item_info[it];
+      const int32_t b = info >= 0 ? info : ~info;
+      int present = 0, held = 0;
+      for (int s = 0; s < kBlockRows; ++s) {
+        const int32_t p = P.slot_phys[it * kBlockRows + s];
+        if (b * (int64_t)kBlockRows + s < T) ++present;
+        if (p >= 0) {
+          CHECK(p < (int32_t)rl.size());
+          CHECK(rl[p] == b * kBlockRows + s);
+          seen[p]++;
+          ++held;
+        }
+      }
+      CHECK((info >= 0) == (held == present));
+    }
+    for (int32_t p : P.pad_rows) { CHECK(rl[p] == -1); seen[p]++; }
+    for (size_t p = 0; p < rl.size(); ++p) CHECK(seen[p] == 1);
+    // accumulator: one call then finalize must report missing rows unless all held
+    AccHost A;
+    A.init(T, 8);
+    CHECK(A.register_call(&P, (int64_t)rl.size(), &err) == kOk);
+    CHECK(A.register_call(&P, (int64_t)rl.size(), &err) == (ids.empty() ? kOk : kECoverage));
+    std::vector<int32_t> spilled;
+    const int frc = A.prepare_finalize(&spilled, &err);
+    CHECK(frc == ((int64_t)ids.size() == T ? kOk : kECoverage));
+    // invalid maps: out of range, duplicate, below -1
+    if (!rl.empty()) {
+      std::vector<int32_t> bad = rl;
+      bad[rng() % bad.size()] = (int32_t)T;
+      CHECK(build_plan(bad.data(), (int64_t)bad.size(), T, &P, &err) == kELayout);
+      bad = rl;
+      bad[rng() % bad.size()] = -7;
+      CHECK(build_plan(bad.data(), (int64_t)bad.size(), T, &P, &err) == kELayout);
+      if (ids.size() >= 2) {
+        // copy one real row's logical id onto another real row
+        std::vector<size_t> real;
+        for (size_t p = 0; p < rl.size(); ++p) if (rl[p] >= 0) real.push_back(p);
+        bad = rl;
+        bad[real[1]] = bad[real[0]];
+        CHECK(build_plan(bad.data(), (int64_t)bad.size(), T, &P, &err) == kELayout);
+      }
+    }
+  }
+  // identity accumulator path and state machine
+  AccHost A;
+  std::string err;
+  A.init(100, 16);
+  CHECK(A.register_call(nullptr, 99, &err) == kELayout);
+  CHECK(A.register_call(nullptr, 100, &err) == kOk);
+  std::vector<int32_t> sp;
+  CHECK(A.prepare_finalize(&sp, &err) == kOk && sp.empty());
+  A.finalized = true;
+  CHECK(A.register_call(nullptr, 100, &err) == kEState);
+  A.reset();
+  CHECK(A.register_call(nullptr, 100, &err) == kOk);
+  std::printf("plan fuzz: %s\n", fails ? "FAILED" : "ok");
+  return fails ? 1 : 0;
+}
