@@ -61,29 +61,39 @@ def measured_traffic(bwd_bytes: int):
 
 
 def cpu_baseline(wl, budget_s: float = 12.0):
-    """The FP64 oracle as it stands, single thread, on the first rows of the
-    same workload until about budget_s seconds of work have been timed."""
+    """The FP64 oracle as it stands, single thread, over the rows of the same
+    workload in 1024-row pieces, passing over the workload again (with the
+    inputs kept from the first pass) until about budget_s seconds of work
+    have been timed."""
     import oracle
     from invariant_rmsnorm_backward_amd import inputs
     import numpy as np
     chunk = 1024
     H = wl.hidden
     wb = inputs.bf16_bits(inputs.gen_w(wl))
+    pieces = []
     done, spent, a = 0, 0.0, 0
-    while spent < budget_s and a < wl.n_logical:
-        rows = np.arange(a, min(a + chunk, wl.n_logical))
-        xb = inputs.bf16_bits(inputs.gen_x(wl, rows))
-        dyb = inputs.bf16_bits(inputs.gen_dy(wl, rows))
+    while spent < budget_s:
+        k = a // chunk
+        if k == len(pieces):
+            if a >= wl.n_logical:
+                a, k = 0, 0
+            else:
+                rows = np.arange(a, min(a + chunk, wl.n_logical))
+                pieces.append((inputs.bf16_bits(inputs.gen_x(wl, rows)),
+                               inputs.bf16_bits(inputs.gen_dy(wl, rows))))
+        xb, dyb = pieces[k]
         t0 = time.perf_counter()
         oracle.rmsnorm_fwd_bf16(xb, wb, wl.eps)
         oracle.rmsnorm_bwd_bf16(xb, wb, dyb, wl.eps)
         spent += time.perf_counter() - t0
-        done += len(rows)
+        done += xb.shape[0]
         a += chunk
     f, b = algorithmic_bytes(done, done, H)
     return {"value": round((f + b) / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of {wl.n_logical} rows of {wl.name}, fwd+bwd in FP64 "
-                      f"(single-threaded C), {spent:.1f} s timed, input generation excluded",
+            "sample": f"{done} rows of {wl.name} ({done / wl.n_logical:.2f} passes over its "
+                      f"{wl.n_logical} rows, 1024-row pieces), fwd+bwd in FP64 (single-threaded C), "
+                      f"{spent:.1f} s timed, input generation excluded",
             "rows_per_s": round(done / spent, 1)}
 
 
