@@ -115,6 +115,167 @@ def copy_ceiling(torch, nbytes: int, iters: int = 20) -> float:
     del src, dst
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
+QK_PAIR = "qknorm_d128_t16384"
+
+
+def measure_cell(args, torch, np, binding, inputs, layouts):
+    """Info measurement of one workload on one layout cell: a step runs every
+    call of the cell (rmsnorm_fwd, then rmsnorm_bwd_dx into the accumulator),
+    then rmsnorm_dw_finalize, for each norm of the workload (Q and K for the
+    per-head pair).  Physical inputs are gathered before timing; padding rows
+    hold a NaN pattern that the kernels never read.  The cell's dweight is
+    also checked bitwise against one B=N call on the same logical rows."""
+    if args.workload == QK_PAIR:
+        wls = [inputs.ALL_WORKLOADS[QK_PAIR + "_q"](), inputs.ALL_WORKLOADS[QK_PAIR + "_k"]()]
+    else:
+        wls = [inputs.ALL_WORKLOADS[args.workload]()]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    norms = []
+    for wl in wls:
+        T, H = wl.n_logical, wl.hidden
+        chunk = 7 if wl.hidden <= 8 else 512
+        cells = {c.name: c for c in layouts.standard_matrix(wl, chunk)}
+        if args.cell not in cells:
+            print(f"unknown cell {args.cell!r}; cells: {sorted(cells)}", file=sys.stderr)
+            sys.exit(2)
+        cell = cells[args.cell]
+        print(f"[bench] generating {wl.name} ({T} x {H}), cell {cell.name}: "
+              f"{len(cell.calls)} call(s)", file=sys.stderr, flush=True)
+        x = inputs.gen_x(wl, device="cuda")
+        dy = inputs.gen_dy(wl, device="cuda")
+        w = inputs.gen_w(wl, device="cuda")
+        calls = []
+        for call in cell.calls:
+            if call.row_logical is None:
+                calls.append(dict(rows=call.rows, real=call.rows, layout=None, x=x, dy=dy))
+                continue
+            rl = torch.from_numpy(call.row_logical.astype(np.int64)).cuda()
+            real = rl >= 0
+            xc = torch.full((call.rows, H), 0x7FC1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+            dyc = xc.clone()
+            xc[real] = x[rl[real]]
+            dyc[real] = dy[rl[real]]
+            calls.append(dict(rows=call.rows, real=int(real.sum()),
+                              layout=binding.Layout(call.row_logical, T), x=xc, dy=dyc))
+        sets = []
+        for k in range(args.sets):
+            sets.append([dict(x=c["x"] if k == 0 else c["x"].clone(),
+                              dy=c["dy"] if k == 0 else c["dy"].clone(),
+                              y=torch.empty_like(c["x"]), dx=torch.empty_like(c["x"]),
+                              rstd=torch.empty(c["rows"], dtype=torch.float32, device="cuda"))
+                         for c in calls])
+        acc = binding.DwAccumulator(T, H)
+        # B=N reference dweight on the logical rows (identity layout)
+        acc_ref = binding.DwAccumulator(T, H)
+        _, r_ref = binding.fwd(x, w, wl.eps)
+        binding.bwd(x, w, dy, r_ref, None, acc_ref)
+        dw_ref = acc_ref.finalize()
+        norms.append(dict(wl=wl, T=T, H=H, w=w, calls=calls, sets=sets, acc=acc,
+                          dw=torch.empty(H, dtype=torch.float32, device="cuda"),
+                          dw_ref=dw_ref, acc_ref=acc_ref, cell=cell))
+
+    def run_fwd(n, s):
+        for c, b in zip(n["calls"], s):
+            binding.rmsnorm_fwd(b["x"].data_ptr(), n["w"].data_ptr(), b["y"].data_ptr(),
+                                b["rstd"].data_ptr(), c["rows"], n["H"], n["wl"].eps,
+                                None if c["layout"] is None else c["layout"].handle, sh)
+
+    def run_bwd(n, s):
+        for c, b in zip(n["calls"], s):
+            binding.rmsnorm_bwd_dx(b["x"].data_ptr(), n["w"].data_ptr(), b["dy"].data_ptr(),
+                                   b["rstd"].data_ptr(), b["dx"].data_ptr(), c["rows"], n["H"],
+                                   None if c["layout"] is None else c["layout"].handle,
+                                   n["acc"].handle, sh)
+
+    def run_fin(n):
+        binding.rmsnorm_dw_finalize(n["acc"].handle, n["dw"].data_ptr(), sh)
+        binding.rmsnorm_dw_acc_reset(n["acc"].handle, sh)
+
+    def step(i):
+        for n in norms:
+            s = n["sets"][i % len(n["sets"])]
+            run_fwd(n, s)
+            run_bwd(n, s)
+            run_fin(n)
+
+    step(0)
+    torch.cuda.synchronize()
+    inv_ok = all(torch.equal(n["dw"].view(torch.int32), n["dw_ref"].view(torch.int32)) for n in norms)
+    for i in range(args.warmup):
+        step(i)
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / K * 1e3
+
+    # per-phase times: events around each phase of each norm
+    ph = {"fwd": [], "bwd": [], "finalize": []}
+    for i in range(K):
+        tot = {"fwd": [], "bwd": [], "finalize": []}
+        for n in norms:
+            s = n["sets"][i % len(n["sets"])]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+            run_fwd(n, s)
+            e[1].record(stream)
+            run_bwd(n, s)
+            e[2].record(stream)
+            run_fin(n)
+            e[3].record(stream)
+            tot["fwd"].append((e[0], e[1]))
+            tot["bwd"].append((e[1], e[2]))
+            tot["finalize"].append((e[2], e[3]))
+        for k in ph:
+            ph[k].append(tot[k])
+    torch.cuda.synchronize()
+    med = {k: float(np.median([sum(a.elapsed_time(b) for a, b in step_ev) for step_ev in v]))
+           for k, v in ph.items()}
+
+    fb = bb = 0
+    for n in norms:
+        for c in n["calls"]:
+            f1, b1 = algorithmic_bytes(c["real"], c["rows"], n["H"])
+            fb += f1
+            bb += b1 - 4 * n["H"]          # dweight is written once per norm, not per call
+        bb += 4 * n["H"]
+    rows_real = sum(c["real"] for n in norms for c in n["calls"])
+    rows_phys = sum(c["rows"] for n in norms for c in n["calls"])
+    value = (fb + bb) / (ms_step * 1e-3) / 1e9
+    achieved = bb / (med["bwd"] * 1e-3) / 1e9
+    n_calls = sum(len(n["calls"]) for n in norms)
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "cell": args.cell, "hidden": norms[0]["H"],
+                   "rows_real": rows_real, "rows_physical": rows_phys, "calls_per_step": n_calls,
+                   "norms": [n["wl"].name for n in norms], "io_dtype": "bf16",
+                   "buffer_sets": args.sets},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "backward phase (all bwd launches of the step)",
+                     "algorithmic_bytes_per_step": bb, "bwd_ms": round(med["bwd"], 5)},
+        "cpu_baseline": None,
+        "phases_ms": {k: round(v, 5) for k, v in med.items()},
+        "phases_gbps": {"fwd": round(fb / (med["fwd"] * 1e-3) / 1e9, 1),
+                        "bwd": round(achieved, 1)},
+        "rows_per_s": round(rows_real / (ms_step * 1e-3), 1),
+        "frac_of_peak": round(value / PEAK_GBPS, 4),
+        "dweight_bitwise_equal_to_bn_full": inv_ok,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    for n in norms:
+        for c in n["calls"]:
+            if c["layout"] is not None:
+                c["layout"].close()
+        n["acc"].close()
+        n["acc_ref"].close()
+    print(json.dumps(out))
+
 
 def main():
     ap = argparse.ArgumentParser()
@@ -124,6 +285,9 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotating input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true")
+    ap.add_argument("--workload", default=None,
+                    help="measure another workload (info line; the default run is the headline)")
+    ap.add_argument("--cell", default="BN/full", help="layout cell for --workload")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -140,6 +304,9 @@ def main():
         sys.exit(2)
     binding.load()
     torch.cuda.set_device(0)
+    if args.workload is not None:
+        measure_cell(args, torch, np, binding, inputs, layouts)
+        return
     wl = inputs.workload_h4096()
     T, H = wl.n_logical, wl.hidden
     stream = torch.cuda.current_stream()

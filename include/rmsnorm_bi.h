@@ -145,8 +145,21 @@ int rmsnorm_dw_acc_destroy(rmsnorm_dw_acc* acc);
 const char* rmsnorm_last_error(void);
 
 /* Provenance: target, canonical-order version and kernel variants, e.g.
- * "hip gfx950; cdo=v1 R=64 S=8 tree=pairwise; ...".  Static string. */
+ * "hip gfx950; cdo=v1 R=64 S=4; ...".  Static string. */
 const char* rmsnorm_backend_info(void);
+
+/* Work distribution of the backward for hidden > 256 (a tuning knob; no
+ * output bit depends on it).  A call whose rows touch fewer than `blocks`
+ * canonical 64-row blocks runs the backward in two passes -- row-parallel
+ * dx, then the dweight fold split over 512-column tiles -- instead of the
+ * fused one-workgroup-per-block kernel, so that small calls (chunked
+ * prefill pieces, single samples) still occupy the whole GPU.  Both paths
+ * run the same per-row and per-block arithmetic, so dx and dweight are
+ * bitwise the same either way.  0 disables the two-pass path; a negative
+ * value restores the default.  If `previous` is non-NULL it receives the
+ * threshold in force before the call.  Process-wide; takes effect for
+ * backward calls enqueued afterwards.  Always returns RMSNORM_OK. */
+int rmsnorm_set_split_threshold(int64_t blocks, int64_t* previous);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,8 @@ STATUS_NAMES = {OK: "OK", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", ELAYOU
 EXPORTED = ("rmsnorm_max_hidden", "rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_contrib",
             "rmsnorm_dw_finalize", "rmsnorm_layout_create", "rmsnorm_layout_destroy",
             "rmsnorm_layout_check", "rmsnorm_dw_acc_create", "rmsnorm_dw_acc_reset",
-            "rmsnorm_dw_acc_destroy", "rmsnorm_last_error", "rmsnorm_backend_info")
+            "rmsnorm_dw_acc_destroy", "rmsnorm_last_error", "rmsnorm_backend_info",
+            "rmsnorm_set_split_threshold")
 
 
 class RmsNormError(RuntimeError):
@@ -68,6 +69,7 @@ def load() -> ctypes.CDLL:
         "rmsnorm_dw_acc_destroy": ([P], I32),
         "rmsnorm_last_error": ([], ctypes.c_char_p),
         "rmsnorm_backend_info": ([], ctypes.c_char_p),
+        "rmsnorm_set_split_threshold": ([I64, ctypes.POINTER(ctypes.c_int64)], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -153,6 +155,15 @@ def rmsnorm_dw_acc_destroy(acc: Optional[int]) -> None:
 
 
 # ------------------------------------------------------------------ helpers
+def rmsnorm_set_split_threshold(blocks: int) -> int:
+    """Sets the backward's two-pass threshold (in canonical blocks; 0 disables
+    the two-pass path, negative restores the default); returns the previous one."""
+    prev = ctypes.c_int64(0)
+    _check(load().rmsnorm_set_split_threshold(int(blocks), ctypes.byref(prev)),
+           "rmsnorm_set_split_threshold")
+    return int(prev.value)
+
+
 def current_stream() -> int:
     import torch
     return torch.cuda.current_stream().cuda_stream

@@ -87,8 +87,15 @@ const char* rmsnorm_backend_info(void) {
   return "hip gfx950; cdo=v1 R=64 S=4, "
          "contribution fl32(fl32(dy*x)*rstd), streams fold ascending from +0.0, "
          "stream tree pairwise, block tree pairwise with +0.0 padding; no atomics; "
-         "fwd=wave_per_row|lanes_per_row bwd=fused dx+dW, one workgroup per 64-row block, nt loads/stores; "
+         "fwd=wave_per_row|lanes_per_row bwd=fused dx+dW, one workgroup per 64-row block "
+         "(calls with few blocks: row-parallel dx + column-split dW fold), nt loads/stores; "
          "max_hidden=10240";
+}
+
+int rmsnorm_set_split_threshold(int64_t blocks, int64_t* previous) {
+  if (previous != nullptr) *previous = rbi::split_items();
+  rbi::set_split_items(blocks);
+  return RMSNORM_OK;
 }
 
 int rmsnorm_fwd(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y, float* rstd,

@@ -1,7 +1,8 @@
 // kernels.h -- launchers of the gfx950 kernels (internal C++ interface used
-// by the C-ABI layer).  Kernel variants are chosen from `hidden` alone, never
-// from the row count or the layout, so a row's results cannot depend on how
-// many rows share its call.
+// by the C-ABI layer).  The arithmetic a row or a canonical block goes
+// through is fixed by `hidden` alone; the row count of a call only chooses
+// how that same arithmetic is spread over workgroups, so a result cannot
+// depend on how many rows share its call.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -10,6 +11,14 @@
 namespace rbi {
 
 constexpr int kMaxHidden = 10240;
+
+// Calls that touch fewer canonical blocks than the split threshold run the
+// backward in two passes (row-parallel dx, column-split dweight fold); the
+// per-row and per-block arithmetic is the same code as the fused kernel's,
+// so the choice never changes a bit of any output.
+constexpr int64_t kDefaultSplitItems = 96;   // measured crossover: 64 vs 128 blocks
+void set_split_items(int64_t n);   // n < 0 restores the default
+int64_t split_items();
 
 // Physical->logical plan as the kernels see it (device pointers).
 struct PlanDev {

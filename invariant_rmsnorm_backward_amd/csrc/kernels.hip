@@ -17,6 +17,8 @@
 // tree.  Blocks that a call holds only in part write their rows'
 // contributions to a spill area instead, and the finalize step folds them in
 // exactly the same order.  No atomics anywhere: every sum has one owner.
+#include <mutex>
+
 #include "kernels.h"
 
 #include "device_math.h"
@@ -144,6 +146,18 @@ struct WideShape {
   static constexpr int COLS = 512 * V * TW;        // columns the workgroup covers
   static constexpr int NTILE = (V * TW + 1) / 2;   // 1024-column tiles of the stream tree
 };
+
+// w as FP32 in LDS; columns past hidden hold 0 so masked lanes read zeros.
+template <typename Sh>
+__device__ __forceinline__ void stage_w(const BwdArgs& a, float* w_s, int tid, int nchunk) {
+  for (int q = tid; q < Sh::COLS / 8; q += Sh::THREADS) {
+    float f[8];
+    unpack8(q < nchunk ? load16(a.w + q * 8) : make_uint4(0, 0, 0, 0), f);
+    store_f4(&w_s[q * 8], f[0], f[1], f[2], f[3]);
+    store_f4(&w_s[q * 8 + 4], f[4], f[5], f[6], f[7]);
+  }
+  __syncthreads();
+}
 
 // One canonical block: the stream's slots in ascending order.  COMPLETE: the
 // call holds every present row of the block, so the contributions are folded
@@ -325,16 +339,7 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
     return;
   }
 
-  if (DX) {
-    // w as FP32 in LDS; columns past hidden hold 0 so masked lanes read zeros
-    for (int q = tid; q < Sh::COLS / 8; q += Sh::THREADS) {
-      float f[8];
-      unpack8(q < nchunk ? load16(a.w + q * 8) : make_uint4(0, 0, 0, 0), f);
-      store_f4(&w_s[q * 8], f[0], f[1], f[2], f[3]);
-      store_f4(&w_s[q * 8 + 4], f[4], f[5], f[6], f[7]);
-    }
-    __syncthreads();
-  }
+  if (DX) stage_w<Sh>(a, w_s, tid, nchunk);
 
   int blk;
   bool complete;
@@ -387,6 +392,134 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
   }
 }
 
+// ------------------------------------------------- two-pass backward (few blocks)
+// A call that touches few canonical blocks would leave most compute units
+// idle in the fused kernel (one workgroup per block).  It runs in two passes
+// instead, each with enough workgroups for the whole chip:
+//   pass 1 (bwd_dx_rows_kernel): dx, four physical rows per workgroup step,
+//     through the very same per-row code as the fused kernel (WideBlock's
+//     load + process with the dweight part compiled out), so every dx bit
+//     equals the fused kernel's;
+//   pass 2 (dw_cols_kernel): the dweight contributions and the in-block
+//     stream fold of one canonical block over 512 columns per workgroup,
+//     with the same operations in the same order as the fused kernel, so
+//     the block partials and spill rows are bitwise the same.
+// The second pass reads x and dy again; for the calls that take this path
+// they are small enough to be served largely from the last-level cache.
+template <int V, int TW, bool FULL, bool PLAN>
+__global__ __launch_bounds__(256 * TW) void bwd_dx_rows_kernel(BwdArgs a) {
+  using Sh = WideShape<V, TW, FULL>;
+  __shared__ float w_s[Sh::COLS];
+  __shared__ float dot_s[TW > 1 ? 2 * 16 : 1];
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int stream = wv / TW;          // the workgroup's row slot (0..3)
+  const int half = wv % TW;
+  const int H = FULL ? Sh::COLS : a.hidden;
+  const int nchunk = H >> 3;
+  stage_w<Sh>(a, w_s, tid, nchunk);
+  float acc[1];
+  const int base = half * V * 512 + lane * 8;
+  WideBlock<V, TW, FULL, PLAN, true, false, true> wb{a, 0, 0, stream, half, lane, wv, H, nchunk,
+                                                     base, w_s, dot_s, acc};
+  const int64_t step = (int64_t)gridDim.x * Sh::S;
+  int i = 0;
+  // the trip count is the same for every wavefront of the workgroup (the
+  // TW > 1 dot exchange synchronises the workgroup once per row)
+  for (int64_t r0 = (int64_t)blockIdx.x * Sh::S; r0 < a.rows; r0 += step, ++i) {
+    const int64_t row = r0 + stream;
+    int p = row < a.rows ? (int)row : -1;
+    if (PLAN && p >= 0 && a.plan.row_logical[p] < 0) {
+      // padding row: dx = 0, nothing read
+      uint16_t* d = a.dx + (int64_t)p * H + base;
+#pragma unroll
+      for (int k = 0; k < V; ++k)
+        if (wb.in_row(k)) store16_stream(d + k * 512, make_uint4(0, 0, 0, 0));
+      p = -1;
+    }
+    const float r = p >= 0 ? a.rstd[p] : 0.0f;
+    uint4 xv[V], dv[V];
+    wb.load(p, xv, dv);
+    wb.process(i, p, xv, dv, r);
+  }
+}
+
+// One canonical block over 512 columns: wavefront w is fold stream w and
+// lane l holds columns 8*(64*blockIdx.y + l) .. +8.  All 16 rows of the
+// stream are loaded before the fold, which then runs in slot order.
+template <bool PLAN>
+__global__ __launch_bounds__(256) void dw_cols_kernel(BwdArgs a) {
+  __shared__ float q_s[kStreams - 1][512];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int stream = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int item = blockIdx.x;
+  const int H = a.hidden;
+  const int q = blockIdx.y * 64 + lane;         // this lane's 8-column chunk
+  const bool on = q < (H >> 3);
+  int blk;
+  bool complete;
+  if (PLAN) {
+    const int info = a.plan.item_info[item];
+    complete = info >= 0;
+    blk = complete ? info : ~info;
+  } else {
+    blk = item;
+    complete = true;
+  }
+  // lane i (< 16) holds the physical row and rstd of the stream's slot i
+  const int sp = slot_row_t<PLAN>(a, item, blk, stream + kStreams * (lane & (kSlotsPerStream - 1)));
+  const float sr = a.rstd[sp >= 0 ? sp : 0];
+  uint4 xv[kSlotsPerStream], dv[kSlotsPerStream];
+#pragma unroll
+  for (int i = 0; i < kSlotsPerStream; ++i) {
+    const int p = __builtin_amdgcn_readlane(sp, i);
+    const int64_t off = (int64_t)(p >= 0 ? p : 0) * H + (on ? q * 8 : 0);
+    xv[i] = load16_stream(a.x + off);
+    dv[i] = load16_stream(a.dy + off);
+  }
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kSlotsPerStream; ++i) {
+    const int p = __builtin_amdgcn_readlane(sp, i);
+    if (p < 0) continue;
+    const float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sr), i));
+    float xf[8], df[8], c[8];
+    unpack8(xv[i], xf);
+    unpack8(dv[i], df);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pr = df[e] * xf[e];          // exact: two bf16 significands
+      c[e] = pr * r;                           // the row's contribution, rounded once
+      acc[e] = acc[e] + c[e];
+    }
+    if (!complete && on) {
+      float* srow = a.S + ((int64_t)blk * kBlockRows + stream + kStreams * i) * H + q * 8;
+      store_f4_stream(srow, c[0], c[1], c[2], c[3]);
+      store_f4_stream(srow + 4, c[4], c[5], c[6], c[7]);
+    }
+  }
+  if (!complete) return;
+  if (stream > 0) {
+    float* d = &q_s[stream - 1][lane * 8];
+    store_f4(d, acc[0], acc[1], acc[2], acc[3]);
+    store_f4(d + 4, acc[4], acc[5], acc[6], acc[7]);
+  }
+  __syncthreads();
+  if (stream == 0 && on) {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      o[e] = stream_tree4(acc[e], q_s[0][lane * 8 + e], q_s[1][lane * 8 + e], q_s[2][lane * 8 + e]);
+    float* dst = a.P + (int64_t)blk * H + q * 8;
+    store_f4(dst, o[0], o[1], o[2], o[3]);
+    store_f4(dst + 4, o[4], o[5], o[6], o[7]);
+  }
+}
+
 // Small rows: hidden = 8L (L in 1..32), one group of L lanes per row; the
 // 64 slots' contributions go through LDS and the 4 streams fold them there.
 template <int L, bool DX, bool DW>
@@ -423,19 +556,31 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
     complete = true;
   }
 
+  // Every row of the group is loaded before any is processed (absent slots
+  // read row 0 and are never used), so the block's loads are all in flight.
+  int pp[ITERS];
+  uint4 xv[ITERS], dv[ITERS];
+  float rr[ITERS];
+#pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int s = g + it * GROUPS;
-    const int p = s < kBlockRows ? slot_row(a, item, blk, s) : -1;
-    uint4 xv = make_uint4(0, 0, 0, 0), dv = make_uint4(0, 0, 0, 0);
-    float r = 0.0f;
-    if (p >= 0) {
-      xv = load16_stream(a.x + (int64_t)p * H + sub * 8);
-      dv = load16_stream(a.dy + (int64_t)p * H + sub * 8);
-      r = a.rstd[p];
-    }
+    pp[it] = s < kBlockRows ? slot_row(a, item, blk, s) : -1;
+  }
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int row = pp[it] >= 0 ? pp[it] : 0;
+    xv[it] = load16_stream(a.x + (int64_t)row * H + sub * 8);
+    dv[it] = load16_stream(a.dy + (int64_t)row * H + sub * 8);
+    rr[it] = a.rstd[row];
+  }
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int s = g + it * GROUPS;
+    const int p = pp[it];
+    const float r = p >= 0 ? rr[it] : 0.0f;
     float xf[8], df[8], pr[8];
-    unpack8(xv, xf);
-    unpack8(dv, df);
+    unpack8(p >= 0 ? xv[it] : make_uint4(0, 0, 0, 0), xf);
+    unpack8(p >= 0 ? dv[it] : make_uint4(0, 0, 0, 0), df);
 #pragma unroll
     for (int e = 0; e < 8; ++e) pr[e] = df[e] * xf[e];
     if (DX) {
@@ -571,8 +716,8 @@ const char* fwd_variant(int hidden) {
 }
 const char* bwd_variant(int hidden) {
   if (small_lanes(hidden)) return "bwd_small(lds_fold, streams=4)";
-  return wide_tw(hidden) == 1 ? "bwd_wide(wave_per_row, streams=4)"
-                              : "bwd_wide(two_waves_per_row, streams=4)";
+  return wide_tw(hidden) == 1 ? "bwd_wide(wave_per_row, streams=4; few blocks: dx_rows + dw_cols)"
+                              : "bwd_wide(two_waves_per_row, streams=4; few blocks: dx_rows + dw_cols)";
 }
 
 static int grid_cap() { return 256 * 16; }
@@ -614,9 +759,35 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Calls touching fewer canonical blocks than this take the two-pass path
+// (host-side setting, guarded by a mutex).
+static std::mutex g_split_mu;
+static int64_t g_split_items = kDefaultSplitItems;
+
+void set_split_items(int64_t n) {
+  std::lock_guard<std::mutex> lk(g_split_mu);
+  g_split_items = n < 0 ? kDefaultSplitItems : n;
+}
+int64_t split_items() {
+  std::lock_guard<std::mutex> lk(g_split_mu);
+  return g_split_items;
+}
+
 template <int V, int TW, bool FULL, bool PLAN>
 static void bwd_wide_go3(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
   using Sh = WideShape<V, TW, FULL>;
+  if (a.plan.n_items < split_items()) {
+    if (dx && a.rows > 0) {
+      int64_t g = (a.rows + Sh::S - 1) / Sh::S;
+      if (g > grid_cap()) g = grid_cap();
+      bwd_dx_rows_kernel<V, TW, FULL, PLAN><<<dim3((unsigned)g), dim3(Sh::THREADS), 0, st>>>(a);
+    }
+    if (dw && a.plan.n_items > 0) {
+      const dim3 grid((unsigned)a.plan.n_items, (unsigned)((a.hidden / 8 + 63) / 64));
+      dw_cols_kernel<PLAN><<<grid, dim3(256), 0, st>>>(a);
+    }
+    return;
+  }
   const int pad_groups = dx ? (a.plan.n_pad + Sh::WAVES - 1) / Sh::WAVES : 0;
   const dim3 grid((unsigned)(a.plan.n_items + pad_groups)), block(Sh::THREADS);
   if (dx && dw) bwd_wide_kernel<V, TW, FULL, PLAN, true, true><<<grid, block, 0, st>>>(a);

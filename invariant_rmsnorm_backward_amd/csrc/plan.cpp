@@ -79,13 +79,29 @@ void AccHost::init(int64_t T, int64_t H) {
   nb = num_blocks(T);
   covered.assign(static_cast<size_t>(T), 0);
   block_state.assign(static_cast<size_t>(nb), kBlockNone);
+  n_covered = 0;
+  n_spilled = 0;
+  identity_call = false;
+  dirty = false;
   finalized = false;
 }
 
 void AccHost::reset() {
-  std::fill(covered.begin(), covered.end(), 0);
-  std::fill(block_state.begin(), block_state.end(), kBlockNone);
+  if (dirty) {
+    std::fill(covered.begin(), covered.end(), 0);
+    std::fill(block_state.begin(), block_state.end(), kBlockNone);
+  }
+  n_covered = 0;
+  n_spilled = 0;
+  identity_call = false;
+  dirty = false;
   finalized = false;
+}
+
+static int64_t first_set(const std::vector<uint8_t>& v) {
+  for (size_t i = 0; i < v.size(); ++i)
+    if (v[i]) return static_cast<int64_t>(i);
+  return -1;
 }
 
 int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err) {
@@ -99,14 +115,13 @@ int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err)
              ") == n_logical (" + std::to_string(n_logical) + ")";
       return kELayout;
     }
-    for (int64_t l = 0; l < rows; ++l) {
-      if (covered[l]) {
-        *err = "logical row " + std::to_string(l) + " already contributed";
-        return kECoverage;
-      }
+    if (n_covered > 0) {
+      const int64_t l = identity_call ? 0 : first_set(covered);
+      *err = "logical row " + std::to_string(l) + " already contributed";
+      return kECoverage;
     }
-    std::memset(covered.data(), 1, covered.size());
-    std::fill(block_state.begin(), block_state.end(), kBlockDirect);
+    identity_call = true;
+    n_covered = n_logical;
     return kOk;
   }
   if (plan->n_logical != n_logical) {
@@ -115,29 +130,37 @@ int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err)
     return kELayout;
   }
   for (int32_t l : plan->logical_rows) {
-    if (covered[l]) {
+    if (identity_call || covered[l]) {
       *err = "logical row " + std::to_string(l) + " already contributed";
       return kECoverage;
     }
   }
+  if (!plan->logical_rows.empty() || !plan->item_info.empty()) dirty = true;
   for (int32_t l : plan->logical_rows) covered[l] = 1;
+  n_covered += static_cast<int64_t>(plan->logical_rows.size());
   for (int32_t info : plan->item_info) {
-    if (info >= 0) block_state[info] = kBlockDirect;
-    else block_state[~info] = kBlockSpilled;
+    if (info >= 0) {
+      block_state[info] = kBlockDirect;
+    } else if (block_state[~info] != kBlockSpilled) {
+      block_state[~info] = kBlockSpilled;
+      ++n_spilled;
+    }
   }
   return kOk;
 }
 
 int AccHost::prepare_finalize(std::vector<int32_t>* spilled, std::string* err) const {
-  for (int64_t l = 0; l < n_logical; ++l) {
-    if (covered[l] != 1) {
-      *err = "logical row " + std::to_string(l) + " has not contributed";
-      return kECoverage;
-    }
+  if (n_covered != n_logical) {
+    // rows are registered at most once, so fewer than n_logical means a gap
+    int64_t l = 0;
+    while (l < n_logical && covered[l]) ++l;
+    *err = "logical row " + std::to_string(l) + " has not contributed";
+    return kECoverage;
   }
   spilled->clear();
-  for (int64_t b = 0; b < nb; ++b)
-    if (block_state[b] == kBlockSpilled) spilled->push_back(static_cast<int32_t>(b));
+  if (n_spilled > 0)
+    for (int64_t b = 0; b < nb; ++b)
+      if (block_state[b] == kBlockSpilled) spilled->push_back(static_cast<int32_t>(b));
   return kOk;
 }
 

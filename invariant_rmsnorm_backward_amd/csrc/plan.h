@@ -54,12 +54,19 @@ int build_plan(const int32_t* row_logical, int64_t rows, int64_t n_logical, Plan
 
 enum BlockState : uint8_t { kBlockNone = 0, kBlockDirect = 1, kBlockSpilled = 2 };
 
+// Coverage bookkeeping costs O(1) for a call with the identity map and
+// O(rows of the call) for a call with a layout; the per-row state is only
+// scanned to name the offending row when a check fails.
 struct AccHost {
   int64_t n_logical = 0;
   int64_t hidden = 0;
   int64_t nb = 0;
-  std::vector<uint8_t> covered;       // per logical row: contributions so far (0/1)
-  std::vector<uint8_t> block_state;   // per block: BlockState
+  std::vector<uint8_t> covered;       // per logical row: contributed (0/1), layout calls only
+  std::vector<uint8_t> block_state;   // per block: BlockState, layout calls only
+  int64_t n_covered = 0;              // logical rows that have contributed
+  int64_t n_spilled = 0;              // blocks marked kBlockSpilled
+  bool identity_call = false;         // an identity-map call covered every row
+  bool dirty = false;                 // covered / block_state were written
   bool finalized = false;
 
   void init(int64_t T, int64_t H);

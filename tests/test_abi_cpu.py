@@ -106,7 +106,8 @@ def test_no_atomics_and_no_fallbacks_in_the_library_sources():
         assert not re.search(r"\batomic\w*\s*\(|__atomic|std::atomic|__hip_atomic", code), name
         assert "__CUDA" not in code and "cuda_runtime" not in code, name
         assert "__HIP_PLATFORM" not in code, name
-    # variant selection keys on the hidden size only
+    # the arithmetic variant (lane groups, wavefronts per row, chunks per lane)
+    # keys on the hidden size only
     k = open(os.path.join(csrc, "kernels.hip")).read()
     for fn in ("small_lanes", "wide_tw", "wide_v"):
         sig = re.search(rf"static int {fn}\(([^)]*)\)", k).group(1)
@@ -121,3 +122,14 @@ def test_product_code_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "liboracle" not in text, f
+
+
+def test_split_threshold_knob():
+    """The backward's work-distribution threshold: set, read back, restore."""
+    prev = binding.rmsnorm_set_split_threshold(5)
+    try:
+        assert binding.rmsnorm_set_split_threshold(0) == 5
+        assert binding.rmsnorm_set_split_threshold(-1) == 0      # negative: back to the default
+        assert binding.rmsnorm_set_split_threshold(prev) > 0
+    finally:
+        binding.rmsnorm_set_split_threshold(prev)

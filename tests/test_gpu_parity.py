@@ -20,6 +20,20 @@ def _gpu():
     binding.load()
 
 
+# The backward for hidden > 256 has two work distributions with the same
+# arithmetic: the fused kernel (one workgroup per canonical block) and the
+# two-pass path that calls touching few blocks take.  Tests that take this
+# fixture run on each, forced through the split threshold.
+BWD_PATHS = {"fused": 0, "two_pass": 1 << 40}
+
+
+@pytest.fixture(params=sorted(BWD_PATHS))
+def bwd_path(request):
+    prev = binding.rmsnorm_set_split_threshold(BWD_PATHS[request.param])
+    yield request.param
+    binding.rmsnorm_set_split_threshold(prev)
+
+
 def _run(op, cells, data, ref, name):
     print(f"[parity] {name}: {len(cells)} cells", flush=True)
     rep = harness.assert_gradient_batch_invariant(op, cells, CONTRACT, data=data, reference=ref,
@@ -57,14 +71,14 @@ WIDE_CASES = {
 
 
 @pytest.mark.parametrize("case", sorted(WIDE_CASES))
-def test_rms_norm_parity_and_invariance(case):
+def test_rms_norm_parity_and_invariance(case, bwd_path):
     base, H, lengths, chunk = WIDE_CASES[case]
     wl = inputs.scaled(base(), f"{case}_t{sum(lengths)}", hidden=H, lengths=lengths, pad_rows=0)
     data = pu.make_data(wl)
     ref = pu.oracle_reference(wl)
     cells = pu.standard_cells(wl, chunk)
     ad = adapters.RmsNormAdapter()
-    rep = _run(ad, cells, data, ref, case)
+    rep = _run(ad, cells, data, ref, f"{case} ({bwd_path})")
     _check_call_log(ad.call_log, cells)
     # diagnostics that are reported, not gated: bf16 outputs within one ulp of FP64
     out = ad.run_cell(cells[0], data)
@@ -131,7 +145,7 @@ def test_inactive_rows_do_not_change_dweight_bits():
 @pytest.mark.parametrize("H,lengths", [(8, [59]), (128, [200, 77]), (4096, [130, 70]),
                                        (5120, [100, 29]), (1000, [64, 1]), (8192, [66, 70]),
                                        (9000, [40, 41]), (8, [40000]), (16, [70000, 33001])])
-def test_dweight_is_the_canonical_order_bit_for_bit(H, lengths):
+def test_dweight_is_the_canonical_order_bit_for_bit(H, lengths, bwd_path):
     """Tree conformance: given the same FP32 rstd, the GPU dweight equals the
     oracle's FP32 emulation of CDO-v1 bit for bit, for one call and for
     chunked calls."""
@@ -162,7 +176,7 @@ def test_dweight_is_the_canonical_order_bit_for_bit(H, lengths):
         got = acc.finalize().cpu().numpy()
         torch.cuda.synchronize()
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (H, cell.name)
-    print(f"[cdo] H={H}: GPU dweight == CDO-v1 emulation bit for bit", flush=True)
+    print(f"[cdo] H={H} ({bwd_path}): GPU dweight == CDO-v1 emulation bit for bit", flush=True)
 
 
 def test_fused_dweight_equals_dweight_only_path():
@@ -179,6 +193,46 @@ def test_fused_dweight_equals_dweight_only_path():
     assert np.array_equal(d1.view(np.uint32), d2.view(np.uint32))
 
 
+@pytest.mark.parametrize("case", ["h4096", "h5120", "h512", "h1000_masked", "h6144_two_waves",
+                                  "h9000_two_waves_masked"])
+def test_two_pass_backward_is_bitwise_the_fused_one(case):
+    """Every cell (partial blocks, spills, padding, permutations) gives the
+    same dx, dweight, y and rstd bits on both work distributions, so a cell
+    whose calls take different paths stays invariant."""
+    base, H, lengths, chunk = WIDE_CASES[case]
+    wl = inputs.scaled(base(), f"{case}_paths", hidden=H, lengths=lengths, pad_rows=0)
+    data = pu.make_data(wl)
+    cells = pu.standard_cells(wl, chunk)
+    outs = {}
+    for path, thr in BWD_PATHS.items():
+        prev = binding.rmsnorm_set_split_threshold(thr)
+        try:
+            ad = adapters.RmsNormAdapter()
+            outs[path] = [ad.run_cell(c, data) for c in cells]
+        finally:
+            binding.rmsnorm_set_split_threshold(prev)
+    for c, a, b in zip(cells, outs["fused"], outs["two_pass"]):
+        for t in ("dx", "dweight", "y", "rstd"):
+            assert np.array_equal(a[t].view(np.uint8), b[t].view(np.uint8)), (case, c.name, t)
+    # dx alone and the dweight contributions alone take the same two paths
+    T = wl.n_logical
+    _, rstd = binding.fwd(data.x, data.w, data.eps)
+    got = {}
+    for path, thr in BWD_PATHS.items():
+        prev = binding.rmsnorm_set_split_threshold(thr)
+        try:
+            acc = binding.DwAccumulator(T, H)
+            binding.dw_contrib(data.x, data.dy, rstd, acc)
+            got[path] = (binding.bwd(data.x, data.w, data.dy, rstd).view(torch.int16).cpu(),
+                         acc.finalize().view(torch.int32).cpu())
+            acc.close()
+        finally:
+            binding.rmsnorm_set_split_threshold(prev)
+    assert torch.equal(got["fused"][0], got["two_pass"][0])
+    assert torch.equal(got["fused"][1], got["two_pass"][1])
+    print(f"[paths] {case}: fused == two-pass bitwise over {len(cells)} cells", flush=True)
+
+
 def test_run_to_run_repeatability():
     wl = inputs.scaled(inputs.workload_h4096(), "repeat", lengths=[700, 300])
     data = pu.make_data(wl)
@@ -191,7 +245,7 @@ def test_run_to_run_repeatability():
 
 
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 129])
-def test_small_and_ragged_row_counts(T):
+def test_small_and_ragged_row_counts(T, bwd_path):
     wl = inputs.scaled(inputs.workload_h4096(), f"ragged_{T}", hidden=768, lengths=[T])
     data = pu.make_data(wl)
     ref = pu.oracle_reference(wl)
