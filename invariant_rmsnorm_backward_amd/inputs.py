@@ -23,6 +23,7 @@ Distributions (the input recipe):
   dy : active * U[-1, 1) / N_active, rounded to bf16; N_active = number of
        active tokens of the whole logical multiset (mean over active tokens)
   mask (density < 1): Bernoulli(density) per (sample, pos)
+  W  (linear-layer workloads, [out, in]): U[-1, 1) / sqrt(in), rounded to bf16
 """
 from __future__ import annotations
 
@@ -40,6 +41,7 @@ _M2 = 0x94D049BB133111EB
 
 # Tensor tags of the counter (8 bits).
 TAG_X, TAG_W, TAG_DY, TAG_MASK, TAG_LEN, TAG_COMP, TAG_PERM, TAG_PADCOMP = 1, 2, 3, 4, 5, 6, 7, 8
+TAG_WMAT = 9       # weight matrix of a linear-layer workload
 TAG_K_OFFSET = 16  # K-side tensors of a QK-norm workload use tag + 16
 
 
@@ -110,6 +112,7 @@ class Workload:
     tag_offset: int = 0               # separates the Q and K tensors of a QK-norm
     mask_density: float = 1.0         # fraction of active tokens
     pad_rows: int = 0                 # padding rows of the packed physical layout
+    out_features: int = 0             # linear-layer workloads: N (hidden is the input width K)
     description: str = ""
 
     @property
@@ -123,6 +126,11 @@ class Workload:
     @property
     def n_samples(self) -> int:
         return len(self.lengths)
+
+    @property
+    def dy_cols(self) -> int:
+        """Columns of the upstream gradient: the output width."""
+        return self.out_features or self.hidden
 
 
 def token_offsets(lengths: Sequence[int]) -> np.ndarray:
@@ -208,11 +216,24 @@ def workload_h5120() -> Workload:
 
 
 def scaled(wl: Workload, name: str, hidden: Optional[int] = None,
-           lengths: Optional[Sequence[int]] = None, pad_rows: Optional[int] = None) -> Workload:
+           lengths: Optional[Sequence[int]] = None, pad_rows: Optional[int] = None,
+           out_features: Optional[int] = None) -> Workload:
     """A smaller variant of a workload (same seed/recipe) for fast parity runs."""
     return dataclasses.replace(wl, name=name, hidden=hidden or wl.hidden,
                                lengths=tuple(lengths) if lengths is not None else wl.lengths,
-                               pad_rows=wl.pad_rows if pad_rows is None else pad_rows)
+                               pad_rows=wl.pad_rows if pad_rows is None else pad_rows,
+                               out_features=wl.out_features if out_features is None
+                               else out_features)
+
+
+def workload_linear() -> Workload:
+    return Workload("linear_h4096_o4096_t32768", 4096, (4096,) * 8, _seed(6), out_features=4096,
+                    description="linear layer 4096 -> 4096, 8 x 4096 tokens, all active")
+
+
+LINEAR_WORKLOADS = {
+    "linear_h4096_o4096_t32768": workload_linear,
+}
 
 
 ALL_WORKLOADS = {
@@ -266,9 +287,10 @@ def _row_keys(wl: Workload, tag: int, rows: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(k.astype(np.int64)).to(device)
 
 
-def _hash_rows(wl: Workload, tag: int, rows: np.ndarray, device) -> torch.Tensor:
+def _hash_rows(wl: Workload, tag: int, rows: np.ndarray, device, ncols: Optional[int] = None
+               ) -> torch.Tensor:
     rk = _row_keys(wl, tag, rows, device)
-    cols = torch.arange(wl.hidden, dtype=torch.int64, device=device)
+    cols = torch.arange(wl.hidden if ncols is None else ncols, dtype=torch.int64, device=device)
     return mix64_t((rk[:, None] | cols[None, :]) ^ _signed(seed_mix(wl.seed)))
 
 
@@ -307,13 +329,27 @@ def gen_dy(wl: Workload, rows: Optional[np.ndarray] = None, device="cpu",
     n_act = n_active(wl) if denominator is None else int(denominator)
     s, p, _ = logical_keys(wl, rows)
     act = torch.from_numpy(active_mask(wl, s, p).astype(np.float64)).to(device)
-    out = torch.empty((len(rows), wl.hidden), dtype=torch.bfloat16, device=device)
+    out = torch.empty((len(rows), wl.dy_cols), dtype=torch.bfloat16, device=device)
     for a in range(0, len(rows), chunk):
-        z = _hash_rows(wl, TAG_DY, rows[a:a + chunk], device)
+        z = _hash_rows(wl, TAG_DY, rows[a:a + chunk], device, wl.dy_cols)
         u = (_lsr(z, 40) - (1 << 23)).to(torch.float64) / float(1 << 23)   # exact, [-1, 1)
         g = (u * act[a:a + chunk, None]) / float(n_act)                       # one rounding
         out[a:a + chunk] = _bits_to_bf16_tensor(_f32_to_bf16_bits(g.to(torch.float32)))
     return out
+
+
+def gen_wmat(wl: Workload, device="cpu") -> torch.Tensor:
+    """Weight matrix W[out_features, hidden] (bf16) of a linear-layer workload,
+    U[-1, 1) / sqrt(hidden), keyed by (row, column)."""
+    assert wl.out_features > 0
+    n, k = wl.out_features, wl.hidden
+    rows = torch.arange(n, dtype=torch.int64, device=device)
+    cols = torch.arange(k, dtype=torch.int64, device=device)
+    key = ((TAG_WMAT + wl.tag_offset) << 50) | (rows[:, None] << 22) | cols[None, :]
+    z = mix64_t(key ^ _signed(seed_mix(wl.seed)))
+    u = (_lsr(z, 40) - (1 << 23)).to(torch.float64) / float(1 << 23)      # exact, [-1, 1)
+    f = (u / math.sqrt(k)).to(torch.float32)                             # one rounding
+    return _bits_to_bf16_tensor(_f32_to_bf16_bits(f))
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

@@ -1,12 +1,13 @@
-"""FP64 CPU oracle for RMSNorm forward/backward and the CDO-v1 dweight order.
+"""FP64 CPU oracle for RMSNorm forward/backward, the CDO-v1 dweight order and
+the backward of a linear layer (dX, dW).
 
 TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
 with the HIP library (``invariant_rmsnorm_backward_amd``) and never imports it.
 
-The arithmetic lives in ``rmsnorm_oracle.c`` (plain C, FP64, single thread);
-this module only marshals numpy arrays.  See the C file's header for the
-definitions followed and the pins that check them.
+The arithmetic lives in ``rmsnorm_oracle.c`` and ``linear_oracle.c`` (plain C,
+FP64, single thread); this module only marshals numpy arrays.  See the C
+files' headers for the definitions followed and the pins that check them.
 """
 from __future__ import annotations
 
@@ -19,6 +20,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "rmsnorm_oracle.c")
+SRCS = [SRC, os.path.join(_HERE, "linear_oracle.c")]
 LIB_PATH = os.path.join(_HERE, "liboracle_rmsnorm.so")
 
 # -ffp-contract=off and no fast-math: each float operation rounds once, as written.
@@ -27,9 +29,13 @@ GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", 
 _lib = None
 
 
-def build(src: str = SRC, out: str = LIB_PATH) -> str:
-    """Compile an oracle library with gcc; returns its path."""
-    subprocess.run(["gcc", *GCC_FLAGS, src, "-o", out, "-lm"], check=True)
+def build(src=None, out: str = LIB_PATH) -> str:
+    """Compile an oracle library with gcc; returns its path.  ``src`` replaces
+    the RMSNorm source (the pin tests build deliberately broken copies)."""
+    srcs = list(SRCS)
+    if src is not None:
+        srcs = [src] + SRCS[1:] if not isinstance(src, (list, tuple)) else list(src)
+    subprocess.run(["gcc", *GCC_FLAGS, *srcs, "-o", out, "-lm"], check=True)
     return out
 
 
@@ -44,13 +50,20 @@ def _bind(lib):
     lib.oracle_rmsnorm_bwd.restype = ctypes.c_int
     lib.oracle_cdo_v1_dweight_f32.argtypes = [P, P, P, I64, I64, P, I64, P]
     lib.oracle_cdo_v1_dweight_f32.restype = ctypes.c_int
+    lib.oracle_linear_fwd.argtypes = [P, P, I64, I64, I64, P, P]
+    lib.oracle_linear_fwd.restype = ctypes.c_int
+    lib.oracle_linear_bwd.argtypes = [P, P, P, I64, I64, I64, P, I64, P, P, P]
+    lib.oracle_linear_bwd.restype = ctypes.c_int
+    lib.oracle_linear_sample.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, P]
+    lib.oracle_linear_sample.restype = ctypes.c_int
     return lib
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC):
+        if not os.path.exists(LIB_PATH) or any(os.path.getmtime(LIB_PATH) < os.path.getmtime(f)
+                                               for f in SRCS):
             build()
         _lib = _bind(ctypes.CDLL(LIB_PATH))
     return _lib
@@ -149,6 +162,57 @@ class Oracle:
                "oracle_cdo_v1_dweight_f32")
         return out
 
+    # ------------------------------------------------------------- linear layer
+    def linear_fwd_bf16(self, x_bits, w_bits, row_logical=None) -> np.ndarray:
+        """y = x W^T in FP64 from raw bf16 x[rows, K], W[N, K]; padding rows 0."""
+        x = _c(x_bits, np.uint16)
+        w = _c(w_bits, np.uint16)
+        rows, k = x.shape
+        n = w.shape[0]
+        assert w.shape == (n, k)
+        rl = None if row_logical is None else _c(row_logical, np.int32)
+        y = np.empty((rows, n), dtype=np.float64)
+        _check(self._lib().oracle_linear_fwd(_ptr(x), _ptr(w), rows, n, k, _ptr(rl), _ptr(y)),
+               "oracle_linear_fwd")
+        return y
+
+    def linear_bwd_bf16(self, x_bits, w_bits, dy_bits, row_logical=None, n_logical=None):
+        """(dX, dW, |dW|) in FP64 from raw bf16 x[rows, K], W[N, K], dY[rows, N].
+        dX is per physical row (padding rows 0); dW sums the rows the call
+        holds in ascending logical index; |dW| is the matching sum of
+        absolute terms (an error scale)."""
+        x = _c(x_bits, np.uint16)
+        w = _c(w_bits, np.uint16)
+        dy = _c(dy_bits, np.uint16)
+        rows, k = x.shape
+        n = w.shape[0]
+        assert w.shape == (n, k) and dy.shape == (rows, n)
+        rl = None if row_logical is None else _c(row_logical, np.int32)
+        nl = rows if n_logical is None else int(n_logical)
+        dx = np.empty((rows, k), dtype=np.float64)
+        dw = np.empty((n, k), dtype=np.float64)
+        dwa = np.empty((n, k), dtype=np.float64)
+        _check(self._lib().oracle_linear_bwd(_ptr(x), _ptr(w), _ptr(dy), rows, n, k, _ptr(rl), nl,
+                                             _ptr(dx), _ptr(dw), _ptr(dwa)), "oracle_linear_bwd")
+        return dx, dw, dwa
+
+    def linear_sample_bf16(self, x_bits, w_bits, dy_bits, kind, ia, ib) -> np.ndarray:
+        """Single outputs of an identity-layout call: kind 0 = dX[ia][ib],
+        1 = dW[ia][ib], 2 = |dW|[ia][ib]."""
+        x = _c(x_bits, np.uint16)
+        w = _c(w_bits, np.uint16)
+        dy = _c(dy_bits, np.uint16)
+        rows, k = x.shape
+        n = w.shape[0]
+        kd = _c(kind, np.int32)
+        a = _c(ia, np.int64)
+        b = _c(ib, np.int64)
+        out = np.empty(len(kd), dtype=np.float64)
+        _check(self._lib().oracle_linear_sample(_ptr(x), _ptr(w), _ptr(dy), rows, n, k, len(kd),
+                                                _ptr(kd), _ptr(a), _ptr(b), _ptr(out)),
+               "oracle_linear_sample")
+        return out
+
 
 def load_library(path: str) -> Oracle:
     """Bind another build of the oracle source (the pin tests use this on
@@ -163,3 +227,6 @@ rmsnorm_bwd = _default.rmsnorm_bwd
 rmsnorm_fwd_bf16 = _default.rmsnorm_fwd_bf16
 rmsnorm_bwd_bf16 = _default.rmsnorm_bwd_bf16
 cdo_v1_dweight_f32 = _default.cdo_v1_dweight_f32
+linear_fwd_bf16 = _default.linear_fwd_bf16
+linear_bwd_bf16 = _default.linear_bwd_bf16
+linear_sample_bf16 = _default.linear_sample_bf16

@@ -1,8 +1,9 @@
 """The oracle's pins catch plausible mistakes.
 
-Each case copies ``oracle/rmsnorm_oracle.c`` to a temporary directory, plants
-one mistake by a textual edit, builds the copy with gcc and runs every pin
-against it on the CPU.  At least one pin must fail for every mutant; the
+Each case copies an oracle source (``oracle/rmsnorm_oracle.c`` or
+``oracle/linear_oracle.c``) to a temporary directory, plants one mistake by a
+textual edit, builds the copy with gcc and runs every pin against it on the
+CPU.  At least one pin must fail for every mutant; the
 unmodified source must pass them all.
 """
 import inspect
@@ -41,9 +42,24 @@ MUTANTS = {
 }
 
 
+LINEAR_MUTANTS = {
+    "linear_dx_mirrored_weight_index": ("lin_widen(dy[r * n + o]) * lin_widen(w[o * k + i]);\n            dx",
+                                        "lin_widen(dy[r * n + o]) * lin_widen(w[o * k + (k - 1 - i)]);\n            dx"),
+    "linear_dw_drops_last_logical_row": ("for (int64_t l = 0; l < n_logical; ++l) {\n        const int64_t p = inv[l];",
+                                         "for (int64_t l = 0; l + 1 < n_logical; ++l) {\n        const int64_t p = inv[l];"),
+    "linear_dw_wrong_sign": ("dw[o * k + i] += c;", "dw[o * k + i] -= c;"),
+    "linear_dw_uses_physical_row_of_wrong_tensor": ("const double c = g * lin_widen(x[p * k + i]);",
+                                                    "const double c = g * lin_widen(x[(l < rows ? l : p) * k + i]);"),
+    "linear_fwd_transposed_weight": ("s += lin_widen(x[r * k + i]) * lin_widen(w[o * k + i]);",
+                                     "s += lin_widen(x[r * k + i]) * lin_widen(w[(i % n) * k + (o % k)]);"),
+    "linear_pad_rows_read": ("        const int pad = row_logical && row_logical[r] < 0;\n        for (int64_t i = 0; i < k; ++i) {",
+                             "        const int pad = 0;\n        for (int64_t i = 0; i < k; ++i) {"),
+}
+
+
 def _run_all_pins(orc):
     failures = []
-    for pin in pins.PINS:
+    for pin in list(pins.PINS) + list(pins.LINEAR_PINS):
         args = [orc]
         if "eps" in inspect.signature(pin).parameters:
             args.append(1e-6)
@@ -54,17 +70,21 @@ def _run_all_pins(orc):
     return failures
 
 
-def _build_variant(tmp_path, name, edit):
-    with open(oracle.SRC) as f:
-        src = f.read()
-    if edit is not None:
-        old, new = edit
-        assert src.count(old) >= 1, f"mutation anchor for {name} not found"
-        src = src.replace(old, new, 1)
-    path = os.path.join(str(tmp_path), f"{name}.c")
-    with open(path, "w") as f:
-        f.write(src)
-    return oracle.load_library(oracle.build(path, os.path.join(str(tmp_path), f"lib{name}.so")))
+def _build_variant(tmp_path, name, edit, which=0):
+    """Build the oracle with source ``which`` (index into oracle.SRCS) edited."""
+    srcs = []
+    for i, src_path in enumerate(oracle.SRCS):
+        with open(src_path) as f:
+            src = f.read()
+        if edit is not None and i == which:
+            old, new = edit
+            assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+            src = src.replace(old, new, 1)
+        path = os.path.join(str(tmp_path), f"{name}_{i}.c")
+        with open(path, "w") as f:
+            f.write(src)
+        srcs.append(path)
+    return oracle.load_library(oracle.build(srcs, os.path.join(str(tmp_path), f"lib{name}.so")))
 
 
 def test_unmodified_source_passes_every_pin(tmp_path):
@@ -74,4 +94,10 @@ def test_unmodified_source_passes_every_pin(tmp_path):
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(tmp_path, name):
     failures = _run_all_pins(_build_variant(tmp_path, name, MUTANTS[name]))
+    assert failures, f"no pin caught the planted mistake {name}"
+
+
+@pytest.mark.parametrize("name", sorted(LINEAR_MUTANTS))
+def test_linear_mutant_is_caught(tmp_path, name):
+    failures = _run_all_pins(_build_variant(tmp_path, name, LINEAR_MUTANTS[name], which=1))
     assert failures, f"no pin caught the planted mistake {name}"

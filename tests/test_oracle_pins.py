@@ -343,6 +343,155 @@ def pin_cdo_v1_within_fp32_error_bound_of_fp64(orc):
     assert np.all(np.abs(got - ref) <= depth * 2.0 ** -24 * scale * 1.01)
 
 
+# -------------------------------------------------------- linear layer (GEMM)
+def _bits(vals) -> np.ndarray:
+    """bf16 bit patterns of float values that bf16 represents exactly."""
+    f = np.asarray(vals, dtype=np.float32)
+    u = f.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value not exactly representable in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def _val(bits) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _rand_bf16(rng, shape, scale=1.0):
+    """Random bf16 patterns of N(0, scale^2) values (rounded by truncation)."""
+    f = (rng.normal(size=shape) * scale).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def pin_linear_brute_force_tiny(orc):
+    """Triple loops in Python floats over values k/8 in [-2, 2]: every partial
+    sum is exact, so the oracle must agree bit for bit."""
+    rng = _rng(20)
+    R, N, K = 5, 3, 4
+    x = _bits(rng.integers(-16, 17, size=(R, K)) / 8.0)
+    w = _bits(rng.integers(-16, 17, size=(N, K)) / 8.0)
+    dy = _bits(rng.integers(-16, 17, size=(R, N)) / 8.0)
+    X, W, DY = _val(x), _val(w), _val(dy)
+    y = [[sum(X[r][k] * W[n][k] for k in range(K)) for n in range(N)] for r in range(R)]
+    dx = [[sum(DY[r][n] * W[n][k] for n in range(N)) for k in range(K)] for r in range(R)]
+    dw = [[sum(DY[r][n] * X[r][k] for r in range(R)) for k in range(K)] for n in range(N)]
+    np.testing.assert_array_equal(orc.linear_fwd_bf16(x, w), np.array(y))
+    gdx, gdw, gabs = orc.linear_bwd_bf16(x, w, dy)
+    np.testing.assert_array_equal(gdx, np.array(dx))
+    np.testing.assert_array_equal(gdw, np.array(dw))
+    absum = [[sum(abs(DY[r][n] * X[r][k]) for r in range(R)) for k in range(K)] for n in range(N)]
+    np.testing.assert_array_equal(gabs, np.array(absum))
+
+
+def pin_linear_single_row_is_an_outer_product(orc):
+    rng = _rng(21)
+    x = _rand_bf16(rng, (1, 7))
+    w = _rand_bf16(rng, (5, 7))
+    dy = _rand_bf16(rng, (1, 5))
+    _, dw, _ = orc.linear_bwd_bf16(x, w, dy)
+    np.testing.assert_array_equal(dw, np.outer(_val(dy)[0], _val(x)[0]))   # products of bf16 are exact
+
+
+def pin_linear_identity_weight(orc):
+    rng = _rng(22)
+    K = 6
+    x = _rand_bf16(rng, (9, K))
+    dy = _rand_bf16(rng, (9, K))
+    w = _bits(np.eye(K))
+    np.testing.assert_array_equal(orc.linear_fwd_bf16(x, w), _val(x))
+    dx, _, _ = orc.linear_bwd_bf16(x, w, dy)
+    np.testing.assert_array_equal(dx, _val(dy))
+
+
+def pin_linear_trace_identity(orc):
+    """<dY, X W^T> = <dW, W> = <dX, X>: the forward, dW and dX agree."""
+    rng = _rng(23)
+    R, N, K = 37, 11, 13
+    x, w, dy = _rand_bf16(rng, (R, K)), _rand_bf16(rng, (N, K)), _rand_bf16(rng, (R, N))
+    y = orc.linear_fwd_bf16(x, w)
+    dx, dw, _ = orc.linear_bwd_bf16(x, w, dy)
+    a = float(np.sum(_val(dy) * y))
+    b = float(np.sum(dw * _val(w)))
+    c = float(np.sum(dx * _val(x)))
+    scale = float(np.sum(np.abs(_val(dy)) @ np.abs(_val(w)) * np.abs(_val(x)).sum(0) / R)) + 1.0
+    assert abs(a - b) <= 1e-12 * scale and abs(a - c) <= 1e-12 * scale
+
+
+def pin_linear_finite_differences(orc):
+    """L = <dY, X W^T> is bilinear, so moving one entry of W (or X) to its
+    neighbouring bf16 value, a change d, changes L by exactly d * dW (or
+    d * dX) up to FP64 rounding."""
+    rng = _rng(24)
+    R, N, K = 9, 4, 6
+    x, w, dy = _rand_bf16(rng, (R, K)), _rand_bf16(rng, (N, K)), _rand_bf16(rng, (R, N))
+    dx, dw, _ = orc.linear_bwd_bf16(x, w, dy)
+
+    def L(xb, wb):
+        return float(np.sum(_val(dy) * orc.linear_fwd_bf16(xb, wb)))
+
+    base = L(x, w)
+    for n in range(N):
+        for k in range(K):
+            w2 = w.copy()
+            w2[n, k] = w[n, k] + 1          # the neighbouring bf16 value
+            d = _val(w2[n, k]) - _val(w[n, k])
+            if d == 0:
+                continue
+            assert abs((L(x, w2) - base) / d - dw[n, k]) <= 1e-9 * (1 + abs(dw[n, k])), (n, k)
+    for r in range(R):
+        for k in range(K):
+            x2 = x.copy()
+            x2[r, k] = x[r, k] + 1
+            d = _val(x2[r, k]) - _val(x[r, k])
+            if d == 0:
+                continue
+            assert abs((L(x2, w) - base) / d - dx[r, k]) <= 1e-9 * (1 + abs(dx[r, k])), (r, k)
+
+
+def pin_linear_padding_and_layout_invariance(orc):
+    rng = _rng(25)
+    T, N, K = 23, 5, 8
+    x, w, dy = _rand_bf16(rng, (T, K)), _rand_bf16(rng, (N, K)), _rand_bf16(rng, (T, N))
+    dx0, dw0, _ = orc.linear_bwd_bf16(x, w, dy)
+    perm = rng.permutation(T)
+    # padding rows full of NaN patterns, interleaved with the permuted rows
+    rl = np.concatenate([perm[:10], [-1, -1], perm[10:], [-1]]).astype(np.int32)
+    xp = np.full((len(rl), K), 0x7FC1, np.uint16)
+    dyp = np.full((len(rl), N), 0x7FC1, np.uint16)
+    real = rl >= 0
+    xp[real] = x[rl[real]]
+    dyp[real] = dy[rl[real]]
+    dx1, dw1, _ = orc.linear_bwd_bf16(xp, w, dyp, rl, T)
+    np.testing.assert_array_equal(dw1, dw0)
+    assert np.all(dx1[~real] == 0)
+    np.testing.assert_array_equal(dx1[real], dx0[rl[real]])
+    y1 = orc.linear_fwd_bf16(xp, w, rl)
+    assert np.all(y1[~real] == 0)
+    with pytest.raises(oracle.OracleError):
+        orc.linear_bwd_bf16(x[:3], w, dy[:3], np.array([0, 0, 1], np.int32), 3)
+
+
+def pin_linear_samples_match_the_full_products(orc):
+    rng = _rng(26)
+    R, N, K = 31, 7, 9
+    x, w, dy = _rand_bf16(rng, (R, K)), _rand_bf16(rng, (N, K)), _rand_bf16(rng, (R, N))
+    dx, dw, dwa = orc.linear_bwd_bf16(x, w, dy)
+    kind = np.array([0, 0, 1, 1, 2], np.int32)
+    ia = np.array([3, 30, 0, 6, 4], np.int64)
+    ib = np.array([8, 0, 5, 8, 2], np.int64)
+    got = orc.linear_sample_bf16(x, w, dy, kind, ia, ib)
+    np.testing.assert_array_equal(got, [dx[3, 8], dx[30, 0], dw[0, 5], dw[6, 8], dwa[4, 2]])
+
+
+LINEAR_PINS = [pin_linear_brute_force_tiny, pin_linear_single_row_is_an_outer_product,
+               pin_linear_identity_weight, pin_linear_trace_identity, pin_linear_finite_differences,
+               pin_linear_padding_and_layout_invariance, pin_linear_samples_match_the_full_products]
+
+
+@pytest.mark.parametrize("pin", LINEAR_PINS, ids=lambda f: f.__name__)
+def test_linear_oracle_pins(pin):
+    pin(oracle)
+
+
 # ------------------------------------------------------------- the tests
 PINS = [pin_widen_bf16_exact_bit_patterns, pin_forward_constant_row_closed_form, pin_forward_zero_row_and_eps_inside_sqrt, pin_forward_two_element_worked_example, pin_forward_norm_identity_and_scale_invariance, pin_backward_matches_central_finite_differences_h8_t59, pin_backward_explicit_jacobian, pin_backward_orthogonality_and_radial_identity, pin_dweight_euler_identity, pin_h1_closed_form, pin_zero_row_backward, pin_padding_rows_are_never_read_and_contribute_nothing, pin_inactive_rows_contribute_exactly_zero, pin_oracle_is_layout_invariant, pin_invalid_layouts_are_refused, pin_cdo_v1_golden_cases, pin_cdo_v1_golden_cases_are_layout_invariant, pin_cdo_v1_exact_when_every_partial_is_representable, pin_cdo_v1_within_fp32_error_bound_of_fp64]
 

@@ -30,14 +30,14 @@ def test_oracle_under_asan_ubsan(tmp_path):
     import oracle
     from tests import test_oracle_pins as pins
     so = str(tmp_path / "liboracle_san.so")
-    subprocess.run(["gcc", *oracle.GCC_FLAGS, *SAN, oracle.SRC, "-o", so, "-lm"], check=True)
+    subprocess.run(["gcc", *oracle.GCC_FLAGS, *SAN, *oracle.SRCS, "-o", so, "-lm"], check=True)
     # the sanitizer runtime must be loaded first: run the pins in a child process
     code = (
         "import sys, inspect; sys.path.insert(0, %r)\n"
         "import oracle\n"
         "from tests import test_oracle_pins as pins\n"
         "orc = oracle.load_library(%r)\n"
-        "for pin in pins.PINS:\n"
+        "for pin in list(pins.PINS) + list(pins.LINEAR_PINS):\n"
         "    args = [orc] + ([1e-6] if 'eps' in inspect.signature(pin).parameters else [])\n"
         "    pin(*args)\n"
         "print('oracle pins under sanitizers: ok')\n" % (ROOT, so))
