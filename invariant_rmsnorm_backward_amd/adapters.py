@@ -5,7 +5,8 @@ Closeout][Backward] Reusable gradient-invariance harness and operator
 adapters", Required adapters: RMSNorm dx/dweight; "WS1 C4 (#270) closeout
 evidence", status table: rms_norm and qk_norm).  Stable gradient names:
 ``rms_norm`` -> dx, dweight (plus forward y, rstd); ``qk_norm`` -> dq, dk,
-dweight_q, dweight_k (plus yq, yk, rstd_q, rstd_k).
+dweight_q, dweight_k (plus yq, yk, rstd_q, rstd_k); ``det_gemm`` (a linear
+layer, "GEMM dX/dW" in Required adapters) -> dX, dW (plus forward y).
 
 An adapter runs the operator on each call's *physical* rows: real rows are
 gathered from the logical tensors, padding rows are filled with a NaN
@@ -166,7 +167,86 @@ class QkNormAdapter(RmsNormAdapter):
                 "pad_rows_clean": np.array([bool(q["pad_rows_clean"][0] and k["pad_rows_clean"][0])])}
 
 
+@dataclasses.dataclass
+class LinearInputs:
+    """Logical inputs of a linear layer: x[n_logical, k], W[n, k], dY[n_logical, n]."""
+    name: str
+    workload: inputs.Workload
+    x: torch.Tensor
+    w: torch.Tensor
+    dy: torch.Tensor
+    active_token_denominator: int
+    loss_reduction: str = "mean_over_active_tokens"
+
+
+def make_linear_inputs(wl: inputs.Workload, device="cuda", gen_device=None) -> LinearInputs:
+    g = device if gen_device is None else gen_device
+    return LinearInputs(wl.name, wl, inputs.gen_x(wl, device=g).to(device),
+                        inputs.gen_wmat(wl, device=g).to(device),
+                        inputs.gen_dy(wl, device=g).to(device), inputs.n_active(wl))
+
+
+class LinearAdapter(GradientAdapter):
+    """det_gemm: y = x W^T, dX = dY W, dW = dY^T X over logical rows."""
+    name = "det_gemm"
+    grad_names = ("dX", "dW")
+    forward_names = ("y",)
+    aggregation_order = "GDO-v1"
+
+    def run_cell(self, cell: Cell, data: LinearInputs) -> Dict[str, np.ndarray]:
+        x, w, dy = data.x, data.w, data.dy
+        T, K = x.shape
+        N = w.shape[0]
+        dev = x.device
+        acc = binding.GemmDwAccumulator(T, N, K)
+        y_l = torch.zeros((T, N), dtype=x.dtype, device=dev)
+        dx_l = torch.zeros_like(x)
+        pads_clean = True
+        layouts: List[binding.Layout] = []
+        for call in cell.calls:
+            self.call_log.append((cell.name, call.name, call.rows))
+            if call.row_logical is None:
+                assert call.rows == T
+                y_l.copy_(binding.gemm_fwd(x, w))
+                dx_l.copy_(binding.gemm_bwd_dx(dy, w))
+                acc.contrib(x, dy)
+                continue
+            rl = torch.from_numpy(call.row_logical.astype(np.int64)).to(dev)
+            real = rl >= 0
+            xc = _poisoned(call.rows, K, dev)
+            dyc = _poisoned(call.rows, N, dev)
+            xc[real] = x[rl[real]]
+            dyc[real] = dy[rl[real]]
+            layout = binding.Layout(call.row_logical, T)
+            layouts.append(layout)
+            y = binding.gemm_fwd(xc, w, layout)
+            dx = binding.gemm_bwd_dx(dyc, w, layout)
+            acc.contrib(xc, dyc, layout)
+            y_l[rl[real]] = y[real]
+            dx_l[rl[real]] = dx[real]
+            if bool((~real).any()):
+                pad = ~real
+                pads_clean &= bool((y[pad].view(torch.int16) == 0).all())
+                pads_clean &= bool((dx[pad].view(torch.int16) == 0).all())
+        dw = acc.finalize()
+        torch.cuda.synchronize()
+        res = {
+            "dX": dx_l.view(torch.int16).cpu().numpy().view(np.uint16),
+            "dW": dw.cpu().numpy(),
+            "y": y_l.view(torch.int16).cpu().numpy().view(np.uint16),
+            "pad_rows_clean": np.array([pads_clean]),
+        }
+        for lay in layouts:
+            lay.close()
+        acc.close()
+        return res
+
+    def provenance(self) -> dict:
+        return {"backend": binding.rmsnorm_backend_info(), "library": binding.library_path()}
+
+
 GRADIENT_ADAPTERS = {
     "rms_norm": RmsNormAdapter,
     "qk_norm": QkNormAdapter,
+    "det_gemm": LinearAdapter,
 }

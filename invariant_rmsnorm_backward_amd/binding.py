@@ -26,7 +26,9 @@ EXPORTED = ("rmsnorm_max_hidden", "rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_c
             "rmsnorm_dw_finalize", "rmsnorm_layout_create", "rmsnorm_layout_destroy",
             "rmsnorm_layout_check", "rmsnorm_dw_acc_create", "rmsnorm_dw_acc_reset",
             "rmsnorm_dw_acc_destroy", "rmsnorm_last_error", "rmsnorm_backend_info",
-            "rmsnorm_set_split_threshold")
+            "rmsnorm_set_split_threshold",
+            "det_gemm_fwd", "det_gemm_bwd_dx", "det_gemm_dw_acc_create", "det_gemm_dw_contrib",
+            "det_gemm_dw_finalize", "det_gemm_dw_acc_reset", "det_gemm_dw_acc_destroy")
 
 
 class RmsNormError(RuntimeError):
@@ -70,6 +72,13 @@ def load() -> ctypes.CDLL:
         "rmsnorm_last_error": ([], ctypes.c_char_p),
         "rmsnorm_backend_info": ([], ctypes.c_char_p),
         "rmsnorm_set_split_threshold": ([I64, ctypes.POINTER(ctypes.c_int64)], I32),
+        "det_gemm_fwd": ([P, P, P, I64, I64, I64, P, P], I32),
+        "det_gemm_bwd_dx": ([P, P, P, I64, I64, I64, P, P], I32),
+        "det_gemm_dw_acc_create": ([PP, I64, I64, I64, P], I32),
+        "det_gemm_dw_contrib": ([P, P, I64, I64, I64, P, P, P], I32),
+        "det_gemm_dw_finalize": ([P, P, P], I32),
+        "det_gemm_dw_acc_reset": ([P, P], I32),
+        "det_gemm_dw_acc_destroy": ([P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -162,6 +171,42 @@ def rmsnorm_set_split_threshold(blocks: int) -> int:
     _check(load().rmsnorm_set_split_threshold(int(blocks), ctypes.byref(prev)),
            "rmsnorm_set_split_threshold")
     return int(prev.value)
+
+
+# ---------------------------------------------------------------- det_gemm
+def det_gemm_fwd(x: int, w: int, y: int, rows: int, n: int, k: int, layout: Optional[int],
+                 stream: Optional[int]) -> None:
+    _check(load().det_gemm_fwd(x, w, y, rows, n, k, layout, stream), "det_gemm_fwd")
+
+
+def det_gemm_bwd_dx(dy: int, w: int, dx: int, rows: int, n: int, k: int, layout: Optional[int],
+                    stream: Optional[int]) -> None:
+    _check(load().det_gemm_bwd_dx(dy, w, dx, rows, n, k, layout, stream), "det_gemm_bwd_dx")
+
+
+def det_gemm_dw_acc_create(n_logical: int, n: int, k: int, stream: Optional[int]) -> int:
+    h = ctypes.c_void_p(None)
+    _check(load().det_gemm_dw_acc_create(ctypes.byref(h), n_logical, n, k, stream),
+           "det_gemm_dw_acc_create")
+    return h.value
+
+
+def det_gemm_dw_contrib(x: int, dy: int, rows: int, n: int, k: int, layout: Optional[int],
+                        acc: Optional[int], stream: Optional[int]) -> None:
+    _check(load().det_gemm_dw_contrib(x, dy, rows, n, k, layout, acc, stream),
+           "det_gemm_dw_contrib")
+
+
+def det_gemm_dw_finalize(acc: Optional[int], dw: int, stream: Optional[int]) -> None:
+    _check(load().det_gemm_dw_finalize(acc, dw, stream), "det_gemm_dw_finalize")
+
+
+def det_gemm_dw_acc_reset(acc: Optional[int], stream: Optional[int]) -> None:
+    _check(load().det_gemm_dw_acc_reset(acc, stream), "det_gemm_dw_acc_reset")
+
+
+def det_gemm_dw_acc_destroy(acc: Optional[int]) -> None:
+    _check(load().det_gemm_dw_acc_destroy(acc), "det_gemm_dw_acc_destroy")
 
 
 def current_stream() -> int:
@@ -260,3 +305,62 @@ def dw_contrib(x, dy, rstd, acc: DwAccumulator, layout: Optional[Layout] = None,
     rows, hidden = x.shape
     rmsnorm_dw_contrib(x.data_ptr(), dy.data_ptr(), rstd.data_ptr(), rows, hidden,
                        _handle(layout), acc.handle, current_stream() if stream is None else stream)
+
+
+# --------------------------------------------------------- det_gemm helpers
+class GemmDwAccumulator:
+    """Owns a canonical dW accumulator of a linear layer (n outputs, k inputs)."""
+
+    def __init__(self, n_logical: int, n: int, k: int, stream: Optional[int] = None):
+        self.n_logical, self.n, self.k = int(n_logical), int(n), int(k)
+        self.handle = det_gemm_dw_acc_create(self.n_logical, self.n, self.k,
+                                             current_stream() if stream is None else stream)
+
+    def contrib(self, x, dy, layout: Optional[Layout] = None, stream: Optional[int] = None):
+        rows = x.shape[0]
+        det_gemm_dw_contrib(x.data_ptr(), dy.data_ptr(), rows, self.n, self.k, _handle(layout),
+                            self.handle, current_stream() if stream is None else stream)
+
+    def reset(self, stream: Optional[int] = None):
+        det_gemm_dw_acc_reset(self.handle, current_stream() if stream is None else stream)
+
+    def finalize(self, dw=None, stream: Optional[int] = None):
+        import torch
+        if dw is None:
+            dw = torch.empty((self.n, self.k), dtype=torch.float32, device="cuda")
+        det_gemm_dw_finalize(self.handle, dw.data_ptr(),
+                             current_stream() if stream is None else stream)
+        return dw
+
+    def close(self):
+        if self.handle:
+            det_gemm_dw_acc_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gemm_fwd(x, w, layout: Optional[Layout] = None, y=None, stream: Optional[int] = None):
+    """y = x W^T for bf16 x[rows, k], W[n, k] (device tensors)."""
+    import torch
+    rows, k = x.shape
+    n = w.shape[0]
+    y = torch.empty((rows, n), dtype=x.dtype, device=x.device) if y is None else y
+    det_gemm_fwd(x.data_ptr(), w.data_ptr(), y.data_ptr(), rows, n, k, _handle(layout),
+                 current_stream() if stream is None else stream)
+    return y
+
+
+def gemm_bwd_dx(dy, w, layout: Optional[Layout] = None, dx=None, stream: Optional[int] = None):
+    """dX = dY W for bf16 dY[rows, n], W[n, k]."""
+    import torch
+    rows, n = dy.shape
+    k = w.shape[1]
+    dx = torch.empty((rows, k), dtype=dy.dtype, device=dy.device) if dx is None else dx
+    det_gemm_bwd_dx(dy.data_ptr(), w.data_ptr(), dx.data_ptr(), rows, n, k, _handle(layout),
+                    current_stream() if stream is None else stream)
+    return dx

@@ -9,29 +9,26 @@
 #include <vector>
 
 #include "../../include/rmsnorm_bi.h"
+#include "abi_internal.h"
 #include "kernels.h"
 #include "plan.h"
 
+namespace rbi {
+namespace abi {
+std::string& last_error() {
+  thread_local std::string err;
+  return err;
+}
+}  // namespace abi
+}  // namespace rbi
+
 namespace {
 
-thread_local std::string g_err;
-
-int fail(int code, const std::string& msg) {
-  g_err = msg;
-  return code;
-}
-
-int hip_fail(hipError_t e, const char* what) {
-  return fail(RMSNORM_EHIP, std::string(what) + ": " + hipGetErrorString(e));
-}
-
-bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  if (!a || !b || na == 0 || nb == 0) return false;
-  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-  return a0 < b0 + nb && b0 < a0 + na;
-}
+using rbi::abi::check_rows;
+using rbi::abi::check_tensor;
+using rbi::abi::fail;
+using rbi::abi::hip_fail;
+using rbi::abi::overlaps;
 
 int check_hidden(int64_t hidden) {
   if (hidden <= 0) return fail(RMSNORM_EINVAL, "hidden must be positive");
@@ -44,27 +41,7 @@ int check_hidden(int64_t hidden) {
   return RMSNORM_OK;
 }
 
-int check_rows(int64_t rows) {
-  if (rows < 0) return fail(RMSNORM_EINVAL, "rows must be non-negative");
-  if (rows > INT32_MAX) return fail(RMSNORM_EUNSUPPORTED, "rows must be below 2^31");
-  return RMSNORM_OK;
-}
-
-int check_tensor(const void* p, const char* name, size_t align) {
-  if (p == nullptr) return fail(RMSNORM_EINVAL, std::string(name) + " is NULL");
-  if (!aligned(p, align))
-    return fail(RMSNORM_EUNSUPPORTED,
-                std::string(name) + " is not " + std::to_string(align) + "-byte aligned");
-  return RMSNORM_OK;
-}
-
 }  // namespace
-
-struct rmsnorm_layout {
-  rbi::PlanHost host;
-  void* d_mem = nullptr;
-  rbi::PlanDev dev;
-};
 
 struct rmsnorm_dw_acc {
   rbi::AccHost host;
@@ -81,7 +58,7 @@ extern "C" {
 
 int rmsnorm_max_hidden(void) { return rbi::kMaxHidden; }
 
-const char* rmsnorm_last_error(void) { return g_err.c_str(); }
+const char* rmsnorm_last_error(void) { return rbi::abi::last_error().c_str(); }
 
 const char* rmsnorm_backend_info(void) {
   return "hip gfx950; cdo=v1 R=64 S=4, "

@@ -1,0 +1,347 @@
+// linear.hip -- gfx950 kernels of the batch-invariant linear-layer backward
+// (the "GEMM dX/dW" gradients of "[WS1 Closeout][Backward] Reusable
+// gradient-invariance harness and operator adapters", Required adapters).
+//
+// A linear layer y = x W^T (x[rows][K], W[N][K], bf16) has the VJP
+//     dX = dY W            row-local, [rows][N] x [N][K]
+//     dW = dY^T X          a sum over rows, [N][rows] x [rows][K]
+// "WS1 C4 (#270) closeout evidence" puts the deterministic GEMM's dW in the
+// same class as RMSNorm's dweight: a sum whose association follows the
+// physical row count is not batch invariant.  Here dW is reduced in one
+// canonical order over *logical* rows (GDO-v1):
+//   * group g = logical rows [16384 g, 16384 (g+1)); rows >= T are zero;
+//   * Q_g = the chain of v_mfma_f32_32x32x16_bf16 over the group's rows in
+//     ascending 16-row steps, accumulator starting at +0.0;
+//   * dW = perfect pairwise tree over Q_0 .. Q_{G-1}, +0.0 leaves up to the
+//     next power of two.
+// Each output element's chain is the same whatever tile or workgroup
+// computes it, and the kernel always reads the rows in logical order (the
+// caller's buffer when one call holds every row in order, else rows staged
+// by logical index), so no layout can change a bit.
+//
+// All three products run on one MFMA tile engine: 128 x 128 output tiles,
+// 4 wavefronts of 64 x 64 (2 x 2 blocks of 32 x 32), 32-deep K stages
+// double-buffered in LDS with K contiguous.  Operands whose K index is the
+// slow one in memory (W in dX, both operands of dW) are transposed on the
+// way into LDS, two K rows at a time packed into 32-bit words.
+#include "linear.h"
+
+#include <hip/hip_runtime.h>
+
+namespace rbi {
+namespace lin {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4v_t __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int LDSK = BK + 8;          // LDS row stride (bf16) of a K-contiguous tile
+constexpr int THREADS = 256;
+
+struct alignas(16) Tile {
+  uint16_t a[2][BM * LDSK];
+  uint16_t b[2][BN * LDSK];
+};
+
+__device__ __forceinline__ u32x4v_t ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4v_t*>(p);
+}
+__device__ __forceinline__ u32x4v_t ld16_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t*>(p));
+}
+
+// One operand's share of a K stage held in registers between the global
+// load and the LDS store.  Tile rows are the operand's M (or N) index.
+//   direct:     element (m, k) at g[m * ld + k]; thread t loads chunks
+//               c = t and t + 256 (row c / 4, k offset 8 * (c % 4)).
+//   transposed: element (m, k) at g[k * ld + m]; thread t loads rows
+//               k = 2p, 2p + 1 (p = t % 16) of columns 8q .. 8q + 7
+//               (q = t / 16) and packs them per column.
+template <bool TRANS>
+struct Stage {
+  u32x4v_t v[2];
+
+  // m0: first tile row; k0: first K index of the stage; m_lim / k_lim:
+  // indices at or past them read as zero; rowmap (direct only): a tile
+  // row whose map value is negative reads as zero.
+  __device__ __forceinline__ void load(const uint16_t* g, int64_t ld, int64_t m0, int64_t m_lim,
+                                       int64_t k0, int64_t k_lim, const int32_t* rowmap, int t) {
+    if (!TRANS) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = t + THREADS * i;
+        const int64_t m = m0 + (c >> 2);
+        const int64_t k = k0 + 8 * (c & 3);
+        bool ok = m < m_lim && k < k_lim;
+        if (ok && rowmap != nullptr) ok = rowmap[m] >= 0;
+        v[i] = ok ? ld16(g + m * ld + k) : u32x4v_t{0u, 0u, 0u, 0u};
+      }
+    } else {
+      const int p = t & 15, q = t >> 4;
+      const int64_t m = m0 + 8 * q;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t k = k0 + 2 * p + i;
+        const bool ok = m < m_lim && k < k_lim;
+        v[i] = ok ? ld16(g + k * ld + m) : u32x4v_t{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint16_t* s, int t) const {
+    if (!TRANS) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = t + THREADS * i;
+        *reinterpret_cast<u32x4v_t*>(s + (c >> 2) * LDSK + 8 * (c & 3)) = v[i];
+      }
+    } else {
+      const int p = t & 15, q = t >> 4;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const unsigned lo = (v[0][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;   // row 2p, column 8q + j
+        const unsigned hi = (v[1][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;   // row 2p + 1
+        *reinterpret_cast<unsigned*>(s + (8 * q + j) * LDSK + 2 * p) = lo | (hi << 16);
+      }
+    }
+  }
+};
+
+// The 64 x 64 share of wavefront w: blocks (i, j) of 32 x 32 at rows
+// wm + 32 i, columns wn + 32 j.
+struct Acc {
+  f32x16_t c[2][2];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[i][j][r] = 0.0f;
+  }
+};
+
+// Two 16-deep MFMA steps over one LDS stage, in ascending K.
+__device__ __forceinline__ void mma_stage(const uint16_t* as, const uint16_t* bs, Acc& acc,
+                                          int wm, int wn, int lane) {
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < BK; ks += 16) {
+    bf16x8_t a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      a[i] = *reinterpret_cast<const bf16x8_t*>(as + (wm + 32 * i + r) * LDSK + ks + 8 * h);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      b[j] = *reinterpret_cast<const bf16x8_t*>(bs + (wn + 32 * j + r) * LDSK + ks + 8 * h);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.c[i][j], 0, 0, 0);
+  }
+}
+
+// C[m][n] += sum over k in [k_begin, k_end) of A(m, k) B(k, n), K stages of
+// 32 in ascending order (k_end - k_begin is a multiple of 32; indices at or
+// past k_lim read as zero).
+template <bool AT, bool BT>
+__device__ __forceinline__ void gemm_tile(Tile& sm, Acc& acc, const uint16_t* a, int64_t lda,
+                                          const uint16_t* b, int64_t ldb, int64_t m0, int64_t m_lim,
+                                          int64_t n0, int64_t n_lim, int64_t k_begin, int64_t k_end,
+                                          int64_t k_lim, const int32_t* rowmap_a) {
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  Stage<AT> sa;
+  Stage<BT> sb;
+  sa.load(a, lda, m0, m_lim, k_begin, k_lim, rowmap_a, t);
+  sb.load(b, ldb, n0, n_lim, k_begin, k_lim, nullptr, t);
+  sa.store(sm.a[0], t);
+  sb.store(sm.b[0], t);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += BK) {
+    const bool more = k0 + BK < k_end;
+    if (more) {
+      sa.load(a, lda, m0, m_lim, k0 + BK, k_lim, rowmap_a, t);
+      sb.load(b, ldb, n0, n_lim, k0 + BK, k_lim, nullptr, t);
+    }
+    mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane);
+    if (more) {
+      sa.store(sm.a[buf ^ 1], t);
+      sb.store(sm.b[buf ^ 1], t);
+    }
+    __syncthreads();
+    buf ^= 1;
+  }
+}
+
+// Result of block (i, j), register e: row wm + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,
+// column wn + 32 j + lane % 32.
+template <typename F>
+__device__ __forceinline__ void for_each_result(const Acc& acc, F&& f) {
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        f(wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3), wn + 32 * j + (lane & 31),
+          acc.c[i][j][e]);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
+  const unsigned u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// y = x W^T (fwd) and dX = dY W: bf16 result rows of the call, padding rows 0.
+template <bool BT>
+__global__ __launch_bounds__(THREADS) void rowwise_kernel(RowwiseArgs p) {
+  __shared__ Tile sm;
+  const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
+  Acc acc;
+  acc.zero();
+  gemm_tile<false, BT>(sm, acc, p.a, p.lda, p.b, p.ldb, m0, p.rows, n0, p.n, 0,
+                       (p.k + BK - 1) / BK * BK, p.k, p.row_logical);
+  for_each_result(acc, [&](int mi, int ni, float v) {
+    const int64_t m = m0 + mi, n = n0 + ni;
+    if (m < p.rows && n < p.n) {
+      const bool pad = p.row_logical != nullptr && p.row_logical[m] < 0;
+      p.out[m * p.n + n] = pad ? (uint16_t)0 : to_bf16_rne(v);
+    }
+  });
+}
+
+// Q_g for one 128 x 128 tile of dW and one group g = blockIdx.z of logical
+// rows (dY and X in logical row order, T rows).
+__global__ __launch_bounds__(THREADS) void dw_group_kernel(DwArgs p) {
+  __shared__ Tile sm;
+  const int64_t n0 = (int64_t)blockIdx.x * BM, k0 = (int64_t)blockIdx.y * BN;
+  const int64_t g = blockIdx.z;
+  const int64_t r0 = g * kGroupRows;
+  int64_t r1 = r0 + kGroupRows;
+  if (r1 > p.T) r1 = (p.T + BK - 1) / BK * BK;   // the rest of the group is zero rows
+  Acc acc;
+  acc.zero();
+  gemm_tile<true, true>(sm, acc, p.dy, p.n, p.x, p.k, n0, p.n, k0, p.k, r0, r1, p.T, nullptr);
+  float* out = p.out + g * p.n * p.k;
+  for_each_result(acc, [&](int mi, int ni, float v) {
+    const int64_t n = n0 + mi, k = k0 + ni;
+    if (n < p.n && k < p.k) out[n * p.k + k] = v;
+  });
+}
+
+// dW = perfect pairwise tree over the G group results (+0.0 past G), G <= 64.
+template <int L>
+__global__ __launch_bounds__(256) void group_tree_kernel(const float* __restrict__ q, int G,
+                                                         int64_t nk, float* __restrict__ dw) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= nk) return;
+  float v[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) v[i] = i < G ? q[(int64_t)i * nk + e] : 0.0f;
+#pragma unroll
+  for (int s = 1; s < L; s *= 2)
+#pragma unroll
+    for (int i = 0; i < L; i += 2 * s) v[i] = v[i] + v[i + s];
+  dw[e] = v[0];
+}
+
+// Rows of one call copied to their logical positions (staging for calls
+// that do not hold every row in order); padding rows are skipped.
+__global__ __launch_bounds__(256) void stage_rows_kernel(const uint16_t* __restrict__ src,
+                                                         int64_t rows, int64_t cols,
+                                                         const int32_t* __restrict__ row_logical,
+                                                         uint16_t* __restrict__ dst) {
+  const int64_t nchunk = cols / 8;
+  const int64_t total = rows * nchunk;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t p = i / nchunk, c = i % nchunk;
+    const int32_t l = row_logical[p];
+    if (l >= 0)
+      *reinterpret_cast<u32x4v_t*>(dst + (int64_t)l * cols + 8 * c) = ld16_nt(src + p * cols + 8 * c);
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_rows_kernel(uint16_t* __restrict__ dst, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    *reinterpret_cast<u32x4v_t*>(dst + 8 * i) = u32x4v_t{0u, 0u, 0u, 0u};
+}
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = 0.0f;
+}
+
+// ----------------------------------------------------------------- launchers
+hipError_t launch_rowwise(const RowwiseArgs& a, bool b_transposed, hipStream_t st) {
+  if (a.rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.rows + BM - 1) / BM), (unsigned)((a.n + BN - 1) / BN));
+  if (b_transposed) rowwise_kernel<true><<<grid, dim3(THREADS), 0, st>>>(a);
+  else rowwise_kernel<false><<<grid, dim3(THREADS), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+int64_t num_groups(int64_t T) { return (T + kGroupRows - 1) / kGroupRows; }
+
+hipError_t launch_dw_groups(const DwArgs& a, hipStream_t st) {
+  const int64_t G = num_groups(a.T);
+  if (G == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.n + BM - 1) / BM), (unsigned)((a.k + BN - 1) / BN), (unsigned)G);
+  dw_group_kernel<<<grid, dim3(THREADS), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_tree(const float* q, int64_t G, int64_t nk, float* dw, hipStream_t st) {
+  const dim3 grid((unsigned)((nk + 255) / 256));
+  int L = 1;
+  while (L < G) L *= 2;
+  switch (L) {
+    case 1: group_tree_kernel<1><<<grid, dim3(256), 0, st>>>(q, (int)G, nk, dw); break;
+    case 2: group_tree_kernel<2><<<grid, dim3(256), 0, st>>>(q, (int)G, nk, dw); break;
+    case 4: group_tree_kernel<4><<<grid, dim3(256), 0, st>>>(q, (int)G, nk, dw); break;
+    case 8: group_tree_kernel<8><<<grid, dim3(256), 0, st>>>(q, (int)G, nk, dw); break;
+    case 16: group_tree_kernel<16><<<grid, dim3(256), 0, st>>>(q, (int)G, nk, dw); break;
+    case 32: group_tree_kernel<32><<<grid, dim3(256), 0, st>>>(q, (int)G, nk, dw); break;
+    case 64: group_tree_kernel<64><<<grid, dim3(256), 0, st>>>(q, (int)G, nk, dw); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_rows(const uint16_t* src, int64_t rows, int64_t cols,
+                             const int32_t* row_logical, uint16_t* dst, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  int64_t g = (rows * (cols / 8) + 255) / 256;
+  if (g > 4096) g = 4096;
+  stage_rows_kernel<<<dim3((unsigned)g), dim3(256), 0, st>>>(src, rows, cols, row_logical, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(uint16_t* dst, int64_t n_elems, hipStream_t st) {
+  const int64_t n16 = n_elems / 8;
+  if (n16 == 0) return hipSuccess;
+  int64_t g = (n16 + 255) / 256;
+  if (g > 4096) g = 4096;
+  zero_rows_kernel<<<dim3((unsigned)g), dim3(256), 0, st>>>(dst, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_f32(float* dst, int64_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  int64_t g = (n + 255) / 256;
+  if (g > 4096) g = 4096;
+  zero_f32_kernel<<<dim3((unsigned)g), dim3(256), 0, st>>>(dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace lin
+}  // namespace rbi

@@ -10,7 +10,8 @@ import pytest
 from invariant_rmsnorm_backward_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rmsnorm_bi.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -22,14 +23,17 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rmsnorm_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:rmsnorm|det_gemm)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_contrib", "rmsnorm_dw_finalize"):
+    for n in ("rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_contrib", "rmsnorm_dw_finalize",
+              "det_gemm_bwd_dx", "det_gemm_dw_contrib", "det_gemm_dw_finalize"):
         assert n in names
     assert sorted(binding.EXPORTED) == names
 

@@ -1,0 +1,139 @@
+"""GPU parity of the linear layer (det_gemm): the HIP MFMA path against the
+FP64 oracle, and bitwise invariance of dX and dW across every layout of the
+same logical rows.  Sizes span several 128 x 128 output tiles with ragged
+tails in rows, outputs and inputs, and more than one dW group."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from invariant_rmsnorm_backward_amd import adapters, binding, contract, harness, inputs, layouts
+
+pytestmark = pytest.mark.gpu
+CONTRACT = contract.load_contract()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the gpu tests need an MI355X"
+    binding.load()
+
+
+def _wl(name, k, n, lengths, pad_rows=0):
+    return inputs.scaled(inputs.workload_linear(), name, hidden=k, lengths=lengths,
+                         pad_rows=pad_rows, out_features=n)
+
+
+def _reference(wl):
+    xb = inputs.bf16_bits(inputs.gen_x(wl))
+    wb = inputs.bf16_bits(inputs.gen_wmat(wl))
+    dyb = inputs.bf16_bits(inputs.gen_dy(wl))
+    dx, dw, dwa = oracle.linear_bwd_bf16(xb, wb, dyb)
+    return {"dX": dx, "dW": dw, "y": oracle.linear_fwd_bf16(xb, wb)}, dwa
+
+
+CASES = {
+    # name: (k in, n out, lengths, chunk)
+    "k200_n136_ragged": (200, 136, [300, 257, 150], 100),
+    "k256_n384": (256, 384, [128, 129, 64], 64),
+    "k1024_n512": (1024, 512, [333, 211], 128),
+    "k72_n8_thin": (72, 8, [77, 60], 33),
+    "k8_n200_tiny_k": (8, 200, [50, 13], 17),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_det_gemm_parity_and_invariance(case):
+    k, n, lengths, chunk = CASES[case]
+    wl = _wl(f"lin_{case}", k, n, lengths)
+    data = adapters.make_linear_inputs(wl, device="cuda", gen_device="cpu")
+    ref, _ = _reference(wl)
+    cells = layouts.standard_matrix(wl, chunk)
+    print(f"[linear] {case}: {len(cells)} cells", flush=True)
+    rep = harness.assert_gradient_batch_invariant("det_gemm", cells, CONTRACT, data=data,
+                                                  reference=ref, raise_on_red=False)
+    if not rep.strict:
+        print(rep.to_json()[:4000], flush=True)
+    assert rep.strict, rep.first_failure
+    assert all(v.max_abs == 0.0 for v in rep.invariance_reports)
+
+
+def test_det_gemm_two_groups_and_the_group_tree():
+    """More than 16384 logical rows: two dW groups joined by the tree, for one
+    call and for staged chunks."""
+    wl = _wl("lin_two_groups", 64, 72, [9000, 7384, 700])
+    data = adapters.make_linear_inputs(wl, device="cuda", gen_device="cpu")
+    ref, dwa = _reference(wl)
+    cells = [layouts.full(wl), layouts.chunked_packed(wl, chunk=4000),
+             layouts.permuted(wl)]
+    rep = harness.assert_gradient_batch_invariant("det_gemm", cells, CONTRACT, data=data,
+                                                  reference=ref, raise_on_red=False)
+    assert rep.strict, rep.first_failure
+    out = adapters.LinearAdapter().run_cell(cells[0], data)
+    err = np.abs(out["dW"].astype(np.float64) - ref["dW"])
+    # error bound of the canonical order: one rounding per 16-row step of a
+    # group chain (1024 steps) plus the tree, relative to the sum of |terms|
+    assert np.all(err <= (1024 + 2) * 2.0 ** -24 * dwa + 1e-30)
+
+
+def test_det_gemm_padding_rows_are_never_read():
+    wl = _wl("lin_pad", 128, 128, [100, 60, 31], pad_rows=40)
+    data = adapters.make_linear_inputs(wl, device="cuda", gen_device="cpu")
+    ref, _ = _reference(wl)
+    cells = [layouts.full(wl), layouts.packed_with_padding(wl), layouts.padded(wl, 230, "left")]
+    rep = harness.assert_gradient_batch_invariant("det_gemm", cells, CONTRACT, data=data,
+                                                  reference=ref, raise_on_red=False)
+    assert rep.strict, rep.first_failure
+    out = adapters.LinearAdapter().run_cell(cells[1], data)
+    assert bool(out["pad_rows_clean"][0])
+
+
+def test_det_gemm_accumulator_protocol():
+    wl = _wl("lin_proto", 64, 64, [100])
+    data = adapters.make_linear_inputs(wl, device="cuda", gen_device="cpu")
+    T = wl.n_logical
+    acc = binding.GemmDwAccumulator(T, 64, 64)
+    half = layouts.chunked_packed(wl, sizes=[60, 40]).calls
+    l0 = binding.Layout(half[0].row_logical, T)
+    l1 = binding.Layout(half[1].row_logical, T)
+    acc.contrib(data.x[:60], data.dy[:60], l0)
+    with pytest.raises(binding.RmsNormError) as ei:
+        acc.contrib(data.x[:60], data.dy[:60], l0)
+    assert ei.value.code == binding.ECOVERAGE
+    with pytest.raises(binding.RmsNormError) as ei:
+        acc.finalize()
+    assert ei.value.code == binding.ECOVERAGE
+    acc.contrib(data.x[60:], data.dy[60:], l1)
+    d1 = acc.finalize().cpu().numpy()
+    d2 = acc.finalize().cpu().numpy()
+    assert np.array_equal(d1.view(np.uint32), d2.view(np.uint32))
+    with pytest.raises(binding.RmsNormError) as ei:
+        acc.contrib(data.x[60:], data.dy[60:], l1)
+    assert ei.value.code == binding.ESTATE
+    acc.reset()
+    acc.contrib(data.x, data.dy)
+    d3 = acc.finalize().cpu().numpy()
+    assert np.array_equal(d1.view(np.uint32), d3.view(np.uint32))
+    acc.close()
+    # zero logical rows: dW = 0
+    acc0 = binding.GemmDwAccumulator(0, 64, 64)
+    e = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    acc0.contrib(e, e)
+    assert bool((acc0.finalize() == 0).all())
+    acc0.close()
+
+
+def test_det_gemm_rows_are_independent_of_the_call():
+    """The same row gives the same dX and y bits alone, in a small call and
+    inside the full batch (tile position and row count do not matter)."""
+    wl = _wl("lin_rows", 384, 256, [700])
+    data = adapters.make_linear_inputs(wl, device="cuda", gen_device="cpu")
+    full_dx = binding.gemm_bwd_dx(data.dy, data.w)
+    full_y = binding.gemm_fwd(data.x, data.w)
+    for a, b in ((0, 1), (5, 6), (129, 300), (650, 700)):
+        dx = binding.gemm_bwd_dx(data.dy[a:b].contiguous(), data.w)
+        y = binding.gemm_fwd(data.x[a:b].contiguous(), data.w)
+        assert torch.equal(dx.view(torch.int16), full_dx[a:b].view(torch.int16))
+        assert torch.equal(y.view(torch.int16), full_y[a:b].view(torch.int16))

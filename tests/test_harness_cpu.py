@@ -153,7 +153,7 @@ def test_adapter_without_backward_is_red_no_backward():
 
 def test_required_ops_are_enumerable():
     from invariant_rmsnorm_backward_amd import adapters
-    assert set(adapters.GRADIENT_ADAPTERS) == {"rms_norm", "qk_norm"}
+    assert set(adapters.GRADIENT_ADAPTERS) == {"rms_norm", "qk_norm", "det_gemm"}
     for name, cls in adapters.GRADIENT_ADAPTERS.items():
         a = cls()
         assert a.name == name and len(a.grad_names) >= 2
