@@ -277,6 +277,111 @@ def measure_cell(args, torch, np, binding, inputs, layouts):
     print(json.dumps(out))
 
 
+GEMM_METRIC = "det_gemm fwd+bwd achieved TFLOP/s (% of bf16 MFMA peak) with bitwise B1/BN/chunk invariant dW"
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def gemm_cpu_baseline(x_bits, w_bits, dy_bits, budget_rows=24):
+    """The FP64 oracle (single-threaded C) on the first rows of the workload:
+    dX of those rows and their dW contribution (2 x rows x N x K multiply-adds)."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.linear_bwd_bf16(x_bits[:budget_rows], w_bits, dy_bits[:budget_rows])
+    dt = time.perf_counter() - t0
+    n, k = w_bits.shape
+    flops = 2.0 * 2 * budget_rows * n * k
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"dX and dW of the first {budget_rows} rows ({n} x {k} weight), FP64 C, "
+                      f"{dt:.1f} s timed"}
+
+
+def measure_det_gemm(args, torch, np, binding, inputs):
+    """One step = y = x W^T, dX = dY W and dW = dY^T X (one B=N call into the
+    canonical accumulator, then finalize) on the linear workload; inputs
+    resident in HBM.  torch.matmul (hipBLASLt, not batch invariant) on the same
+    three products is timed beside it as a reference point."""
+    wl = inputs.workload_linear()
+    T, K, N = wl.n_logical, wl.hidden, wl.out_features
+    st = torch.cuda.current_stream()
+    sh = st.cuda_stream
+    print(f"[bench] generating {wl.name} on the GPU", file=sys.stderr, flush=True)
+    x = inputs.gen_x(wl, device="cuda")
+    w = inputs.gen_wmat(wl, device="cuda")
+    dy = inputs.gen_dy(wl, device="cuda")
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    acc = binding.GemmDwAccumulator(T, N, K)
+
+    def fwd():
+        binding.det_gemm_fwd(x.data_ptr(), w.data_ptr(), y.data_ptr(), T, N, K, None, sh)
+
+    def bdx():
+        binding.det_gemm_bwd_dx(dy.data_ptr(), w.data_ptr(), dx.data_ptr(), T, N, K, None, sh)
+
+    def bdw():
+        binding.det_gemm_dw_contrib(x.data_ptr(), dy.data_ptr(), T, N, K, None, acc.handle, sh)
+        binding.det_gemm_dw_finalize(acc.handle, dw.data_ptr(), sh)
+        binding.det_gemm_dw_acc_reset(acc.handle, sh)
+
+    def step():
+        fwd()
+        bdx()
+        bdw()
+
+    def timed(f, iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(iters):
+            f()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    for _ in range(args.warmup):
+        step()
+    K_ = max(1, args.steps // 5)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K_):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / K_ * 1e3
+    ph = {"fwd": timed(fwd, K_), "dx": timed(bdx, K_), "dw": timed(bdw, K_)}
+    lib_ops = {"fwd": lambda: torch.matmul(x, w.t()), "dx": lambda: torch.matmul(dy, w),
+               "dw": lambda: torch.matmul(dy.t(), x)}
+    lib = {}
+    for name, f in lib_ops.items():
+        timed(f, 3)                      # first calls select and load the library kernels
+        lib[name] = timed(f, K_)
+    gf = 2.0 * T * N * K
+    value = 3 * gf / (ms_step * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = gemm_cpu_baseline(inputs.bf16_bits(x), inputs.bf16_bits(w), inputs.bf16_bits(dy))
+    out = {
+        "metric": GEMM_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K_, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "rows": T, "in_features": K, "out_features": N,
+                   "layout": "BN/full (one call)", "step": "fwd + bwd_dx + dw_contrib + dw_finalize"},
+        "roofline": {"bound": "mfma", "achieved": round(gf / (ph["dw"] * 1e-3) / 1e12, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gf / (ph["dw"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "dw_group_kernel<256,128> + group tree (dW)",
+                     "algorithmic_flops_per_launch": gf, "avg_launch_ms": round(ph["dw"], 5)},
+        "cpu_baseline": cpu,
+        "phases_ms": {k: round(v, 5) for k, v in ph.items()},
+        "phases_tflops": {k: round(gf / (v * 1e-3) / 1e12, 1) for k, v in ph.items()},
+        "hipblaslt_torch_matmul_ms": {k: round(v, 5) for k, v in lib.items()},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    acc.close()
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +393,8 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="measure another workload (info line; the default run is the headline)")
     ap.add_argument("--cell", default="BN/full", help="layout cell for --workload")
+    ap.add_argument("--op", default="rms_norm", choices=["rms_norm", "det_gemm"],
+                    help="det_gemm: the linear layer 4096 -> 4096 on 32768 rows (info line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -304,6 +411,9 @@ def main():
         sys.exit(2)
     binding.load()
     torch.cuda.set_device(0)
+    if args.op == "det_gemm":
+        measure_det_gemm(args, torch, np, binding, inputs)
+        return
     if args.workload is not None:
         measure_cell(args, torch, np, binding, inputs, layouts)
         return

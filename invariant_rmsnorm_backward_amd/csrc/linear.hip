@@ -19,8 +19,9 @@
 // caller's buffer when one call holds every row in order, else rows staged
 // by logical index), so no layout can change a bit.
 //
-// All three products run on one MFMA tile engine: 128 x 128 output tiles,
-// 4 wavefronts of 64 x 64 (2 x 2 blocks of 32 x 32), 32-deep K stages
+// All three products run on one MFMA tile engine: 256 x 256 output tiles for
+// y and dX, 256 x 128 for dW (128 x 128 for small outputs), 4 wavefronts
+// each owning a quarter made of 32 x 32 blocks, 32-deep K stages
 // double-buffered in LDS with K contiguous.  Operands whose K index is the
 // slow one in memory (W in dX, both operands of dW) are transposed on the
 // way into LDS, two K rows at a time packed into 32-bit words.
@@ -35,10 +36,13 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4v_t __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int BK = 32;
 constexpr int LDSK = BK + 8;          // LDS row stride (bf16) of a K-contiguous tile
 constexpr int THREADS = 256;
 
+// Output tile BM x BN per workgroup; the 4 wavefronts each own a
+// (BM/2) x (BN/2) quarter made of 32 x 32 matrix-core blocks.
+template <int BM, int BN>
 struct alignas(16) Tile {
   uint16_t a[2][BM * LDSK];
   uint16_t b[2][BN * LDSK];
@@ -51,16 +55,18 @@ __device__ __forceinline__ u32x4v_t ld16_nt(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t*>(p));
 }
 
-// One operand's share of a K stage held in registers between the global
-// load and the LDS store.  Tile rows are the operand's M (or N) index.
+// One operand's share of a K stage (ROWS tile rows x 32 K) held in
+// registers between the global load and the LDS store.  Tile rows are the
+// operand's M (or N) index.
 //   direct:     element (m, k) at g[m * ld + k]; thread t loads chunks
-//               c = t and t + 256 (row c / 4, k offset 8 * (c % 4)).
+//               c = t + 256 i (row c / 4, k offset 8 * (c % 4)).
 //   transposed: element (m, k) at g[k * ld + m]; thread t loads rows
 //               k = 2p, 2p + 1 (p = t % 16) of columns 8q .. 8q + 7
-//               (q = t / 16) and packs them per column.
-template <bool TRANS>
+//               (q = t / 16 + 16 i) and packs them per column.
+template <bool TRANS, int ROWS>
 struct Stage {
-  u32x4v_t v[2];
+  static constexpr int NV = TRANS ? 2 * (ROWS / 128) : ROWS / 64;
+  u32x4v_t v[NV];
 
   // m0: first tile row; k0: first K index of the stage; m_lim / k_lim:
   // indices at or past them read as zero; rowmap (direct only): a tile
@@ -69,7 +75,7 @@ struct Stage {
                                        int64_t k0, int64_t k_lim, const int32_t* rowmap, int t) {
     if (!TRANS) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < NV; ++i) {
         const int c = t + THREADS * i;
         const int64_t m = m0 + (c >> 2);
         const int64_t k = k0 + 8 * (c & 3);
@@ -78,13 +84,16 @@ struct Stage {
         v[i] = ok ? ld16(g + m * ld + k) : u32x4v_t{0u, 0u, 0u, 0u};
       }
     } else {
-      const int p = t & 15, q = t >> 4;
-      const int64_t m = m0 + 8 * q;
+      const int p = t & 15;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int64_t k = k0 + 2 * p + i;
-        const bool ok = m < m_lim && k < k_lim;
-        v[i] = ok ? ld16(g + k * ld + m) : u32x4v_t{0u, 0u, 0u, 0u};
+      for (int i = 0; i < NV / 2; ++i) {
+        const int64_t m = m0 + 8 * ((t >> 4) + 16 * i);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t k = k0 + 2 * p + h;
+          const bool ok = m < m_lim && k < k_lim;
+          v[2 * i + h] = ok ? ld16(g + k * ld + m) : u32x4v_t{0u, 0u, 0u, 0u};
+        }
       }
     }
   }
@@ -92,53 +101,58 @@ struct Stage {
   __device__ __forceinline__ void store(uint16_t* s, int t) const {
     if (!TRANS) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < NV; ++i) {
         const int c = t + THREADS * i;
         *reinterpret_cast<u32x4v_t*>(s + (c >> 2) * LDSK + 8 * (c & 3)) = v[i];
       }
     } else {
-      const int p = t & 15, q = t >> 4;
+      const int p = t & 15;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const unsigned lo = (v[0][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;   // row 2p, column 8q + j
-        const unsigned hi = (v[1][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;   // row 2p + 1
-        *reinterpret_cast<unsigned*>(s + (8 * q + j) * LDSK + 2 * p) = lo | (hi << 16);
+      for (int i = 0; i < NV / 2; ++i) {
+        const int q = (t >> 4) + 16 * i;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const unsigned lo = (v[2 * i][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;       // row 2p, column 8q + j
+          const unsigned hi = (v[2 * i + 1][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;   // row 2p + 1
+          *reinterpret_cast<unsigned*>(s + (8 * q + j) * LDSK + 2 * p) = lo | (hi << 16);
+        }
       }
     }
   }
 };
 
-// The 64 x 64 share of wavefront w: blocks (i, j) of 32 x 32 at rows
-// wm + 32 i, columns wn + 32 j.
+// The (BM/2) x (BN/2) share of wavefront w: MI x NJ blocks of 32 x 32.
+template <int MI, int NJ>
 struct Acc {
-  f32x16_t c[2][2];
+  f32x16_t c[MI][NJ];
   __device__ __forceinline__ void zero() {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) c[i][j][r] = 0.0f;
   }
 };
 
 // Two 16-deep MFMA steps over one LDS stage, in ascending K.
-__device__ __forceinline__ void mma_stage(const uint16_t* as, const uint16_t* bs, Acc& acc,
+template <int MI, int NJ>
+__device__ __forceinline__ void mma_stage(const uint16_t* as, const uint16_t* bs, Acc<MI, NJ>& acc,
                                           int wm, int wn, int lane) {
   const int r = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int ks = 0; ks < BK; ks += 16) {
-    bf16x8_t a[2], b[2];
+    bf16x8_t a[MI], b[NJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
       a[i] = *reinterpret_cast<const bf16x8_t*>(as + (wm + 32 * i + r) * LDSK + ks + 8 * h);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
       b[j] = *reinterpret_cast<const bf16x8_t*>(bs + (wn + 32 * j + r) * LDSK + ks + 8 * h);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
         acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.c[i][j], 0, 0, 0);
   }
 }
@@ -146,16 +160,17 @@ __device__ __forceinline__ void mma_stage(const uint16_t* as, const uint16_t* bs
 // C[m][n] += sum over k in [k_begin, k_end) of A(m, k) B(k, n), K stages of
 // 32 in ascending order (k_end - k_begin is a multiple of 32; indices at or
 // past k_lim read as zero).
-template <bool AT, bool BT>
-__device__ __forceinline__ void gemm_tile(Tile& sm, Acc& acc, const uint16_t* a, int64_t lda,
-                                          const uint16_t* b, int64_t ldb, int64_t m0, int64_t m_lim,
-                                          int64_t n0, int64_t n_lim, int64_t k_begin, int64_t k_end,
+template <int BM, int BN, bool AT, bool BT>
+__device__ __forceinline__ void gemm_tile(Tile<BM, BN>& sm, Acc<BM / 64, BN / 64>& acc,
+                                          const uint16_t* a, int64_t lda, const uint16_t* b,
+                                          int64_t ldb, int64_t m0, int64_t m_lim, int64_t n0,
+                                          int64_t n_lim, int64_t k_begin, int64_t k_end,
                                           int64_t k_lim, const int32_t* rowmap_a) {
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
-  Stage<AT> sa;
-  Stage<BT> sb;
+  const int wm = (w >> 1) * (BM / 2), wn = (w & 1) * (BN / 2);
+  Stage<AT, BM> sa;
+  Stage<BT, BN> sb;
   sa.load(a, lda, m0, m_lim, k_begin, k_lim, rowmap_a, t);
   sb.load(b, ldb, n0, n_lim, k_begin, k_lim, nullptr, t);
   sa.store(sm.a[0], t);
@@ -180,15 +195,15 @@ __device__ __forceinline__ void gemm_tile(Tile& sm, Acc& acc, const uint16_t* a,
 
 // Result of block (i, j), register e: row wm + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,
 // column wn + 32 j + lane % 32.
-template <typename F>
-__device__ __forceinline__ void for_each_result(const Acc& acc, F&& f) {
+template <int BM, int BN, typename F>
+__device__ __forceinline__ void for_each_result(const Acc<BM / 64, BN / 64>& acc, F&& f) {
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const int wm = (w >> 1) * (BM / 2), wn = (w & 1) * (BN / 2);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < BM / 64; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < BN / 64; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         f(wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3), wn + 32 * j + (lane & 31),
@@ -202,37 +217,49 @@ __device__ __forceinline__ uint16_t to_bf16_rne(float f) {
 }
 
 // y = x W^T (fwd) and dX = dY W: bf16 result rows of the call, padding rows 0.
-template <bool BT>
+template <int BM, int BN, bool BT>
 __global__ __launch_bounds__(THREADS) void rowwise_kernel(RowwiseArgs p) {
-  __shared__ Tile sm;
+  __shared__ Tile<BM, BN> sm;
   const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
-  Acc acc;
+  Acc<BM / 64, BN / 64> acc;
   acc.zero();
-  gemm_tile<false, BT>(sm, acc, p.a, p.lda, p.b, p.ldb, m0, p.rows, n0, p.n, 0,
-                       (p.k + BK - 1) / BK * BK, p.k, p.row_logical);
-  for_each_result(acc, [&](int mi, int ni, float v) {
-    const int64_t m = m0 + mi, n = n0 + ni;
-    if (m < p.rows && n < p.n) {
+  gemm_tile<BM, BN, false, BT>(sm, acc, p.a, p.lda, p.b, p.ldb, m0, p.rows, n0, p.n, 0,
+                               (p.k + BK - 1) / BK * BK, p.k, p.row_logical);
+  // padding rows were loaded as zeros; they are written as 0 explicitly
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int wm = (w >> 1) * (BM / 2), wn = (w & 1) * (BN / 2);
+#pragma unroll
+  for (int i = 0; i < BM / 64; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t m = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (m >= p.rows) continue;
       const bool pad = p.row_logical != nullptr && p.row_logical[m] < 0;
-      p.out[m * p.n + n] = pad ? (uint16_t)0 : to_bf16_rne(v);
+#pragma unroll
+      for (int j = 0; j < BN / 64; ++j) {
+        const int64_t n = n0 + wn + 32 * j + (lane & 31);
+        if (n < p.n) p.out[m * p.n + n] = pad ? (uint16_t)0 : to_bf16_rne(acc.c[i][j][e]);
+      }
     }
-  });
 }
 
-// Q_g for one 128 x 128 tile of dW and one group g = blockIdx.z of logical
+// Q_g for one BM x BN tile of dW and one group g = blockIdx.z of logical
 // rows (dY and X in logical row order, T rows).
+template <int BM, int BN>
 __global__ __launch_bounds__(THREADS) void dw_group_kernel(DwArgs p) {
-  __shared__ Tile sm;
+  __shared__ Tile<BM, BN> sm;
   const int64_t n0 = (int64_t)blockIdx.x * BM, k0 = (int64_t)blockIdx.y * BN;
   const int64_t g = blockIdx.z;
   const int64_t r0 = g * kGroupRows;
   int64_t r1 = r0 + kGroupRows;
   if (r1 > p.T) r1 = (p.T + BK - 1) / BK * BK;   // the rest of the group is zero rows
-  Acc acc;
+  Acc<BM / 64, BN / 64> acc;
   acc.zero();
-  gemm_tile<true, true>(sm, acc, p.dy, p.n, p.x, p.k, n0, p.n, k0, p.k, r0, r1, p.T, nullptr);
+  gemm_tile<BM, BN, true, true>(sm, acc, p.dy, p.n, p.x, p.k, n0, p.n, k0, p.k, r0, r1, p.T,
+                                nullptr);
   float* out = p.out + g * p.n * p.k;
-  for_each_result(acc, [&](int mi, int ni, float v) {
+  for_each_result<BM, BN>(acc, [&](int mi, int ni, float v) {
     const int64_t n = n0 + mi, k = k0 + ni;
     if (n < p.n && k < p.k) out[n * p.k + k] = v;
   });
@@ -282,21 +309,38 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ dst, 
 }
 
 // ----------------------------------------------------------------- launchers
+// Tile shape from the output size only (the results do not depend on it:
+// every output element runs the same chain whatever tile holds it).
+static bool big_tiles(int64_t m, int64_t n) { return m >= 256 && n >= 256; }
+
+template <int BM, int BN>
+static void rowwise_go(const RowwiseArgs& a, bool bt, hipStream_t st) {
+  const dim3 grid((unsigned)((a.rows + BM - 1) / BM), (unsigned)((a.n + BN - 1) / BN));
+  if (bt) rowwise_kernel<BM, BN, true><<<grid, dim3(THREADS), 0, st>>>(a);
+  else rowwise_kernel<BM, BN, false><<<grid, dim3(THREADS), 0, st>>>(a);
+}
+
 hipError_t launch_rowwise(const RowwiseArgs& a, bool b_transposed, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.rows + BM - 1) / BM), (unsigned)((a.n + BN - 1) / BN));
-  if (b_transposed) rowwise_kernel<true><<<grid, dim3(THREADS), 0, st>>>(a);
-  else rowwise_kernel<false><<<grid, dim3(THREADS), 0, st>>>(a);
+  if (big_tiles(a.rows, a.n)) rowwise_go<256, 256>(a, b_transposed, st);
+  else rowwise_go<128, 128>(a, b_transposed, st);
   return hipGetLastError();
 }
 
 int64_t num_groups(int64_t T) { return (T + kGroupRows - 1) / kGroupRows; }
 
+template <int BM, int BN>
+static void dw_go(const DwArgs& a, int64_t G, hipStream_t st) {
+  const dim3 grid((unsigned)((a.n + BM - 1) / BM), (unsigned)((a.k + BN - 1) / BN), (unsigned)G);
+  dw_group_kernel<BM, BN><<<grid, dim3(THREADS), 0, st>>>(a);
+}
+
 hipError_t launch_dw_groups(const DwArgs& a, hipStream_t st) {
   const int64_t G = num_groups(a.T);
   if (G == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.n + BM - 1) / BM), (unsigned)((a.k + BN - 1) / BN), (unsigned)G);
-  dw_group_kernel<<<grid, dim3(THREADS), 0, st>>>(a);
+  // 256 x 128 keeps the dW kernel at two wavefronts per SIMD (212 VGPRs)
+  if (big_tiles(a.n, a.k)) dw_go<256, 128>(a, G, st);
+  else dw_go<128, 128>(a, G, st);
   return hipGetLastError();
 }
 
