@@ -245,8 +245,105 @@ class LinearAdapter(GradientAdapter):
         return {"backend": binding.rmsnorm_backend_info(), "library": binding.library_path()}
 
 
+@dataclasses.dataclass
+class ChainInputs:
+    """Logical inputs of the norm -> linear chain: x[T, H], the norm weight
+    w[H], the linear weight W[N, H] and the upstream gradient dY[T, N] of the
+    linear output."""
+    name: str
+    workload: inputs.Workload
+    x: torch.Tensor
+    w: torch.Tensor
+    wmat: torch.Tensor
+    dy: torch.Tensor
+    eps: float
+    active_token_denominator: int
+    loss_reduction: str = "mean_over_active_tokens"
+
+
+def make_chain_inputs(wl: inputs.Workload, device="cuda", gen_device=None) -> ChainInputs:
+    """Inputs of a linear workload run behind an RMSNorm of its input width."""
+    g = device if gen_device is None else gen_device
+    return ChainInputs(wl.name, wl, inputs.gen_x(wl, device=g).to(device),
+                       inputs.gen_w(wl, device=g).to(device), inputs.gen_wmat(wl, device=g).to(device),
+                       inputs.gen_dy(wl, device=g).to(device), wl.eps, inputs.n_active(wl))
+
+
+class NormLinearChainAdapter(GradientAdapter):
+    """A two-op training chain, y = Linear(RMSNorm(x)), run call by call in
+    each layout: forward through both ops, backward from dY through the
+    linear layer (dX, dW) into the norm (dx, dweight).  Tensors are named
+    ``op.tensor`` and listed in ``tensor_order`` (forward order, then the
+    backward in the order the gradients are produced), which the harness
+    uses to attribute the first tensor that drifts in each cell ("Phase 4:
+    Add single-card operator comparisons and drift attribution", Scope)."""
+    name = "rms_norm+det_gemm"
+    grad_names = ("det_gemm.dX", "det_gemm.dW", "rms_norm.dx", "rms_norm.dweight")
+    forward_names = ("rms_norm.y", "rms_norm.rstd", "det_gemm.y")
+    tensor_order = ("rms_norm.y", "rms_norm.rstd", "det_gemm.y", "det_gemm.dX", "det_gemm.dW",
+                    "rms_norm.dx", "rms_norm.dweight")
+    aggregation_order = "CDO-v1 (dweight), GDO-v1 (dW)"
+
+    def run_cell(self, cell: Cell, data: ChainInputs) -> Dict[str, np.ndarray]:
+        x, w, W, dy = data.x, data.w, data.wmat, data.dy
+        T, H = x.shape
+        N = W.shape[0]
+        dev = x.device
+        acc_n = binding.DwAccumulator(T, H)
+        acc_l = binding.GemmDwAccumulator(T, N, H)
+        out = {k: None for k in self.tensor_order}
+        y1_l = torch.zeros_like(x)
+        r_l = torch.zeros(T, dtype=torch.float32, device=dev)
+        y2_l = torch.zeros((T, N), dtype=x.dtype, device=dev)
+        d1_l = torch.zeros_like(x)
+        dx_l = torch.zeros_like(x)
+        layouts_: List[binding.Layout] = []
+        for call in cell.calls:
+            self.call_log.append((cell.name, call.name, call.rows))
+            if call.row_logical is None:
+                lay, xc, dyc, real, rl = None, x, dy, None, None
+            else:
+                rl = torch.from_numpy(call.row_logical.astype(np.int64)).to(dev)
+                real = rl >= 0
+                xc = _poisoned(call.rows, H, dev)
+                dyc = _poisoned(call.rows, N, dev)
+                xc[real] = x[rl[real]]
+                dyc[real] = dy[rl[real]]
+                lay = binding.Layout(call.row_logical, T)
+                layouts_.append(lay)
+            y1, r = binding.fwd(xc, w, data.eps, lay)
+            y2 = binding.gemm_fwd(y1, W, lay)
+            d1 = binding.gemm_bwd_dx(dyc, W, lay)
+            acc_l.contrib(y1, dyc, lay)
+            dx = binding.bwd(xc, w, d1, r, lay, acc_n)
+            for dst, src in ((y1_l, y1), (r_l, r), (y2_l, y2), (d1_l, d1), (dx_l, dx)):
+                if real is None:
+                    dst.copy_(src)
+                else:
+                    dst[rl[real]] = src[real]
+        dweight = acc_n.finalize()
+        dW = acc_l.finalize()
+        torch.cuda.synchronize()
+
+        def bits(t):
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+        out = {"rms_norm.y": bits(y1_l), "rms_norm.rstd": r_l.cpu().numpy(),
+               "det_gemm.y": bits(y2_l), "det_gemm.dX": bits(d1_l), "det_gemm.dW": dW.cpu().numpy(),
+               "rms_norm.dx": bits(dx_l), "rms_norm.dweight": dweight.cpu().numpy()}
+        for lay in layouts_:
+            lay.close()
+        acc_n.close()
+        acc_l.close()
+        return out
+
+    def provenance(self) -> dict:
+        return {"backend": binding.rmsnorm_backend_info(), "library": binding.library_path()}
+
+
 GRADIENT_ADAPTERS = {
     "rms_norm": RmsNormAdapter,
     "qk_norm": QkNormAdapter,
     "det_gemm": LinearAdapter,
+    "rms_norm+det_gemm": NormLinearChainAdapter,
 }

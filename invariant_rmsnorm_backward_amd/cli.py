@@ -4,11 +4,13 @@
     python -m invariant_rmsnorm_backward_amd.cli check --workload rmsnorm_h8_t59 --cell BN/chunked
     python -m invariant_rmsnorm_backward_amd.cli sweep [--workload NAME ...] [--small] [--json FILE]
 
-A sweep runs the operator on every cell of the workload through the HIP
+A sweep runs the operator (RMSNorm, QK-norm, the linear layer, or the
+RMSNorm -> linear chain) on every cell of the workload through the HIP
 library and classifies each cell (green / red_verdict / red_no_backward /
 blocked_hardware / skipped) against the B=N reference cell, bitwise.  It
 exits non-zero unless every non-skipped cell is green ("WS1 C4 (#270)
-closeout evidence", Runtime verification).  Without a GPU every cell is
+closeout evidence", Runtime verification); a red cell of a chain names the
+first tensor, in chain order, that drifts.  Without a GPU every cell is
 blocked_hardware: nothing falls back to another implementation.  Accuracy
 against a reference VJP is the test suite's job (it needs the oracle).
 """
@@ -27,12 +29,15 @@ SMALL = {  # reduced lengths for quick sweeps (same recipe and seed)
     "qknorm_d128_t16384_q": dict(lengths=[100, 37, 64]),
     "qknorm_d128_t16384_k": dict(lengths=[100, 37, 64]),
     "rmsnorm_h5120_packed131072": dict(lengths=[200, 100, 50, 30, 77], pad_rows=150),
+    "linear_h4096_o4096_t32768": dict(hidden=256, out_features=384, lengths=[300, 257, 150]),
 }
+# Multi-op targets: a linear workload run behind an RMSNorm of its input width.
+CHAINS = {"chain_rmsnorm_linear_h4096_o4096_t32768": "linear_h4096_o4096_t32768"}
 CHUNK = {"rmsnorm_h8_t59": 7, "qknorm": 512}
 
 
 def _workload(name: str, small: bool) -> inputs.Workload:
-    wl = inputs.ALL_WORKLOADS[name]()
+    wl = (inputs.ALL_WORKLOADS.get(name) or inputs.LINEAR_WORKLOADS[name])()
     if small and name in SMALL:
         wl = inputs.scaled(wl, wl.name + "_small", **SMALL[name])
     return wl
@@ -66,6 +71,10 @@ def _run(op_name: str, wls, cells_by_side, names=None):
     if op_name == "qk_norm":
         data = adapters.QkInputs(wls[0].name.rsplit("_", 1)[0], adapters.make_inputs(wls[0]),
                                  adapters.make_inputs(wls[1]))
+    elif op_name == "det_gemm":
+        data = adapters.make_linear_inputs(wls[0])
+    elif op_name == "rms_norm+det_gemm":
+        data = adapters.make_chain_inputs(wls[0])
     else:
         data = adapters.make_inputs(wls[0])
     rep = harness.assert_gradient_batch_invariant(op_name, cells, c, data=data, raise_on_red=False)
@@ -75,9 +84,16 @@ def _run(op_name: str, wls, cells_by_side, names=None):
 def _targets(names, small):
     out = []
     names = names or ["rmsnorm_h8_t59", "rmsnorm_h4096_t32768", "rmsnorm_h8192_varlen16",
-                      "qknorm_d128_t16384", "rmsnorm_h5120_packed131072"]
+                      "qknorm_d128_t16384", "rmsnorm_h5120_packed131072",
+                      "linear_h4096_o4096_t32768", "chain_rmsnorm_linear_h4096_o4096_t32768"]
     for n in names:
-        if n.startswith("qknorm"):
+        if n in CHAINS:
+            wl = _workload(CHAINS[n], small)
+            out.append(("rms_norm+det_gemm", n, (wl,), (_cells(wl),)))
+        elif n in inputs.LINEAR_WORKLOADS:
+            wl = _workload(n, small)
+            out.append(("det_gemm", n, (wl,), (_cells(wl),)))
+        elif n.startswith("qknorm"):
             base = "qknorm_d128_t16384"
             wq, wk = _workload(base + "_q", small), _workload(base + "_k", small)
             out.append(("qk_norm", base, (wq, wk), (_cells(wq), _cells(wk))))
@@ -103,7 +119,8 @@ def main(argv=None) -> int:
 
     if args.cmd == "list":
         for op, name, wls, cells in _targets(None, small=False):
-            print(f"{name} ({op}): hidden {wls[0].hidden}, {wls[0].n_logical} logical rows")
+            extra = f" -> {wls[0].out_features}" if wls[0].out_features else ""
+            print(f"{name} ({op}): hidden {wls[0].hidden}{extra}, {wls[0].n_logical} logical rows")
             for c in cells[0]:
                 print(f"    {c.name}: {len(c.calls)} call(s), rows {sum(c.call_shapes)}")
         return 0
@@ -121,7 +138,10 @@ def main(argv=None) -> int:
             results.append(json.loads(rep.to_json()))
         print(f"{name} ({op})")
         for cname, status in rows:
-            print(f"    {cname:44s} {status}")
+            extra = ""
+            if rep is not None and rep.chain_attribution.get(cname):
+                extra = f"  (first drift: {rep.chain_attribution[cname]})"
+            print(f"    {cname:44s} {status}{extra}")
     if getattr(args, "json", None):
         with open(args.json, "w") as f:
             json.dump(results, f, indent=1)

@@ -17,7 +17,10 @@ Acceptance criteria) and "WS1 C4 (#270) closeout evidence" (Acceptance map,
     proves that B=N is one call, that chunking splits it and that padding
     reaches the operator;
   * diagnostics per named gradient: max abs / max rel / mean / p99 drift and
-    the first failing op / tensor / cell;
+    the first failing op / tensor / cell; for a multi-op chain the adapter
+    lists its tensors in chain order and every red cell is attributed to the
+    first tensor that drifts ("Phase 4: Add single-card operator comparisons
+    and drift attribution", Scope);
   * an op without a backward is a categorised red (``red_no_backward``), not a
     stack trace; the report's ``strict`` flag is set only when every cell is
     green.
@@ -70,6 +73,7 @@ class CellResult:
     call_rows: List[int]
     n_pad_rows: int
     verdicts: List[TensorVerdict] = dataclasses.field(default_factory=list)
+    first_drift: Optional[str] = None   # first differing tensor in the adapter's tensor order
 
 
 @dataclasses.dataclass
@@ -88,6 +92,7 @@ class GradientInvarianceReport:
     first_failure: Optional[dict]
     strict: bool
     provenance: dict
+    chain_attribution: Dict[str, str] = dataclasses.field(default_factory=dict)
 
     def to_json(self) -> str:
         return json.dumps(dataclasses.asdict(self), indent=1, default=float)
@@ -218,10 +223,15 @@ def assert_gradient_batch_invariant(op, configs: Sequence[Cell], contract: Toler
                              max_abs=None)
 
     ref = results.get(reference_cell)
+    order = list(getattr(adapter, "tensor_order", ()) or [])
+    attribution: Dict[str, str] = {}
     for c in configs:
         cr = CellResult(c.name, status[c.name], c.call_shapes, sum(k.n_pad for k in c.calls))
         if c.name != reference_cell and status[c.name] == GREEN and ref is not None:
-            for t, got in results[c.name].items():
+            got_all = results[c.name]
+            names_in_order = [t for t in order if t in got_all] + [t for t in got_all if t not in order]
+            for t in names_in_order:
+                got = got_all[t]
                 want = ref[t]
                 same = contract.invariance_passes(_bits(got), _bits(want))
                 if same:   # bitwise equal: every drift statistic is exactly 0
@@ -237,6 +247,9 @@ def assert_gradient_batch_invariant(op, configs: Sequence[Cell], contract: Toler
                 note(v)
                 if not same:
                     cr.status = RED_VERDICT
+                    if cr.first_drift is None:
+                        cr.first_drift = t
+                        attribution[c.name] = t
         cells_out.append(cr)
 
     if reference is not None and ref is not None:
@@ -260,7 +273,7 @@ def assert_gradient_batch_invariant(op, configs: Sequence[Cell], contract: Toler
         aggregation_order=getattr(adapter, "aggregation_order", "?"),
         contract_version=contract.version, accuracy_reports=acc, invariance_reports=inv,
         singleton_aggregate_reports=singleton, cells=cells_out, first_failure=first,
-        strict=strict, provenance=adapter.provenance())
+        strict=strict, provenance=adapter.provenance(), chain_attribution=attribution)
     if raise_on_red and not strict:
         raise GradientInvarianceError(report)
     return report

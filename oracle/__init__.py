@@ -44,6 +44,8 @@ def _bind(lib):
     I64 = ctypes.c_int64
     lib.oracle_widen_bf16.argtypes = [P, I64, P]
     lib.oracle_widen_bf16.restype = None
+    lib.oracle_round_bf16.argtypes = [P, I64, P]
+    lib.oracle_round_bf16.restype = None
     lib.oracle_rmsnorm_fwd.argtypes = [P, P, I64, I64, ctypes.c_double, P, P, P]
     lib.oracle_rmsnorm_fwd.restype = ctypes.c_int
     lib.oracle_rmsnorm_bwd.argtypes = [P, P, P, I64, I64, ctypes.c_double, P, I64, P, P, P]
@@ -100,6 +102,13 @@ class Oracle:
         b = _c(bits, np.uint16)
         out = np.empty(b.shape, dtype=np.float64)
         self._lib().oracle_widen_bf16(_ptr(b), b.size, _ptr(out))
+        return out
+
+    def round_bf16(self, x: np.ndarray) -> np.ndarray:
+        """Raw bf16 patterns (uint16) nearest to finite float64 values."""
+        a = _c(x, np.float64)
+        out = np.empty(a.shape, dtype=np.uint16)
+        self._lib().oracle_round_bf16(_ptr(a), a.size, _ptr(out))
         return out
 
     def rmsnorm_fwd(self, x: np.ndarray, w: np.ndarray, eps: float,
@@ -222,6 +231,7 @@ def load_library(path: str) -> Oracle:
 
 _default = Oracle()
 widen_bf16 = _default.widen_bf16
+round_bf16 = _default.round_bf16
 rmsnorm_fwd = _default.rmsnorm_fwd
 rmsnorm_bwd = _default.rmsnorm_bwd
 rmsnorm_fwd_bf16 = _default.rmsnorm_fwd_bf16

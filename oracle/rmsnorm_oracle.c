@@ -56,6 +56,19 @@ void oracle_widen_bf16(const uint16_t* in, int64_t n, double* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = (double)bf16_bits_to_float(in[i]);
 }
 
+/* bf16 bit pattern nearest to a finite double: round to FP32 (nearest even),
+ * then keep the upper half, rounding to nearest even on the dropped half.
+ * This is how a bf16 activation is stored between two ops of a chain. */
+void oracle_round_bf16(const double* in, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) {
+        const float f = (float)in[i];
+        uint32_t u;
+        memcpy(&u, &f, sizeof u);
+        const uint32_t lsb = (u >> 16) & 1u;
+        out[i] = (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+    }
+}
+
 /* Inverse of a physical->logical row map.  Every value must be -1 (padding)
  * or a logical index in [0, n_logical), each logical index at most once.
  * inv[l] = physical row holding logical row l, or -1 if this call does not

@@ -137,3 +137,38 @@ def test_det_gemm_rows_are_independent_of_the_call():
         y = binding.gemm_fwd(data.x[a:b].contiguous(), data.w)
         assert torch.equal(dx.view(torch.int16), full_dx[a:b].view(torch.int16))
         assert torch.equal(y.view(torch.int16), full_y[a:b].view(torch.int16))
+
+
+@pytest.mark.parametrize("k,n,lengths,chunk", [(1024, 512, [333, 211], 128), (4096, 256, [300, 97], 64),
+                                               (128, 256, [150, 77, 9], 32)])
+def test_norm_linear_chain_is_invariant_in_every_tensor(k, n, lengths, chunk):
+    """RMSNorm -> linear, forward and backward, call by call in every layout:
+    every intermediate and every gradient bitwise equal to the B=N run, and
+    the per-op gradients within the contract of each op's own oracle."""
+    wl = _wl(f"chain_k{k}_n{n}", k, n, lengths)
+    data = adapters.make_chain_inputs(wl, device="cuda", gen_device="cpu")
+    cells = layouts.standard_matrix(wl, chunk)
+    ad = adapters.NormLinearChainAdapter()
+    rep = harness.assert_gradient_batch_invariant(ad, cells, CONTRACT, data=data,
+                                                  raise_on_red=False)
+    assert rep.strict, (rep.first_failure, rep.chain_attribution)
+    assert rep.chain_attribution == {}
+    assert {v.tensor for v in rep.invariance_reports} == set(ad.tensor_order)
+    # the chain against an oracle chain of its own: FP64 ops, bf16 rounding between them
+    # done on the oracle side (row-local outputs only: the sums over rows inherit the
+    # occasional one-ulp difference of a rounded intermediate, and each op's dW /
+    # dweight is checked against its own oracle in the single-op tests)
+    out = ad.run_cell(cells[0], data)
+    xb = inputs.bf16_bits(data.x.cpu())
+    wb = inputs.bf16_bits(data.w.cpu())
+    Wb = inputs.bf16_bits(data.wmat.cpu())
+    dyb = inputs.bf16_bits(data.dy.cpu())
+    y1, _ = oracle.rmsnorm_fwd_bf16(xb, wb, wl.eps)
+    y1b = oracle.round_bf16(y1)
+    y2 = oracle.linear_fwd_bf16(y1b, Wb)
+    dX, _, _ = oracle.linear_bwd_bf16(y1b, Wb, dyb)
+    dx, _, _ = oracle.rmsnorm_bwd_bf16(xb, wb, oracle.round_bf16(dX), wl.eps)
+    for name, want, tol in (("rms_norm.y", y1, "y"), ("det_gemm.y", y2, "y"),
+                            ("det_gemm.dX", dX, "dX"), ("rms_norm.dx", dx, "dx")):
+        got = harness.bf16_bits_to_f32(out[name])
+        assert CONTRACT.accuracy_passes(got, want, tol), name

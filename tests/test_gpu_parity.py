@@ -319,9 +319,12 @@ def test_cli_sweeps_are_green(tmp_path):
     from invariant_rmsnorm_backward_amd import cli
     out = tmp_path / "sweep.json"
     assert cli.main(["sweep", "--workload", "rmsnorm_h8_t59", "--workload", "qknorm_d128_t16384",
-                     "--workload", "rmsnorm_h5120_packed131072", "--small", "--json", str(out)]) == 0
+                     "--workload", "rmsnorm_h5120_packed131072",
+                     "--workload", "linear_h4096_o4096_t32768",
+                     "--workload", "chain_rmsnorm_linear_h4096_o4096_t32768",
+                     "--small", "--json", str(out)]) == 0
     assert cli.main(["check", "--workload", "rmsnorm_h4096_t32768", "--cell", "BN/chunked",
                      "--small"]) == 0
     import json
     reps = json.loads(out.read_text())
-    assert len(reps) == 3 and all(r["strict"] for r in reps)
+    assert len(reps) == 5 and all(r["strict"] for r in reps)

@@ -153,7 +153,7 @@ def test_adapter_without_backward_is_red_no_backward():
 
 def test_required_ops_are_enumerable():
     from invariant_rmsnorm_backward_amd import adapters
-    assert set(adapters.GRADIENT_ADAPTERS) == {"rms_norm", "qk_norm", "det_gemm"}
+    assert set(adapters.GRADIENT_ADAPTERS) == {"rms_norm", "qk_norm", "det_gemm", "rms_norm+det_gemm"}
     for name, cls in adapters.GRADIENT_ADAPTERS.items():
         a = cls()
         assert a.name == name and len(a.grad_names) >= 2
@@ -191,3 +191,66 @@ def test_cli_list_and_blocked_hardware_without_gpu(capsys):
     if not torch.cuda.is_available():
         assert cli.main(["sweep", "--workload", "rmsnorm_h8_t59"]) == 1
         assert "blocked_hardware" in capsys.readouterr().out
+
+
+class _SyntheticChain(_SyntheticOp):
+    """Three stages in chain order: a row-local forward, a layout-sensitive
+    parameter gradient (left fold in physical order, per call), and a
+    row-local input gradient; optionally an earlier layout-sensitive stage."""
+    name = "synthetic_chain"
+    tensor_order = ("a.y", "a.stat", "b.dW", "c.dx")
+
+    def __init__(self, early_red=False):
+        super().__init__()
+        self.early_red = early_red
+
+    def run_cell(self, cell, data):
+        T, H = data.x.shape
+        y = np.zeros_like(data.x)
+        dx = np.zeros_like(data.dy)
+        dW = np.zeros(H, dtype=np.float32)
+        stat = np.zeros(1, dtype=np.float32)
+        contrib = np.zeros((T, H), dtype=np.float32)
+        for call in cell.calls:
+            self.call_log.append((cell.name, call.name, call.rows))
+            x, dy = self.physical(call, data)
+            rl = np.arange(call.rows) if call.row_logical is None else call.row_logical
+            real = rl >= 0
+            y += self.restore(call, np.where(real[:, None], 2 * x, 0), T)
+            dx += self.restore(call, np.where(real[:, None], dy, 0), T)
+            part = np.zeros(H, dtype=np.float32)
+            for p in range(call.rows):
+                if rl[p] >= 0:
+                    part = (part + (dy[p] * x[p]).astype(np.float32)).astype(np.float32)
+            dW = (dW + part).astype(np.float32)
+            if self.early_red:
+                s1 = np.float32(0)
+                for p in range(call.rows):
+                    if rl[p] >= 0:
+                        s1 = np.float32(s1 + np.float32(x[p, 0] * 1e-3))
+                stat = (stat + s1).astype(np.float32)
+            else:
+                contrib += self.restore(call, np.nan_to_num(x[:, :1] * 1e-3).astype(np.float32)
+                                        * np.ones((1, H), np.float32), T)
+        if not self.early_red:
+            s = np.float32(0)
+            for l in range(T):
+                s = np.float32(s + contrib[l, 0])
+            stat[0] = s
+        return {"c.dx": dx.astype(np.float32), "b.dW": dW, "a.y": y.astype(np.float32), "a.stat": stat}
+
+
+def test_chain_drift_is_attributed_to_the_first_drifting_tensor():
+    wl = _wl()
+    rep = harness.assert_gradient_batch_invariant(_SyntheticChain(), layouts.page_matrix(wl),
+                                                  CONTRACT, data=_Data(wl), raise_on_red=False)
+    assert rep.chain_attribution["BN/chunked"] == "b.dW"
+    assert rep.first_failure["tensor"] == "b.dW"
+    by = {c.name: c for c in rep.cells}
+    assert by["BN/chunked"].first_drift == "b.dW" and by["BN/full"].first_drift is None
+    # an earlier drifting stage takes the attribution, whatever the dict order
+    rep2 = harness.assert_gradient_batch_invariant(_SyntheticChain(early_red=True),
+                                                   layouts.page_matrix(wl), CONTRACT,
+                                                   data=_Data(wl), raise_on_red=False)
+    assert rep2.chain_attribution["BN/chunked"] == "a.stat"
+    assert "a.y" not in rep2.chain_attribution.values()

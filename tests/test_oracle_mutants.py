@@ -39,6 +39,9 @@ MUTANTS = {
                                "acc = fmaf(prod, rstd[p], acc);"),
     "cdo_eight_streams": ("#define CDO_STREAMS 4", "#define CDO_STREAMS 8"),
     "cdo_contribution_x_rstd_first": ("float c = prod * rstd[p];", "float c = dyv * (xv * rstd[p]);"),
+    "round_bf16_truncates": ("out[i] = (uint16_t)((u + 0x7FFFu + lsb) >> 16);", "out[i] = (uint16_t)(u >> 16);"),
+    "round_bf16_ties_away": ("out[i] = (uint16_t)((u + 0x7FFFu + lsb) >> 16);",
+                             "out[i] = (uint16_t)((u + 0x8000u) >> 16);"),
 }
 
 

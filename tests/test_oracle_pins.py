@@ -482,7 +482,23 @@ def pin_linear_samples_match_the_full_products(orc):
     np.testing.assert_array_equal(got, [dx[3, 8], dx[30, 0], dw[0, 5], dw[6, 8], dwa[4, 2]])
 
 
-LINEAR_PINS = [pin_linear_brute_force_tiny, pin_linear_single_row_is_an_outer_product,
+def pin_round_bf16(orc):
+    """Exactly representable values keep their bits; halfway cases go to the
+    even neighbour; everything else to the nearest bf16 value."""
+    exact = np.array([0.0, 1.0, -2.5, 1.5 * 2.0 ** 127, 2.0 ** -126, -0.0078125])
+    np.testing.assert_array_equal(_val(orc.round_bf16(exact)), exact)
+    one_ulp = 2.0 ** -7                        # bf16 spacing in [1, 2)
+    ties = np.array([1.0 + one_ulp / 2, 1.0 + 3 * one_ulp / 2, -(1.0 + one_ulp / 2)])
+    np.testing.assert_array_equal(_val(orc.round_bf16(ties)), [1.0, 1.0 + 2 * one_ulp, -1.0])
+    rng = _rng(27)
+    v = rng.normal(size=4000) * 10.0 ** rng.integers(-20, 20, size=4000)
+    got = _val(orc.round_bf16(v))
+    lo = (np.frexp(np.abs(v))[1] - 1).astype(np.float64)
+    spacing = 2.0 ** (lo - 7)
+    assert np.all(np.abs(got - v) <= spacing / 2 * (1 + 2.0 ** -20))
+
+
+LINEAR_PINS = [pin_round_bf16, pin_linear_brute_force_tiny, pin_linear_single_row_is_an_outer_product,
                pin_linear_identity_weight, pin_linear_trace_identity, pin_linear_finite_differences,
                pin_linear_padding_and_layout_invariance, pin_linear_samples_match_the_full_products]
 
