@@ -39,10 +39,16 @@ def algorithmic_bytes(rows_real: int, rows_phys: int, H: int):
     return fwd, bwd
 
 
-def kernel_source_hash() -> str:
+# Sources that define the RMSNorm kernels (the linear-layer kernels and the
+# C-ABI glue do not change them).
+NORM_KERNEL_SOURCES = ("kernels.hip", "kernels.h", "device_math.h", "plan.h")
+GEMM_KERNEL_SOURCES = ("linear.hip", "linear.h")
+
+
+def kernel_source_hash(names=NORM_KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "invariant_rmsnorm_backward_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(names):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -376,7 +382,7 @@ def measure_det_gemm(args, torch, np, binding, inputs):
         "phases_ms": {k: round(v, 5) for k, v in ph.items()},
         "phases_tflops": {k: round(gf / (v * 1e-3) / 1e12, 1) for k, v in ph.items()},
         "hipblaslt_torch_matmul_ms": {k: round(v, 5) for k, v in lib.items()},
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash(GEMM_KERNEL_SOURCES),
     }
     acc.close()
     print(json.dumps(out))
