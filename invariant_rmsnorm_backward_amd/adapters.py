@@ -6,7 +6,9 @@ adapters", Required adapters: RMSNorm dx/dweight; "WS1 C4 (#270) closeout
 evidence", status table: rms_norm and qk_norm).  Stable gradient names:
 ``rms_norm`` -> dx, dweight (plus forward y, rstd); ``qk_norm`` -> dq, dk,
 dweight_q, dweight_k (plus yq, yk, rstd_q, rstd_k); ``det_gemm`` (a linear
-layer, "GEMM dX/dW" in Required adapters) -> dX, dW (plus forward y).
+layer, "GEMM dX/dW" in Required adapters) -> dX, dW (plus forward y);
+``embedding`` ("Embedding / LM-head") -> dE (plus forward y); the chain
+``rms_norm+det_gemm`` -> every tensor of both ops, named ``op.tensor``.
 
 An adapter runs the operator on each call's *physical* rows: real rows are
 gathered from the logical tensors, padding rows are filled with a NaN
@@ -341,9 +343,78 @@ class NormLinearChainAdapter(GradientAdapter):
         return {"backend": binding.rmsnorm_backend_info(), "library": binding.library_path()}
 
 
+@dataclasses.dataclass
+class EmbeddingInputs:
+    """Logical inputs of an embedding: token ids (host int32, logical order),
+    the table E[vocab, dim] and the upstream gradient dY[n_logical, dim]."""
+    name: str
+    workload: inputs.Workload
+    ids: np.ndarray
+    table: torch.Tensor
+    dy: torch.Tensor
+    active_token_denominator: int
+    loss_reduction: str = "mean_over_active_tokens"
+
+
+def make_embedding_inputs(wl: inputs.Workload, device="cuda", gen_device=None) -> EmbeddingInputs:
+    g = device if gen_device is None else gen_device
+    return EmbeddingInputs(wl.name, wl, inputs.gen_ids(wl), inputs.gen_table(wl, device=g).to(device),
+                           inputs.gen_dy(wl, device=g).to(device), inputs.n_active(wl))
+
+
+class EmbeddingAdapter(GradientAdapter):
+    """det_embedding: y = E[id], dE = scatter-add of dY by token (EDO-v1)."""
+    name = "embedding"
+    grad_names = ("dE",)
+    forward_names = ("y",)
+    aggregation_order = "EDO-v1"
+
+    def run_cell(self, cell: Cell, data: EmbeddingInputs) -> Dict[str, np.ndarray]:
+        table, dy = data.table, data.dy
+        vocab, dim = table.shape
+        T = len(data.ids)
+        dev = table.device
+        ids_l = torch.from_numpy(data.ids.astype(np.int32)).to(dev)
+        acc = binding.EmbeddingDwAccumulator(data.ids, vocab, dim)
+        y_l = torch.zeros((T, dim), dtype=table.dtype, device=dev)
+        pads_clean = True
+        layouts_: List[binding.Layout] = []
+        for call in cell.calls:
+            self.call_log.append((cell.name, call.name, call.rows))
+            if call.row_logical is None:
+                y_l.copy_(binding.embedding_fwd(ids_l, table))
+                acc.contrib(dy)
+                continue
+            rl = torch.from_numpy(call.row_logical.astype(np.int64)).to(dev)
+            real = rl >= 0
+            idc = torch.full((call.rows,), 1 << 30, dtype=torch.int32, device=dev)
+            idc[real] = ids_l[rl[real]]
+            dyc = _poisoned(call.rows, dim, dev)
+            dyc[real] = dy[rl[real]]
+            lay = binding.Layout(call.row_logical, T)
+            layouts_.append(lay)
+            y = binding.embedding_fwd(idc, table, lay)
+            acc.contrib(dyc, lay)
+            y_l[rl[real]] = y[real]
+            if bool((~real).any()):
+                pads_clean &= bool((y[~real].view(torch.int16) == 0).all())
+        dE = acc.finalize()
+        torch.cuda.synchronize()
+        res = {"dE": dE.cpu().numpy(), "y": y_l.view(torch.int16).cpu().numpy().view(np.uint16),
+               "pad_rows_clean": np.array([pads_clean])}
+        for lay in layouts_:
+            lay.close()
+        acc.close()
+        return res
+
+    def provenance(self) -> dict:
+        return {"backend": binding.rmsnorm_backend_info(), "library": binding.library_path()}
+
+
 GRADIENT_ADAPTERS = {
     "rms_norm": RmsNormAdapter,
     "qk_norm": QkNormAdapter,
     "det_gemm": LinearAdapter,
     "rms_norm+det_gemm": NormLinearChainAdapter,
+    "embedding": EmbeddingAdapter,
 }

@@ -28,7 +28,10 @@ EXPORTED = ("rmsnorm_max_hidden", "rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_c
             "rmsnorm_dw_acc_destroy", "rmsnorm_last_error", "rmsnorm_backend_info",
             "rmsnorm_set_split_threshold",
             "det_gemm_fwd", "det_gemm_bwd_dx", "det_gemm_dw_acc_create", "det_gemm_dw_contrib",
-            "det_gemm_dw_finalize", "det_gemm_dw_acc_reset", "det_gemm_dw_acc_destroy")
+            "det_gemm_dw_finalize", "det_gemm_dw_acc_reset", "det_gemm_dw_acc_destroy",
+            "det_embedding_fwd", "det_embedding_dw_acc_create", "det_embedding_dw_acc_set_ids",
+            "det_embedding_dw_contrib", "det_embedding_dw_finalize", "det_embedding_dw_acc_reset",
+            "det_embedding_dw_acc_destroy")
 
 
 class RmsNormError(RuntimeError):
@@ -79,6 +82,13 @@ def load() -> ctypes.CDLL:
         "det_gemm_dw_finalize": ([P, P, P], I32),
         "det_gemm_dw_acc_reset": ([P, P], I32),
         "det_gemm_dw_acc_destroy": ([P], I32),
+        "det_embedding_fwd": ([P, P, P, I64, I64, I64, P, P], I32),
+        "det_embedding_dw_acc_create": ([PP, P, I64, I64, I64, P], I32),
+        "det_embedding_dw_acc_set_ids": ([P, P, P], I32),
+        "det_embedding_dw_contrib": ([P, I64, I64, P, P, P], I32),
+        "det_embedding_dw_finalize": ([P, P, P], I32),
+        "det_embedding_dw_acc_reset": ([P, P], I32),
+        "det_embedding_dw_acc_destroy": ([P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -207,6 +217,48 @@ def det_gemm_dw_acc_reset(acc: Optional[int], stream: Optional[int]) -> None:
 
 def det_gemm_dw_acc_destroy(acc: Optional[int]) -> None:
     _check(load().det_gemm_dw_acc_destroy(acc), "det_gemm_dw_acc_destroy")
+
+
+# ------------------------------------------------------------- det_embedding
+def det_embedding_fwd(ids: int, table: int, y: int, rows: int, vocab: int, dim: int,
+                      layout: Optional[int], stream: Optional[int]) -> None:
+    _check(load().det_embedding_fwd(ids, table, y, rows, vocab, dim, layout, stream),
+           "det_embedding_fwd")
+
+
+def det_embedding_dw_acc_create(ids_host: np.ndarray, vocab: int, dim: int,
+                                stream: Optional[int]) -> int:
+    ids = np.ascontiguousarray(ids_host, dtype=np.int32)
+    h = ctypes.c_void_p(None)
+    _check(load().det_embedding_dw_acc_create(ctypes.byref(h), ids.ctypes.data_as(ctypes.c_void_p),
+                                              ids.size, vocab, dim, stream),
+           "det_embedding_dw_acc_create")
+    return h.value
+
+
+def det_embedding_dw_acc_set_ids(acc: Optional[int], ids_host: np.ndarray,
+                                 stream: Optional[int]) -> None:
+    ids = np.ascontiguousarray(ids_host, dtype=np.int32)
+    _check(load().det_embedding_dw_acc_set_ids(acc, ids.ctypes.data_as(ctypes.c_void_p), stream),
+           "det_embedding_dw_acc_set_ids")
+
+
+def det_embedding_dw_contrib(dy: int, rows: int, dim: int, layout: Optional[int],
+                             acc: Optional[int], stream: Optional[int]) -> None:
+    _check(load().det_embedding_dw_contrib(dy, rows, dim, layout, acc, stream),
+           "det_embedding_dw_contrib")
+
+
+def det_embedding_dw_finalize(acc: Optional[int], dE: int, stream: Optional[int]) -> None:
+    _check(load().det_embedding_dw_finalize(acc, dE, stream), "det_embedding_dw_finalize")
+
+
+def det_embedding_dw_acc_reset(acc: Optional[int], stream: Optional[int]) -> None:
+    _check(load().det_embedding_dw_acc_reset(acc, stream), "det_embedding_dw_acc_reset")
+
+
+def det_embedding_dw_acc_destroy(acc: Optional[int]) -> None:
+    _check(load().det_embedding_dw_acc_destroy(acc), "det_embedding_dw_acc_destroy")
 
 
 def current_stream() -> int:
@@ -364,3 +416,55 @@ def gemm_bwd_dx(dy, w, layout: Optional[Layout] = None, dx=None, stream: Optiona
     det_gemm_bwd_dx(dy.data_ptr(), w.data_ptr(), dx.data_ptr(), rows, n, k, _handle(layout),
                     current_stream() if stream is None else stream)
     return dx
+
+
+# ----------------------------------------------------- det_embedding helpers
+class EmbeddingDwAccumulator:
+    """Owns a canonical embedding-gradient accumulator for one batch's ids."""
+
+    def __init__(self, ids_host: np.ndarray, vocab: int, dim: int, stream: Optional[int] = None):
+        self.n_logical, self.vocab, self.dim = int(len(ids_host)), int(vocab), int(dim)
+        self.handle = det_embedding_dw_acc_create(ids_host, self.vocab, self.dim,
+                                                  current_stream() if stream is None else stream)
+
+    def set_ids(self, ids_host: np.ndarray, stream: Optional[int] = None):
+        det_embedding_dw_acc_set_ids(self.handle, ids_host,
+                                     current_stream() if stream is None else stream)
+
+    def contrib(self, dy, layout: Optional[Layout] = None, stream: Optional[int] = None):
+        det_embedding_dw_contrib(dy.data_ptr(), dy.shape[0], self.dim, _handle(layout), self.handle,
+                                 current_stream() if stream is None else stream)
+
+    def reset(self, stream: Optional[int] = None):
+        det_embedding_dw_acc_reset(self.handle, current_stream() if stream is None else stream)
+
+    def finalize(self, dE=None, stream: Optional[int] = None):
+        import torch
+        if dE is None:
+            dE = torch.empty((self.vocab, self.dim), dtype=torch.float32, device="cuda")
+        det_embedding_dw_finalize(self.handle, dE.data_ptr(),
+                                  current_stream() if stream is None else stream)
+        return dE
+
+    def close(self):
+        if self.handle:
+            det_embedding_dw_acc_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def embedding_fwd(ids, table, layout: Optional[Layout] = None, y=None,
+                  stream: Optional[int] = None):
+    """y = table[ids] for device int32 ids[rows] and bf16 table[vocab, dim]."""
+    import torch
+    rows = ids.shape[0]
+    vocab, dim = table.shape
+    y = torch.empty((rows, dim), dtype=table.dtype, device=table.device) if y is None else y
+    det_embedding_fwd(ids.data_ptr(), table.data_ptr(), y.data_ptr(), rows, vocab, dim,
+                      _handle(layout), current_stream() if stream is None else stream)
+    return y

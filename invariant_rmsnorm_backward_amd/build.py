@@ -27,7 +27,8 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contr
              "-Wall", "-Wno-unused-result", f"-I{CSRC}", f"-I{os.path.join(ROOT, 'include')}"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", f"-I{CSRC}"]
 
-SOURCES_HIP = ["kernels.hip", "abi.cpp", "linear.hip", "linear_abi.cpp"]
+SOURCES_HIP = ["kernels.hip", "abi.cpp", "linear.hip", "linear_abi.cpp", "embedding.hip",
+               "embedding_abi.cpp"]
 SOURCES_CXX = ["plan.cpp"]
 
 

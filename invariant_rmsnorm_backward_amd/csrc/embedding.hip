@@ -1,0 +1,172 @@
+// embedding.hip -- gfx950 kernels of the batch-invariant embedding table
+// gradient (the "Embedding / LM-head" adapter of "[WS1 Closeout][Backward]
+// Reusable gradient-invariance harness and operator adapters", Required
+// adapters).
+//
+// Forward y[r] = E[id(r)] is a row gather.  The backward is a scatter-add,
+// dE[v] = sum of dY over the logical rows whose token is v: the other
+// order-sensitive parameter VJP next to RMSNorm's dweight.  It is reduced in
+// one canonical order keyed by (token id, logical row), EDO-v1:
+//   * the occurrences of token v in ascending logical row index are cut into
+//     blocks of 64 consecutive occurrences;
+//   * a block is folded from +0.0 in occurrence order, one FP32 rounding per
+//     added row (bf16 dY widened exactly);
+//   * the token's block partials meet in a perfect pairwise tree with +0.0
+//     leaves up to the next power of two; absent tokens get +0.0.
+// The occurrence lists come from a host-built plan of the batch's token ids
+// (logical order), and the dY rows are read in logical order (the caller's
+// buffer when one call holds every row in order, else rows staged by
+// logical index), so no layout can change a bit.  No atomics: every output
+// element has one owner.
+#include "embedding.h"
+
+namespace rbi {
+namespace emb {
+
+typedef unsigned int u32x4e_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void widen8(const u32x4e_t v, float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+}
+
+// One 16-byte chunk (8 columns) per thread, grid-stride over rows x chunks.
+__global__ __launch_bounds__(256) void fwd_kernel(const int32_t* __restrict__ ids,
+                                                  const uint16_t* __restrict__ table,
+                                                  uint16_t* __restrict__ y, int64_t rows,
+                                                  int64_t vocab, int64_t dim,
+                                                  const int32_t* __restrict__ row_logical) {
+  const int64_t nq = dim / 8;
+  const int64_t total = rows * nq;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / nq, q = i % nq;
+    u32x4e_t v = {0u, 0u, 0u, 0u};
+    const bool pad = row_logical != nullptr && row_logical[r] < 0;
+    if (!pad) {
+      const int64_t id = ids[r];
+      if (id >= 0 && id < vocab)   // ids outside the table read nothing and give 0
+        v = *reinterpret_cast<const u32x4e_t*>(table + id * dim + 8 * q);
+    }
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4e_t*>(y + r * dim + 8 * q));
+  }
+}
+
+// One block of <= 64 occurrences over 512 columns: one wavefront, 8 columns
+// per lane.  Rows are loaded 8 at a time, then added in occurrence order.
+__global__ __launch_bounds__(64) void block_kernel(const uint16_t* __restrict__ dy, PlanView p,
+                                                   int64_t dim, float* __restrict__ P) {
+  const int lane = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  const int64_t q = (int64_t)blockIdx.y * 64 + lane;
+  const bool on = q < dim / 8;
+  const int start = p.blk_start[b], len = p.blk_len[b];
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int i0 = 0; i0 < len; i0 += 8) {
+    u32x4e_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u < len ? i0 + u : len - 1;       // in bounds; extra loads unused
+      const int64_t l = p.occ[start + i];
+      v[u] = on ? *reinterpret_cast<const u32x4e_t*>(dy + l * dim + 8 * q) : u32x4e_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (i0 + u < len) {
+        float f[8];
+        widen8(v[u], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + f[e];
+      }
+    }
+  }
+  if (on) {
+    float* dst = P + b * dim + 8 * q;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = acc[e];
+  }
+}
+
+// Every vocabulary row v over 4 columns per thread (1024 per workgroup):
+// the token's block partials, read in order, are combined like the digits of
+// a binary counter -- level k holds a finished subtree of 2^k leaves, a new
+// leaf merges upward as its left neighbours complete -- which is the perfect
+// pairwise tree; the pending levels are joined from the lowest up, which is
+// the same tree with +0.0 leaves to the next power of two (x + 0.0 == x for
+// every partial: none is -0.0, all folds start from +0.0).
+__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ P, PlanView p,
+                                                       int64_t dim, float* __restrict__ dE) {
+  const int64_t v = blockIdx.x;
+  const int64_t c0 = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c0 >= dim) return;
+  const int first = p.tok_first[v];
+  float r[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (first >= 0) {
+    const int nb = p.tok_nblk[v];
+    float st[kTreeLevels][4] = {};
+    for (int i = 0; i < nb; ++i) {
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = P[(int64_t)(first + i) * dim + c0 + e];
+      bool placed = false;
+#pragma unroll
+      for (int k = 0; k < kTreeLevels; ++k) {
+        if (!placed) {
+          if ((i >> k) & 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = st[k][e] + x[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[k][e] = x[e];
+            placed = true;
+          }
+        }
+      }
+    }
+    bool have = false;
+#pragma unroll
+    for (int k = 0; k < kTreeLevels; ++k) {
+      if ((nb >> k) & 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = have ? st[k][e] + r[e] : st[k][e];
+        have = true;
+      }
+    }
+  }
+  float* dst = dE + v * dim + c0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) dst[e] = r[e];
+}
+
+hipError_t launch_fwd(const int32_t* ids, const uint16_t* table, uint16_t* y, int64_t rows,
+                      int64_t vocab, int64_t dim, const int32_t* row_logical, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  int64_t g = (rows * (dim / 8) + 255) / 256;
+  if (g > 8192) g = 8192;
+  fwd_kernel<<<dim3((unsigned)g), dim3(256), 0, st>>>(ids, table, y, rows, vocab, dim, row_logical);
+  return hipGetLastError();
+}
+
+hipError_t launch_blocks(const uint16_t* dy, const PlanView& plan, int64_t dim, float* P,
+                         hipStream_t st) {
+  if (plan.n_blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)plan.n_blocks, (unsigned)((dim / 8 + 63) / 64));
+  block_kernel<<<grid, dim3(64), 0, st>>>(dy, plan, dim, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const float* P, const PlanView& plan, int64_t dim, float* dE,
+                           hipStream_t st) {
+  if (plan.vocab == 0) return hipSuccess;
+  const dim3 grid((unsigned)plan.vocab, (unsigned)((dim / 4 + 255) / 256));
+  finalize_kernel<<<grid, dim3(256), 0, st>>>(P, plan, dim, dE);
+  return hipGetLastError();
+}
+
+}  // namespace emb
+}  // namespace rbi

@@ -24,6 +24,9 @@ Distributions (the input recipe):
        active tokens of the whole logical multiset (mean over active tokens)
   mask (density < 1): Bernoulli(density) per (sample, pos)
   W  (linear-layer workloads, [out, in]): U[-1, 1) / sqrt(in), rounded to bf16
+  ids (embedding workloads): token of each logical row drawn from a Zipf law
+       P(rank k) ~ 1/k^s over the vocabulary (inverse CDF of a 53-bit uniform)
+  E  (embedding table, [vocab, dim]): U[-1, 1) * 2^-5, rounded to bf16
 """
 from __future__ import annotations
 
@@ -42,6 +45,7 @@ _M2 = 0x94D049BB133111EB
 # Tensor tags of the counter (8 bits).
 TAG_X, TAG_W, TAG_DY, TAG_MASK, TAG_LEN, TAG_COMP, TAG_PERM, TAG_PADCOMP = 1, 2, 3, 4, 5, 6, 7, 8
 TAG_WMAT = 9       # weight matrix of a linear-layer workload
+TAG_TABLE, TAG_IDS = 10, 11   # embedding table and token ids of an embedding workload
 TAG_K_OFFSET = 16  # K-side tensors of a QK-norm workload use tag + 16
 
 
@@ -113,6 +117,8 @@ class Workload:
     mask_density: float = 1.0         # fraction of active tokens
     pad_rows: int = 0                 # padding rows of the packed physical layout
     out_features: int = 0             # linear-layer workloads: N (hidden is the input width K)
+    vocab: int = 0                    # embedding workloads: table rows (hidden is the row width)
+    zipf_s: float = 1.1               # embedding workloads: token frequency exponent
     description: str = ""
 
     @property
@@ -217,18 +223,29 @@ def workload_h5120() -> Workload:
 
 def scaled(wl: Workload, name: str, hidden: Optional[int] = None,
            lengths: Optional[Sequence[int]] = None, pad_rows: Optional[int] = None,
-           out_features: Optional[int] = None) -> Workload:
+           out_features: Optional[int] = None, vocab: Optional[int] = None) -> Workload:
     """A smaller variant of a workload (same seed/recipe) for fast parity runs."""
     return dataclasses.replace(wl, name=name, hidden=hidden or wl.hidden,
                                lengths=tuple(lengths) if lengths is not None else wl.lengths,
                                pad_rows=wl.pad_rows if pad_rows is None else pad_rows,
                                out_features=wl.out_features if out_features is None
-                               else out_features)
+                               else out_features,
+                               vocab=wl.vocab if vocab is None else vocab)
 
 
 def workload_linear() -> Workload:
     return Workload("linear_h4096_o4096_t32768", 4096, (4096,) * 8, _seed(6), out_features=4096,
                     description="linear layer 4096 -> 4096, 8 x 4096 tokens, all active")
+
+
+def workload_embedding() -> Workload:
+    return Workload("embedding_v32000_d4096_t32768", 4096, (4096,) * 8, _seed(7), vocab=32000,
+                    description="embedding 32000 x 4096, 8 x 4096 tokens, Zipf(1.1) token ids")
+
+
+EMBEDDING_WORKLOADS = {
+    "embedding_v32000_d4096_t32768": workload_embedding,
+}
 
 
 LINEAR_WORKLOADS = {
@@ -350,6 +367,37 @@ def gen_wmat(wl: Workload, device="cpu") -> torch.Tensor:
     u = (_lsr(z, 40) - (1 << 23)).to(torch.float64) / float(1 << 23)      # exact, [-1, 1)
     f = (u / math.sqrt(k)).to(torch.float32)                             # one rounding
     return _bits_to_bf16_tensor(_f32_to_bf16_bits(f))
+
+
+def gen_ids(wl: Workload) -> np.ndarray:
+    """Token id (int32) of every logical row of an embedding workload: a
+    seeded Zipf(s) draw over the vocabulary keyed by (sample, pos)."""
+    assert wl.vocab > 0
+    s_, p_, _ = logical_keys(wl)
+    key = ((TAG_IDS + wl.tag_offset) << 50) | (s_.astype(np.int64) << 40) | (p_.astype(np.int64) << 22)
+    z = mix64_t(torch.from_numpy(key ^ _signed(seed_mix(wl.seed))))
+    u = (_lsr(z, 11).numpy().astype(np.float64) + 0.5) / float(1 << 53)    # (0, 1)
+    w = 1.0 / np.arange(1, wl.vocab + 1, dtype=np.float64) ** wl.zipf_s
+    cdf = np.cumsum(w)
+    cdf /= cdf[-1]
+    ids = np.searchsorted(cdf, u, side="left")
+    return np.minimum(ids, wl.vocab - 1).astype(np.int32)
+
+
+def gen_table(wl: Workload, device="cpu") -> torch.Tensor:
+    """Embedding table E[vocab, hidden] (bf16), U[-1, 1) * 2^-5, keyed by (row, column)."""
+    assert wl.vocab > 0
+    rows = torch.arange(wl.vocab, dtype=torch.int64, device=device)
+    cols = torch.arange(wl.hidden, dtype=torch.int64, device=device)
+    out = torch.empty((wl.vocab, wl.hidden), dtype=torch.bfloat16, device=device)
+    for a in range(0, wl.vocab, 4096):
+        r = rows[a:a + 4096]
+        key = ((TAG_TABLE + wl.tag_offset) << 50) | ((r[:, None] >> 18) << 40) | \
+              ((r[:, None] & ((1 << 18) - 1)) << 22) | cols[None, :]
+        z = mix64_t(key ^ _signed(seed_mix(wl.seed)))
+        u = (_lsr(z, 40) - (1 << 23)).to(torch.float64) / float(1 << 23)
+        out[a:a + 4096] = _bits_to_bf16_tensor(_f32_to_bf16_bits((u / 32.0).to(torch.float32)))
+    return out
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

@@ -1,12 +1,13 @@
-"""FP64 CPU oracle for RMSNorm forward/backward, the CDO-v1 dweight order and
-the backward of a linear layer (dX, dW).
+"""FP64 CPU oracle for RMSNorm forward/backward, the CDO-v1 dweight order,
+the backward of a linear layer (dX, dW) and the embedding table gradient
+(with an FP32 emulation of its EDO-v1 order).
 
 TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
 with the HIP library (``invariant_rmsnorm_backward_amd``) and never imports it.
 
-The arithmetic lives in ``rmsnorm_oracle.c`` and ``linear_oracle.c`` (plain C,
-FP64, single thread); this module only marshals numpy arrays.  See the C
+The arithmetic lives in ``rmsnorm_oracle.c``, ``linear_oracle.c`` and
+``embedding_oracle.c`` (plain C, FP64, single thread); this module only marshals numpy arrays.  See the C
 files' headers for the definitions followed and the pins that check them.
 """
 from __future__ import annotations
@@ -20,7 +21,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "rmsnorm_oracle.c")
-SRCS = [SRC, os.path.join(_HERE, "linear_oracle.c")]
+SRCS = [SRC, os.path.join(_HERE, "linear_oracle.c"), os.path.join(_HERE, "embedding_oracle.c")]
 LIB_PATH = os.path.join(_HERE, "liboracle_rmsnorm.so")
 
 # -ffp-contract=off and no fast-math: each float operation rounds once, as written.
@@ -58,6 +59,12 @@ def _bind(lib):
     lib.oracle_linear_bwd.restype = ctypes.c_int
     lib.oracle_linear_sample.argtypes = [P, P, P, I64, I64, I64, I64, P, P, P, P]
     lib.oracle_linear_sample.restype = ctypes.c_int
+    lib.oracle_embedding_fwd.argtypes = [P, P, I64, I64, I64, P, P]
+    lib.oracle_embedding_fwd.restype = ctypes.c_int
+    lib.oracle_embedding_bwd.argtypes = [P, P, I64, I64, I64, P, I64, P, I64, P, P]
+    lib.oracle_embedding_bwd.restype = ctypes.c_int
+    lib.oracle_edo_v1_f32.argtypes = [P, P, I64, I64, I64, P]
+    lib.oracle_edo_v1_f32.restype = ctypes.c_int
     return lib
 
 
@@ -222,6 +229,46 @@ class Oracle:
                "oracle_linear_sample")
         return out
 
+    # ---------------------------------------------------------------- embedding
+    def embedding_fwd_bf16(self, ids, table_bits, row_logical=None) -> np.ndarray:
+        """y = table[ids] (FP64) for the call's rows; padding rows 0."""
+        i = _c(ids, np.int32)
+        t = _c(table_bits, np.uint16)
+        vocab, dim = t.shape
+        rl = None if row_logical is None else _c(row_logical, np.int32)
+        y = np.empty((len(i), dim), dtype=np.float64)
+        _check(self._lib().oracle_embedding_fwd(_ptr(i), _ptr(t), len(i), vocab, dim, _ptr(rl),
+                                                _ptr(y)), "oracle_embedding_fwd")
+        return y
+
+    def embedding_bwd_bf16(self, ids, dy_bits, vocab, row_logical=None, n_logical=None, cols=None):
+        """(dE, |dE|) in FP64, [vocab, len(cols) or dim], summed over the rows the
+        call holds in ascending logical index."""
+        i = _c(ids, np.int32)
+        dy = _c(dy_bits, np.uint16)
+        rows, dim = dy.shape
+        rl = None if row_logical is None else _c(row_logical, np.int32)
+        nl = rows if n_logical is None else int(n_logical)
+        cl = None if cols is None else _c(cols, np.int64)
+        nc = dim if cols is None else len(cl)
+        dE = np.empty((vocab, nc), dtype=np.float64)
+        dEa = np.empty((vocab, nc), dtype=np.float64)
+        _check(self._lib().oracle_embedding_bwd(_ptr(i), _ptr(dy), rows, vocab, dim, _ptr(rl), nl,
+                                                _ptr(cl), nc, _ptr(dE), _ptr(dEa)),
+               "oracle_embedding_bwd")
+        return dE, dEa
+
+    def edo_v1_f32(self, ids, dy_bits, vocab) -> np.ndarray:
+        """FP32 emulation of the canonical embedding-gradient order EDO-v1 on
+        logical-order ids[n_logical] and dy[n_logical, dim]."""
+        i = _c(ids, np.int32)
+        dy = _c(dy_bits, np.uint16)
+        n, dim = dy.shape
+        out = np.empty((vocab, dim), dtype=np.float32)
+        _check(self._lib().oracle_edo_v1_f32(_ptr(i), _ptr(dy), n, vocab, dim, _ptr(out)),
+               "oracle_edo_v1_f32")
+        return out
+
 
 def load_library(path: str) -> Oracle:
     """Bind another build of the oracle source (the pin tests use this on
@@ -240,3 +287,6 @@ cdo_v1_dweight_f32 = _default.cdo_v1_dweight_f32
 linear_fwd_bf16 = _default.linear_fwd_bf16
 linear_bwd_bf16 = _default.linear_bwd_bf16
 linear_sample_bf16 = _default.linear_sample_bf16
+embedding_fwd_bf16 = _default.embedding_fwd_bf16
+embedding_bwd_bf16 = _default.embedding_bwd_bf16
+edo_v1_f32 = _default.edo_v1_f32

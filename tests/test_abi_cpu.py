@@ -26,7 +26,7 @@ def declared_functions():
     names = set()
     for h in HEADERS:
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
-        names |= set(re.findall(r"\b((?:rmsnorm|det_gemm)_\w+)\s*\(", text))
+        names |= set(re.findall(r"\b((?:rmsnorm|det_gemm|det_embedding)_\w+)\s*\(", text))
     return sorted(names)
 
 

@@ -60,9 +60,23 @@ LINEAR_MUTANTS = {
 }
 
 
+EMBEDDING_MUTANTS = {
+    "edo_blocks_of_32": ("#define EDO_BLOCK 64", "#define EDO_BLOCK 32"),
+    "edo_left_fold_over_blocks": ("out[v * dim + j] = edo_tree(q, nb, 0, width);",
+                                  "{ float s = 0.0f; for (int64_t b = 0; b < nb; ++b) s = s + q[b]; out[v * dim + j] = s; }"),
+    "edo_descending_occurrences": ("acc = acc + emb_widen(dy[occ[a + i] * dim + j]);",
+                                   "acc = acc + emb_widen(dy[occ[a + (n - 1 - i)] * dim + j]);"),
+    "embedding_bwd_wrong_token": ("dE[v * ncols + c] += g;", "dE[((v + 1) % vocab) * ncols + c] += g;"),
+    "embedding_bwd_drops_last_row": ("for (int64_t l = 0; l < n_logical; ++l) {\n        const int64_t p = inv[l];",
+                                     "for (int64_t l = 0; l + 1 < n_logical; ++l) {\n        const int64_t p = inv[l];"),
+    "embedding_fwd_reads_padding": ("const int pad = row_logical && row_logical[r] < 0;\n        if (!pad && (ids[r]",
+                                    "const int pad = 0;\n        if (!pad && (ids[r]"),
+}
+
+
 def _run_all_pins(orc):
     failures = []
-    for pin in list(pins.PINS) + list(pins.LINEAR_PINS):
+    for pin in list(pins.PINS) + list(pins.LINEAR_PINS) + list(pins.EMBEDDING_PINS):
         args = [orc]
         if "eps" in inspect.signature(pin).parameters:
             args.append(1e-6)
@@ -103,4 +117,10 @@ def test_mutant_is_caught(tmp_path, name):
 @pytest.mark.parametrize("name", sorted(LINEAR_MUTANTS))
 def test_linear_mutant_is_caught(tmp_path, name):
     failures = _run_all_pins(_build_variant(tmp_path, name, LINEAR_MUTANTS[name], which=1))
+    assert failures, f"no pin caught the planted mistake {name}"
+
+
+@pytest.mark.parametrize("name", sorted(EMBEDDING_MUTANTS))
+def test_embedding_mutant_is_caught(tmp_path, name):
+    failures = _run_all_pins(_build_variant(tmp_path, name, EMBEDDING_MUTANTS[name], which=2))
     assert failures, f"no pin caught the planted mistake {name}"

@@ -498,6 +498,119 @@ def pin_round_bf16(orc):
     assert np.all(np.abs(got - v) <= spacing / 2 * (1 + 2.0 ** -20))
 
 
+# ------------------------------------------------------- embedding (EDO-v1)
+def pin_embedding_brute_force_tiny(orc):
+    rng = _rng(30)
+    T, V, D = 11, 5, 3
+    ids = rng.integers(0, V, size=T).astype(np.int32)
+    table = _bits(rng.integers(-16, 17, size=(V, D)) / 8.0)
+    dy = _bits(rng.integers(-16, 17, size=(T, D)) / 8.0)
+    Y = [[float(_val(table[ids[r], j])) for j in range(D)] for r in range(T)]
+    np.testing.assert_array_equal(orc.embedding_fwd_bf16(ids, table), np.array(Y))
+    dE = [[sum(float(_val(dy[l, j])) for l in range(T) if ids[l] == v) for j in range(D)]
+          for v in range(V)]
+    got, _ = orc.embedding_bwd_bf16(ids, dy, V)
+    np.testing.assert_array_equal(got, np.array(dE))
+    got_cols, _ = orc.embedding_bwd_bf16(ids, dy, V, cols=np.array([2, 0]))
+    np.testing.assert_array_equal(got_cols, np.array(dE)[:, [2, 0]])
+
+
+def pin_embedding_counts_closed_form(orc):
+    """dY = 1 everywhere: dE[v][j] is the number of occurrences of v."""
+    rng = _rng(31)
+    T, V, D = 300, 17, 4
+    ids = rng.integers(0, V, size=T).astype(np.int32)
+    ones = _bits(np.ones((T, D)))
+    dE, _ = orc.embedding_bwd_bf16(ids, ones, V)
+    hist = np.bincount(ids, minlength=V).astype(np.float64)
+    np.testing.assert_array_equal(dE, np.repeat(hist[:, None], D, axis=1))
+    np.testing.assert_array_equal(orc.edo_v1_f32(ids, ones, V), dE.astype(np.float32))
+
+
+def pin_embedding_padding_layout_and_refusals(orc):
+    rng = _rng(32)
+    T, V, D = 40, 9, 8
+    ids = rng.integers(0, V, size=T).astype(np.int32)
+    dy = _rand_bf16(rng, (T, D))
+    dE0, _ = orc.embedding_bwd_bf16(ids, dy, V)
+    perm = rng.permutation(T)
+    rl = np.concatenate([perm[:7], [-1], perm[7:], [-1, -1]]).astype(np.int32)
+    real = rl >= 0
+    ids_p = np.full(len(rl), 10 ** 6, np.int32)          # padding ids are never read
+    ids_p[real] = ids[rl[real]]
+    dy_p = np.full((len(rl), D), 0x7FC1, np.uint16)
+    dy_p[real] = dy[rl[real]]
+    dE1, _ = orc.embedding_bwd_bf16(ids_p, dy_p, V, rl, T)
+    np.testing.assert_array_equal(dE1, dE0)
+    table = _rand_bf16(rng, (V, D))
+    y = orc.embedding_fwd_bf16(ids_p, table, rl)
+    assert np.all(y[~real] == 0)
+    np.testing.assert_array_equal(y[real], _val(table[ids[rl[real]]]))
+    with pytest.raises(oracle.OracleError):
+        orc.embedding_bwd_bf16(np.array([0, V], np.int32), dy[:2], V)
+    with pytest.raises(oracle.OracleError):
+        orc.edo_v1_f32(np.array([0, -1], np.int32), dy[:2], V)
+
+
+def pin_edo_v1_exact_when_every_partial_is_representable(orc):
+    rng = _rng(33)
+    T, V, D = 500, 7, 5                       # tokens with several 64-occurrence blocks
+    ids = rng.integers(0, V, size=T).astype(np.int32)
+    dy = _bits(rng.integers(-16, 17, size=(T, D)) / 8.0)
+    dE, _ = orc.embedding_bwd_bf16(ids, dy, V)
+    np.testing.assert_array_equal(orc.edo_v1_f32(ids, dy, V), dE.astype(np.float32))
+
+
+def pin_edo_v1_hand_derived_order(orc):
+    """Token 0 occurs 130 times: 2^24 first, then 129 ones.  FP32 spacing at
+    2^24 is 2, so a 1 added to 2^24 is lost (ties to even).  EDO-v1: block 0
+    (occurrences 0..63) = 2^24, block 1 = 64, block 2 = 2; tree over 4 leaves
+    (2^24 + 64) + (2 + 0) = 16777282.  A left fold over all occurrences would
+    give 2^24 = 16777216, blocks of 32 would give 16777314.  Token 1 occurs
+    once (value 0.5) and token 2 never.  Token 3 occurs 193 times: 2^24,
+    then zeros except occurrences 128 and 192 (value 1): blocks 2^24, 0, 1,
+    1, and the tree (2^24 + 0) + (1 + 1) = 16777218, where a left fold over
+    the blocks would lose both ones (16777216)."""
+    n0, n3 = 130, 193
+    ids = np.concatenate([np.zeros(n0, np.int32), np.full(n3, 3, np.int32)])
+    ids = np.insert(ids, 57, 1)                   # token 1 sits between token 0's rows
+    vals0 = np.ones(n0)
+    vals0[0] = 2.0 ** 24
+    vals3 = np.zeros(n3)
+    vals3[0] = 2.0 ** 24
+    vals3[128] = 1.0
+    vals3[192] = 1.0
+    vals = np.insert(np.concatenate([vals0, vals3]), 57, 0.5)
+    dy = _bits(vals[:, None])
+    got = orc.edo_v1_f32(ids, dy, 4)
+    assert got[0, 0] == np.float32(16777282.0)
+    assert got[1, 0] == np.float32(0.5) and got[2, 0] == 0.0
+    assert got[3, 0] == np.float32(16777218.0)
+
+
+def pin_edo_v1_within_fp32_error_bound(orc):
+    rng = _rng(34)
+    T, V, D = 3000, 11, 6
+    ids = np.minimum(rng.zipf(1.3, size=T) - 1, V - 1).astype(np.int32)
+    dy = _rand_bf16(rng, (T, D))
+    ref, dabs = orc.embedding_bwd_bf16(ids, dy, V)
+    got = orc.edo_v1_f32(ids, dy, V).astype(np.float64)
+    nmax = np.bincount(ids, minlength=V).max()
+    depth = 64 + int(math.ceil(math.log2(max(1, (nmax + 63) // 64)))) + 1
+    assert np.all(np.abs(got - ref) <= depth * 2.0 ** -24 * dabs * 1.01)
+
+
+EMBEDDING_PINS = [pin_embedding_brute_force_tiny, pin_embedding_counts_closed_form,
+                  pin_embedding_padding_layout_and_refusals,
+                  pin_edo_v1_exact_when_every_partial_is_representable, pin_edo_v1_hand_derived_order,
+                  pin_edo_v1_within_fp32_error_bound]
+
+
+@pytest.mark.parametrize("pin", EMBEDDING_PINS, ids=lambda f: f.__name__)
+def test_embedding_oracle_pins(pin):
+    pin(oracle)
+
+
 LINEAR_PINS = [pin_round_bf16, pin_linear_brute_force_tiny, pin_linear_single_row_is_an_outer_product,
                pin_linear_identity_weight, pin_linear_trace_identity, pin_linear_finite_differences,
                pin_linear_padding_and_layout_invariance, pin_linear_samples_match_the_full_products]

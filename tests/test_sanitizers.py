@@ -37,7 +37,7 @@ def test_oracle_under_asan_ubsan(tmp_path):
         "import oracle\n"
         "from tests import test_oracle_pins as pins\n"
         "orc = oracle.load_library(%r)\n"
-        "for pin in list(pins.PINS) + list(pins.LINEAR_PINS):\n"
+        "for pin in list(pins.PINS) + list(pins.LINEAR_PINS) + list(pins.EMBEDDING_PINS):\n"
         "    args = [orc] + ([1e-6] if 'eps' in inspect.signature(pin).parameters else [])\n"
         "    pin(*args)\n"
         "print('oracle pins under sanitizers: ok')\n" % (ROOT, so))
