@@ -388,6 +388,100 @@ def measure_det_gemm(args, torch, np, binding, inputs):
     print(json.dumps(out))
 
 
+EMB_METRIC = "det_embedding fwd+bwd achieved HBM GB/s (% of peak) with bitwise B1/BN/chunk invariant dE"
+EMB_KERNEL_SOURCES = ("embedding.hip", "embedding.h")
+
+
+def emb_cpu_baseline(ids, dy_bits, vocab, budget_rows=4096):
+    """The FP64 oracle (single-threaded C) on the first rows of the batch."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.embedding_bwd_bf16(ids[:budget_rows], dy_bits[:budget_rows], vocab)
+    dt = time.perf_counter() - t0
+    dim = dy_bits.shape[1]
+    nbytes = budget_rows * dim * 2 + vocab * dim * 4
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"dE of the first {budget_rows} rows ({vocab} x {dim} table), FP64 C, "
+                      f"{dt:.1f} s timed, same byte formula as value"}
+
+
+def measure_det_embedding(args, torch, np, binding, inputs):
+    """One step = y = E[ids] (gather) and dE (one B=N call into the canonical
+    accumulator, then finalize, every table row written) on the embedding
+    workload; ids, table and dY resident in HBM.  Algorithmic bytes: gather
+    T*4 + 2*T*dim (table rows read) + 2*T*dim (y); gradient 2*T*dim (dY) +
+    4*vocab*dim (dE).  Block partials are not counted."""
+    wl = inputs.workload_embedding()
+    T, D, V = wl.n_logical, wl.hidden, wl.vocab
+    st = torch.cuda.current_stream()
+    sh = st.cuda_stream
+    print(f"[bench] generating {wl.name}", file=sys.stderr, flush=True)
+    ids_h = inputs.gen_ids(wl)
+    ids = torch.from_numpy(ids_h).cuda()
+    table = inputs.gen_table(wl, device="cuda")
+    dy = inputs.gen_dy(wl, device="cuda")
+    y = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    dE = torch.empty((V, D), dtype=torch.float32, device="cuda")
+    acc = binding.EmbeddingDwAccumulator(ids_h, V, D)
+
+    def fwd():
+        binding.det_embedding_fwd(ids.data_ptr(), table.data_ptr(), y.data_ptr(), T, V, D, None, sh)
+
+    def bwd():
+        binding.det_embedding_dw_contrib(dy.data_ptr(), T, D, None, acc.handle, sh)
+        binding.det_embedding_dw_finalize(acc.handle, dE.data_ptr(), sh)
+        binding.det_embedding_dw_acc_reset(acc.handle, sh)
+
+    def timed(f, iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(iters):
+            f()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / K * 1e3
+    ph = {"fwd": timed(fwd, K), "bwd": timed(bwd, K)}
+    fb = T * 4 + 4 * T * D
+    bb = 2 * T * D + 4 * V * D
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = emb_cpu_baseline(ids_h, inputs.bf16_bits(dy), V)
+    out = {
+        "metric": EMB_METRIC, "value": round((fb + bb) / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "rows": T, "vocab": V, "dim": D,
+                   "distinct_tokens": int((np.bincount(ids_h, minlength=V) > 0).sum()),
+                   "layout": "BN/full (one call)", "step": "fwd + dw_contrib + dw_finalize"},
+        "roofline": {"bound": "hbm", "achieved": round(bb / (ph["bwd"] * 1e-3) / 1e9, 2),
+                     "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(bb / (ph["bwd"] * 1e-3) / 1e9 / PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "block_kernel + finalize_kernel (dE)",
+                     "algorithmic_bytes_per_launch": bb, "avg_launch_ms": round(ph["bwd"], 5)},
+        "cpu_baseline": cpu,
+        "phases_ms": {k: round(v, 5) for k, v in ph.items()},
+        "phases_gbps": {"fwd": round(fb / (ph["fwd"] * 1e-3) / 1e9, 1),
+                        "bwd": round(bb / (ph["bwd"] * 1e-3) / 1e9, 1)},
+        "kernel_source_hash": kernel_source_hash(EMB_KERNEL_SOURCES),
+    }
+    acc.close()
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -399,8 +493,9 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="measure another workload (info line; the default run is the headline)")
     ap.add_argument("--cell", default="BN/full", help="layout cell for --workload")
-    ap.add_argument("--op", default="rms_norm", choices=["rms_norm", "det_gemm"],
-                    help="det_gemm: the linear layer 4096 -> 4096 on 32768 rows (info line)")
+    ap.add_argument("--op", default="rms_norm", choices=["rms_norm", "det_gemm", "det_embedding"],
+                    help="det_gemm: the linear layer 4096 -> 4096 on 32768 rows; det_embedding: "
+                         "a 32000 x 4096 table on 32768 rows (info lines)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -419,6 +514,9 @@ def main():
     torch.cuda.set_device(0)
     if args.op == "det_gemm":
         measure_det_gemm(args, torch, np, binding, inputs)
+        return
+    if args.op == "det_embedding":
+        measure_det_embedding(args, torch, np, binding, inputs)
         return
     if args.workload is not None:
         measure_cell(args, torch, np, binding, inputs, layouts)

@@ -20,6 +20,7 @@ struct PlanView {
   const int32_t* blk_len;      // [n_blocks] 1..64
   const int32_t* tok_first;    // [vocab] first block of the token, -1 if it does not occur
   const int32_t* tok_nblk;     // [vocab] number of blocks of the token
+  const int32_t* blk_order;    // [n_blocks] block ids by decreasing length (work order only)
   int64_t n_blocks;
   int64_t vocab;
 };

@@ -24,6 +24,7 @@ namespace rbi {
 namespace emb {
 
 typedef unsigned int u32x4e_t __attribute__((ext_vector_type(4)));
+typedef float f32x4e_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void widen8(const u32x4e_t v, float (&f)[8]) {
 #pragma unroll
@@ -56,27 +57,31 @@ __global__ __launch_bounds__(256) void fwd_kernel(const int32_t* __restrict__ id
 }
 
 // One block of <= 64 occurrences over 512 columns: one wavefront, 8 columns
-// per lane.  Rows are loaded 8 at a time, then added in occurrence order.
+// per lane.  Lane i first loads the block's i-th logical row index; the rows
+// are then loaded 16 at a time (their indices read across lanes) and added
+// in occurrence order.  Workgroups take the blocks longest first (the plan's
+// work order; it does not enter any result).
 __global__ __launch_bounds__(64) void block_kernel(const uint16_t* __restrict__ dy, PlanView p,
                                                    int64_t dim, float* __restrict__ P) {
   const int lane = threadIdx.x;
-  const int64_t b = blockIdx.x;
+  const int64_t b = p.blk_order[blockIdx.x];
   const int64_t q = (int64_t)blockIdx.y * 64 + lane;
   const bool on = q < dim / 8;
   const int start = p.blk_start[b], len = p.blk_len[b];
+  const int my_row = p.occ[start + (lane < len ? lane : len - 1)];
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-  for (int i0 = 0; i0 < len; i0 += 8) {
-    u32x4e_t v[8];
+  for (int i0 = 0; i0 < len; i0 += 16) {
+    u32x4e_t v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 16; ++u) {
       const int i = i0 + u < len ? i0 + u : len - 1;       // in bounds; extra loads unused
-      const int64_t l = p.occ[start + i];
+      const int64_t l = __builtin_amdgcn_readlane(my_row, i);
       v[u] = on ? *reinterpret_cast<const u32x4e_t*>(dy + l * dim + 8 * q) : u32x4e_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 16; ++u) {
       if (i0 + u < len) {
         float f[8];
         widen8(v[u], f);
@@ -86,9 +91,9 @@ __global__ __launch_bounds__(64) void block_kernel(const uint16_t* __restrict__ 
     }
   }
   if (on) {
-    float* dst = P + b * dim + 8 * q;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dst[e] = acc[e];
+    f32x4e_t* dst = reinterpret_cast<f32x4e_t*>(P + b * dim + 8 * q);
+    dst[0] = f32x4e_t{acc[0], acc[1], acc[2], acc[3]};
+    dst[1] = f32x4e_t{acc[4], acc[5], acc[6], acc[7]};
   }
 }
 
@@ -111,8 +116,9 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
     float st[kTreeLevels][4] = {};
     for (int i = 0; i < nb; ++i) {
       float x[4];
+      const f32x4e_t pv = *reinterpret_cast<const f32x4e_t*>(P + (int64_t)(first + i) * dim + c0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = P[(int64_t)(first + i) * dim + c0 + e];
+      for (int e = 0; e < 4; ++e) x[e] = pv[e];
       bool placed = false;
 #pragma unroll
       for (int k = 0; k < kTreeLevels; ++k) {
@@ -138,9 +144,8 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
       }
     }
   }
-  float* dst = dE + v * dim + c0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) dst[e] = r[e];
+  __builtin_nontemporal_store(f32x4e_t{r[0], r[1], r[2], r[3]},
+                              reinterpret_cast<f32x4e_t*>(dE + v * dim + c0));
 }
 
 hipError_t launch_fwd(const int32_t* ids, const uint16_t* table, uint16_t* y, int64_t rows,

@@ -37,7 +37,7 @@ enum Mode { kEmpty = 0, kComputed = 1, kStaged = 2 };
 // Host plan: occurrences grouped by token (counting sort, stable in the
 // logical row), cut into blocks of kBlockOcc.
 struct HostPlan {
-  std::vector<int32_t> occ, blk_start, blk_len, tok_first, tok_nblk;
+  std::vector<int32_t> occ, blk_start, blk_len, tok_first, tok_nblk, blk_order;
 };
 
 int build_plan(const int32_t* ids, int64_t T, int64_t vocab, HostPlan* P) {
@@ -67,6 +67,11 @@ int build_plan(const int32_t* ids, int64_t T, int64_t vocab, HostPlan* P) {
     }
     P->tok_nblk[v] = static_cast<int32_t>(P->blk_start.size()) - P->tok_first[v];
   }
+  // work order: longest blocks first (does not enter any result)
+  P->blk_order.resize(P->blk_start.size());
+  for (size_t i = 0; i < P->blk_order.size(); ++i) P->blk_order[i] = static_cast<int32_t>(i);
+  std::stable_sort(P->blk_order.begin(), P->blk_order.end(),
+                   [&](int32_t a, int32_t b) { return P->blk_len[a] > P->blk_len[b]; });
   return RMSNORM_OK;
 }
 
@@ -93,12 +98,13 @@ int upload_plan(det_embedding_dw_acc* A, const int32_t* ids, hipStream_t st) {
   const int64_t nb = static_cast<int64_t>(P.blk_start.size());
   if (nb > A->max_blocks) return fail(RMSNORM_EINVAL, "internal: block count exceeds the bound");
   std::vector<int32_t> buf;
-  buf.reserve(P.occ.size() + 2 * nb + 2 * A->vocab + 1);
+  buf.reserve(P.occ.size() + 3 * nb + 2 * A->vocab + 1);
   buf.insert(buf.end(), P.occ.begin(), P.occ.end());
   buf.insert(buf.end(), P.blk_start.begin(), P.blk_start.end());
   buf.insert(buf.end(), P.blk_len.begin(), P.blk_len.end());
   buf.insert(buf.end(), P.tok_first.begin(), P.tok_first.end());
   buf.insert(buf.end(), P.tok_nblk.begin(), P.tok_nblk.end());
+  buf.insert(buf.end(), P.blk_order.begin(), P.blk_order.end());
   if (buf.size() > A->plan_cap) return fail(RMSNORM_EINVAL, "internal: plan exceeds its buffer");
   hipError_t e = hipStreamSynchronize(st);   // earlier work may still read the old plan
   if (e == hipSuccess && !buf.empty())
@@ -111,6 +117,7 @@ int upload_plan(det_embedding_dw_acc* A, const int32_t* ids, hipStream_t st) {
   A->view.blk_len = b + T + nb;
   A->view.tok_first = b + T + 2 * nb;
   A->view.tok_nblk = b + T + 2 * nb + A->vocab;
+  A->view.blk_order = b + T + 2 * nb + 2 * A->vocab;
   A->view.n_blocks = nb;
   A->view.vocab = A->vocab;
   A->host.reset();
@@ -158,7 +165,7 @@ int det_embedding_dw_acc_create(det_embedding_dw_acc** out, const int32_t* ids_h
   A->dim = dim;
   // every token has at most one partly filled block: blocks <= T/64 + distinct tokens
   A->max_blocks = n_logical / rbi::emb::kBlockOcc + std::min<int64_t>(n_logical, vocab);
-  A->plan_cap = static_cast<size_t>(n_logical + 2 * A->max_blocks + 2 * vocab + 1);
+  A->plan_cap = static_cast<size_t>(n_logical + 3 * A->max_blocks + 2 * vocab + 1);
   hipError_t e = hipSuccess;
   auto cleanup = [&](const char* what) {
     if (A->d_plan) (void)hipFree(A->d_plan);
