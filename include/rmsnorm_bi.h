@@ -95,6 +95,24 @@ int rmsnorm_bwd_dx(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_b
                    const float* rstd, rmsnorm_bf16* dx, int64_t rows, int64_t hidden,
                    const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, void* stream);
 
+/* Per-head norm inside a packed tensor (for example the Q or K heads of a
+ * fused QKV projection output, with no copy out of it).  The rows are
+ * tokens x heads rows of head_dim values; row r = t * heads + h (logical
+ * order, also the order of rstd, of a layout's map and of an accumulator's
+ * rows) starts at element t * token_stride + h * head_dim of x, y, dy and
+ * dx, which all share that placement.  Everything else, including the
+ * bits of every result, is as in rmsnorm_fwd / rmsnorm_bwd_dx on the
+ * extracted rows.  head_dim must be 8, 16, 32, 64, 128 or 256;
+ * token_stride a multiple of 8 and >= heads * head_dim. */
+int rmsnorm_fwd_packed(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y,
+                       float* rstd, int64_t tokens, int64_t heads, int64_t head_dim,
+                       int64_t token_stride, float eps, const rmsnorm_layout* layout,
+                       void* stream);
+int rmsnorm_bwd_dx_packed(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
+                          const float* rstd, rmsnorm_bf16* dx, int64_t tokens, int64_t heads,
+                          int64_t head_dim, int64_t token_stride, const rmsnorm_layout* layout,
+                          rmsnorm_dw_acc* acc, void* stream);
+
 /* dweight contributions only (no dx): same accumulation as rmsnorm_bwd_dx
  * with an accumulator; rstd is an input (any FP32 values). */
 int rmsnorm_dw_contrib(const rmsnorm_bf16* x, const rmsnorm_bf16* dy, const float* rstd,

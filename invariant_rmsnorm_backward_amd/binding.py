@@ -26,7 +26,7 @@ EXPORTED = ("rmsnorm_max_hidden", "rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_c
             "rmsnorm_dw_finalize", "rmsnorm_layout_create", "rmsnorm_layout_destroy",
             "rmsnorm_layout_check", "rmsnorm_dw_acc_create", "rmsnorm_dw_acc_reset",
             "rmsnorm_dw_acc_destroy", "rmsnorm_last_error", "rmsnorm_backend_info",
-            "rmsnorm_set_split_threshold",
+            "rmsnorm_set_split_threshold", "rmsnorm_fwd_packed", "rmsnorm_bwd_dx_packed",
             "det_gemm_fwd", "det_gemm_bwd_dx", "det_gemm_dw_acc_create", "det_gemm_dw_contrib",
             "det_gemm_dw_finalize", "det_gemm_dw_acc_reset", "det_gemm_dw_acc_destroy",
             "det_embedding_fwd", "det_embedding_dw_acc_create", "det_embedding_dw_acc_set_ids",
@@ -75,6 +75,8 @@ def load() -> ctypes.CDLL:
         "rmsnorm_last_error": ([], ctypes.c_char_p),
         "rmsnorm_backend_info": ([], ctypes.c_char_p),
         "rmsnorm_set_split_threshold": ([I64, ctypes.POINTER(ctypes.c_int64)], I32),
+        "rmsnorm_fwd_packed": ([P, P, P, P, I64, I64, I64, I64, ctypes.c_float, P, P], I32),
+        "rmsnorm_bwd_dx_packed": ([P, P, P, P, P, I64, I64, I64, I64, P, P, P], I32),
         "det_gemm_fwd": ([P, P, P, I64, I64, I64, P, P], I32),
         "det_gemm_bwd_dx": ([P, P, P, I64, I64, I64, P, P], I32),
         "det_gemm_dw_acc_create": ([PP, I64, I64, I64, P], I32),
@@ -174,6 +176,20 @@ def rmsnorm_dw_acc_destroy(acc: Optional[int]) -> None:
 
 
 # ------------------------------------------------------------------ helpers
+def rmsnorm_fwd_packed(x: int, w: int, y: int, rstd: int, tokens: int, heads: int, head_dim: int,
+                       token_stride: int, eps: float, layout: Optional[int],
+                       stream: Optional[int]) -> None:
+    _check(load().rmsnorm_fwd_packed(x, w, y, rstd, tokens, heads, head_dim, token_stride, eps,
+                                     layout, stream), "rmsnorm_fwd_packed")
+
+
+def rmsnorm_bwd_dx_packed(x: int, w: int, dy: int, rstd: int, dx: int, tokens: int, heads: int,
+                          head_dim: int, token_stride: int, layout: Optional[int],
+                          acc: Optional[int], stream: Optional[int]) -> None:
+    _check(load().rmsnorm_bwd_dx_packed(x, w, dy, rstd, dx, tokens, heads, head_dim, token_stride,
+                                        layout, acc, stream), "rmsnorm_bwd_dx_packed")
+
+
 def rmsnorm_set_split_threshold(blocks: int) -> int:
     """Sets the backward's two-pass threshold (in canonical blocks; 0 disables
     the two-pass path, negative restores the default); returns the previous one."""

@@ -3,6 +3,7 @@
 // anything is enqueued; there is no fallback path.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -75,9 +76,9 @@ int rmsnorm_set_split_threshold(int64_t blocks, int64_t* previous) {
   return RMSNORM_OK;
 }
 
-int rmsnorm_fwd(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y, float* rstd,
-                int64_t rows, int64_t hidden, float eps, const rmsnorm_layout* layout,
-                void* stream) {
+static int fwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y, float* rstd,
+                      int64_t rows, int64_t hidden, float eps, const rmsnorm_layout* layout,
+                      void* stream, const rbi::RowPacking& pk, int64_t extent) {
   int rc;
   if ((rc = check_rows(rows)) || (rc = check_hidden(hidden))) return rc;
   if (!(eps >= 0.0f) || std::isinf(eps)) return fail(RMSNORM_EINVAL, "eps must be finite and >= 0");
@@ -88,21 +89,39 @@ int rmsnorm_fwd(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y, f
   if ((rc = check_tensor(x, "x", 16)) || (rc = check_tensor(w, "w", 16)) ||
       (rc = check_tensor(y, "y", 16)) || (rc = check_tensor(rstd, "rstd", 4)))
     return rc;
-  const size_t nbytes = static_cast<size_t>(rows) * hidden * 2;
+  const size_t nbytes = static_cast<size_t>(extent) * 2;
   if (overlaps(y, nbytes, x, nbytes) || overlaps(y, nbytes, w, hidden * 2) ||
       overlaps(rstd, rows * 4, x, nbytes) || overlaps(rstd, rows * 4, y, nbytes))
     return fail(RMSNORM_EINVAL, "outputs must not alias inputs or each other");
   rbi::FwdArgs a{x, w, y, rstd, rows, static_cast<int32_t>(hidden), eps,
-                 layout ? layout->dev.row_logical : nullptr};
+                 layout ? layout->dev.row_logical : nullptr, pk};
   hipError_t e = rbi::launch_fwd(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "rmsnorm_fwd launch");
+  return RMSNORM_OK;
+}
+
+// Packed rows: tokens x heads rows of head_dim values, row (t, h) at
+// t * token_stride + h * head_dim.  Returns the element extent through *extent.
+static int check_packing(int64_t tokens, int64_t heads, int64_t head_dim, int64_t token_stride,
+                         rbi::RowPacking* pk, int64_t* rows, int64_t* extent) {
+  if (tokens < 0 || heads <= 0) return fail(RMSNORM_EINVAL, "tokens must be >= 0 and heads > 0");
+  if (heads > INT32_MAX) return fail(RMSNORM_EUNSUPPORTED, "too many heads");
+  if (!rbi::packed_hidden_supported(static_cast<int>(std::min<int64_t>(head_dim, 1 << 20))))
+    return fail(RMSNORM_EUNSUPPORTED, "packed rows need head_dim in {8, 16, 32, 64, 128, 256}");
+  if (token_stride % 8 != 0 || token_stride < heads * head_dim)
+    return fail(RMSNORM_EINVAL, "token_stride must be a multiple of 8 and >= heads * head_dim");
+  if (tokens > INT32_MAX / heads) return fail(RMSNORM_EUNSUPPORTED, "rows must be below 2^31");
+  pk->heads = static_cast<int32_t>(heads);
+  pk->token_stride = token_stride;
+  *rows = tokens * heads;
+  *extent = tokens == 0 ? 0 : (tokens - 1) * token_stride + heads * head_dim;
   return RMSNORM_OK;
 }
 
 static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
                       const float* rstd, rmsnorm_bf16* dx, int64_t rows, int64_t hidden,
                       const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, void* stream,
-                      bool with_dx) {
+                      bool with_dx, const rbi::RowPacking& pk, int64_t extent) {
   int rc;
   if ((rc = check_rows(rows)) || (rc = check_hidden(hidden))) return rc;
   if (layout != nullptr && layout->host.rows != rows)
@@ -121,7 +140,7 @@ static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnor
       return rc;
     if (with_dx) {
       if ((rc = check_tensor(w, "w", 16)) || (rc = check_tensor(dx, "dx", 16))) return rc;
-      const size_t nbytes = static_cast<size_t>(rows) * hidden * 2;
+      const size_t nbytes = static_cast<size_t>(extent) * 2;
       if (overlaps(dx, nbytes, x, nbytes) || overlaps(dx, nbytes, dy, nbytes) ||
           overlaps(dx, nbytes, w, hidden * 2) || overlaps(dx, nbytes, rstd, rows * 4))
         return fail(RMSNORM_EINVAL, "dx must not alias an input");
@@ -144,6 +163,7 @@ static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnor
   a.S = acc ? acc->d_S : nullptr;
   a.rows = rows;
   a.hidden = static_cast<int32_t>(hidden);
+  a.pack = pk;
   if (layout != nullptr) {
     a.plan = layout->dev;
   } else {
@@ -155,17 +175,48 @@ static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnor
   return RMSNORM_OK;
 }
 
+int rmsnorm_fwd(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y, float* rstd,
+                int64_t rows, int64_t hidden, float eps, const rmsnorm_layout* layout,
+                void* stream) {
+  return fwd_common(x, w, y, rstd, rows, hidden, eps, layout, stream, rbi::RowPacking{},
+                    rows * hidden);
+}
+
+int rmsnorm_fwd_packed(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y,
+                       float* rstd, int64_t tokens, int64_t heads, int64_t head_dim,
+                       int64_t token_stride, float eps, const rmsnorm_layout* layout,
+                       void* stream) {
+  rbi::RowPacking pk;
+  int64_t rows = 0, extent = 0;
+  int rc = check_packing(tokens, heads, head_dim, token_stride, &pk, &rows, &extent);
+  if (rc != RMSNORM_OK) return rc;
+  return fwd_common(x, w, y, rstd, rows, head_dim, eps, layout, stream, pk, extent);
+}
+
 int rmsnorm_bwd_dx(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
                    const float* rstd, rmsnorm_bf16* dx, int64_t rows, int64_t hidden,
                    const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, void* stream) {
-  return bwd_common(x, w, dy, rstd, dx, rows, hidden, layout, acc, stream, true);
+  return bwd_common(x, w, dy, rstd, dx, rows, hidden, layout, acc, stream, true,
+                    rbi::RowPacking{}, rows * hidden);
+}
+
+int rmsnorm_bwd_dx_packed(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
+                          const float* rstd, rmsnorm_bf16* dx, int64_t tokens, int64_t heads,
+                          int64_t head_dim, int64_t token_stride, const rmsnorm_layout* layout,
+                          rmsnorm_dw_acc* acc, void* stream) {
+  rbi::RowPacking pk;
+  int64_t rows = 0, extent = 0;
+  int rc = check_packing(tokens, heads, head_dim, token_stride, &pk, &rows, &extent);
+  if (rc != RMSNORM_OK) return rc;
+  return bwd_common(x, w, dy, rstd, dx, rows, head_dim, layout, acc, stream, true, pk, extent);
 }
 
 int rmsnorm_dw_contrib(const rmsnorm_bf16* x, const rmsnorm_bf16* dy, const float* rstd,
                        int64_t rows, int64_t hidden, const rmsnorm_layout* layout,
                        rmsnorm_dw_acc* acc, void* stream) {
   if (acc == nullptr) return fail(RMSNORM_EINVAL, "rmsnorm_dw_contrib needs an accumulator");
-  return bwd_common(x, nullptr, dy, rstd, nullptr, rows, hidden, layout, acc, stream, false);
+  return bwd_common(x, nullptr, dy, rstd, nullptr, rows, hidden, layout, acc, stream, false,
+                    rbi::RowPacking{}, rows * hidden);
 }
 
 int rmsnorm_dw_finalize(rmsnorm_dw_acc* acc, float* dweight, void* stream) {

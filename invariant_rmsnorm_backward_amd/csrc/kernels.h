@@ -30,6 +30,16 @@ struct PlanDev {
   int32_t n_pad = 0;
 };
 
+// Row placement of the bf16 row tensors (x, y, dy, dx): row r = (token t,
+// head h) with r = t * heads + h starts at t * token_stride + h * hidden.
+// heads = 1 and token_stride = hidden is the contiguous [rows][hidden]
+// layout; heads > 1 is a per-head norm applied inside a packed tensor (the
+// heads of a fused QKV projection), supported for hidden <= 256.
+struct RowPacking {
+  int32_t heads = 1;
+  int64_t token_stride = 0;   // 0: contiguous
+};
+
 struct FwdArgs {
   const uint16_t* x;
   const uint16_t* w;
@@ -39,6 +49,7 @@ struct FwdArgs {
   int32_t hidden;
   float eps;
   const int32_t* row_logical;  // nullptr: no padding
+  RowPacking pack{};
 };
 
 struct BwdArgs {
@@ -52,6 +63,7 @@ struct BwdArgs {
   int64_t rows;
   int32_t hidden;
   PlanDev plan;
+  RowPacking pack{};
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
@@ -66,6 +78,7 @@ hipError_t launch_tree(const float* P, int64_t nb, float* tmp, float* dweight, i
 int64_t tree_scratch_rows(int64_t nb);
 
 bool hidden_supported(int hidden);
+bool packed_hidden_supported(int hidden);   // hidden values the packed-row kernels take
 const char* fwd_variant(int hidden);
 const char* bwd_variant(int hidden);
 

@@ -26,6 +26,14 @@
 
 namespace rbi {
 
+// Element offset of row r of a row tensor (see RowPacking).  PACKED is a
+// compile-time switch so the contiguous kernels keep their plain addressing.
+template <bool PACKED>
+__device__ __forceinline__ int64_t row_off(const RowPacking& pk, int64_t r, int H) {
+  if (!PACKED) return r * H;
+  return (r / pk.heads) * pk.token_stride + (r % pk.heads) * H;
+}
+
 // ----------------------------------------------------------------- forward
 template <int V>
 __global__ __launch_bounds__(256) void fwd_wide_kernel(FwdArgs a) {
@@ -86,7 +94,7 @@ __global__ __launch_bounds__(256) void fwd_wide_kernel(FwdArgs a) {
 }
 
 // hidden = 8L with L lanes per row (L in 1..32, a power of two).
-template <int L>
+template <int L, bool PACKED>
 __global__ __launch_bounds__(256) void fwd_small_kernel(FwdArgs a) {
   constexpr int H = 8 * L;
   constexpr int GROUPS = 256 / L;
@@ -100,7 +108,8 @@ __global__ __launch_bounds__(256) void fwd_small_kernel(FwdArgs a) {
     const bool valid = row < a.rows;
     const bool pad = valid && a.row_logical != nullptr && a.row_logical[row] < 0;
     uint4 xv = make_uint4(0, 0, 0, 0);
-    if (valid && !pad) xv = load16_stream(a.x + row * H + sub * 8);
+    const int64_t off = valid ? row_off<PACKED>(a.pack, row, H) : 0;
+    if (valid && !pad) xv = load16_stream(a.x + off + sub * 8);
     float f[8];
     unpack8(xv, f);
     float ss = 0.0f;
@@ -112,7 +121,7 @@ __global__ __launch_bounds__(256) void fwd_small_kernel(FwdArgs a) {
       float o[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = pad ? 0.0f : (f[e] * r) * wf[e];
-      store16_stream(a.y + row * H + sub * 8, pack8(o));
+      store16_stream(a.y + off + sub * 8, pack8(o));
       if (sub == 0) a.rstd[row] = pad ? 0.0f : r;
     }
   }
@@ -522,7 +531,7 @@ __global__ __launch_bounds__(256) void dw_cols_kernel(BwdArgs a) {
 
 // Small rows: hidden = 8L (L in 1..32), one group of L lanes per row; the
 // 64 slots' contributions go through LDS and the 4 streams fold them there.
-template <int L, bool DX, bool DW>
+template <int L, bool DX, bool DW, bool PACKED>
 __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
   constexpr int H = 8 * L;
   constexpr int GROUPS = 256 / L;
@@ -538,7 +547,8 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
     if (DX) {
       const int idx = (item - a.plan.n_items) * GROUPS + g;
       if (idx < a.plan.n_pad)
-        store16_stream(a.dx + (int64_t)a.plan.pad_rows[idx] * H + sub * 8, make_uint4(0, 0, 0, 0));
+        store16_stream(a.dx + row_off<PACKED>(a.pack, a.plan.pad_rows[idx], H) + sub * 8,
+                       make_uint4(0, 0, 0, 0));
     }
     return;
   }
@@ -569,8 +579,9 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int row = pp[it] >= 0 ? pp[it] : 0;
-    xv[it] = load16_stream(a.x + (int64_t)row * H + sub * 8);
-    dv[it] = load16_stream(a.dy + (int64_t)row * H + sub * 8);
+    const int64_t off = row_off<PACKED>(a.pack, row, H);
+    xv[it] = load16_stream(a.x + off + sub * 8);
+    dv[it] = load16_stream(a.dy + off + sub * 8);
     rr[it] = a.rstd[row];
   }
 #pragma unroll
@@ -593,7 +604,7 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = fmaf(-xf[e], kk, r * (df[e] * wf[e]));
-        store16_stream(a.dx + (int64_t)p * H + sub * 8, pack8(o));
+        store16_stream(a.dx + row_off<PACKED>(a.pack, p, H) + sub * 8, pack8(o));
       }
     }
     if (DW) {
@@ -704,6 +715,8 @@ bool hidden_supported(int hidden) {
   return hidden > 0 && hidden % 8 == 0 && hidden <= kMaxHidden;
 }
 
+bool packed_hidden_supported(int hidden) { return small_lanes(hidden) != 0; }
+
 // Wavefronts per row: one up to 1024 columns, two above.
 static int wide_tw(int hidden) { return hidden <= 1024 ? 1 : 2; }
 static int wide_v(int hidden) {
@@ -728,16 +741,24 @@ static void fwd_wide_go(const FwdArgs& a, hipStream_t st) {
   if (g > grid_cap()) g = grid_cap();
   fwd_wide_kernel<V><<<dim3((unsigned)g), dim3(256), 0, st>>>(a);
 }
+static bool is_packed(const RowPacking& pk, int hidden) {
+  return pk.heads > 1 || (pk.token_stride != 0 && pk.token_stride != hidden);
+}
+
 template <int L>
 static void fwd_small_go(const FwdArgs& a, hipStream_t st) {
   constexpr int GROUPS = 256 / L;
   int64_t g = (a.rows + GROUPS - 1) / GROUPS;
   if (g > grid_cap()) g = grid_cap();
-  fwd_small_kernel<L><<<dim3((unsigned)g), dim3(256), 0, st>>>(a);
+  if (is_packed(a.pack, a.hidden))
+    fwd_small_kernel<L, true><<<dim3((unsigned)g), dim3(256), 0, st>>>(a);
+  else
+    fwd_small_kernel<L, false><<<dim3((unsigned)g), dim3(256), 0, st>>>(a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
+  if (is_packed(a.pack, a.hidden) && !packed_hidden_supported(a.hidden)) return hipErrorInvalidValue;
   switch (small_lanes(a.hidden)) {
     case 1: fwd_small_go<1>(a, st); return hipGetLastError();
     case 2: fwd_small_go<2>(a, st); return hipGetLastError();
@@ -809,12 +830,19 @@ static void bwd_small_go(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
   constexpr int GROUPS = 256 / L;
   const int pad_groups = dx ? (a.plan.n_pad + GROUPS - 1) / GROUPS : 0;
   const dim3 grid((unsigned)(a.plan.n_items + pad_groups)), block(256);
-  if (dx && dw) bwd_small_kernel<L, true, true><<<grid, block, 0, st>>>(a);
-  else if (dx) bwd_small_kernel<L, true, false><<<grid, block, 0, st>>>(a);
-  else bwd_small_kernel<L, false, true><<<grid, block, 0, st>>>(a);
+  if (is_packed(a.pack, a.hidden)) {
+    if (dx && dw) bwd_small_kernel<L, true, true, true><<<grid, block, 0, st>>>(a);
+    else if (dx) bwd_small_kernel<L, true, false, true><<<grid, block, 0, st>>>(a);
+    else bwd_small_kernel<L, false, true, true><<<grid, block, 0, st>>>(a);
+  } else {
+    if (dx && dw) bwd_small_kernel<L, true, true, false><<<grid, block, 0, st>>>(a);
+    else if (dx) bwd_small_kernel<L, true, false, false><<<grid, block, 0, st>>>(a);
+    else bwd_small_kernel<L, false, true, false><<<grid, block, 0, st>>>(a);
+  }
 }
 
 hipError_t launch_bwd(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+  if (is_packed(a.pack, a.hidden) && !packed_hidden_supported(a.hidden)) return hipErrorInvalidValue;
   const int pads = dx ? a.plan.n_pad : 0;
   if (a.plan.n_items + pads == 0) return hipSuccess;
   switch (small_lanes(a.hidden)) {

@@ -137,3 +137,23 @@ def test_split_threshold_knob():
         assert binding.rmsnorm_set_split_threshold(prev) > 0
     finally:
         binding.rmsnorm_set_split_threshold(prev)
+
+
+def test_packed_entry_points_check_their_arguments(lib):
+    A = 1 << 12
+    cases = [
+        (dict(head_dim=96), binding.EUNSUPPORTED),        # no packed kernel for 96
+        (dict(token_stride=100), binding.EINVAL),         # not a multiple of 8
+        (dict(token_stride=8), binding.EINVAL),           # shorter than heads * head_dim
+        (dict(heads=0), binding.EINVAL),
+        (dict(tokens=-1), binding.EINVAL),
+    ]
+    for over, code in cases:
+        a = dict(tokens=4, heads=2, head_dim=128, token_stride=512)
+        a.update(over)
+        with pytest.raises(binding.RmsNormError) as ei:
+            binding.rmsnorm_fwd_packed(A, A, A, A, a["tokens"], a["heads"], a["head_dim"],
+                                       a["token_stride"], 1e-6, None, None)
+        assert ei.value.code == code, over
+    # zero tokens is a successful no-op
+    binding.rmsnorm_fwd_packed(A, A, A, A, 0, 2, 128, 512, 1e-6, None, None)
