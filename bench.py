@@ -482,6 +482,93 @@ def measure_det_embedding(args, torch, np, binding, inputs):
     print(json.dumps(out))
 
 
+def measure_qk_packed(args, torch, np, binding, inputs):
+    """The QK-norm workload with Q (32 heads) and K (8 heads) inside one packed
+    QKV tensor [16384, 48 x 128] (V heads untouched): per step, for Q then K,
+    rmsnorm_fwd_packed, rmsnorm_bwd_dx_packed with the accumulator, finalize.
+    The same two norms on contiguous Q and K are timed beside it."""
+    wq, wk = inputs.workload_qk("q"), inputs.workload_qk("k")
+    T, d = wq.n_tokens, wq.hidden
+    hq, hk = wq.heads, wk.heads
+    ts = (hq + 2 * hk) * d
+    st = torch.cuda.current_stream()
+    sh = st.cuda_stream
+    sides = []
+    for wl, heads, col0 in ((wq, hq, 0), (wk, hk, hq * d)):
+        x = inputs.gen_x(wl, device="cuda")
+        dy = inputs.gen_dy(wl, device="cuda")
+        w = inputs.gen_w(wl, device="cuda")
+        sides.append(dict(wl=wl, heads=heads, col0=col0, x=x, dy=dy, w=w, rows=T * heads,
+                          acc=binding.DwAccumulator(T * heads, d),
+                          rstd=torch.empty(T * heads, dtype=torch.float32, device="cuda"),
+                          y=torch.empty_like(x), dx=torch.empty_like(x),
+                          dw=torch.empty(d, dtype=torch.float32, device="cuda")))
+    qkv = torch.zeros((T, ts), dtype=torch.bfloat16, device="cuda")
+    dqkv = torch.zeros_like(qkv)
+    yqkv = torch.zeros_like(qkv)
+    gqkv = torch.zeros_like(qkv)
+    for s_ in sides:
+        sl = slice(s_["col0"], s_["col0"] + s_["heads"] * d)
+        qkv[:, sl] = s_["x"].view(T, -1)
+        dqkv[:, sl] = s_["dy"].view(T, -1)
+
+    def base(t, s_):
+        return t.data_ptr() + 2 * s_["col0"]
+
+    def packed_step():
+        for s_ in sides:
+            binding.rmsnorm_fwd_packed(base(qkv, s_), s_["w"].data_ptr(), base(yqkv, s_),
+                                       s_["rstd"].data_ptr(), T, s_["heads"], d, ts, wq.eps, None, sh)
+            binding.rmsnorm_bwd_dx_packed(base(qkv, s_), s_["w"].data_ptr(), base(dqkv, s_),
+                                          s_["rstd"].data_ptr(), base(gqkv, s_), T, s_["heads"], d,
+                                          ts, None, s_["acc"].handle, sh)
+            binding.rmsnorm_dw_finalize(s_["acc"].handle, s_["dw"].data_ptr(), sh)
+            binding.rmsnorm_dw_acc_reset(s_["acc"].handle, sh)
+
+    def contiguous_step():
+        for s_ in sides:
+            binding.rmsnorm_fwd(s_["x"].data_ptr(), s_["w"].data_ptr(), s_["y"].data_ptr(),
+                                s_["rstd"].data_ptr(), s_["rows"], d, wq.eps, None, sh)
+            binding.rmsnorm_bwd_dx(s_["x"].data_ptr(), s_["w"].data_ptr(), s_["dy"].data_ptr(),
+                                   s_["rstd"].data_ptr(), s_["dx"].data_ptr(), s_["rows"], d, None,
+                                   s_["acc"].handle, sh)
+            binding.rmsnorm_dw_finalize(s_["acc"].handle, s_["dw"].data_ptr(), sh)
+            binding.rmsnorm_dw_acc_reset(s_["acc"].handle, sh)
+
+    def timed(f, iters):
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(iters):
+            f()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / iters * 1e3
+
+    ms_p = timed(packed_step, args.steps)
+    ms_c = timed(contiguous_step, args.steps)
+    nbytes = 0
+    for s_ in sides:
+        f, b = algorithmic_bytes(s_["rows"], s_["rows"], d)
+        nbytes += f + b
+    out = {
+        "metric": METRIC + " (per-head norm inside a packed QKV tensor)",
+        "value": round(nbytes / (ms_p * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_p, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "qknorm_d128_t16384 packed", "tokens": T, "q_heads": hq, "k_heads": hk,
+                   "head_dim": d, "token_stride": ts},
+        "roofline": None, "cpu_baseline": None,
+        "contiguous_ms_per_step": round(ms_c, 4),
+        "contiguous_gbps": round(nbytes / (ms_c * 1e-3) / 1e9, 2),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    for s_ in sides:
+        s_["acc"].close()
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -493,7 +580,8 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="measure another workload (info line; the default run is the headline)")
     ap.add_argument("--cell", default="BN/full", help="layout cell for --workload")
-    ap.add_argument("--op", default="rms_norm", choices=["rms_norm", "det_gemm", "det_embedding"],
+    ap.add_argument("--op", default="rms_norm",
+                    choices=["rms_norm", "det_gemm", "det_embedding", "qk_packed"],
                     help="det_gemm: the linear layer 4096 -> 4096 on 32768 rows; det_embedding: "
                          "a 32000 x 4096 table on 32768 rows (info lines)")
     args = ap.parse_args()
@@ -517,6 +605,9 @@ def main():
         return
     if args.op == "det_embedding":
         measure_det_embedding(args, torch, np, binding, inputs)
+        return
+    if args.op == "qk_packed":
+        measure_qk_packed(args, torch, np, binding, inputs)
         return
     if args.workload is not None:
         measure_cell(args, torch, np, binding, inputs, layouts)

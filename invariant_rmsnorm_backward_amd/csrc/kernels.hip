@@ -31,7 +31,10 @@ namespace rbi {
 template <bool PACKED>
 __device__ __forceinline__ int64_t row_off(const RowPacking& pk, int64_t r, int H) {
   if (!PACKED) return r * H;
-  return (r / pk.heads) * pk.token_stride + (r % pk.heads) * H;
+  // rows < 2^31: a 32-bit division is enough (and much cheaper than 64-bit)
+  const uint32_t t = static_cast<uint32_t>(r) / static_cast<uint32_t>(pk.heads);
+  const uint32_t h = static_cast<uint32_t>(r) - t * static_cast<uint32_t>(pk.heads);
+  return static_cast<int64_t>(t) * pk.token_stride + static_cast<int64_t>(h) * H;
 }
 
 // ----------------------------------------------------------------- forward
