@@ -19,10 +19,11 @@
 // caller's buffer when one call holds every row in order, else rows staged
 // by logical index), so no layout can change a bit.
 //
-// All three products run on one MFMA tile engine: 256 x 256 output tiles for
-// y and dX, 256 x 128 for dW (128 x 128 for small outputs), 4 wavefronts
-// each owning a quarter made of 32 x 32 blocks, 32-deep K stages
-// double-buffered in LDS with K contiguous.  Operands whose K index is the
+// All three products run on one MFMA tile engine: 256 x 256 output tiles
+// with 64-deep K stages for y and dX, 256 x 128 tiles with 32-deep stages
+// for dW (128 x 128 x 32 for small outputs); 4 wavefronts each owning a
+// quarter made of 32 x 32 blocks; stages double-buffered in LDS with K
+// contiguous.  Operands whose K index is the
 // slow one in memory (W in dX, both operands of dW) are transposed on the
 // way into LDS, two K rows at a time packed into 32-bit words.
 #include "linear.h"
@@ -36,16 +37,17 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4v_t __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 32;
-constexpr int LDSK = BK + 8;          // LDS row stride (bf16) of a K-contiguous tile
 constexpr int THREADS = 256;
+// LDS row stride (bf16) of a K-contiguous tile of depth BK
+template <int BK>
+constexpr int ldsk() { return BK + 8; }
 
 // Output tile BM x BN per workgroup; the 4 wavefronts each own a
 // (BM/2) x (BN/2) quarter made of 32 x 32 matrix-core blocks.
-template <int BM, int BN>
+template <int BM, int BN, int BK>
 struct alignas(16) Tile {
-  uint16_t a[2][BM * LDSK];
-  uint16_t b[2][BN * LDSK];
+  uint16_t a[2][BM * ldsk<BK>()];
+  uint16_t b[2][BN * ldsk<BK>()];
 };
 
 __device__ __forceinline__ u32x4v_t ld16(const uint16_t* p) {
@@ -63,9 +65,14 @@ __device__ __forceinline__ u32x4v_t ld16_nt(const uint16_t* p) {
 //   transposed: element (m, k) at g[k * ld + m]; thread t loads rows
 //               k = 2p, 2p + 1 (p = t % 16) of columns 8q .. 8q + 7
 //               (q = t / 16 + 16 i) and packs them per column.
-template <bool TRANS, int ROWS>
+template <bool TRANS, int ROWS, int BK>
 struct Stage {
-  static constexpr int NV = TRANS ? 2 * (ROWS / 128) : ROWS / 64;
+  static constexpr int LDSK = ldsk<BK>();
+  static constexpr int CPR = BK / 8;                 // 16-byte chunks per tile row (direct)
+  static constexpr int PAIRS = BK / 2;               // K row pairs (transposed)
+  static constexpr int QPP = THREADS / PAIRS;        // column chunks per pass (transposed)
+  static constexpr int NPASS = (ROWS / 8) / QPP;
+  static constexpr int NV = TRANS ? 2 * NPASS : ROWS * CPR / THREADS;
   u32x4v_t v[NV];
 
   // m0: first tile row; k0: first K index of the stage; m_lim / k_lim:
@@ -77,17 +84,17 @@ struct Stage {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int c = t + THREADS * i;
-        const int64_t m = m0 + (c >> 2);
-        const int64_t k = k0 + 8 * (c & 3);
+        const int64_t m = m0 + c / CPR;
+        const int64_t k = k0 + 8 * (c % CPR);
         bool ok = m < m_lim && k < k_lim;
         if (ok && rowmap != nullptr) ok = rowmap[m] >= 0;
         v[i] = ok ? ld16(g + m * ld + k) : u32x4v_t{0u, 0u, 0u, 0u};
       }
     } else {
-      const int p = t & 15;
+      const int p = t % PAIRS;
 #pragma unroll
-      for (int i = 0; i < NV / 2; ++i) {
-        const int64_t m = m0 + 8 * ((t >> 4) + 16 * i);
+      for (int i = 0; i < NPASS; ++i) {
+        const int64_t m = m0 + 8 * (t / PAIRS + QPP * i);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int64_t k = k0 + 2 * p + h;
@@ -103,13 +110,13 @@ struct Stage {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int c = t + THREADS * i;
-        *reinterpret_cast<u32x4v_t*>(s + (c >> 2) * LDSK + 8 * (c & 3)) = v[i];
+        *reinterpret_cast<u32x4v_t*>(s + (c / CPR) * LDSK + 8 * (c % CPR)) = v[i];
       }
     } else {
-      const int p = t & 15;
+      const int p = t % PAIRS;
 #pragma unroll
-      for (int i = 0; i < NV / 2; ++i) {
-        const int q = (t >> 4) + 16 * i;
+      for (int i = 0; i < NPASS; ++i) {
+        const int q = t / PAIRS + QPP * i;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const unsigned lo = (v[2 * i][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;       // row 2p, column 8q + j
@@ -135,10 +142,11 @@ struct Acc {
   }
 };
 
-// Two 16-deep MFMA steps over one LDS stage, in ascending K.
-template <int MI, int NJ>
+// The 16-deep MFMA steps over one LDS stage, in ascending K.
+template <int MI, int NJ, int BK>
 __device__ __forceinline__ void mma_stage(const uint16_t* as, const uint16_t* bs, Acc<MI, NJ>& acc,
                                           int wm, int wn, int lane) {
+  constexpr int LDSK = ldsk<BK>();
   const int r = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int ks = 0; ks < BK; ks += 16) {
@@ -158,10 +166,10 @@ __device__ __forceinline__ void mma_stage(const uint16_t* as, const uint16_t* bs
 }
 
 // C[m][n] += sum over k in [k_begin, k_end) of A(m, k) B(k, n), K stages of
-// 32 in ascending order (k_end - k_begin is a multiple of 32; indices at or
+// BK in ascending order (k_end - k_begin is a multiple of BK; indices at or
 // past k_lim read as zero).
-template <int BM, int BN, bool AT, bool BT>
-__device__ __forceinline__ void gemm_tile(Tile<BM, BN>& sm, Acc<BM / 64, BN / 64>& acc,
+template <int BM, int BN, int BK, bool AT, bool BT>
+__device__ __forceinline__ void gemm_tile(Tile<BM, BN, BK>& sm, Acc<BM / 64, BN / 64>& acc,
                                           const uint16_t* a, int64_t lda, const uint16_t* b,
                                           int64_t ldb, int64_t m0, int64_t m_lim, int64_t n0,
                                           int64_t n_lim, int64_t k_begin, int64_t k_end,
@@ -169,8 +177,8 @@ __device__ __forceinline__ void gemm_tile(Tile<BM, BN>& sm, Acc<BM / 64, BN / 64
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
   const int wm = (w >> 1) * (BM / 2), wn = (w & 1) * (BN / 2);
-  Stage<AT, BM> sa;
-  Stage<BT, BN> sb;
+  Stage<AT, BM, BK> sa;
+  Stage<BT, BN, BK> sb;
   sa.load(a, lda, m0, m_lim, k_begin, k_lim, rowmap_a, t);
   sb.load(b, ldb, n0, n_lim, k_begin, k_lim, nullptr, t);
   sa.store(sm.a[0], t);
@@ -183,7 +191,7 @@ __device__ __forceinline__ void gemm_tile(Tile<BM, BN>& sm, Acc<BM / 64, BN / 64
       sa.load(a, lda, m0, m_lim, k0 + BK, k_lim, rowmap_a, t);
       sb.load(b, ldb, n0, n_lim, k0 + BK, k_lim, nullptr, t);
     }
-    mma_stage(sm.a[buf], sm.b[buf], acc, wm, wn, lane);
+    mma_stage<BM / 64, BN / 64, BK>(sm.a[buf], sm.b[buf], acc, wm, wn, lane);
     if (more) {
       sa.store(sm.a[buf ^ 1], t);
       sb.store(sm.b[buf ^ 1], t);
@@ -217,14 +225,14 @@ __device__ __forceinline__ uint16_t to_bf16_rne(float f) {
 }
 
 // y = x W^T (fwd) and dX = dY W: bf16 result rows of the call, padding rows 0.
-template <int BM, int BN, bool BT>
+template <int BM, int BN, int BK, bool BT>
 __global__ __launch_bounds__(THREADS) void rowwise_kernel(RowwiseArgs p) {
-  __shared__ Tile<BM, BN> sm;
+  __shared__ Tile<BM, BN, BK> sm;
   const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
   Acc<BM / 64, BN / 64> acc;
   acc.zero();
-  gemm_tile<BM, BN, false, BT>(sm, acc, p.a, p.lda, p.b, p.ldb, m0, p.rows, n0, p.n, 0,
-                               (p.k + BK - 1) / BK * BK, p.k, p.row_logical);
+  gemm_tile<BM, BN, BK, false, BT>(sm, acc, p.a, p.lda, p.b, p.ldb, m0, p.rows, n0, p.n, 0,
+                                   (p.k + BK - 1) / BK * BK, p.k, p.row_logical);
   // padding rows were loaded as zeros; they are written as 0 explicitly
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
@@ -246,9 +254,9 @@ __global__ __launch_bounds__(THREADS) void rowwise_kernel(RowwiseArgs p) {
 
 // Q_g for one BM x BN tile of dW and one group g = blockIdx.z of logical
 // rows (dY and X in logical row order, T rows).
-template <int BM, int BN>
+template <int BM, int BN, int BK>
 __global__ __launch_bounds__(THREADS) void dw_group_kernel(DwArgs p) {
-  __shared__ Tile<BM, BN> sm;
+  __shared__ Tile<BM, BN, BK> sm;
   const int64_t n0 = (int64_t)blockIdx.x * BM, k0 = (int64_t)blockIdx.y * BN;
   const int64_t g = blockIdx.z;
   const int64_t r0 = g * kGroupRows;
@@ -256,8 +264,8 @@ __global__ __launch_bounds__(THREADS) void dw_group_kernel(DwArgs p) {
   if (r1 > p.T) r1 = (p.T + BK - 1) / BK * BK;   // the rest of the group is zero rows
   Acc<BM / 64, BN / 64> acc;
   acc.zero();
-  gemm_tile<BM, BN, true, true>(sm, acc, p.dy, p.n, p.x, p.k, n0, p.n, k0, p.k, r0, r1, p.T,
-                                nullptr);
+  gemm_tile<BM, BN, BK, true, true>(sm, acc, p.dy, p.n, p.x, p.k, n0, p.n, k0, p.k, r0, r1, p.T,
+                                    nullptr);
   float* out = p.out + g * p.n * p.k;
   for_each_result<BM, BN>(acc, [&](int mi, int ni, float v) {
     const int64_t n = n0 + mi, k = k0 + ni;
@@ -313,34 +321,35 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ dst, 
 // every output element runs the same chain whatever tile holds it).
 static bool big_tiles(int64_t m, int64_t n) { return m >= 256 && n >= 256; }
 
-template <int BM, int BN>
+template <int BM, int BN, int BK>
 static void rowwise_go(const RowwiseArgs& a, bool bt, hipStream_t st) {
   const dim3 grid((unsigned)((a.rows + BM - 1) / BM), (unsigned)((a.n + BN - 1) / BN));
-  if (bt) rowwise_kernel<BM, BN, true><<<grid, dim3(THREADS), 0, st>>>(a);
-  else rowwise_kernel<BM, BN, false><<<grid, dim3(THREADS), 0, st>>>(a);
+  if (bt) rowwise_kernel<BM, BN, BK, true><<<grid, dim3(THREADS), 0, st>>>(a);
+  else rowwise_kernel<BM, BN, BK, false><<<grid, dim3(THREADS), 0, st>>>(a);
 }
 
 hipError_t launch_rowwise(const RowwiseArgs& a, bool b_transposed, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
-  if (big_tiles(a.rows, a.n)) rowwise_go<256, 256>(a, b_transposed, st);
-  else rowwise_go<128, 128>(a, b_transposed, st);
+  // 64-deep stages: the 256 x 256 kernel holds one workgroup per CU either way
+  if (big_tiles(a.rows, a.n)) rowwise_go<256, 256, 64>(a, b_transposed, st);
+  else rowwise_go<128, 128, 32>(a, b_transposed, st);
   return hipGetLastError();
 }
 
 int64_t num_groups(int64_t T) { return (T + kGroupRows - 1) / kGroupRows; }
 
-template <int BM, int BN>
+template <int BM, int BN, int BK>
 static void dw_go(const DwArgs& a, int64_t G, hipStream_t st) {
   const dim3 grid((unsigned)((a.n + BM - 1) / BM), (unsigned)((a.k + BN - 1) / BN), (unsigned)G);
-  dw_group_kernel<BM, BN><<<grid, dim3(THREADS), 0, st>>>(a);
+  dw_group_kernel<BM, BN, BK><<<grid, dim3(THREADS), 0, st>>>(a);
 }
 
 hipError_t launch_dw_groups(const DwArgs& a, hipStream_t st) {
   const int64_t G = num_groups(a.T);
   if (G == 0) return hipSuccess;
-  // 256 x 128 keeps the dW kernel at two wavefronts per SIMD (212 VGPRs)
-  if (big_tiles(a.n, a.k)) dw_go<256, 128>(a, G, st);
-  else dw_go<128, 128>(a, G, st);
+  // 256 x 128 x 32 keeps the dW kernel at two wavefronts per SIMD (212 VGPRs)
+  if (big_tiles(a.n, a.k)) dw_go<256, 128, 32>(a, G, st);
+  else dw_go<128, 128, 32>(a, G, st);
   return hipGetLastError();
 }
 
