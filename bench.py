@@ -376,7 +376,7 @@ def measure_det_gemm(args, torch, np, binding, inputs):
         "roofline": {"bound": "mfma", "achieved": round(gf / (ph["dw"] * 1e-3) / 1e12, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gf / (ph["dw"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "dw_group_kernel<256,128> + group tree (dW)",
+                     "traffic": None, "kernel": "dw_group_kernel<256x256, 64-deep stages, 8 wavefronts> + group tree (dW)",
                      "algorithmic_flops_per_launch": gf, "avg_launch_ms": round(ph["dw"], 5)},
         "cpu_baseline": cpu,
         "phases_ms": {k: round(v, 5) for k, v in ph.items()},

@@ -15,120 +15,71 @@
 //   * dW = perfect pairwise tree over Q_0 .. Q_{G-1}, +0.0 leaves up to the
 //     next power of two.
 // Each output element's chain is the same whatever tile or workgroup
-// computes it, and the kernel always reads the rows in logical order (the
-// caller's buffer when one call holds every row in order, else rows staged
-// by logical index), so no layout can change a bit.
+// computes it (steps of zero rows or columns past the end add +0.0 products
+// to an accumulator that started at +0.0, which changes no bit), and the
+// kernel always reads the rows in logical order (the caller's buffer when one
+// call holds every row in order, else rows staged by logical index), so no
+// layout can change a bit.
 //
-// All three products run on one MFMA tile engine: 256 x 256 output tiles
-// with 64-deep K stages for y and dX, 256 x 128 tiles with 32-deep stages
-// for dW (128 x 128 x 32 for small outputs); 4 wavefronts each owning a
-// quarter made of 32 x 32 blocks; stages double-buffered in LDS with K
-// contiguous.  Operands whose K index is the
-// slow one in memory (W in dX, both operands of dW) are transposed on the
-// way into LDS, two K rows at a time packed into 32-bit words.
+// All three products run on one MFMA tile engine (Engine below):
+//   * 256 x 256 output tiles, 8 wavefronts (two per SIMD) each owning a
+//     128 x 64 share of 32 x 32 blocks; 128 x 128 tiles with 4 wavefronts for
+//     small outputs;
+//   * K stages of 64 (32 for the small tiles) in an LDS ring of NS stages,
+//     filled by global_load_lds_dwordx4 (16 bytes per lane straight into LDS,
+//     no staging registers); one workgroup barrier per stage;
+//   * LDS rows XOR-swizzled in 16-byte chunks so that the matrix-core
+//     fragment reads hit distinct banks in every 16-lane phase;
+//   * operands whose K index is the slow one in memory (W in dX, both
+//     operands of dW) stay in that order in LDS and are read with the
+//     transposing ds_read_b64_tr_b16, so no operand is rearranged by the ALU;
+//   * the 16-deep steps are software pipelined: the fragments of step s + 1
+//     are read while the MFMAs of step s run, and the loads of stage
+//     it + NS are issued one after each MFMA of the last step of stage it;
+//   * tiles are mapped to workgroups so that the 32 workgroups one XCD runs
+//     at a time share 4 row blocks and 8 column blocks (the round-robin
+//     dispatch puts workgroup id on XCD id % 8).
 #include "linear.h"
 
 #include <hip/hip_runtime.h>
+
+#include <cstdint>
 
 namespace rbi {
 namespace lin {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4v_t __attribute__((ext_vector_type(4)));
+#define RBI_LDS __attribute__((address_space(3)))
 
-constexpr int THREADS = 256;
-// LDS row stride (bf16) of a K-contiguous tile of depth BK
-template <int BK>
-constexpr int ldsk() { return BK + 8; }
+// 16 zero bytes: the source of every load whose rows or columns are out of range.
+__device__ __align__(16) uint32_t kZero16[4];
 
-// Output tile BM x BN per workgroup; the 4 wavefronts each own a
-// (BM/2) x (BN/2) quarter made of 32 x 32 matrix-core blocks.
-template <int BM, int BN, int BK>
-struct alignas(16) Tile {
-  uint16_t a[2][BM * ldsk<BK>()];
-  uint16_t b[2][BN * ldsk<BK>()];
-};
-
-__device__ __forceinline__ u32x4v_t ld16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4v_t*>(p);
+// s_waitcnt vmcnt(N) lgkmcnt(0)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
-__device__ __forceinline__ u32x4v_t ld16_nt(const uint16_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t*>(p));
+// Workgroup barrier without a memory fence: the engine waits for its own loads
+// explicitly (a fenced barrier would wait for every load still in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (the LDS
+// base goes through m0, which is saved and restored around the load).  The
+// compiler does not track this load; the engine waits for it with vmcnt.
+__device__ __forceinline__ void load_to_lds(uint64_t src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds));
 }
+#define RBI_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// One operand's share of a K stage (ROWS tile rows x 32 K) held in
-// registers between the global load and the LDS store.  Tile rows are the
-// operand's M (or N) index.
-//   direct:     element (m, k) at g[m * ld + k]; thread t loads chunks
-//               c = t + 256 i (row c / 4, k offset 8 * (c % 4)).
-//   transposed: element (m, k) at g[k * ld + m]; thread t loads rows
-//               k = 2p, 2p + 1 (p = t % 16) of columns 8q .. 8q + 7
-//               (q = t / 16 + 16 i) and packs them per column.
-template <bool TRANS, int ROWS, int BK>
-struct Stage {
-  static constexpr int LDSK = ldsk<BK>();
-  static constexpr int CPR = BK / 8;                 // 16-byte chunks per tile row (direct)
-  static constexpr int PAIRS = BK / 2;               // K row pairs (transposed)
-  static constexpr int QPP = THREADS / PAIRS;        // column chunks per pass (transposed)
-  static constexpr int NPASS = (ROWS / 8) / QPP;
-  static constexpr int NV = TRANS ? 2 * NPASS : ROWS * CPR / THREADS;
-  u32x4v_t v[NV];
-
-  // m0: first tile row; k0: first K index of the stage; m_lim / k_lim:
-  // indices at or past them read as zero; rowmap (direct only): a tile
-  // row whose map value is negative reads as zero.
-  __device__ __forceinline__ void load(const uint16_t* g, int64_t ld, int64_t m0, int64_t m_lim,
-                                       int64_t k0, int64_t k_lim, const int32_t* rowmap, int t) {
-    if (!TRANS) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int c = t + THREADS * i;
-        const int64_t m = m0 + c / CPR;
-        const int64_t k = k0 + 8 * (c % CPR);
-        bool ok = m < m_lim && k < k_lim;
-        if (ok && rowmap != nullptr) ok = rowmap[m] >= 0;
-        v[i] = ok ? ld16(g + m * ld + k) : u32x4v_t{0u, 0u, 0u, 0u};
-      }
-    } else {
-      const int p = t % PAIRS;
-#pragma unroll
-      for (int i = 0; i < NPASS; ++i) {
-        const int64_t m = m0 + 8 * (t / PAIRS + QPP * i);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int64_t k = k0 + 2 * p + h;
-          const bool ok = m < m_lim && k < k_lim;
-          v[2 * i + h] = ok ? ld16(g + k * ld + m) : u32x4v_t{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(uint16_t* s, int t) const {
-    if (!TRANS) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int c = t + THREADS * i;
-        *reinterpret_cast<u32x4v_t*>(s + (c / CPR) * LDSK + 8 * (c % CPR)) = v[i];
-      }
-    } else {
-      const int p = t % PAIRS;
-#pragma unroll
-      for (int i = 0; i < NPASS; ++i) {
-        const int q = t / PAIRS + QPP * i;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const unsigned lo = (v[2 * i][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;       // row 2p, column 8q + j
-          const unsigned hi = (v[2 * i + 1][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;   // row 2p + 1
-          *reinterpret_cast<unsigned*>(s + (8 * q + j) * LDSK + 2 * p) = lo | (hi << 16);
-        }
-      }
-    }
-  }
-};
-
-// The (BM/2) x (BN/2) share of wavefront w: MI x NJ blocks of 32 x 32.
 template <int MI, int NJ>
 struct Acc {
   f32x16_t c[MI][NJ];
@@ -142,80 +93,263 @@ struct Acc {
   }
 };
 
-// The 16-deep MFMA steps over one LDS stage, in ascending K.
-template <int MI, int NJ, int BK>
-__device__ __forceinline__ void mma_stage(const uint16_t* as, const uint16_t* bs, Acc<MI, NJ>& acc,
-                                          int wm, int wn, int lane) {
-  constexpr int LDSK = ldsk<BK>();
-  const int r = lane & 31, h = lane >> 5;
+// One operand's tile of one K stage: ROWS tile rows (the operand's M or N
+// index) x BK, loaded by NT threads.
+//  KM = false (K contiguous): element (m, k) at g[m ld + k]; LDS row r holds
+//      its BK values, 16-byte chunk c at position c ^ swz(r).
+//  KM = true (K slow): element (m, k) at g[k ld + m]; LDS row kr holds ROWS
+//      values of one k, chunk c at position c ^ swk(kr).
+// Thread t loads the chunks P = NT i + t of the tile (i < NI); a wavefront's
+// 64 loads fill 1 KB of LDS contiguously.
+template <bool KM, int ROWS, int BK, int NT>
+struct Operand {
+  static constexpr int CHUNKS = ROWS * BK / 8;
+  static constexpr int NI = CHUNKS / NT;
+  static constexpr int BYTES = ROWS * BK * 2;
+  static constexpr int CPR = BK / 8;                        // chunks per LDS row (KM = false)
+  static constexpr int CPK = ROWS / 8;                      // chunks per LDS row (KM = true)
+  static constexpr int RSTEP = KM ? NT / CPK : NT / CPR;    // tile rows between a thread's loads
+  static_assert(CHUNKS % NT == 0 && NI >= 1, "tile");
+  static_assert(KM ? (CPK >= 16 && NT % CPK == 0 && RSTEP % 4 == 0)
+                   : (CPR <= 8 && NT % CPR == 0 && RSTEP % 16 == 0),
+                "the swizzle of a thread's chunks must not depend on i");
+  uint64_t base, zp;
+  int64_t ld, k_lim;
+  unsigned ok;   // KM: the thread's column is in range; else bit i: row of load i in range
+  int kc;        // KM: the thread's row within a stage; else its k offset within a stage
+
+  // Conflict-free for the 8- and the 16-lane phases of a 128-bit read.
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
+    else if constexpr (CPR == 4) return ((((r >> 2) ^ (r >> 3)) & 1) << 1) | (((r >> 1) ^ (r >> 2)) & 1);
+    else return 0;
+  }
+  // Conflict-free for the transposing 64-bit reads (4 rows x 32 or 64 bytes).
+  __device__ static __forceinline__ int swk(int kr) { return (2 * (kr & 3)) ^ (8 * (kr & 1)); }
+
+  // m0: first tile row; m_lim / k_lim: rows and k at or past them read as
+  // zero; rowmap (KM = false only): a row whose map value is negative reads as zero.
+  __device__ __forceinline__ void init(const uint16_t* g, int64_t ld_, int64_t m0, int64_t m_lim,
+                                       int64_t k_lim_, const int32_t* rowmap, int t) {
+    ld = ld_;
+    k_lim = k_lim_;
+    zp = (uint64_t)(uintptr_t)kZero16;
+    if (!KM) {
+      const int r = t / CPR;
+      const int c = (t % CPR) ^ swz(r);
+      kc = 8 * c;
+      ok = 0;
 #pragma unroll
-  for (int ks = 0; ks < BK; ks += 16) {
-    bf16x8_t a[MI], b[NJ];
+      for (int i = 0; i < NI; ++i) {
+        const int64_t m = m0 + r + (int64_t)RSTEP * i;
+        bool v = m < m_lim;
+        if (v && rowmap != nullptr) v = rowmap[m] >= 0;
+        ok |= (unsigned)v << i;
+      }
+      base = (uint64_t)(uintptr_t)(g + (m0 + r) * ld + kc);
+    } else {
+      const int kr = t / CPK;
+      const int c = (t % CPK) ^ swk(kr);
+      kc = kr;
+      const int64_t m = m0 + 8 * c;
+      ok = m < m_lim;
+      base = (uint64_t)(uintptr_t)(g + (int64_t)kr * ld + m);
+    }
+  }
+
+  template <int I>
+  __device__ __forceinline__ void issue_one(uint32_t tile, int64_t k0, int w) const {
+    bool v;
+    uint64_t a;
+    if (!KM) {
+      v = (bool)((ok >> I) & 1u) & (k0 + kc < k_lim);
+      a = base + (uint64_t)(((int64_t)RSTEP * I * ld + k0) * 2);
+    } else {
+      v = (bool)ok & (k0 + kc + RSTEP * I < k_lim);
+      a = base + (uint64_t)((k0 + (int64_t)RSTEP * I) * ld * 2);
+    }
+    load_to_lds(v ? a : zp, tile + (uint32_t)((NT * I + 64 * w) * 16));
+  }
+  template <int I = 0>
+  __device__ __forceinline__ void issue_all(uint32_t tile, int64_t k0, int w) const {
+    if constexpr (I < NI) {
+      issue_one<I>(tile, k0, w);
+      issue_all<I + 1>(tile, k0, w);
+    }
+  }
+
+  // Matrix-core fragment: lane l holds (tile row R0 + l % 32, k = ks + 8 (l / 32) + 0..7).
+  // KM: two transposing reads; in each 16-lane group lane j addresses 4 values
+  // of row kr = ks + 8 (l / 32) + j / 4 (+ 4 for the second read) at columns
+  // R0 + 16 ((l / 16) % 2) + 4 (j % 4), and lane i receives column .. + i of
+  // the group's 4 rows.
+  __device__ __forceinline__ bf16x8_t frag(uint32_t tile, int R0, int ks, int lane) const {
+    if (!KM) {
+      const int R = R0 + (lane & 31);
+      const int c = (ks >> 3) + (lane >> 5);
+      return *(const RBI_LDS bf16x8_t*)(uintptr_t)(tile + (uint32_t)((R * CPR + (c ^ swz(R))) * 16));
+    } else {
+      const int j = lane & 15;
+      const int m = R0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+      const int phys = (m >> 3) ^ swk(j >> 2);
+      const int kr = ks + 8 * (lane >> 5) + (j >> 2);
+      const uint32_t p0 = tile + (uint32_t)((kr * CPK + phys) * 16 + (m & 7) * 2);
+      const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RBI_LDS s16x4_t*)(uintptr_t)p0);
+      const s16x4_t v1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((RBI_LDS s16x4_t*)(uintptr_t)(p0 + 4 * CPK * 16));
+      const s16x8_t v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+};
+
+// BM x BN output tile, K stages of BK in an LDS ring of NS stages, WGM x WGN
+// wavefronts (each owning a (BM / WGM) x (BN / WGN) share of 32 x 32 blocks).
+// AKM / BKM: the operand's K index is the slow one in memory.
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool AKM, bool BKM>
+struct Engine {
+  static constexpr int NT = 64 * WGM * WGN;
+  using OA = Operand<AKM, BM, BK, NT>;
+  using OB = Operand<BKM, BN, BK, NT>;
+  static constexpr int STAGE = OA::BYTES + OB::BYTES;
+  static constexpr int L = OA::NI + OB::NI;                  // loads per thread per stage
+  static constexpr int LDS_BYTES = NS * STAGE;
+  static constexpr int MI = BM / (32 * WGM), NJ = BN / (32 * WGN);
+  static constexpr int STEPS = BK / 16;
+  static_assert(STEPS % 2 == 0 && L <= MI * NJ && NS >= 2, "engine shape");
+  static_assert((NS - 1) * L < 64, "vmcnt range");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  using AccT = Acc<MI, NJ>;
+
+  __device__ static __forceinline__ int wm(int w) { return (w / WGN) * (BM / WGM); }
+  __device__ static __forceinline__ int wn(int w) { return (w % WGN) * (BN / WGN); }
+
+  __device__ static __forceinline__ void frags(const OA& oa, const OB& ob, uint32_t as, int ks, int m0,
+                                               int n0, int lane, bf16x8_t* a, bf16x8_t* b) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
-      a[i] = *reinterpret_cast<const bf16x8_t*>(as + (wm + 32 * i + r) * LDSK + ks + 8 * h);
+    for (int i = 0; i < MI; ++i) a[i] = oa.frag(as, m0 + 32 * i, ks, lane);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      b[j] = *reinterpret_cast<const bf16x8_t*>(bs + (wn + 32 * j + r) * LDSK + ks + 8 * h);
+    for (int j = 0; j < NJ; ++j) b[j] = ob.frag(as + OA::BYTES, n0 + 32 * j, ks, lane);
+  }
+
+  template <int Q>
+  __device__ static __forceinline__ void load_q(const OA& oa, const OB& ob, uint32_t tile, int64_t k0,
+                                                int w) {
+    if constexpr (Q < OA::NI) oa.template issue_one<Q>(tile, k0, w);
+    else if constexpr (Q < L) ob.template issue_one<Q - OA::NI>(tile + OA::BYTES, k0, w);
+  }
+
+  // The MI x NJ MFMAs of one step; with LOADS, load Q of the next stage after MFMA Q.
+  template <bool LOADS, int Q = 0>
+  __device__ static __forceinline__ void mma(AccT& acc, const bf16x8_t* a, const bf16x8_t* b,
+                                             const OA& oa, const OB& ob, uint32_t tile, int64_t k0,
+                                             int w) {
+    if constexpr (Q < MI * NJ) {
+      acc.c[Q / NJ][Q % NJ] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[Q / NJ], b[Q % NJ], acc.c[Q / NJ][Q % NJ], 0, 0, 0);
+      if constexpr (LOADS && Q < L) {
+        RBI_SCHED_FENCE();
+        load_q<Q>(oa, ob, tile, k0, w);
+        RBI_SCHED_FENCE();
+      }
+      mma<LOADS, Q + 1>(acc, a, b, oa, ob, tile, k0, w);
+    }
+  }
+
+  // Step S of stage `it` (buffer `as`): the fragments of the next step (or of
+  // the next stage's first step) are read into (na, nb) while the MFMAs use
+  // (ca, cb).  The last step waits for the next stage, meets the other
+  // wavefronts, and refills this stage's buffer with stage it + NS.
+  template <int S>
+  __device__ static __forceinline__ void step(uint32_t sm, uint32_t as, int it, AccT& acc,
+                                              const OA& oa, const OB& ob, int64_t k_begin, int w,
+                                              int m0, int n0, int lane, bf16x8_t* ca, bf16x8_t* cb,
+                                              bf16x8_t* na, bf16x8_t* nb) {
+    RBI_SCHED_FENCE();
+    if constexpr (S == STEPS - 1) {
+      wait_vm_lgkm<(NS - 2) * L>();
+      lds_barrier();
+      frags(oa, ob, sm + (uint32_t)(((it + 1) % NS) * STAGE), 0, m0, n0, lane, na, nb);
+      RBI_SCHED_FENCE();
+      mma<true>(acc, ca, cb, oa, ob, as, k_begin + (int64_t)(it + NS) * BK, w);
+    } else {
+      frags(oa, ob, as, 16 * (S + 1), m0, n0, lane, na, nb);
+      RBI_SCHED_FENCE();
+      mma<false>(acc, ca, cb, oa, ob, as, 0, w);
+    }
+    RBI_SCHED_FENCE();
+  }
+  template <int S>
+  __device__ static __forceinline__ void steps(uint32_t sm, uint32_t as, int it, AccT& acc,
+                                               const OA& oa, const OB& ob, int64_t k_begin, int w,
+                                               int m0, int n0, int lane, bf16x8_t* a0, bf16x8_t* b0,
+                                               bf16x8_t* a1, bf16x8_t* b1) {
+    if constexpr (S < STEPS) {
+      if constexpr (S % 2 == 0) step<S>(sm, as, it, acc, oa, ob, k_begin, w, m0, n0, lane, a0, b0, a1, b1);
+      else step<S>(sm, as, it, acc, oa, ob, k_begin, w, m0, n0, lane, a1, b1, a0, b0);
+      steps<S + 1>(sm, as, it, acc, oa, ob, k_begin, w, m0, n0, lane, a0, b0, a1, b1);
+    }
+  }
+
+  // acc += the product over the K stages [k_begin, k_begin + nst BK) in
+  // ascending order.  Every stage issues its loads (stages past the end read
+  // the zero chunk into a buffer no later stage reads), so the wait counts
+  // are constants.
+  __device__ static __forceinline__ void run(uint32_t sm, AccT& acc, const OA& oa, const OB& ob,
+                                             int64_t k_begin, int nst) {
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int m0 = wm(w), n0 = wn(w);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      oa.issue_all(sm + s * STAGE, k_begin + (int64_t)s * BK, w);
+      ob.issue_all(sm + s * STAGE + OA::BYTES, k_begin + (int64_t)s * BK, w);
+    }
+    wait_vm_lgkm<(NS - 1) * L>();
+    lds_barrier();
+    bf16x8_t a0[MI], b0[NJ], a1[MI], b1[NJ];
+    frags(oa, ob, sm, 0, m0, n0, lane, a0, b0);
+    for (int it = 0; it < nst; ++it) {
+      const uint32_t as = sm + (uint32_t)((it % NS) * STAGE);
+      steps<0>(sm, as, it, acc, oa, ob, k_begin, w, m0, n0, lane, a0, b0, a1, b1);
+    }
+    wait_vm_lgkm<0>();
+  }
+
+  // Result (block i, j; register e) of wavefront w: tile row
+  // wm + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, tile column wn + 32 j + lane % 32.
+  template <typename F>
+  __device__ static __forceinline__ void for_each(const AccT& acc, F&& f) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int mb = wm(w), nb = wn(w);
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.c[i][j], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          f(mb + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3), nb + 32 * j + (lane & 31),
+            acc.c[i][j][e]);
   }
-}
+};
 
-// C[m][n] += sum over k in [k_begin, k_end) of A(m, k) B(k, n), K stages of
-// BK in ascending order (k_end - k_begin is a multiple of BK; indices at or
-// past k_lim read as zero).
-template <int BM, int BN, int BK, bool AT, bool BT>
-__device__ __forceinline__ void gemm_tile(Tile<BM, BN, BK>& sm, Acc<BM / 64, BN / 64>& acc,
-                                          const uint16_t* a, int64_t lda, const uint16_t* b,
-                                          int64_t ldb, int64_t m0, int64_t m_lim, int64_t n0,
-                                          int64_t n_lim, int64_t k_begin, int64_t k_end,
-                                          int64_t k_lim, const int32_t* rowmap_a) {
-  const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
-  const int wm = (w >> 1) * (BM / 2), wn = (w & 1) * (BN / 2);
-  Stage<AT, BM, BK> sa;
-  Stage<BT, BN, BK> sb;
-  sa.load(a, lda, m0, m_lim, k_begin, k_lim, rowmap_a, t);
-  sb.load(b, ldb, n0, n_lim, k_begin, k_lim, nullptr, t);
-  sa.store(sm.a[0], t);
-  sb.store(sm.b[0], t);
-  __syncthreads();
-  int buf = 0;
-  for (int64_t k0 = k_begin; k0 < k_end; k0 += BK) {
-    const bool more = k0 + BK < k_end;
-    if (more) {
-      sa.load(a, lda, m0, m_lim, k0 + BK, k_lim, rowmap_a, t);
-      sb.load(b, ldb, n0, n_lim, k0 + BK, k_lim, nullptr, t);
-    }
-    mma_stage<BM / 64, BN / 64, BK>(sm.a[buf], sm.b[buf], acc, wm, wn, lane);
-    if (more) {
-      sa.store(sm.a[buf ^ 1], t);
-      sb.store(sm.b[buf ^ 1], t);
-    }
-    __syncthreads();
-    buf ^= 1;
+// Tile (tm, tn) of workgroup id in a tmc x tnc grid: the tiles are cut into
+// 4 x 8 super-blocks; XCD x (id % 8) takes super-blocks x, x + 8, ... so its
+// 32 concurrent workgroups share 4 row blocks and 8 column blocks.  Grids the
+// super-blocks do not tile fall back to column-major order.
+__device__ __forceinline__ void xcd_tile(int id, int tmc, int tnc, int& tm, int& tn) {
+  constexpr int GM = 4, GN = 8;
+  if (tmc % GM || tnc % GN || ((tmc / GM) * (tnc / GN)) % 8) {
+    tm = id % tmc;
+    tn = id / tmc;
+    return;
   }
-}
-
-// Result of block (i, j), register e: row wm + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,
-// column wn + 32 j + lane % 32.
-template <int BM, int BN, typename F>
-__device__ __forceinline__ void for_each_result(const Acc<BM / 64, BN / 64>& acc, F&& f) {
-  const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
-  const int wm = (w >> 1) * (BM / 2), wn = (w & 1) * (BN / 2);
-#pragma unroll
-  for (int i = 0; i < BM / 64; ++i)
-#pragma unroll
-    for (int j = 0; j < BN / 64; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        f(wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3), wn + 32 * j + (lane & 31),
-          acc.c[i][j][e]);
+  const int sbm = tmc / GM;
+  const int xcd = id & 7, slot = id >> 3;
+  const int sb = (slot >> 5) * 8 + xcd, w = slot & 31;
+  tm = (sb % sbm) * GM + w % GM;
+  tn = (sb / sbm) * GN + w / GM;
 }
 
 __device__ __forceinline__ uint16_t to_bf16_rne(float f) {
@@ -224,50 +358,64 @@ __device__ __forceinline__ uint16_t to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// y = x W^T (fwd) and dX = dY W: bf16 result rows of the call, padding rows 0.
-template <int BM, int BN, int BK, bool BT>
-__global__ __launch_bounds__(THREADS) void rowwise_kernel(RowwiseArgs p) {
-  __shared__ Tile<BM, BN, BK> sm;
-  const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
-  Acc<BM / 64, BN / 64> acc;
-  acc.zero();
-  gemm_tile<BM, BN, BK, false, BT>(sm, acc, p.a, p.lda, p.b, p.ldb, m0, p.rows, n0, p.n, 0,
-                                   (p.k + BK - 1) / BK * BK, p.k, p.row_logical);
-  // padding rows were loaded as zeros; they are written as 0 explicitly
-  const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
-  const int wm = (w >> 1) * (BM / 2), wn = (w & 1) * (BN / 2);
-#pragma unroll
-  for (int i = 0; i < BM / 64; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t m = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (m >= p.rows) continue;
-      const bool pad = p.row_logical != nullptr && p.row_logical[m] < 0;
-#pragma unroll
-      for (int j = 0; j < BN / 64; ++j) {
-        const int64_t n = n0 + wn + 32 * j + (lane & 31);
-        if (n < p.n) p.out[m * p.n + n] = pad ? (uint16_t)0 : to_bf16_rne(acc.c[i][j][e]);
-      }
-    }
+__device__ __forceinline__ u32x4v_t ld16_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t*>(p));
 }
 
-// Q_g for one BM x BN tile of dW and one group g = blockIdx.z of logical
-// rows (dY and X in logical row order, T rows).
-template <int BM, int BN, int BK>
-__global__ __launch_bounds__(THREADS) void dw_group_kernel(DwArgs p) {
-  __shared__ Tile<BM, BN, BK> sm;
-  const int64_t n0 = (int64_t)blockIdx.x * BM, k0 = (int64_t)blockIdx.y * BN;
-  const int64_t g = blockIdx.z;
-  const int64_t r0 = g * kGroupRows;
+__device__ __forceinline__ uint32_t lds_addr(RBI_LDS uint8_t* p) { return (uint32_t)(uintptr_t)p; }
+
+// y = x W^T (fwd, B K-contiguous) and dX = dY W (B K-slow): bf16 result rows of
+// the call, padding rows 0.  One workgroup per tile, 1-D grid.
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool BT>
+__global__ __launch_bounds__(64 * WGM * WGN) void rowwise_kernel(RowwiseArgs p) {
+  using E = Engine<BM, BN, BK, NS, WGM, WGN, false, BT>;
+  __shared__ __align__(16) uint8_t smem[E::LDS_BYTES];
+  int tm, tn;
+  xcd_tile((int)blockIdx.x, (int)((p.rows + BM - 1) / BM), (int)((p.n + BN - 1) / BN), tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int t = threadIdx.x;
+  typename E::OA oa;
+  typename E::OB ob;
+  oa.init(p.a, p.lda, m0, p.rows, p.k, p.row_logical, t);
+  ob.init(p.b, p.ldb, n0, p.n, p.k, nullptr, t);
+  typename E::AccT acc;
+  acc.zero();
+  E::run(lds_addr((RBI_LDS uint8_t*)smem), acc, oa, ob, 0, (int)((p.k + BK - 1) / BK));
+  // padding rows were loaded as zeros; they are written as 0 explicitly
+  E::for_each(acc, [&](int mi, int ni, float v) {
+    const int64_t m = m0 + mi, n = n0 + ni;
+    if (m < p.rows && n < p.n) {
+      const bool pad = p.row_logical != nullptr && p.row_logical[m] < 0;
+      p.out[m * p.n + n] = pad ? (uint16_t)0 : to_bf16_rne(v);
+    }
+  });
+}
+
+// Q_g for one tile of dW and one group g of logical rows (dY and X in logical
+// row order, T rows); 1-D grid, workgroup id = g * tiles + tile.
+template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void dw_group_kernel(DwArgs p) {
+  using E = Engine<BM, BN, BK, NS, WGM, WGN, true, true>;
+  __shared__ __align__(16) uint8_t smem[E::LDS_BYTES];
+  const int tmc = (int)((p.n + BM - 1) / BM), tnc = (int)((p.k + BN - 1) / BN);
+  const int per_group = tmc * tnc;
+  const int g = (int)blockIdx.x / per_group;
+  int tm, tn;
+  xcd_tile((int)blockIdx.x % per_group, tmc, tnc, tm, tn);
+  const int64_t n0 = (int64_t)tm * BM, k0 = (int64_t)tn * BN;
+  const int64_t r0 = (int64_t)g * kGroupRows;
   int64_t r1 = r0 + kGroupRows;
   if (r1 > p.T) r1 = (p.T + BK - 1) / BK * BK;   // the rest of the group is zero rows
-  Acc<BM / 64, BN / 64> acc;
+  const int t = threadIdx.x;
+  typename E::OA oa;
+  typename E::OB ob;
+  oa.init(p.dy, p.n, n0, p.n, p.T, nullptr, t);
+  ob.init(p.x, p.k, k0, p.k, p.T, nullptr, t);
+  typename E::AccT acc;
   acc.zero();
-  gemm_tile<BM, BN, BK, true, true>(sm, acc, p.dy, p.n, p.x, p.k, n0, p.n, k0, p.k, r0, r1, p.T,
-                                    nullptr);
-  float* out = p.out + g * p.n * p.k;
-  for_each_result<BM, BN>(acc, [&](int mi, int ni, float v) {
+  E::run(lds_addr((RBI_LDS uint8_t*)smem), acc, oa, ob, r0, (int)((r1 - r0) / BK));
+  float* out = p.out + (int64_t)g * p.n * p.k;
+  E::for_each(acc, [&](int mi, int ni, float v) {
     const int64_t n = n0 + mi, k = k0 + ni;
     if (n < p.n && k < p.k) out[n * p.k + k] = v;
   });
@@ -321,36 +469,37 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ dst, 
 // every output element runs the same chain whatever tile holds it).
 static bool big_tiles(int64_t m, int64_t n) { return m >= 256 && n >= 256; }
 
-template <int BM, int BN, int BK>
-static void rowwise_go(const RowwiseArgs& a, bool bt, hipStream_t st) {
-  const dim3 grid((unsigned)((a.rows + BM - 1) / BM), (unsigned)((a.n + BN - 1) / BN));
-  if (bt) rowwise_kernel<BM, BN, BK, true><<<grid, dim3(THREADS), 0, st>>>(a);
-  else rowwise_kernel<BM, BN, BK, false><<<grid, dim3(THREADS), 0, st>>>(a);
+template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+static hipError_t rowwise_go(const RowwiseArgs& a, bool bt, hipStream_t st) {
+  const int64_t tiles = ((a.rows + BM - 1) / BM) * ((a.n + BN - 1) / BN);
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles), block(64 * WGM * WGN);
+  if (bt) rowwise_kernel<BM, BN, BK, NS, WGM, WGN, true><<<grid, block, 0, st>>>(a);
+  else rowwise_kernel<BM, BN, BK, NS, WGM, WGN, false><<<grid, block, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_rowwise(const RowwiseArgs& a, bool b_transposed, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
-  // 64-deep stages: the 256 x 256 kernel holds one workgroup per CU either way
-  if (big_tiles(a.rows, a.n)) rowwise_go<256, 256, 64>(a, b_transposed, st);
-  else rowwise_go<128, 128, 32>(a, b_transposed, st);
-  return hipGetLastError();
+  if (big_tiles(a.rows, a.n)) return rowwise_go<256, 256, 64, 2, 2, 4>(a, b_transposed, st);
+  return rowwise_go<128, 128, 32, 4, 2, 2>(a, b_transposed, st);
 }
 
 int64_t num_groups(int64_t T) { return (T + kGroupRows - 1) / kGroupRows; }
 
-template <int BM, int BN, int BK>
-static void dw_go(const DwArgs& a, int64_t G, hipStream_t st) {
-  const dim3 grid((unsigned)((a.n + BM - 1) / BM), (unsigned)((a.k + BN - 1) / BN), (unsigned)G);
-  dw_group_kernel<BM, BN, BK><<<grid, dim3(THREADS), 0, st>>>(a);
+template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+static hipError_t dw_go(const DwArgs& a, int64_t G, hipStream_t st) {
+  const int64_t tiles = ((a.n + BM - 1) / BM) * ((a.k + BN - 1) / BN) * G;
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  dw_group_kernel<BM, BN, BK, NS, WGM, WGN><<<dim3((unsigned)tiles), dim3(64 * WGM * WGN), 0, st>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_dw_groups(const DwArgs& a, hipStream_t st) {
   const int64_t G = num_groups(a.T);
   if (G == 0) return hipSuccess;
-  // 256 x 128 x 32 keeps the dW kernel at two wavefronts per SIMD (212 VGPRs)
-  if (big_tiles(a.n, a.k)) dw_go<256, 128, 32>(a, G, st);
-  else dw_go<128, 128, 32>(a, G, st);
-  return hipGetLastError();
+  if (big_tiles(a.n, a.k)) return dw_go<256, 256, 64, 2, 2, 4>(a, G, st);
+  return dw_go<128, 128, 32, 4, 2, 2>(a, G, st);
 }
 
 hipError_t launch_group_tree(const float* q, int64_t G, int64_t nk, float* dw, hipStream_t st) {
