@@ -66,6 +66,18 @@ int det_embedding_dw_contrib(const rmsnorm_bf16* dy, int64_t rows, int64_t dim,
 /* dE[vocab][dim] (FP32, every row written).  May be called again: the same bits. */
 int det_embedding_dw_finalize(det_embedding_dw_acc* acc, float* dE, void* stream);
 
+/* The whole backward in one call, for a caller whose one call holds all
+ * n_logical rows of dY in logical order (the B=N case): dE[vocab][dim] as
+ * det_embedding_dw_contrib(layout NULL) + det_embedding_dw_finalize would
+ * give it, bit for bit, with the same EDO-v1 order.  A token with one block
+ * is folded straight into its dE row, so no block partial is written for it.
+ * Needs an accumulator with no contribution (RMSNORM_ESTATE) and
+ * rows == n_logical (RMSNORM_ECOVERAGE); leaves it finalized without
+ * partials, so det_embedding_dw_finalize then returns RMSNORM_ESTATE until
+ * det_embedding_dw_acc_reset.  dE must not alias dy. */
+int det_embedding_bwd(const rmsnorm_bf16* dy, int64_t rows, int64_t dim, det_embedding_dw_acc* acc,
+                      float* dE, void* stream);
+
 int det_embedding_dw_acc_reset(det_embedding_dw_acc* acc, void* stream);
 int det_embedding_dw_acc_destroy(det_embedding_dw_acc* acc);
 

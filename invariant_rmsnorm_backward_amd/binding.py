@@ -30,8 +30,8 @@ EXPORTED = ("rmsnorm_max_hidden", "rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_c
             "det_gemm_fwd", "det_gemm_bwd_dx", "det_gemm_dw_acc_create", "det_gemm_dw_contrib",
             "det_gemm_dw_finalize", "det_gemm_dw_acc_reset", "det_gemm_dw_acc_destroy",
             "det_embedding_fwd", "det_embedding_dw_acc_create", "det_embedding_dw_acc_set_ids",
-            "det_embedding_dw_contrib", "det_embedding_dw_finalize", "det_embedding_dw_acc_reset",
-            "det_embedding_dw_acc_destroy")
+            "det_embedding_dw_contrib", "det_embedding_dw_finalize", "det_embedding_bwd",
+            "det_embedding_dw_acc_reset", "det_embedding_dw_acc_destroy")
 
 
 class RmsNormError(RuntimeError):
@@ -89,6 +89,7 @@ def load() -> ctypes.CDLL:
         "det_embedding_dw_acc_set_ids": ([P, P, P], I32),
         "det_embedding_dw_contrib": ([P, I64, I64, P, P, P], I32),
         "det_embedding_dw_finalize": ([P, P, P], I32),
+        "det_embedding_bwd": ([P, I64, I64, P, P, P], I32),
         "det_embedding_dw_acc_reset": ([P, P], I32),
         "det_embedding_dw_acc_destroy": ([P], I32),
     }
@@ -267,6 +268,11 @@ def det_embedding_dw_contrib(dy: int, rows: int, dim: int, layout: Optional[int]
 
 def det_embedding_dw_finalize(acc: Optional[int], dE: int, stream: Optional[int]) -> None:
     _check(load().det_embedding_dw_finalize(acc, dE, stream), "det_embedding_dw_finalize")
+
+
+def det_embedding_bwd(dy: int, rows: int, dim: int, acc: Optional[int], dE: int,
+                      stream: Optional[int]) -> None:
+    _check(load().det_embedding_bwd(dy, rows, dim, acc, dE, stream), "det_embedding_bwd")
 
 
 def det_embedding_dw_acc_reset(acc: Optional[int], stream: Optional[int]) -> None:
@@ -460,6 +466,15 @@ class EmbeddingDwAccumulator:
             dE = torch.empty((self.vocab, self.dim), dtype=torch.float32, device="cuda")
         det_embedding_dw_finalize(self.handle, dE.data_ptr(),
                                   current_stream() if stream is None else stream)
+        return dE
+
+    def backward(self, dy, dE=None, stream: Optional[int] = None):
+        """The one-call backward (all rows in logical order): dE, bitwise as contrib + finalize."""
+        import torch
+        if dE is None:
+            dE = torch.empty((self.vocab, self.dim), dtype=torch.float32, device="cuda")
+        det_embedding_bwd(dy.data_ptr(), dy.shape[0], self.dim, self.handle, dE.data_ptr(),
+                          current_stream() if stream is None else stream)
         return dE
 
     def close(self):

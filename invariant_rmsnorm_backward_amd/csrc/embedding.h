@@ -21,7 +21,15 @@ struct PlanView {
   const int32_t* tok_first;    // [vocab] first block of the token, -1 if it does not occur
   const int32_t* tok_nblk;     // [vocab] number of blocks of the token
   const int32_t* blk_order;    // [n_blocks] block ids by decreasing length (work order only)
+  const int32_t* mb_blocks;    // [n_mb_blocks] blocks of tokens with two or more blocks
+  const int32_t* mb_tokens;    // [n_mb_tokens] tokens with two or more blocks
+  const int32_t* single_tokens;  // [n_single_tokens] tokens with one block
+  const int32_t* zero_tokens;    // [n_zero_tokens] tokens that do not occur
   int64_t n_blocks;
+  int64_t n_mb_blocks;
+  int64_t n_mb_tokens;
+  int64_t n_single_tokens;
+  int64_t n_zero_tokens;
   int64_t vocab;
 };
 
@@ -33,6 +41,11 @@ hipError_t launch_blocks(const uint16_t* dy, const PlanView& plan, int64_t dim, 
 // dE[vocab][dim]: each token's tree over its block partials, 0 for absent tokens.
 hipError_t launch_finalize(const float* P, const PlanView& plan, int64_t dim, float* dE,
                            hipStream_t stream);
+// The one-call backward: dE[vocab][dim] from dY rows in logical order --
+// block partials into P only for tokens with two or more blocks, single-block
+// tokens folded straight into dE, absent tokens 0 -- then those tokens' trees.
+hipError_t launch_bwd_one_call(const uint16_t* dy, float* P, const PlanView& plan, int64_t dim,
+                               float* dE, hipStream_t stream);
 
 }  // namespace emb
 }  // namespace rbi

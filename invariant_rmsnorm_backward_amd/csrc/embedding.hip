@@ -97,13 +97,61 @@ __global__ __launch_bounds__(64) void block_kernel(const uint16_t* __restrict__ 
   }
 }
 
+// The tree of token v's nb block partials (rows first .. first + nb - 1 of P)
+// over the 4 columns at c0: the partials, read in order, are combined like
+// the digits of a binary counter -- level k holds a finished subtree of 2^k
+// leaves, a new leaf merges upward as its left neighbours complete -- which
+// is the perfect pairwise tree; the pending levels are joined from the
+// lowest up, which is the same tree with +0.0 leaves to the next power of
+// two (x + 0.0 == x for every partial: none is -0.0, all folds start from
+// +0.0).  The partials are loaded 8 at a time ahead of the merges.
+__device__ __forceinline__ void token_tree(const float* __restrict__ P, int first, int nb,
+                                           int64_t dim, int64_t c0, float (&r)[4]) {
+  float st[kTreeLevels][4] = {};
+  for (int i0 = 0; i0 < nb; i0 += 8) {
+    f32x4e_t pv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u < nb ? i0 + u : nb - 1;          // in bounds; extra loads unused
+      pv[u] = *reinterpret_cast<const f32x4e_t*>(P + (int64_t)(first + i) * dim + c0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u;
+      if (i < nb) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = pv[u][e];
+        bool placed = false;
+#pragma unroll
+        for (int k = 0; k < kTreeLevels; ++k) {
+          if (!placed) {
+            if ((i >> k) & 1) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) x[e] = st[k][e] + x[e];
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) st[k][e] = x[e];
+              placed = true;
+            }
+          }
+        }
+      }
+    }
+  }
+  bool have = false;
+#pragma unroll
+  for (int k = 0; k < kTreeLevels; ++k) {
+    if ((nb >> k) & 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = have ? st[k][e] + r[e] : st[k][e];
+      have = true;
+    }
+  }
+}
+
 // Every vocabulary row v over 4 columns per thread (1024 per workgroup):
-// the token's block partials, read in order, are combined like the digits of
-// a binary counter -- level k holds a finished subtree of 2^k leaves, a new
-// leaf merges upward as its left neighbours complete -- which is the perfect
-// pairwise tree; the pending levels are joined from the lowest up, which is
-// the same tree with +0.0 leaves to the next power of two (x + 0.0 == x for
-// every partial: none is -0.0, all folds start from +0.0).
+// the token's tree, or 0 for an absent token.
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ P, PlanView p,
                                                        int64_t dim, float* __restrict__ dE) {
   const int64_t v = blockIdx.x;
@@ -111,39 +159,88 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   if (c0 >= dim) return;
   const int first = p.tok_first[v];
   float r[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (first >= 0) {
-    const int nb = p.tok_nblk[v];
-    float st[kTreeLevels][4] = {};
-    for (int i = 0; i < nb; ++i) {
-      float x[4];
-      const f32x4e_t pv = *reinterpret_cast<const f32x4e_t*>(P + (int64_t)(first + i) * dim + c0);
+  if (first >= 0) token_tree(P, first, p.tok_nblk[v], dim, c0, r);
+  __builtin_nontemporal_store(f32x4e_t{r[0], r[1], r[2], r[3]},
+                              reinterpret_cast<f32x4e_t*>(dE + v * dim + c0));
+}
+
+// The one-call backward in one launch; each workgroup takes one item of a
+// three-part work list (its order is only a schedule, no result depends on it):
+//   [0, n_mb_blocks)          a block of a token with two or more blocks:
+//                             its fold over every column -> P[b];
+//   [.., + n_single_tokens)   a token with a single block: the same fold,
+//                             written straight to its dE row (the tree of one
+//                             leaf is that leaf), so no partial exists for it;
+//   [.., + ceil(n_zero / 4))  up to 4 absent tokens: their dE rows are 0.
+// Folds run over 2048 columns at a time, 8 per thread, with the rows loaded 8
+// at a time ahead of the adds, in occurrence order from +0.0: the additions of
+// block_kernel, in the same order.
+constexpr int kZeroRowsPerGroup = 4;
+
+__global__ __launch_bounds__(256) void fused_bwd_kernel(const uint16_t* __restrict__ dy,
+                                                        PlanView p, int64_t dim,
+                                                        float* __restrict__ P,
+                                                        float* __restrict__ dE) {
+  const int64_t g = blockIdx.x;
+  const int t = threadIdx.x;
+  if (g >= p.n_mb_blocks + p.n_single_tokens) {
+    const int64_t z0 = (g - p.n_mb_blocks - p.n_single_tokens) * kZeroRowsPerGroup;
+    const f32x4e_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t z = z0; z < z0 + kZeroRowsPerGroup && z < p.n_zero_tokens; ++z) {
+      f32x4e_t* row = reinterpret_cast<f32x4e_t*>(dE + (int64_t)p.zero_tokens[z] * dim);
+      for (int64_t q = t; q < dim / 4; q += 256) __builtin_nontemporal_store(zero, row + q);
+    }
+    return;
+  }
+  int start, len;
+  float* out;
+  if (g < p.n_mb_blocks) {
+    const int64_t b = p.mb_blocks[g];
+    start = p.blk_start[b];
+    len = p.blk_len[b];
+    out = P + b * dim;
+  } else {
+    const int64_t v = p.single_tokens[g - p.n_mb_blocks];
+    const int b = p.tok_first[v];
+    start = p.blk_start[b];
+    len = p.blk_len[b];
+    out = dE + v * dim;
+  }
+  for (int64_t c0 = (int64_t)t * 8; c0 < dim; c0 += 256 * 8) {
+    float r[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i0 = 0; i0 < len; i0 += 8) {
+      u32x4e_t q[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = pv[e];
-      bool placed = false;
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u < len ? i0 + u : len - 1;       // in bounds; extra loads unused
+        const int64_t l = p.occ[start + i];
+        q[u] = *reinterpret_cast<const u32x4e_t*>(dy + l * dim + c0);
+      }
 #pragma unroll
-      for (int k = 0; k < kTreeLevels; ++k) {
-        if (!placed) {
-          if ((i >> k) & 1) {
+      for (int u = 0; u < 8; ++u) {
+        if (i0 + u < len) {
+          float f[8];
+          widen8(q[u], f);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = st[k][e] + x[e];
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) st[k][e] = x[e];
-            placed = true;
-          }
+          for (int e = 0; e < 8; ++e) r[e] = r[e] + f[e];
         }
       }
     }
-    bool have = false;
-#pragma unroll
-    for (int k = 0; k < kTreeLevels; ++k) {
-      if ((nb >> k) & 1) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = have ? st[k][e] + r[e] : st[k][e];
-        have = true;
-      }
-    }
+    f32x4e_t* dst = reinterpret_cast<f32x4e_t*>(out + c0);
+    __builtin_nontemporal_store(f32x4e_t{r[0], r[1], r[2], r[3]}, dst);
+    __builtin_nontemporal_store(f32x4e_t{r[4], r[5], r[6], r[7]}, dst + 1);
   }
+}
+
+// The trees of the tokens with two or more blocks (the plan's list), 4
+// columns per thread.
+__global__ __launch_bounds__(256) void tree_list_kernel(const float* __restrict__ P, PlanView p,
+                                                        int64_t dim, float* __restrict__ dE) {
+  const int64_t v = p.mb_tokens[blockIdx.x];
+  const int64_t c0 = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c0 >= dim) return;
+  float r[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  token_tree(P, p.tok_first[v], p.tok_nblk[v], dim, c0, r);
   __builtin_nontemporal_store(f32x4e_t{r[0], r[1], r[2], r[3]},
                               reinterpret_cast<f32x4e_t*>(dE + v * dim + c0));
 }
@@ -170,6 +267,18 @@ hipError_t launch_finalize(const float* P, const PlanView& plan, int64_t dim, fl
   if (plan.vocab == 0) return hipSuccess;
   const dim3 grid((unsigned)plan.vocab, (unsigned)((dim / 4 + 255) / 256));
   finalize_kernel<<<grid, dim3(256), 0, st>>>(P, plan, dim, dE);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_one_call(const uint16_t* dy, float* P, const PlanView& plan, int64_t dim,
+                               float* dE, hipStream_t st) {
+  const int64_t groups = plan.n_mb_blocks + plan.n_single_tokens +
+                         (plan.n_zero_tokens + kZeroRowsPerGroup - 1) / kZeroRowsPerGroup;
+  if (groups > 0) fused_bwd_kernel<<<dim3((unsigned)groups), dim3(256), 0, st>>>(dy, plan, dim, P, dE);
+  if (plan.n_mb_tokens > 0) {
+    const dim3 tg((unsigned)plan.n_mb_tokens, (unsigned)((dim / 4 + 255) / 256));
+    tree_list_kernel<<<tg, dim3(256), 0, st>>>(P, plan, dim, dE);
+  }
   return hipGetLastError();
 }
 

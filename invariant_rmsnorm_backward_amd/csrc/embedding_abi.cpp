@@ -32,12 +32,13 @@ int check_dims(int64_t vocab, int64_t dim) {
   return RMSNORM_OK;
 }
 
-enum Mode { kEmpty = 0, kComputed = 1, kStaged = 2 };
+enum Mode { kEmpty = 0, kComputed = 1, kStaged = 2, kDirect = 3 };
 
 // Host plan: occurrences grouped by token (counting sort, stable in the
 // logical row), cut into blocks of kBlockOcc.
 struct HostPlan {
-  std::vector<int32_t> occ, blk_start, blk_len, tok_first, tok_nblk, blk_order;
+  std::vector<int32_t> occ, blk_start, blk_len, tok_first, tok_nblk, blk_order, mb_blocks, mb_tokens,
+      single_tokens, zero_tokens;
 };
 
 int build_plan(const int32_t* ids, int64_t T, int64_t vocab, HostPlan* P) {
@@ -72,6 +73,21 @@ int build_plan(const int32_t* ids, int64_t T, int64_t vocab, HostPlan* P) {
   for (size_t i = 0; i < P->blk_order.size(); ++i) P->blk_order[i] = static_cast<int32_t>(i);
   std::stable_sort(P->blk_order.begin(), P->blk_order.end(),
                    [&](int32_t a, int32_t b) { return P->blk_len[a] > P->blk_len[b]; });
+  // the blocks of tokens with two or more blocks (the one-call backward folds
+  // single-block tokens in its finalize), in the same work order
+  P->mb_blocks.clear();
+  std::vector<int32_t> blk_tok(P->blk_start.size());
+  for (int64_t v = 0; v < vocab; ++v)
+    for (int32_t i = 0; i < P->tok_nblk[v]; ++i) blk_tok[P->tok_first[v] + i] = static_cast<int32_t>(v);
+  for (int32_t b : P->blk_order)
+    if (P->tok_nblk[blk_tok[b]] > 1) P->mb_blocks.push_back(b);
+  P->mb_tokens.clear();
+  P->single_tokens.clear();
+  P->zero_tokens.clear();
+  for (int64_t v = 0; v < vocab; ++v) {
+    const int32_t n = P->tok_nblk[v];
+    (n > 1 ? P->mb_tokens : n == 1 ? P->single_tokens : P->zero_tokens).push_back(static_cast<int32_t>(v));
+  }
   return RMSNORM_OK;
 }
 
@@ -80,7 +96,8 @@ int build_plan(const int32_t* ids, int64_t T, int64_t vocab, HostPlan* P) {
 struct det_embedding_dw_acc {
   rbi::AccHost host;
   int64_t vocab = 0, dim = 0;
-  int32_t* d_plan = nullptr;      // occ | blk_start | blk_len | tok_first | tok_nblk
+  int32_t* d_plan = nullptr;      // occ | blk_start | blk_len | tok_first | tok_nblk | blk_order |
+                                  // mb_blocks | mb_tokens | single_tokens | zero_tokens
   size_t plan_cap = 0;            // int32 entries allocated
   rbi::emb::PlanView view{};
   float* d_P = nullptr;           // [max blocks][dim]
@@ -98,13 +115,17 @@ int upload_plan(det_embedding_dw_acc* A, const int32_t* ids, hipStream_t st) {
   const int64_t nb = static_cast<int64_t>(P.blk_start.size());
   if (nb > A->max_blocks) return fail(RMSNORM_EINVAL, "internal: block count exceeds the bound");
   std::vector<int32_t> buf;
-  buf.reserve(P.occ.size() + 3 * nb + 2 * A->vocab + 1);
+  buf.reserve(P.occ.size() + 4 * nb + 3 * A->vocab + 1);
   buf.insert(buf.end(), P.occ.begin(), P.occ.end());
   buf.insert(buf.end(), P.blk_start.begin(), P.blk_start.end());
   buf.insert(buf.end(), P.blk_len.begin(), P.blk_len.end());
   buf.insert(buf.end(), P.tok_first.begin(), P.tok_first.end());
   buf.insert(buf.end(), P.tok_nblk.begin(), P.tok_nblk.end());
   buf.insert(buf.end(), P.blk_order.begin(), P.blk_order.end());
+  buf.insert(buf.end(), P.mb_blocks.begin(), P.mb_blocks.end());
+  buf.insert(buf.end(), P.mb_tokens.begin(), P.mb_tokens.end());
+  buf.insert(buf.end(), P.single_tokens.begin(), P.single_tokens.end());
+  buf.insert(buf.end(), P.zero_tokens.begin(), P.zero_tokens.end());
   if (buf.size() > A->plan_cap) return fail(RMSNORM_EINVAL, "internal: plan exceeds its buffer");
   hipError_t e = hipStreamSynchronize(st);   // earlier work may still read the old plan
   if (e == hipSuccess && !buf.empty())
@@ -118,7 +139,15 @@ int upload_plan(det_embedding_dw_acc* A, const int32_t* ids, hipStream_t st) {
   A->view.tok_first = b + T + 2 * nb;
   A->view.tok_nblk = b + T + 2 * nb + A->vocab;
   A->view.blk_order = b + T + 2 * nb + 2 * A->vocab;
+  A->view.mb_blocks = b + T + 3 * nb + 2 * A->vocab;
+  A->view.mb_tokens = A->view.mb_blocks + P.mb_blocks.size();
+  A->view.single_tokens = A->view.mb_tokens + P.mb_tokens.size();
+  A->view.zero_tokens = A->view.single_tokens + P.single_tokens.size();
   A->view.n_blocks = nb;
+  A->view.n_mb_blocks = static_cast<int64_t>(P.mb_blocks.size());
+  A->view.n_mb_tokens = static_cast<int64_t>(P.mb_tokens.size());
+  A->view.n_single_tokens = static_cast<int64_t>(P.single_tokens.size());
+  A->view.n_zero_tokens = static_cast<int64_t>(P.zero_tokens.size());
   A->view.vocab = A->vocab;
   A->host.reset();
   A->mode = kEmpty;
@@ -165,7 +194,8 @@ int det_embedding_dw_acc_create(det_embedding_dw_acc** out, const int32_t* ids_h
   A->dim = dim;
   // every token has at most one partly filled block: blocks <= T/64 + distinct tokens
   A->max_blocks = n_logical / rbi::emb::kBlockOcc + std::min<int64_t>(n_logical, vocab);
-  A->plan_cap = static_cast<size_t>(n_logical + 3 * A->max_blocks + 2 * vocab + 1);
+  // occ, 4 block lists, 2 per-token arrays, 3 token lists that partition the vocabulary
+  A->plan_cap = static_cast<size_t>(n_logical + 4 * A->max_blocks + 3 * vocab + 1);
   hipError_t e = hipSuccess;
   auto cleanup = [&](const char* what) {
     if (A->d_plan) (void)hipFree(A->d_plan);
@@ -234,6 +264,9 @@ int det_embedding_dw_finalize(det_embedding_dw_acc* acc, float* dE, void* stream
   if (acc == nullptr) return fail(RMSNORM_EINVAL, "accumulator is NULL");
   int rc;
   if ((rc = check_tensor(dE, "dE", 16))) return rc;
+  if (acc->mode == kDirect)
+    return fail(RMSNORM_ESTATE,
+                "det_embedding_bwd keeps no block partials; call det_embedding_dw_acc_reset first");
   std::vector<int32_t> spilled;
   std::string err;
   rc = acc->host.prepare_finalize(&spilled, &err);
@@ -245,6 +278,36 @@ int det_embedding_dw_finalize(det_embedding_dw_acc* acc, float* dE, void* stream
     return hip_fail(e, "embedding block folds");
   if ((e = rbi::emb::launch_finalize(acc->d_P, acc->view, acc->dim, dE, st)) != hipSuccess)
     return hip_fail(e, "embedding token trees");
+  acc->host.finalized = true;
+  return RMSNORM_OK;
+}
+
+int det_embedding_bwd(const rmsnorm_bf16* dy, int64_t rows, int64_t dim, det_embedding_dw_acc* acc,
+                      float* dE, void* stream) {
+  if (acc == nullptr) return fail(RMSNORM_EINVAL, "accumulator is NULL");
+  int rc;
+  if ((rc = check_rows(rows))) return rc;
+  if (dim != acc->dim) return fail(RMSNORM_EINVAL, "dim differs from the accumulator's");
+  if (acc->host.finalized || acc->mode != kEmpty)
+    return fail(RMSNORM_ESTATE,
+                "det_embedding_bwd needs an accumulator with no contribution; call det_embedding_dw_acc_reset first");
+  if (rows != acc->host.n_logical)
+    return fail(RMSNORM_ECOVERAGE, "det_embedding_bwd takes all " +
+                                       std::to_string(acc->host.n_logical) + " logical rows, got " +
+                                       std::to_string(rows));
+  if ((rc = check_tensor(dE, "dE", 16))) return rc;
+  if (rows > 0 && (rc = check_tensor(dy, "dy", 16))) return rc;
+  if (rows > 0 && overlaps(dE, acc->vocab * dim * 4, dy, rows * dim * 2))
+    return fail(RMSNORM_EINVAL, "dE must not alias dy");
+  std::string err;
+  if ((rc = acc->host.register_call(nullptr, rows, &err)) != RMSNORM_OK) return fail(rc, err);
+  std::vector<int32_t> spilled;
+  if ((rc = acc->host.prepare_finalize(&spilled, &err)) != RMSNORM_OK) return fail(rc, err);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if ((e = rbi::emb::launch_bwd_one_call(dy, acc->d_P, acc->view, dim, dE, st)) != hipSuccess)
+    return hip_fail(e, "embedding one-call backward");
+  acc->mode = kDirect;
   acc->host.finalized = true;
   return RMSNORM_OK;
 }

@@ -110,3 +110,60 @@ def test_embedding_accumulator_protocol_and_new_ids():
         acc.set_ids(np.full(T, 50, np.int32))              # id outside the vocabulary
     assert ei.value.code == binding.EINVAL
     acc.close()
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_one_call_backward_is_the_accumulator_path(case):
+    """det_embedding_bwd (single-block tokens folded straight into dE) gives
+    the bits of contrib + finalize and of the EDO-v1 emulation."""
+    dim, vocab, lengths, _ = CASES[case]
+    wl = _wl(f"emb1_{case}", dim, vocab, lengths)
+    data = adapters.make_embedding_inputs(wl, device="cuda", gen_device="cpu")
+    counts = np.bincount(data.ids, minlength=vocab)
+    print(f"[embedding] {case}: one-call backward, {int((counts > 0).sum())} tokens, "
+          f"{int((counts > 64).sum())} with more than one block", flush=True)
+    acc = binding.EmbeddingDwAccumulator(data.ids, vocab, dim)
+    acc.contrib(data.dy)
+    via_acc = acc.finalize().cpu().numpy()
+    acc.reset()
+    one = acc.backward(data.dy).cpu().numpy()
+    assert np.array_equal(one.view(np.uint32), via_acc.view(np.uint32))
+    want = oracle.edo_v1_f32(data.ids, inputs.bf16_bits(data.dy.cpu()), vocab)
+    assert np.array_equal(one.view(np.uint32), want.view(np.uint32))
+    # a dE buffer holding garbage is fully overwritten
+    dE = torch.full((vocab, dim), float("nan"), device="cuda")
+    acc.reset()
+    acc.backward(data.dy, dE)
+    assert np.array_equal(dE.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    acc.close()
+
+
+def test_one_call_backward_protocol():
+    wl = _wl("emb1_proto", 64, 50, [100])
+    data = adapters.make_embedding_inputs(wl, device="cuda", gen_device="cpu")
+    T = wl.n_logical
+    acc = binding.EmbeddingDwAccumulator(data.ids, 50, 64)
+    with pytest.raises(binding.RmsNormError) as ei:
+        acc.backward(data.dy[:T - 1])                          # not every logical row
+    assert ei.value.code == binding.ECOVERAGE
+    half = layouts.chunked_packed(wl, sizes=[60, 40]).calls
+    acc.contrib(data.dy[:60], binding.Layout(half[0].row_logical, T))
+    with pytest.raises(binding.RmsNormError) as ei:
+        acc.backward(data.dy)                                  # already holds a contribution
+    assert ei.value.code == binding.ESTATE
+    acc.reset()
+    d1 = acc.backward(data.dy).cpu().numpy()
+    with pytest.raises(binding.RmsNormError) as ei:
+        acc.finalize()                                         # no partials are kept
+    assert ei.value.code == binding.ESTATE
+    with pytest.raises(binding.RmsNormError) as ei:
+        acc.backward(data.dy)                                  # finalized
+    assert ei.value.code == binding.ESTATE
+    acc.reset()
+    assert np.array_equal(d1.view(np.uint32), acc.backward(data.dy).cpu().numpy().view(np.uint32))
+    # a new batch's ids
+    ids2 = data.ids[::-1].copy()
+    acc.set_ids(ids2)
+    want = oracle.edo_v1_f32(ids2, inputs.bf16_bits(data.dy.cpu()), 50)
+    assert np.array_equal(acc.backward(data.dy).cpu().numpy().view(np.uint32), want.view(np.uint32))
+    acc.close()

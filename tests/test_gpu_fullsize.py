@@ -206,4 +206,11 @@ def test_embedding_v32000_d4096_t32768_sampled_columns():
     tb = inputs.bf16_bits(data.table)
     rows = _sample_rows(wl.n_logical)
     assert np.array_equal(out["y"][rows], tb[data.ids[rows]])
-    _log(f"{wl.name}: sampled columns match; {int((np.bincount(data.ids) > 0).sum())} tokens occur")
+    # the one-call backward: every bit of dE as the accumulator path
+    acc = binding.EmbeddingDwAccumulator(data.ids, wl.vocab, wl.hidden)
+    one = acc.backward(data.dy)
+    torch.cuda.synchronize()
+    acc.close()
+    assert np.array_equal(one.cpu().numpy().view(np.uint32), out["dE"].view(np.uint32))
+    _log(f"{wl.name}: sampled columns match, one-call backward bitwise; "
+         f"{int((np.bincount(data.ids) > 0).sum())} tokens occur")
