@@ -720,6 +720,29 @@ def main():
     torch.cuda.synchronize()
     bwd_only_ms = eb0.elapsed_time(eb1) / K
 
+    # The rstd-recompute backward on the same rows (no rstd read; rstd rebuilt
+    # in the forward's order): timed the same way, and checked bit for bit
+    # against the saved-rstd backward (dx and dweight).
+    s0 = sets[0]
+    dx_rc = torch.empty_like(s0["dx"])
+    dw_rc = torch.empty_like(s0["dw"])
+    binding.rmsnorm_bwd_dx_recompute(s0["x"].data_ptr(), w.data_ptr(), s0["dy"].data_ptr(),
+                                     wl.eps, dx_rc.data_ptr(), T, H, None, acc.handle, sh)
+    binding.rmsnorm_dw_finalize(acc.handle, dw_rc.data_ptr(), sh)
+    binding.rmsnorm_dw_acc_reset(acc.handle, sh)
+    torch.cuda.synchronize()
+    rc_same = bool(torch.equal(dx_rc.view(torch.int16), ref_dx.view(torch.int16))
+                   and torch.equal(dw_rc.view(torch.int32), ref_dw.view(torch.int32)))
+    eb0.record(stream)
+    for i in range(K):
+        s = sets[i % len(sets)]
+        binding.rmsnorm_bwd_dx_recompute(s["x"].data_ptr(), w.data_ptr(), s["dy"].data_ptr(),
+                                         wl.eps, s["dx"].data_ptr(), T, H, None, acc.handle, sh)
+        binding.rmsnorm_dw_acc_reset(acc.handle, sh)
+    eb1.record(stream)
+    torch.cuda.synchronize()
+    rc_ms = eb0.elapsed_time(eb1) / K
+
     fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     fin_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
@@ -776,6 +799,9 @@ def main():
         "copy_ceiling_gbps": None if copy_gbps is None else round(copy_gbps, 1),
         "frac_of_copy_ceiling": None if copy_gbps is None else round(value / copy_gbps, 4),
         "invariance_bn_vs_8xb1_bitwise": inv_ok,
+        "bwd_rstd_recompute": {"avg_launch_ms": round(rc_ms, 5),
+                               "gbps": round((bb - 4 * T) / (rc_ms * 1e-3) / 1e9, 1),
+                               "bitwise_equal_to_saved_rstd": rc_same},
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(out))

@@ -76,8 +76,9 @@ typedef struct rmsnorm_dw_acc rmsnorm_dw_acc;
 int rmsnorm_max_hidden(void);
 
 /* Forward.  x[rows][hidden] -> y[rows][hidden] (bf16, rounded to nearest
- * even) and rstd[rows] (FP32, kept for the backward).  With a layout, rows
- * mapped to -1 are padding: they are not read and get y = 0, rstd = 0.
+ * even) and rstd[rows] (FP32, kept for the backward; rstd may be NULL when
+ * the backward rebuilds it, see rmsnorm_bwd_dx_recompute).  With a layout,
+ * rows mapped to -1 are padding: they are not read and get y = 0, rstd = 0.
  * layout->rows must equal rows.  The result of a row depends only on that
  * row's values (never on its position, the row count or the layout). */
 int rmsnorm_fwd(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y, float* rstd,
@@ -94,6 +95,20 @@ int rmsnorm_fwd(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y, f
 int rmsnorm_bwd_dx(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
                    const float* rstd, rmsnorm_bf16* dx, int64_t rows, int64_t hidden,
                    const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, void* stream);
+
+/* Backward dx without the saved rstd: the same formulas as rmsnorm_bwd_dx,
+ * with rstd rebuilt from x and eps (the forward's eps) inside the same pass.
+ * The pages define the backward from rstd and leave open whether it is
+ * saved or recomputed; this is the recompute form.  The sum of x_j^2 runs
+ * in the same order as in rmsnorm_fwd, so rstd -- and therefore dx and the
+ * dweight contributions -- are bit for bit those of rmsnorm_bwd_dx given
+ * the forward's rstd.  Arguments and errors as rmsnorm_bwd_dx, plus eps
+ * (finite, >= 0, else RMSNORM_EINVAL); dx is required.  Contiguous rows
+ * only.  Every call runs the fused one-pass kernel (calls touching few
+ * blocks do not take the two-pass path, which reads rstd). */
+int rmsnorm_bwd_dx_recompute(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
+                             float eps, rmsnorm_bf16* dx, int64_t rows, int64_t hidden,
+                             const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, void* stream);
 
 /* Per-head norm inside a packed tensor (for example the Q or K heads of a
  * fused QKV projection output, with no copy out of it).  The rows are

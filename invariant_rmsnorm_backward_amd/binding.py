@@ -27,6 +27,7 @@ EXPORTED = ("rmsnorm_max_hidden", "rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_c
             "rmsnorm_layout_check", "rmsnorm_dw_acc_create", "rmsnorm_dw_acc_reset",
             "rmsnorm_dw_acc_destroy", "rmsnorm_last_error", "rmsnorm_backend_info",
             "rmsnorm_set_split_threshold", "rmsnorm_fwd_packed", "rmsnorm_bwd_dx_packed",
+            "rmsnorm_bwd_dx_recompute",
             "det_gemm_fwd", "det_gemm_bwd_dx", "det_gemm_dw_acc_create", "det_gemm_dw_contrib",
             "det_gemm_dw_finalize", "det_gemm_dw_acc_reset", "det_gemm_dw_acc_destroy",
             "det_embedding_fwd", "det_embedding_dw_acc_create", "det_embedding_dw_acc_set_ids",
@@ -64,6 +65,7 @@ def load() -> ctypes.CDLL:
         "rmsnorm_max_hidden": ([], I32),
         "rmsnorm_fwd": ([P, P, P, P, I64, I64, ctypes.c_float, P, P], I32),
         "rmsnorm_bwd_dx": ([P, P, P, P, P, I64, I64, P, P, P], I32),
+        "rmsnorm_bwd_dx_recompute": ([P, P, P, ctypes.c_float, P, I64, I64, P, P, P], I32),
         "rmsnorm_dw_contrib": ([P, P, P, I64, I64, P, P, P], I32),
         "rmsnorm_dw_finalize": ([P, P, P], I32),
         "rmsnorm_layout_create": ([PP, P, I64, I64, P], I32),
@@ -128,6 +130,13 @@ def rmsnorm_bwd_dx(x: int, w: int, dy: int, rstd: int, dx: int, rows: int, hidde
                    layout: Optional[int], acc: Optional[int], stream: Optional[int]) -> None:
     _check(load().rmsnorm_bwd_dx(x, w, dy, rstd, dx, rows, hidden, layout, acc, stream),
            "rmsnorm_bwd_dx")
+
+
+def rmsnorm_bwd_dx_recompute(x: int, w: int, dy: int, eps: float, dx: int, rows: int, hidden: int,
+                             layout: Optional[int], acc: Optional[int],
+                             stream: Optional[int]) -> None:
+    _check(load().rmsnorm_bwd_dx_recompute(x, w, dy, eps, dx, rows, hidden, layout, acc, stream),
+           "rmsnorm_bwd_dx_recompute")
 
 
 def rmsnorm_dw_contrib(x: int, dy: int, rstd: int, rows: int, hidden: int,
@@ -351,15 +360,18 @@ def _handle(obj) -> Optional[int]:
 
 
 def fwd(x, w, eps: float, layout: Optional[Layout] = None, y=None, rstd=None,
-        stream: Optional[int] = None) -> Tuple:
-    """y, rstd = RMSNorm forward of bf16 ``x[rows, hidden]`` (device tensors)."""
+        stream: Optional[int] = None, save_rstd: bool = True) -> Tuple:
+    """y, rstd = RMSNorm forward of bf16 ``x[rows, hidden]`` (device tensors);
+    with save_rstd=False no rstd is written and None is returned for it."""
     import torch
     rows, hidden = x.shape
     y = torch.empty_like(x) if y is None else y
-    rstd = torch.empty(rows, dtype=torch.float32, device=x.device) if rstd is None else rstd
-    rmsnorm_fwd(x.data_ptr(), w.data_ptr(), y.data_ptr(), rstd.data_ptr(), rows, hidden,
-                float(eps), _handle(layout), current_stream() if stream is None else stream)
-    return y, rstd
+    if save_rstd and rstd is None:
+        rstd = torch.empty(rows, dtype=torch.float32, device=x.device)
+    rmsnorm_fwd(x.data_ptr(), w.data_ptr(), y.data_ptr(), rstd.data_ptr() if save_rstd else None,
+                rows, hidden, float(eps), _handle(layout),
+                current_stream() if stream is None else stream)
+    return y, (rstd if save_rstd else None)
 
 
 def bwd(x, w, dy, rstd, layout: Optional[Layout] = None, acc: Optional[DwAccumulator] = None,
@@ -371,6 +383,18 @@ def bwd(x, w, dy, rstd, layout: Optional[Layout] = None, acc: Optional[DwAccumul
     rmsnorm_bwd_dx(x.data_ptr(), w.data_ptr(), dy.data_ptr(), rstd.data_ptr(), dx.data_ptr(),
                    rows, hidden, _handle(layout), _handle(acc),
                    current_stream() if stream is None else stream)
+    return dx
+
+
+def bwd_recompute(x, w, dy, eps: float, layout: Optional[Layout] = None,
+                  acc: Optional[DwAccumulator] = None, dx=None, stream: Optional[int] = None):
+    """dx of bf16 ``x`` with rstd rebuilt from x (bitwise the forward's rstd)."""
+    import torch
+    rows, hidden = x.shape
+    dx = torch.empty_like(x) if dx is None else dx
+    rmsnorm_bwd_dx_recompute(x.data_ptr(), w.data_ptr(), dy.data_ptr(), float(eps), dx.data_ptr(),
+                             rows, hidden, _handle(layout), _handle(acc),
+                             current_stream() if stream is None else stream)
     return dx
 
 

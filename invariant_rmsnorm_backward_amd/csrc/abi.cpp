@@ -87,11 +87,12 @@ static int fwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16
                                      ") differ from rows (" + std::to_string(rows) + ")");
   if (rows == 0) return RMSNORM_OK;
   if ((rc = check_tensor(x, "x", 16)) || (rc = check_tensor(w, "w", 16)) ||
-      (rc = check_tensor(y, "y", 16)) || (rc = check_tensor(rstd, "rstd", 4)))
+      (rc = check_tensor(y, "y", 16)))
     return rc;
+  if (rstd != nullptr && (rc = check_tensor(rstd, "rstd", 4))) return rc;   // NULL: not saved
   const size_t nbytes = static_cast<size_t>(extent) * 2;
   if (overlaps(y, nbytes, x, nbytes) || overlaps(y, nbytes, w, hidden * 2) ||
-      overlaps(rstd, rows * 4, x, nbytes) || overlaps(rstd, rows * 4, y, nbytes))
+      (rstd != nullptr && (overlaps(rstd, rows * 4, x, nbytes) || overlaps(rstd, rows * 4, y, nbytes))))
     return fail(RMSNORM_EINVAL, "outputs must not alias inputs or each other");
   rbi::FwdArgs a{x, w, y, rstd, rows, static_cast<int32_t>(hidden), eps,
                  layout ? layout->dev.row_logical : nullptr, pk};
@@ -118,12 +119,16 @@ static int check_packing(int64_t tokens, int64_t heads, int64_t head_dim, int64_
   return RMSNORM_OK;
 }
 
+// recompute: rstd is not read (NULL) but rebuilt from x with eps.
 static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
                       const float* rstd, rmsnorm_bf16* dx, int64_t rows, int64_t hidden,
                       const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, void* stream,
-                      bool with_dx, const rbi::RowPacking& pk, int64_t extent) {
+                      bool with_dx, const rbi::RowPacking& pk, int64_t extent,
+                      bool recompute = false, float eps = 0.0f) {
   int rc;
   if ((rc = check_rows(rows)) || (rc = check_hidden(hidden))) return rc;
+  if (recompute && (!(eps >= 0.0f) || std::isinf(eps)))
+    return fail(RMSNORM_EINVAL, "eps must be finite and >= 0");
   if (layout != nullptr && layout->host.rows != rows)
     return fail(RMSNORM_ELAYOUT, "layout rows (" + std::to_string(layout->host.rows) +
                                      ") differ from rows (" + std::to_string(rows) + ")");
@@ -135,14 +140,14 @@ static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnor
       return fail(RMSNORM_ESTATE, "accumulator already finalized; call rmsnorm_dw_acc_reset first");
   }
   if (rows > 0) {
-    if ((rc = check_tensor(x, "x", 16)) || (rc = check_tensor(dy, "dy", 16)) ||
-        (rc = check_tensor(rstd, "rstd", 4)))
-      return rc;
+    if ((rc = check_tensor(x, "x", 16)) || (rc = check_tensor(dy, "dy", 16))) return rc;
+    if (!recompute && (rc = check_tensor(rstd, "rstd", 4))) return rc;
     if (with_dx) {
       if ((rc = check_tensor(w, "w", 16)) || (rc = check_tensor(dx, "dx", 16))) return rc;
       const size_t nbytes = static_cast<size_t>(extent) * 2;
       if (overlaps(dx, nbytes, x, nbytes) || overlaps(dx, nbytes, dy, nbytes) ||
-          overlaps(dx, nbytes, w, hidden * 2) || overlaps(dx, nbytes, rstd, rows * 4))
+          overlaps(dx, nbytes, w, hidden * 2) ||
+          (!recompute && overlaps(dx, nbytes, rstd, rows * 4)))
         return fail(RMSNORM_EINVAL, "dx must not alias an input");
     }
   }
@@ -157,7 +162,8 @@ static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnor
   a.x = x;
   a.w = w;
   a.dy = dy;
-  a.rstd = rstd;
+  a.rstd = recompute ? nullptr : rstd;
+  a.eps = eps;
   a.dx = with_dx ? dx : nullptr;
   a.P = acc ? acc->d_P : nullptr;
   a.S = acc ? acc->d_S : nullptr;
@@ -170,7 +176,8 @@ static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnor
     a.plan.n_items = static_cast<int32_t>(rbi::num_blocks(rows));
     a.plan.n_pad = 0;
   }
-  hipError_t e = rbi::launch_bwd(a, with_dx, acc != nullptr, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = rbi::launch_bwd(a, with_dx, acc != nullptr, reinterpret_cast<hipStream_t>(stream),
+                                 recompute);
   if (e != hipSuccess) return hip_fail(e, "rmsnorm backward launch");
   return RMSNORM_OK;
 }
@@ -198,6 +205,13 @@ int rmsnorm_bwd_dx(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_b
                    const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, void* stream) {
   return bwd_common(x, w, dy, rstd, dx, rows, hidden, layout, acc, stream, true,
                     rbi::RowPacking{}, rows * hidden);
+}
+
+int rmsnorm_bwd_dx_recompute(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
+                             float eps, rmsnorm_bf16* dx, int64_t rows, int64_t hidden,
+                             const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, void* stream) {
+  return bwd_common(x, w, dy, nullptr, dx, rows, hidden, layout, acc, stream, true,
+                    rbi::RowPacking{}, rows * hidden, true, eps);
 }
 
 int rmsnorm_bwd_dx_packed(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,

@@ -64,11 +64,15 @@ struct BwdArgs {
   int32_t hidden;
   PlanDev plan;
   RowPacking pack{};
+  float eps = 0.0f;    // used only when rstd is rebuilt
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // with_dx: write dx (and zero padding rows); with_dw: fold dweight contributions.
-hipError_t launch_bwd(const BwdArgs& a, bool with_dx, bool with_dw, hipStream_t stream);
+// recompute: rstd is not read but rebuilt from x with a.eps in the forward's
+// order (bitwise the saved rstd); needs with_dx and contiguous rows.
+hipError_t launch_bwd(const BwdArgs& a, bool with_dx, bool with_dw, hipStream_t stream,
+                      bool recompute = false);
 // Rebuild the partials of spilled blocks from their spill rows.
 hipError_t launch_rebuild(const float* S, float* P, const int32_t* blocks, int32_t n_blocks,
                           int64_t n_logical, int32_t hidden, hipStream_t stream);

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void fwd_wide_kernel(FwdArgs a) {
         const int q = k * 64 + lane;
         if (k < V - 1 || q < nchunk) store16_stream(yr + q * 8, make_uint4(0, 0, 0, 0));
       }
-      if (lane == 0) a.rstd[row] = 0.0f;
+      if (lane == 0 && a.rstd != nullptr) a.rstd[row] = 0.0f;
       continue;
     }
     const uint16_t* xr = a.x + row * H;
@@ -68,15 +68,25 @@ __global__ __launch_bounds__(256) void fwd_wide_kernel(FwdArgs a) {
       const int q = k * 64 + lane;
       xv[k] = (k < V - 1 || q < nchunk) ? load16_stream(xr + q * 8) : make_uint4(0, 0, 0, 0);
     }
-    float ss = 0.0f;
+    // The sum of squares in the order the backward can rebuild without the
+    // saved rstd: above 1024 columns the backward splits a row over two
+    // wavefronts (chunks k < VB and k >= VB of every lane), so each part has
+    // its own chain and wavefront sum, and the two sums are added.
+    const int VB = (H + 1023) >> 10;
+    float ss0 = 0.0f, ss1 = 0.0f;
 #pragma unroll
     for (int k = 0; k < V; ++k) {
       float f[8];
       unpack8(xv[k], f);
+      if (H > 1024 && k >= VB) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+        for (int e = 0; e < 8; ++e) ss1 = fmaf(f[e], f[e], ss1);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss0 = fmaf(f[e], f[e], ss0);
+      }
     }
-    ss = wave_sum(ss);
+    const float ss = H > 1024 ? wave_sum(ss0) + wave_sum(ss1) : wave_sum(ss0);
     const float r = rsqrtf(ss / (float)H + a.eps);
 #pragma unroll
     for (int k = 0; k < V; ++k) launder(xv[k]);
@@ -92,7 +102,7 @@ __global__ __launch_bounds__(256) void fwd_wide_kernel(FwdArgs a) {
         store16_stream(yr + q * 8, pack8(o));
       }
     }
-    if (lane == 0) a.rstd[row] = r;
+    if (lane == 0 && a.rstd != nullptr) a.rstd[row] = r;
   }
 }
 
@@ -125,7 +135,7 @@ __global__ __launch_bounds__(256) void fwd_small_kernel(FwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = pad ? 0.0f : (f[e] * r) * wf[e];
       store16_stream(a.y + off + sub * 8, pack8(o));
-      if (sub == 0) a.rstd[row] = pad ? 0.0f : r;
+      if (sub == 0 && a.rstd != nullptr) a.rstd[row] = pad ? 0.0f : r;
     }
   }
 }
@@ -176,7 +186,10 @@ __device__ __forceinline__ void stage_w(const BwdArgs& a, float* w_s, int tid, i
 // in registers; otherwise they are written to the spill rows.  When two row
 // buffers fit in registers the loop is software-pipelined: the next slot's
 // row is loaded before the current row's reduction and dx pass.
-template <int V, int TW, bool FULL, bool PLAN, bool DX, bool DW, bool COMPLETE>
+// RC: rstd is not read but rebuilt from the row, in the forward's order
+// (each wavefront's chain and wavefront sum; the TW sums added in order), so
+// its bits are the saved rstd's; the contributions then wait for it.
+template <int V, int TW, bool FULL, bool PLAN, bool DX, bool DW, bool COMPLETE, bool RC = false>
 struct WideBlock {
   using Sh = WideShape<V, TW, FULL>;
   const BwdArgs& a;
@@ -184,6 +197,7 @@ struct WideBlock {
   const float* w_s;
   float* dot_s;
   float (&acc)[DW ? V * 8 : 1];
+  float* ss_s = nullptr;
   // Lane j (< SLOTS) holds the physical row of this stream's slot j and its
   // rstd, loaded once per block; the row loop reads them as scalars, so the
   // only vector loads in the loop are the row data (in-order waits stay
@@ -194,7 +208,7 @@ struct WideBlock {
   __device__ __forceinline__ void load_slots() {
     // every lane loads (lanes past SLOTS repeat a slot): no divergent memory ops
     slot_p = slot_row_t<PLAN>(a, item, blk, stream + Sh::S * (lane & (Sh::SLOTS - 1)));
-    slot_r = a.rstd[slot_p >= 0 ? slot_p : 0];
+    if (!RC) slot_r = a.rstd[slot_p >= 0 ? slot_p : 0];
   }
   // Consume both slot registers before the row loop: the compiler then waits
   // for their loads once, instead of inserting a full vmcnt(0) wait inside
@@ -227,7 +241,7 @@ struct WideBlock {
 
   __device__ __forceinline__ void process(int i, int p, uint4 (&xv)[V], uint4 (&dv)[V], float r) {
     const int s = stream + Sh::S * i;
-    float dot = 0.0f;
+    float dot = 0.0f, ss = 0.0f;
     if (p >= 0) {
       float* srow = COMPLETE ? nullptr : a.S + ((int64_t)blk * kBlockRows + s) * H + base;
 #pragma unroll
@@ -240,25 +254,61 @@ struct WideBlock {
         for (int e = 0; e < 8; ++e) {
           const float pr = df[e] * xf[e];          // exact: two bf16 significands
           if (DX) dot = fmaf(pr, w_s[base + k * 512 + e], dot);
+          if (RC) ss = fmaf(xf[e], xf[e], ss);
           c[e] = pr * r;                           // the row's contribution, rounded once
-          if (DW && COMPLETE) acc[k * 8 + e] = acc[k * 8 + e] + c[e];
+          if (!RC && DW && COMPLETE) acc[k * 8 + e] = acc[k * 8 + e] + c[e];
         }
-        if (DW && !COMPLETE && in_row(k)) {
+        if (!RC && DW && !COMPLETE && in_row(k)) {
           store_f4_stream(srow + k * 512, c[0], c[1], c[2], c[3]);
           store_f4_stream(srow + k * 512 + 4, c[4], c[5], c[6], c[7]);
         }
       }
-      if (DX && TW == 1) dot = wave_sum(dot);
+      if (TW == 1) {
+        if (DX) dot = wave_sum(dot);
+        if (RC) ss = wave_sum(ss);
+      }
+    }
+    if (DX || RC) {
+      if (TW > 1) {
+        // the row's wavefronts exchange their partial sums through LDS
+        if (DX) dot = wave_sum(dot);
+        if (RC) ss = wave_sum(ss);
+        if (lane == 0) {
+          if (DX) dot_s[(i & 1) * 16 + wv] = dot;
+          if (RC) ss_s[(i & 1) * 16 + wv] = ss;
+        }
+        __syncthreads();
+        if (DX) {
+          const float* d = &dot_s[(i & 1) * 16 + stream * TW];
+          dot = TW == 2 ? d[0] + d[1] : (d[0] + d[1]) + (d[2 % TW] + d[3 % TW]);
+        }
+        if (RC) {
+          static_assert(!RC || TW <= 2, "the forward's order covers two wavefronts per row");
+          const float* q = &ss_s[(i & 1) * 16 + stream * TW];
+          ss = q[0] + q[1];
+        }
+      }
+      if (RC) r = p >= 0 ? rsqrtf(ss / (float)H + a.eps) : 0.0f;
+    }
+    if (RC && DW && p >= 0) {
+      float* srow = COMPLETE ? nullptr : a.S + ((int64_t)blk * kBlockRows + s) * H + base;
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        float xf[8], df[8], c[8];
+        unpack8(xv[k], xf);
+        unpack8(dv[k], df);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          c[e] = (df[e] * xf[e]) * r;
+          if (COMPLETE) acc[k * 8 + e] = acc[k * 8 + e] + c[e];
+        }
+        if (!COMPLETE && in_row(k)) {
+          store_f4_stream(srow + k * 512, c[0], c[1], c[2], c[3]);
+          store_f4_stream(srow + k * 512 + 4, c[4], c[5], c[6], c[7]);
+        }
+      }
     }
     if (DX) {
-      if (TW > 1) {
-        // the row's wavefronts exchange their partial dots through LDS
-        dot = wave_sum(dot);
-        if (lane == 0) dot_s[(i & 1) * 16 + wv] = dot;
-        __syncthreads();
-        const float* d = &dot_s[(i & 1) * 16 + stream * TW];
-        dot = TW == 2 ? d[0] + d[1] : (d[0] + d[1]) + (d[2 % TW] + d[3 % TW]);
-      }
       if (p >= 0) {
         const float kk = ((r * r) * r) * (dot / (float)H);
         uint16_t* xo = a.dx + (int64_t)p * H + base;
@@ -287,8 +337,9 @@ struct WideBlock {
   }
 
   // Two row buffers fit in the register file only up to 8 chunks per lane
-  // without masks; wider or masked rows are processed one at a time.
-  static constexpr bool PIPE = FULL && V <= 8;
+  // without masks (4 when rstd is rebuilt, which keeps the row for a second
+  // pass); wider or masked rows are processed one at a time.
+  static constexpr bool PIPE = FULL && V <= (RC ? 4 : 8);
 
   __device__ __forceinline__ void run() {
     load_slots();
@@ -323,12 +374,13 @@ struct WideBlock {
   }
 };
 
-template <int V, int TW, bool FULL, bool PLAN, bool DX, bool DW>
+template <int V, int TW, bool FULL, bool PLAN, bool DX, bool DW, bool RC>
 __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
   using Sh = WideShape<V, TW, FULL>;
   __shared__ float w_s[DX ? Sh::COLS : 1];
   __shared__ float tile_s[DW ? kStreams * 1024 : 1];
   __shared__ float dot_s[(DX && TW > 1) ? 2 * 16 : 1];
+  __shared__ float ss_s[(RC && TW > 1) ? 2 * 16 : 1];
 
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
@@ -370,11 +422,11 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
 
   const int base = half * V * 512 + lane * 8;      // this lane's first column
   if (!DW || complete) {
-    WideBlock<V, TW, FULL, PLAN, DX, DW, true>{a, item, blk, stream, half, lane, wv, H, nchunk,
-                                               base, w_s, dot_s, acc}.run();
+    WideBlock<V, TW, FULL, PLAN, DX, DW, true, RC>{a, item, blk, stream, half, lane, wv, H, nchunk,
+                                                   base, w_s, dot_s, acc, ss_s}.run();
   } else {
-    WideBlock<V, TW, FULL, PLAN, DX, DW, false>{a, item, blk, stream, half, lane, wv, H, nchunk,
-                                                base, w_s, dot_s, acc}.run();
+    WideBlock<V, TW, FULL, PLAN, DX, DW, false, RC>{a, item, blk, stream, half, lane, wv, H, nchunk,
+                                                    base, w_s, dot_s, acc, ss_s}.run();
     return;
   }
 
@@ -534,7 +586,9 @@ __global__ __launch_bounds__(256) void dw_cols_kernel(BwdArgs a) {
 
 // Small rows: hidden = 8L (L in 1..32), one group of L lanes per row; the
 // 64 slots' contributions go through LDS and the 4 streams fold them there.
-template <int L, bool DX, bool DW, bool PACKED>
+// RC: rstd rebuilt from the row in the forward's order (the same lanes, the
+// same chain and group sum), so its bits are the saved rstd's.
+template <int L, bool DX, bool DW, bool PACKED, bool RC>
 __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
   constexpr int H = 8 * L;
   constexpr int GROUPS = 256 / L;
@@ -585,16 +639,25 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
     const int64_t off = row_off<PACKED>(a.pack, row, H);
     xv[it] = load16_stream(a.x + off + sub * 8);
     dv[it] = load16_stream(a.dy + off + sub * 8);
-    rr[it] = a.rstd[row];
+    if (!RC) rr[it] = a.rstd[row];
   }
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int s = g + it * GROUPS;
     const int p = pp[it];
-    const float r = p >= 0 ? rr[it] : 0.0f;
     float xf[8], df[8], pr[8];
     unpack8(p >= 0 ? xv[it] : make_uint4(0, 0, 0, 0), xf);
     unpack8(p >= 0 ? dv[it] : make_uint4(0, 0, 0, 0), df);
+    float r;
+    if (RC) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(xf[e], xf[e], ss);
+      ss = group_sum<L>(ss);
+      r = p >= 0 ? rsqrtf(ss / (float)H + a.eps) : 0.0f;
+    } else {
+      r = p >= 0 ? rr[it] : 0.0f;
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) pr[e] = df[e] * xf[e];
     if (DX) {
@@ -798,8 +861,15 @@ int64_t split_items() {
 }
 
 template <int V, int TW, bool FULL, bool PLAN>
-static void bwd_wide_go3(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+static void bwd_wide_go3(const BwdArgs& a, bool dx, bool dw, bool rc, hipStream_t st) {
   using Sh = WideShape<V, TW, FULL>;
+  if (rc) {   // rstd rebuilt in the fused kernel (the two-pass path reads rstd)
+    const int pad_groups = (a.plan.n_pad + Sh::WAVES - 1) / Sh::WAVES;
+    const dim3 grid((unsigned)(a.plan.n_items + pad_groups)), block(Sh::THREADS);
+    if (dw) bwd_wide_kernel<V, TW, FULL, PLAN, true, true, true><<<grid, block, 0, st>>>(a);
+    else bwd_wide_kernel<V, TW, FULL, PLAN, true, false, true><<<grid, block, 0, st>>>(a);
+    return;
+  }
   if (a.plan.n_items < split_items()) {
     if (dx && a.rows > 0) {
       int64_t g = (a.rows + Sh::S - 1) / Sh::S;
@@ -814,59 +884,63 @@ static void bwd_wide_go3(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
   }
   const int pad_groups = dx ? (a.plan.n_pad + Sh::WAVES - 1) / Sh::WAVES : 0;
   const dim3 grid((unsigned)(a.plan.n_items + pad_groups)), block(Sh::THREADS);
-  if (dx && dw) bwd_wide_kernel<V, TW, FULL, PLAN, true, true><<<grid, block, 0, st>>>(a);
-  else if (dx) bwd_wide_kernel<V, TW, FULL, PLAN, true, false><<<grid, block, 0, st>>>(a);
-  else bwd_wide_kernel<V, TW, FULL, PLAN, false, true><<<grid, block, 0, st>>>(a);
+  if (dx && dw) bwd_wide_kernel<V, TW, FULL, PLAN, true, true, false><<<grid, block, 0, st>>>(a);
+  else if (dx) bwd_wide_kernel<V, TW, FULL, PLAN, true, false, false><<<grid, block, 0, st>>>(a);
+  else bwd_wide_kernel<V, TW, FULL, PLAN, false, true, false><<<grid, block, 0, st>>>(a);
 }
 template <int V, int TW, bool FULL>
-static void bwd_wide_go2(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
-  if (a.plan.item_info != nullptr) bwd_wide_go3<V, TW, FULL, true>(a, dx, dw, st);
-  else bwd_wide_go3<V, TW, FULL, false>(a, dx, dw, st);
+static void bwd_wide_go2(const BwdArgs& a, bool dx, bool dw, bool rc, hipStream_t st) {
+  if (a.plan.item_info != nullptr) bwd_wide_go3<V, TW, FULL, true>(a, dx, dw, rc, st);
+  else bwd_wide_go3<V, TW, FULL, false>(a, dx, dw, rc, st);
 }
 template <int V, int TW>
-static void bwd_wide_go(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
-  if (a.hidden == 512 * V * TW) bwd_wide_go2<V, TW, true>(a, dx, dw, st);
-  else bwd_wide_go2<V, TW, false>(a, dx, dw, st);
+static void bwd_wide_go(const BwdArgs& a, bool dx, bool dw, bool rc, hipStream_t st) {
+  if (a.hidden == 512 * V * TW) bwd_wide_go2<V, TW, true>(a, dx, dw, rc, st);
+  else bwd_wide_go2<V, TW, false>(a, dx, dw, rc, st);
 }
 template <int L>
-static void bwd_small_go(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+static void bwd_small_go(const BwdArgs& a, bool dx, bool dw, bool rc, hipStream_t st) {
   constexpr int GROUPS = 256 / L;
   const int pad_groups = dx ? (a.plan.n_pad + GROUPS - 1) / GROUPS : 0;
   const dim3 grid((unsigned)(a.plan.n_items + pad_groups)), block(256);
-  if (is_packed(a.pack, a.hidden)) {
-    if (dx && dw) bwd_small_kernel<L, true, true, true><<<grid, block, 0, st>>>(a);
-    else if (dx) bwd_small_kernel<L, true, false, true><<<grid, block, 0, st>>>(a);
-    else bwd_small_kernel<L, false, true, true><<<grid, block, 0, st>>>(a);
+  if (rc) {   // contiguous rows only (the packed entry points read the saved rstd)
+    if (dw) bwd_small_kernel<L, true, true, false, true><<<grid, block, 0, st>>>(a);
+    else bwd_small_kernel<L, true, false, false, true><<<grid, block, 0, st>>>(a);
+  } else if (is_packed(a.pack, a.hidden)) {
+    if (dx && dw) bwd_small_kernel<L, true, true, true, false><<<grid, block, 0, st>>>(a);
+    else if (dx) bwd_small_kernel<L, true, false, true, false><<<grid, block, 0, st>>>(a);
+    else bwd_small_kernel<L, false, true, true, false><<<grid, block, 0, st>>>(a);
   } else {
-    if (dx && dw) bwd_small_kernel<L, true, true, false><<<grid, block, 0, st>>>(a);
-    else if (dx) bwd_small_kernel<L, true, false, false><<<grid, block, 0, st>>>(a);
-    else bwd_small_kernel<L, false, true, false><<<grid, block, 0, st>>>(a);
+    if (dx && dw) bwd_small_kernel<L, true, true, false, false><<<grid, block, 0, st>>>(a);
+    else if (dx) bwd_small_kernel<L, true, false, false, false><<<grid, block, 0, st>>>(a);
+    else bwd_small_kernel<L, false, true, false, false><<<grid, block, 0, st>>>(a);
   }
 }
 
-hipError_t launch_bwd(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+hipError_t launch_bwd(const BwdArgs& a, bool dx, bool dw, hipStream_t st, bool rc) {
+  if (rc && (!dx || is_packed(a.pack, a.hidden))) return hipErrorInvalidValue;
   if (is_packed(a.pack, a.hidden) && !packed_hidden_supported(a.hidden)) return hipErrorInvalidValue;
   const int pads = dx ? a.plan.n_pad : 0;
   if (a.plan.n_items + pads == 0) return hipSuccess;
   switch (small_lanes(a.hidden)) {
-    case 1: bwd_small_go<1>(a, dx, dw, st); return hipGetLastError();
-    case 2: bwd_small_go<2>(a, dx, dw, st); return hipGetLastError();
-    case 4: bwd_small_go<4>(a, dx, dw, st); return hipGetLastError();
-    case 8: bwd_small_go<8>(a, dx, dw, st); return hipGetLastError();
-    case 16: bwd_small_go<16>(a, dx, dw, st); return hipGetLastError();
-    case 32: bwd_small_go<32>(a, dx, dw, st); return hipGetLastError();
+    case 1: bwd_small_go<1>(a, dx, dw, rc, st); return hipGetLastError();
+    case 2: bwd_small_go<2>(a, dx, dw, rc, st); return hipGetLastError();
+    case 4: bwd_small_go<4>(a, dx, dw, rc, st); return hipGetLastError();
+    case 8: bwd_small_go<8>(a, dx, dw, rc, st); return hipGetLastError();
+    case 16: bwd_small_go<16>(a, dx, dw, rc, st); return hipGetLastError();
+    case 32: bwd_small_go<32>(a, dx, dw, rc, st); return hipGetLastError();
     default: break;
   }
   const int tw = wide_tw(a.hidden), V = wide_v(a.hidden);
   if (tw == 1) {
     switch (V) {
-      case 1: bwd_wide_go<1, 1>(a, dx, dw, st); break;
-      case 2: bwd_wide_go<2, 1>(a, dx, dw, st); break;
+      case 1: bwd_wide_go<1, 1>(a, dx, dw, rc, st); break;
+      case 2: bwd_wide_go<2, 1>(a, dx, dw, rc, st); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (V) {
-#define RBI_BWD2(v) case v: bwd_wide_go<v, 2>(a, dx, dw, st); break;
+#define RBI_BWD2(v) case v: bwd_wide_go<v, 2>(a, dx, dw, rc, st); break;
       RBI_BWD2(2) RBI_BWD2(3) RBI_BWD2(4) RBI_BWD2(5) RBI_BWD2(6)
       RBI_BWD2(7) RBI_BWD2(8) RBI_BWD2(9) RBI_BWD2(10)
 #undef RBI_BWD2
