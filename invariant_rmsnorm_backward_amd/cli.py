@@ -34,6 +34,8 @@ SMALL = {  # reduced lengths for quick sweeps (same recipe and seed)
 # Multi-op targets: a linear workload run behind an RMSNorm of its input width.
 CHAINS = {"chain_rmsnorm_linear_h4096_o4096_t32768": "linear_h4096_o4096_t32768"}
 CHUNK = {"rmsnorm_h8_t59": 7, "qknorm": 512}
+# An RMSNorm workload name with this suffix runs the rstd-recompute backward.
+RECOMPUTE = "+recompute"
 
 
 def _workload(name: str, small: bool) -> inputs.Workload:
@@ -93,6 +95,10 @@ def _targets(names, small):
         elif n in inputs.LINEAR_WORKLOADS:
             wl = _workload(n, small)
             out.append(("det_gemm", n, (wl,), (_cells(wl),)))
+        elif n.endswith(RECOMPUTE):
+            base = n[: -len(RECOMPUTE)]
+            wl = _workload(base, small)
+            out.append(("rms_norm_recompute", n, (wl,), (_cells(wl),)))
         elif n.startswith("qknorm"):
             base = "qknorm_d128_t16384"
             wq, wk = _workload(base + "_q", small), _workload(base + "_k", small)

@@ -322,9 +322,10 @@ def test_cli_sweeps_are_green(tmp_path):
                      "--workload", "rmsnorm_h5120_packed131072",
                      "--workload", "linear_h4096_o4096_t32768",
                      "--workload", "chain_rmsnorm_linear_h4096_o4096_t32768",
+                     "--workload", "rmsnorm_h5120_packed131072+recompute",
                      "--small", "--json", str(out)]) == 0
     assert cli.main(["check", "--workload", "rmsnorm_h4096_t32768", "--cell", "BN/chunked",
                      "--small"]) == 0
     import json
     reps = json.loads(out.read_text())
-    assert len(reps) == 5 and all(r["strict"] for r in reps)
+    assert len(reps) == 6 and all(r["strict"] for r in reps)

@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from invariant_rmsnorm_backward_amd import binding, inputs, layouts
+from invariant_rmsnorm_backward_amd import binding, contract, harness, inputs, layouts
+from tests import parity_utils as pu
 
 pytestmark = pytest.mark.gpu
 EPS = 1e-6
@@ -95,3 +96,21 @@ def test_recompute_argument_errors():
         binding.rmsnorm_bwd_dx_recompute(x.data_ptr(), w.data_ptr(), x.data_ptr(), 1e-6, None,
                                          10, 64, None, None, None)
     assert ei.value.code == binding.EINVAL
+
+
+def test_recompute_adapter_through_the_harness():
+    """rms_norm_recompute over every layout family of a padded, permuted,
+    masked workload: bitwise invariant and within the contract of the oracle."""
+    wl = inputs.scaled(inputs.workload_h5120(), "rc_h5120_small", lengths=[200, 100, 50, 30, 77],
+                       pad_rows=150)
+    data = pu.make_data(wl)
+    ref = pu.oracle_reference(wl)
+    ref = {k: v for k, v in ref.items() if k in ("dx", "dweight", "y")}
+    cells = pu.standard_cells(wl, 64)
+    print(f"[recompute] harness: {len(cells)} cells", flush=True)
+    rep = harness.assert_gradient_batch_invariant("rms_norm_recompute", cells,
+                                                  contract.load_contract(), data=data,
+                                                  reference=ref, raise_on_red=False)
+    if not rep.strict:
+        print(rep.to_json()[:3000], flush=True)
+    assert rep.strict, rep.first_failure
