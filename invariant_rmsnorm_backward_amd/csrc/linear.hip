@@ -294,7 +294,9 @@ struct Engine {
   // acc += the product over the K stages [k_begin, k_begin + nst BK) in
   // ascending order.  Every stage issues its loads (stages past the end read
   // the zero chunk into a buffer no later stage reads), so the wait counts
-  // are constants.
+  // are constants.  They count the engine's own loads only: the loop issues
+  // no other vector-memory load, and the row-map reads of Operand::init feed
+  // the first load addresses, so they are complete before any stage is issued.
   __device__ static __forceinline__ void run(uint32_t sm, AccT& acc, const OA& oa, const OB& ob,
                                              int64_t k_begin, int nst) {
     const int t = threadIdx.x;
