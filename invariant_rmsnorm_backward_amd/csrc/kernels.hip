@@ -729,37 +729,36 @@ __global__ __launch_bounds__(256) void rebuild_kernel(const float* __restrict__ 
 
 // One level of the cross-block tree: out[g] = perfect pairwise tree over the
 // 512 leaves in[g*512 .. g*512+512), +0.0 past n_in.  A workgroup of 8
-// wavefronts covers 16 columns: in wavefront w, the lanes of quarter q
-// (lane / 16) reduce the aligned 16-leaf subtree 4w + q of column lane % 16
-// in registers; the quarters meet as (q0 + q1) + (q2 + q3) -- the 64-leaf
-// subtree w -- and the 8 subtree roots meet in LDS in the same pairwise
-// shape, so the result is the 512-leaf perfect tree.
+// wavefronts covers 32 columns: in wavefront w, the lanes of half h
+// (lane / 32) reduce the aligned 32-leaf subtree 2w + h of column lane % 32 in
+// registers (each load: 32 lanes x 4 bytes, one 128-byte line); the halves
+// meet as h0 + h1 -- the 64-leaf subtree w -- and the 8 subtree roots meet in
+// LDS in the same pairwise shape, so the result is the 512-leaf perfect tree.
 constexpr int kTreeLeaves = 512;
-constexpr int kTreeCols = 16;     // columns per workgroup
+constexpr int kTreeCols = 32;     // columns per workgroup
 __global__ __launch_bounds__(512) void tree_kernel(const float* __restrict__ in, int64_t n_in,
                                                    float* __restrict__ out, int H) {
   __shared__ float root_s[8][kTreeCols];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int q = lane >> 4;
-  const int j = blockIdx.y * kTreeCols + (lane & 15);
+  const int h = lane >> 5;
+  const int j = blockIdx.y * kTreeCols + (lane & 31);
   const int64_t g = blockIdx.x;
-  float v[16];
+  float v[32];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t idx = g * kTreeLeaves + wv * 64 + q * 16 + i;
+  for (int i = 0; i < 32; ++i) {
+    const int64_t idx = g * kTreeLeaves + wv * 64 + h * 32 + i;
     v[i] = (idx < n_in && j < H) ? in[idx * H + j] : 0.0f;
   }
 #pragma unroll
-  for (int st = 1; st < 16; st *= 2)
+  for (int st = 1; st < 32; st *= 2)
 #pragma unroll
-    for (int i = 0; i < 16; i += 2 * st) v[i] = v[i] + v[i + st];
-  // quarter 0 ends with (q0 + q1) + (q2 + q3); the other quarters' sums are unused
-  float r = v[0] + __shfl_xor(v[0], 16, 64);
-  r = r + __shfl_xor(r, 32, 64);
-  if (q == 0) root_s[wv][lane] = r;
+    for (int i = 0; i < 32; i += 2 * st) v[i] = v[i] + v[i + st];
+  // half 0 ends with h0 + h1; half 1's sum is unused
+  const float r = v[0] + __shfl_xor(v[0], 32, 64);
+  if (h == 0) root_s[wv][lane] = r;
   __syncthreads();
-  if (wv == 0 && q == 0 && j < H) {
+  if (wv == 0 && h == 0 && j < H) {
     const float r01 = root_s[0][lane] + root_s[1][lane], r23 = root_s[2][lane] + root_s[3][lane];
     const float r45 = root_s[4][lane] + root_s[5][lane], r67 = root_s[6][lane] + root_s[7][lane];
     out[g * H + j] = (r01 + r23) + (r45 + r67);
