@@ -194,6 +194,21 @@ const char* rmsnorm_backend_info(void);
  * backward calls enqueued afterwards.  Always returns RMSNORM_OK. */
 int rmsnorm_set_split_threshold(int64_t blocks, int64_t* previous);
 
+/* Workgroup count of the fused backward (a tuning and test knob; no output
+ * bit depends on it).  For rows of 2048, 3072 and 4096 columns the fused
+ * backward launches at most as many block-owning workgroups as the GPU
+ * holds at once (kernel occupancy x compute units); workgroup g takes the
+ * canonical blocks g, g + groups, g + 2*groups, ... and loads the first row
+ * of its next block while it folds the current block's partial.  Other
+ * widths run one workgroup per block and ignore the cap.  `groups` > 0 caps
+ * the count (1 makes one workgroup walk every block); 0 or a negative value
+ * restores the default.  Each block's arithmetic is the same whichever
+ * workgroup runs it, so dx and dweight are bitwise the same for every cap.
+ * If `previous` is non-NULL it receives the cap in force before the call
+ * (0 = default).  Process-wide; takes effect for backward calls enqueued
+ * afterwards.  Always returns RMSNORM_OK. */
+int rmsnorm_set_workgroup_cap(int64_t groups, int64_t* previous);
+
 #ifdef __cplusplus
 }
 #endif

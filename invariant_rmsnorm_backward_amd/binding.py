@@ -26,8 +26,8 @@ EXPORTED = ("rmsnorm_max_hidden", "rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_c
             "rmsnorm_dw_finalize", "rmsnorm_layout_create", "rmsnorm_layout_destroy",
             "rmsnorm_layout_check", "rmsnorm_dw_acc_create", "rmsnorm_dw_acc_reset",
             "rmsnorm_dw_acc_destroy", "rmsnorm_last_error", "rmsnorm_backend_info",
-            "rmsnorm_set_split_threshold", "rmsnorm_fwd_packed", "rmsnorm_bwd_dx_packed",
-            "rmsnorm_bwd_dx_recompute",
+            "rmsnorm_set_split_threshold", "rmsnorm_set_workgroup_cap", "rmsnorm_fwd_packed",
+            "rmsnorm_bwd_dx_packed", "rmsnorm_bwd_dx_recompute",
             "det_gemm_fwd", "det_gemm_bwd_dx", "det_gemm_dw_acc_create", "det_gemm_dw_contrib",
             "det_gemm_dw_finalize", "det_gemm_dw_acc_reset", "det_gemm_dw_acc_destroy",
             "det_embedding_fwd", "det_embedding_dw_acc_create", "det_embedding_dw_acc_set_ids",
@@ -77,6 +77,7 @@ def load() -> ctypes.CDLL:
         "rmsnorm_last_error": ([], ctypes.c_char_p),
         "rmsnorm_backend_info": ([], ctypes.c_char_p),
         "rmsnorm_set_split_threshold": ([I64, ctypes.POINTER(ctypes.c_int64)], I32),
+        "rmsnorm_set_workgroup_cap": ([I64, ctypes.POINTER(ctypes.c_int64)], I32),
         "rmsnorm_fwd_packed": ([P, P, P, P, I64, I64, I64, I64, ctypes.c_float, P, P], I32),
         "rmsnorm_bwd_dx_packed": ([P, P, P, P, P, I64, I64, I64, I64, P, P, P], I32),
         "det_gemm_fwd": ([P, P, P, I64, I64, I64, P, P], I32),
@@ -206,6 +207,16 @@ def rmsnorm_set_split_threshold(blocks: int) -> int:
     prev = ctypes.c_int64(0)
     _check(load().rmsnorm_set_split_threshold(int(blocks), ctypes.byref(prev)),
            "rmsnorm_set_split_threshold")
+    return int(prev.value)
+
+
+def rmsnorm_set_workgroup_cap(groups: int) -> int:
+    """Caps the block-owning workgroups of the fused backward (0 or negative
+    restores the default, the number the GPU holds at once); returns the
+    previous cap (0 = default)."""
+    prev = ctypes.c_int64(0)
+    _check(load().rmsnorm_set_workgroup_cap(int(groups), ctypes.byref(prev)),
+           "rmsnorm_set_workgroup_cap")
     return int(prev.value)
 
 

@@ -65,7 +65,8 @@ const char* rmsnorm_backend_info(void) {
   return "hip gfx950; cdo=v1 R=64 S=4, "
          "contribution fl32(fl32(dy*x)*rstd), streams fold ascending from +0.0, "
          "stream tree pairwise, block tree pairwise with +0.0 padding; no atomics; "
-         "fwd=wave_per_row|lanes_per_row bwd=fused dx+dW, one workgroup per 64-row block "
+         "fwd=wave_per_row|lanes_per_row bwd=fused dx+dW, 64-row blocks owned by resident "
+         "workgroups (next block's first row prefetched across the block tree) "
          "(calls with few blocks: row-parallel dx + column-split dW fold), nt loads/stores; "
          "max_hidden=10240";
 }
@@ -73,6 +74,12 @@ const char* rmsnorm_backend_info(void) {
 int rmsnorm_set_split_threshold(int64_t blocks, int64_t* previous) {
   if (previous != nullptr) *previous = rbi::split_items();
   rbi::set_split_items(blocks);
+  return RMSNORM_OK;
+}
+
+int rmsnorm_set_workgroup_cap(int64_t groups, int64_t* previous) {
+  if (previous != nullptr) *previous = rbi::wide_group_cap();
+  rbi::set_wide_group_cap(groups);
   return RMSNORM_OK;
 }
 

@@ -20,6 +20,13 @@ constexpr int64_t kDefaultSplitItems = 96;   // measured crossover: 64 vs 128 bl
 void set_split_items(int64_t n);   // n < 0 restores the default
 int64_t split_items();
 
+// Cap on the workgroups of the looping fused backward (hidden 2048, 3072,
+// 4096; 0: what the chip holds at once, occupancy x compute units).  A
+// tuning and test knob: the arithmetic of every item is the same whichever
+// workgroup runs it.
+void set_wide_group_cap(int64_t n);   // n <= 0 restores the default
+int64_t wide_group_cap();
+
 // Physical->logical plan as the kernels see it (device pointers).
 struct PlanDev {
   const int32_t* item_info = nullptr;  // nullptr: identity map, item = block
@@ -65,6 +72,9 @@ struct BwdArgs {
   PlanDev plan;
   RowPacking pack{};
   float eps = 0.0f;    // used only when rstd is rebuilt
+  // Fused wide backward: workgroups that loop over the work items (set by
+  // the launcher; the padding-row workgroups come after them).
+  int32_t item_groups = 0;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

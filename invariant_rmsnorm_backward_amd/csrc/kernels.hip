@@ -358,25 +358,92 @@ struct WideBlock {
   }
 
   __device__ __forceinline__ void run_pipelined() {
-    static_assert(Sh::SLOTS % 2 == 0, "slots per stream must be even");
-    uint4 xa[V], da[V], xb[V], db[V];
+    uint4 xa[V], da[V];
     int pa = row_of(0);
     load(pa, xa, da);
     settle_slots();
+    run_from(xa, da, pa, -1, false);
+  }
+
+  // The pipelined slot loop with slot 0's row already issued into (xa, da).
+  // When `more`, the last step issues the first row of the workgroup's next
+  // block (lane 0 of `next_slots`, read only there) into (xa, da), so that
+  // row is in flight across this block's stream tree; otherwise it issues a
+  // dummy load of row 0 (never used) to keep the wait counts exact.
+  __device__ __forceinline__ void run_from(uint4 (&xa)[V], uint4 (&da)[V], int pa, int next_slots,
+                                           bool more) {
+    static_assert(Sh::SLOTS % 2 == 0, "slots per stream must be even");
+    uint4 xb[V], db[V];
+#pragma unroll
     for (int i = 0; i < Sh::SLOTS; i += 2) {
       const int pb = row_of(i + 1);
       load(pb, xb, db);
       process(i, pa, xa, da, rstd_of(i));
-      pa = (i + 2 < Sh::SLOTS) ? row_of(i + 2) : -1;
+      if (i + 2 < Sh::SLOTS) pa = row_of(i + 2);
+      else pa = more ? __builtin_amdgcn_readlane(next_slots, 0) : -1;
       load(pa, xa, da);
       process(i + 1, pb, xb, db, rstd_of(i + 1));
     }
   }
 };
 
+// The in-block stream tree, 1024 columns at a time: every stream stores its
+// sums for the tile, then each thread reduces its columns into P[blk].
+// LOOP: the workgroup folds several blocks, so tile_s may still be read for
+// the previous block when the first tile is stored (a barrier comes first).
+template <int V, int TW, bool FULL, bool LOOP>
+__device__ __forceinline__ void block_partial(const BwdArgs& a, int blk, int H, int tid, int stream,
+                                              int half, int lane, const float (&acc)[V * 8],
+                                              float* tile_s) {
+  using Sh = WideShape<V, TW, FULL>;
+  float* Pb = a.P + (int64_t)blk * H;
+#pragma unroll
+  for (int t = 0; t < Sh::NTILE; ++t) {
+    if (LOOP || t > 0) __syncthreads();   // tile_s is free again
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const int K = half * V + k;   // 512-column chunk index within the row
+      if ((K >> 1) == t) {
+        float* dst = &tile_s[stream * 1024 + ((K & 1) * 64 + lane) * 8];
+        store_f4(dst, acc[k * 8 + 0], acc[k * 8 + 1], acc[k * 8 + 2], acc[k * 8 + 3]);
+        store_f4(dst + 4, acc[k * 8 + 4], acc[k * 8 + 5], acc[k * 8 + 6], acc[k * 8 + 7]);
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < 1024; c += Sh::THREADS) {
+      const int col = t * 1024 + c;
+      if (col < H)
+        Pb[col] = stream_tree4(tile_s[c], tile_s[1024 + c], tile_s[2048 + c], tile_s[3072 + c]);
+    }
+  }
+}
+
+// Whether the fused backward loops over several work items per workgroup:
+// the pipelined two-wavefront kernels up to 4 chunks per lane (hidden 2048,
+// 3072, 4096).  Measured at hidden 4096 the loop saves about 1% of the
+// backward; at 5120 the loop's extra registers cost more than the block
+// hand-over it hides, and the one-block kernel is kept there and above.
+template <int V, int TW, bool FULL, bool RC>
+constexpr bool wide_persistent() {
+  return FULL && TW == 2 && V <= 4;
+}
+
+// Workgroups 0 .. item_groups-1 each take work items g, g + item_groups, ...
+// (for the looping kernels item_groups is at most what the chip holds at
+// once, so every workgroup is resident and they all end after the same
+// number of items; otherwise it is the item count, one item each); the
+// workgroups after them zero padding rows.  Which workgroup takes an item
+// changes nothing in its arithmetic.  In the looping kernels the first row
+// of a workgroup's next item is loaded during the last step of the current
+// one, so it is in flight across the block's stream tree.
 template <int V, int TW, bool FULL, bool PLAN, bool DX, bool DW, bool RC>
 __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
   using Sh = WideShape<V, TW, FULL>;
+  using BlkC = WideBlock<V, TW, FULL, PLAN, DX, DW, true, RC>;    // complete block: fold
+  using BlkS = WideBlock<V, TW, FULL, PLAN, DX, DW, false, RC>;   // partial block: spill
+  constexpr bool PIPE = BlkC::PIPE;
+  constexpr bool LOOP = wide_persistent<V, TW, FULL, RC>();
+  static_assert(!LOOP || PIPE, "the looping kernels are the pipelined ones");
   __shared__ float w_s[DX ? Sh::COLS : 1];
   __shared__ float tile_s[DW ? kStreams * 1024 : 1];
   __shared__ float dot_s[(DX && TW > 1) ? 2 * 16 : 1];
@@ -389,12 +456,13 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
   const int half = wv % TW;
   const int H = FULL ? Sh::COLS : a.hidden;
   const int nchunk = H >> 3;
-  const int item = blockIdx.x;
+  const int n_items = a.plan.n_items;
+  const int groups = a.item_groups;
 
-  if (item >= a.plan.n_items) {
+  if ((int)blockIdx.x >= groups) {
     // padding rows: dx = 0, nothing read (one row per wavefront)
     if (DX) {
-      const int idx = (item - a.plan.n_items) * Sh::WAVES + wv;
+      const int idx = ((int)blockIdx.x - groups) * Sh::WAVES + wv;
       if (idx < a.plan.n_pad) {
         uint16_t* d = a.dx + (int64_t)a.plan.pad_rows[idx] * H;
         for (int q = lane; q < nchunk; q += 64) store16_stream(d + q * 8, make_uint4(0, 0, 0, 0));
@@ -402,57 +470,78 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
     }
     return;
   }
+  int item = blockIdx.x;
+  if (item >= n_items) return;
 
   if (DX) stage_w<Sh>(a, w_s, tid, nchunk);
 
-  int blk;
-  bool complete;
-  if (PLAN) {
-    const int info = a.plan.item_info[item];
-    complete = info >= 0;
-    blk = complete ? info : ~info;
-  } else {
-    blk = item;
-    complete = true;
-  }
+  // item -> (canonical block, does the call hold all of its present rows)
+  auto info_of = [&](int it, int& blk, bool& complete) {
+    if (PLAN) {
+      const int info = a.plan.item_info[it];
+      complete = info >= 0;
+      blk = complete ? info : ~info;
+    } else {
+      blk = it;
+      complete = true;
+    }
+  };
 
   float acc[DW ? V * 8 : 1];
-#pragma unroll
-  for (int i = 0; i < (DW ? V * 8 : 1); ++i) acc[i] = 0.0f;
-
   const int base = half * V * 512 + lane * 8;      // this lane's first column
-  if (!DW || complete) {
-    WideBlock<V, TW, FULL, PLAN, DX, DW, true, RC>{a, item, blk, stream, half, lane, wv, H, nchunk,
-                                                   base, w_s, dot_s, acc, ss_s}.run();
-  } else {
-    WideBlock<V, TW, FULL, PLAN, DX, DW, false, RC>{a, item, blk, stream, half, lane, wv, H, nchunk,
-                                                    base, w_s, dot_s, acc, ss_s}.run();
+  int blk;
+  bool complete;
+  info_of(item, blk, complete);
+  if constexpr (!LOOP) {
+    // one item per workgroup
+#pragma unroll
+    for (int i = 0; i < (DW ? V * 8 : 1); ++i) acc[i] = 0.0f;
+    if (!DW || complete) {
+      BlkC{a, item, blk, stream, half, lane, wv, H, nchunk, base, w_s, dot_s, acc, ss_s}.run();
+      if constexpr (DW) block_partial<V, TW, FULL, LOOP>(a, blk, H, tid, stream, half, lane, acc, tile_s);
+    } else {
+      BlkS{a, item, blk, stream, half, lane, wv, H, nchunk, base, w_s, dot_s, acc, ss_s}.run();
+    }
     return;
   }
-
-  if (DW) {
-    // In-block stream tree, 1024 columns at a time: every stream stores its
-    // sums for the tile, then each thread reduces its columns.
-    float* Pb = a.P + (int64_t)blk * H;
-#pragma unroll
-    for (int t = 0; t < Sh::NTILE; ++t) {
-      if (t > 0) __syncthreads();
-#pragma unroll
-      for (int k = 0; k < V; ++k) {
-        const int K = half * V + k;   // 512-column chunk index within the row
-        if ((K >> 1) == t) {
-          float* dst = &tile_s[stream * 1024 + ((K & 1) * 64 + lane) * 8];
-          store_f4(dst, acc[k * 8 + 0], acc[k * 8 + 1], acc[k * 8 + 2], acc[k * 8 + 3]);
-          store_f4(dst + 4, acc[k * 8 + 4], acc[k * 8 + 5], acc[k * 8 + 6], acc[k * 8 + 7]);
-        }
-      }
-      __syncthreads();
-      for (int c = tid; c < 1024; c += Sh::THREADS) {
-        const int col = t * 1024 + c;
-        if (col < H)
-          Pb[col] = stream_tree4(tile_s[c], tile_s[1024 + c], tile_s[2048 + c], tile_s[3072 + c]);
-      }
+  BlkC cur{a, item, blk, stream, half, lane, wv, H, nchunk, base, w_s, dot_s, acc, ss_s};
+  cur.load_slots();
+  uint4 xa[V], da[V];
+  int pa = cur.row_of(0);
+  cur.load(pa, xa, da);
+  cur.settle_slots();
+  while (true) {
+    const int nxt = item + groups;
+    const bool more = nxt < n_items;
+    int nblk = 0;
+    bool ncomplete = true;
+    BlkC nx{a, nxt, 0, stream, half, lane, wv, H, nchunk, base, w_s, dot_s, acc, ss_s};
+    if (more) {
+      info_of(nxt, nblk, ncomplete);
+      nx.blk = nblk;
+      nx.load_slots();
     }
+#pragma unroll
+    for (int i = 0; i < (DW ? V * 8 : 1); ++i) acc[i] = 0.0f;
+    if (!DW || complete) {
+      cur.run_from(xa, da, pa, nx.slot_p, more);
+      if constexpr (DW) block_partial<V, TW, FULL, LOOP>(a, blk, H, tid, stream, half, lane, acc, tile_s);
+    } else {
+      BlkS sp{a, item, blk, stream, half, lane, wv, H, nchunk, base, w_s, dot_s, acc, ss_s};
+      sp.slot_p = cur.slot_p;
+      sp.slot_r = cur.slot_r;
+      sp.run_from(xa, da, pa, nx.slot_p, more);
+    }
+    if (!more) break;
+    item = nxt;
+    blk = nblk;
+    complete = ncomplete;
+    cur.item = nxt;
+    cur.blk = nblk;
+    cur.slot_p = nx.slot_p;
+    cur.slot_r = nx.slot_r;
+    pa = cur.row_of(0);   // its loads were issued in the last step
+    cur.settle_slots();
   }
 }
 
@@ -865,15 +954,60 @@ int64_t split_items() {
   std::lock_guard<std::mutex> lk(g_split_mu);
   return g_split_items;
 }
+static int64_t g_group_cap = 0;
+void set_wide_group_cap(int64_t n) {
+  std::lock_guard<std::mutex> lk(g_split_mu);
+  g_group_cap = n < 0 ? 0 : n;
+}
+int64_t wide_group_cap() {
+  std::lock_guard<std::mutex> lk(g_split_mu);
+  return g_group_cap;
+}
+
+// Workgroups of the fused backward: one per work item, capped at the number
+// the chip holds at once (occupancy x compute units), so with more items
+// every workgroup stays resident and loops over its share.
+static int compute_units() {
+  static std::mutex mu;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int V, int TW, bool FULL, bool PLAN, bool DX, bool DW, bool RC>
+static void bwd_wide_launch(BwdArgs a, int pad_groups, hipStream_t st) {
+  using Sh = WideShape<V, TW, FULL>;
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(&bwd_wide_kernel<V, TW, FULL, PLAN, DX, DW, RC>),
+            Sh::THREADS, 0) != hipSuccess || n <= 0)
+      n = 1;
+    return n;
+  }();
+  const int64_t knob = wide_group_cap();
+  const int64_t cap = knob > 0 ? knob : (int64_t)per_cu * compute_units();
+  a.item_groups = (int32_t)(wide_persistent<V, TW, FULL, RC>() && a.plan.n_items > cap ? cap
+                                                                                  : a.plan.n_items);
+  const dim3 grid((unsigned)(a.item_groups + pad_groups)), block(Sh::THREADS);
+  bwd_wide_kernel<V, TW, FULL, PLAN, DX, DW, RC><<<grid, block, 0, st>>>(a);
+}
 
 template <int V, int TW, bool FULL, bool PLAN>
 static void bwd_wide_go3(const BwdArgs& a, bool dx, bool dw, bool rc, hipStream_t st) {
   using Sh = WideShape<V, TW, FULL>;
   if (rc) {   // rstd rebuilt in the fused kernel (the two-pass path reads rstd)
     const int pad_groups = (a.plan.n_pad + Sh::WAVES - 1) / Sh::WAVES;
-    const dim3 grid((unsigned)(a.plan.n_items + pad_groups)), block(Sh::THREADS);
-    if (dw) bwd_wide_kernel<V, TW, FULL, PLAN, true, true, true><<<grid, block, 0, st>>>(a);
-    else bwd_wide_kernel<V, TW, FULL, PLAN, true, false, true><<<grid, block, 0, st>>>(a);
+    if (dw) bwd_wide_launch<V, TW, FULL, PLAN, true, true, true>(a, pad_groups, st);
+    else bwd_wide_launch<V, TW, FULL, PLAN, true, false, true>(a, pad_groups, st);
     return;
   }
   if (a.plan.n_items < split_items()) {
@@ -889,10 +1023,9 @@ static void bwd_wide_go3(const BwdArgs& a, bool dx, bool dw, bool rc, hipStream_
     return;
   }
   const int pad_groups = dx ? (a.plan.n_pad + Sh::WAVES - 1) / Sh::WAVES : 0;
-  const dim3 grid((unsigned)(a.plan.n_items + pad_groups)), block(Sh::THREADS);
-  if (dx && dw) bwd_wide_kernel<V, TW, FULL, PLAN, true, true, false><<<grid, block, 0, st>>>(a);
-  else if (dx) bwd_wide_kernel<V, TW, FULL, PLAN, true, false, false><<<grid, block, 0, st>>>(a);
-  else bwd_wide_kernel<V, TW, FULL, PLAN, false, true, false><<<grid, block, 0, st>>>(a);
+  if (dx && dw) bwd_wide_launch<V, TW, FULL, PLAN, true, true, false>(a, pad_groups, st);
+  else if (dx) bwd_wide_launch<V, TW, FULL, PLAN, true, false, false>(a, pad_groups, st);
+  else bwd_wide_launch<V, TW, FULL, PLAN, false, true, false>(a, pad_groups, st);
 }
 template <int V, int TW, bool FULL>
 static void bwd_wide_go2(const BwdArgs& a, bool dx, bool dw, bool rc, hipStream_t st) {

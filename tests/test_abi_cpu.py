@@ -139,6 +139,17 @@ def test_split_threshold_knob():
         binding.rmsnorm_set_split_threshold(prev)
 
 
+def test_workgroup_cap_knob():
+    """The fused backward's workgroup cap: set, read back, restore."""
+    prev = binding.rmsnorm_set_workgroup_cap(3)
+    try:
+        assert binding.rmsnorm_set_workgroup_cap(1) == 3
+        assert binding.rmsnorm_set_workgroup_cap(-5) == 1       # negative: back to the default
+        assert binding.rmsnorm_set_workgroup_cap(prev) == 0
+    finally:
+        binding.rmsnorm_set_workgroup_cap(prev)
+
+
 def test_packed_entry_points_check_their_arguments(lib):
     A = 1 << 12
     cases = [

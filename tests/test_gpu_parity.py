@@ -61,6 +61,7 @@ WIDE_CASES = {
     "h512": (inputs.workload_h4096, 512, [70, 45, 129], 50),
     "h1000_masked": (inputs.workload_h4096, 1000, [70, 45], 33),
     "h2048": (inputs.workload_h4096, 2048, [64, 64, 65], 64),
+    "h3072": (inputs.workload_h4096, 3072, [150, 97, 64], 48),
     "h6144_two_waves": (inputs.workload_h8192, 6144, [99, 30], 40),
     "h9000_two_waves_masked": (inputs.workload_h8192, 9000, [77, 60], 64),
     "h40_masked": (inputs.workload_h8, 40, [70, 45, 3], 17),
@@ -231,6 +232,57 @@ def test_two_pass_backward_is_bitwise_the_fused_one(case):
     assert torch.equal(got["fused"][0], got["two_pass"][0])
     assert torch.equal(got["fused"][1], got["two_pass"][1])
     print(f"[paths] {case}: fused == two-pass bitwise over {len(cells)} cells", flush=True)
+
+
+# Caps on the block-owning workgroups of the fused backward: with a cap the
+# workgroups each walk many canonical blocks in turn (prefetching the next
+# block's first row across the current block's tree).
+GROUP_CAPS = (1, 3, 7)
+
+
+@pytest.mark.parametrize("case", ["h4096", "h2048", "h3072", "h5120", "h512", "h1000_masked"])
+def test_workgroup_cap_changes_no_bit(case):
+    """Every cell (complete blocks, spilled partial blocks, padding rows,
+    permutations) gives the same dx, dweight, y and rstd bits whatever the
+    number of workgroups the fused backward runs with, and so do dx alone,
+    the dweight contributions alone and the rstd-recompute backward."""
+    base, H, lengths, chunk = WIDE_CASES[case]
+    wl = inputs.scaled(base(), f"{case}_caps", hidden=H, lengths=lengths, pad_rows=0)
+    data = pu.make_data(wl)
+    cells = pu.standard_cells(wl, chunk)
+    T = wl.n_logical
+    print(f"[caps] {case}: hidden {H}, {T} rows, {len(cells)} cells, caps {GROUP_CAPS}", flush=True)
+    outs, single = {}, {}
+    prev_thr = binding.rmsnorm_set_split_threshold(0)    # the fused kernel for every call
+    try:
+        for cap in (0,) + GROUP_CAPS:
+            prev = binding.rmsnorm_set_workgroup_cap(cap)
+            try:
+                ad = adapters.RmsNormAdapter()
+                outs[cap] = [ad.run_cell(c, data) for c in cells]
+                _, rstd = binding.fwd(data.x, data.w, data.eps)
+                acc = binding.DwAccumulator(T, H)
+                binding.dw_contrib(data.x, data.dy, rstd, acc)
+                dw_only = acc.finalize().view(torch.int32).cpu()
+                acc.reset()
+                dx_rc = binding.bwd_recompute(data.x, data.w, data.dy, data.eps, acc=acc)
+                dw_rc = acc.finalize().view(torch.int32).cpu()
+                acc.close()
+                dx_only = binding.bwd(data.x, data.w, data.dy, rstd)
+                single[cap] = (dx_only.view(torch.int16).cpu(), dw_only,
+                               dx_rc.view(torch.int16).cpu(), dw_rc)
+            finally:
+                binding.rmsnorm_set_workgroup_cap(prev)
+    finally:
+        binding.rmsnorm_set_split_threshold(prev_thr)
+    for cap in GROUP_CAPS:
+        for c, a, b in zip(cells, outs[0], outs[cap]):
+            for t in ("dx", "dweight", "y", "rstd"):
+                assert np.array_equal(a[t].view(np.uint8), b[t].view(np.uint8)), (case, cap, c.name, t)
+        for i, (a, b) in enumerate(zip(single[0], single[cap])):
+            assert torch.equal(a, b), (case, cap, ("dx", "dw_contrib", "dx_rc", "dw_rc")[i])
+    # the recompute backward equals the saved-rstd one
+    assert torch.equal(single[0][0], single[0][2]) and torch.equal(single[0][1], single[0][3])
 
 
 def test_run_to_run_repeatability():
