@@ -65,7 +65,7 @@ const char* rmsnorm_backend_info(void) {
   return "hip gfx950; cdo=v1 R=64 S=4, "
          "contribution fl32(fl32(dy*x)*rstd), streams fold ascending from +0.0, "
          "stream tree pairwise, block tree pairwise with +0.0 padding; no atomics; "
-         "fwd=wave_per_row|lanes_per_row bwd=fused dx+dW, 64-row blocks owned by resident "
+         "fwd=rows_per_workgroup|lanes_per_row bwd=fused dx+dW, 64-row blocks owned by resident "
          "workgroups (next block's first row prefetched across the block tree) "
          "(calls with few blocks: row-parallel dx + column-split dW fold), nt loads/stores; "
          "max_hidden=10240";

@@ -1,9 +1,10 @@
 // kernels.hip -- gfx950 kernels of batch-invariant RMSNorm.
 //
-// Forward: one wavefront per row (hidden >= 512, or any hidden that is not a
-// power of two below 512) or one group of hidden/8 lanes per row (hidden in
-// {8..256}); streaming 16-byte bf16 loads and stores, FP32 math, a DPP
-// wavefront sum of squares.
+// Forward: the backward's row shape -- one wavefront per row up to 1024
+// columns, two above -- with 2 or 4 rows per workgroup (hidden >= 512, or any
+// hidden that is not a power of two below 512), or one group of hidden/8
+// lanes per row (hidden in {8..256}); streaming 16-byte bf16 loads and
+// stores, FP32 math, DPP wavefront sums of squares.
 //
 // Backward: one workgroup per canonical block of 64 logical rows.  The
 // dweight order (CDO-v1, following "WS1 C4 (#270) closeout evidence":
@@ -38,72 +39,107 @@ __device__ __forceinline__ int64_t row_off(const RowPacking& pk, int64_t r, int 
 }
 
 // ----------------------------------------------------------------- forward
-template <int V>
-__global__ __launch_bounds__(256) void fwd_wide_kernel(FwdArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int H = a.hidden;
+// The row's sum of squares, in the order every wide kernel uses (the
+// forward here, and the backward that rebuilds rstd from x): the row's
+// 16-byte chunks are grouped 64 at a time -- chunk q = 64k + l is lane l of
+// group k -- and
+//   s_q   = fmaf chain over the chunk's 8 squares, from +0.0, in column order
+//   S_k   = wavefront sum (wave_sum) of s_{64k+l} over l (absent chunks: 0)
+//   ss    = perfect pairwise tree over S_0 .. S_{K-1}, K = ceil(hidden/512),
+//           padded with +0.0 to a power of two (pad_tree below).
+// The padding makes the tree over any longer list with +0.0 past K the same
+// value, so a kernel may hold more (empty) groups than the row has.
+template <int N>
+__device__ __forceinline__ float pad_tree(float (&v)[N]) {
+#pragma unroll
+  for (int st = 1; st < N; st *= 2)
+#pragma unroll
+    for (int k = 0; k + st < N; k += 2 * st) v[k] = v[k] + v[k + st];   // v + (+0.0) == v
+  return v[0];
+}
+__device__ __forceinline__ float chunk_squares(const uint4& v) {
+  float f[8];
+  unpack8(v, f);
+  float c = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = fmaf(f[e], f[e], c);
+  return c;
+}
+
+// Row shape of the wide forward, the backward's own: TW wavefronts per row
+// (one up to 1024 columns, else two), V chunks per lane; lane l of wavefront
+// h holds chunk groups h*V .. h*V+V-1, i.e. chunks (h*V + j)*64 + l.  A
+// 256-thread workgroup takes 4/TW consecutive rows, each row's wavefronts
+// swapping their group sums through LDS.  Many short workgroups that read
+// their rows once and write them once keep the access stream in address
+// order across the chip (measured on hidden 4096, 5120 and 8192: 74-77% of
+// 8 TB/s, against 63-72% for one wavefront per row over a capped grid and
+// for one chunk per thread at 5120 and 8192).
+// FULL: hidden == 512*V*TW (no lane masks).  PAD: the call has padding rows.
+template <int V, int TW, bool FULL, bool PAD>
+__global__ __launch_bounds__(256) void fwd_row_kernel(FwdArgs a) {
+  constexpr int RPW = 4 / TW;          // rows per workgroup
+  constexpr int G = V * TW;            // chunk groups held (at least the row's)
+  __shared__ float s_s[TW > 1 ? RPW * G : 1];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int rg = wv / TW;              // the workgroup's row
+  const int half = wv % TW;            // wavefront within the row
+  const int H = FULL ? 512 * G : a.hidden;
   const int nchunk = H >> 3;
-  uint4 wv[V];
+  const int64_t row = (int64_t)blockIdx.x * RPW + rg;
+  const bool live = row < a.rows;
+  const bool real = live && (!PAD || a.row_logical[row] >= 0);   // uniform per wavefront
+  const int base = (half * V * 64 + lane) * 8;                     // first column of chunk 0
+  auto in_row = [&](int j) { return FULL || (half * V + j) * 64 + lane < nchunk; };
+  uint4 wc[V], xv[V];
 #pragma unroll
-  for (int k = 0; k < V; ++k) {
-    const int q = k * 64 + lane;
-    wv[k] = (k < V - 1 || q < nchunk) ? load16(a.w + q * 8) : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < V; ++j) wc[j] = in_row(j) ? load16(a.w + base + j * 512) : make_uint4(0, 0, 0, 0);
+  if (real) {
+    const uint16_t* xr = a.x + row * H + base;
+#pragma unroll
+    for (int j = 0; j < V; ++j) xv[j] = in_row(j) ? load16_stream(xr + j * 512) : make_uint4(0, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; ++j) xv[j] = make_uint4(0, 0, 0, 0);
   }
-  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < a.rows; row += (int64_t)gridDim.x * 4) {
-    uint16_t* yr = a.y + row * H;
-    if (a.row_logical != nullptr && a.row_logical[row] < 0) {
+  float S[V];
 #pragma unroll
-      for (int k = 0; k < V; ++k) {
-        const int q = k * 64 + lane;
-        if (k < V - 1 || q < nchunk) store16_stream(yr + q * 8, make_uint4(0, 0, 0, 0));
-      }
-      if (lane == 0 && a.rstd != nullptr) a.rstd[row] = 0.0f;
-      continue;
+  for (int j = 0; j < V; ++j) S[j] = wave_sum(chunk_squares(xv[j]));
+  float ss;
+  if constexpr (TW == 1) {
+    ss = pad_tree(S);
+  } else {
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) s_s[rg * G + half * V + j] = S[j];
     }
-    const uint16_t* xr = a.x + row * H;
-    uint4 xv[V];
+    __syncthreads();
+    float g[G];
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-      const int q = k * 64 + lane;
-      xv[k] = (k < V - 1 || q < nchunk) ? load16_stream(xr + q * 8) : make_uint4(0, 0, 0, 0);
-    }
-    // The sum of squares in the order the backward can rebuild without the
-    // saved rstd: above 1024 columns the backward splits a row over two
-    // wavefronts (chunks k < VB and k >= VB of every lane), so each part has
-    // its own chain and wavefront sum, and the two sums are added.
-    const int VB = (H + 1023) >> 10;
-    float ss0 = 0.0f, ss1 = 0.0f;
+    for (int k = 0; k < G; ++k) g[k] = s_s[rg * G + k];
+    ss = pad_tree(g);
+  }
+  if (!live) return;
+  const float r = real ? rsqrtf(ss / (float)H + a.eps) : 0.0f;
+  uint16_t* yr = a.y + row * H + base;
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-      float f[8];
-      unpack8(xv[k], f);
-      if (H > 1024 && k >= VB) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss1 = fmaf(f[e], f[e], ss1);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss0 = fmaf(f[e], f[e], ss0);
-      }
-    }
-    const float ss = H > 1024 ? wave_sum(ss0) + wave_sum(ss1) : wave_sum(ss0);
-    const float r = rsqrtf(ss / (float)H + a.eps);
-#pragma unroll
-    for (int k = 0; k < V; ++k) launder(xv[k]);
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-      const int q = k * 64 + lane;
-      if (k < V - 1 || q < nchunk) {
+  for (int j = 0; j < V; ++j) {
+    if (in_row(j)) {
+      uint4 out = make_uint4(0, 0, 0, 0);   // padding rows: +0.0
+      if (real) {
         float f[8], g[8], o[8];
-        unpack8(xv[k], f);
-        unpack8(wv[k], g);
+        unpack8(xv[j], f);
+        unpack8(wc[j], g);
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = (f[e] * r) * g[e];
-        store16_stream(yr + q * 8, pack8(o));
+        out = pack8(o);
       }
+      store16_stream(yr + j * 512, out);
     }
-    if (lane == 0 && a.rstd != nullptr) a.rstd[row] = r;
   }
+  if (half == 0 && lane == 0 && a.rstd != nullptr) a.rstd[row] = r;
 }
 
 // hidden = 8L with L lanes per row (L in 1..32, a power of two).
@@ -186,9 +222,11 @@ __device__ __forceinline__ void stage_w(const BwdArgs& a, float* w_s, int tid, i
 // in registers; otherwise they are written to the spill rows.  When two row
 // buffers fit in registers the loop is software-pipelined: the next slot's
 // row is loaded before the current row's reduction and dx pass.
-// RC: rstd is not read but rebuilt from the row, in the forward's order
-// (each wavefront's chain and wavefront sum; the TW sums added in order), so
-// its bits are the saved rstd's; the contributions then wait for it.
+// RC: rstd is not read but rebuilt from the row in the forward's order (the
+// chunk chains, one wavefront sum per 64-chunk group, the padded pairwise
+// tree over the groups; the TW wavefronts of a row swap their group sums
+// through LDS), so its bits are the saved rstd's; the contributions then
+// wait for it.
 template <int V, int TW, bool FULL, bool PLAN, bool DX, bool DW, bool COMPLETE, bool RC = false>
 struct WideBlock {
   using Sh = WideShape<V, TW, FULL>;
@@ -242,6 +280,11 @@ struct WideBlock {
   __device__ __forceinline__ void process(int i, int p, uint4 (&xv)[V], uint4 (&dv)[V], float r) {
     const int s = stream + Sh::S * i;
     float dot = 0.0f, ss = 0.0f;
+    // RC: the chunk chains of the forward's sum of squares; chunk k of this
+    // lane is lane `lane` of chunk group half*V + k
+    float sq[RC ? V : 1];
+#pragma unroll
+    for (int k = 0; k < (RC ? V : 1); ++k) sq[k] = 0.0f;
     if (p >= 0) {
       float* srow = COMPLETE ? nullptr : a.S + ((int64_t)blk * kBlockRows + s) * H + base;
 #pragma unroll
@@ -254,7 +297,7 @@ struct WideBlock {
         for (int e = 0; e < 8; ++e) {
           const float pr = df[e] * xf[e];          // exact: two bf16 significands
           if (DX) dot = fmaf(pr, w_s[base + k * 512 + e], dot);
-          if (RC) ss = fmaf(xf[e], xf[e], ss);
+          if (RC) sq[RC ? k : 0] = fmaf(xf[e], xf[e], sq[RC ? k : 0]);
           c[e] = pr * r;                           // the row's contribution, rounded once
           if (!RC && DW && COMPLETE) acc[k * 8 + e] = acc[k * 8 + e] + c[e];
         }
@@ -265,17 +308,29 @@ struct WideBlock {
       }
       if (TW == 1) {
         if (DX) dot = wave_sum(dot);
-        if (RC) ss = wave_sum(ss);
+        if (RC) {
+          // this wavefront holds every chunk group of the row
+#pragma unroll
+          for (int k = 0; k < (RC ? V : 1); ++k) sq[k] = wave_sum(sq[k]);
+          ss = pad_tree(sq);
+        }
       }
     }
     if (DX || RC) {
       if (TW > 1) {
         // the row's wavefronts exchange their partial sums through LDS
         if (DX) dot = wave_sum(dot);
-        if (RC) ss = wave_sum(ss);
+        if (RC) {
+#pragma unroll
+          for (int k = 0; k < (RC ? V : 1); ++k) sq[k] = wave_sum(sq[k]);
+        }
         if (lane == 0) {
           if (DX) dot_s[(i & 1) * 16 + wv] = dot;
-          if (RC) ss_s[(i & 1) * 16 + wv] = ss;
+          if (RC) {
+#pragma unroll
+            for (int k = 0; k < (RC ? V : 1); ++k)
+              ss_s[((i & 1) * Sh::S + stream) * (TW * V) + half * V + k] = sq[k];
+          }
         }
         __syncthreads();
         if (DX) {
@@ -283,9 +338,13 @@ struct WideBlock {
           dot = TW == 2 ? d[0] + d[1] : (d[0] + d[1]) + (d[2 % TW] + d[3 % TW]);
         }
         if (RC) {
-          static_assert(!RC || TW <= 2, "the forward's order covers two wavefronts per row");
-          const float* q = &ss_s[(i & 1) * 16 + stream * TW];
-          ss = q[0] + q[1];
+          // every chunk group of the row, in group order (groups past the
+          // row's end hold +0.0, which the padded tree absorbs)
+          float g[RC ? TW * V : 1];
+#pragma unroll
+          for (int k = 0; k < (RC ? TW * V : 1); ++k)
+            g[k] = ss_s[((i & 1) * Sh::S + stream) * (TW * V) + k];
+          ss = pad_tree(g);
         }
       }
       if (RC) r = p >= 0 ? rsqrtf(ss / (float)H + a.eps) : 0.0f;
@@ -447,7 +506,7 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
   __shared__ float w_s[DX ? Sh::COLS : 1];
   __shared__ float tile_s[DW ? kStreams * 1024 : 1];
   __shared__ float dot_s[(DX && TW > 1) ? 2 * 16 : 1];
-  __shared__ float ss_s[(RC && TW > 1) ? 2 * 16 : 1];
+  __shared__ float ss_s[(RC && TW > 1) ? 2 * kStreams * TW * V : 1];
 
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
@@ -886,7 +945,9 @@ static int wide_v(int hidden) {
 }
 
 const char* fwd_variant(int hidden) {
-  return small_lanes(hidden) ? "fwd_small(lanes_per_row=hidden/8)" : "fwd_wide(wave_per_row)";
+  return small_lanes(hidden) ? "fwd_small(lanes_per_row=hidden/8)"
+         : wide_tw(hidden) == 1 ? "fwd_rows(wave_per_row, 4 rows per workgroup)"
+                                : "fwd_rows(two_waves_per_row, 2 rows per workgroup)";
 }
 const char* bwd_variant(int hidden) {
   if (small_lanes(hidden)) return "bwd_small(lds_fold, streams=4)";
@@ -896,11 +957,16 @@ const char* bwd_variant(int hidden) {
 
 static int grid_cap() { return 256 * 16; }
 
-template <int V>
-static void fwd_wide_go(const FwdArgs& a, hipStream_t st) {
-  int64_t g = (a.rows + 3) / 4;
-  if (g > grid_cap()) g = grid_cap();
-  fwd_wide_kernel<V><<<dim3((unsigned)g), dim3(256), 0, st>>>(a);
+// rows < 2^31 (checked at the C-ABI), so the grid always fits.
+template <int V, int TW>
+static void fwd_row_go(const FwdArgs& a, hipStream_t st) {
+  constexpr int RPW = 4 / TW;
+  const dim3 grid((unsigned)((a.rows + RPW - 1) / RPW)), block(256);
+  const bool full = a.hidden == 512 * V * TW, pad = a.row_logical != nullptr;
+  if (full && !pad) fwd_row_kernel<V, TW, true, false><<<grid, block, 0, st>>>(a);
+  else if (full) fwd_row_kernel<V, TW, true, true><<<grid, block, 0, st>>>(a);
+  else if (!pad) fwd_row_kernel<V, TW, false, false><<<grid, block, 0, st>>>(a);
+  else fwd_row_kernel<V, TW, false, true><<<grid, block, 0, st>>>(a);
 }
 static bool is_packed(const RowPacking& pk, int hidden) {
   return pk.heads > 1 || (pk.token_stride != 0 && pk.token_stride != hidden);
@@ -929,14 +995,22 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
     case 32: fwd_small_go<32>(a, st); return hipGetLastError();
     default: break;
   }
-  const int V = (a.hidden + 511) / 512;
-  switch (V) {
-#define RBI_FWD(v) case v: fwd_wide_go<v>(a, st); break;
-    RBI_FWD(1) RBI_FWD(2) RBI_FWD(3) RBI_FWD(4) RBI_FWD(5) RBI_FWD(6) RBI_FWD(7) RBI_FWD(8)
-    RBI_FWD(9) RBI_FWD(10) RBI_FWD(11) RBI_FWD(12) RBI_FWD(13) RBI_FWD(14) RBI_FWD(15)
-    RBI_FWD(16) RBI_FWD(17) RBI_FWD(18) RBI_FWD(19) RBI_FWD(20)
+  // the backward's row shape: wide_tw wavefronts per row, wide_v chunks per lane
+  const int V = wide_v(a.hidden);
+  if (wide_tw(a.hidden) == 1) {
+    switch (V) {
+      case 1: fwd_row_go<1, 1>(a, st); break;
+      case 2: fwd_row_go<2, 1>(a, st); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (V) {
+#define RBI_FWD(v) case v: fwd_row_go<v, 2>(a, st); break;
+      RBI_FWD(1) RBI_FWD(2) RBI_FWD(3) RBI_FWD(4) RBI_FWD(5) RBI_FWD(6) RBI_FWD(7) RBI_FWD(8)
+      RBI_FWD(9) RBI_FWD(10)
 #undef RBI_FWD
-    default: return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
