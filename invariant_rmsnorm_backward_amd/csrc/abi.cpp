@@ -284,7 +284,7 @@ int rmsnorm_layout_check(const int32_t* row_logical_host, int64_t rows, int64_t 
     stats[1] = plan.n_complete;
     stats[2] = plan.n_partial;
     stats[3] = static_cast<int64_t>(plan.pad_rows.size());
-    stats[4] = static_cast<int64_t>(plan.logical_rows.size());
+    stats[4] = plan.n_real;
   }
   return RMSNORM_OK;
 }

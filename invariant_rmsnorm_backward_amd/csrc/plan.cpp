@@ -47,7 +47,7 @@ int build_plan(const int32_t* row_logical, int64_t rows, int64_t n_logical, Plan
   P.rows = rows;
   P.n_logical = n_logical;
   P.row_logical.assign(row_logical, row_logical + rows);
-  P.logical_rows.reserve(static_cast<size_t>(n_real));
+  P.n_real = n_real;
 
   // Items in ascending block order.
   std::vector<int32_t> item_of_block(static_cast<size_t>(nb), -1);
@@ -68,7 +68,7 @@ int build_plan(const int32_t* row_logical, int64_t rows, int64_t n_logical, Plan
     }
     const int32_t item = item_of_block[l / kBlockRows];
     P.slot_phys[static_cast<size_t>(item) * kBlockRows + (l % kBlockRows)] = static_cast<int32_t>(p);
-    P.logical_rows.push_back(l);
+    if (P.item_info[static_cast<size_t>(item)] < 0) P.partial_rows.push_back(l);
   }
   return kOk;
 }
@@ -82,26 +82,46 @@ void AccHost::init(int64_t T, int64_t H) {
   n_covered = 0;
   n_spilled = 0;
   identity_call = false;
-  dirty = false;
+  rows_dirty = false;
+  blocks_dirty = false;
   finalized = false;
 }
 
 void AccHost::reset() {
-  if (dirty) {
-    std::fill(covered.begin(), covered.end(), 0);
-    std::fill(block_state.begin(), block_state.end(), kBlockNone);
-  }
+  if (rows_dirty) std::fill(covered.begin(), covered.end(), 0);
+  if (blocks_dirty) std::fill(block_state.begin(), block_state.end(), kBlockNone);
   n_covered = 0;
   n_spilled = 0;
   identity_call = false;
-  dirty = false;
+  rows_dirty = false;
+  blocks_dirty = false;
   finalized = false;
 }
 
-static int64_t first_set(const std::vector<uint8_t>& v) {
-  for (size_t i = 0; i < v.size(); ++i)
-    if (v[i]) return static_cast<int64_t>(i);
+// First registered logical row of block b (-1 if none).
+static int64_t first_registered_in(const AccHost& A, int64_t b) {
+  const int64_t lo = b * kBlockRows, hi = std::min<int64_t>(lo + kBlockRows, A.n_logical);
+  if (A.identity_call || A.block_state[static_cast<size_t>(b)] == kBlockDirect) return lo;
+  for (int64_t l = lo; l < hi; ++l)
+    if (A.covered[static_cast<size_t>(l)]) return l;
   return -1;
+}
+
+// First registered logical row of the accumulator (-1 if none).
+static int64_t first_registered(const AccHost& A) {
+  if (A.identity_call) return 0;
+  for (int64_t b = 0; b < A.nb; ++b)
+    if (A.block_state[static_cast<size_t>(b)] != kBlockNone) return first_registered_in(A, b);
+  return -1;
+}
+
+// First logical row the plan holds in item `it`.
+static int64_t first_held(const PlanHost& P, size_t it) {
+  const int32_t info = P.item_info[it];
+  const int64_t b = info >= 0 ? info : ~info;
+  for (int s = 0; s < kBlockRows; ++s)
+    if (P.slot_phys[it * kBlockRows + s] >= 0) return b * kBlockRows + s;
+  return b * kBlockRows;
 }
 
 int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err) {
@@ -109,17 +129,17 @@ int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err)
     *err = "accumulator already finalized; call rmsnorm_dw_acc_reset first";
     return kEState;
   }
+  auto dup = [&](int64_t l) {
+    *err = "logical row " + std::to_string(l) + " already contributed";
+    return kECoverage;
+  };
   if (plan == nullptr) {
     if (rows != n_logical) {
       *err = "identity layout with an accumulator needs rows (" + std::to_string(rows) +
              ") == n_logical (" + std::to_string(n_logical) + ")";
       return kELayout;
     }
-    if (n_covered > 0) {
-      const int64_t l = identity_call ? 0 : first_set(covered);
-      *err = "logical row " + std::to_string(l) + " already contributed";
-      return kECoverage;
-    }
+    if (n_covered > 0) return dup(first_registered(*this));
     identity_call = true;
     n_covered = n_logical;
     return kOk;
@@ -129,23 +149,32 @@ int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err)
            ") differs from the accumulator's (" + std::to_string(n_logical) + ")";
     return kELayout;
   }
-  for (int32_t l : plan->logical_rows) {
-    if (identity_call || covered[l]) {
-      *err = "logical row " + std::to_string(l) + " already contributed";
-      return kECoverage;
-    }
+  // Check everything before changing any state.  A block this call holds
+  // completely must have no registered row; a block it holds in part must
+  // not be held completely by an earlier call, and its rows are checked one
+  // by one.
+  for (size_t it = 0; it < plan->item_info.size(); ++it) {
+    const int32_t info = plan->item_info[it];
+    const int64_t b = info >= 0 ? info : ~info;
+    if (identity_call) return dup(first_held(*plan, it));
+    const uint8_t st = block_state[static_cast<size_t>(b)];
+    if (info >= 0 && st != kBlockNone) return dup(first_registered_in(*this, b));
+    if (info < 0 && st == kBlockDirect) return dup(first_held(*plan, it));
   }
-  if (!plan->logical_rows.empty() || !plan->item_info.empty()) dirty = true;
-  for (int32_t l : plan->logical_rows) covered[l] = 1;
-  n_covered += static_cast<int64_t>(plan->logical_rows.size());
+  for (int32_t l : plan->partial_rows)
+    if (covered[static_cast<size_t>(l)]) return dup(l);
   for (int32_t info : plan->item_info) {
     if (info >= 0) {
-      block_state[info] = kBlockDirect;
-    } else if (block_state[~info] != kBlockSpilled) {
-      block_state[~info] = kBlockSpilled;
+      block_state[static_cast<size_t>(info)] = kBlockDirect;
+    } else if (block_state[static_cast<size_t>(~info)] != kBlockSpilled) {
+      block_state[static_cast<size_t>(~info)] = kBlockSpilled;
       ++n_spilled;
     }
   }
+  for (int32_t l : plan->partial_rows) covered[static_cast<size_t>(l)] = 1;
+  if (!plan->item_info.empty()) blocks_dirty = true;
+  if (!plan->partial_rows.empty()) rows_dirty = true;
+  n_covered += plan->n_real;
   return kOk;
 }
 
@@ -153,7 +182,16 @@ int AccHost::prepare_finalize(std::vector<int32_t>* spilled, std::string* err) c
   if (n_covered != n_logical) {
     // rows are registered at most once, so fewer than n_logical means a gap
     int64_t l = 0;
-    while (l < n_logical && covered[l]) ++l;
+    while (l < n_logical) {
+      const int64_t b = l / kBlockRows;
+      if (block_state[static_cast<size_t>(b)] == kBlockDirect) {
+        l = (b + 1) * kBlockRows;
+      } else if (covered[static_cast<size_t>(l)]) {
+        ++l;
+      } else {
+        break;
+      }
+    }
     *err = "logical row " + std::to_string(l) + " has not contributed";
     return kECoverage;
   }

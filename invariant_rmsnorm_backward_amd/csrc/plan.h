@@ -41,7 +41,9 @@ struct PlanHost {
   std::vector<int32_t> item_info;    // [n_items]: block id if complete, ~block id if partial
   std::vector<int32_t> slot_phys;    // [n_items * 64]: physical row or -1
   std::vector<int32_t> pad_rows;     // physical rows mapped to -1
-  std::vector<int32_t> logical_rows; // real rows' logical ids (for coverage accounting)
+  std::vector<int32_t> partial_rows; // logical ids of the rows of partial items (the only
+                                     // rows whose coverage is tracked one by one)
+  int64_t n_real = 0;                // rows with a logical id
   int64_t n_complete = 0;
   int64_t n_partial = 0;
   int64_t n_items() const { return static_cast<int64_t>(item_info.size()); }
@@ -55,18 +57,22 @@ int build_plan(const int32_t* row_logical, int64_t rows, int64_t n_logical, Plan
 enum BlockState : uint8_t { kBlockNone = 0, kBlockDirect = 1, kBlockSpilled = 2 };
 
 // Coverage bookkeeping costs O(1) for a call with the identity map and
-// O(rows of the call) for a call with a layout; the per-row state is only
-// scanned to name the offending row when a check fails.
+// O(items + rows of partial items) for a call with a layout: a block that a
+// call holds completely is recorded once (kBlockDirect), since any other
+// call touching it would repeat a row; only the rows of blocks split across
+// calls are tracked one by one.  The per-row state is scanned only to name
+// the offending row when a check fails.
 struct AccHost {
   int64_t n_logical = 0;
   int64_t hidden = 0;
   int64_t nb = 0;
-  std::vector<uint8_t> covered;       // per logical row: contributed (0/1), layout calls only
+  std::vector<uint8_t> covered;       // per logical row of split blocks: contributed (0/1)
   std::vector<uint8_t> block_state;   // per block: BlockState, layout calls only
   int64_t n_covered = 0;              // logical rows that have contributed
   int64_t n_spilled = 0;              // blocks marked kBlockSpilled
   bool identity_call = false;         // an identity-map call covered every row
-  bool dirty = false;                 // covered / block_state were written
+  bool rows_dirty = false;            // covered was written
+  bool blocks_dirty = false;          // block_state was written
   bool finalized = false;
 
   void init(int64_t T, int64_t H);

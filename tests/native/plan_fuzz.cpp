@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <random>
 #include <string>
 #include <vector>
@@ -79,6 +80,101 @@ int main() {
         CHECK(build_plan(bad.data(), (int64_t)bad.size(), T, &P, &err) == kELayout);
       }
     }
+  }
+  // Call sequences against a per-row reference: random subsets (contiguous
+  // chunks, whole blocks, scattered rows, some repeating earlier rows) and
+  // identity calls, each permuted and padded.  A call must be accepted iff
+  // none of its rows contributed before; a refusal names a repeated row; the
+  // finalize check passes iff every row contributed, names the first missing
+  // row otherwise, and lists exactly the blocks some call held in part.
+  auto named_row = [](const std::string& e) -> int64_t {
+    const std::string key = "logical row ";
+    const size_t at = e.find(key);
+    return at == std::string::npos ? -2 : std::strtoll(e.c_str() + at + key.size(), nullptr, 10);
+  };
+  for (int iter = 0; iter < 3000; ++iter) {
+    const int64_t T = rng() % 400;
+    const int64_t nb = (T + kBlockRows - 1) / kBlockRows;
+    AccHost A;
+    A.init(T, 8);
+    std::vector<uint8_t> ref(T, 0);
+    std::vector<uint8_t> ref_split(nb, 0);
+    int64_t ref_n = 0;
+    const int ncalls = 1 + rng() % 6;
+    std::string err;
+    for (int c = 0; c < ncalls; ++c) {
+      if (rng() % 10 == 0) {
+        const int rc = A.register_call(nullptr, T, &err);
+        CHECK((rc == kOk) == (ref_n == 0));
+        if (rc != kOk) {
+          CHECK(rc == kECoverage);
+          const int64_t l = named_row(err);
+          CHECK(l >= 0 && l < T && ref[l]);
+        } else {
+          std::fill(ref.begin(), ref.end(), 1);
+          ref_n = T;
+        }
+        continue;
+      }
+      std::vector<int32_t> ids;
+      const int mode = rng() % 3;
+      if (mode == 0 && T > 0) {
+        int64_t a = rng() % (T + 1), b = rng() % (T + 1);
+        if (a > b) std::swap(a, b);
+        for (int64_t l = a; l < b; ++l) ids.push_back((int32_t)l);
+      } else if (mode == 1) {
+        for (int64_t l = 0; l < T; ++l)
+          if (ref[l] ? rng() % 16 == 0 : rng() % 2 == 0) ids.push_back((int32_t)l);
+      } else if (T > 0) {
+        const int64_t b0 = rng() % nb;
+        for (int64_t l = b0 * kBlockRows; l < std::min<int64_t>(T, (b0 + 1) * kBlockRows); ++l)
+          ids.push_back((int32_t)l);
+      }
+      std::shuffle(ids.begin(), ids.end(), rng);
+      std::vector<int32_t> rl;
+      for (int32_t l : ids) {
+        if (rng() % 7 == 0) rl.push_back(-1);
+        rl.push_back(l);
+      }
+      PlanHost P;
+      CHECK(build_plan(rl.data(), (int64_t)rl.size(), T, &P, &err) == kOk);
+      bool fresh = true;
+      for (int32_t l : ids) fresh = fresh && !ref[l];
+      const int rc = A.register_call(&P, (int64_t)rl.size(), &err);
+      CHECK((rc == kOk) == fresh);
+      if (rc != kOk) {
+        CHECK(rc == kECoverage);
+        const int64_t l = named_row(err);
+        CHECK(l >= 0 && l < T && ref[l] && std::find(ids.begin(), ids.end(), (int32_t)l) != ids.end());
+        continue;
+      }
+      std::vector<int> held(nb, 0);
+      for (int32_t l : ids) {
+        ref[l] = 1;
+        ++ref_n;
+        held[l / kBlockRows]++;
+      }
+      for (int64_t b = 0; b < nb; ++b) {
+        const int64_t present = std::min<int64_t>(kBlockRows, T - b * kBlockRows);
+        if (held[b] > 0 && held[b] < present) ref_split[b] = 1;
+      }
+    }
+    std::vector<int32_t> spilled;
+    const int frc = A.prepare_finalize(&spilled, &err);
+    CHECK((frc == kOk) == (ref_n == T));
+    if (frc == kOk) {
+      std::vector<int32_t> want;
+      for (int64_t b = 0; b < nb; ++b) if (ref_split[b]) want.push_back((int32_t)b);
+      CHECK(spilled == want);
+    } else {
+      CHECK(frc == kECoverage);
+      const int64_t l = named_row(err);
+      CHECK(l >= 0 && l < T && !ref[l]);
+      for (int64_t k = 0; k < l && k < T; ++k) CHECK(ref[k]);
+    }
+    A.reset();
+    CHECK(A.register_call(nullptr, T, &err) == kOk);
+    CHECK(A.prepare_finalize(&spilled, &err) == kOk && spilled.empty());
   }
   // identity accumulator path and state machine
   AccHost A;
