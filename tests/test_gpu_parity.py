@@ -180,6 +180,38 @@ def test_dweight_is_the_canonical_order_bit_for_bit(H, lengths, bwd_path):
     print(f"[cdo] H={H} ({bwd_path}): GPU dweight == CDO-v1 emulation bit for bit", flush=True)
 
 
+@pytest.mark.parametrize("H", [24, 128, 520, 1024, 1032, 4096, 5120, 9000])
+def test_padding_rows_are_written_as_positive_zero(H):
+    """Padding rows are never read (they hold NaN here) and come out as +0.0
+    bits in y and dx, with rstd +0.0, also where the weight is negative (a
+    computed (0*rstd)*w would be -0.0 there); real rows match the unpadded call."""
+    wl = inputs.scaled(inputs.workload_h4096(), f"pads_h{H}", hidden=H, lengths=[70, 59])
+    data = pu.make_data(wl)
+    T = wl.n_logical
+    w = -data.w                                   # negative weights
+    rl = np.full(T + 40, -1, dtype=np.int32)
+    real_at = np.sort(np.random.default_rng(H).choice(T + 40, size=T, replace=False))
+    rl[real_at] = np.arange(T, dtype=np.int32)
+    lay = binding.Layout(rl, T)
+    nan = torch.full((T + 40, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    idx = torch.from_numpy(real_at.astype(np.int64)).cuda()
+    x, dy = nan.clone(), nan.clone()
+    x[idx] = data.x
+    dy[idx] = data.dy
+    y, rstd = binding.fwd(x, w, data.eps, lay)
+    dx = binding.bwd(x, w, dy, rstd, lay)
+    y0, r0 = binding.fwd(data.x, w, data.eps)
+    dx0 = binding.bwd(data.x, w, data.dy, r0)
+    pad = torch.from_numpy(np.flatnonzero(rl < 0).astype(np.int64)).cuda()
+    assert torch.equal(y[pad].view(torch.int16), torch.zeros_like(y[pad]).view(torch.int16)), H
+    assert torch.equal(dx[pad].view(torch.int16), torch.zeros_like(dx[pad]).view(torch.int16)), H
+    assert torch.equal(rstd[pad].view(torch.int32), torch.zeros_like(rstd[pad]).view(torch.int32)), H
+    assert torch.equal(y[idx].view(torch.int16), y0.view(torch.int16)), H
+    assert torch.equal(rstd[idx].view(torch.int32), r0.view(torch.int32)), H
+    assert torch.equal(dx[idx].view(torch.int16), dx0.view(torch.int16)), H
+    lay.close()
+
+
 def test_fused_dweight_equals_dweight_only_path():
     wl = inputs.scaled(inputs.workload_h4096(), "fused_vs_contrib", lengths=[300, 100])
     data = pu.make_data(wl)
