@@ -606,23 +606,25 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
 
 // ------------------------------------------------- two-pass backward (few blocks)
 // A call that touches few canonical blocks would leave most compute units
-// idle in the fused kernel (one workgroup per block).  It runs in two passes
-// instead, each with enough workgroups for the whole chip:
-//   pass 1 (bwd_dx_rows_kernel): dx, four physical rows per workgroup step,
+// idle in the fused kernel (one workgroup per block).  It runs two passes
+// instead, with enough workgroups for the whole chip between them:
+//   dx rows (dx_rows_part): dx, four physical rows per workgroup step,
 //     through the very same per-row code as the fused kernel (WideBlock's
 //     load + process with the dweight part compiled out), so every dx bit
 //     equals the fused kernel's;
-//   pass 2 (dw_cols_kernel): the dweight contributions and the in-block
-//     stream fold of one canonical block over 512 columns per workgroup,
-//     with the same operations in the same order as the fused kernel, so
-//     the block partials and spill rows are bitwise the same.
-// The second pass reads x and dy again; for the calls that take this path
-// they are small enough to be served largely from the last-level cache.
+//   dweight columns (dw_cols_part): the dweight contributions and the
+//     in-block stream fold of one canonical block over 512 columns, with the
+//     same operations in the same order as the fused kernel, so the block
+//     partials and spill rows are bitwise the same.
+// The passes are independent, so one launch (bwd_split_kernel) runs both:
+// its first workgroups fold column units, the rest compute dx rows, and the
+// two work lists overlap on the chip.  The column pass reads x and dy a
+// second time; for the calls that take this path they are small enough to
+// be served largely from the last-level cache.
 template <int V, int TW, bool FULL, bool PLAN>
-__global__ __launch_bounds__(256 * TW) void bwd_dx_rows_kernel(BwdArgs a) {
+__device__ __forceinline__ void dx_rows_part(const BwdArgs& a, float* w_s, float* dot_s, int64_t wg,
+                                             int64_t n_wg) {
   using Sh = WideShape<V, TW, FULL>;
-  __shared__ float w_s[Sh::COLS];
-  __shared__ float dot_s[TW > 1 ? 2 * 16 : 1];
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -635,11 +637,11 @@ __global__ __launch_bounds__(256 * TW) void bwd_dx_rows_kernel(BwdArgs a) {
   const int base = half * V * 512 + lane * 8;
   WideBlock<V, TW, FULL, PLAN, true, false, true> wb{a, 0, 0, stream, half, lane, wv, H, nchunk,
                                                      base, w_s, dot_s, acc};
-  const int64_t step = (int64_t)gridDim.x * Sh::S;
+  const int64_t step = n_wg * Sh::S;
   int i = 0;
   // the trip count is the same for every wavefront of the workgroup (the
   // TW > 1 dot exchange synchronises the workgroup once per row)
-  for (int64_t r0 = (int64_t)blockIdx.x * Sh::S; r0 < a.rows; r0 += step, ++i) {
+  for (int64_t r0 = wg * Sh::S; r0 < a.rows; r0 += step, ++i) {
     const int64_t row = r0 + stream;
     int p = row < a.rows ? (int)row : -1;
     if (PLAN && p >= 0 && a.plan.row_logical[p] < 0) {
@@ -657,71 +659,82 @@ __global__ __launch_bounds__(256 * TW) void bwd_dx_rows_kernel(BwdArgs a) {
   }
 }
 
-// One canonical block over 512 columns: wavefront w is fold stream w and
-// lane l holds columns 8*(64*blockIdx.y + l) .. +8.  All 16 rows of the
-// stream are loaded before the fold, which then runs in slot order.
+// One column unit: the canonical block of work item `item` over the 512
+// columns of `slice`, folded by 4 wavefronts starting at wavefront `w0`:
+// wavefront w0 + w is stream w and lane l holds columns 8*(64*slice + l)
+// .. +8.  The stream's 16 rows are loaded in two batches of 8 (all of a
+// batch before its fold), and the fold runs in slot order across both; the
+// batches keep the unit's registers near the dx rows' so the launch that
+// runs both keeps its occupancy.  `live` false: no unit, but the barrier is
+// still reached (the workgroup's other unit may need it).
 template <bool PLAN>
-__global__ __launch_bounds__(256) void dw_cols_kernel(BwdArgs a) {
-  __shared__ float q_s[kStreams - 1][512];
+__device__ __forceinline__ void dw_cols_part(const BwdArgs& a, float (*q_s)[512], int item, int slice,
+                                             int w0, bool live) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int stream = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int item = blockIdx.x;
+  const int stream = __builtin_amdgcn_readfirstlane(tid >> 6) - w0;
   const int H = a.hidden;
-  const int q = blockIdx.y * 64 + lane;         // this lane's 8-column chunk
-  const bool on = q < (H >> 3);
-  int blk;
-  bool complete;
-  if (PLAN) {
-    const int info = a.plan.item_info[item];
-    complete = info >= 0;
-    blk = complete ? info : ~info;
-  } else {
-    blk = item;
-    complete = true;
-  }
-  // lane i (< 16) holds the physical row and rstd of the stream's slot i
-  const int sp = slot_row_t<PLAN>(a, item, blk, stream + kStreams * (lane & (kSlotsPerStream - 1)));
-  const float sr = a.rstd[sp >= 0 ? sp : 0];
-  uint4 xv[kSlotsPerStream], dv[kSlotsPerStream];
-#pragma unroll
-  for (int i = 0; i < kSlotsPerStream; ++i) {
-    const int p = __builtin_amdgcn_readlane(sp, i);
-    const int64_t off = (int64_t)(p >= 0 ? p : 0) * H + (on ? q * 8 : 0);
-    xv[i] = load16_stream(a.x + off);
-    dv[i] = load16_stream(a.dy + off);
+  const int q = slice * 64 + lane;         // this lane's 8-column chunk
+  const bool on = live && q < (H >> 3);
+  int blk = 0;
+  bool complete = true;
+  if (live) {
+    if (PLAN) {
+      const int info = a.plan.item_info[item];
+      complete = info >= 0;
+      blk = complete ? info : ~info;
+    } else {
+      blk = item;
+    }
   }
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  if (live) {
+    // lane i (< 16) holds the physical row and rstd of the stream's slot i
+    const int sp = slot_row_t<PLAN>(a, item, blk, stream + kStreams * (lane & (kSlotsPerStream - 1)));
+    const float sr = a.rstd[sp >= 0 ? sp : 0];
+    constexpr int B = kSlotsPerStream / 2;
 #pragma unroll
-  for (int i = 0; i < kSlotsPerStream; ++i) {
-    const int p = __builtin_amdgcn_readlane(sp, i);
-    if (p < 0) continue;
-    const float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sr), i));
-    float xf[8], df[8], c[8];
-    unpack8(xv[i], xf);
-    unpack8(dv[i], df);
+    for (int b0 = 0; b0 < kSlotsPerStream; b0 += B) {
+      uint4 xv[B], dv[B];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pr = df[e] * xf[e];          // exact: two bf16 significands
-      c[e] = pr * r;                           // the row's contribution, rounded once
-      acc[e] = acc[e] + c[e];
-    }
-    if (!complete && on) {
-      float* srow = a.S + ((int64_t)blk * kBlockRows + stream + kStreams * i) * H + q * 8;
-      store_f4_stream(srow, c[0], c[1], c[2], c[3]);
-      store_f4_stream(srow + 4, c[4], c[5], c[6], c[7]);
+      for (int i = 0; i < B; ++i) {
+        const int p = __builtin_amdgcn_readlane(sp, b0 + i);
+        const int64_t off = (int64_t)(p >= 0 ? p : 0) * H + (on ? q * 8 : 0);
+        xv[i] = load16_stream(a.x + off);
+        dv[i] = load16_stream(a.dy + off);
+      }
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const int p = __builtin_amdgcn_readlane(sp, b0 + i);
+        if (p < 0) continue;
+        const float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sr), b0 + i));
+        float xf[8], df[8], c[8];
+        unpack8(xv[i], xf);
+        unpack8(dv[i], df);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pr = df[e] * xf[e];          // exact: two bf16 significands
+          c[e] = pr * r;                           // the row's contribution, rounded once
+          acc[e] = acc[e] + c[e];
+        }
+        if (!complete && on) {
+          float* srow = a.S + ((int64_t)blk * kBlockRows + stream + kStreams * (b0 + i)) * H + q * 8;
+          store_f4_stream(srow, c[0], c[1], c[2], c[3]);
+          store_f4_stream(srow + 4, c[4], c[5], c[6], c[7]);
+        }
+      }
     }
   }
-  if (!complete) return;
-  if (stream > 0) {
+  const bool fold = live && complete;
+  if (fold && stream > 0) {
     float* d = &q_s[stream - 1][lane * 8];
     store_f4(d, acc[0], acc[1], acc[2], acc[3]);
     store_f4(d + 4, acc[4], acc[5], acc[6], acc[7]);
   }
   __syncthreads();
-  if (stream == 0 && on) {
+  if (fold && stream == 0 && on) {
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -729,6 +742,29 @@ __global__ __launch_bounds__(256) void dw_cols_kernel(BwdArgs a) {
     float* dst = a.P + (int64_t)blk * H + q * 8;
     store_f4(dst, o[0], o[1], o[2], o[3]);
     store_f4(dst + 4, o[4], o[5], o[6], o[7]);
+  }
+}
+
+// Both passes in one launch.  Workgroups 0 .. n_cols_wg-1 fold column units
+// (TW units per workgroup: wavefronts 4u .. 4u+3 take unit TW*wg + u of the
+// n_units = items x column slices); the following n_rows_wg workgroups
+// compute dx rows.  Either list may be empty (dx alone, contributions alone).
+template <int V, int TW, bool FULL, bool PLAN>
+__global__ __launch_bounds__(256 * TW) void bwd_split_kernel(BwdArgs a, int n_cols_wg, int n_units,
+                                                             int n_slices, int n_rows_wg) {
+  using Sh = WideShape<V, TW, FULL>;
+  constexpr int ROWS_LDS = Sh::COLS + 2 * 16;
+  constexpr int COLS_LDS = TW * (kStreams - 1) * 512;
+  __shared__ float lds[ROWS_LDS > COLS_LDS ? ROWS_LDS : COLS_LDS];
+  const int wg = blockIdx.x;
+  if (wg < n_cols_wg) {
+    const int u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);   // the workgroup's unit
+    const int unit = wg * TW + u;
+    const bool live = unit < n_units;
+    dw_cols_part<PLAN>(a, reinterpret_cast<float (*)[512]>(lds + u * (kStreams - 1) * 512),
+                       live ? unit / n_slices : 0, live ? unit % n_slices : 0, u * kStreams, live);
+  } else {
+    dx_rows_part<V, TW, FULL, PLAN>(a, lds, lds + Sh::COLS, wg - n_cols_wg, n_rows_wg);
   }
 }
 
@@ -1085,15 +1121,17 @@ static void bwd_wide_go3(const BwdArgs& a, bool dx, bool dw, bool rc, hipStream_
     return;
   }
   if (a.plan.n_items < split_items()) {
+    int64_t rows_wg = 0;
     if (dx && a.rows > 0) {
-      int64_t g = (a.rows + Sh::S - 1) / Sh::S;
-      if (g > grid_cap()) g = grid_cap();
-      bwd_dx_rows_kernel<V, TW, FULL, PLAN><<<dim3((unsigned)g), dim3(Sh::THREADS), 0, st>>>(a);
+      rows_wg = (a.rows + Sh::S - 1) / Sh::S;
+      if (rows_wg > grid_cap()) rows_wg = grid_cap();
     }
-    if (dw && a.plan.n_items > 0) {
-      const dim3 grid((unsigned)a.plan.n_items, (unsigned)((a.hidden / 8 + 63) / 64));
-      dw_cols_kernel<PLAN><<<grid, dim3(256), 0, st>>>(a);
-    }
+    const int n_slices = (a.hidden / 8 + 63) / 64;
+    const int64_t units = dw ? (int64_t)a.plan.n_items * n_slices : 0;
+    const int64_t cols_wg = (units + TW - 1) / TW;
+    if (rows_wg + cols_wg == 0) return;
+    bwd_split_kernel<V, TW, FULL, PLAN><<<dim3((unsigned)(cols_wg + rows_wg)), dim3(Sh::THREADS), 0, st>>>(
+        a, (int)cols_wg, (int)units, n_slices, (int)rows_wg);
     return;
   }
   const int pad_groups = dx ? (a.plan.n_pad + Sh::WAVES - 1) / Sh::WAVES : 0;
