@@ -209,6 +209,16 @@ int rmsnorm_set_split_threshold(int64_t blocks, int64_t* previous);
  * afterwards.  Always returns RMSNORM_OK. */
 int rmsnorm_set_workgroup_cap(int64_t groups, int64_t* previous);
 
+/* Streaming copy of `bytes` bytes from device buffer `src` to device buffer
+ * `dst` on `stream`, with the access policy the kernels use (16-byte
+ * non-temporal loads and stores, one 16-byte unit per thread).  Not part of
+ * the method: it measures the practical HBM ceiling of the GPU the library
+ * runs on, the copy rate the kernels' traffic is compared with.  bytes must
+ * be a multiple of 16, both pointers 16-byte aligned and the ranges
+ * disjoint (RMSNORM_EUNSUPPORTED / RMSNORM_EINVAL otherwise); bytes == 0 is
+ * a no-op.  Caller-owned memory; nothing is allocated. */
+int rmsnorm_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,8 @@ EXPORTED = ("rmsnorm_max_hidden", "rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_c
             "rmsnorm_dw_finalize", "rmsnorm_layout_create", "rmsnorm_layout_destroy",
             "rmsnorm_layout_check", "rmsnorm_dw_acc_create", "rmsnorm_dw_acc_reset",
             "rmsnorm_dw_acc_destroy", "rmsnorm_last_error", "rmsnorm_backend_info",
-            "rmsnorm_set_split_threshold", "rmsnorm_set_workgroup_cap", "rmsnorm_fwd_packed",
+            "rmsnorm_set_split_threshold", "rmsnorm_set_workgroup_cap", "rmsnorm_stream_copy",
+            "rmsnorm_fwd_packed",
             "rmsnorm_bwd_dx_packed", "rmsnorm_bwd_dx_recompute",
             "det_gemm_fwd", "det_gemm_bwd_dx", "det_gemm_dw_acc_create", "det_gemm_dw_contrib",
             "det_gemm_dw_finalize", "det_gemm_dw_acc_reset", "det_gemm_dw_acc_destroy",
@@ -78,6 +79,7 @@ def load() -> ctypes.CDLL:
         "rmsnorm_backend_info": ([], ctypes.c_char_p),
         "rmsnorm_set_split_threshold": ([I64, ctypes.POINTER(ctypes.c_int64)], I32),
         "rmsnorm_set_workgroup_cap": ([I64, ctypes.POINTER(ctypes.c_int64)], I32),
+        "rmsnorm_stream_copy": ([P, P, I64, P], I32),
         "rmsnorm_fwd_packed": ([P, P, P, P, I64, I64, I64, I64, ctypes.c_float, P, P], I32),
         "rmsnorm_bwd_dx_packed": ([P, P, P, P, P, I64, I64, I64, I64, P, P, P], I32),
         "det_gemm_fwd": ([P, P, P, I64, I64, I64, P, P], I32),
@@ -218,6 +220,11 @@ def rmsnorm_set_workgroup_cap(groups: int) -> int:
     _check(load().rmsnorm_set_workgroup_cap(int(groups), ctypes.byref(prev)),
            "rmsnorm_set_workgroup_cap")
     return int(prev.value)
+
+
+def rmsnorm_stream_copy(src: int, dst: int, nbytes: int, stream: Optional[int]) -> None:
+    """Streaming device copy with the kernels' access policy (bandwidth ceiling probe)."""
+    _check(load().rmsnorm_stream_copy(src, dst, int(nbytes), stream), "rmsnorm_stream_copy")
 
 
 # ---------------------------------------------------------------- det_gemm

@@ -77,6 +77,20 @@ int rmsnorm_set_split_threshold(int64_t blocks, int64_t* previous) {
   return RMSNORM_OK;
 }
 
+int rmsnorm_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0) return fail(RMSNORM_EINVAL, "bytes must be non-negative");
+  if (bytes == 0) return RMSNORM_OK;
+  if (src == nullptr || dst == nullptr) return fail(RMSNORM_EINVAL, "src and dst must be non-NULL");
+  if (bytes % 16 != 0) return fail(RMSNORM_EUNSUPPORTED, "bytes must be a multiple of 16");
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+    return fail(RMSNORM_EUNSUPPORTED, "src and dst must be 16-byte aligned");
+  if (overlaps(src, static_cast<size_t>(bytes), dst, static_cast<size_t>(bytes)))
+    return fail(RMSNORM_EINVAL, "src and dst must not overlap");
+  const hipError_t e = rbi::launch_stream_copy(src, dst, bytes / 16, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream copy launch");
+  return RMSNORM_OK;
+}
+
 int rmsnorm_set_workgroup_cap(int64_t groups, int64_t* previous) {
   if (previous != nullptr) *previous = rbi::wide_group_cap();
   rbi::set_wide_group_cap(groups);

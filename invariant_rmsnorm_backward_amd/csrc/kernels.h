@@ -78,6 +78,9 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// dst[0..n16) = src[0..n16) in 16-byte units with the kernels' streaming
+// access policy, one unit per thread (a practical bandwidth ceiling).
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t n16, hipStream_t stream);
 // with_dx: write dx (and zero padding rows); with_dw: fold dweight contributions.
 // recompute: rstd is not read but rebuilt from x with a.eps in the forward's
 // order (bitwise the saved rstd); needs with_dx and contiguous rows.

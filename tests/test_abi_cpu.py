@@ -139,6 +139,21 @@ def test_split_threshold_knob():
         binding.rmsnorm_set_split_threshold(prev)
 
 
+def test_stream_copy_checks_its_arguments(lib):
+    """The bandwidth-probe copy refuses bad arguments before touching the GPU."""
+    A = 1 << 12
+    cases = [((A, A + 4096, -16), binding.EINVAL),           # negative size
+             ((0, A, 64), binding.EINVAL),                   # NULL source
+             ((A, A + 4096, 40), binding.EUNSUPPORTED),      # not a multiple of 16
+             ((A + 8, A + 8192, 64), binding.EUNSUPPORTED),  # misaligned
+             ((A, A + 32, 64), binding.EINVAL)]              # overlapping ranges
+    for (src, dst, n), code in cases:
+        with pytest.raises(binding.RmsNormError) as ei:
+            binding.rmsnorm_stream_copy(src, dst, n, None)
+        assert ei.value.code == code, (src, dst, n)
+    binding.rmsnorm_stream_copy(A, A + 4096, 0, None)       # zero bytes: a no-op
+
+
 def test_workgroup_cap_knob():
     """The fused backward's workgroup cap: set, read back, restore."""
     prev = binding.rmsnorm_set_workgroup_cap(3)

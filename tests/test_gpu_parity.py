@@ -212,6 +212,16 @@ def test_padding_rows_are_written_as_positive_zero(H):
     lay.close()
 
 
+@pytest.mark.parametrize("nbytes", [16, 4096, 3 * (1 << 20) + 16 * 37])
+def test_stream_copy_copies_every_byte(nbytes):
+    src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros(nbytes // 4 + 8, dtype=torch.int32, device="cuda")
+    binding.rmsnorm_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, binding.current_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(dst[: nbytes // 4], src)
+    assert not dst[nbytes // 4:].any()            # nothing past the end is written
+
+
 def test_fused_dweight_equals_dweight_only_path():
     wl = inputs.scaled(inputs.workload_h4096(), "fused_vs_contrib", lengths=[300, 100])
     data = pu.make_data(wl)
