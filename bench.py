@@ -633,9 +633,9 @@ def main():
                          "a 32000 x 4096 table on 32768 rows (info lines)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(rows would shard across GPUs with an all-gather of block partials; see the design notes).",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(rows would shard across GPUs, with an all-gather of the block partials before the "
+              "same finalize on every GPU).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
