@@ -898,14 +898,21 @@ __global__ __launch_bounds__(256) void rebuild_kernel(const float* __restrict__ 
   const int b = blocks[blockIdx.x];
   const int j = blockIdx.y * 256 + threadIdx.x;
   if (j >= H) return;
+  // every slot's value is loaded before the folds (absent slots, l >= T,
+  // load nothing and add nothing), so the 64 loads are in flight together
+  float v[kBlockRows];
+#pragma unroll
+  for (int s = 0; s < kBlockRows; ++s) {
+    const int64_t l = (int64_t)b * kBlockRows + s;
+    v[s] = l < T ? S[l * H + j] : 0.0f;
+  }
   float q[kStreams];
 #pragma unroll
   for (int w = 0; w < kStreams; ++w) {
     float acc = 0.0f;
-    for (int s = w; s < kBlockRows; s += kStreams) {
-      const int64_t l = (int64_t)b * kBlockRows + s;
-      if (l < T) acc = acc + S[l * H + j];
-    }
+#pragma unroll
+    for (int s = w; s < kBlockRows; s += kStreams)
+      if ((int64_t)b * kBlockRows + s < T) acc = acc + v[s];
     q[w] = acc;
   }
   P[(int64_t)b * H + j] = stream_tree4(q[0], q[1], q[2], q[3]);
