@@ -218,29 +218,29 @@ def measure_cell(args, torch, np, binding, inputs, layouts):
                           dw=torch.empty(H, dtype=torch.float32, device="cuda"),
                           dw_ref=dw_ref, acc_ref=acc_ref, cell=cell))
 
-    def run_fwd(n, s):
+    def run_fwd(n, s, st=sh):
         for c, b in zip(n["calls"], s):
             binding.rmsnorm_fwd(b["x"].data_ptr(), n["w"].data_ptr(), b["y"].data_ptr(),
                                 b["rstd"].data_ptr(), c["rows"], n["H"], n["wl"].eps,
-                                None if c["layout"] is None else c["layout"].handle, sh)
+                                None if c["layout"] is None else c["layout"].handle, st)
 
-    def run_bwd(n, s):
+    def run_bwd(n, s, st=sh):
         for c, b in zip(n["calls"], s):
             binding.rmsnorm_bwd_dx(b["x"].data_ptr(), n["w"].data_ptr(), b["dy"].data_ptr(),
                                    b["rstd"].data_ptr(), b["dx"].data_ptr(), c["rows"], n["H"],
                                    None if c["layout"] is None else c["layout"].handle,
-                                   n["acc"].handle, sh)
+                                   n["acc"].handle, st)
 
-    def run_fin(n):
-        binding.rmsnorm_dw_finalize(n["acc"].handle, n["dw"].data_ptr(), sh)
-        binding.rmsnorm_dw_acc_reset(n["acc"].handle, sh)
+    def run_fin(n, st=sh):
+        binding.rmsnorm_dw_finalize(n["acc"].handle, n["dw"].data_ptr(), st)
+        binding.rmsnorm_dw_acc_reset(n["acc"].handle, st)
 
-    def step(i):
+    def step(i, st=sh):
         for n in norms:
             s = n["sets"][i % len(n["sets"])]
-            run_fwd(n, s)
-            run_bwd(n, s)
-            run_fin(n)
+            run_fwd(n, s, st)
+            run_bwd(n, s, st)
+            run_fin(n, st)
 
     step(0)
     torch.cuda.synchronize()
@@ -278,6 +278,34 @@ def measure_cell(args, torch, np, binding, inputs, layouts):
     med = {k: float(np.median([sum(a.elapsed_time(b) for a, b in step_ev) for step_ev in v]))
            for k, v in ph.items()}
 
+    # The same steps captured once in a HIP graph and replayed (launch-bound
+    # cells); only when no block is split across calls, since the finalize
+    # then enqueues kernels alone (with split blocks it uploads a spill list).
+    graph = None
+    if args.graph:
+        split = sum(binding.rmsnorm_layout_check(c.row_logical, n["T"])["partial_blocks"]
+                    for n in norms for c in n["cell"].calls if c.row_logical is not None)
+        if split:
+            graph = {"skipped": f"{split} block(s) split across calls: the finalize uploads a spill list"}
+        else:
+            nsets = len(norms[0]["sets"])
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cs = torch.cuda.current_stream().cuda_stream
+                for i in range(nsets):
+                    step(i, cs)
+            for _ in range(2):
+                g.replay()
+            reps = max(1, K // nsets)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            graph = {"ms_per_step": round((time.perf_counter() - t0) / (reps * nsets) * 1e3, 4),
+                     "steps": reps * nsets}
+            del g
+
     fb = bb = 0
     for n in norms:
         for c in n["calls"]:
@@ -311,6 +339,10 @@ def measure_cell(args, torch, np, binding, inputs, layouts):
         "dweight_bitwise_equal_to_bn_full": inv_ok,
         "kernel_source_hash": kernel_source_hash(),
     }
+    if graph is not None:
+        if "ms_per_step" in graph:
+            graph["value"] = round((fb + bb) / (graph["ms_per_step"] * 1e-3) / 1e9, 2)
+        out["graph_replay"] = graph
     for n in norms:
         for c in n["calls"]:
             if c["layout"] is not None:
@@ -627,6 +659,8 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="measure another workload (info line; the default run is the headline)")
     ap.add_argument("--cell", default="BN/full", help="layout cell for --workload")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --workload: also time the cell's steps captured in one HIP graph and replayed")
     ap.add_argument("--op", default="rms_norm",
                     choices=["rms_norm", "det_gemm", "det_embedding", "qk_packed"],
                     help="det_gemm: the linear layer 4096 -> 4096 on 32768 rows; det_embedding: "

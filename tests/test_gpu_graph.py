@@ -1,0 +1,94 @@
+"""GPU: a whole step -- every call's forward and backward into one dweight
+accumulator, then the finalize -- captured once in a HIP graph (through
+torch.cuda.graph, on the capturing stream) and replayed.  Every replay,
+with eager work and synchronisations between the replays, gives the bits of
+the same step run eagerly.  The calls enqueue kernels only; a finalize with
+blocks split across calls also uploads its spill list and is not captured
+here, so the chunks hold whole 64-row blocks."""
+import numpy as np
+import pytest
+import torch
+
+from invariant_rmsnorm_backward_amd import binding, inputs, layouts
+from tests import parity_utils as pu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the gpu tests need an MI355X"
+    binding.load()
+
+
+def _bits(t):
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32).clone()
+
+
+# (hidden, chunk sizes over the 6144 rows): the two-pass one-launch backward
+# (12 calls of 8 blocks), the fused backward with a layout (one call of 96
+# blocks; resident block owners at hidden 4096), two calls of 48 blocks at
+# hidden 5120, and the lane-group kernels of the per-head norm.
+CASES = [(4096, [512] * 12), (4096, [6144]), (5120, [3072, 3072]), (128, [1024] * 6)]
+
+
+@pytest.mark.parametrize("H,sizes", CASES)
+def test_graph_replay_of_a_chunked_step_matches_eager(H, sizes):
+    wl = inputs.scaled(inputs.workload_h4096(), f"graph_h{H}", hidden=H, lengths=[3072, 2048, 1024])
+    data = pu.make_data(wl)
+    T = wl.n_logical
+    cell = layouts.chunked_packed(wl, sizes)
+    assert all(c.rows % 64 == 0 for c in cell.calls)          # whole blocks: no spills
+    calls = []
+    for c in cell.calls:
+        a, b = int(c.row_logical[0]), int(c.row_logical[-1]) + 1
+        calls.append(dict(x=data.x[a:b], dy=data.dy[a:b], y=torch.empty_like(data.x[a:b]),
+                          rstd=torch.empty(b - a, dtype=torch.float32, device="cuda"),
+                          dx=torch.empty_like(data.x[a:b]), lay=binding.Layout(c.row_logical, T)))
+
+    def step(acc, dw):
+        for c in calls:
+            binding.fwd(c["x"], data.w, data.eps, c["lay"], y=c["y"], rstd=c["rstd"])
+            binding.bwd(c["x"], data.w, c["dy"], c["rstd"], c["lay"], acc, dx=c["dx"])
+        acc.finalize(dweight=dw)
+
+    # eager reference
+    acc_e = binding.DwAccumulator(T, H)
+    dw_e = torch.empty(H, dtype=torch.float32, device="cuda")
+    step(acc_e, dw_e)
+    torch.cuda.synchronize()
+    ref = [(_bits(c["y"]), _bits(c["rstd"]), _bits(c["dx"])) for c in calls] + [_bits(dw_e)]
+
+    # capture (after a warm-up step on the same accumulator, reset)
+    acc_g = binding.DwAccumulator(T, H)
+    dw_g = torch.empty(H, dtype=torch.float32, device="cuda")
+    step(acc_g, dw_g)
+    acc_g.reset()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(acc_g, dw_g)
+    torch.cuda.synchronize()
+    print(f"[graph] H={H}: {len(calls)} calls captured", flush=True)
+
+    for rep in range(3):
+        for c in calls:                                   # clear the outputs eagerly
+            c["y"].zero_()
+            c["rstd"].zero_()
+            c["dx"].zero_()
+        dw_g.zero_()
+        acc_e.reset()                                     # eager work between the replays
+        step(acc_e, dw_e)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [(_bits(c["y"]), _bits(c["rstd"]), _bits(c["dx"])) for c in calls] + [_bits(dw_g)]
+        for i, (a, b) in enumerate(zip(ref[:-1], got[:-1])):
+            for name, u, v in zip(("y", "rstd", "dx"), a, b):
+                assert torch.equal(u, v), (H, rep, i, name)
+        assert torch.equal(ref[-1], got[-1]), (H, rep, "dweight")
+    del g
+    for c in calls:
+        c["lay"].close()
+    acc_e.close()
+    acc_g.close()
