@@ -64,6 +64,7 @@ WIDE_CASES = {
     "h3072": (inputs.workload_h4096, 3072, [150, 97, 64], 48),
     "h6144_two_waves": (inputs.workload_h8192, 6144, [99, 30], 40),
     "h9000_two_waves_masked": (inputs.workload_h8192, 9000, [77, 60], 64),
+    "h10240_max": (inputs.workload_h8192, 10240, [90, 41], 64),
     "h40_masked": (inputs.workload_h8, 40, [70, 45, 3], 17),
     "h16": (inputs.workload_h8, 16, [70, 45, 3], 17),
     "h128": (inputs.workload_h8, 128, [130, 2, 61], 32),
