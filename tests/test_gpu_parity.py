@@ -223,6 +223,46 @@ def test_stream_copy_copies_every_byte(nbytes):
     assert not dst[nbytes // 4:].any()            # nothing past the end is written
 
 
+def _bf16_scaled(bits: np.ndarray, log2: int) -> np.ndarray:
+    """bf16 bit patterns times 2**log2, exactly (exponent field shifted);
+    zeros stay zero and a value that would leave the normal range becomes a
+    zero of its sign (inputs only: the oracle sees the same bits)."""
+    b = bits.astype(np.int32)
+    exp = (b >> 7) & 0xFF
+    new_exp = exp + log2
+    keep = (exp != 0) & (new_exp >= 1) & (new_exp <= 254)
+    out = b & 0x8000
+    out[keep] = (b[keep] & ~(0xFF << 7)) | (new_exp[keep] << 7)
+    return out.astype(np.uint16)
+
+
+@pytest.mark.parametrize("H", [128, 1024, 4096, 5120])
+def test_degenerate_rows_match_the_oracle(H, bwd_path):
+    """Rows the method treats specially or that stress FP32, planted in the
+    inputs and checked against the FP64 oracle on the same bits in every
+    layout cell: an all-zero row (rstd = eps^-1/2, y = 0), a constant row, a
+    row scaled by 2^40 and one by 2^-60 (squares near the bottom of FP32), a
+    row with a zero upstream gradient (contributes exactly 0), and a row with
+    one 2^20 outlier."""
+    wl = inputs.scaled(inputs.workload_h4096(), f"degen_h{H}", hidden=H, lengths=[70, 59])
+    xb = inputs.bf16_bits(inputs.gen_x(wl)).copy()
+    wb = inputs.bf16_bits(inputs.gen_w(wl))
+    dyb = inputs.bf16_bits(inputs.gen_dy(wl)).copy()
+    xb[0] = 0
+    xb[1] = 0x4040                                        # 3.0 in every column
+    xb[2] = _bf16_scaled(xb[2], 40)
+    xb[3] = _bf16_scaled(xb[3], -60)
+    dyb[4] = 0
+    xb[5, 7] = 0x4980                                     # 2^20
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)
+    data = adapters.NormInputs(wl.name, wl, dev(xb), dev(wb), dev(dyb), wl.eps, inputs.n_active(wl))
+    y, rstd = oracle.rmsnorm_fwd_bf16(xb, wb, wl.eps)
+    dx, dw, _ = oracle.rmsnorm_bwd_bf16(xb, wb, dyb, wl.eps)
+    assert abs(rstd[0] - wl.eps ** -0.5) <= 1e-9 * wl.eps ** -0.5 and not y[0].any()
+    ref = {"y": y, "rstd": rstd, "dx": dx, "dweight": dw}
+    _run("rms_norm", pu.standard_cells(wl, 37), data, ref, f"degenerate h{H} ({bwd_path})")
+
+
 def test_fused_dweight_equals_dweight_only_path():
     wl = inputs.scaled(inputs.workload_h4096(), "fused_vs_contrib", lengths=[300, 100])
     data = pu.make_data(wl)
