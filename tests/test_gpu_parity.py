@@ -243,7 +243,7 @@ def test_degenerate_rows_match_the_oracle(H, bwd_path):
     layout cell: an all-zero row (rstd = eps^-1/2, y = 0), a constant row, a
     row scaled by 2^40 and one by 2^-60 (squares near the bottom of FP32), a
     row with a zero upstream gradient (contributes exactly 0), and a row with
-    one 2^20 outlier."""
+    one 2^20 outlier.  The rstd-recompute backward meets the same rows."""
     wl = inputs.scaled(inputs.workload_h4096(), f"degen_h{H}", hidden=H, lengths=[70, 59])
     xb = inputs.bf16_bits(inputs.gen_x(wl)).copy()
     wb = inputs.bf16_bits(inputs.gen_w(wl))
@@ -260,7 +260,10 @@ def test_degenerate_rows_match_the_oracle(H, bwd_path):
     dx, dw, _ = oracle.rmsnorm_bwd_bf16(xb, wb, dyb, wl.eps)
     assert abs(rstd[0] - wl.eps ** -0.5) <= 1e-9 * wl.eps ** -0.5 and not y[0].any()
     ref = {"y": y, "rstd": rstd, "dx": dx, "dweight": dw}
-    _run("rms_norm", pu.standard_cells(wl, 37), data, ref, f"degenerate h{H} ({bwd_path})")
+    cells = pu.standard_cells(wl, 37)
+    _run("rms_norm", cells, data, ref, f"degenerate h{H} ({bwd_path})")
+    if bwd_path == "fused":   # the rstd-recompute backward always takes the fused kernel
+        _run("rms_norm_recompute", cells, data, ref, f"degenerate h{H} (rstd rebuilt)")
 
 
 def test_fused_dweight_equals_dweight_only_path():
