@@ -184,9 +184,10 @@ const char* rmsnorm_backend_info(void);
 /* Work distribution of the backward for hidden > 256 (a tuning knob; no
  * output bit depends on it).  A call whose rows touch fewer than `blocks`
  * canonical 64-row blocks runs the backward in two passes -- row-parallel
- * dx, then the dweight fold split over 512-column tiles -- instead of the
- * fused one-workgroup-per-block kernel, so that small calls (chunked
- * prefill pieces, single samples) still occupy the whole GPU.  Both paths
+ * dx and the dweight fold split over 512-column tiles, side by side in one
+ * launch -- instead of the fused kernel whose workgroups own whole blocks,
+ * so that small calls (chunked prefill pieces, single samples) still occupy
+ * the whole GPU (default 96 blocks, the measured crossover).  Both paths
  * run the same per-row and per-block arithmetic, so dx and dweight are
  * bitwise the same either way.  0 disables the two-pass path; a negative
  * value restores the default.  If `previous` is non-NULL it receives the
