@@ -29,11 +29,14 @@ def _bits(t):
 # (12 calls of 8 blocks), the fused backward with a layout (one call of 96
 # blocks; resident block owners at hidden 4096), two calls of 48 blocks at
 # hidden 5120, and the lane-group kernels of the per-head norm.
-CASES = [(4096, [512] * 12), (4096, [6144]), (5120, [3072, 3072]), (128, [1024] * 6)]
+# The last case rebuilds rstd in the backward (no saved statistic; those
+# calls always take the fused kernel).
+CASES = [(4096, [512] * 12, False), (4096, [6144], False), (5120, [3072, 3072], False),
+         (128, [1024] * 6, False), (4096, [512] * 12, True)]
 
 
-@pytest.mark.parametrize("H,sizes", CASES)
-def test_graph_replay_of_a_chunked_step_matches_eager(H, sizes):
+@pytest.mark.parametrize("H,sizes,recompute", CASES)
+def test_graph_replay_of_a_chunked_step_matches_eager(H, sizes, recompute):
     wl = inputs.scaled(inputs.workload_h4096(), f"graph_h{H}", hidden=H, lengths=[3072, 2048, 1024])
     data = pu.make_data(wl)
     T = wl.n_logical
@@ -49,7 +52,10 @@ def test_graph_replay_of_a_chunked_step_matches_eager(H, sizes):
     def step(acc, dw):
         for c in calls:
             binding.fwd(c["x"], data.w, data.eps, c["lay"], y=c["y"], rstd=c["rstd"])
-            binding.bwd(c["x"], data.w, c["dy"], c["rstd"], c["lay"], acc, dx=c["dx"])
+            if recompute:
+                binding.bwd_recompute(c["x"], data.w, c["dy"], data.eps, c["lay"], acc, dx=c["dx"])
+            else:
+                binding.bwd(c["x"], data.w, c["dy"], c["rstd"], c["lay"], acc, dx=c["dx"])
         acc.finalize(dweight=dw)
 
     # eager reference
