@@ -852,7 +852,8 @@ def main():
                    "buffer_sets": args.sets},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "bwd_wide_kernel<V=4,TW=2,FULL,DX,DW> (4 streams x 2 wavefronts per row)",
+                     "kernel": "bwd_team_kernel<V=2,TW=4,TEAMS=2,PD=1,FULL,identity,DX,DW> (two rows in flight per "
+                               "workgroup, 4 wavefronts per row, 64-row block walked in two passes)",
                      "algorithmic_bytes_per_launch": bb, "avg_launch_ms": round(bwd_avg, 5)},
         "cpu_baseline": cpu,
         "phases_ms": {"fwd": round(float(np.median(fwd_ms)), 5),

@@ -19,6 +19,7 @@
 // contributions to a spill area instead, and the finalize step folds them in
 // exactly the same order.  No atomics anywhere: every sum has one owner.
 #include <mutex>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -57,6 +58,35 @@ __device__ __forceinline__ float pad_tree(float (&v)[N]) {
     for (int k = 0; k + st < N; k += 2 * st) v[k] = v[k] + v[k + st];   // v + (+0.0) == v
   return v[0];
 }
+// The perfect pairwise tree over N = 2^m values fed one at a time, in
+// order: the pending subtree roots are joined as the digits of a binary
+// counter (left operand the earlier subtree), so at most m values are live.
+template <int N>
+struct RunningTree {
+  static_assert((N & (N - 1)) == 0, "a power of two");
+  static constexpr int LEVELS = N > 1 ? 1 + RunningTree<(N > 1 ? N / 2 : 1)>::LEVELS : 1;
+  float pend[LEVELS];
+  // value number i (0-based, compile-time in unrolled loops)
+  __device__ __forceinline__ void push(int i, float v) {
+#pragma unroll
+    for (int l = 0; l < LEVELS; ++l) {
+      if (((i >> l) & 1) == 0) {
+        pend[l] = v;
+        return;
+      }
+      v = pend[l] + v;
+    }
+  }
+  __device__ __forceinline__ float root() const { return pend[LEVELS - 1]; }
+};
+template <>
+struct RunningTree<1> {
+  static constexpr int LEVELS = 1;
+  float pend[1];
+  __device__ __forceinline__ void push(int, float v) { pend[0] = v; }
+  __device__ __forceinline__ float root() const { return pend[0]; }
+};
+
 __device__ __forceinline__ float chunk_squares(const uint4& v) {
   float f[8];
   unpack8(v, f);
@@ -191,24 +221,37 @@ __device__ __forceinline__ int slot_row_t(const BwdArgs& a, int item, int blk, i
   return r < a.rows ? (int)r : -1;
 }
 
-// Wide rows: V chunks of 8 columns per lane, TW wavefronts per row, 4
-// streams; the workgroup is 4*TW wavefronts.  Chunk q of the row held by
-// lane `lane` of wave-part `half` at step k is q = (half*V + k)*64 + lane.
-// FULL means hidden == 512*V*TW exactly, so no lane needs a bounds mask.
+// Wide rows (hidden > 256).  A row is held by a team of TW wavefronts:
+// wavefront h of the team holds the chunk groups h*V .. h*V+V-1, where chunk
+// group g is the 64 16-byte chunks 64g .. 64g+63 and lane l holds chunk
+// 64g + l.  FULL means hidden == 512*V*TW exactly, so no lane needs a mask.
+//
+// The row's dot = sum_j (dy_j*x_j)*w_j has one order for every wide kernel,
+// whatever its shape (the same grouping as the sum of squares above):
+//   d_q = fmaf chain over chunk q's 8 products (dy*x, exact) times w, from
+//         +0.0, in column order
+//   D_g = wave_sum of d_{64g+l} over l (absent chunks: +0.0)
+//   dot = perfect pairwise tree over D_0 .. D_{K-1}, padded with +0.0.
+// So dx is a function of the row and hidden alone, and each kernel may spread
+// a row over as many wavefronts as suits it (the fused backward, the dx rows
+// of the two-pass path and the rstd-recompute backward all give the same
+// bits).  No partial sum is ever -0.0 (every chain starts from +0.0), so the
+// +0.0 padding of the tree changes nothing.
 template <int V, int TW, bool FULL>
-struct WideShape {
-  static constexpr int S = kStreams;               // fold streams
-  static constexpr int SLOTS = kSlotsPerStream;    // slots per stream
-  static constexpr int WAVES = S * TW;             // wavefronts per workgroup
-  static constexpr int THREADS = 64 * WAVES;
-  static constexpr int COLS = 512 * V * TW;        // columns the workgroup covers
-  static constexpr int NTILE = (V * TW + 1) / 2;   // 1024-column tiles of the stream tree
+struct RowLanes {
+  static constexpr int G = V * TW;     // chunk groups a team holds
+  static constexpr int COLS = 512 * G; // columns a team covers
+  int lane, half, nchunk, base;        // base: first column of chunk 0 of this lane
+  __device__ __forceinline__ bool in_row(int k) const {
+    return FULL || (half * V + k) * 64 + lane < nchunk;
+  }
 };
 
-// w as FP32 in LDS; columns past hidden hold 0 so masked lanes read zeros.
-template <typename Sh>
+// w as FP32 in LDS (columns past hidden hold 0).  FP32 rather than bf16
+// saves the widening on every use: 1.2% of the hidden-4096 backward.
+template <int COLS, int THREADS>
 __device__ __forceinline__ void stage_w(const BwdArgs& a, float* w_s, int tid, int nchunk) {
-  for (int q = tid; q < Sh::COLS / 8; q += Sh::THREADS) {
+  for (int q = tid; q < COLS / 8; q += THREADS) {
     float f[8];
     unpack8(q < nchunk ? load16(a.w + q * 8) : make_uint4(0, 0, 0, 0), f);
     store_f4(&w_s[q * 8], f[0], f[1], f[2], f[3]);
@@ -217,140 +260,158 @@ __device__ __forceinline__ void stage_w(const BwdArgs& a, float* w_s, int tid, i
   __syncthreads();
 }
 
-// One canonical block: the stream's slots in ascending order.  COMPLETE: the
-// call holds every present row of the block, so the contributions are folded
-// in registers; otherwise they are written to the spill rows.  When two row
-// buffers fit in registers the loop is software-pipelined: the next slot's
-// row is loaded before the current row's reduction and dx pass.
-// RC: rstd is not read but rebuilt from the row in the forward's order (the
-// chunk chains, one wavefront sum per 64-chunk group, the padded pairwise
-// tree over the groups; the TW wavefronts of a row swap their group sums
-// through LDS), so its bits are the saved rstd's; the contributions then
-// wait for it.
-template <int V, int TW, bool FULL, bool PLAN, bool DX, bool DW, bool COMPLETE, bool RC = false>
-struct WideBlock {
-  using Sh = WideShape<V, TW, FULL>;
+// The per-row work of a team: one row's partial sums, the team's exchange of
+// its group sums through LDS (TW > 1; the workgroup meets at a barrier, so
+// every team of the workgroup calls row() the same number of times), dx, and
+// the row's dweight contributions c = fl32(fl32(dy*x)*rstd) -- added to the
+// stream sums `acc` (a block the call holds completely) or written to the
+// spill row `srow` (a block held in part).  RC: rstd is not given but
+// rebuilt from the row in the forward's order, so its bits are the saved
+// rstd's; the contributions then wait for it.
+//
+// When V is a power of two, a wavefront's V groups h*V .. h*V+V-1 are an
+// aligned subtree of the padded tree over the row's groups, so the
+// wavefront reduces them itself and the team exchanges one value per
+// wavefront (the tree over those values, padded with +0.0, is the rest of
+// the same tree); otherwise every group sum is exchanged.
+template <int V, int TW, int TEAMS, bool FULL, bool DX, bool RC>
+struct RowOps {
+  using L = RowLanes<V, TW, FULL>;
+  static constexpr int G = L::G;
+  static constexpr bool SUBTREE = (V & (V - 1)) == 0;
+  static constexpr int XG = SUBTREE ? TW : G;       // values a team exchanges per sum
+  static constexpr int XN = RC ? 2 : 1;            // sums exchanged (dot, squares)
+  static constexpr bool XCH = TW > 1 && (DX || RC);
+  static constexpr int XCH_FLOATS = XCH ? 2 * TEAMS * XN * XG : 1;
   const BwdArgs& a;
-  int item, blk, stream, half, lane, wv, H, nchunk, base;
   const float* w_s;
-  float* dot_s;
-  float (&acc)[DW ? V * 8 : 1];
-  float* ss_s = nullptr;
-  // Lane j (< SLOTS) holds the physical row of this stream's slot j and its
-  // rstd, loaded once per block; the row loop reads them as scalars, so the
-  // only vector loads in the loop are the row data (in-order waits stay
-  // precise and the next row's loads stay in flight).
-  int slot_p = -1;
-  float slot_r = 0.0f;
+  float* xch;     // [2][TEAMS][XN][G]
+  L ln;
+  int team, H;
 
-  __device__ __forceinline__ void load_slots() {
-    // every lane loads (lanes past SLOTS repeat a slot): no divergent memory ops
-    slot_p = slot_row_t<PLAN>(a, item, blk, stream + Sh::S * (lane & (Sh::SLOTS - 1)));
-    if (!RC) slot_r = a.rstd[slot_p >= 0 ? slot_p : 0];
-  }
-  // Consume both slot registers before the row loop: the compiler then waits
-  // for their loads once, instead of inserting a full vmcnt(0) wait inside
-  // the loop (which would also wait for the prefetched row).  Called after
-  // the first row's loads are issued, so that row is in flight meanwhile.
-  __device__ __forceinline__ void settle_slots() { asm volatile("" : "+v"(slot_p), "+v"(slot_r)); }
-  __device__ __forceinline__ int row_of(int i) const { return __builtin_amdgcn_readlane(slot_p, i); }
-  __device__ __forceinline__ float rstd_of(int i) const {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(slot_r), i));
-  }
-
-  __device__ __forceinline__ bool in_row(int k) const {
-    return FULL || (half * V + k) * 64 + lane < nchunk;
-  }
-
-  // The loads are issued whether or not the slot is present (an absent slot
-  // reads row 0 and its data is never used): with the same number of memory
-  // operations on every path, the compiler's wait counts stay exact and the
-  // next row's loads remain in flight while the current row is processed.
   __device__ __forceinline__ void load(int p, uint4 (&xv)[V], uint4 (&dv)[V]) const {
+    // Loads are issued whether or not the slot is present (an absent slot
+    // reads row 0) and whether or not the lane's chunk is inside the row (a
+    // lane past the row's end reads the row's first chunk); mask() discards
+    // what they read.  The same memory operations on every path and in every
+    // lane keep the compiler's wait counts exact, so the rows issued ahead
+    // stay in flight while this one is processed.
     const int row = p >= 0 ? p : 0;
-    const uint16_t* xr = a.x + (int64_t)row * H + base;
-    const uint16_t* dr = a.dy + (int64_t)row * H + base;
+    const uint16_t* xr = a.x + (int64_t)row * H + ln.base;
+    const uint16_t* dr = a.dy + (int64_t)row * H + ln.base;
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-      xv[k] = in_row(k) ? load16_stream(xr + k * 512) : make_uint4(0, 0, 0, 0);
-      dv[k] = in_row(k) ? load16_stream(dr + k * 512) : make_uint4(0, 0, 0, 0);
+      const int off = ln.in_row(k) ? k * 512 : -ln.base;
+      xv[k] = load16_stream(xr + off);
+      dv[k] = load16_stream(dr + off);
+    }
+  }
+  // Zero the chunks of lanes past the row's end (after the data has arrived).
+  __device__ __forceinline__ void mask(uint4 (&xv)[V], uint4 (&dv)[V]) const {
+    if (FULL) return;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      if (!ln.in_row(k)) {
+        xv[k] = make_uint4(0, 0, 0, 0);
+        dv[k] = make_uint4(0, 0, 0, 0);
+      }
     }
   }
 
-  __device__ __forceinline__ void process(int i, int p, uint4 (&xv)[V], uint4 (&dv)[V], float r) {
-    const int s = stream + Sh::S * i;
-    float dot = 0.0f, ss = 0.0f;
-    // RC: the chunk chains of the forward's sum of squares; chunk k of this
-    // lane is lane `lane` of chunk group half*V + k
-    float sq[RC ? V : 1];
+  // DW: contributions wanted; COMPLETE: into acc, else into srow.
+  template <bool DW, bool COMPLETE>
+  __device__ __forceinline__ void row(int j, int p, uint4 (&xv)[V], uint4 (&dv)[V], float r,
+                                      float (&acc)[DW ? V * 8 : 1], float* srow) const {
+    mask(xv, dv);
+    // the group sums of this wavefront's chunk groups: kept one per group,
+    // or (a power-of-two count) folded into the subtree as they come
+    float d[SUBTREE ? 1 : V], sq[SUBTREE ? 1 : V];
+    RunningTree<SUBTREE ? V : 1> td, ts;
 #pragma unroll
-    for (int k = 0; k < (RC ? V : 1); ++k) sq[k] = 0.0f;
-    if (p >= 0) {
-      float* srow = COMPLETE ? nullptr : a.S + ((int64_t)blk * kBlockRows + s) * H + base;
-#pragma unroll
-      for (int k = 0; k < V; ++k) {
-        float xf[8], df[8];
+    for (int k = 0; k < V; ++k) {
+      float dk = 0.0f, sk = 0.0f;
+      if (p >= 0) {
+        float xf[8], df[8], c[8];
         unpack8(xv[k], xf);
         unpack8(dv[k], df);
-        float c[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float pr = df[e] * xf[e];          // exact: two bf16 significands
-          if (DX) dot = fmaf(pr, w_s[base + k * 512 + e], dot);
-          if (RC) sq[RC ? k : 0] = fmaf(xf[e], xf[e], sq[RC ? k : 0]);
+          if (DX) dk = fmaf(pr, w_s[ln.base + k * 512 + e], dk);
+          if (RC) sk = fmaf(xf[e], xf[e], sk);
           c[e] = pr * r;                           // the row's contribution, rounded once
           if (!RC && DW && COMPLETE) acc[k * 8 + e] = acc[k * 8 + e] + c[e];
         }
-        if (!RC && DW && !COMPLETE && in_row(k)) {
+        if (!RC && DW && !COMPLETE && ln.in_row(k)) {
           store_f4_stream(srow + k * 512, c[0], c[1], c[2], c[3]);
           store_f4_stream(srow + k * 512 + 4, c[4], c[5], c[6], c[7]);
         }
       }
-      if (TW == 1) {
-        if (DX) dot = wave_sum(dot);
-        if (RC) {
-          // this wavefront holds every chunk group of the row
-#pragma unroll
-          for (int k = 0; k < (RC ? V : 1); ++k) sq[k] = wave_sum(sq[k]);
-          ss = pad_tree(sq);
-        }
+      if constexpr (SUBTREE) {
+        if (DX) td.push(k, wave_sum(dk));
+        if (RC) ts.push(k, wave_sum(sk));
+      } else {
+        if (DX) d[k] = wave_sum(dk);
+        if (RC) sq[k] = wave_sum(sk);
       }
     }
+    float dot = 0.0f;
     if (DX || RC) {
-      if (TW > 1) {
-        // the row's wavefronts exchange their partial sums through LDS
-        if (DX) dot = wave_sum(dot);
+      float ss = 0.0f;
+      if constexpr (!XCH) {
+        // this wavefront holds every chunk group of the row
+        if constexpr (SUBTREE) {
+          if (DX) dot = td.root();
+          if (RC) ss = ts.root();
+        } else {
+          if (DX) dot = pad_tree(d);
+          if (RC) ss = pad_tree(sq);
+        }
+      } else if constexpr (SUBTREE) {
+        // this wavefront's subtree, then the tree over the team's subtrees
+        float* xs = xch + ((j & 1) * TEAMS + team) * XN * XG;
+        if (ln.lane == 0) {
+          if (DX) xs[ln.half] = td.root();
+          if (RC) xs[(XN - 1) * XG + ln.half] = ts.root();
+        }
+        __syncthreads();
+        float g[XG];
+        if (DX) {
+#pragma unroll
+          for (int k = 0; k < XG; ++k) g[k] = xs[k];
+          dot = pad_tree(g);
+        }
         if (RC) {
 #pragma unroll
-          for (int k = 0; k < (RC ? V : 1); ++k) sq[k] = wave_sum(sq[k]);
+          for (int k = 0; k < XG; ++k) g[k] = xs[(XN - 1) * XG + k];
+          ss = pad_tree(g);
         }
-        if (lane == 0) {
-          if (DX) dot_s[(i & 1) * 16 + wv] = dot;
-          if (RC) {
+      } else {
+        float* xs = xch + ((j & 1) * TEAMS + team) * XN * XG;
+        if (ln.lane == 0) {
 #pragma unroll
-            for (int k = 0; k < (RC ? V : 1); ++k)
-              ss_s[((i & 1) * Sh::S + stream) * (TW * V) + half * V + k] = sq[k];
+          for (int k = 0; k < V; ++k) {
+            if (DX) xs[ln.half * V + k] = d[k];
+            if (RC) xs[(XN - 1) * XG + ln.half * V + k] = sq[k];
           }
         }
         __syncthreads();
+        // every chunk group of the row, in group order
+        float g[XG];
         if (DX) {
-          const float* d = &dot_s[(i & 1) * 16 + stream * TW];
-          dot = TW == 2 ? d[0] + d[1] : (d[0] + d[1]) + (d[2 % TW] + d[3 % TW]);
+#pragma unroll
+          for (int k = 0; k < XG; ++k) g[k] = xs[k];
+          dot = pad_tree(g);
         }
         if (RC) {
-          // every chunk group of the row, in group order (groups past the
-          // row's end hold +0.0, which the padded tree absorbs)
-          float g[RC ? TW * V : 1];
 #pragma unroll
-          for (int k = 0; k < (RC ? TW * V : 1); ++k)
-            g[k] = ss_s[((i & 1) * Sh::S + stream) * (TW * V) + k];
+          for (int k = 0; k < XG; ++k) g[k] = xs[(XN - 1) * XG + k];
           ss = pad_tree(g);
         }
       }
       if (RC) r = p >= 0 ? rsqrtf(ss / (float)H + a.eps) : 0.0f;
     }
     if (RC && DW && p >= 0) {
-      float* srow = COMPLETE ? nullptr : a.S + ((int64_t)blk * kBlockRows + s) * H + base;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
         float xf[8], df[8], c[8];
@@ -361,159 +422,81 @@ struct WideBlock {
           c[e] = (df[e] * xf[e]) * r;
           if (COMPLETE) acc[k * 8 + e] = acc[k * 8 + e] + c[e];
         }
-        if (!COMPLETE && in_row(k)) {
+        if (!COMPLETE && ln.in_row(k)) {
           store_f4_stream(srow + k * 512, c[0], c[1], c[2], c[3]);
           store_f4_stream(srow + k * 512 + 4, c[4], c[5], c[6], c[7]);
         }
       }
     }
-    if (DX) {
-      if (p >= 0) {
-        const float kk = ((r * r) * r) * (dot / (float)H);
-        uint16_t* xo = a.dx + (int64_t)p * H + base;
-        compiler_fence();
+    if (DX && p >= 0) {
+      const float kk = ((r * r) * r) * (dot / (float)H);
+      uint16_t* xo = a.dx + (int64_t)p * H + ln.base;
+      // re-derive the FP32 values from the packed registers instead of
+      // keeping twice as many registers live across the exchange
+      compiler_fence();
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-          launder(xv[k]);
-          launder(dv[k]);
-        }
+      for (int k = 0; k < V; ++k) {
+        launder(xv[k]);
+        launder(dv[k]);
+      }
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-          if (in_row(k)) {
-            float xf[8], df[8], o[8];
-            unpack8(xv[k], xf);
-            unpack8(dv[k], df);
+      for (int k = 0; k < V; ++k) {
+        if (ln.in_row(k)) {
+          float xf[8], df[8], o[8];
+          unpack8(xv[k], xf);
+          unpack8(dv[k], df);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float g = df[e] * w_s[base + k * 512 + e];
-              o[e] = fmaf(-xf[e], kk, r * g);
-            }
-            store16_stream(xo + k * 512, pack8(o));
+          for (int e = 0; e < 8; ++e) {
+            const float g = df[e] * w_s[ln.base + k * 512 + e];
+            o[e] = fmaf(-xf[e], kk, r * g);
           }
+          store16_stream(xo + k * 512, pack8(o));
         }
       }
-    }
-  }
-
-  // Two row buffers fit in the register file only up to 8 chunks per lane
-  // without masks (4 when rstd is rebuilt, which keeps the row for a second
-  // pass); wider or masked rows are processed one at a time.
-  static constexpr bool PIPE = FULL && V <= (RC ? 4 : 8);
-
-  __device__ __forceinline__ void run() {
-    load_slots();
-    if constexpr (PIPE) run_pipelined();
-    else run_sequential();
-  }
-
-  __device__ __forceinline__ void run_sequential() {
-    settle_slots();
-    for (int i = 0; i < Sh::SLOTS; ++i) {
-      uint4 xv[V], dv[V];
-      const int p = row_of(i);
-      load(p, xv, dv);
-      process(i, p, xv, dv, rstd_of(i));
-    }
-  }
-
-  __device__ __forceinline__ void run_pipelined() {
-    uint4 xa[V], da[V];
-    int pa = row_of(0);
-    load(pa, xa, da);
-    settle_slots();
-    run_from(xa, da, pa, -1, false);
-  }
-
-  // The pipelined slot loop with slot 0's row already issued into (xa, da).
-  // When `more`, the last step issues the first row of the workgroup's next
-  // block (lane 0 of `next_slots`, read only there) into (xa, da), so that
-  // row is in flight across this block's stream tree; otherwise it issues a
-  // dummy load of row 0 (never used) to keep the wait counts exact.
-  __device__ __forceinline__ void run_from(uint4 (&xa)[V], uint4 (&da)[V], int pa, int next_slots,
-                                           bool more) {
-    static_assert(Sh::SLOTS % 2 == 0, "slots per stream must be even");
-    uint4 xb[V], db[V];
-#pragma unroll
-    for (int i = 0; i < Sh::SLOTS; i += 2) {
-      const int pb = row_of(i + 1);
-      load(pb, xb, db);
-      process(i, pa, xa, da, rstd_of(i));
-      if (i + 2 < Sh::SLOTS) pa = row_of(i + 2);
-      else pa = more ? __builtin_amdgcn_readlane(next_slots, 0) : -1;
-      load(pa, xa, da);
-      process(i + 1, pb, xb, db, rstd_of(i + 1));
     }
   }
 };
 
-// The in-block stream tree, 1024 columns at a time: every stream stores its
-// sums for the tile, then each thread reduces its columns into P[blk].
-// LOOP: the workgroup folds several blocks, so tile_s may still be read for
-// the previous block when the first tile is stored (a barrier comes first).
-template <int V, int TW, bool FULL, bool LOOP>
-__device__ __forceinline__ void block_partial(const BwdArgs& a, int blk, int H, int tid, int stream,
-                                              int half, int lane, const float (&acc)[V * 8],
-                                              float* tile_s) {
-  using Sh = WideShape<V, TW, FULL>;
-  float* Pb = a.P + (int64_t)blk * H;
-#pragma unroll
-  for (int t = 0; t < Sh::NTILE; ++t) {
-    if (LOOP || t > 0) __syncthreads();   // tile_s is free again
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-      const int K = half * V + k;   // 512-column chunk index within the row
-      if ((K >> 1) == t) {
-        float* dst = &tile_s[stream * 1024 + ((K & 1) * 64 + lane) * 8];
-        store_f4(dst, acc[k * 8 + 0], acc[k * 8 + 1], acc[k * 8 + 2], acc[k * 8 + 3]);
-        store_f4(dst + 4, acc[k * 8 + 4], acc[k * 8 + 5], acc[k * 8 + 6], acc[k * 8 + 7]);
-      }
-    }
-    __syncthreads();
-    for (int c = tid; c < 1024; c += Sh::THREADS) {
-      const int col = t * 1024 + c;
-      if (col < H)
-        Pb[col] = stream_tree4(tile_s[c], tile_s[1024 + c], tile_s[2048 + c], tile_s[3072 + c]);
-    }
-  }
-}
-
-// Whether the fused backward loops over several work items per workgroup:
-// the pipelined two-wavefront kernels up to 4 chunks per lane (hidden 2048,
-// 3072, 4096).  Measured at hidden 4096 the loop saves about 1% of the
-// backward; at 5120 the loop's extra registers cost more than the block
-// hand-over it hides, and the one-block kernel is kept there and above.
-template <int V, int TW, bool FULL, bool RC>
-constexpr bool wide_persistent() {
-  return FULL && TW == 2 && V <= 4;
-}
-
-// Workgroups 0 .. item_groups-1 each take work items g, g + item_groups, ...
-// (for the looping kernels item_groups is at most what the chip holds at
-// once, so every workgroup is resident and they all end after the same
-// number of items; otherwise it is the item count, one item each); the
-// workgroups after them zero padding rows.  Which workgroup takes an item
-// changes nothing in its arithmetic.  In the looping kernels the first row
-// of a workgroup's next item is loaded during the last step of the current
-// one, so it is in flight across the block's stream tree.
-template <int V, int TW, bool FULL, bool PLAN, bool DX, bool DW, bool RC>
-__global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
-  using Sh = WideShape<V, TW, FULL>;
-  using BlkC = WideBlock<V, TW, FULL, PLAN, DX, DW, true, RC>;    // complete block: fold
-  using BlkS = WideBlock<V, TW, FULL, PLAN, DX, DW, false, RC>;   // partial block: spill
-  constexpr bool PIPE = BlkC::PIPE;
-  constexpr bool LOOP = wide_persistent<V, TW, FULL, RC>();
-  static_assert(!LOOP || PIPE, "the looping kernels are the pipelined ones");
-  __shared__ float w_s[DX ? Sh::COLS : 1];
-  __shared__ float tile_s[DW ? kStreams * 1024 : 1];
-  __shared__ float dot_s[(DX && TW > 1) ? 2 * 16 : 1];
-  __shared__ float ss_s[(RC && TW > 1) ? 2 * kStreams * TW * V : 1];
+// ------------------------------------------------------- fused backward
+// One workgroup owns each canonical block of 64 logical rows it is given and
+// runs dx and the dweight fold in one pass over x and dy.  The workgroup is
+// TEAMS teams of TW wavefronts, each team on one row at a time:
+//   TEAMS = 2 (hidden > 1024): the block is walked in two passes, streams
+//     {0, 1} then {2, 3}; at step i of pass p team t takes slot 4i + 2p + t,
+//     i.e. its stream 2p + t in ascending slot order.  At the end of pass 0
+//     team 0 keeps q0 + q1 in registers; at the end of pass 1 it adds
+//     q2 + q3 and writes P[b] = (q0 + q1) + (q2 + q3).
+//   TEAMS = 4 (hidden <= 1024): one pass, team t on stream t.
+// Team 0 receives the other teams' stream sums through LDS.  Two rows in
+// flight per workgroup with several wavefronts per row, one resident
+// workgroup per compute unit walking its blocks in turn, and the next rows
+// prefetched PD steps ahead across pass and block boundaries measured about
+// 5% faster than one row per stream (four rows in flight) on the hidden-4096
+// backward, for the same arithmetic.
+template <int V, int TW, int TEAMS, int PD, bool FULL, bool PLAN, bool DX, bool DW, bool RC>
+__global__ __launch_bounds__(64 * TW * TEAMS) void bwd_team_kernel(BwdArgs a) {
+  using Ops = RowOps<V, TW, TEAMS, FULL, DX, RC>;
+  using L = typename Ops::L;
+  constexpr int COLS = L::COLS;
+  constexpr int WAVES = TW * TEAMS;
+  constexpr int THREADS = 64 * WAVES;
+  constexpr int STEPS = kBlockRows / TEAMS;   // slots a team takes per block
+  constexpr int R = PD + 1;                   // row buffers in the ring
+  static_assert(TEAMS == 2 || TEAMS == 4, "two or four teams");
+  static_assert(STEPS % R == 0 && 16 % R == 0, "the ring must divide a pass");
+  // TEAMS = 2 keeps q0 + q1 across the block's second pass: in registers,
+  // or in LDS when a wavefront holds 4 or more chunk groups per row
+  constexpr bool HQ_LDS = TEAMS == 2 && V >= 4;
+  __shared__ float w_s[DX ? COLS : 1];
+  __shared__ float q_s[DW ? (TEAMS / 2 + (HQ_LDS ? 1 : 0)) * COLS : 1];
+  __shared__ float xch[Ops::XCH_FLOATS];
 
   const int tid = threadIdx.x;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int stream = wv / TW;
+  const int team = wv / TW;
   const int half = wv % TW;
-  const int H = FULL ? Sh::COLS : a.hidden;
+  const int H = FULL ? COLS : a.hidden;
   const int nchunk = H >> 3;
   const int n_items = a.plan.n_items;
   const int groups = a.item_groups;
@@ -521,7 +504,7 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
   if ((int)blockIdx.x >= groups) {
     // padding rows: dx = 0, nothing read (one row per wavefront)
     if (DX) {
-      const int idx = ((int)blockIdx.x - groups) * Sh::WAVES + wv;
+      const int idx = ((int)blockIdx.x - groups) * WAVES + wv;
       if (idx < a.plan.n_pad) {
         uint16_t* d = a.dx + (int64_t)a.plan.pad_rows[idx] * H;
         for (int q = lane; q < nchunk; q += 64) store16_stream(d + q * 8, make_uint4(0, 0, 0, 0));
@@ -531,10 +514,11 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
   }
   int item = blockIdx.x;
   if (item >= n_items) return;
+  if (DX) stage_w<COLS, THREADS>(a, w_s, tid, nchunk);
 
-  if (DX) stage_w<Sh>(a, w_s, tid, nchunk);
+  const L ln{lane, half, nchunk, (half * V * 64 + lane) * 8};
+  const Ops ops{a, w_s, xch, ln, team, H};
 
-  // item -> (canonical block, does the call hold all of its present rows)
   auto info_of = [&](int it, int& blk, bool& complete) {
     if (PLAN) {
       const int info = a.plan.item_info[it];
@@ -545,62 +529,179 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
       complete = true;
     }
   };
+  // step j of a team: pass j / 16, slot 4*(j % 16) + TEAMS*(j / 16) + team
+  auto slot_of = [&](int j) { return 4 * (j & 15) + TEAMS * (j >> 4) + team; };
+  // lane j (< STEPS) holds the physical row and rstd of step j; the step
+  // loop reads them as scalars, so its only vector loads are the rows
+  auto slots_of = [&](int it, int blk, int& sp, float& sr) {
+    sp = slot_row_t<PLAN>(a, it, blk, slot_of(lane & (STEPS - 1)));
+    if (!RC) sr = a.rstd[sp >= 0 ? sp : 0];
+  };
 
   float acc[DW ? V * 8 : 1];
-  const int base = half * V * 512 + lane * 8;      // this lane's first column
-  int blk;
-  bool complete;
-  info_of(item, blk, complete);
-  if constexpr (!LOOP) {
-    // one item per workgroup
+  float hq[(DW && TEAMS == 2 && !HQ_LDS) ? V * 8 : 1];
+  // Stream sums (or their pairs) handed between teams through q_s: the
+  // sending team writes, all meet at a barrier, the receiving team adds.
+  auto hand = [&](int region, bool send) {
+    if (send) {
 #pragma unroll
-    for (int i = 0; i < (DW ? V * 8 : 1); ++i) acc[i] = 0.0f;
-    if (!DW || complete) {
-      BlkC{a, item, blk, stream, half, lane, wv, H, nchunk, base, w_s, dot_s, acc, ss_s}.run();
-      if constexpr (DW) block_partial<V, TW, FULL, LOOP>(a, blk, H, tid, stream, half, lane, acc, tile_s);
-    } else {
-      BlkS{a, item, blk, stream, half, lane, wv, H, nchunk, base, w_s, dot_s, acc, ss_s}.run();
+      for (int k = 0; k < V; ++k) {
+        float* dst = &q_s[region * COLS + ln.base + k * 512];
+        store_f4(dst, acc[k * 8 + 0], acc[k * 8 + 1], acc[k * 8 + 2], acc[k * 8 + 3]);
+        store_f4(dst + 4, acc[k * 8 + 4], acc[k * 8 + 5], acc[k * 8 + 6], acc[k * 8 + 7]);
+      }
     }
-    return;
-  }
-  BlkC cur{a, item, blk, stream, half, lane, wv, H, nchunk, base, w_s, dot_s, acc, ss_s};
-  cur.load_slots();
-  uint4 xa[V], da[V];
-  int pa = cur.row_of(0);
-  cur.load(pa, xa, da);
-  cur.settle_slots();
+    __syncthreads();
+  };
+  auto hand_own = [&](int region) {
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      float* dst = &q_s[region * COLS + ln.base + k * 512];
+      store_f4(dst, acc[k * 8 + 0], acc[k * 8 + 1], acc[k * 8 + 2], acc[k * 8 + 3]);
+      store_f4(dst + 4, acc[k * 8 + 4], acc[k * 8 + 5], acc[k * 8 + 6], acc[k * 8 + 7]);
+    }
+  };
+  auto load_own = [&](int region, float (&h)[V * 8]) {
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const float4 lo = *reinterpret_cast<const float4*>(&q_s[region * COLS + ln.base + k * 512]);
+      const float4 hi = *reinterpret_cast<const float4*>(&q_s[region * COLS + ln.base + k * 512 + 4]);
+      h[k * 8 + 0] = lo.x; h[k * 8 + 1] = lo.y; h[k * 8 + 2] = lo.z; h[k * 8 + 3] = lo.w;
+      h[k * 8 + 4] = hi.x; h[k * 8 + 5] = hi.y; h[k * 8 + 6] = hi.z; h[k * 8 + 7] = hi.w;
+    }
+  };
+  auto take = [&](int region) {
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const float4 lo = *reinterpret_cast<const float4*>(&q_s[region * COLS + ln.base + k * 512]);
+      const float4 hi = *reinterpret_cast<const float4*>(&q_s[region * COLS + ln.base + k * 512 + 4]);
+      acc[k * 8 + 0] = acc[k * 8 + 0] + lo.x;
+      acc[k * 8 + 1] = acc[k * 8 + 1] + lo.y;
+      acc[k * 8 + 2] = acc[k * 8 + 2] + lo.z;
+      acc[k * 8 + 3] = acc[k * 8 + 3] + lo.w;
+      acc[k * 8 + 4] = acc[k * 8 + 4] + hi.x;
+      acc[k * 8 + 5] = acc[k * 8 + 5] + hi.y;
+      acc[k * 8 + 6] = acc[k * 8 + 6] + hi.z;
+      acc[k * 8 + 7] = acc[k * 8 + 7] + hi.w;
+    }
+  };
+  auto store_p = [&](int blk) {
+    float* Pb = a.P + (int64_t)blk * H + ln.base;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      if (ln.in_row(k)) {
+        store_f4(Pb + k * 512, acc[k * 8 + 0], acc[k * 8 + 1], acc[k * 8 + 2], acc[k * 8 + 3]);
+        store_f4(Pb + k * 512 + 4, acc[k * 8 + 4], acc[k * 8 + 5], acc[k * 8 + 6], acc[k * 8 + 7]);
+      }
+    }
+  };
+  // End of a pass over a complete block.
+  //   TEAMS = 4 (streams 0..3 on teams 0..3): teams 1 and 3 hand q1, q3 to
+  //     teams 0 and 2, which form q0 + q1 and q2 + q3; team 2 hands q2 + q3
+  //     to team 0: P[b] = (q0 + q1) + (q2 + q3).
+  //   TEAMS = 2: pass 0 (streams 0, 1): team 1 hands q1 to team 0, which
+  //     keeps q0 + q1 in registers; pass 1 (streams 2, 3): team 0 forms
+  //     q2 + q3 the same way and writes P[b] = (q0 + q1) + (q2 + q3).
+  auto pass_end = [&](int pass, int blk) {
+    if (TEAMS == 4) {
+      hand(team >> 1, team & 1);
+      if ((team & 1) == 0) take(team >> 1);
+      hand(1, team == 2);
+      if (team == 0) {
+        take(1);
+        store_p(blk);
+      }
+    } else {
+      hand(0, team == 1);
+      if (team == 0) {
+        take(0);
+        if constexpr (HQ_LDS) {
+          // region 1 is written and read by this team's own lanes only
+          if (pass == 0) {
+            hand_own(1);
+          } else {
+            float h[V * 8];
+            load_own(1, h);
+#pragma unroll
+            for (int i = 0; i < V * 8; ++i) acc[i] = h[i] + acc[i];
+            store_p(blk);
+          }
+        } else if (pass == 0) {
+#pragma unroll
+          for (int i = 0; i < V * 8; ++i) hq[(TEAMS == 2) ? i : 0] = acc[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < V * 8; ++i) acc[i] = hq[(TEAMS == 2) ? i : 0] + acc[i];
+          store_p(blk);
+        }
+      }
+    }
+    __syncthreads();   // q_s is free again
+#pragma unroll
+    for (int i = 0; i < V * 8; ++i) acc[i] = 0.0f;
+  };
+
+  int blk, sp, nsp = -1;
+  bool complete;
+  float sr = 0.0f, nsr = 0.0f;
+  info_of(item, blk, complete);
+  slots_of(item, blk, sp, sr);
+  uint4 xb[R][V], db[R][V];
+#pragma unroll
+  for (int j = 0; j < PD; ++j) ops.load(__builtin_amdgcn_readlane(sp, j), xb[j], db[j]);
+  // consume the slot registers once here, so the compiler does not insert a
+  // full wait (which would also wait for the rows in flight) in the loop
+  asm volatile("" : "+v"(sp), "+v"(sr));
+#pragma unroll
+  for (int i = 0; i < (DW ? V * 8 : 1); ++i) acc[i] = 0.0f;
+
+  // One block's steps.  The last PD steps issue the first rows of the
+  // workgroup's next block (or, past the last one, dummy loads of row 0 that
+  // keep the wait counts exact).
+  auto run = [&](auto complete_tag, int nblk_more, int nxt_sp) {
+    constexpr bool CPL = decltype(complete_tag)::value;
+#pragma unroll
+    for (int j0 = 0; j0 < STEPS; j0 += R) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int j = j0 + u;
+        const int jn = j + PD;
+        int pj;
+        if (jn < STEPS) pj = __builtin_amdgcn_readlane(sp, jn);
+        else pj = nblk_more ? __builtin_amdgcn_readlane(nxt_sp, jn - STEPS) : -1;
+        ops.load(pj, xb[(u + PD) % R], db[(u + PD) % R]);
+        const int p = __builtin_amdgcn_readlane(sp, j);
+        const float r = RC ? 0.0f : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sr), j));
+        float* srow = nullptr;
+        if (DW && !CPL) srow = a.S + ((int64_t)blk * kBlockRows + slot_of(j)) * H + ln.base;
+        ops.template row<DW, CPL>(j, p, xb[u], db[u], r, acc, srow);
+        if (DW && CPL && (j & 15) == 15) pass_end(j >> 4, blk);
+        // keep the scheduler from interleaving steps: the row loads are
+        // already issued PD steps ahead, and moving work across steps only
+        // raises register use
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   while (true) {
     const int nxt = item + groups;
     const bool more = nxt < n_items;
     int nblk = 0;
     bool ncomplete = true;
-    BlkC nx{a, nxt, 0, stream, half, lane, wv, H, nchunk, base, w_s, dot_s, acc, ss_s};
     if (more) {
       info_of(nxt, nblk, ncomplete);
-      nx.blk = nblk;
-      nx.load_slots();
+      slots_of(nxt, nblk, nsp, nsr);
     }
-#pragma unroll
-    for (int i = 0; i < (DW ? V * 8 : 1); ++i) acc[i] = 0.0f;
-    if (!DW || complete) {
-      cur.run_from(xa, da, pa, nx.slot_p, more);
-      if constexpr (DW) block_partial<V, TW, FULL, LOOP>(a, blk, H, tid, stream, half, lane, acc, tile_s);
-    } else {
-      BlkS sp{a, item, blk, stream, half, lane, wv, H, nchunk, base, w_s, dot_s, acc, ss_s};
-      sp.slot_p = cur.slot_p;
-      sp.slot_r = cur.slot_r;
-      sp.run_from(xa, da, pa, nx.slot_p, more);
-    }
+    if (!PLAN || complete) run(std::true_type{}, more, nsp);
+    else run(std::false_type{}, more, nsp);
     if (!more) break;
     item = nxt;
     blk = nblk;
     complete = ncomplete;
-    cur.item = nxt;
-    cur.blk = nblk;
-    cur.slot_p = nx.slot_p;
-    cur.slot_r = nx.slot_r;
-    pa = cur.row_of(0);   // its loads were issued in the last step
-    cur.settle_slots();
+    sp = nsp;
+    sr = nsr;
+    asm volatile("" : "+v"(sp), "+v"(sr));
   }
 }
 
@@ -608,10 +709,10 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
 // A call that touches few canonical blocks would leave most compute units
 // idle in the fused kernel (one workgroup per block).  It runs two passes
 // instead, with enough workgroups for the whole chip between them:
-//   dx rows (dx_rows_part): dx, four physical rows per workgroup step,
-//     through the very same per-row code as the fused kernel (WideBlock's
-//     load + process with the dweight part compiled out), so every dx bit
-//     equals the fused kernel's;
+//   dx rows (dx_rows_part): dx, two physical rows per workgroup step, one per
+//     team, through the same per-row code as the fused kernel (RowOps with
+//     the dweight part compiled out); the dot order does not depend on the
+//     row shape, so every dx bit equals the fused kernel's;
 //   dweight columns (dw_cols_part): the dweight contributions and the
 //     in-block stream fold of one canonical block over 512 columns, with the
 //     same operations in the same order as the fused kernel, so the block
@@ -622,40 +723,42 @@ __global__ __launch_bounds__(256 * TW) void bwd_wide_kernel(BwdArgs a) {
 // second time; for the calls that take this path they are small enough to
 // be served largely from the last-level cache.
 template <int V, int TW, bool FULL, bool PLAN>
-__device__ __forceinline__ void dx_rows_part(const BwdArgs& a, float* w_s, float* dot_s, int64_t wg,
+__device__ __forceinline__ void dx_rows_part(const BwdArgs& a, float* w_s, float* xch, int64_t wg,
                                              int64_t n_wg) {
-  using Sh = WideShape<V, TW, FULL>;
+  constexpr int TEAMS = 2;
+  using Ops = RowOps<V, TW, TEAMS, FULL, true, false>;
+  using L = typename Ops::L;
+  constexpr int THREADS = 64 * TW * TEAMS;
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int stream = wv / TW;          // the workgroup's row slot (0..3)
+  const int team = wv / TW;
   const int half = wv % TW;
-  const int H = FULL ? Sh::COLS : a.hidden;
+  const int H = FULL ? L::COLS : a.hidden;
   const int nchunk = H >> 3;
-  stage_w<Sh>(a, w_s, tid, nchunk);
+  stage_w<L::COLS, THREADS>(a, w_s, tid, nchunk);
+  const L ln{lane, half, nchunk, (half * V * 64 + lane) * 8};
+  const Ops ops{a, w_s, xch, ln, team, H};
   float acc[1];
-  const int base = half * V * 512 + lane * 8;
-  WideBlock<V, TW, FULL, PLAN, true, false, true> wb{a, 0, 0, stream, half, lane, wv, H, nchunk,
-                                                     base, w_s, dot_s, acc};
-  const int64_t step = n_wg * Sh::S;
+  const int64_t step = n_wg * TEAMS;
   int i = 0;
-  // the trip count is the same for every wavefront of the workgroup (the
-  // TW > 1 dot exchange synchronises the workgroup once per row)
-  for (int64_t r0 = wg * Sh::S; r0 < a.rows; r0 += step, ++i) {
-    const int64_t row = r0 + stream;
+  // the trip count is the same for every team of the workgroup (the row's
+  // exchange synchronises the workgroup once per step)
+  for (int64_t r0 = wg * TEAMS; r0 < a.rows; r0 += step, ++i) {
+    const int64_t row = r0 + team;
     int p = row < a.rows ? (int)row : -1;
     if (PLAN && p >= 0 && a.plan.row_logical[p] < 0) {
       // padding row: dx = 0, nothing read
-      uint16_t* d = a.dx + (int64_t)p * H + base;
+      uint16_t* d = a.dx + (int64_t)p * H + ln.base;
 #pragma unroll
       for (int k = 0; k < V; ++k)
-        if (wb.in_row(k)) store16_stream(d + k * 512, make_uint4(0, 0, 0, 0));
+        if (ln.in_row(k)) store16_stream(d + k * 512, make_uint4(0, 0, 0, 0));
       p = -1;
     }
     const float r = p >= 0 ? a.rstd[p] : 0.0f;
     uint4 xv[V], dv[V];
-    wb.load(p, xv, dv);
-    wb.process(i, p, xv, dv, r);
+    ops.load(p, xv, dv);
+    ops.template row<false, true>(i, p, xv, dv, r, acc, nullptr);
   }
 }
 
@@ -746,25 +849,30 @@ __device__ __forceinline__ void dw_cols_part(const BwdArgs& a, float (*q_s)[512]
 }
 
 // Both passes in one launch.  Workgroups 0 .. n_cols_wg-1 fold column units
-// (TW units per workgroup: wavefronts 4u .. 4u+3 take unit TW*wg + u of the
-// n_units = items x column slices); the following n_rows_wg workgroups
+// (TW/2 units per workgroup: wavefronts 4u .. 4u+3 take unit (TW/2)*wg + u of
+// the n_units = items x column slices); the following n_rows_wg workgroups
 // compute dx rows.  Either list may be empty (dx alone, contributions alone).
 template <int V, int TW, bool FULL, bool PLAN>
-__global__ __launch_bounds__(256 * TW) void bwd_split_kernel(BwdArgs a, int n_cols_wg, int n_units,
+__global__ __launch_bounds__(128 * TW) void bwd_split_kernel(BwdArgs a, int n_cols_wg, int n_units,
                                                              int n_slices, int n_rows_wg) {
-  using Sh = WideShape<V, TW, FULL>;
-  constexpr int ROWS_LDS = Sh::COLS + 2 * 16;
-  constexpr int COLS_LDS = TW * (kStreams - 1) * 512;
-  __shared__ float lds[ROWS_LDS > COLS_LDS ? ROWS_LDS : COLS_LDS];
+  using Ops = RowOps<V, TW, 2, FULL, true, false>;
+  constexpr int COLS = Ops::L::COLS;
+  constexpr int UNITS = TW / 2;
+  static_assert(TW % 2 == 0, "column units take four wavefronts");
+  constexpr int ROWS_LDS = COLS + Ops::XCH_FLOATS;   // w, then the exchange
+  constexpr int COLS_LDS = UNITS * (kStreams - 1) * 512;
+  constexpr int LDS = ROWS_LDS > COLS_LDS ? ROWS_LDS : COLS_LDS;
+  __shared__ float4 lds4[(LDS + 3) / 4];
+  float* lds = reinterpret_cast<float*>(lds4);
   const int wg = blockIdx.x;
   if (wg < n_cols_wg) {
     const int u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);   // the workgroup's unit
-    const int unit = wg * TW + u;
+    const int unit = wg * UNITS + u;
     const bool live = unit < n_units;
     dw_cols_part<PLAN>(a, reinterpret_cast<float (*)[512]>(lds + u * (kStreams - 1) * 512),
                        live ? unit / n_slices : 0, live ? unit % n_slices : 0, u * kStreams, live);
   } else {
-    dx_rows_part<V, TW, FULL, PLAN>(a, lds, lds + Sh::COLS, wg - n_cols_wg, n_rows_wg);
+    dx_rows_part<V, TW, FULL, PLAN>(a, lds, lds + COLS, wg - n_cols_wg, n_rows_wg);
   }
 }
 
@@ -990,22 +1098,63 @@ bool hidden_supported(int hidden) {
 
 bool packed_hidden_supported(int hidden) { return small_lanes(hidden) != 0; }
 
-// Wavefronts per row: one up to 1024 columns, two above.
-static int wide_tw(int hidden) { return hidden <= 1024 ? 1 : 2; }
-static int wide_v(int hidden) {
-  const int per = 512 * wide_tw(hidden);
+// Forward row shape: one wavefront per row up to 1024 columns, two above.
+static int fwd_tw(int hidden) { return hidden <= 1024 ? 1 : 2; }
+static int fwd_v(int hidden) {
+  const int per = 512 * fwd_tw(hidden);
   return (hidden + per - 1) / per;
+}
+
+// Backward shapes, by the number of 512-column chunk groups K of a row
+// (chunk groups per wavefront V, wavefronts per row TW, rows in flight per
+// workgroup TEAMS, rows prefetched ahead PD).  The shape decides only how
+// the row's fixed arithmetic is spread over the hardware: no output bit
+// depends on it.  Measured on MI355X (one call, x and dy 0.5-1.2 GB): at
+// 4096 columns two rows in flight per workgroup, four wavefronts each, one
+// resident workgroup per compute unit, beat four rows in flight by 5%; at
+// 5120 and 8192 columns four rows in flight of two wavefronts each beat two
+// rows of four or five wavefronts by 1-5%.
+struct BwdShape {
+  int v, tw, teams, pd;
+};
+static BwdShape fused_shape(int hidden) {
+  const int K = (hidden + 511) / 512;
+  if (K <= 1) return {1, 1, 4, 1};
+  if (K <= 2) return {1, 2, 4, 1};
+  if (K <= 4) return {1, 4, 2, 1};
+  if (K <= 8) return {2, 4, 2, 1};
+  if (K <= 10) return {5, 2, 4, 1};
+  if (K <= 16) return {8, 2, 4, 1};
+  return {10, 2, 4, 0};
+}
+// The rstd-recompute backward keeps the row for a second pass (the
+// contributions wait for rstd): above 4096 columns it keeps no prefetch
+// ring, and above 8192 it runs two teams of four wavefronts.
+static BwdShape recompute_shape(int hidden) {
+  const int K = (hidden + 511) / 512;
+  if (K <= 8) return fused_shape(hidden);
+  if (K <= 10) return {5, 2, 4, 0};
+  if (K <= 16) return {8, 2, 4, 0};
+  return {5, 4, 2, 0};
+}
+// The dx rows of the two-pass path: two teams, each wide enough that the
+// workgroup is a whole number of 4-wavefront column units.
+static BwdShape split_shape(int hidden) {
+  const int K = (hidden + 511) / 512;
+  if (K <= 2) return {1, 2, 2, 0};
+  return {(K + 3) / 4, 4, 2, 0};
 }
 
 const char* fwd_variant(int hidden) {
   return small_lanes(hidden) ? "fwd_small(lanes_per_row=hidden/8)"
-         : wide_tw(hidden) == 1 ? "fwd_rows(wave_per_row, 4 rows per workgroup)"
-                                : "fwd_rows(two_waves_per_row, 2 rows per workgroup)";
+         : fwd_tw(hidden) == 1 ? "fwd_rows(wave_per_row, 4 rows per workgroup)"
+                               : "fwd_rows(two_waves_per_row, 2 rows per workgroup)";
 }
 const char* bwd_variant(int hidden) {
   if (small_lanes(hidden)) return "bwd_small(lds_fold, streams=4)";
-  return wide_tw(hidden) == 1 ? "bwd_wide(wave_per_row, streams=4; few blocks: dx_rows + dw_cols)"
-                              : "bwd_wide(two_waves_per_row, streams=4; few blocks: dx_rows + dw_cols)";
+  return fused_shape(hidden).teams == 4
+             ? "bwd_team(one pass, 4 teams x 1 row, streams=4; few blocks: dx_rows + dw_cols)"
+             : "bwd_team(two passes, 2 teams x 1 row, streams=4; few blocks: dx_rows + dw_cols)";
 }
 
 static int grid_cap() { return 256 * 16; }
@@ -1057,9 +1206,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
     case 32: fwd_small_go<32>(a, st); return hipGetLastError();
     default: break;
   }
-  // the backward's row shape: wide_tw wavefronts per row, wide_v chunks per lane
-  const int V = wide_v(a.hidden);
-  if (wide_tw(a.hidden) == 1) {
+  // fwd_tw wavefronts per row, fwd_v chunks per lane
+  const int V = fwd_v(a.hidden);
+  if (fwd_tw(a.hidden) == 1) {
     switch (V) {
       case 1: fwd_row_go<1, 1>(a, st); break;
       case 2: fwd_row_go<2, 1>(a, st); break;
@@ -1118,63 +1267,81 @@ static int compute_units() {
   return cus[dev];
 }
 
-template <int V, int TW, bool FULL, bool PLAN, bool DX, bool DW, bool RC>
-static void bwd_wide_launch(BwdArgs a, int pad_groups, hipStream_t st) {
-  using Sh = WideShape<V, TW, FULL>;
-  static const int per_cu = [] {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(&bwd_wide_kernel<V, TW, FULL, PLAN, DX, DW, RC>),
-            Sh::THREADS, 0) != hipSuccess || n <= 0)
-      n = 1;
-    return n;
-  }();
+// Workgroups of the fused backward: one per work item, capped so that the
+// workgroups walk their share of the items in turn -- one per compute unit
+// with two teams (two resident workgroups per compute unit were about 4%
+// slower at hidden 4096), two with four teams, and at least 8 wavefronts
+// per compute unit.  Which workgroup takes an item changes nothing in its
+// arithmetic.
+template <int V, int TW, int TEAMS, int PD, bool FULL, bool PLAN, bool DX, bool DW, bool RC>
+static void bwd_team_launch(BwdArgs a, hipStream_t st) {
+  constexpr int WAVES = TW * TEAMS;
   const int64_t knob = wide_group_cap();
-  const int64_t cap = knob > 0 ? knob : (int64_t)per_cu * compute_units();
-  a.item_groups = (int32_t)(wide_persistent<V, TW, FULL, RC>() && a.plan.n_items > cap ? cap
-                                                                                  : a.plan.n_items);
-  const dim3 grid((unsigned)(a.item_groups + pad_groups)), block(Sh::THREADS);
-  bwd_wide_kernel<V, TW, FULL, PLAN, DX, DW, RC><<<grid, block, 0, st>>>(a);
+  const int64_t per_cu = (TEAMS == 2 ? 1 : 2) * (WAVES >= 8 ? 1 : 8 / WAVES);
+  const int64_t cap = knob > 0 ? knob : per_cu * compute_units();
+  a.item_groups = (int32_t)(a.plan.n_items > cap ? cap : a.plan.n_items);
+  const int pad_groups = DX ? (a.plan.n_pad + WAVES - 1) / WAVES : 0;
+  if (a.item_groups + pad_groups == 0) return;
+  const dim3 grid((unsigned)(a.item_groups + pad_groups)), block(64 * WAVES);
+  bwd_team_kernel<V, TW, TEAMS, PD, FULL, PLAN, DX, DW, RC><<<grid, block, 0, st>>>(a);
+}
+
+template <int V, int TW, int TEAMS, int PD, bool RC, bool FULL, bool PLAN>
+static void bwd_team_go3(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+  if constexpr (RC) {
+    if (dw) bwd_team_launch<V, TW, TEAMS, PD, FULL, PLAN, true, true, true>(a, st);
+    else bwd_team_launch<V, TW, TEAMS, PD, FULL, PLAN, true, false, true>(a, st);
+  } else {
+    if (dx && dw) bwd_team_launch<V, TW, TEAMS, PD, FULL, PLAN, true, true, false>(a, st);
+    else if (dx) bwd_team_launch<V, TW, TEAMS, PD, FULL, PLAN, true, false, false>(a, st);
+    else bwd_team_launch<V, TW, TEAMS, PD, FULL, PLAN, false, true, false>(a, st);
+  }
+}
+// RC: the shape serves the rstd-recompute backward (only its instances are
+// built); otherwise the saved-rstd one.  With a layout plan a kernel carries
+// the spill path next to the fold, and a row narrower than the shape carries
+// the lane masks: at 8 or more chunk groups per wavefront the prefetch ring
+// would not fit the register file beside either.
+template <int V, int TW, int TEAMS, int PD, bool RC>
+static void bwd_team_go(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+  constexpr int PD_LEAN = V >= 8 ? 0 : PD;
+  const bool plan = a.plan.item_info != nullptr;
+  if constexpr (512 * V * TW <= kMaxHidden) {
+    if (a.hidden == 512 * V * TW) {
+      if (plan) bwd_team_go3<V, TW, TEAMS, PD_LEAN, RC, true, true>(a, dx, dw, st);
+      else bwd_team_go3<V, TW, TEAMS, PD, RC, true, false>(a, dx, dw, st);
+      return;
+    }
+  }
+  if (plan) bwd_team_go3<V, TW, TEAMS, PD_LEAN, RC, false, true>(a, dx, dw, st);
+  else bwd_team_go3<V, TW, TEAMS, PD_LEAN, RC, false, false>(a, dx, dw, st);
 }
 
 template <int V, int TW, bool FULL, bool PLAN>
-static void bwd_wide_go3(const BwdArgs& a, bool dx, bool dw, bool rc, hipStream_t st) {
-  using Sh = WideShape<V, TW, FULL>;
-  if (rc) {   // rstd rebuilt in the fused kernel (the two-pass path reads rstd)
-    const int pad_groups = (a.plan.n_pad + Sh::WAVES - 1) / Sh::WAVES;
-    if (dw) bwd_wide_launch<V, TW, FULL, PLAN, true, true, true>(a, pad_groups, st);
-    else bwd_wide_launch<V, TW, FULL, PLAN, true, false, true>(a, pad_groups, st);
-    return;
+static void bwd_split_go2(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+  constexpr int TEAMS = 2;
+  int64_t rows_wg = 0;
+  if (dx && a.rows > 0) {
+    rows_wg = (a.rows + TEAMS - 1) / TEAMS;
+    if (rows_wg > grid_cap()) rows_wg = grid_cap();
   }
-  if (a.plan.n_items < split_items()) {
-    int64_t rows_wg = 0;
-    if (dx && a.rows > 0) {
-      rows_wg = (a.rows + Sh::S - 1) / Sh::S;
-      if (rows_wg > grid_cap()) rows_wg = grid_cap();
-    }
-    const int n_slices = (a.hidden / 8 + 63) / 64;
-    const int64_t units = dw ? (int64_t)a.plan.n_items * n_slices : 0;
-    const int64_t cols_wg = (units + TW - 1) / TW;
-    if (rows_wg + cols_wg == 0) return;
-    bwd_split_kernel<V, TW, FULL, PLAN><<<dim3((unsigned)(cols_wg + rows_wg)), dim3(Sh::THREADS), 0, st>>>(
-        a, (int)cols_wg, (int)units, n_slices, (int)rows_wg);
-    return;
-  }
-  const int pad_groups = dx ? (a.plan.n_pad + Sh::WAVES - 1) / Sh::WAVES : 0;
-  if (dx && dw) bwd_wide_launch<V, TW, FULL, PLAN, true, true, false>(a, pad_groups, st);
-  else if (dx) bwd_wide_launch<V, TW, FULL, PLAN, true, false, false>(a, pad_groups, st);
-  else bwd_wide_launch<V, TW, FULL, PLAN, false, true, false>(a, pad_groups, st);
-}
-template <int V, int TW, bool FULL>
-static void bwd_wide_go2(const BwdArgs& a, bool dx, bool dw, bool rc, hipStream_t st) {
-  if (a.plan.item_info != nullptr) bwd_wide_go3<V, TW, FULL, true>(a, dx, dw, rc, st);
-  else bwd_wide_go3<V, TW, FULL, false>(a, dx, dw, rc, st);
+  constexpr int UNITS = TW / 2;
+  const int n_slices = (a.hidden / 8 + 63) / 64;
+  const int64_t units = dw ? (int64_t)a.plan.n_items * n_slices : 0;
+  const int64_t cols_wg = (units + UNITS - 1) / UNITS;
+  if (rows_wg + cols_wg == 0) return;
+  bwd_split_kernel<V, TW, FULL, PLAN><<<dim3((unsigned)(cols_wg + rows_wg)), dim3(128 * TW), 0, st>>>(
+      a, (int)cols_wg, (int)units, n_slices, (int)rows_wg);
 }
 template <int V, int TW>
-static void bwd_wide_go(const BwdArgs& a, bool dx, bool dw, bool rc, hipStream_t st) {
-  if (a.hidden == 512 * V * TW) bwd_wide_go2<V, TW, true>(a, dx, dw, rc, st);
-  else bwd_wide_go2<V, TW, false>(a, dx, dw, rc, st);
+static void bwd_split_go(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
+  const bool full = a.hidden == 512 * V * TW, plan = a.plan.item_info != nullptr;
+  if (full && plan) bwd_split_go2<V, TW, true, true>(a, dx, dw, st);
+  else if (full) bwd_split_go2<V, TW, true, false>(a, dx, dw, st);
+  else if (plan) bwd_split_go2<V, TW, false, true>(a, dx, dw, st);
+  else bwd_split_go2<V, TW, false, false>(a, dx, dw, st);
 }
+
 template <int L>
 static void bwd_small_go(const BwdArgs& a, bool dx, bool dw, bool rc, hipStream_t st) {
   constexpr int GROUPS = 256 / L;
@@ -1208,21 +1375,43 @@ hipError_t launch_bwd(const BwdArgs& a, bool dx, bool dw, hipStream_t st, bool r
     case 32: bwd_small_go<32>(a, dx, dw, rc, st); return hipGetLastError();
     default: break;
   }
-  const int tw = wide_tw(a.hidden), V = wide_v(a.hidden);
-  if (tw == 1) {
-    switch (V) {
-      case 1: bwd_wide_go<1, 1>(a, dx, dw, rc, st); break;
-      case 2: bwd_wide_go<2, 1>(a, dx, dw, rc, st); break;
+  if (!rc && a.plan.n_items < split_items()) {
+    const BwdShape s = split_shape(a.hidden);
+    switch (s.v * 16 + s.tw) {
+      case 1 * 16 + 2: bwd_split_go<1, 2>(a, dx, dw, st); break;
+      case 1 * 16 + 4: bwd_split_go<1, 4>(a, dx, dw, st); break;
+      case 2 * 16 + 4: bwd_split_go<2, 4>(a, dx, dw, st); break;
+      case 3 * 16 + 4: bwd_split_go<3, 4>(a, dx, dw, st); break;
+      case 4 * 16 + 4: bwd_split_go<4, 4>(a, dx, dw, st); break;
+      case 5 * 16 + 4: bwd_split_go<5, 4>(a, dx, dw, st); break;
       default: return hipErrorInvalidValue;
     }
-  } else {
-    switch (V) {
-#define RBI_BWD2(v) case v: bwd_wide_go<v, 2>(a, dx, dw, rc, st); break;
-      RBI_BWD2(2) RBI_BWD2(3) RBI_BWD2(4) RBI_BWD2(5) RBI_BWD2(6)
-      RBI_BWD2(7) RBI_BWD2(8) RBI_BWD2(9) RBI_BWD2(10)
-#undef RBI_BWD2
+    return hipGetLastError();
+  }
+  if (rc) {
+    const BwdShape s = recompute_shape(a.hidden);
+    switch (s.v * 16 + s.tw) {
+      case 1 * 16 + 1: bwd_team_go<1, 1, 4, 1, true>(a, dx, dw, st); break;
+      case 1 * 16 + 2: bwd_team_go<1, 2, 4, 1, true>(a, dx, dw, st); break;
+      case 1 * 16 + 4: bwd_team_go<1, 4, 2, 1, true>(a, dx, dw, st); break;
+      case 2 * 16 + 4: bwd_team_go<2, 4, 2, 1, true>(a, dx, dw, st); break;
+      case 5 * 16 + 2: bwd_team_go<5, 2, 4, 0, true>(a, dx, dw, st); break;
+      case 8 * 16 + 2: bwd_team_go<8, 2, 4, 0, true>(a, dx, dw, st); break;
+      case 5 * 16 + 4: bwd_team_go<5, 4, 2, 0, true>(a, dx, dw, st); break;
       default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+  }
+  const BwdShape s = fused_shape(a.hidden);
+  switch (s.v * 16 + s.tw) {
+    case 1 * 16 + 1: bwd_team_go<1, 1, 4, 1, false>(a, dx, dw, st); break;
+    case 1 * 16 + 2: bwd_team_go<1, 2, 4, 1, false>(a, dx, dw, st); break;
+    case 1 * 16 + 4: bwd_team_go<1, 4, 2, 1, false>(a, dx, dw, st); break;
+    case 2 * 16 + 4: bwd_team_go<2, 4, 2, 1, false>(a, dx, dw, st); break;
+    case 5 * 16 + 2: bwd_team_go<5, 2, 4, 1, false>(a, dx, dw, st); break;
+    case 8 * 16 + 2: bwd_team_go<8, 2, 4, 1, false>(a, dx, dw, st); break;
+    case 10 * 16 + 2: bwd_team_go<10, 2, 4, 0, false>(a, dx, dw, st); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -110,11 +110,12 @@ def test_no_atomics_and_no_fallbacks_in_the_library_sources():
         assert not re.search(r"\batomic\w*\s*\(|__atomic|std::atomic|__hip_atomic", code), name
         assert "__CUDA" not in code and "cuda_runtime" not in code, name
         assert "__HIP_PLATFORM" not in code, name
-    # the arithmetic variant (lane groups, wavefronts per row, chunks per lane)
-    # keys on the hidden size only
+    # the kernel shapes (lane groups, wavefronts per row, chunks per lane,
+    # rows in flight) key on the hidden size only
     k = open(os.path.join(csrc, "kernels.hip")).read()
-    for fn in ("small_lanes", "wide_tw", "wide_v"):
-        sig = re.search(rf"static int {fn}\(([^)]*)\)", k).group(1)
+    for ret, fn in (("int", "small_lanes"), ("int", "fwd_tw"), ("int", "fwd_v"),
+                    ("BwdShape", "fused_shape"), ("BwdShape", "split_shape")):
+        sig = re.search(rf"static {ret} {fn}\(([^)]*)\)", k).group(1)
         assert sig.strip() == "int hidden", fn
 
 
