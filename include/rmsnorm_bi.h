@@ -210,6 +210,32 @@ int rmsnorm_set_split_threshold(int64_t blocks, int64_t* previous);
  * afterwards.  Always returns RMSNORM_OK. */
 int rmsnorm_set_workgroup_cap(int64_t groups, int64_t* previous);
 
+/* Allocation-free one-call backward, for callers that cannot allocate device
+ * memory while they run: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Computes what rmsnorm_bwd_dx with an
+ * accumulator followed by rmsnorm_dw_finalize computes for one call that
+ * holds every logical row (identity map, rows == n_logical): dx[rows][hidden]
+ * (bf16) and dweight[hidden] (FP32), bit for bit the same.  Inputs and
+ * outputs are the caller's device memory as in rmsnorm_bwd_dx; dweight must
+ * not alias anything.  The block partials and the block tree's levels live
+ * in a device array inside the library, one copy per GPU, held until the
+ * process ends: (ceil(rows/64) + tree levels) * hidden floats must fit in
+ * rmsnorm_bwd_noalloc_max_scratch() floats (16M floats, 64 MiB; 32768 x 4096,
+ * 74780 x 8192 and 131072 x 5120 fit), RMSNORM_EUNSUPPORTED otherwise,
+ * checked before anything is enqueued.  No call allocates: the array's
+ * device address is looked up once per device, on the first call on it.
+ * Every call on a GPU uses that GPU's one array: calls that overlap on one
+ * GPU (on different streams, or from different host threads) race and give
+ * undefined results; calls on one stream are ordered and safe.  Every
+ * element of the array a call reads was written by the same call, so
+ * nothing carries over between calls.  The stream must belong to the
+ * current device.  rows == 0 writes dweight = 0. */
+int rmsnorm_bwd_noalloc(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
+                        const float* rstd, rmsnorm_bf16* dx, float* dweight, int64_t rows,
+                        int64_t hidden, void* stream);
+/* Floats of device scratch rmsnorm_bwd_noalloc holds per GPU. */
+int64_t rmsnorm_bwd_noalloc_max_scratch(void);
+
 /* Streaming copy of `bytes` bytes from device buffer `src` to device buffer
  * `dst` on `stream`, with the access policy the kernels use (16-byte
  * non-temporal loads and stores, one 16-byte unit per thread).  Not part of

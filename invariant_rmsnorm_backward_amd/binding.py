@@ -28,7 +28,8 @@ EXPORTED = ("rmsnorm_max_hidden", "rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_c
             "rmsnorm_dw_acc_destroy", "rmsnorm_last_error", "rmsnorm_backend_info",
             "rmsnorm_set_split_threshold", "rmsnorm_set_workgroup_cap", "rmsnorm_stream_copy",
             "rmsnorm_fwd_packed",
-            "rmsnorm_bwd_dx_packed", "rmsnorm_bwd_dx_recompute",
+            "rmsnorm_bwd_dx_packed", "rmsnorm_bwd_dx_recompute", "rmsnorm_bwd_noalloc",
+            "rmsnorm_bwd_noalloc_max_scratch",
             "det_gemm_fwd", "det_gemm_bwd_dx", "det_gemm_dw_acc_create", "det_gemm_dw_contrib",
             "det_gemm_dw_finalize", "det_gemm_dw_acc_reset", "det_gemm_dw_acc_destroy",
             "det_embedding_fwd", "det_embedding_dw_acc_create", "det_embedding_dw_acc_set_ids",
@@ -68,6 +69,8 @@ def load() -> ctypes.CDLL:
         "rmsnorm_bwd_dx": ([P, P, P, P, P, I64, I64, P, P, P], I32),
         "rmsnorm_bwd_dx_recompute": ([P, P, P, ctypes.c_float, P, I64, I64, P, P, P], I32),
         "rmsnorm_dw_contrib": ([P, P, P, I64, I64, P, P, P], I32),
+        "rmsnorm_bwd_noalloc": ([P, P, P, P, P, P, I64, I64, P], I32),
+        "rmsnorm_bwd_noalloc_max_scratch": ([], I64),
         "rmsnorm_dw_finalize": ([P, P, P], I32),
         "rmsnorm_layout_create": ([PP, P, I64, I64, P], I32),
         "rmsnorm_layout_destroy": ([P], I32),
@@ -150,6 +153,16 @@ def rmsnorm_dw_contrib(x: int, dy: int, rstd: int, rows: int, hidden: int,
 
 def rmsnorm_dw_finalize(acc: Optional[int], dweight: int, stream: Optional[int]) -> None:
     _check(load().rmsnorm_dw_finalize(acc, dweight, stream), "rmsnorm_dw_finalize")
+
+
+def rmsnorm_bwd_noalloc(x: int, w: int, dy: int, rstd: int, dx: int, dweight: int, rows: int,
+                        hidden: int, stream: Optional[int]) -> None:
+    _check(load().rmsnorm_bwd_noalloc(x, w, dy, rstd, dx, dweight, rows, hidden, stream),
+           "rmsnorm_bwd_noalloc")
+
+
+def rmsnorm_bwd_noalloc_max_scratch() -> int:
+    return int(load().rmsnorm_bwd_noalloc_max_scratch())
 
 
 def rmsnorm_layout_create(row_logical: np.ndarray, n_logical: int, stream: Optional[int]) -> int:

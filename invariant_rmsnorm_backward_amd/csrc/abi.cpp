@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -39,6 +40,39 @@ int check_hidden(int64_t hidden) {
     return fail(RMSNORM_EUNSUPPORTED,
                 "hidden " + std::to_string(hidden) + " exceeds the maximum " +
                     std::to_string(rbi::kMaxHidden));
+  return RMSNORM_OK;
+}
+
+}  // namespace
+
+// Device scratch of rmsnorm_bwd_noalloc: the block partials of one call and
+// the partial levels of its block tree.  Every GPU the library runs on holds
+// its own copy of the array until the process ends; host code reaches it only
+// through the address hipGetSymbolAddress gives for the current device.
+constexpr int64_t kNoAllocScratchFloats = int64_t(16) << 20;   // 64 MiB
+static __device__ __align__(256) float scratch[kNoAllocScratchFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_addr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+int scratch_of_current_device(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RMSNORM_EUNSUPPORTED, "device index " + std::to_string(dev) + " is above 63");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "address of the device scratch");
+    g_scratch_addr[dev] = static_cast<float*>(addr);
+  }
+  *out = g_scratch_addr[dev];
   return RMSNORM_OK;
 }
 
@@ -286,6 +320,67 @@ int rmsnorm_dw_finalize(rmsnorm_dw_acc* acc, float* dweight, void* stream) {
   acc->host.finalized = true;
   return RMSNORM_OK;
 }
+
+int rmsnorm_bwd_noalloc(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
+                        const float* rstd, rmsnorm_bf16* dx, float* dweight, int64_t rows,
+                        int64_t hidden, void* stream) {
+  int rc;
+  if ((rc = check_rows(rows)) || (rc = check_hidden(hidden))) return rc;
+  if ((rc = check_tensor(dweight, "dweight", 4))) return rc;
+  const int64_t nb = rbi::num_blocks(rows);
+  const int64_t need = (nb + rbi::tree_scratch_rows(nb)) * hidden;
+  if (need > kNoAllocScratchFloats)
+    return fail(RMSNORM_EUNSUPPORTED,
+                "rows x hidden needs " + std::to_string(need) + " floats of scratch (block partials "
+                "and block tree), above the " + std::to_string(kNoAllocScratchFloats) +
+                " this entry point holds; use rmsnorm_bwd_dx with an accumulator");
+  if (rows > 0) {
+    if ((rc = check_tensor(x, "x", 16)) || (rc = check_tensor(dy, "dy", 16)) ||
+        (rc = check_tensor(w, "w", 16)) || (rc = check_tensor(rstd, "rstd", 4)) ||
+        (rc = check_tensor(dx, "dx", 16)))
+      return rc;
+    const size_t nbytes = static_cast<size_t>(rows * hidden) * 2;
+    if (overlaps(dx, nbytes, x, nbytes) || overlaps(dx, nbytes, dy, nbytes) ||
+        overlaps(dx, nbytes, w, hidden * 2) || overlaps(dx, nbytes, rstd, rows * 4) ||
+        overlaps(dx, nbytes, dweight, hidden * 4))
+      return fail(RMSNORM_EINVAL, "dx must not alias an input or dweight");
+    if (overlaps(dweight, hidden * 4, x, nbytes) || overlaps(dweight, hidden * 4, dy, nbytes) ||
+        overlaps(dweight, hidden * 4, w, hidden * 2) || overlaps(dweight, hidden * 4, rstd, rows * 4))
+      return fail(RMSNORM_EINVAL, "dweight must not alias an input");
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int32_t H = static_cast<int32_t>(hidden);
+  hipError_t e;
+  if (rows == 0) {
+    // the empty multiset: dweight = 0, no scratch used
+    if ((e = rbi::launch_tree(nullptr, 0, nullptr, dweight, H, st)) != hipSuccess)
+      return hip_fail(e, "dweight zero fill");
+    return RMSNORM_OK;
+  }
+  float* scr = nullptr;
+  if ((rc = scratch_of_current_device(&scr))) return rc;
+  // One call holding every logical row (identity map): every block is
+  // complete, so every block partial is written and nothing spills; the
+  // block tree writes every scratch row it reads.  Nothing needs clearing.
+  rbi::BwdArgs a{};
+  a.x = x;
+  a.w = w;
+  a.dy = dy;
+  a.rstd = rstd;
+  a.dx = dx;
+  a.P = scr;
+  a.S = nullptr;
+  a.rows = rows;
+  a.hidden = H;
+  a.plan.n_items = static_cast<int32_t>(nb);
+  a.plan.n_pad = 0;
+  if ((e = rbi::launch_bwd(a, true, true, st)) != hipSuccess) return hip_fail(e, "rmsnorm backward launch");
+  if ((e = rbi::launch_tree(scr, nb, scr + nb * hidden, dweight, H, st)) != hipSuccess)
+    return hip_fail(e, "block tree");
+  return RMSNORM_OK;
+}
+
+int64_t rmsnorm_bwd_noalloc_max_scratch(void) { return kNoAllocScratchFloats; }
 
 int rmsnorm_layout_check(const int32_t* row_logical_host, int64_t rows, int64_t n_logical,
                          int64_t stats[5]) {

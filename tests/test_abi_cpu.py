@@ -184,3 +184,24 @@ def test_packed_entry_points_check_their_arguments(lib):
         assert ei.value.code == code, over
     # zero tokens is a successful no-op
     binding.rmsnorm_fwd_packed(A, A, A, A, 0, 2, 128, 512, 1e-6, None, None)
+
+
+def test_noalloc_refusals_before_any_launch(lib):
+    """The allocation-free backward checks its sizes and pointers on the host:
+    more block partials than its scratch holds, a NULL dweight, aliasing and a
+    bad width are refused before anything is enqueued."""
+    A = 1 << 20
+    limit = binding.rmsnorm_bwd_noalloc_max_scratch()
+    assert limit == 16 << 20
+    # 16M floats hold 262,143 rows at hidden 4096 (plus the tree levels); refuse beyond
+    too_many = (limit // 4096) * 64 + 64
+    for args, code in (((A, A, A, A, A, A, too_many, 4096), binding.EUNSUPPORTED),
+                       ((A, A, A, A, A, 0, 10, 4096), binding.EINVAL),
+                       ((A, A, A, A, A, A, 10, 12), binding.EUNSUPPORTED),
+                       ((A, A + (1 << 24), A + (2 << 24), A + (3 << 24), A, A + (4 << 24), 10, 4096),
+                        binding.EINVAL),   # dx aliases x
+                       ((A, A + (1 << 24), A + (2 << 24), A + (3 << 24), A + (4 << 24), A, 10, 4096),
+                        binding.EINVAL)):  # dweight aliases x
+        with pytest.raises(binding.RmsNormError) as ei:
+            binding.rmsnorm_bwd_noalloc(*args, None)
+        assert ei.value.code == code, (args, ei.value)
