@@ -39,6 +39,11 @@ __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
   f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
+__device__ __forceinline__ void unpack4(const uint2& v, float (&f)[4]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+}
+
 __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
   uint4 r;
   r.x = pack_bf16x2(f[0], f[1]);
@@ -65,6 +70,11 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load16_stream(const void* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 load8_stream(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
 }
 __device__ __forceinline__ void store16_stream(void* p, const uint4& v) {
   const u32x4_t u = {v.x, v.y, v.z, v.w};

@@ -714,7 +714,7 @@ __global__ __launch_bounds__(64 * TW * TEAMS) void bwd_team_kernel(BwdArgs a) {
 //     the dweight part compiled out); the dot order does not depend on the
 //     row shape, so every dx bit equals the fused kernel's;
 //   dweight columns (dw_cols_part): the dweight contributions and the
-//     in-block stream fold of one canonical block over 512 columns, with the
+//     in-block stream fold of one canonical block over 256 columns, with the
 //     same operations in the same order as the fused kernel, so the block
 //     partials and spill rows are bitwise the same.
 // The passes are independent, so one launch (bwd_split_kernel) runs both:
@@ -762,23 +762,22 @@ __device__ __forceinline__ void dx_rows_part(const BwdArgs& a, float* w_s, float
   }
 }
 
-// One column unit: the canonical block of work item `item` over the 512
+// One column unit: the canonical block of work item `item` over the 256
 // columns of `slice`, folded by 4 wavefronts starting at wavefront `w0`:
-// wavefront w0 + w is stream w and lane l holds columns 8*(64*slice + l)
-// .. +8.  The stream's 16 rows are loaded in two batches of 8 (all of a
-// batch before its fold), and the fold runs in slot order across both; the
-// batches keep the unit's registers near the dx rows' so the launch that
-// runs both keeps its occupancy.  `live` false: no unit, but the barrier is
-// still reached (the workgroup's other unit may need it).
+// wavefront w0 + w is stream w and lane l holds columns 4*(64*slice + l)
+// .. +4 (8-byte loads).  All 16 rows of the stream are loaded before the
+// fold, which then runs in slot order, so the unit waits for memory once.
+// `live` false: no unit, but the barrier is still reached (the workgroup's
+// other unit may need it).
 template <bool PLAN>
-__device__ __forceinline__ void dw_cols_part(const BwdArgs& a, float (*q_s)[512], int item, int slice,
+__device__ __forceinline__ void dw_cols_part(const BwdArgs& a, float (*q_s)[256], int item, int slice,
                                              int w0, bool live) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int stream = __builtin_amdgcn_readfirstlane(tid >> 6) - w0;
   const int H = a.hidden;
-  const int q = slice * 64 + lane;         // this lane's 8-column chunk
-  const bool on = live && q < (H >> 3);
+  const int col = (slice * 64 + lane) * 4;   // this lane's first column (hidden % 8 == 0)
+  const bool on = live && col < H;
   int blk = 0;
   bool complete = true;
   if (live) {
@@ -790,61 +789,50 @@ __device__ __forceinline__ void dw_cols_part(const BwdArgs& a, float (*q_s)[512]
       blk = item;
     }
   }
-  float acc[8];
+  float acc[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int e = 0; e < 4; ++e) acc[e] = 0.0f;
   if (live) {
     // lane i (< 16) holds the physical row and rstd of the stream's slot i
     const int sp = slot_row_t<PLAN>(a, item, blk, stream + kStreams * (lane & (kSlotsPerStream - 1)));
     const float sr = a.rstd[sp >= 0 ? sp : 0];
-    constexpr int B = kSlotsPerStream / 2;
+    uint2 xv[kSlotsPerStream], dv[kSlotsPerStream];
 #pragma unroll
-    for (int b0 = 0; b0 < kSlotsPerStream; b0 += B) {
-      uint4 xv[B], dv[B];
+    for (int i = 0; i < kSlotsPerStream; ++i) {
+      const int p = __builtin_amdgcn_readlane(sp, i);
+      const int64_t off = (int64_t)(p >= 0 ? p : 0) * H + (on ? col : 0);
+      xv[i] = load8_stream(a.x + off);
+      dv[i] = load8_stream(a.dy + off);
+    }
 #pragma unroll
-      for (int i = 0; i < B; ++i) {
-        const int p = __builtin_amdgcn_readlane(sp, b0 + i);
-        const int64_t off = (int64_t)(p >= 0 ? p : 0) * H + (on ? q * 8 : 0);
-        xv[i] = load16_stream(a.x + off);
-        dv[i] = load16_stream(a.dy + off);
+    for (int i = 0; i < kSlotsPerStream; ++i) {
+      const int p = __builtin_amdgcn_readlane(sp, i);
+      if (p < 0) continue;
+      const float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sr), i));
+      float xf[4], df[4], c[4];
+      unpack4(xv[i], xf);
+      unpack4(dv[i], df);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pr = df[e] * xf[e];          // exact: two bf16 significands
+        c[e] = pr * r;                           // the row's contribution, rounded once
+        acc[e] = acc[e] + c[e];
       }
-#pragma unroll
-      for (int i = 0; i < B; ++i) {
-        const int p = __builtin_amdgcn_readlane(sp, b0 + i);
-        if (p < 0) continue;
-        const float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sr), b0 + i));
-        float xf[8], df[8], c[8];
-        unpack8(xv[i], xf);
-        unpack8(dv[i], df);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pr = df[e] * xf[e];          // exact: two bf16 significands
-          c[e] = pr * r;                           // the row's contribution, rounded once
-          acc[e] = acc[e] + c[e];
-        }
-        if (!complete && on) {
-          float* srow = a.S + ((int64_t)blk * kBlockRows + stream + kStreams * (b0 + i)) * H + q * 8;
-          store_f4_stream(srow, c[0], c[1], c[2], c[3]);
-          store_f4_stream(srow + 4, c[4], c[5], c[6], c[7]);
-        }
+      if (!complete && on) {
+        float* srow = a.S + ((int64_t)blk * kBlockRows + stream + kStreams * i) * H + col;
+        store_f4_stream(srow, c[0], c[1], c[2], c[3]);
       }
     }
   }
   const bool fold = live && complete;
-  if (fold && stream > 0) {
-    float* d = &q_s[stream - 1][lane * 8];
-    store_f4(d, acc[0], acc[1], acc[2], acc[3]);
-    store_f4(d + 4, acc[4], acc[5], acc[6], acc[7]);
-  }
+  if (fold && stream > 0) store_f4(&q_s[stream - 1][lane * 4], acc[0], acc[1], acc[2], acc[3]);
   __syncthreads();
   if (fold && stream == 0 && on) {
-    float o[8];
+    float o[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      o[e] = stream_tree4(acc[e], q_s[0][lane * 8 + e], q_s[1][lane * 8 + e], q_s[2][lane * 8 + e]);
-    float* dst = a.P + (int64_t)blk * H + q * 8;
-    store_f4(dst, o[0], o[1], o[2], o[3]);
-    store_f4(dst + 4, o[4], o[5], o[6], o[7]);
+    for (int e = 0; e < 4; ++e)
+      o[e] = stream_tree4(acc[e], q_s[0][lane * 4 + e], q_s[1][lane * 4 + e], q_s[2][lane * 4 + e]);
+    store_f4(a.P + (int64_t)blk * H + col, o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -860,7 +848,7 @@ __global__ __launch_bounds__(128 * TW) void bwd_split_kernel(BwdArgs a, int n_co
   constexpr int UNITS = TW / 2;
   static_assert(TW % 2 == 0, "column units take four wavefronts");
   constexpr int ROWS_LDS = COLS + Ops::XCH_FLOATS;   // w, then the exchange
-  constexpr int COLS_LDS = UNITS * (kStreams - 1) * 512;
+  constexpr int COLS_LDS = UNITS * (kStreams - 1) * 256;
   constexpr int LDS = ROWS_LDS > COLS_LDS ? ROWS_LDS : COLS_LDS;
   __shared__ float4 lds4[(LDS + 3) / 4];
   float* lds = reinterpret_cast<float*>(lds4);
@@ -869,7 +857,7 @@ __global__ __launch_bounds__(128 * TW) void bwd_split_kernel(BwdArgs a, int n_co
     const int u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);   // the workgroup's unit
     const int unit = wg * UNITS + u;
     const bool live = unit < n_units;
-    dw_cols_part<PLAN>(a, reinterpret_cast<float (*)[512]>(lds + u * (kStreams - 1) * 512),
+    dw_cols_part<PLAN>(a, reinterpret_cast<float (*)[256]>(lds + u * (kStreams - 1) * 256),
                        live ? unit / n_slices : 0, live ? unit % n_slices : 0, u * kStreams, live);
   } else {
     dx_rows_part<V, TW, FULL, PLAN>(a, lds, lds + COLS, wg - n_cols_wg, n_rows_wg);
@@ -1326,7 +1314,7 @@ static void bwd_split_go2(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
     if (rows_wg > grid_cap()) rows_wg = grid_cap();
   }
   constexpr int UNITS = TW / 2;
-  const int n_slices = (a.hidden / 8 + 63) / 64;
+  const int n_slices = (a.hidden + 255) / 256;
   const int64_t units = dw ? (int64_t)a.plan.n_items * n_slices : 0;
   const int64_t cols_wg = (units + UNITS - 1) / UNITS;
   if (rows_wg + cols_wg == 0) return;
