@@ -17,7 +17,7 @@
  * dweight is not chunk/batch decomposable", traces the failure this library
  * removes to a dweight fold whose shape follows the physical row count; here
  * dweight is reduced from per-logical-row FP32 contributions in one canonical
- * order (CDO-v1) that depends only on the logical row index and on nothing
+ * order (CDO-v2) that depends only on the logical row index and on nothing
  * else:
  *     c = fl32(fl32(dy*x)*rstd)  (dy*x of two bf16 values is exact)
  *     block b = logical rows 64b..64b+63; stream w = slot mod 4 folds its
@@ -178,7 +178,7 @@ int rmsnorm_dw_acc_destroy(rmsnorm_dw_acc* acc);
 const char* rmsnorm_last_error(void);
 
 /* Provenance: target, canonical-order version and kernel variants, e.g.
- * "hip gfx950; cdo=v1 R=64 S=4; ...".  Static string. */
+ * "hip gfx950; cdo=v2 R=64 S=4; ...".  Static string. */
 const char* rmsnorm_backend_info(void);
 
 /* Work distribution of the backward for hidden > 256 (a tuning knob; no

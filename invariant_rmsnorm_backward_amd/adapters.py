@@ -93,7 +93,7 @@ class RmsNormAdapter(GradientAdapter):
     name = "rms_norm"
     grad_names = ("dx", "dweight")
     forward_names = ("y", "rstd")
-    aggregation_order = "CDO-v1"
+    aggregation_order = "CDO-v2"
     recompute = False          # backward from the forward's saved rstd
 
     def run_cell(self, cell: Cell, data: NormInputs) -> Dict[str, np.ndarray]:
@@ -307,7 +307,7 @@ class NormLinearChainAdapter(GradientAdapter):
     forward_names = ("rms_norm.y", "rms_norm.rstd", "det_gemm.y")
     tensor_order = ("rms_norm.y", "rms_norm.rstd", "det_gemm.y", "det_gemm.dX", "det_gemm.dW",
                     "rms_norm.dx", "rms_norm.dweight")
-    aggregation_order = "CDO-v1 (dweight), GDO-v1 (dW)"
+    aggregation_order = "CDO-v2 (dweight), GDO-v1 (dW)"
 
     def run_cell(self, cell: Cell, data: ChainInputs) -> Dict[str, np.ndarray]:
         x, w, W, dy = data.x, data.w, data.wmat, data.dy

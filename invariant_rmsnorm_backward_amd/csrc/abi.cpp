@@ -96,12 +96,14 @@ int rmsnorm_max_hidden(void) { return rbi::kMaxHidden; }
 const char* rmsnorm_last_error(void) { return rbi::abi::last_error().c_str(); }
 
 const char* rmsnorm_backend_info(void) {
-  return "hip gfx950; cdo=v1 R=64 S=4, "
+  return "hip gfx950; cdo=v2 R=64 S=4, "
          "contribution fl32(fl32(dy*x)*rstd), streams fold ascending from +0.0, "
-         "stream tree pairwise, block tree pairwise with +0.0 padding; no atomics; "
-         "fwd=rows_per_workgroup|lanes_per_row bwd=fused dx+dW, 64-row blocks owned by resident "
-         "workgroups (next block's first row prefetched across the block tree) "
-         "(calls with few blocks: row-parallel dx + column-split dW fold), nt loads/stores; "
+         "stream tree pairwise, block tree pairwise with +0.0 padding; "
+         "row sums (x*x, dy*x*w): fmaf chain per 16-byte chunk, one wavefront sum per "
+         "64-chunk group, pairwise tree over the groups with +0.0 padding; no atomics; "
+         "fwd=rows_per_workgroup|lanes_per_row; bwd=fused dx+dW by resident block-owning "
+         "workgroups, two or four rows in flight, next rows prefetched across blocks "
+         "(calls with few blocks: row-parallel dx + 256-column dW units), nt loads/stores; "
          "max_hidden=10240";
 }
 

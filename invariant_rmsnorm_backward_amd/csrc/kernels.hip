@@ -7,7 +7,7 @@
 // stores, FP32 math, DPP wavefront sums of squares.
 //
 // Backward: one workgroup per canonical block of 64 logical rows.  The
-// dweight order (CDO-v1, following "WS1 C4 (#270) closeout evidence":
+// dweight order (CDO-v2, following "WS1 C4 (#270) closeout evidence":
 // parameter gradients from logical-row FP32 contributions reduced in a fixed
 // order) is laid onto the hardware: each of the 4 fold streams is one
 // wavefront (hidden <= 1024) or a pair of wavefronts (wider rows) that walks

@@ -1,4 +1,4 @@
-"""FP64 CPU oracle for RMSNorm forward/backward, the CDO-v1 dweight order,
+"""FP64 CPU oracle for RMSNorm forward/backward, the CDO-v2 dweight order,
 the backward of a linear layer (dX, dW) and the embedding table gradient
 (with an FP32 emulation of its EDO-v1 order).
 
@@ -51,8 +51,8 @@ def _bind(lib):
     lib.oracle_rmsnorm_fwd.restype = ctypes.c_int
     lib.oracle_rmsnorm_bwd.argtypes = [P, P, P, I64, I64, ctypes.c_double, P, I64, P, P, P]
     lib.oracle_rmsnorm_bwd.restype = ctypes.c_int
-    lib.oracle_cdo_v1_dweight_f32.argtypes = [P, P, P, I64, I64, P, I64, P]
-    lib.oracle_cdo_v1_dweight_f32.restype = ctypes.c_int
+    lib.oracle_cdo_v2_dweight_f32.argtypes = [P, P, P, I64, I64, P, I64, P]
+    lib.oracle_cdo_v2_dweight_f32.restype = ctypes.c_int
     lib.oracle_linear_fwd.argtypes = [P, P, I64, I64, I64, P, P]
     lib.oracle_linear_fwd.restype = ctypes.c_int
     lib.oracle_linear_bwd.argtypes = [P, P, P, I64, I64, I64, P, I64, P, P, P]
@@ -162,10 +162,10 @@ class Oracle:
         return self.rmsnorm_bwd(self.widen_bf16(x_bits), self.widen_bf16(w_bits),
                                 self.widen_bf16(dy_bits), eps, row_logical, n_logical)
 
-    def cdo_v1_dweight_f32(self, x_bits: np.ndarray, dy_bits: np.ndarray, rstd: np.ndarray,
+    def cdo_v2_dweight_f32(self, x_bits: np.ndarray, dy_bits: np.ndarray, rstd: np.ndarray,
                            row_logical: Optional[np.ndarray] = None,
                            n_logical: Optional[int] = None) -> np.ndarray:
-        """FP32 emulation of the canonical dweight order CDO-v1 (see the C source)."""
+        """FP32 emulation of the canonical dweight order CDO-v2 (see the C source)."""
         x = _c(x_bits, np.uint16)
         dy = _c(dy_bits, np.uint16)
         r = _c(rstd, np.float32)
@@ -173,9 +173,9 @@ class Oracle:
         rl = None if row_logical is None else _c(row_logical, np.int32)
         nl = rows if n_logical is None else int(n_logical)
         out = np.empty(H, dtype=np.float32)
-        _check(self._lib().oracle_cdo_v1_dweight_f32(_ptr(x), _ptr(dy), _ptr(r), rows, H,
+        _check(self._lib().oracle_cdo_v2_dweight_f32(_ptr(x), _ptr(dy), _ptr(r), rows, H,
                                                      _ptr(rl), nl, _ptr(out)),
-               "oracle_cdo_v1_dweight_f32")
+               "oracle_cdo_v2_dweight_f32")
         return out
 
     # ------------------------------------------------------------- linear layer
@@ -283,7 +283,7 @@ rmsnorm_fwd = _default.rmsnorm_fwd
 rmsnorm_bwd = _default.rmsnorm_bwd
 rmsnorm_fwd_bf16 = _default.rmsnorm_fwd_bf16
 rmsnorm_bwd_bf16 = _default.rmsnorm_bwd_bf16
-cdo_v1_dweight_f32 = _default.cdo_v1_dweight_f32
+cdo_v2_dweight_f32 = _default.cdo_v2_dweight_f32
 linear_fwd_bf16 = _default.linear_fwd_bf16
 linear_bwd_bf16 = _default.linear_bwd_bf16
 linear_sample_bf16 = _default.linear_sample_bf16

@@ -1,7 +1,7 @@
 /*
  * rmsnorm_oracle.c -- plain, slow FP64 CPU oracle for RMSNorm forward and
  * backward (dx, dweight), plus an FP32 emulation of the canonical dweight
- * order CDO-v1.
+ * order CDO-v2.
  *
  * TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check and the CPU
  * baseline leg of the benchmark may load this library.  It shares no source,
@@ -28,9 +28,9 @@
  * differences of the FP64 forward, the radial identity sum_j x_j dx_j =
  * eps*rstd^3*dot, the dx/dweight cross identity, H=1 and zero-row closed
  * forms, scale invariance and the norm identity of the forward, padding
- * neutrality and layout invariance.  The CDO-v1 emulation is pinned by
+ * neutrality and layout invariance.  The CDO-v2 emulation is pinned by
  * exactly representable sums and a hand-derived golden case
- * (tests/golden/cdo_v1_order.json).  Nothing here is "parity unpinned".
+ * (tests/golden/cdo_v2_order.json).  Nothing here is "parity unpinned".
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared (no fast-math:
  * every float operation below must round exactly once as written).
@@ -169,7 +169,7 @@ int oracle_rmsnorm_bwd(const double* x, const double* w, const double* dy, int64
 }
 
 /* ------------------------------------------------------------------------
- * CDO-v1: the canonical FP32 order in which dweight is reduced.  The pages
+ * CDO-v2: the canonical FP32 order in which dweight is reduced.  The pages
  * fix only that parameter gradients come from "logical-row FP32
  * contributions" reduced in a "fixed aggregation order" ("WS1 C4 (#270)
  * closeout evidence", opening note and "Acceptance map"); the order below is
@@ -197,7 +197,7 @@ static float cdo_tree(const float* leaves, int64_t nb, int64_t lo, int64_t n) {
     return a + b;
 }
 
-int oracle_cdo_v1_dweight_f32(const uint16_t* x, const uint16_t* dy, const float* rstd,
+int oracle_cdo_v2_dweight_f32(const uint16_t* x, const uint16_t* dy, const float* rstd,
                               int64_t rows, int64_t H, const int32_t* row_logical,
                               int64_t n_logical, float* dweight) {
     if (rows < 0 || H <= 0 || n_logical < 0) return ORACLE_EINVAL;

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_backend_info_names_the_order(lib):
     info = binding.rmsnorm_backend_info()
-    assert "gfx950" in info and "cdo=v1" in info and "no atomics" in info
+    assert "gfx950" in info and "cdo=v2" in info and "no atomics" in info
     assert binding.rmsnorm_max_hidden() >= 8192
 
 

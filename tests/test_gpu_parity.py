@@ -149,7 +149,7 @@ def test_inactive_rows_do_not_change_dweight_bits():
                                        (9000, [40, 41]), (8, [40000]), (16, [70000, 33001])])
 def test_dweight_is_the_canonical_order_bit_for_bit(H, lengths, bwd_path):
     """Tree conformance: given the same FP32 rstd, the GPU dweight equals the
-    oracle's FP32 emulation of CDO-v1 bit for bit, for one call and for
+    oracle's FP32 emulation of CDO-v2 bit for bit, for one call and for
     chunked calls."""
     wl = inputs.scaled(inputs.workload_h4096(), f"cdo_h{H}", hidden=H, lengths=lengths)
     xb = inputs.bf16_bits(inputs.gen_x(wl))
@@ -157,7 +157,7 @@ def test_dweight_is_the_canonical_order_bit_for_bit(H, lengths, bwd_path):
     dyb = inputs.bf16_bits(inputs.gen_dy(wl))
     _, rstd64 = oracle.rmsnorm_fwd_bf16(xb, wb, wl.eps)
     rstd32 = rstd64.astype(np.float32)
-    want = oracle.cdo_v1_dweight_f32(xb, dyb, rstd32)
+    want = oracle.cdo_v2_dweight_f32(xb, dyb, rstd32)
     data = pu.make_data(wl)
     T = wl.n_logical
     for cell in (layouts.full(wl), layouts.chunked_packed(wl, chunk=23),
@@ -178,7 +178,7 @@ def test_dweight_is_the_canonical_order_bit_for_bit(H, lengths, bwd_path):
         got = acc.finalize().cpu().numpy()
         torch.cuda.synchronize()
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (H, cell.name)
-    print(f"[cdo] H={H} ({bwd_path}): GPU dweight == CDO-v1 emulation bit for bit", flush=True)
+    print(f"[cdo] H={H} ({bwd_path}): GPU dweight == CDO-v2 emulation bit for bit", flush=True)
 
 
 @pytest.mark.parametrize("H", [24, 128, 520, 1024, 1032, 4096, 5120, 9000])

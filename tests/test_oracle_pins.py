@@ -4,7 +4,7 @@ Each test checks the oracle against mathematics it does not restate: brute
 force (central finite differences of the forward), closed forms of special
 cases (constant rows, H = 1, zero rows), invariants (scale invariance,
 Euler/homogeneity identities, orthogonality of dx to x when eps = 0), exact
-bit patterns, and the hand-derived CDO-v1 golden case.  A plausible mistake
+bit patterns, and the hand-derived CDO-v2 golden case.  A plausible mistake
 (a dropped term, a wrong sign or index, eps outside the square root, a sum
 instead of a mean, the wrong fold order) fails at least one of them.
 """
@@ -260,9 +260,9 @@ def pin_invalid_layouts_are_refused(orc):
         orc.rmsnorm_bwd(x, w, dy, 1e-6, np.array([0, 1, 3], np.int32), 3)   # out of range
 
 
-# ------------------------------------------------------------ CDO-v1 (FP32)
+# ------------------------------------------------------------ CDO-v2 (FP32)
 def _golden_cases():
-    with open(os.path.join(GOLDEN, "cdo_v1_order.json")) as f:
+    with open(os.path.join(GOLDEN, "cdo_v2_order.json")) as f:
         g = json.load(f)
     out = []
     for c in g["cases"]:
@@ -281,17 +281,17 @@ def _golden_cases():
 
 
 def _expected(c):
-    if "expected_cdo_v1" in c:
-        return c["expected_cdo_v1"]
+    if "expected_cdo_v2" in c:
+        return c["expected_cdo_v2"]
     want = [0.0] * c["hidden"]
-    for col, v in c["expected_cdo_v1_sparse"].items():
+    for col, v in c["expected_cdo_v2_sparse"].items():
         want[int(col)] = v
     return want
 
 
-def pin_cdo_v1_golden_cases(orc):
+def pin_cdo_v2_golden_cases(orc):
     for c, x, dy, rstd in _golden_cases():
-        got = orc.cdo_v1_dweight_f32(x, dy, rstd)
+        got = orc.cdo_v2_dweight_f32(x, dy, rstd)
         assert [float(v) for v in got] == _expected(c), c["name"]
     # the order case really distinguishes the order: a logical left fold differs
     c, x, dy, rstd = _golden_cases()[0]
@@ -301,15 +301,15 @@ def pin_cdo_v1_golden_cases(orc):
     assert [float(v) for v in left] == c["expected_logical_left_fold"]
 
 
-def pin_cdo_v1_golden_cases_are_layout_invariant(orc):
+def pin_cdo_v2_golden_cases_are_layout_invariant(orc):
     for c, x, dy, rstd in _golden_cases():
         T = c["n_logical"]
         perm = _rng(11).permutation(T)
-        got = orc.cdo_v1_dweight_f32(x[perm], dy[perm], rstd[perm], perm.astype(np.int32), T)
+        got = orc.cdo_v2_dweight_f32(x[perm], dy[perm], rstd[perm], perm.astype(np.int32), T)
         assert [float(v) for v in got] == _expected(c), c["name"]
 
 
-def pin_cdo_v1_exact_when_every_partial_is_representable(orc):
+def pin_cdo_v2_exact_when_every_partial_is_representable(orc):
     # small integers: every partial sum is exact in FP32, so the canonical
     # order must reproduce the exact (FP64) dweight bit for bit.
     rng = _rng(12)
@@ -319,12 +319,12 @@ def pin_cdo_v1_exact_when_every_partial_is_representable(orc):
     to_bits = lambda a: (a.view(np.uint32) >> 16).astype(np.uint16)
     x, dy = to_bits(xv), to_bits(dyv)
     rstd = np.ones(T, dtype=np.float32)
-    got = orc.cdo_v1_dweight_f32(x, dy, rstd)
+    got = orc.cdo_v2_dweight_f32(x, dy, rstd)
     exact = np.sum(xv.astype(np.float64) * dyv.astype(np.float64), axis=0)
     np.testing.assert_array_equal(got.astype(np.float64), exact)
 
 
-def pin_cdo_v1_within_fp32_error_bound_of_fp64(orc):
+def pin_cdo_v2_within_fp32_error_bound_of_fp64(orc):
     from invariant_rmsnorm_backward_amd import inputs
     wl = inputs.scaled(inputs.workload_h8(), "h64_t1000", hidden=64, lengths=[300, 200, 500])
     xb = inputs.bf16_bits(inputs.gen_x(wl))
@@ -332,7 +332,7 @@ def pin_cdo_v1_within_fp32_error_bound_of_fp64(orc):
     dyb = inputs.bf16_bits(inputs.gen_dy(wl))
     _, rstd64 = orc.rmsnorm_fwd_bf16(xb, wb, wl.eps)
     rstd32 = rstd64.astype(np.float32)
-    got = orc.cdo_v1_dweight_f32(xb, dyb, rstd32).astype(np.float64)
+    got = orc.cdo_v2_dweight_f32(xb, dyb, rstd32).astype(np.float64)
     # exact-in-FP64 reference with the same FP32 rstd
     x = orc.widen_bf16(xb); dy = orc.widen_bf16(dyb)
     terms = dy * x * rstd32.astype(np.float64)[:, None]
@@ -622,7 +622,7 @@ def test_linear_oracle_pins(pin):
 
 
 # ------------------------------------------------------------- the tests
-PINS = [pin_widen_bf16_exact_bit_patterns, pin_forward_constant_row_closed_form, pin_forward_zero_row_and_eps_inside_sqrt, pin_forward_two_element_worked_example, pin_forward_norm_identity_and_scale_invariance, pin_backward_matches_central_finite_differences_h8_t59, pin_backward_explicit_jacobian, pin_backward_orthogonality_and_radial_identity, pin_dweight_euler_identity, pin_h1_closed_form, pin_zero_row_backward, pin_padding_rows_are_never_read_and_contribute_nothing, pin_inactive_rows_contribute_exactly_zero, pin_oracle_is_layout_invariant, pin_invalid_layouts_are_refused, pin_cdo_v1_golden_cases, pin_cdo_v1_golden_cases_are_layout_invariant, pin_cdo_v1_exact_when_every_partial_is_representable, pin_cdo_v1_within_fp32_error_bound_of_fp64]
+PINS = [pin_widen_bf16_exact_bit_patterns, pin_forward_constant_row_closed_form, pin_forward_zero_row_and_eps_inside_sqrt, pin_forward_two_element_worked_example, pin_forward_norm_identity_and_scale_invariance, pin_backward_matches_central_finite_differences_h8_t59, pin_backward_explicit_jacobian, pin_backward_orthogonality_and_radial_identity, pin_dweight_euler_identity, pin_h1_closed_form, pin_zero_row_backward, pin_padding_rows_are_never_read_and_contribute_nothing, pin_inactive_rows_contribute_exactly_zero, pin_oracle_is_layout_invariant, pin_invalid_layouts_are_refused, pin_cdo_v2_golden_cases, pin_cdo_v2_golden_cases_are_layout_invariant, pin_cdo_v2_exact_when_every_partial_is_representable, pin_cdo_v2_within_fp32_error_bound_of_fp64]
 
 
 def test_widen_bf16_exact_bit_patterns():
@@ -686,17 +686,17 @@ def test_invalid_layouts_are_refused():
     pin_invalid_layouts_are_refused(oracle)
 
 
-def test_cdo_v1_golden_cases():
-    pin_cdo_v1_golden_cases(oracle)
+def test_cdo_v2_golden_cases():
+    pin_cdo_v2_golden_cases(oracle)
 
 
-def test_cdo_v1_golden_cases_are_layout_invariant():
-    pin_cdo_v1_golden_cases_are_layout_invariant(oracle)
+def test_cdo_v2_golden_cases_are_layout_invariant():
+    pin_cdo_v2_golden_cases_are_layout_invariant(oracle)
 
 
-def test_cdo_v1_exact_when_every_partial_is_representable():
-    pin_cdo_v1_exact_when_every_partial_is_representable(oracle)
+def test_cdo_v2_exact_when_every_partial_is_representable():
+    pin_cdo_v2_exact_when_every_partial_is_representable(oracle)
 
 
-def test_cdo_v1_within_fp32_error_bound_of_fp64():
-    pin_cdo_v1_within_fp32_error_bound_of_fp64(oracle)
+def test_cdo_v2_within_fp32_error_bound_of_fp64():
+    pin_cdo_v2_within_fp32_error_bound_of_fp64(oracle)
