@@ -172,3 +172,34 @@ def test_norm_linear_chain_is_invariant_in_every_tensor(k, n, lengths, chunk):
                             ("det_gemm.dX", dX, "dX"), ("rms_norm.dx", dx, "dx")):
         got = harness.bf16_bits_to_f32(out[name])
         assert CONTRACT.accuracy_passes(got, want, tol), name
+
+
+@pytest.mark.parametrize("k,n,lengths", [
+    (64, 72, [9000, 7384, 700]),       # 128 x 128 output tiles, two dW groups
+    (512, 384, [12000, 4500, 1200]),   # 256 x 256 output tiles, two dW groups
+])
+def test_det_gemm_dw_bits_equal_the_exact_sum(k, n, lengths):
+    """Small-integer x and dY (|x|, |dY| <= 3): every product and every partial
+    sum of dW = dY^T X is an integer below 2^24, so every FP32 addition in any
+    order is exact and the canonical order must give the FP64 oracle's value
+    bit for bit, whatever the tile shape, the group split and the layout.
+    A dropped, repeated or misplaced row, a wrong group join or a tile that
+    reads outside its block changes an integer and fails here."""
+    wl = _wl(f"lin_exact_k{k}_n{n}", k, n, lengths)
+    T = wl.n_logical
+    g = torch.Generator().manual_seed(0x6D0E + k)
+    xi = torch.randint(-3, 4, (T, k), generator=g).to(torch.bfloat16)
+    gi = torch.randint(-3, 4, (T, n), generator=g).to(torch.bfloat16)
+    data = adapters.LinearInputs(wl.name, wl, xi.cuda(), inputs.gen_wmat(wl, device="cuda"),
+                                 gi.cuda(), inputs.n_active(wl))
+    xb = xi.view(torch.int16).numpy().view(np.uint16)
+    gb = gi.view(torch.int16).numpy().view(np.uint16)
+    wb = inputs.bf16_bits(inputs.gen_wmat(wl))
+    _, dw_ref, _ = oracle.linear_bwd_bf16(xb, wb, gb)
+    assert np.abs(dw_ref).max() < 2.0 ** 24 and np.all(dw_ref == np.round(dw_ref))
+    want = dw_ref.astype(np.float32)
+    cells = [layouts.full(wl), layouts.chunked_packed(wl, chunk=3001), layouts.permuted(wl),
+             layouts.singleton_aggregate(wl), layouts.padded(wl, T + 77, "left")]
+    for cell in cells:
+        out = adapters.LinearAdapter().run_cell(cell, data)
+        assert np.array_equal(out["dW"].view(np.uint32), want.view(np.uint32)), cell.name

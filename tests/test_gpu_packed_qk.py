@@ -1,7 +1,9 @@
 """Per-head norm inside a packed QKV tensor (no copy of Q or K out of it):
-every output bit equals the contiguous path on the extracted rows, the
-rows of other heads (V) are never written, and dweight stays bitwise
-invariant across layouts of the packed rows."""
+every output matches the FP64 oracle within the tolerance contract (also
+with a padded, permuted token order inside the packed tensor), every output
+bit equals the contiguous path on the extracted rows, the rows of other
+heads (V) are never written, and dweight stays bitwise invariant across
+layouts of the packed rows."""
 import numpy as np
 import pytest
 import torch
@@ -118,3 +120,96 @@ def test_packed_rows_with_a_layout_are_invariant():
     lay.close()
     acc.close()
     acc0.close()
+
+
+def _oracle_side(wl):
+    """FP64 oracle of one side (logical rows t * heads + h), from CPU inputs."""
+    import oracle
+    xb = inputs.bf16_bits(inputs.gen_x(wl))
+    wb = inputs.bf16_bits(inputs.gen_w(wl))
+    gb = inputs.bf16_bits(inputs.gen_dy(wl))
+    y, rstd = oracle.rmsnorm_fwd_bf16(xb, wb, wl.eps)
+    dx, dw, _ = oracle.rmsnorm_bwd_bf16(xb, wb, gb, wl.eps)
+    return {"y": y, "rstd": rstd, "dx": dx, "dweight": dw}
+
+
+@pytest.mark.parametrize("lengths,layout", [([100, 37, 64], "identity"), ([70, 3, 41], "padded_permuted")])
+def test_packed_qk_norm_matches_the_oracle(lengths, layout):
+    """Q and K inside one packed QKV tensor (32 + 8 + 8 heads of 128), run in
+    place, against the FP64 oracle element by element: y, dx (bf16) and
+    rstd, dweight_q, dweight_k (FP32) within the tolerance contract, and more
+    than 99% of y and dx within one bf16 ulp of FP64.  The padded, permuted
+    case puts the tokens in a seeded order with padding tokens between them
+    inside the packed tensor; its outputs are gathered back to logical order."""
+    from tests import parity_utils as pu
+    from invariant_rmsnorm_backward_amd import contract
+    con = contract.load_contract()
+    wq, wk = _side("q", lengths), _side("k", lengths)
+    d, T = wq.hidden, wq.n_tokens
+    hq, hk = wq.heads, wk.heads
+    if layout == "identity":
+        tok = np.arange(T)
+    else:
+        perm = np.random.default_rng(11).permutation(T)
+        tok = np.concatenate([[-1] * 2, perm[: T // 2], [-1] * 5, perm[T // 2:], [-1]])
+    P = len(tok)
+    real = tok >= 0
+    ts = (hq + 2 * hk) * d
+    st = binding.current_stream()
+    phys = torch.from_numpy(np.nonzero(real)[0]).cuda()
+    logi = torch.from_numpy(tok[real]).cuda()
+
+    def packed(q, k):
+        t = torch.zeros((P, ts), dtype=torch.bfloat16, device="cuda")
+        t[phys, : hq * d] = q.view(T, hq * d)[logi]
+        t[phys, hq * d: (hq + hk) * d] = k.view(T, hk * d)[logi]
+        return t
+
+    x = packed(inputs.gen_x(wq, device="cuda"), inputs.gen_x(wk, device="cuda"))
+    dy = packed(inputs.gen_dy(wq, device="cuda"), inputs.gen_dy(wk, device="cuda"))
+    y = torch.full((P, ts), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    dx = y.clone()
+    inv = np.empty(T, dtype=np.int64)
+    inv[tok[real]] = np.nonzero(real)[0]
+    for side, wl, heads, col0 in (("q", wq, hq, 0), ("k", wk, hk, hq * d)):
+        ref = _oracle_side(wl)
+        wv = inputs.gen_w(wl, device="cuda")
+        rows_log = T * heads
+        rl = np.where(tok[:, None] < 0, -1, tok[:, None] * heads + np.arange(heads)[None, :]).reshape(-1)
+        lay = None if layout == "identity" else binding.Layout(rl.astype(np.int32), rows_log)
+        r = torch.empty(P * heads, dtype=torch.float32, device="cuda")
+        acc = binding.DwAccumulator(rows_log, d)
+        xb, yb, gb, db = (t.view(torch.int16)[:, col0:].view(torch.bfloat16) for t in (x, y, dy, dx))
+        lh = None if lay is None else lay.handle
+        binding.rmsnorm_fwd_packed(xb.data_ptr(), wv.data_ptr(), yb.data_ptr(), r.data_ptr(), P,
+                                   heads, d, ts, wl.eps, lh, st)
+        binding.rmsnorm_bwd_dx_packed(xb.data_ptr(), wv.data_ptr(), gb.data_ptr(), r.data_ptr(),
+                                      db.data_ptr(), P, heads, d, ts, lh, acc.handle, st)
+        dw = acc.finalize()
+        torch.cuda.synchronize()
+        # gather the physical outputs to logical row order t * heads + h
+        sl = slice(col0, col0 + heads * d)
+        order = torch.from_numpy(inv).cuda()
+        y_log = y.view(torch.int16)[:, sl][order].reshape(rows_log, d).cpu().numpy().view(np.uint16)
+        dx_log = dx.view(torch.int16)[:, sl][order].reshape(rows_log, d).cpu().numpy().view(np.uint16)
+        r_log = r.view(P, heads)[order].reshape(rows_log).cpu().numpy()
+        got = {"y": (y_log.astype(np.uint32) << 16).view(np.float32).astype(np.float64),
+               "dx": (dx_log.astype(np.uint32) << 16).view(np.float32).astype(np.float64),
+               "rstd": r_log.astype(np.float64), "dweight": dw.cpu().numpy().astype(np.float64)}
+        names = {"y": f"y{side}", "dx": f"d{side}", "rstd": f"rstd_{side}", "dweight": f"dweight_{side}"}
+        for t in ("y", "dx", "rstd", "dweight"):
+            assert con.accuracy_passes(got[t], ref[t], names[t]), (side, layout, t)
+        for t, bits in (("y", y_log), ("dx", dx_log)):
+            frac = pu.bf16_ulp_fraction(bits, ref[t])
+            print(f"[packed-qk] {side} {layout}: {t} within 1 bf16 ulp of FP64: {frac:.5f}", flush=True)
+            assert frac > 0.99, (side, layout, t, frac)
+        if not real.all():
+            pad = torch.from_numpy(np.nonzero(~real)[0]).cuda()
+            assert bool((y.view(torch.int16)[pad, sl] == 0).all())
+            assert bool((dx.view(torch.int16)[pad, sl] == 0).all())
+        acc.close()
+        if lay is not None:
+            lay.close()
+    v0 = (hq + hk) * d
+    for t in (y, dx):
+        assert bool((t.view(torch.int16)[:, v0:] == SENTINEL).all())   # V never written
