@@ -208,12 +208,16 @@ static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnor
         return fail(RMSNORM_EINVAL, "dx must not alias an input");
     }
   }
+  const rbi::PlanHost* plan_host = layout ? &layout->host : nullptr;
   if (acc != nullptr) {
     std::string err;
-    rc = acc->host.register_call(layout ? &layout->host : nullptr, rows, &err);
+    rc = acc->host.check_call(plan_host, rows, &err);
     if (rc != RMSNORM_OK) return fail(rc, err);
   }
-  if (rows == 0) return RMSNORM_OK;
+  if (rows == 0) {
+    if (acc != nullptr) acc->host.commit_call(plan_host);
+    return RMSNORM_OK;
+  }
 
   rbi::BwdArgs a{};
   a.x = x;
@@ -236,6 +240,8 @@ static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnor
   hipError_t e = rbi::launch_bwd(a, with_dx, acc != nullptr, reinterpret_cast<hipStream_t>(stream),
                                  recompute);
   if (e != hipSuccess) return hip_fail(e, "rmsnorm backward launch");
+  // the rows count as contributed only once their kernels are enqueued
+  if (acc != nullptr) acc->host.commit_call(plan_host);
   return RMSNORM_OK;
 }
 
@@ -302,6 +308,15 @@ int rmsnorm_dw_finalize(rmsnorm_dw_acc* acc, float* dweight, void* stream) {
   const int32_t H = static_cast<int32_t>(acc->host.hidden);
   hipError_t e;
   if (!spilled.empty()) {
+    // The spilled-block list goes to the device through a pinned host buffer
+    // that the next finalize rewrites: a captured graph would replay that
+    // copy from whatever the buffer holds then.  Refuse rather than record it.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(st, &cap)) != hipSuccess) return hip_fail(e, "capture query");
+    if (cap != hipStreamCaptureStatusNone)
+      return fail(RMSNORM_EUNSUPPORTED,
+                  "finalize of an accumulator with blocks split across calls cannot be captured in "
+                  "a HIP graph (it uploads the spilled-block list); finalize outside the capture");
     if (acc->staging_pending) {
       if ((e = hipEventSynchronize(acc->staged)) != hipSuccess) return hip_fail(e, "staging wait");
       acc->staging_pending = false;

@@ -242,20 +242,26 @@ int det_embedding_dw_contrib(const rmsnorm_bf16* dy, int64_t rows, int64_t dim,
     return fail(RMSNORM_ESTATE, "accumulator already finalized; call det_embedding_dw_acc_reset first");
   if (rows > 0 && (rc = check_tensor(dy, "dy", 16))) return rc;
   std::string err;
-  rc = acc->host.register_call(layout ? &layout->host : nullptr, rows, &err);
+  const rbi::PlanHost* plan_host = layout ? &layout->host : nullptr;
+  rc = acc->host.check_call(plan_host, rows, &err);
   if (rc != RMSNORM_OK) return fail(rc, err);
-  if (rows == 0) return RMSNORM_OK;
+  if (rows == 0) {
+    acc->host.commit_call(plan_host);
+    return RMSNORM_OK;
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (layout == nullptr) {
     if ((e = rbi::emb::launch_blocks(dy, acc->view, dim, acc->d_P, st)) != hipSuccess)
       return hip_fail(e, "embedding block folds");
+    acc->host.commit_call(plan_host);
     acc->mode = kComputed;
     return RMSNORM_OK;
   }
   if ((e = rbi::lin::launch_stage_rows(dy, rows, dim, layout->dev.row_logical, acc->d_dy, st)) !=
       hipSuccess)
     return hip_fail(e, "embedding staging");
+  acc->host.commit_call(plan_host);
   acc->mode = kStaged;
   return RMSNORM_OK;
 }
@@ -300,13 +306,13 @@ int det_embedding_bwd(const rmsnorm_bf16* dy, int64_t rows, int64_t dim, det_emb
   if (rows > 0 && overlaps(dE, acc->vocab * dim * 4, dy, rows * dim * 2))
     return fail(RMSNORM_EINVAL, "dE must not alias dy");
   std::string err;
-  if ((rc = acc->host.register_call(nullptr, rows, &err)) != RMSNORM_OK) return fail(rc, err);
-  std::vector<int32_t> spilled;
-  if ((rc = acc->host.prepare_finalize(&spilled, &err)) != RMSNORM_OK) return fail(rc, err);
+  // the one call holds every logical row: check it, enqueue, then record it
+  if ((rc = acc->host.check_call(nullptr, rows, &err)) != RMSNORM_OK) return fail(rc, err);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if ((e = rbi::emb::launch_bwd_one_call(dy, acc->d_P, acc->view, dim, dE, st)) != hipSuccess)
     return hip_fail(e, "embedding one-call backward");
+  acc->host.commit_call(nullptr);
   acc->mode = kDirect;
   acc->host.finalized = true;
   return RMSNORM_OK;

@@ -137,14 +137,19 @@ int det_gemm_dw_contrib(const rmsnorm_bf16* x, const rmsnorm_bf16* dy, int64_t r
     return fail(RMSNORM_ESTATE, "accumulator already finalized; call det_gemm_dw_acc_reset first");
   if (rows > 0 && ((rc = check_tensor(x, "x", 16)) || (rc = check_tensor(dy, "dy", 16)))) return rc;
   std::string err;
-  rc = acc->host.register_call(layout ? &layout->host : nullptr, rows, &err);
+  const rbi::PlanHost* plan_host = layout ? &layout->host : nullptr;
+  rc = acc->host.check_call(plan_host, rows, &err);
   if (rc != RMSNORM_OK) return fail(rc, err);
-  if (rows == 0) return RMSNORM_OK;
+  if (rows == 0) {
+    acc->host.commit_call(plan_host);
+    return RMSNORM_OK;
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (layout == nullptr) {
     rbi::lin::DwArgs a{dy, x, rows, n, k, acc->d_q};
     if ((e = rbi::lin::launch_dw_groups(a, st)) != hipSuccess) return hip_fail(e, "dW groups");
+    acc->host.commit_call(plan_host);
     acc->mode = kComputed;
     return RMSNORM_OK;
   }
@@ -153,6 +158,7 @@ int det_gemm_dw_contrib(const rmsnorm_bf16* x, const rmsnorm_bf16* dy, int64_t r
       (e = rbi::lin::launch_stage_rows(dy, rows, n, layout->dev.row_logical, acc->d_dy, st)) !=
           hipSuccess)
     return hip_fail(e, "dW staging");
+  acc->host.commit_call(plan_host);
   acc->mode = kStaged;
   return RMSNORM_OK;
 }

@@ -124,7 +124,7 @@ static int64_t first_held(const PlanHost& P, size_t it) {
   return b * kBlockRows;
 }
 
-int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err) {
+int AccHost::check_call(const PlanHost* plan, int64_t rows, std::string* err) const {
   if (finalized) {
     *err = "accumulator already finalized; call rmsnorm_dw_acc_reset first";
     return kEState;
@@ -140,8 +140,6 @@ int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err)
       return kELayout;
     }
     if (n_covered > 0) return dup(first_registered(*this));
-    identity_call = true;
-    n_covered = n_logical;
     return kOk;
   }
   if (plan->n_logical != n_logical) {
@@ -149,10 +147,9 @@ int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err)
            ") differs from the accumulator's (" + std::to_string(n_logical) + ")";
     return kELayout;
   }
-  // Check everything before changing any state.  A block this call holds
-  // completely must have no registered row; a block it holds in part must
-  // not be held completely by an earlier call, and its rows are checked one
-  // by one.
+  // A block this call holds completely must have no registered row; a block
+  // it holds in part must not be held completely by an earlier call, and its
+  // rows are checked one by one.
   for (size_t it = 0; it < plan->item_info.size(); ++it) {
     const int32_t info = plan->item_info[it];
     const int64_t b = info >= 0 ? info : ~info;
@@ -163,6 +160,15 @@ int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err)
   }
   for (int32_t l : plan->partial_rows)
     if (covered[static_cast<size_t>(l)]) return dup(l);
+  return kOk;
+}
+
+void AccHost::commit_call(const PlanHost* plan) {
+  if (plan == nullptr) {
+    identity_call = true;
+    n_covered = n_logical;
+    return;
+  }
   for (int32_t info : plan->item_info) {
     if (info >= 0) {
       block_state[static_cast<size_t>(info)] = kBlockDirect;
@@ -175,7 +181,12 @@ int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err)
   if (!plan->item_info.empty()) blocks_dirty = true;
   if (!plan->partial_rows.empty()) rows_dirty = true;
   n_covered += plan->n_real;
-  return kOk;
+}
+
+int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err) {
+  const int rc = check_call(plan, rows, err);
+  if (rc == kOk) commit_call(plan);
+  return rc;
 }
 
 int AccHost::prepare_finalize(std::vector<int32_t>* spilled, std::string* err) const {

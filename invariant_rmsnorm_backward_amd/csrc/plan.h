@@ -78,7 +78,12 @@ struct AccHost {
   void init(int64_t T, int64_t H);
   void reset();
   // Registers one call.  plan == nullptr means the identity map over `rows`
-  // rows (all blocks complete).  Checks everything before changing state.
+  // rows (all blocks complete).  check_call validates without changing any
+  // state; commit_call records a call that check_call accepted, once its
+  // kernels are enqueued (a launch that fails leaves the accumulator as it
+  // was); register_call does both.
+  int check_call(const PlanHost* plan, int64_t rows, std::string* err) const;
+  void commit_call(const PlanHost* plan);
   int register_call(const PlanHost* plan, int64_t rows, std::string* err);
   // Checks that every logical row contributed exactly once and lists the
   // spilled blocks in ascending order.

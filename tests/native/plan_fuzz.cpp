@@ -188,6 +188,26 @@ int main() {
   CHECK(A.register_call(nullptr, 100, &err) == kEState);
   A.reset();
   CHECK(A.register_call(nullptr, 100, &err) == kOk);
+  // check_call changes nothing: a call whose launch fails after the check is
+  // never counted, so the accumulator still misses its rows at finalize
+  A.reset();
+  CHECK(A.check_call(nullptr, 100, &err) == kOk);
+  CHECK(A.prepare_finalize(&sp, &err) == kECoverage);
+  CHECK(A.check_call(nullptr, 100, &err) == kOk);   // still accepted: nothing was recorded
+  A.commit_call(nullptr);
+  CHECK(A.prepare_finalize(&sp, &err) == kOk);
+  CHECK(A.check_call(nullptr, 100, &err) == kECoverage);
+  {
+    PlanHost P;
+    std::vector<int32_t> rl = {5, 70, 71};
+    CHECK(build_plan(rl.data(), (int64_t)rl.size(), 100, &P, &err) == kOk);
+    AccHost B;
+    B.init(100, 16);
+    CHECK(B.check_call(&P, 3, &err) == kOk);
+    CHECK(B.check_call(&P, 3, &err) == kOk);          // unchanged by the first check
+    B.commit_call(&P);
+    CHECK(B.check_call(&P, 3, &err) == kECoverage);   // now the rows are recorded
+  }
   std::printf("plan fuzz: %s\n", fails ? "FAILED" : "ok");
   return fails ? 1 : 0;
 }

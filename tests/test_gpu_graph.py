@@ -98,3 +98,47 @@ def test_graph_replay_of_a_chunked_step_matches_eager(H, sizes, recompute):
         c["lay"].close()
     acc_e.close()
     acc_g.close()
+
+
+def test_finalize_with_split_blocks_is_refused_under_capture():
+    """A finalize that has spilled blocks to rebuild uploads their list from a
+    pinned host buffer; under stream capture it returns RMSNORM_EUNSUPPORTED
+    (nothing is recorded), and the same finalize outside the capture gives
+    the one-call dweight bits."""
+    H = 4096
+    wl = inputs.scaled(inputs.workload_h4096(), "graph_split_h4096", hidden=H, lengths=[100, 60])
+    data = pu.make_data(wl)
+    T = wl.n_logical
+    cell = layouts.chunked_packed(wl, [100, 60])              # block 1 is split across the calls
+    acc = binding.DwAccumulator(T, H)
+    lays = []
+    for c in cell.calls:
+        a, b = int(c.row_logical[0]), int(c.row_logical[-1]) + 1
+        lay = binding.Layout(c.row_logical, T)
+        lays.append(lay)
+        _, r = binding.fwd(data.x[a:b], data.w, data.eps, lay)
+        binding.bwd(data.x[a:b], data.w, data.dy[a:b], r, lay, acc)
+    torch.cuda.synchronize()
+    dw = torch.empty(H, dtype=torch.float32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    refused = None
+    with torch.cuda.graph(g):
+        dw.zero_()
+        try:
+            acc.finalize(dweight=dw)
+        except binding.RmsNormError as e:
+            refused = e
+    torch.cuda.synchronize()
+    assert refused is not None and refused.code == binding.EUNSUPPORTED, refused
+    acc.finalize(dweight=dw)                                   # outside the capture
+    acc1 = binding.DwAccumulator(T, H)
+    _, r1 = binding.fwd(data.x, data.w, data.eps)
+    binding.bwd(data.x, data.w, data.dy, r1, acc=acc1)
+    dw1 = acc1.finalize()
+    torch.cuda.synchronize()
+    assert torch.equal(dw.view(torch.int32), dw1.view(torch.int32))
+    del g
+    for lay in lays:
+        lay.close()
+    acc.close()
+    acc1.close()
