@@ -229,8 +229,23 @@ def assert_gradient_batch_invariant(op, configs: Sequence[Cell], contract: Toler
         cr = CellResult(c.name, status[c.name], c.call_shapes, sum(k.n_pad for k in c.calls))
         if c.name != reference_cell and status[c.name] == GREEN and ref is not None:
             got_all = results[c.name]
-            names_in_order = [t for t in order if t in got_all] + [t for t in got_all if t not in order]
+            # every tensor either cell produced: one the other lacks is a drift
+            # (a layout that drops a gradient must not be judged green)
+            names = list(ref) + [t for t in got_all if t not in ref]
+            names_in_order = [t for t in order if t in names] + [t for t in names if t not in order]
             for t in names_in_order:
+                if t not in got_all or t not in ref:
+                    v = TensorVerdict(op_name, t, "gradient_invariance", c.name, False, False, -1,
+                                      max_abs=float("inf"), max_rel=float("inf"),
+                                      mean_abs=float("inf"), p99_abs=float("inf"))
+                    cr.verdicts.append(v)
+                    inv.append(v)
+                    note(v)
+                    cr.status = RED_VERDICT
+                    if cr.first_drift is None:
+                        cr.first_drift = t
+                        attribution[c.name] = t
+                    continue
                 got = got_all[t]
                 want = ref[t]
                 same = contract.invariance_passes(_bits(got), _bits(want))

@@ -1,7 +1,8 @@
-"""Falsifiability of the harness with synthetic CPU operators ("WS1 C4 (#270)
-closeout evidence", "The matrix is falsifiable": a layout-sensitive operator
-must be judged red, a logical-identity-only operator green; B=N is one call,
-chunking splits it, padding reaches the operator)."""
+"""The harness can fail: synthetic CPU operators show that an operator whose
+result follows the physical layout is judged red and one that sees only
+logical identity green, that the one-call cell really is one call, that
+chunked cells really split it and that padding rows reach the operator
+("WS1 C4 (#270) closeout evidence", section "The matrix is falsifiable")."""
 import numpy as np
 import pytest
 
@@ -84,6 +85,29 @@ class LayoutBlindOp(LogicalOrderOp):
 
     def run_cell(self, cell, data):
         return super().run_cell(layouts.full(data.wl), data)
+
+
+class DropsDweightWhenChunked(LogicalOrderOp):
+    """Correct everywhere, except that chunked cells return no dweight."""
+    name = "drops_dweight_when_chunked"
+
+    def run_cell(self, cell, data):
+        out = super().run_cell(cell, data)
+        if cell.name.startswith("BN/chunked"):
+            del out["dweight"]
+        return out
+
+
+class ExtraTensorWhenChunked(LogicalOrderOp):
+    """Correct everywhere, except that chunked cells return a tensor the
+    reference cell does not have."""
+    name = "extra_tensor_when_chunked"
+
+    def run_cell(self, cell, data):
+        out = super().run_cell(cell, data)
+        if cell.name.startswith("BN/chunked"):
+            out["stray"] = np.zeros(3, dtype=np.float32)
+        return out
 
 
 def _wl():
@@ -255,3 +279,18 @@ def test_chain_drift_is_attributed_to_the_first_drifting_tensor():
                                                    data=_Data(wl), raise_on_red=False)
     assert rep2.chain_attribution["BN/chunked"] == "a.stat"
     assert "a.y" not in rep2.chain_attribution.values()
+
+
+@pytest.mark.parametrize("op", [DropsDweightWhenChunked(), ExtraTensorWhenChunked()])
+def test_a_missing_or_extra_tensor_is_red(op):
+    """A cell that omits a gradient the reference cell has (or returns one it
+    lacks) is a red verdict on that tensor, not a green cell or an exception."""
+    wl = _wl()
+    rep = harness.assert_gradient_batch_invariant(op, layouts.page_matrix(wl), CONTRACT,
+                                                  data=_Data(wl), raise_on_red=False)
+    by = {c.name: c for c in rep.cells}
+    bad = "dweight" if isinstance(op, DropsDweightWhenChunked) else "stray"
+    assert by["BN/chunked"].status == harness.RED_VERDICT
+    assert by["BN/chunked"].first_drift == bad
+    assert by["BN/permuted"].status == harness.GREEN
+    assert not rep.strict and rep.first_failure["tensor"] == bad
