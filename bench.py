@@ -370,12 +370,15 @@ def gemm_cpu_baseline(x_bits, w_bits, dy_bits, budget_rows=24):
                       f"{dt:.1f} s timed"}
 
 
-def measure_det_gemm(args, torch, np, binding, inputs):
+def measure_det_gemm(args, torch, np, binding, inputs, layouts):
     """One step = y = x W^T, dX = dY W and dW = dY^T X (one B=N call into the
-    canonical accumulator, then finalize) on the linear workload; inputs
-    resident in HBM.  torch.matmul (hipBLASLt, not batch invariant) on the same
-    three products is timed beside it as a reference point."""
-    wl = inputs.workload_linear()
+    canonical accumulator, then finalize) on the linear workload (--op
+    det_gemm) or the LM head (--op lm_head: N = the 32,000-token vocabulary);
+    inputs resident in HBM.  torch.matmul (hipBLASLt, not batch invariant) on
+    the same three products is timed beside it as a reference point, and the
+    dW of the chunked-512 cell (64 calls with layouts, staged rows) beside the
+    one-call dW."""
+    wl = inputs.workload_lmhead() if args.op == "lm_head" else inputs.workload_linear()
     T, K, N = wl.n_logical, wl.hidden, wl.out_features
     st = torch.cuda.current_stream()
     sh = st.cuda_stream
@@ -387,6 +390,8 @@ def measure_det_gemm(args, torch, np, binding, inputs):
     dx = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
     dw = torch.empty((N, K), dtype=torch.float32, device="cuda")
     acc = binding.GemmDwAccumulator(T, N, K)
+    G = (T + 16383) // 16384
+    acc_bytes = {"q": 4 * G * N * K, "staging": 2 * T * (N + K)}
 
     def fwd():
         binding.det_gemm_fwd(x.data_ptr(), w.data_ptr(), y.data_ptr(), T, N, K, None, sh)
@@ -423,7 +428,27 @@ def measure_det_gemm(args, torch, np, binding, inputs):
         step()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) / K_ * 1e3
+    # the chunked-512 cell's dW: every call's rows staged by logical index
+    # (no call holds a whole 16384-row group), the group chains at finalize
+    chunk_cell = layouts.chunked_packed(wl, chunk=512, name="BN/chunked_512")
+    chunk_lays = [(binding.Layout(c.row_logical, T), int(c.row_logical[0]), c.rows)
+                  for c in chunk_cell.calls]
+
+    def bdw_chunked():
+        for lay, a0, n_rows in chunk_lays:
+            binding.det_gemm_dw_contrib(x[a0:a0 + n_rows].data_ptr(), dy[a0:a0 + n_rows].data_ptr(),
+                                        n_rows, N, K, lay.handle, acc.handle, sh)
+        binding.det_gemm_dw_finalize(acc.handle, dw.data_ptr(), sh)
+        binding.det_gemm_dw_acc_reset(acc.handle, sh)
+
     ph = {"fwd": timed(fwd, K_), "dx": timed(bdx, K_), "dw": timed(bdw, K_)}
+    dw_one = dw.clone()
+    bdw_chunked()
+    torch.cuda.synchronize()
+    chunk_same = bool(torch.equal(dw.view(torch.int32), dw_one.view(torch.int32)))
+    ph["dw_chunked512"] = timed(bdw_chunked, max(1, K_ // 2))
+    for lay, _, _ in chunk_lays:
+        lay.close()
     lib_ops = {"fwd": lambda: torch.matmul(x, w.t()), "dx": lambda: torch.matmul(dy, w),
                "dw": lambda: torch.matmul(dy.t(), x)}
     lib = {}
@@ -434,7 +459,8 @@ def measure_det_gemm(args, torch, np, binding, inputs):
     value = 3 * gf / (ms_step * 1e-3) / 1e12
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = gemm_cpu_baseline(inputs.bf16_bits(x), inputs.bf16_bits(w), inputs.bf16_bits(dy))
+        cpu = gemm_cpu_baseline(inputs.bf16_bits(x[:32]), inputs.bf16_bits(w), inputs.bf16_bits(dy[:32]),
+                                budget_rows=24 if N <= 8192 else 6)
     out = {
         "metric": GEMM_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K_, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -450,6 +476,8 @@ def measure_det_gemm(args, torch, np, binding, inputs):
         "cpu_baseline": cpu,
         "phases_ms": {k: round(v, 5) for k, v in ph.items()},
         "phases_tflops": {k: round(gf / (v * 1e-3) / 1e12, 1) for k, v in ph.items()},
+        "dw_chunked512_bitwise_equal_to_one_call": chunk_same,
+        "dw_accumulator_bytes": {"group_results": int(acc_bytes["q"]), "staging": int(acc_bytes["staging"])},
         "hipblaslt_torch_matmul_ms": {k: round(v, 5) for k, v in lib.items()},
         "kernel_source_hash": kernel_source_hash(GEMM_KERNEL_SOURCES),
     }
@@ -662,8 +690,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="with --workload: also time the cell's steps captured in one HIP graph and replayed")
     ap.add_argument("--op", default="rms_norm",
-                    choices=["rms_norm", "det_gemm", "det_embedding", "qk_packed"],
-                    help="det_gemm: the linear layer 4096 -> 4096 on 32768 rows; det_embedding: "
+                    choices=["rms_norm", "det_gemm", "lm_head", "det_embedding", "qk_packed"],
+                    help="det_gemm: the linear layer 4096 -> 4096 on 32768 rows; lm_head: the "
+                         "4096 -> 32000 vocabulary projection on 32768 rows; det_embedding: "
                          "a 32000 x 4096 table on 32768 rows (info lines)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -681,8 +710,8 @@ def main():
         sys.exit(2)
     binding.load()
     torch.cuda.set_device(0)
-    if args.op == "det_gemm":
-        measure_det_gemm(args, torch, np, binding, inputs)
+    if args.op in ("det_gemm", "lm_head"):
+        measure_det_gemm(args, torch, np, binding, inputs, layouts)
         return
     if args.op == "det_embedding":
         measure_det_embedding(args, torch, np, binding, inputs)

@@ -30,7 +30,9 @@ struct RowwiseArgs {
 };
 
 // Group results Q[g][n][k] (fp32) of dW = dY^T X over T logical rows in
-// logical order: dy[T][n], x[T][k].
+// logical order: row l of dY at dy + l * n, of X at x + l * k (the caller may
+// shift both pointers so that a call's buffer is addressed by logical row).
+// Groups g_first .. g_first + g_count - 1 are computed (g_count = 0: all).
 struct DwArgs {
   const uint16_t* dy;
   const uint16_t* x;
@@ -38,14 +40,19 @@ struct DwArgs {
   int64_t n;
   int64_t k;
   float* out;
+  int64_t g_first = 0;
+  int64_t g_count = 0;
 };
 
 hipError_t launch_rowwise(const RowwiseArgs& a, bool b_transposed, hipStream_t stream);
 int64_t num_groups(int64_t T);
 hipError_t launch_dw_groups(const DwArgs& a, hipStream_t stream);
 hipError_t launch_group_tree(const float* q, int64_t G, int64_t nk, float* dw, hipStream_t stream);
+// Copies the call's real rows to their logical positions, except rows of the
+// groups whose bit is set in skip_groups (bit g: logical rows of group g).
 hipError_t launch_stage_rows(const uint16_t* src, int64_t rows, int64_t cols,
-                             const int32_t* row_logical, uint16_t* dst, hipStream_t stream);
+                             const int32_t* row_logical, uint16_t* dst, hipStream_t stream,
+                             uint64_t skip_groups = 0);
 hipError_t launch_zero(uint16_t* dst, int64_t n_elems, hipStream_t stream);
 hipError_t launch_zero_f32(float* dst, int64_t n, hipStream_t stream);
 

@@ -401,7 +401,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void dw_group_kernel(DwArgs p) {
   __shared__ __align__(16) uint8_t smem[E::LDS_BYTES];
   const int tmc = (int)((p.n + BM - 1) / BM), tnc = (int)((p.k + BN - 1) / BN);
   const int per_group = tmc * tnc;
-  const int g = (int)blockIdx.x / per_group;
+  const int g = (int)p.g_first + (int)blockIdx.x / per_group;
   int tm, tn;
   xcd_tile((int)blockIdx.x % per_group, tmc, tnc, tm, tn);
   const int64_t n0 = (int64_t)tm * BM, k0 = (int64_t)tn * BN;
@@ -439,19 +439,22 @@ __global__ __launch_bounds__(256) void group_tree_kernel(const float* __restrict
   dw[e] = v[0];
 }
 
-// Rows of one call copied to their logical positions (staging for calls
-// that do not hold every row in order); padding rows are skipped.
+// Rows of one call copied to their logical positions (staging for the rows
+// of groups a call does not hold whole and in order); padding rows and the
+// rows of groups flagged in skip_groups are skipped.
 __global__ __launch_bounds__(256) void stage_rows_kernel(const uint16_t* __restrict__ src,
                                                          int64_t rows, int64_t cols,
                                                          const int32_t* __restrict__ row_logical,
-                                                         uint16_t* __restrict__ dst) {
+                                                         uint16_t* __restrict__ dst,
+                                                         uint64_t skip_groups) {
   const int64_t nchunk = cols / 8;
   const int64_t total = rows * nchunk;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * 256) {
     const int64_t p = i / nchunk, c = i % nchunk;
     const int32_t l = row_logical[p];
-    if (l >= 0)
+    const int64_t g = l / kGroupRows;
+    if (l >= 0 && !(skip_groups != 0 && g < 64 && ((skip_groups >> g) & 1u)))
       *reinterpret_cast<u32x4v_t*>(dst + (int64_t)l * cols + 8 * c) = ld16_nt(src + p * cols + 8 * c);
   }
 }
@@ -497,11 +500,17 @@ static hipError_t dw_go(const DwArgs& a, int64_t G, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_dw_groups(const DwArgs& a, hipStream_t st) {
-  const int64_t G = num_groups(a.T);
-  if (G == 0) return hipSuccess;
-  if (big_tiles(a.n, a.k)) return dw_go<256, 256, 64, 2, 2, 4>(a, G, st);
-  return dw_go<128, 128, 32, 4, 2, 2>(a, G, st);
+hipError_t launch_dw_groups(const DwArgs& a_in, hipStream_t st) {
+  const int64_t total = num_groups(a_in.T);
+  DwArgs a = a_in;
+  if (a.g_count == 0) {
+    a.g_first = 0;
+    a.g_count = total;
+  }
+  if (a.g_count == 0) return hipSuccess;
+  if (a.g_first < 0 || a.g_first + a.g_count > total) return hipErrorInvalidValue;
+  if (big_tiles(a.n, a.k)) return dw_go<256, 256, 64, 2, 2, 4>(a, a.g_count, st);
+  return dw_go<128, 128, 32, 4, 2, 2>(a, a.g_count, st);
 }
 
 hipError_t launch_group_tree(const float* q, int64_t G, int64_t nk, float* dw, hipStream_t st) {
@@ -522,11 +531,13 @@ hipError_t launch_group_tree(const float* q, int64_t G, int64_t nk, float* dw, h
 }
 
 hipError_t launch_stage_rows(const uint16_t* src, int64_t rows, int64_t cols,
-                             const int32_t* row_logical, uint16_t* dst, hipStream_t st) {
+                             const int32_t* row_logical, uint16_t* dst, hipStream_t st,
+                             uint64_t skip_groups) {
   if (rows == 0) return hipSuccess;
   int64_t g = (rows * (cols / 8) + 255) / 256;
   if (g > 4096) g = 4096;
-  stage_rows_kernel<<<dim3((unsigned)g), dim3(256), 0, st>>>(src, rows, cols, row_logical, dst);
+  stage_rows_kernel<<<dim3((unsigned)g), dim3(256), 0, st>>>(src, rows, cols, row_logical, dst,
+                                                              skip_groups);
   return hipGetLastError();
 }
 

@@ -38,8 +38,38 @@ int check_layout(const rmsnorm_layout* layout, int64_t rows) {
   return RMSNORM_OK;
 }
 
-// Rows of the accumulator's staging copy hold data from layout calls.
-enum Mode { kEmpty = 0, kComputed = 1, kStaged = 2 };
+// Where a dW group's chain stands: computed at contrib time from the buffers
+// of the one call that held the whole group in logical order, or staged (its
+// rows copied to the logical-order staging area, the chain runs at finalize).
+enum GroupState : uint8_t { kGroupNone = 0, kGroupComputed = 1, kGroupStaged = 2 };
+
+// The groups a call holds whole, in logical order, as one run of physical
+// rows: for such a group g, the physical row of logical row l is l + off[g].
+struct DirectGroups {
+  std::vector<int64_t> off;
+  std::vector<uint8_t> whole;
+};
+DirectGroups direct_groups(const rbi::PlanHost& plan, int64_t T) {
+  const int64_t G = rbi::lin::num_groups(T);
+  DirectGroups d;
+  d.off.assign(static_cast<size_t>(G), 0);
+  d.whole.assign(static_cast<size_t>(G), 0);
+  std::vector<int64_t> cnt(static_cast<size_t>(G), 0);
+  std::vector<uint8_t> run(static_cast<size_t>(G), 1);
+  for (int64_t p = 0; p < plan.rows; ++p) {
+    const int64_t l = plan.row_logical[static_cast<size_t>(p)];
+    if (l < 0) continue;
+    const size_t g = static_cast<size_t>(l / rbi::lin::kGroupRows);
+    if (cnt[g] == 0) d.off[g] = p - l;
+    else if (p - l != d.off[g]) run[g] = 0;
+    ++cnt[g];
+  }
+  for (int64_t g = 0; g < G; ++g) {
+    const int64_t size = std::min(rbi::lin::kGroupRows, T - g * rbi::lin::kGroupRows);
+    d.whole[static_cast<size_t>(g)] = run[static_cast<size_t>(g)] && cnt[static_cast<size_t>(g)] == size;
+  }
+  return d;
+}
 
 }  // namespace
 
@@ -49,7 +79,7 @@ struct det_gemm_dw_acc {
   float* d_q = nullptr;          // [groups][n][k]
   uint16_t* d_x = nullptr;       // [n_logical][k] staging, logical order
   uint16_t* d_dy = nullptr;      // [n_logical][n]
-  Mode mode = kEmpty;
+  std::vector<uint8_t> group_state;   // GroupState per group
 };
 
 extern "C" {
@@ -105,6 +135,7 @@ int det_gemm_dw_acc_create(det_gemm_dw_acc** out, int64_t n_logical, int64_t n, 
   A->n = n;
   A->k = k;
   A->groups = rbi::lin::num_groups(n_logical);
+  A->group_state.assign(static_cast<size_t>(A->groups), kGroupNone);
   hipError_t e = hipSuccess;
   auto cleanup = [&](const char* what) {
     if (A->d_q) (void)hipFree(A->d_q);
@@ -146,20 +177,48 @@ int det_gemm_dw_contrib(const rmsnorm_bf16* x, const rmsnorm_bf16* dy, int64_t r
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
+  const int64_t T = acc->host.n_logical;
   if (layout == nullptr) {
-    rbi::lin::DwArgs a{dy, x, rows, n, k, acc->d_q};
+    // every row, in logical order: every group's chain runs now
+    rbi::lin::DwArgs a{dy, x, T, n, k, acc->d_q};
     if ((e = rbi::lin::launch_dw_groups(a, st)) != hipSuccess) return hip_fail(e, "dW groups");
     acc->host.commit_call(plan_host);
-    acc->mode = kComputed;
+    std::fill(acc->group_state.begin(), acc->group_state.end(), kGroupComputed);
     return RMSNORM_OK;
   }
-  if ((e = rbi::lin::launch_stage_rows(x, rows, k, layout->dev.row_logical, acc->d_x, st)) !=
-          hipSuccess ||
-      (e = rbi::lin::launch_stage_rows(dy, rows, n, layout->dev.row_logical, acc->d_dy, st)) !=
-          hipSuccess)
+  // Groups this call holds whole and in order run their chains now, from the
+  // call's own buffers (addressed by logical row); the rows of every other
+  // group are staged for the finalize.
+  const DirectGroups dg = direct_groups(layout->host, T);
+  uint64_t direct_mask = 0;
+  bool any_staged = false;
+  for (int64_t g = 0; g < acc->groups; ++g) {
+    if (dg.whole[static_cast<size_t>(g)]) {
+      const int64_t off = dg.off[static_cast<size_t>(g)];
+      rbi::lin::DwArgs a{dy + off * n, x + off * k, T, n, k, acc->d_q, g, 1};
+      if ((e = rbi::lin::launch_dw_groups(a, st)) != hipSuccess) return hip_fail(e, "dW group");
+      direct_mask |= uint64_t(1) << g;
+    } else {
+      any_staged = true;
+    }
+  }
+  if (any_staged &&
+      ((e = rbi::lin::launch_stage_rows(x, rows, k, layout->dev.row_logical, acc->d_x, st,
+                                        direct_mask)) != hipSuccess ||
+       (e = rbi::lin::launch_stage_rows(dy, rows, n, layout->dev.row_logical, acc->d_dy, st,
+                                        direct_mask)) != hipSuccess))
     return hip_fail(e, "dW staging");
   acc->host.commit_call(plan_host);
-  acc->mode = kStaged;
+  // a group touched by this call is either whole here (computed) or split
+  // across calls (staged: all of its rows arrive through the staging copy)
+  std::vector<uint8_t> touched(static_cast<size_t>(acc->groups), 0);
+  for (int32_t l : layout->host.row_logical)
+    if (l >= 0) touched[static_cast<size_t>(l / rbi::lin::kGroupRows)] = 1;
+  for (int64_t g = 0; g < acc->groups; ++g) {
+    if (!touched[static_cast<size_t>(g)]) continue;
+    acc->group_state[static_cast<size_t>(g)] =
+        (direct_mask >> g) & 1u ? kGroupComputed : kGroupStaged;
+  }
   return RMSNORM_OK;
 }
 
@@ -179,9 +238,17 @@ int det_gemm_dw_finalize(det_gemm_dw_acc* acc, float* dw, void* stream) {
     acc->host.finalized = true;
     return RMSNORM_OK;
   }
-  if (acc->mode == kStaged) {
-    rbi::lin::DwArgs a{acc->d_dy, acc->d_x, T, acc->n, acc->k, acc->d_q};
+  // the chains of staged groups, one launch per run of consecutive ones
+  for (int64_t g = 0; g < acc->groups;) {
+    if (acc->group_state[static_cast<size_t>(g)] != kGroupStaged) {
+      ++g;
+      continue;
+    }
+    int64_t g1 = g;
+    while (g1 < acc->groups && acc->group_state[static_cast<size_t>(g1)] == kGroupStaged) ++g1;
+    rbi::lin::DwArgs a{acc->d_dy, acc->d_x, T, acc->n, acc->k, acc->d_q, g, g1 - g};
     if ((e = rbi::lin::launch_dw_groups(a, st)) != hipSuccess) return hip_fail(e, "dW groups");
+    g = g1;
   }
   if ((e = rbi::lin::launch_group_tree(acc->d_q, acc->groups, nk, dw, st)) != hipSuccess)
     return hip_fail(e, "dW group tree");
@@ -193,7 +260,7 @@ int det_gemm_dw_acc_reset(det_gemm_dw_acc* acc, void* stream) {
   (void)stream;
   if (acc == nullptr) return fail(RMSNORM_EINVAL, "accumulator is NULL");
   acc->host.reset();
-  acc->mode = kEmpty;
+  std::fill(acc->group_state.begin(), acc->group_state.end(), kGroupNone);
   return RMSNORM_OK;
 }
 

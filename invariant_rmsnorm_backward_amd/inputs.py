@@ -238,6 +238,13 @@ def workload_linear() -> Workload:
                     description="linear layer 4096 -> 4096, 8 x 4096 tokens, all active")
 
 
+def workload_lmhead() -> Workload:
+    """The LM-head projection of a 32,000-token vocabulary on the same rows:
+    det_gemm with N = vocabulary (reading R20)."""
+    return Workload("lmhead_v32000_h4096_t32768", 4096, (4096,) * 8, _seed(8), out_features=32000,
+                    description="LM head 4096 -> 32000 (vocabulary), 8 x 4096 tokens, all active")
+
+
 def workload_embedding() -> Workload:
     return Workload("embedding_v32000_d4096_t32768", 4096, (4096,) * 8, _seed(7), vocab=32000,
                     description="embedding 32000 x 4096, 8 x 4096 tokens, Zipf(1.1) token ids")
@@ -250,6 +257,7 @@ EMBEDDING_WORKLOADS = {
 
 LINEAR_WORKLOADS = {
     "linear_h4096_o4096_t32768": workload_linear,
+    "lmhead_v32000_h4096_t32768": workload_lmhead,
 }
 
 

@@ -185,6 +185,45 @@ def test_linear_h4096_o4096_t32768_sampled():
          f"{float(np.max(np.abs(dw_got - dw_ref)) / max(np.max(np.abs(dw_ref)), 1e-30)):.2e}")
 
 
+def test_lmhead_v32000_h4096_t32768_sampled():
+    """The LM-head weight gradient at its real shape: det_gemm with N = the
+    32,000-token vocabulary, K = 4096, on 32768 rows (two dW groups).  dX and
+    dW bitwise across B=N, 8 x B=1 and chunked-512 calls (the B=N call runs
+    both group chains at once, the others stage the rows of the groups they
+    split); sampled dX and dW entries against the FP64 oracle and within the
+    error bound of the canonical order."""
+    wl = inputs.workload_lmhead()
+    data = adapters.make_linear_inputs(wl, device="cuda")
+    cells = [layouts.full(wl), layouts.singleton_aggregate(wl),
+             layouts.chunked_packed(wl, chunk=512, name="BN/chunked_512")]
+    _invariance("det_gemm", cells, data, wl.name)
+    out = adapters.LinearAdapter().run_cell(cells[0], data)
+    xb = inputs.bf16_bits(data.x)
+    wb = inputs.bf16_bits(data.w)
+    dyb = inputs.bf16_bits(data.dy)
+    del data
+    rng = np.random.default_rng(13)
+    T, N, K = wl.n_logical, wl.out_features, wl.hidden
+    n_s = 96
+    r = np.concatenate([[0, T - 1, 16383, 16384], rng.integers(0, T, n_s)])
+    kk = np.concatenate([[0, K - 1, 255, 256], rng.integers(0, K, n_s)])
+    nn = np.concatenate([[0, N - 1, 31999 - 255, 256], rng.integers(0, N, n_s)])
+    m = len(r)
+    kind = np.concatenate([np.zeros(m, np.int32), np.ones(m, np.int32), np.full(m, 2, np.int32)])
+    ia = np.concatenate([r, nn, nn]).astype(np.int64)
+    ib = np.concatenate([kk, kk, kk]).astype(np.int64)
+    _log(f"{wl.name}: {3 * m} oracle samples")
+    ref = oracle.linear_sample_bf16(xb, wb, dyb, kind, ia, ib)
+    dx_ref, dw_ref, dwa = ref[:m], ref[m:2 * m], ref[2 * m:]
+    dx_got = harness.bf16_bits_to_f32(out["dX"][r, kk]).astype(np.float64)
+    dw_got = out["dW"][nn, kk].astype(np.float64)
+    assert CONTRACT.accuracy_passes(dx_got, dx_ref, "dX")
+    assert CONTRACT.accuracy_passes(dw_got, dw_ref, "dW")
+    assert np.all(np.abs(dw_got - dw_ref) <= (1024 + 2) * 2.0 ** -24 * dwa + 1e-30)
+    _log(f"{wl.name}: sampled dX/dW match the oracle; max |dW err| / |dW| scale "
+         f"{float(np.max(np.abs(dw_got - dw_ref)) / max(np.max(np.abs(dw_ref)), 1e-30)):.2e}")
+
+
 def test_embedding_v32000_d4096_t32768_sampled_columns():
     """det_embedding at full size (32768 rows, 32000 x 4096 table, Zipf ids):
     dE bitwise across B=N, 8 x B=1 and chunked-512 calls; on sampled columns,
