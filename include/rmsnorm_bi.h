@@ -71,6 +71,7 @@ typedef struct rmsnorm_dw_acc rmsnorm_dw_acc;
 #define RMSNORM_ECOVERAGE (-4)    /* a logical row contributed twice, or missing at finalize */
 #define RMSNORM_ESTATE (-5)       /* contribution after finalize without reset */
 #define RMSNORM_EHIP (-6)         /* HIP runtime error (message attached) */
+#define RMSNORM_ESPILL (-7)       /* a bounded accumulator's spill area is full */
 
 /* Largest supported hidden size. */
 int rmsnorm_max_hidden(void);
@@ -129,12 +130,19 @@ int rmsnorm_bwd_dx_packed(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rm
                           rmsnorm_dw_acc* acc, void* stream);
 
 /* dweight contributions only (no dx): same accumulation as rmsnorm_bwd_dx
- * with an accumulator; rstd is an input (any FP32 values). */
+ * with an accumulator; rstd is an input (any FP32 values).  Defined by the
+ * opening note of "WS1 C4 (#270) closeout evidence" (parameter gradients
+ * built from per-logical-row FP32 contributions) and by the "Acceptance
+ * criteria" of "[WS1 Closeout][Backward] ..." (a fixed aggregation order
+ * shared by the B=1 and B=N runs). */
 int rmsnorm_dw_contrib(const rmsnorm_bf16* x, const rmsnorm_bf16* dy, const float* rstd,
                        int64_t rows, int64_t hidden, const rmsnorm_layout* layout,
                        rmsnorm_dw_acc* acc, void* stream);
 
-/* dweight[hidden] (FP32) of everything contributed since create/reset.  Every
+/* dweight[hidden] (FP32) of everything contributed since create/reset: the
+ * logical aggregation after which "[WS1 Closeout][Backward] ...", section
+ * "Acceptance criteria", requires batch/chunk gradients to be bitwise equal;
+ * here the CDO-v2 block tree above, over the block partials.  Every
  * logical row 0..n_logical-1 must have contributed exactly once
  * (RMSNORM_ECOVERAGE otherwise).  After finalize the accumulator refuses
  * further contributions until rmsnorm_dw_acc_reset.  Calling finalize again
@@ -143,7 +151,11 @@ int rmsnorm_dw_contrib(const rmsnorm_bf16* x, const rmsnorm_bf16* dy, const floa
  * has passed them if they are then reused from another stream. */
 int rmsnorm_dw_finalize(rmsnorm_dw_acc* acc, float* dweight, void* stream);
 
-/* Plan for one call: row_logical_host[rows] (HOST memory, int32) maps each
+/* Plan for one call: the physical layout of "WS1 C4 (#270) closeout
+ * evidence", section "Acceptance map" (adapters run on the configuration's
+ * physical layout and gradients return through the C2 logical map), and the
+ * same logical row multiset of the "Scope" of "[WS1 Closeout][Backward]
+ * ...".  row_logical_host[rows] (HOST memory, int32) maps each
  * physical row to its canonical logical index in [0, n_logical), or -1 for a
  * padding row; each logical index may appear at most once.  The plan is
  * validated (RMSNORM_ELAYOUT on a bad map), built on the host and copied to
@@ -155,18 +167,39 @@ int rmsnorm_layout_create(rmsnorm_layout** out, const int32_t* row_logical_host,
 /* Frees a layout (waits for the device to finish with it).  NULL is a no-op. */
 int rmsnorm_layout_destroy(rmsnorm_layout* layout);
 
-/* Host-only validation and statistics of a row map, without creating a
+/* Host-only validation and statistics of a row map (the plan above),
+ * without creating a
  * layout or touching the GPU: stats[0] = blocks touched, stats[1] = blocks
  * held completely, stats[2] = blocks held in part (their rows are spilled),
  * stats[3] = padding rows, stats[4] = real rows. */
 int rmsnorm_layout_check(const int32_t* row_logical_host, int64_t rows, int64_t n_logical,
                          int64_t stats[5]);
 
-/* Accumulator for n_logical logical rows of width hidden.  Allocates device
- * memory: block partials (ceil(n_logical/64)*hidden FP32), spill rows for
- * blocks that arrive in pieces (n_logical*hidden FP32) and a small scratch
- * for the cross-block tree, plus a pinned host staging buffer. */
+/* Accumulator for n_logical logical rows of width hidden: the holder of the
+ * fixed aggregation order that "[WS1 Closeout][Backward] ...", section
+ * "Acceptance criteria", asks the B=1 and B=N runs to share, and of the
+ * per-logical-row FP32 contributions named in the opening note of "WS1 C4
+ * (#270) closeout evidence".  Allocates device
+ * memory: block partials (ceil(n_logical/64)*hidden FP32), the stream sums
+ * of blocks the stream-owner backward leaves unjoined (three times that),
+ * spill rows for blocks that arrive in pieces (n_logical*hidden FP32; see
+ * rmsnorm_dw_acc_create_bounded for less) and a small scratch for the
+ * cross-block tree, plus a pinned host staging buffer. */
 int rmsnorm_dw_acc_create(rmsnorm_dw_acc** out, int64_t n_logical, int64_t hidden, void* stream);
+
+/* The same accumulator with a bounded spill area: room for max_spill_rows
+ * spill rows (rounded up to whole 64-row slots, and never more than
+ * rmsnorm_dw_acc_create allocates) instead of n_logical.  Every canonical
+ * block that some call holds only in part takes one 64-row slot, from the
+ * first call that holds it in part until reset; blocks a call holds
+ * completely take none.  A call that would need a slot beyond the bound is
+ * refused with RMSNORM_ESPILL, and a call that holds more than 32 blocks in
+ * part with RMSNORM_EUNSUPPORTED, before anything is enqueued and without
+ * changing the accumulator.  Results are bit for bit those of an unbounded
+ * accumulator.  max_spill_rows < 0 is RMSNORM_EINVAL; 0 admits only calls
+ * that hold every block they touch completely. */
+int rmsnorm_dw_acc_create_bounded(rmsnorm_dw_acc** out, int64_t n_logical, int64_t hidden,
+                                  int64_t max_spill_rows, void* stream);
 
 /* Forget all contributions (host bookkeeping only; nothing is enqueued). */
 int rmsnorm_dw_acc_reset(rmsnorm_dw_acc* acc, void* stream);
@@ -183,31 +216,44 @@ const char* rmsnorm_backend_info(void);
 
 /* Work distribution of the backward for hidden > 256 (a tuning knob; no
  * output bit depends on it).  A call whose rows touch fewer than `blocks`
- * canonical 64-row blocks runs the backward in two passes -- row-parallel
- * dx and the dweight fold split over 512-column tiles, side by side in one
- * launch -- instead of the fused kernel whose workgroups own whole blocks,
- * so that small calls (chunked prefill pieces, single samples) still occupy
- * the whole GPU (default 96 blocks, the measured crossover).  Both paths
- * run the same per-row and per-block arithmetic, so dx and dweight are
- * bitwise the same either way.  0 disables the two-pass path; a negative
- * value restores the default.  If `previous` is non-NULL it receives the
- * threshold in force before the call.  Process-wide; takes effect for
- * backward calls enqueued afterwards.  Always returns RMSNORM_OK. */
+ * canonical 64-row blocks does not run the fused kernel, whose workgroups
+ * each own whole blocks, so that small calls (chunked prefill pieces, single
+ * samples) still occupy the whole GPU (default 96 blocks, the measured
+ * crossover).  It runs either the stream-owner kernel (see
+ * rmsnorm_set_stream_threshold) or the two-pass path: dx rows and the
+ * dweight fold split over 256-column units, side by side in one launch.
+ * Every path runs the same per-row and per-block arithmetic, so dx and
+ * dweight are bitwise the same whichever runs.  0 disables the other paths;
+ * a negative value restores the default.  If `previous` is non-NULL it
+ * receives the threshold in force before the call.  Process-wide; takes
+ * effect for backward calls enqueued afterwards.  Always returns
+ * RMSNORM_OK. */
 int rmsnorm_set_split_threshold(int64_t blocks, int64_t* previous);
 
+/* Lower bound of the stream-owner backward (a tuning knob; no output bit
+ * depends on it).  A call below the split threshold that touches at least
+ * `blocks` canonical blocks, writes dx and folds into an accumulator runs
+ * one workgroup per fold stream of each block: four workgroups per block
+ * walk its four streams (the fused kernel's per-row code), x and dy are
+ * read once, and the four stream sums are joined by rmsnorm_dw_finalize in
+ * the fused kernel's order.  Smaller calls, dx-only and
+ * contributions-only calls take the two-pass path (default 48 blocks).  A
+ * negative value restores the default; a value at or above the split
+ * threshold disables the stream-owner path.  `previous` and scope as for
+ * rmsnorm_set_split_threshold.  Always returns RMSNORM_OK. */
+int rmsnorm_set_stream_threshold(int64_t blocks, int64_t* previous);
+
 /* Workgroup count of the fused backward (a tuning and test knob; no output
- * bit depends on it).  For rows of 2048, 3072 and 4096 columns the fused
- * backward launches at most as many block-owning workgroups as the GPU
- * holds at once (kernel occupancy x compute units); workgroup g takes the
- * canonical blocks g, g + groups, g + 2*groups, ... and loads the first row
- * of its next block while it folds the current block's partial.  Other
- * widths run one workgroup per block and ignore the cap.  `groups` > 0 caps
- * the count (1 makes one workgroup walk every block); 0 or a negative value
- * restores the default.  Each block's arithmetic is the same whichever
- * workgroup runs it, so dx and dweight are bitwise the same for every cap.
- * If `previous` is non-NULL it receives the cap in force before the call
- * (0 = default).  Process-wide; takes effect for backward calls enqueued
- * afterwards.  Always returns RMSNORM_OK. */
+ * bit depends on it).  The fused backward launches at most as many
+ * block-owning workgroups as the GPU holds at once (one or two per compute
+ * unit, by row width); workgroup g takes the canonical blocks g, g + groups,
+ * g + 2*groups, ... and keeps the next rows in flight across block
+ * boundaries.  `groups` > 0 caps the count (1 makes one workgroup walk every
+ * block); 0 or a negative value restores the default.  Each block's
+ * arithmetic is the same whichever workgroup runs it, so dx and dweight are
+ * bitwise the same for every cap.  If `previous` is non-NULL it receives the
+ * cap in force before the call (0 = default).  Process-wide; takes effect
+ * for backward calls enqueued afterwards.  Always returns RMSNORM_OK. */
 int rmsnorm_set_workgroup_cap(int64_t groups, int64_t* previous);
 
 /* Allocation-free one-call backward, for callers that cannot allocate device

@@ -89,6 +89,21 @@ def _poisoned(rows: int, hidden: int, device) -> torch.Tensor:
     return t.view(torch.bfloat16)
 
 
+def spill_bound(cell: Cell, n_logical: int) -> Optional[int]:
+    """Spill rows a cell's calls can need (64 per block a call holds in part),
+    for a bounded accumulator; None (unbounded) when a call holds more blocks
+    in part than a bounded accumulator takes per call."""
+    rows = 0
+    for call in cell.calls:
+        if call.row_logical is None:
+            continue
+        part = binding.rmsnorm_layout_check(call.row_logical, n_logical)["partial_blocks"]
+        if part > binding.SPILL_TABLE:
+            return None
+        rows += 64 * part
+    return rows
+
+
 class RmsNormAdapter(GradientAdapter):
     name = "rms_norm"
     grad_names = ("dx", "dweight")
@@ -105,7 +120,7 @@ class RmsNormAdapter(GradientAdapter):
         x, w, dy = data.x, data.w, data.dy
         T, H = x.shape
         dev = x.device
-        acc = binding.DwAccumulator(T, H)
+        acc = binding.DwAccumulator(T, H, max_spill_rows=spill_bound(cell, T))
         y_l = torch.zeros_like(x)
         dx_l = torch.zeros_like(x)
         rstd_l = torch.zeros(T, dtype=torch.float32, device=dev)

@@ -18,15 +18,18 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "librmsnorm_bi.so")
 
-OK, EINVAL, EUNSUPPORTED, ELAYOUT, ECOVERAGE, ESTATE, EHIP = 0, -1, -2, -3, -4, -5, -6
+OK, EINVAL, EUNSUPPORTED, ELAYOUT, ECOVERAGE, ESTATE, EHIP, ESPILL = 0, -1, -2, -3, -4, -5, -6, -7
+SPILL_TABLE = 32   # blocks a call may hold in part with a bounded accumulator
 STATUS_NAMES = {OK: "OK", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", ELAYOUT: "ELAYOUT",
-                ECOVERAGE: "ECOVERAGE", ESTATE: "ESTATE", EHIP: "EHIP"}
+                ECOVERAGE: "ECOVERAGE", ESTATE: "ESTATE", EHIP: "EHIP", ESPILL: "ESPILL"}
 
 EXPORTED = ("rmsnorm_max_hidden", "rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_contrib",
             "rmsnorm_dw_finalize", "rmsnorm_layout_create", "rmsnorm_layout_destroy",
-            "rmsnorm_layout_check", "rmsnorm_dw_acc_create", "rmsnorm_dw_acc_reset",
+            "rmsnorm_layout_check", "rmsnorm_dw_acc_create", "rmsnorm_dw_acc_create_bounded",
+            "rmsnorm_dw_acc_reset",
             "rmsnorm_dw_acc_destroy", "rmsnorm_last_error", "rmsnorm_backend_info",
-            "rmsnorm_set_split_threshold", "rmsnorm_set_workgroup_cap", "rmsnorm_stream_copy",
+            "rmsnorm_set_split_threshold", "rmsnorm_set_stream_threshold",
+            "rmsnorm_set_workgroup_cap", "rmsnorm_stream_copy",
             "rmsnorm_fwd_packed",
             "rmsnorm_bwd_dx_packed", "rmsnorm_bwd_dx_recompute", "rmsnorm_bwd_noalloc",
             "rmsnorm_bwd_noalloc_max_scratch",
@@ -76,11 +79,13 @@ def load() -> ctypes.CDLL:
         "rmsnorm_layout_destroy": ([P], I32),
         "rmsnorm_layout_check": ([P, I64, I64, ctypes.POINTER(ctypes.c_int64)], I32),
         "rmsnorm_dw_acc_create": ([PP, I64, I64, P], I32),
+        "rmsnorm_dw_acc_create_bounded": ([PP, I64, I64, I64, P], I32),
         "rmsnorm_dw_acc_reset": ([P, P], I32),
         "rmsnorm_dw_acc_destroy": ([P], I32),
         "rmsnorm_last_error": ([], ctypes.c_char_p),
         "rmsnorm_backend_info": ([], ctypes.c_char_p),
         "rmsnorm_set_split_threshold": ([I64, ctypes.POINTER(ctypes.c_int64)], I32),
+        "rmsnorm_set_stream_threshold": ([I64, ctypes.POINTER(ctypes.c_int64)], I32),
         "rmsnorm_set_workgroup_cap": ([I64, ctypes.POINTER(ctypes.c_int64)], I32),
         "rmsnorm_stream_copy": ([P, P, I64, P], I32),
         "rmsnorm_fwd_packed": ([P, P, P, P, I64, I64, I64, I64, ctypes.c_float, P, P], I32),
@@ -193,6 +198,15 @@ def rmsnorm_dw_acc_create(n_logical: int, hidden: int, stream: Optional[int]) ->
     return out.value
 
 
+def rmsnorm_dw_acc_create_bounded(n_logical: int, hidden: int, max_spill_rows: int,
+                                  stream: Optional[int]) -> int:
+    out = ctypes.c_void_p()
+    _check(load().rmsnorm_dw_acc_create_bounded(ctypes.byref(out), n_logical, hidden,
+                                                max_spill_rows, stream),
+           "rmsnorm_dw_acc_create_bounded")
+    return out.value
+
+
 def rmsnorm_dw_acc_reset(acc: Optional[int], stream: Optional[int]) -> None:
     _check(load().rmsnorm_dw_acc_reset(acc, stream), "rmsnorm_dw_acc_reset")
 
@@ -222,6 +236,15 @@ def rmsnorm_set_split_threshold(blocks: int) -> int:
     prev = ctypes.c_int64(0)
     _check(load().rmsnorm_set_split_threshold(int(blocks), ctypes.byref(prev)),
            "rmsnorm_set_split_threshold")
+    return int(prev.value)
+
+
+def rmsnorm_set_stream_threshold(blocks: int) -> int:
+    """Sets the lower bound (in canonical blocks) of the stream-owner backward
+    (negative restores the default); returns the previous one."""
+    prev = ctypes.c_int64(0)
+    _check(load().rmsnorm_set_stream_threshold(int(blocks), ctypes.byref(prev)),
+           "rmsnorm_set_stream_threshold")
     return int(prev.value)
 
 
@@ -357,11 +380,17 @@ class Layout:
 class DwAccumulator:
     """Owns a canonical dweight accumulator."""
 
-    def __init__(self, n_logical: int, hidden: int, stream: Optional[int] = None):
+    def __init__(self, n_logical: int, hidden: int, stream: Optional[int] = None,
+                 max_spill_rows: Optional[int] = None):
+        """max_spill_rows: bound on the spill area (None: unbounded)."""
         self.n_logical = int(n_logical)
         self.hidden = int(hidden)
-        self.handle = rmsnorm_dw_acc_create(self.n_logical, self.hidden,
-                                            current_stream() if stream is None else stream)
+        st = current_stream() if stream is None else stream
+        if max_spill_rows is None:
+            self.handle = rmsnorm_dw_acc_create(self.n_logical, self.hidden, st)
+        else:
+            self.handle = rmsnorm_dw_acc_create_bounded(self.n_logical, self.hidden,
+                                                        int(max_spill_rows), st)
 
     def reset(self, stream: Optional[int] = None):
         rmsnorm_dw_acc_reset(self.handle, current_stream() if stream is None else stream)

@@ -9,6 +9,7 @@ The host-only plan code is compiled with g++ (it has no HIP dependency).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -49,7 +50,7 @@ def build(verbose: bool = False, save_temps: Optional[str] = None) -> str:
     obj_dir = os.path.join(PKG, "_build")
     os.makedirs(obj_dir, exist_ok=True)
     os.makedirs(LIB_DIR, exist_ok=True)
-    objs = []
+    cmds = []
     for src in SOURCES_HIP:
         obj = os.path.join(obj_dir, src + ".o")
         cmd = [HIPCC, *HIP_FLAGS]
@@ -59,18 +60,19 @@ def build(verbose: bool = False, save_temps: Optional[str] = None) -> str:
             os.makedirs(save_temps, exist_ok=True)
             cmd += ["-save-temps=obj"]
             obj = os.path.join(save_temps, src + ".o")
-        cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd))
-        _run(cmd)
-        objs.append(obj)
+        cmds.append((cmd + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
     for src in SOURCES_CXX:
         obj = os.path.join(obj_dir, src + ".o")
-        cmd = ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
+        cmds.append((["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+    if verbose:
+        for cmd, _ in cmds:
             print(" ".join(cmd))
-        _run(cmd)
-        objs.append(obj)
+    # the translation units are independent: compile them side by side
+    # (-save-temps writes shared intermediate names, so it stays serial)
+    workers = 1 if save_temps else min(len(cmds), os.cpu_count() or 1, 8)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
+        list(pool.map(_run, [cmd for cmd, _ in cmds]))
+    objs = [obj for _, obj in cmds]
     tmp = LIB_PATH + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB_PATH)

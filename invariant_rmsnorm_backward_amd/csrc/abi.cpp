@@ -83,6 +83,9 @@ struct rmsnorm_dw_acc {
   float* d_P = nullptr;
   float* d_S = nullptr;
   float* d_tmp = nullptr;
+  float* d_Q = nullptr;           // stream sums q1..q3 of blocks in stream form
+  int32_t* d_form = nullptr;      // per block: 1 = in stream form
+  bool stream_form = false;       // some call since reset took the stream-owner path
   int32_t* d_spilled = nullptr;
   int32_t* h_spilled = nullptr;   // pinned staging for the spilled-block list
   hipEvent_t staged = nullptr;
@@ -103,13 +106,20 @@ const char* rmsnorm_backend_info(void) {
          "64-chunk group, pairwise tree over the groups with +0.0 padding; no atomics; "
          "fwd=rows_per_workgroup|lanes_per_row; bwd=fused dx+dW by resident block-owning "
          "workgroups, two or four rows in flight, next rows prefetched across blocks "
-         "(calls with few blocks: row-parallel dx + 256-column dW units), nt loads/stores; "
+         "(calls with a few dozen blocks: one workgroup per fold stream; with fewer: "
+         "row-parallel dx + 256-column dW units on one XCD per block), nt loads/stores; "
          "max_hidden=10240";
 }
 
 int rmsnorm_set_split_threshold(int64_t blocks, int64_t* previous) {
   if (previous != nullptr) *previous = rbi::split_items();
   rbi::set_split_items(blocks);
+  return RMSNORM_OK;
+}
+
+int rmsnorm_set_stream_threshold(int64_t blocks, int64_t* previous) {
+  if (previous != nullptr) *previous = rbi::stream_items();
+  rbi::set_stream_items(blocks);
   return RMSNORM_OK;
 }
 
@@ -209,9 +219,10 @@ static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnor
     }
   }
   const rbi::PlanHost* plan_host = layout ? &layout->host : nullptr;
+  rbi::SpillTable spill;
   if (acc != nullptr) {
     std::string err;
-    rc = acc->host.check_call(plan_host, rows, &err);
+    rc = acc->host.check_call(plan_host, rows, &err, &spill);
     if (rc != RMSNORM_OK) return fail(rc, err);
   }
   if (rows == 0) {
@@ -228,6 +239,9 @@ static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnor
   a.dx = with_dx ? dx : nullptr;
   a.P = acc ? acc->d_P : nullptr;
   a.S = acc ? acc->d_S : nullptr;
+  a.Q = acc ? acc->d_Q : nullptr;
+  a.form = acc ? acc->d_form : nullptr;
+  a.spill = spill;
   a.rows = rows;
   a.hidden = static_cast<int32_t>(hidden);
   a.pack = pk;
@@ -237,11 +251,16 @@ static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnor
     a.plan.n_items = static_cast<int32_t>(rbi::num_blocks(rows));
     a.plan.n_pad = 0;
   }
+  const bool stream_path =
+      rbi::bwd_path(a, with_dx, acc != nullptr, recompute) == rbi::BwdPath::kStream;
   hipError_t e = rbi::launch_bwd(a, with_dx, acc != nullptr, reinterpret_cast<hipStream_t>(stream),
                                  recompute);
   if (e != hipSuccess) return hip_fail(e, "rmsnorm backward launch");
   // the rows count as contributed only once their kernels are enqueued
-  if (acc != nullptr) acc->host.commit_call(plan_host);
+  if (acc != nullptr) {
+    acc->host.commit_call(plan_host);
+    if (stream_path) acc->stream_form = true;
+  }
   return RMSNORM_OK;
 }
 
@@ -300,13 +319,21 @@ int rmsnorm_dw_finalize(rmsnorm_dw_acc* acc, float* dweight, void* stream) {
   if (acc == nullptr) return fail(RMSNORM_EINVAL, "accumulator is NULL");
   int rc;
   if ((rc = check_tensor(dweight, "dweight", 4))) return rc;
-  std::vector<int32_t> spilled;
+  std::vector<int32_t> spilled, slots;
   std::string err;
-  rc = acc->host.prepare_finalize(&spilled, &err);
+  rc = acc->host.prepare_finalize(&spilled, &err, &slots);
   if (rc != RMSNORM_OK) return fail(rc, err);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int32_t H = static_cast<int32_t>(acc->host.hidden);
   hipError_t e;
+  if (acc->stream_form) {
+    // blocks in stream form get their in-block tree (once: a repeated
+    // finalize finds them joined); before the rebuild, which rewrites every
+    // spilled block whatever its flag says
+    if ((e = rbi::launch_join(acc->d_P, acc->d_Q, acc->d_form, acc->host.nb, H, st)) != hipSuccess)
+      return hip_fail(e, "stream-form join");
+    acc->stream_form = false;
+  }
   if (!spilled.empty()) {
     // The spilled-block list goes to the device through a pinned host buffer
     // that the next finalize rewrites: a captured graph would replay that
@@ -321,15 +348,18 @@ int rmsnorm_dw_finalize(rmsnorm_dw_acc* acc, float* dweight, void* stream) {
       if ((e = hipEventSynchronize(acc->staged)) != hipSuccess) return hip_fail(e, "staging wait");
       acc->staging_pending = false;
     }
-    std::memcpy(acc->h_spilled, spilled.data(), spilled.size() * sizeof(int32_t));
-    if ((e = hipMemcpyAsync(acc->d_spilled, acc->h_spilled, spilled.size() * sizeof(int32_t),
+    // blocks, then their spill slots
+    const size_t n = spilled.size();
+    std::memcpy(acc->h_spilled, spilled.data(), n * sizeof(int32_t));
+    std::memcpy(acc->h_spilled + n, slots.data(), n * sizeof(int32_t));
+    if ((e = hipMemcpyAsync(acc->d_spilled, acc->h_spilled, 2 * n * sizeof(int32_t),
                             hipMemcpyHostToDevice, st)) != hipSuccess)
       return hip_fail(e, "spilled-block list upload");
     if ((e = hipEventRecord(acc->staged, st)) != hipSuccess) return hip_fail(e, "event record");
     acc->staging_pending = true;
-    if ((e = rbi::launch_rebuild(acc->d_S, acc->d_P, acc->d_spilled,
-                                 static_cast<int32_t>(spilled.size()), acc->host.n_logical, H,
-                                 st)) != hipSuccess)
+    if ((e = rbi::launch_rebuild(acc->d_S, acc->d_P, acc->d_spilled, acc->d_spilled + n,
+                                 static_cast<int32_t>(n), acc->host.n_logical, H, st)) !=
+        hipSuccess)
       return hip_fail(e, "spilled-block rebuild");
   }
   if ((e = rbi::launch_tree(acc->d_P, acc->host.nb, acc->d_tmp, dweight, H, st)) != hipSuccess)
@@ -469,8 +499,9 @@ int rmsnorm_layout_destroy(rmsnorm_layout* layout) {
   return RMSNORM_OK;
 }
 
-int rmsnorm_dw_acc_create(rmsnorm_dw_acc** out, int64_t n_logical, int64_t hidden, void* stream) {
-  (void)stream;
+// max_spill_rows < 0: spill rows for every logical row (unbounded).
+static int acc_create(rmsnorm_dw_acc** out, int64_t n_logical, int64_t hidden,
+                      int64_t max_spill_rows) {
   if (out == nullptr) return fail(RMSNORM_EINVAL, "out is NULL");
   *out = nullptr;
   int rc;
@@ -478,14 +509,22 @@ int rmsnorm_dw_acc_create(rmsnorm_dw_acc** out, int64_t n_logical, int64_t hidde
   if (n_logical < 0) return fail(RMSNORM_EINVAL, "n_logical must be non-negative");
   if (n_logical > INT32_MAX) return fail(RMSNORM_EUNSUPPORTED, "n_logical must be below 2^31");
   auto* A = new rmsnorm_dw_acc();
-  A->host.init(n_logical, hidden);
+  const int64_t nb_all = rbi::num_blocks(n_logical);
+  // a bounded area holds whole 64-row slots, never more than every block
+  const int64_t spill_slots =
+      max_spill_rows < 0 ? -1 : std::min(nb_all, rbi::num_blocks(max_spill_rows));
+  A->host.init(n_logical, hidden, spill_slots);
   const int64_t nb = A->host.nb;
+  const size_t spill_rows = spill_slots < 0 ? static_cast<size_t>(n_logical)
+                                            : static_cast<size_t>(spill_slots) * rbi::kBlockRows;
   const size_t H = static_cast<size_t>(hidden);
   hipError_t e = hipSuccess;
   auto cleanup = [&](const char* what) {
     if (A->d_P) (void)hipFree(A->d_P);
     if (A->d_S) (void)hipFree(A->d_S);
     if (A->d_tmp) (void)hipFree(A->d_tmp);
+    if (A->d_Q) (void)hipFree(A->d_Q);
+    if (A->d_form) (void)hipFree(A->d_form);
     if (A->d_spilled) (void)hipFree(A->d_spilled);
     if (A->h_spilled) (void)hipHostFree(A->h_spilled);
     if (A->staged) (void)hipEventDestroy(A->staged);
@@ -494,15 +533,21 @@ int rmsnorm_dw_acc_create(rmsnorm_dw_acc** out, int64_t n_logical, int64_t hidde
   };
   if ((e = hipMalloc(&A->d_P, std::max<size_t>(1, nb * H) * sizeof(float))) != hipSuccess)
     return cleanup("block partial allocation");
-  if ((e = hipMalloc(&A->d_S, std::max<size_t>(1, n_logical * H) * sizeof(float))) != hipSuccess)
+  if ((e = hipMalloc(&A->d_S, std::max<size_t>(1, spill_rows * H) * sizeof(float))) != hipSuccess)
     return cleanup("spill allocation");
   if ((e = hipMalloc(&A->d_tmp, std::max<size_t>(1, rbi::tree_scratch_rows(nb) * H) *
                                     sizeof(float))) != hipSuccess)
     return cleanup("tree scratch allocation");
-  if ((e = hipMalloc(&A->d_spilled, std::max<size_t>(1, nb) * sizeof(int32_t))) != hipSuccess)
+  if ((e = hipMalloc(&A->d_Q, std::max<size_t>(1, 3 * nb * H) * sizeof(float))) != hipSuccess)
+    return cleanup("stream-form allocation");
+  if ((e = hipMalloc(&A->d_form, std::max<size_t>(1, nb) * sizeof(int32_t))) != hipSuccess)
+    return cleanup("stream-form flag allocation");
+  if ((e = hipMemset(A->d_form, 0, std::max<size_t>(1, nb) * sizeof(int32_t))) != hipSuccess)
+    return cleanup("stream-form flag clear");
+  if ((e = hipMalloc(&A->d_spilled, std::max<size_t>(1, 2 * nb) * sizeof(int32_t))) != hipSuccess)
     return cleanup("spill list allocation");
   if ((e = hipHostMalloc(reinterpret_cast<void**>(&A->h_spilled),
-                         std::max<size_t>(1, nb) * sizeof(int32_t), hipHostMallocDefault)) !=
+                         std::max<size_t>(1, 2 * nb) * sizeof(int32_t), hipHostMallocDefault)) !=
       hipSuccess)
     return cleanup("pinned staging allocation");
   if ((e = hipEventCreateWithFlags(&A->staged, hipEventDisableTiming)) != hipSuccess)
@@ -511,10 +556,23 @@ int rmsnorm_dw_acc_create(rmsnorm_dw_acc** out, int64_t n_logical, int64_t hidde
   return RMSNORM_OK;
 }
 
+int rmsnorm_dw_acc_create(rmsnorm_dw_acc** out, int64_t n_logical, int64_t hidden, void* stream) {
+  (void)stream;
+  return acc_create(out, n_logical, hidden, -1);
+}
+
+int rmsnorm_dw_acc_create_bounded(rmsnorm_dw_acc** out, int64_t n_logical, int64_t hidden,
+                                  int64_t max_spill_rows, void* stream) {
+  (void)stream;
+  if (max_spill_rows < 0) return fail(RMSNORM_EINVAL, "max_spill_rows must be non-negative");
+  return acc_create(out, n_logical, hidden, max_spill_rows);
+}
+
 int rmsnorm_dw_acc_reset(rmsnorm_dw_acc* acc, void* stream) {
   (void)stream;
   if (acc == nullptr) return fail(RMSNORM_EINVAL, "accumulator is NULL");
   acc->host.reset();
+  acc->stream_form = false;
   return RMSNORM_OK;
 }
 
@@ -524,6 +582,8 @@ int rmsnorm_dw_acc_destroy(rmsnorm_dw_acc* acc) {
   (void)hipFree(acc->d_P);
   (void)hipFree(acc->d_S);
   (void)hipFree(acc->d_tmp);
+  (void)hipFree(acc->d_Q);
+  (void)hipFree(acc->d_form);
   (void)hipFree(acc->d_spilled);
   (void)hipHostFree(acc->h_spilled);
   (void)hipEventDestroy(acc->staged);

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "plan.h"
+
 namespace rbi {
 
 constexpr int kMaxHidden = 10240;
@@ -19,6 +21,14 @@ constexpr int kMaxHidden = 10240;
 constexpr int64_t kDefaultSplitItems = 96;   // measured crossover: 64 vs 128 blocks
 void set_split_items(int64_t n);   // n < 0 restores the default
 int64_t split_items();
+
+// Calls that touch at least the stream threshold of blocks (and fewer than
+// the split threshold), and compute dx and dweight contributions together
+// into an accumulator, run the stream-owner backward: one workgroup per fold
+// stream of each block, x and dy read once.  Same arithmetic again.
+constexpr int64_t kDefaultStreamItems = 48;
+void set_stream_items(int64_t n);   // n < 0 restores the default
+int64_t stream_items();
 
 // Cap on the workgroups of the looping fused backward (hidden 2048, 3072,
 // 4096; 0: what the chip holds at once, occupancy x compute units).  A
@@ -66,7 +76,7 @@ struct BwdArgs {
   const float* rstd;
   uint16_t* dx;        // nullptr when only dweight contributions are wanted
   float* P;            // block partials [nb][hidden]
-  float* S;            // spill rows [n_logical][hidden]
+  float* S;            // spill rows, 64 per slot: [slots * 64][hidden]
   int64_t rows;
   int32_t hidden;
   PlanDev plan;
@@ -75,7 +85,20 @@ struct BwdArgs {
   // Fused wide backward: workgroups that loop over the work items (set by
   // the launcher; the padding-row workgroups come after them).
   int32_t item_groups = 0;
+  // Stream form (both nullptr: the stream-owner backward is not used).  A
+  // block in stream form has q0 in P[b], q1..q3 in Q[b*3 .. b*3+2] and
+  // form[b] = 1; every other writer of a complete block's P[b] sets
+  // form[b] = 0.
+  float* Q = nullptr;         // [nb * 3][hidden]
+  int32_t* form = nullptr;    // [nb]
+  // Spill slots of the call's partial items (n = -1: slot = block).
+  SpillTable spill{};
 };
+
+// Which kernel family a backward call runs (decided by hidden, the call's
+// block count, the thresholds above and whether stream form is available).
+enum class BwdPath { kSmall, kSplit, kStream, kFused };
+BwdPath bwd_path(const BwdArgs& a, bool with_dx, bool with_dw, bool recompute);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // dst[0..n16) = src[0..n16) in 16-byte units with the kernels' streaming
@@ -86,9 +109,13 @@ hipError_t launch_stream_copy(const void* src, void* dst, int64_t n16, hipStream
 // order (bitwise the saved rstd); needs with_dx and contiguous rows.
 hipError_t launch_bwd(const BwdArgs& a, bool with_dx, bool with_dw, hipStream_t stream,
                       bool recompute = false);
-// Rebuild the partials of spilled blocks from their spill rows.
-hipError_t launch_rebuild(const float* S, float* P, const int32_t* blocks, int32_t n_blocks,
-                          int64_t n_logical, int32_t hidden, hipStream_t stream);
+// P[b] = (q0 + q1) + (q2 + q3) for every block b < nb with form[b] == 1.
+hipError_t launch_join(float* P, const float* Q, const int32_t* form, int64_t nb, int32_t hidden,
+                       hipStream_t stream);
+// Rebuild the partials of spilled blocks from their spill rows (block
+// blocks[i] from slot slots[i]: rows slots[i]*64 .. +63 of S).
+hipError_t launch_rebuild(const float* S, float* P, const int32_t* blocks, const int32_t* slots,
+                          int32_t n_blocks, int64_t n_logical, int32_t hidden, hipStream_t stream);
 // dweight = pairwise tree over P[0..nb); tmp needs ceil(nb/32) * hidden floats.
 hipError_t launch_tree(const float* P, int64_t nb, float* tmp, float* dweight, int32_t hidden,
                        hipStream_t stream);

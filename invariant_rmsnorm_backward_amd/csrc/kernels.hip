@@ -221,6 +221,17 @@ __device__ __forceinline__ int slot_row_t(const BwdArgs& a, int item, int blk, i
   return r < a.rows ? (int)r : -1;
 }
 
+// First spill row of work item `item` (a block the call holds in part): its
+// block's own rows, or the slot the accumulator gave the block.  The host
+// lists every partial item of the call in the table.
+__device__ __forceinline__ int64_t spill_row0(const BwdArgs& a, int item, int blk) {
+  if (a.spill.n < 0) return (int64_t)blk * kBlockRows;
+  int slot = 0;
+  for (int j = 0; j < a.spill.n; ++j)
+    if (a.spill.item[j] == item) slot = a.spill.slot[j];
+  return (int64_t)slot * kBlockRows;
+}
+
 // Wide rows (hidden > 256).  A row is held by a team of TW wavefronts:
 // wavefront h of the team holds the chunk groups h*V .. h*V+V-1, where chunk
 // group g is the 64 16-byte chunks 64g .. 64g+63 and lane l holds chunk
@@ -586,6 +597,7 @@ __global__ __launch_bounds__(64 * TW * TEAMS) void bwd_team_kernel(BwdArgs a) {
     }
   };
   auto store_p = [&](int blk) {
+    if (a.form != nullptr && tid == 0) a.form[blk] = 0;
     float* Pb = a.P + (int64_t)blk * H + ln.base;
 #pragma unroll
     for (int k = 0; k < V; ++k) {
@@ -673,7 +685,7 @@ __global__ __launch_bounds__(64 * TW * TEAMS) void bwd_team_kernel(BwdArgs a) {
         const int p = __builtin_amdgcn_readlane(sp, j);
         const float r = RC ? 0.0f : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sr), j));
         float* srow = nullptr;
-        if (DW && !CPL) srow = a.S + ((int64_t)blk * kBlockRows + slot_of(j)) * H + ln.base;
+        if (DW && !CPL) srow = a.S + (spill_row0(a, item, blk) + slot_of(j)) * H + ln.base;
         ops.template row<DW, CPL>(j, p, xb[u], db[u], r, acc, srow);
         if (DW && CPL && (j & 15) == 15) pass_end(j >> 4, blk);
         // keep the scheduler from interleaving steps: the row loads are
@@ -705,26 +717,144 @@ __global__ __launch_bounds__(64 * TW * TEAMS) void bwd_team_kernel(BwdArgs a) {
   }
 }
 
+// ------------------------------------------- stream-owner backward (mid-size calls)
+// A call with a few dozen blocks would run the fused kernel on a few dozen
+// compute units, and the two-pass path reads x and dy twice.  Here every
+// fold stream of every block is a workgroup of its own: workgroup (item, w)
+// walks the stream's slots w, w+4, ..., w+60 in ascending order with the
+// fused kernel's per-row code -- dx of each row and the running FP32 sum of
+// its contributions -- so x and dy are read once and the call fills four
+// times as many compute units as it has blocks.  The stream sums are the
+// fused kernel's q0..q3 bit for bit; they stay apart (q0 in P[b], q1..q3 in
+// Q[b], form[b] = 1) until the finalize step forms P[b] = (q0 + q1) +
+// (q2 + q3), the fused kernel's in-block tree.  A block held in part writes
+// its rows' contributions to the spill rows, as on every path.  The team is
+// TW wavefronts, V chunk groups each; PD rows are in flight ahead of the
+// one being reduced.
+template <int V, int TW, int PD, bool FULL, bool PLAN>
+__global__ __launch_bounds__(64 * TW) void bwd_stream_kernel(BwdArgs a) {
+  using Ops = RowOps<V, TW, 1, FULL, true, false>;
+  using L = typename Ops::L;
+  constexpr int COLS = L::COLS;
+  constexpr int THREADS = 64 * TW;
+  constexpr int R = PD + 1;                   // row buffers in the ring
+  static_assert(kSlotsPerStream % R == 0, "the ring must divide the stream");
+  __shared__ float w_s[COLS];
+  __shared__ float xch[Ops::XCH_FLOATS];
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int H = FULL ? COLS : a.hidden;
+  const int nchunk = H >> 3;
+  const int n_wg = a.plan.n_items * kStreams;
+  if ((int)blockIdx.x >= n_wg) {
+    // padding rows: dx = 0, nothing read (one row per wavefront)
+    const int idx = ((int)blockIdx.x - n_wg) * TW + wv;
+    if (idx < a.plan.n_pad) {
+      uint16_t* d = a.dx + (int64_t)a.plan.pad_rows[idx] * H;
+      for (int q = lane; q < nchunk; q += 64) store16_stream(d + q * 8, make_uint4(0, 0, 0, 0));
+    }
+    return;
+  }
+  const int item = (int)blockIdx.x >> 2;
+  const int w = (int)blockIdx.x & (kStreams - 1);
+  int blk = item;
+  bool complete = true;
+  if (PLAN) {
+    const int info = a.plan.item_info[item];
+    complete = info >= 0;
+    blk = complete ? info : ~info;
+  }
+  const L ln{lane, wv, nchunk, (wv * V * 64 + lane) * 8};
+  const Ops ops{a, w_s, xch, ln, 0, H};
+  // lane i (< 16) holds the physical row and rstd of the stream's step i
+  const int sp = slot_row_t<PLAN>(a, item, blk, w + kStreams * (lane & (kSlotsPerStream - 1)));
+  const float sr = a.rstd[sp >= 0 ? sp : 0];
+  uint4 xb[R][V], db[R][V];
+#pragma unroll
+  for (int j = 0; j < PD; ++j) ops.load(__builtin_amdgcn_readlane(sp, j), xb[j], db[j]);
+  stage_w<COLS, THREADS>(a, w_s, tid, nchunk);
+  float acc[V * 8];
+#pragma unroll
+  for (int i = 0; i < V * 8; ++i) acc[i] = 0.0f;
+
+  auto run = [&](auto complete_tag) {
+    constexpr bool CPL = decltype(complete_tag)::value;
+#pragma unroll
+    for (int j0 = 0; j0 < kSlotsPerStream; j0 += R) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int j = j0 + u;
+        const int jn = j + PD;
+        // past the stream's end: dummy loads of row 0 keep the wait counts exact
+        const int pj = jn < kSlotsPerStream ? __builtin_amdgcn_readlane(sp, jn) : -1;
+        ops.load(pj, xb[(u + PD) % R], db[(u + PD) % R]);
+        const int p = __builtin_amdgcn_readlane(sp, j);
+        const float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sr), j));
+        float* srow = nullptr;
+        if (!CPL) srow = a.S + (spill_row0(a, item, blk) + w + kStreams * j) * H + ln.base;
+        ops.template row<true, CPL>(j, p, xb[u], db[u], r, acc, srow);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  if (!PLAN || complete) {
+    run(std::true_type{});
+    float* dst = w == 0 ? a.P + (int64_t)blk * H : a.Q + ((int64_t)blk * 3 + (w - 1)) * H;
+    dst += ln.base;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      if (ln.in_row(k)) {
+        store_f4(dst + k * 512, acc[k * 8 + 0], acc[k * 8 + 1], acc[k * 8 + 2], acc[k * 8 + 3]);
+        store_f4(dst + k * 512 + 4, acc[k * 8 + 4], acc[k * 8 + 5], acc[k * 8 + 6], acc[k * 8 + 7]);
+      }
+    }
+    if (w == 0 && tid == 0) a.form[blk] = 1;
+  } else {
+    run(std::false_type{});
+  }
+}
+
 // ------------------------------------------------- two-pass backward (few blocks)
 // A call that touches few canonical blocks would leave most compute units
 // idle in the fused kernel (one workgroup per block).  It runs two passes
 // instead, with enough workgroups for the whole chip between them:
-//   dx rows (dx_rows_part): dx, two physical rows per workgroup step, one per
-//     team, through the same per-row code as the fused kernel (RowOps with
-//     the dweight part compiled out); the dot order does not depend on the
-//     row shape, so every dx bit equals the fused kernel's;
+//   dx rows (dx_pair_part): dx, two rows of a work item per workgroup, one
+//     per team, through the same per-row code as the fused kernel (RowOps
+//     with the dweight part compiled out); the dot order does not depend on
+//     the row shape, so every dx bit equals the fused kernel's;
 //   dweight columns (dw_cols_part): the dweight contributions and the
 //     in-block stream fold of one canonical block over 256 columns, with the
 //     same operations in the same order as the fused kernel, so the block
 //     partials and spill rows are bitwise the same.
-// The passes are independent, so one launch (bwd_split_kernel) runs both:
-// its first workgroups fold column units, the rest compute dx rows, and the
-// two work lists overlap on the chip.  The column pass reads x and dy a
-// second time; for the calls that take this path they are small enough to
-// be served largely from the last-level cache.
+// The passes are independent, so one launch (bwd_split_kernel) runs both,
+// and the column pass reads x and dy a second time: the work list places
+// both readers of a block on one XCD, so the second read is served from L2.
+
+// One dx task: slots 2*pair + team of work item `item` (one row per team),
+// through the fused kernel's per-row code with the dweight part compiled out.
+// Work list of the two-pass launch (see bwd_split_kernel).
+struct SplitMap {
+  int groups;     // item groups: workgroup wg serves items wg % groups + groups * i
+  int col_wg;     // column-unit workgroups per item (0: no dweight)
+  int row_wg;     // dx workgroups per item, two rows each (0: no dx)
+  int n_slices;   // 256-column slices of a row
+  int task_wg;    // workgroups before the padding-row ones
+};
+
+// 8 groups (one per XCD) when the items spread evenly enough over them (at
+// most 25% more workgroups than items would need); else 1, which spreads
+// every item's tasks over the whole chip.
+static int split_groups(int n_items) {
+  const int g = 8;
+  if (n_items < g) return 1;
+  const int64_t padded = (int64_t)((n_items + g - 1) / g) * g;
+  return padded * 4 <= (int64_t)n_items * 5 ? g : 1;
+}
+
 template <int V, int TW, bool FULL, bool PLAN>
-__device__ __forceinline__ void dx_rows_part(const BwdArgs& a, float* w_s, float* xch, int64_t wg,
-                                             int64_t n_wg) {
+__device__ __forceinline__ void dx_pair_part(const BwdArgs& a, float* w_s, float* xch, int item,
+                                             int pair) {
   constexpr int TEAMS = 2;
   using Ops = RowOps<V, TW, TEAMS, FULL, true, false>;
   using L = typename Ops::L;
@@ -736,30 +866,22 @@ __device__ __forceinline__ void dx_rows_part(const BwdArgs& a, float* w_s, float
   const int half = wv % TW;
   const int H = FULL ? L::COLS : a.hidden;
   const int nchunk = H >> 3;
-  stage_w<L::COLS, THREADS>(a, w_s, tid, nchunk);
+  int blk = item;
+  if (PLAN) {
+    const int info = a.plan.item_info[item];
+    blk = info >= 0 ? info : ~info;
+  }
+  // an absent slot (a block the call holds in part) reads row 0 and writes
+  // nothing; both teams still reach the row's exchange
+  const int p = slot_row_t<PLAN>(a, item, blk, TEAMS * pair + team);
+  const float r = a.rstd[p >= 0 ? p : 0];
   const L ln{lane, half, nchunk, (half * V * 64 + lane) * 8};
   const Ops ops{a, w_s, xch, ln, team, H};
+  uint4 xv[V], dv[V];
+  ops.load(p, xv, dv);
+  stage_w<L::COLS, THREADS>(a, w_s, tid, nchunk);
   float acc[1];
-  const int64_t step = n_wg * TEAMS;
-  int i = 0;
-  // the trip count is the same for every team of the workgroup (the row's
-  // exchange synchronises the workgroup once per step)
-  for (int64_t r0 = wg * TEAMS; r0 < a.rows; r0 += step, ++i) {
-    const int64_t row = r0 + team;
-    int p = row < a.rows ? (int)row : -1;
-    if (PLAN && p >= 0 && a.plan.row_logical[p] < 0) {
-      // padding row: dx = 0, nothing read
-      uint16_t* d = a.dx + (int64_t)p * H + ln.base;
-#pragma unroll
-      for (int k = 0; k < V; ++k)
-        if (ln.in_row(k)) store16_stream(d + k * 512, make_uint4(0, 0, 0, 0));
-      p = -1;
-    }
-    const float r = p >= 0 ? a.rstd[p] : 0.0f;
-    uint4 xv[V], dv[V];
-    ops.load(p, xv, dv);
-    ops.template row<false, true>(i, p, xv, dv, r, acc, nullptr);
-  }
+  ops.template row<false, true>(0, p, xv, dv, r, acc, nullptr);
 }
 
 // One column unit: the canonical block of work item `item` over the 256
@@ -819,7 +941,7 @@ __device__ __forceinline__ void dw_cols_part(const BwdArgs& a, float (*q_s)[256]
         acc[e] = acc[e] + c[e];
       }
       if (!complete && on) {
-        float* srow = a.S + ((int64_t)blk * kBlockRows + stream + kStreams * i) * H + col;
+        float* srow = a.S + (spill_row0(a, item, blk) + stream + kStreams * i) * H + col;
         store_f4_stream(srow, c[0], c[1], c[2], c[3]);
       }
     }
@@ -833,16 +955,21 @@ __device__ __forceinline__ void dw_cols_part(const BwdArgs& a, float (*q_s)[256]
     for (int e = 0; e < 4; ++e)
       o[e] = stream_tree4(acc[e], q_s[0][lane * 4 + e], q_s[1][lane * 4 + e], q_s[2][lane * 4 + e]);
     store_f4(a.P + (int64_t)blk * H + col, o[0], o[1], o[2], o[3]);
+    if (a.form != nullptr && slice == 0 && lane == 0) a.form[blk] = 0;
   }
 }
 
-// Both passes in one launch.  Workgroups 0 .. n_cols_wg-1 fold column units
-// (TW/2 units per workgroup: wavefronts 4u .. 4u+3 take unit (TW/2)*wg + u of
-// the n_units = items x column slices); the following n_rows_wg workgroups
-// compute dx rows.  Either list may be empty (dx alone, contributions alone).
+// Both passes in one launch, as tasks of the call's work items: per item,
+// m.col_wg workgroups of column units (TW/2 units of 256 columns each:
+// wavefronts 4u .. 4u+3 take unit u) and m.row_wg workgroups of dx rows (two
+// rows each).  Either list may be empty (dx alone, contributions alone).
+// Workgroup wg serves item group g = wg % m.groups -- items g, g + groups,
+// ... -- so with 8 groups all tasks of an item run on one XCD (the chip
+// hands consecutive workgroups to its 8 XCDs in turn): the column units and
+// the dx rows read the same rows of x and dy, and the second reader finds
+// them in that XCD's L2.  Workgroups past m.task_wg zero padding rows.
 template <int V, int TW, bool FULL, bool PLAN>
-__global__ __launch_bounds__(128 * TW) void bwd_split_kernel(BwdArgs a, int n_cols_wg, int n_units,
-                                                             int n_slices, int n_rows_wg) {
+__global__ __launch_bounds__(128 * TW) void bwd_split_kernel(BwdArgs a, SplitMap m) {
   using Ops = RowOps<V, TW, 2, FULL, true, false>;
   constexpr int COLS = Ops::L::COLS;
   constexpr int UNITS = TW / 2;
@@ -853,14 +980,29 @@ __global__ __launch_bounds__(128 * TW) void bwd_split_kernel(BwdArgs a, int n_co
   __shared__ float4 lds4[(LDS + 3) / 4];
   float* lds = reinterpret_cast<float*>(lds4);
   const int wg = blockIdx.x;
-  if (wg < n_cols_wg) {
+  if (wg >= m.task_wg) {
+    // padding rows: dx = 0, nothing read (one row per wavefront)
+    const int idx = (wg - m.task_wg) * 2 * TW + (int)(threadIdx.x >> 6);
+    if (idx < a.plan.n_pad) {
+      const int nchunk = a.hidden >> 3;
+      uint16_t* d = a.dx + (int64_t)a.plan.pad_rows[idx] * a.hidden;
+      for (int q = (int)(threadIdx.x & 63); q < nchunk; q += 64) store16_stream(d + q * 8, make_uint4(0, 0, 0, 0));
+    }
+    return;
+  }
+  const int per = m.col_wg + m.row_wg;
+  const int k = wg / m.groups;
+  const int item = wg % m.groups + m.groups * (k / per);
+  const int t = k % per;
+  if (item >= a.plan.n_items) return;   // the whole workgroup: no barrier is left waiting
+  if (t < m.col_wg) {
     const int u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);   // the workgroup's unit
-    const int unit = wg * UNITS + u;
-    const bool live = unit < n_units;
-    dw_cols_part<PLAN>(a, reinterpret_cast<float (*)[256]>(lds + u * (kStreams - 1) * 256),
-                       live ? unit / n_slices : 0, live ? unit % n_slices : 0, u * kStreams, live);
+    const int slice = t * UNITS + u;
+    const bool live = slice < m.n_slices;
+    dw_cols_part<PLAN>(a, reinterpret_cast<float (*)[256]>(lds + u * (kStreams - 1) * 256), item,
+                       live ? slice : 0, u * kStreams, live);
   } else {
-    dx_rows_part<V, TW, FULL, PLAN>(a, lds, lds + COLS, wg - n_cols_wg, n_rows_wg);
+    dx_pair_part<V, TW, FULL, PLAN>(a, lds, lds + COLS, item, t - m.col_wg);
   }
 }
 
@@ -963,7 +1105,7 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
           store_f4(&c_s[s * H + sub * 8 + 4], c[4], c[5], c[6], c[7]);
         }
       } else if (p >= 0) {
-        float* srow = a.S + ((int64_t)blk * kBlockRows + s) * H + sub * 8;
+        float* srow = a.S + (spill_row0(a, item, blk) + s) * H + sub * 8;
         store_f4_stream(srow, c[0], c[1], c[2], c[3]);
         store_f4_stream(srow + 4, c[4], c[5], c[6], c[7]);
       }
@@ -981,17 +1123,40 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
     __syncthreads();
     for (int j = tid; j < H; j += 256)
       a.P[(int64_t)blk * H + j] = stream_tree4(q_s[j], q_s[H + j], q_s[2 * H + j], q_s[3 * H + j]);
+    if (a.form != nullptr && tid == 0) a.form[blk] = 0;
   }
 }
 
 // ----------------------------------------------------------------- finalize
+// Blocks the stream-owner backward left in stream form: P[b] = (q0 + q1) +
+// (q2 + q3) with q0 = P[b] and q1..q3 = Q[b], the fused kernel's in-block
+// tree.  Workgroup g covers 1024 columns of block g / groups_per_block.
+__global__ __launch_bounds__(256) void join_kernel(float* __restrict__ P, const float* __restrict__ Q,
+                                                   const int32_t* __restrict__ form,
+                                                   int groups_per_block, int H) {
+  const int64_t b = blockIdx.x / groups_per_block;
+  if (form[b] != 1) return;
+  const int c = ((int)(blockIdx.x % groups_per_block) * 256 + (int)threadIdx.x) * 4;
+  if (c >= H) return;   // hidden % 8 == 0, so c + 3 < H otherwise
+  float* pb = P + b * H + c;
+  const float* qb = Q + b * 3 * H + c;
+  const float4 q0 = *reinterpret_cast<const float4*>(pb);
+  const float4 q1 = *reinterpret_cast<const float4*>(qb);
+  const float4 q2 = *reinterpret_cast<const float4*>(qb + H);
+  const float4 q3 = *reinterpret_cast<const float4*>(qb + 2 * H);
+  store_f4(pb, stream_tree4(q0.x, q1.x, q2.x, q3.x), stream_tree4(q0.y, q1.y, q2.y, q3.y),
+           stream_tree4(q0.z, q1.z, q2.z, q3.z), stream_tree4(q0.w, q1.w, q2.w, q3.w));
+}
+
 // Partials of spilled blocks, folded from their spill rows in the same order
 // as the backward kernel folds complete blocks.
 __global__ __launch_bounds__(256) void rebuild_kernel(const float* __restrict__ S,
                                                       float* __restrict__ P,
                                                       const int32_t* __restrict__ blocks,
+                                                      const int32_t* __restrict__ slots,
                                                       int64_t T, int H) {
   const int b = blocks[blockIdx.x];
+  const int64_t srow0 = (int64_t)slots[blockIdx.x] * kBlockRows;
   const int j = blockIdx.y * 256 + threadIdx.x;
   if (j >= H) return;
   // every slot's value is loaded before the folds (absent slots, l >= T,
@@ -1000,7 +1165,7 @@ __global__ __launch_bounds__(256) void rebuild_kernel(const float* __restrict__ 
 #pragma unroll
   for (int s = 0; s < kBlockRows; ++s) {
     const int64_t l = (int64_t)b * kBlockRows + s;
-    v[s] = l < T ? S[l * H + j] : 0.0f;
+    v[s] = l < T ? S[(srow0 + s) * H + j] : 0.0f;
   }
   float q[kStreams];
 #pragma unroll
@@ -1227,6 +1392,15 @@ int64_t split_items() {
   std::lock_guard<std::mutex> lk(g_split_mu);
   return g_split_items;
 }
+static int64_t g_stream_items = kDefaultStreamItems;
+void set_stream_items(int64_t n) {
+  std::lock_guard<std::mutex> lk(g_split_mu);
+  g_stream_items = n < 0 ? kDefaultStreamItems : n;
+}
+int64_t stream_items() {
+  std::lock_guard<std::mutex> lk(g_split_mu);
+  return g_stream_items;
+}
 static int64_t g_group_cap = 0;
 void set_wide_group_cap(int64_t n) {
   std::lock_guard<std::mutex> lk(g_split_mu);
@@ -1307,19 +1481,18 @@ static void bwd_team_go(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
 
 template <int V, int TW, bool FULL, bool PLAN>
 static void bwd_split_go2(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
-  constexpr int TEAMS = 2;
-  int64_t rows_wg = 0;
-  if (dx && a.rows > 0) {
-    rows_wg = (a.rows + TEAMS - 1) / TEAMS;
-    if (rows_wg > grid_cap()) rows_wg = grid_cap();
-  }
   constexpr int UNITS = TW / 2;
-  const int n_slices = (a.hidden + 255) / 256;
-  const int64_t units = dw ? (int64_t)a.plan.n_items * n_slices : 0;
-  const int64_t cols_wg = (units + UNITS - 1) / UNITS;
-  if (rows_wg + cols_wg == 0) return;
-  bwd_split_kernel<V, TW, FULL, PLAN><<<dim3((unsigned)(cols_wg + rows_wg)), dim3(128 * TW), 0, st>>>(
-      a, (int)cols_wg, (int)units, n_slices, (int)rows_wg);
+  const int n = a.plan.n_items;
+  SplitMap m;
+  m.n_slices = (a.hidden + 255) / 256;
+  m.col_wg = dw ? (m.n_slices + UNITS - 1) / UNITS : 0;
+  m.row_wg = dx ? kBlockRows / 2 : 0;
+  m.groups = split_groups(n);
+  const int64_t per_group = (n + m.groups - 1) / m.groups;
+  m.task_wg = (int)(m.groups * per_group * (m.col_wg + m.row_wg));
+  const int pad_wg = dx ? (a.plan.n_pad + 2 * TW - 1) / (2 * TW) : 0;
+  if (m.task_wg + pad_wg == 0) return;
+  bwd_split_kernel<V, TW, FULL, PLAN><<<dim3((unsigned)(m.task_wg + pad_wg)), dim3(128 * TW), 0, st>>>(a, m);
 }
 template <int V, int TW>
 static void bwd_split_go(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
@@ -1328,6 +1501,47 @@ static void bwd_split_go(const BwdArgs& a, bool dx, bool dw, hipStream_t st) {
   else if (full) bwd_split_go2<V, TW, true, false>(a, dx, dw, st);
   else if (plan) bwd_split_go2<V, TW, false, true>(a, dx, dw, st);
   else bwd_split_go2<V, TW, false, false>(a, dx, dw, st);
+}
+
+// Stream-owner shape by chunk groups K: one chunk group per wavefront up to
+// 16 groups (a whole row per workgroup of K wavefronts, rounded up to a
+// shape that is built), two above; 3 rows in flight ahead of the one being
+// reduced, 7 at up to 4096 columns (measured at 4096: 7 ahead beat 3 by 2%
+// and 1 by 11%; two chunk groups per wavefront on half the wavefronts lost
+// 1-3%).
+static BwdShape stream_shape(int hidden) {
+  const int k = (hidden + 511) / 512;
+  if (k <= 2) return {1, 2, 1, 3};
+  if (k <= 4) return {1, 4, 1, 3};
+  if (k <= 8) return {1, 8, 1, 7};
+  if (k <= 10) return {1, 10, 1, 3};
+  if (k <= 12) return {1, 12, 1, 3};
+  if (k <= 16) return {1, 16, 1, 3};
+  return {2, 10, 1, 3};
+}
+template <int V, int TW, int PD, bool FULL, bool PLAN>
+static void bwd_stream_go2(const BwdArgs& a, hipStream_t st) {
+  const int64_t wg = (int64_t)a.plan.n_items * kStreams + (a.plan.n_pad + TW - 1) / TW;
+  bwd_stream_kernel<V, TW, PD, FULL, PLAN><<<dim3((unsigned)wg), dim3(64 * TW), 0, st>>>(a);
+}
+template <int V, int TW, int PD>
+static void bwd_stream_go(const BwdArgs& a, hipStream_t st) {
+  const bool full = a.hidden == 512 * V * TW, plan = a.plan.item_info != nullptr;
+  if (full && plan) bwd_stream_go2<V, TW, PD, true, true>(a, st);
+  else if (full) bwd_stream_go2<V, TW, PD, true, false>(a, st);
+  else if (plan) bwd_stream_go2<V, TW, PD, false, true>(a, st);
+  else bwd_stream_go2<V, TW, PD, false, false>(a, st);
+}
+
+BwdPath bwd_path(const BwdArgs& a, bool dx, bool dw, bool rc) {
+  if (small_lanes(a.hidden) != 0) return BwdPath::kSmall;
+  if (rc) return BwdPath::kFused;
+  const int64_t n = a.plan.n_items;
+  if (n >= split_items()) return BwdPath::kFused;
+  if (dx && dw && a.Q != nullptr && a.form != nullptr && n >= stream_items() && n > 0 &&
+      !is_packed(a.pack, a.hidden))
+    return BwdPath::kStream;
+  return BwdPath::kSplit;
 }
 
 template <int L>
@@ -1363,7 +1577,22 @@ hipError_t launch_bwd(const BwdArgs& a, bool dx, bool dw, hipStream_t st, bool r
     case 32: bwd_small_go<32>(a, dx, dw, rc, st); return hipGetLastError();
     default: break;
   }
-  if (!rc && a.plan.n_items < split_items()) {
+  const BwdPath path = bwd_path(a, dx, dw, rc);
+  if (path == BwdPath::kStream) {
+    const BwdShape s = stream_shape(a.hidden);
+    switch (s.v * 32 + s.tw) {
+      case 1 * 32 + 2: bwd_stream_go<1, 2, 3>(a, st); break;
+      case 1 * 32 + 4: bwd_stream_go<1, 4, 3>(a, st); break;
+      case 1 * 32 + 8: bwd_stream_go<1, 8, 7>(a, st); break;
+      case 1 * 32 + 10: bwd_stream_go<1, 10, 3>(a, st); break;
+      case 1 * 32 + 12: bwd_stream_go<1, 12, 3>(a, st); break;
+      case 1 * 32 + 16: bwd_stream_go<1, 16, 3>(a, st); break;
+      case 2 * 32 + 10: bwd_stream_go<2, 10, 3>(a, st); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  if (path == BwdPath::kSplit) {
     const BwdShape s = split_shape(a.hidden);
     switch (s.v * 16 + s.tw) {
       case 1 * 16 + 2: bwd_split_go<1, 2>(a, dx, dw, st); break;
@@ -1404,11 +1633,19 @@ hipError_t launch_bwd(const BwdArgs& a, bool dx, bool dw, hipStream_t st, bool r
   return hipGetLastError();
 }
 
-hipError_t launch_rebuild(const float* S, float* P, const int32_t* blocks, int32_t n_blocks,
-                          int64_t n_logical, int32_t hidden, hipStream_t st) {
+hipError_t launch_join(float* P, const float* Q, const int32_t* form, int64_t nb, int32_t hidden,
+                       hipStream_t st) {
+  if (nb == 0) return hipSuccess;
+  const int per = (hidden + 1023) / 1024;
+  join_kernel<<<dim3((unsigned)(nb * per)), dim3(256), 0, st>>>(P, Q, form, per, hidden);
+  return hipGetLastError();
+}
+
+hipError_t launch_rebuild(const float* S, float* P, const int32_t* blocks, const int32_t* slots,
+                          int32_t n_blocks, int64_t n_logical, int32_t hidden, hipStream_t st) {
   if (n_blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)n_blocks, (unsigned)((hidden + 255) / 256));
-  rebuild_kernel<<<grid, dim3(256), 0, st>>>(S, P, blocks, n_logical, hidden);
+  rebuild_kernel<<<grid, dim3(256), 0, st>>>(S, P, blocks, slots, n_logical, hidden);
   return hipGetLastError();
 }
 

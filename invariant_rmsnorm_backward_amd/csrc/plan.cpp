@@ -73,10 +73,13 @@ int build_plan(const int32_t* row_logical, int64_t rows, int64_t n_logical, Plan
   return kOk;
 }
 
-void AccHost::init(int64_t T, int64_t H) {
+void AccHost::init(int64_t T, int64_t H, int64_t spill_slots) {
   n_logical = T;
   hidden = H;
   nb = num_blocks(T);
+  spill_cap = spill_slots;
+  spill_slot.assign(spill_slots >= 0 ? static_cast<size_t>(nb) : 0, -1);
+  spill_used = 0;
   covered.assign(static_cast<size_t>(T), 0);
   block_state.assign(static_cast<size_t>(nb), kBlockNone);
   n_covered = 0;
@@ -88,6 +91,8 @@ void AccHost::init(int64_t T, int64_t H) {
 }
 
 void AccHost::reset() {
+  if (spill_used > 0) std::fill(spill_slot.begin(), spill_slot.end(), -1);
+  spill_used = 0;
   if (rows_dirty) std::fill(covered.begin(), covered.end(), 0);
   if (blocks_dirty) std::fill(block_state.begin(), block_state.end(), kBlockNone);
   n_covered = 0;
@@ -124,7 +129,9 @@ static int64_t first_held(const PlanHost& P, size_t it) {
   return b * kBlockRows;
 }
 
-int AccHost::check_call(const PlanHost* plan, int64_t rows, std::string* err) const {
+int AccHost::check_call(const PlanHost* plan, int64_t rows, std::string* err,
+                        SpillTable* table) const {
+  if (table != nullptr) table->n = -1;
   if (finalized) {
     *err = "accumulator already finalized; call rmsnorm_dw_acc_reset first";
     return kEState;
@@ -160,6 +167,38 @@ int AccHost::check_call(const PlanHost* plan, int64_t rows, std::string* err) co
   }
   for (int32_t l : plan->partial_rows)
     if (covered[static_cast<size_t>(l)]) return dup(l);
+  if (spill_cap >= 0 && plan->n_partial > 0) {
+    if (plan->n_partial > kSpillTable) {
+      *err = "the call holds " + std::to_string(plan->n_partial) + " blocks in part; an "
+             "accumulator with a bounded spill area takes at most " +
+             std::to_string(kSpillTable) + " per call";
+      return kEUnsupported;
+    }
+    // the slots commit_call will hand out: assigned ones, then new ones in
+    // item order
+    int64_t next = spill_used;
+    int32_t n = 0;
+    for (size_t it = 0; it < plan->item_info.size(); ++it) {
+      const int32_t info = plan->item_info[it];
+      if (info >= 0) continue;
+      int32_t slot = spill_slot[static_cast<size_t>(~info)];
+      if (slot < 0) {
+        if (next >= spill_cap) {
+          *err = "spill area full: the accumulator holds " + std::to_string(spill_cap) +
+                 " blocks of spill rows (64 rows each) and this call needs more (block " +
+                 std::to_string(~info) + " held in part)";
+          return kESpill;
+        }
+        slot = static_cast<int32_t>(next++);
+      }
+      if (table != nullptr) {
+        table->item[n] = static_cast<int32_t>(it);
+        table->slot[n] = slot;
+      }
+      ++n;
+    }
+    if (table != nullptr) table->n = n;
+  }
   return kOk;
 }
 
@@ -172,9 +211,13 @@ void AccHost::commit_call(const PlanHost* plan) {
   for (int32_t info : plan->item_info) {
     if (info >= 0) {
       block_state[static_cast<size_t>(info)] = kBlockDirect;
-    } else if (block_state[static_cast<size_t>(~info)] != kBlockSpilled) {
-      block_state[static_cast<size_t>(~info)] = kBlockSpilled;
-      ++n_spilled;
+    } else {
+      if (block_state[static_cast<size_t>(~info)] != kBlockSpilled) {
+        block_state[static_cast<size_t>(~info)] = kBlockSpilled;
+        ++n_spilled;
+      }
+      if (spill_cap >= 0 && spill_slot[static_cast<size_t>(~info)] < 0)
+        spill_slot[static_cast<size_t>(~info)] = static_cast<int32_t>(spill_used++);
     }
   }
   for (int32_t l : plan->partial_rows) covered[static_cast<size_t>(l)] = 1;
@@ -189,7 +232,8 @@ int AccHost::register_call(const PlanHost* plan, int64_t rows, std::string* err)
   return rc;
 }
 
-int AccHost::prepare_finalize(std::vector<int32_t>* spilled, std::string* err) const {
+int AccHost::prepare_finalize(std::vector<int32_t>* spilled, std::string* err,
+                              std::vector<int32_t>* slots) const {
   if (n_covered != n_logical) {
     // rows are registered at most once, so fewer than n_logical means a gap
     int64_t l = 0;
@@ -207,9 +251,15 @@ int AccHost::prepare_finalize(std::vector<int32_t>* spilled, std::string* err) c
     return kECoverage;
   }
   spilled->clear();
+  if (slots != nullptr) slots->clear();
   if (n_spilled > 0)
     for (int64_t b = 0; b < nb; ++b)
-      if (block_state[b] == kBlockSpilled) spilled->push_back(static_cast<int32_t>(b));
+      if (block_state[b] == kBlockSpilled) {
+        spilled->push_back(static_cast<int32_t>(b));
+        if (slots != nullptr)
+          slots->push_back(spill_cap >= 0 ? spill_slot[static_cast<size_t>(b)]
+                                          : static_cast<int32_t>(b));
+      }
   return kOk;
 }
 

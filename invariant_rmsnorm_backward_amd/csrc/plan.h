@@ -30,6 +30,18 @@ enum Status : int {
   kECoverage = -4,
   kEState = -5,
   kEHip = -6,
+  kESpill = -7,
+};
+
+// Spill slots of one call's partial items, for an accumulator with a
+// bounded spill area (n = -1: unbounded, a block's spill rows are its own
+// logical rows).  Passed to the kernels by value, so a call may hold at most
+// kSpillTable blocks in part.
+constexpr int kSpillTable = 32;
+struct SpillTable {
+  int32_t n = -1;
+  int32_t item[kSpillTable];   // item index in the call's plan
+  int32_t slot[kSpillTable];   // 64-row spill slot of that item's block
 };
 
 inline int64_t num_blocks(int64_t n_logical) { return (n_logical + kBlockRows - 1) / kBlockRows; }
@@ -74,20 +86,32 @@ struct AccHost {
   bool rows_dirty = false;            // covered was written
   bool blocks_dirty = false;          // block_state was written
   bool finalized = false;
+  // Bounded spill area (spill_cap >= 0 slots of 64 rows): a block held in
+  // part takes the next free slot at its first call and keeps it until
+  // reset.  spill_cap < 0: unbounded (slot = block).
+  int64_t spill_cap = -1;
+  std::vector<int32_t> spill_slot;    // per block, -1 = none (bounded only)
+  int64_t spill_used = 0;
 
-  void init(int64_t T, int64_t H);
+  void init(int64_t T, int64_t H, int64_t spill_slots = -1);
   void reset();
   // Registers one call.  plan == nullptr means the identity map over `rows`
   // rows (all blocks complete).  check_call validates without changing any
   // state; commit_call records a call that check_call accepted, once its
   // kernels are enqueued (a launch that fails leaves the accumulator as it
   // was); register_call does both.
-  int check_call(const PlanHost* plan, int64_t rows, std::string* err) const;
+  // With a bounded spill area check_call also fills *table (if non-NULL)
+  // with the slots of the call's partial items (kESpill when the area is
+  // full, kEUnsupported above kSpillTable partial items) and commit_call
+  // takes them.
+  int check_call(const PlanHost* plan, int64_t rows, std::string* err,
+                 SpillTable* table = nullptr) const;
   void commit_call(const PlanHost* plan);
   int register_call(const PlanHost* plan, int64_t rows, std::string* err);
   // Checks that every logical row contributed exactly once and lists the
-  // spilled blocks in ascending order.
-  int prepare_finalize(std::vector<int32_t>* spilled, std::string* err) const;
+  // spilled blocks in ascending order, with their spill slots in *slots.
+  int prepare_finalize(std::vector<int32_t>* spilled, std::string* err,
+                       std::vector<int32_t>* slots = nullptr) const;
 };
 
 }  // namespace rbi

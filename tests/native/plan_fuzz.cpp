@@ -208,6 +208,92 @@ int main() {
     B.commit_call(&P);
     CHECK(B.check_call(&P, 3, &err) == kECoverage);   // now the rows are recorded
   }
+  // Bounded spill area: contiguous pieces of random lengths cover [0, T).
+  // With exactly as many slots as blocks held in part, every call fits, each
+  // partial item is listed once with its block's one slot, and finalize
+  // reports the same slots; with one slot fewer, the call that needs it is
+  // refused (kESpill) and changes nothing.
+  for (int iter = 0; iter < 400; ++iter) {
+    const int64_t T = 1 + rng() % 900;
+    std::vector<std::vector<int32_t>> calls;
+    for (int64_t a = 0; a < T;) {
+      const int64_t len = std::min<int64_t>(T - a, 1 + rng() % 150);
+      std::vector<int32_t> rl;
+      for (int64_t l = a; l < a + len; ++l) rl.push_back((int32_t)l);
+      std::shuffle(rl.begin(), rl.end(), rng);
+      calls.push_back(rl);
+      a += len;
+    }
+    std::vector<PlanHost> plans(calls.size());
+    std::vector<int> partial_blocks(num_blocks(T), 0);
+    std::string err;
+    for (size_t c = 0; c < calls.size(); ++c) {
+      CHECK(build_plan(calls[c].data(), (int64_t)calls[c].size(), T, &plans[c], &err) == kOk);
+      for (int32_t info : plans[c].item_info) if (info < 0) partial_blocks[~info] = 1;
+    }
+    int64_t need = 0;
+    for (int v : partial_blocks) need += v;
+    for (int shrink = 0; shrink <= 1; ++shrink) {
+      if (shrink && need == 0) continue;
+      AccHost A;
+      A.init(T, 8, need - shrink);
+      std::vector<int32_t> slot_of(num_blocks(T), -1);
+      bool refused = false;
+      for (size_t c = 0; c < calls.size(); ++c) {
+        SpillTable tab;
+        const int rc = A.check_call(&plans[c], (int64_t)calls[c].size(), &err, &tab);
+        if (rc == kESpill) {
+          CHECK(shrink == 1);
+          refused = true;
+          // refused: nothing recorded, the same answer again
+          CHECK(A.check_call(&plans[c], (int64_t)calls[c].size(), &err, &tab) == kESpill);
+          break;
+        }
+        CHECK(rc == kOk);
+        int listed = 0;
+        for (size_t it = 0; it < plans[c].item_info.size(); ++it) {
+          const int32_t info = plans[c].item_info[it];
+          if (info >= 0) continue;
+          CHECK(listed < tab.n && tab.item[listed] == (int32_t)it);
+          const int32_t sl = tab.slot[listed++];
+          CHECK(sl >= 0 && sl < need - shrink);
+          if (slot_of[~info] < 0) {
+            for (int32_t o : slot_of) CHECK(o != sl);   // a new slot is free
+            slot_of[~info] = sl;
+          }
+          CHECK(slot_of[~info] == sl);
+        }
+        CHECK(tab.n == (plans[c].n_partial > 0 ? listed : -1));
+        A.commit_call(&plans[c]);
+      }
+      CHECK(refused == (shrink == 1));
+      if (!refused) {
+        std::vector<int32_t> sp, sl;
+        CHECK(A.prepare_finalize(&sp, &err, &sl) == kOk);
+        CHECK(sp.size() == sl.size() && (int64_t)sp.size() == need);
+        for (size_t i = 0; i < sp.size(); ++i) CHECK(sl[i] == slot_of[sp[i]]);
+        A.reset();
+        CHECK(A.spill_used == 0);
+      }
+    }
+  }
+  {
+    // more blocks in part than a bounded call takes: refused when bounded,
+    // accepted (slot = block) when unbounded
+    std::vector<int32_t> rl;
+    for (int b = 0; b < 40; ++b) rl.push_back(b * kBlockRows);   // one row of each of 40 blocks
+    PlanHost P;
+    CHECK(build_plan(rl.data(), (int64_t)rl.size(), 40 * kBlockRows, &P, &err) == kOk);
+    AccHost B, U;
+    B.init(40 * kBlockRows, 8, 1000);
+    U.init(40 * kBlockRows, 8);
+    SpillTable tab;
+    CHECK(B.check_call(&P, (int64_t)rl.size(), &err, &tab) == kEUnsupported);
+    CHECK(U.check_call(&P, (int64_t)rl.size(), &err, &tab) == kOk && tab.n == -1);
+    std::vector<int32_t> sp, sl;
+    U.commit_call(&P);
+    CHECK(U.prepare_finalize(&sp, &err, &sl) == kECoverage);
+  }
   std::printf("plan fuzz: %s\n", fails ? "FAILED" : "ok");
   return fails ? 1 : 0;
 }

@@ -1,9 +1,11 @@
 """Shared helpers of the GPU parity tests (imports the oracle: test-only)."""
+import contextlib
+
 import numpy as np
 import torch
 
 import oracle
-from invariant_rmsnorm_backward_amd import adapters, inputs, layouts
+from invariant_rmsnorm_backward_amd import adapters, binding, inputs, layouts
 
 
 def make_data(wl: inputs.Workload) -> adapters.NormInputs:
@@ -48,3 +50,23 @@ def physical_rstd(rstd_logical: np.ndarray, call) -> torch.Tensor:
     out = np.full(call.rows, np.nan, dtype=np.float32)
     out[rl >= 0] = rstd_logical[rl[rl >= 0]]
     return torch.from_numpy(out).cuda()
+
+
+# The backward for hidden > 256 has three work distributions with the same
+# arithmetic: the fused kernel (workgroups owning whole canonical blocks),
+# the stream-owner kernel (one workgroup per fold stream of a block; calls
+# with dx and an accumulator) and the two-pass path (dx rows beside 256-column
+# dweight units).  Each is forced through the split and stream thresholds.
+BWD_PATHS = {"fused": (0, -1), "stream": (1 << 40, 0), "two_pass": (1 << 40, 1 << 41)}
+
+
+@contextlib.contextmanager
+def forced_path(name: str):
+    split, stream = BWD_PATHS[name]
+    prev_split = binding.rmsnorm_set_split_threshold(split)
+    prev_stream = binding.rmsnorm_set_stream_threshold(stream)
+    try:
+        yield name
+    finally:
+        binding.rmsnorm_set_stream_threshold(prev_stream)
+        binding.rmsnorm_set_split_threshold(prev_split)

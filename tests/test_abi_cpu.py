@@ -114,7 +114,8 @@ def test_no_atomics_and_no_fallbacks_in_the_library_sources():
     # rows in flight) key on the hidden size only
     k = open(os.path.join(csrc, "kernels.hip")).read()
     for ret, fn in (("int", "small_lanes"), ("int", "fwd_tw"), ("int", "fwd_v"),
-                    ("BwdShape", "fused_shape"), ("BwdShape", "split_shape")):
+                    ("BwdShape", "fused_shape"), ("BwdShape", "split_shape"),
+                    ("BwdShape", "stream_shape")):
         sig = re.search(rf"static {ret} {fn}\(([^)]*)\)", k).group(1)
         assert sig.strip() == "int hidden", fn
 
@@ -138,6 +139,17 @@ def test_split_threshold_knob():
         assert binding.rmsnorm_set_split_threshold(prev) > 0
     finally:
         binding.rmsnorm_set_split_threshold(prev)
+
+
+def test_stream_threshold_knob():
+    """The stream-owner backward's lower bound: set, read back, restore."""
+    prev = binding.rmsnorm_set_stream_threshold(7)
+    try:
+        assert binding.rmsnorm_set_stream_threshold(0) == 7
+        assert binding.rmsnorm_set_stream_threshold(-1) == 0     # negative: back to the default
+        assert binding.rmsnorm_set_stream_threshold(prev) == 48
+    finally:
+        binding.rmsnorm_set_stream_threshold(prev)
 
 
 def test_stream_copy_checks_its_arguments(lib):

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+from tests import parity_utils as pu
 from invariant_rmsnorm_backward_amd import adapters, binding, contract, harness, inputs, layouts
 
 pytestmark = pytest.mark.gpu
@@ -172,6 +173,10 @@ def test_norm_linear_chain_is_invariant_in_every_tensor(k, n, lengths, chunk):
                             ("det_gemm.dX", dX, "dX"), ("rms_norm.dx", dx, "dx")):
         got = harness.bf16_bits_to_f32(out[name])
         assert CONTRACT.accuracy_passes(got, want, tol), name
+        # and the bf16 outputs, element by element, within one bf16 ulp of FP64
+        frac = pu.bf16_ulp_fraction(np.asarray(out[name]), want)
+        print(f"[chain] k{k} n{n}: {name} within 1 bf16 ulp of FP64: {frac:.5f}", flush=True)
+        assert frac > 0.99, (name, frac)
 
 
 @pytest.mark.parametrize("k,n,lengths", [
