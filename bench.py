@@ -158,6 +158,28 @@ def copy_ceiling(torch, nbytes: int, iters: int = 20):
     return ours, theirs
 
 
+def stream_2to1(torch, nbytes: int, iters: int = 20):
+    """Two reads for each write, the backward's traffic mix: torch's bf16
+    elementwise add c = a + b over three nbytes tensors, GB/s of the three
+    (a library kernel, so the ceiling is not one of ours)."""
+    n = nbytes // 2
+    a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.ones_like(a)
+    c = torch.empty_like(a)
+    for _ in range(3):
+        torch.add(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        torch.add(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 3.0 * nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b, c
+    return gbps
+
+
 QK_PAIR = "qknorm_d128_t16384"
 
 
@@ -953,6 +975,7 @@ def main():
     traffic = measured_traffic(bb)
 
     copy_gbps, torch_copy_gbps = (None, None) if args.no_copy else copy_ceiling(torch, 1 << 30)
+    s21_gbps = None if args.no_copy else stream_2to1(torch, 1 << 29)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
 
     # host-side setup, timed on its own: a layout plan for the packed, padded,
@@ -999,6 +1022,8 @@ def main():
         "copy_ceiling_gbps": None if copy_gbps is None else round(copy_gbps, 1),
         "frac_of_copy_ceiling": None if copy_gbps is None else round(value / copy_gbps, 4),
         "torch_copy_gbps": None if torch_copy_gbps is None else round(torch_copy_gbps, 1),
+        "stream_2to1_gbps": None if s21_gbps is None else round(s21_gbps, 1),
+        "bwd_frac_of_stream_2to1": None if s21_gbps is None else round(achieved / s21_gbps, 4),
         "invariance_bn_vs_8xb1_bitwise": inv_ok,
         "bwd_rstd_recompute": {"avg_launch_ms": round(rc_ms, 5),
                                "gbps": round((bb - 4 * T) / (rc_ms * 1e-3) / 1e9, 1),

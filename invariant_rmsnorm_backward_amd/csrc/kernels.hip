@@ -1008,6 +1008,10 @@ __global__ __launch_bounds__(128 * TW) void bwd_split_kernel(BwdArgs a, SplitMap
 
 // Small rows: hidden = 8L (L in 1..32), one group of L lanes per row; the
 // 64 slots' contributions go through LDS and the 4 streams fold them there.
+// (Folding in registers instead -- each block's four streams on 4L lanes of
+// one wavefront, the stream tree as lane shuffles, no LDS -- measured 10-14%
+// slower at 128 columns: a quarter of the wavefronts in flight, each walking
+// 16 rows.)
 // RC: rstd rebuilt from the row in the forward's order (the same lanes, the
 // same chain and group sum), so its bits are the saved rstd's.
 template <int L, bool DX, bool DW, bool PACKED, bool RC>
@@ -1266,7 +1270,11 @@ static int fwd_v(int hidden) {
 // 4096 columns two rows in flight per workgroup, four wavefronts each, one
 // resident workgroup per compute unit, beat four rows in flight by 5%; at
 // 5120 and 8192 columns four rows in flight of two wavefronts each beat two
-// rows of four or five wavefronts by 1-5%.
+// rows of four or five wavefronts by 1-5% (5120 padded and permuted: two
+// rows in flight 3.5% slower, three chunk groups on four wavefronts 2%
+// slower, no prefetch ring the same; 8192: four chunk groups on four
+// wavefronts or two on eight 5% slower, four teams of four wavefronts
+// without a ring the same).
 struct BwdShape {
   int v, tw, teams, pd;
 };
@@ -1433,8 +1441,11 @@ static int compute_units() {
 // workgroups walk their share of the items in turn -- one per compute unit
 // with two teams (two resident workgroups per compute unit were about 4%
 // slower at hidden 4096), two with four teams, and at least 8 wavefronts
-// per compute unit.  Which workgroup takes an item changes nothing in its
-// arithmetic.
+// per compute unit.  With four teams the second workgroup of a compute
+// unit may not fit beside the first (above 128 VGPRs); capping at what
+// fits was 3.5% slower at hidden 8192 (1169 blocks): more, shorter
+// workgroups balance the tail better.  Which workgroup takes an item
+// changes nothing in its arithmetic.
 template <int V, int TW, int TEAMS, int PD, bool FULL, bool PLAN, bool DX, bool DW, bool RC>
 static void bwd_team_launch(BwdArgs a, hipStream_t st) {
   constexpr int WAVES = TW * TEAMS;
@@ -1442,6 +1453,9 @@ static void bwd_team_launch(BwdArgs a, hipStream_t st) {
   const int64_t per_cu = (TEAMS == 2 ? 1 : 2) * (WAVES >= 8 ? 1 : 8 / WAVES);
   const int64_t cap = knob > 0 ? knob : per_cu * compute_units();
   a.item_groups = (int32_t)(a.plan.n_items > cap ? cap : a.plan.n_items);
+  // padding rows get workgroups of their own after the item workgroups
+  // (zeroing them inside the item workgroups, beside the next item's loads,
+  // measured the same on the hidden-5120 padded layout)
   const int pad_groups = DX ? (a.plan.n_pad + WAVES - 1) / WAVES : 0;
   if (a.item_groups + pad_groups == 0) return;
   const dim3 grid((unsigned)(a.item_groups + pad_groups)), block(64 * WAVES);
