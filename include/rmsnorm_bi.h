@@ -237,7 +237,7 @@ int rmsnorm_set_split_threshold(int64_t blocks, int64_t* previous);
  * walk its four streams (the fused kernel's per-row code), x and dy are
  * read once, and the four stream sums are joined by rmsnorm_dw_finalize in
  * the fused kernel's order.  Smaller calls, dx-only and
- * contributions-only calls take the two-pass path (default 48 blocks).  A
+ * contributions-only calls take the two-pass path (default 32 blocks).  A
  * negative value restores the default; a value at or above the split
  * threshold disables the stream-owner path.  `previous` and scope as for
  * rmsnorm_set_split_threshold.  Always returns RMSNORM_OK. */

@@ -26,7 +26,7 @@ int64_t split_items();
 // the split threshold), and compute dx and dweight contributions together
 // into an accumulator, run the stream-owner backward: one workgroup per fold
 // stream of each block, x and dy read once.  Same arithmetic again.
-constexpr int64_t kDefaultStreamItems = 48;
+constexpr int64_t kDefaultStreamItems = 32;
 void set_stream_items(int64_t n);   // n < 0 restores the default
 int64_t stream_items();
 

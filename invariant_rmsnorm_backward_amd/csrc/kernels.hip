@@ -1298,12 +1298,19 @@ static BwdShape recompute_shape(int hidden) {
   if (K <= 16) return {8, 2, 4, 0};
   return {5, 4, 2, 0};
 }
-// The dx rows of the two-pass path: two teams, each wide enough that the
-// workgroup is a whole number of 4-wavefront column units.
+// The dx rows of the two-pass path: two teams of two wavefronts, so a
+// workgroup is one 4-wavefront column unit or two dx rows.  Against four
+// wavefronts per row (the earlier shape) this is 12% faster on 512-row
+// chunks at 8192 columns, 18% at 4096 and 7% on B=1 samples at 5120: the
+// tasks are latency chains, and smaller workgroups start sooner.
 static BwdShape split_shape(int hidden) {
   const int K = (hidden + 511) / 512;
   if (K <= 2) return {1, 2, 2, 0};
-  return {(K + 3) / 4, 4, 2, 0};
+  if (K <= 4) return {2, 2, 2, 0};
+  if (K <= 8) return {4, 2, 2, 0};
+  if (K <= 10) return {5, 2, 2, 0};
+  if (K <= 16) return {8, 2, 2, 0};
+  return {10, 2, 2, 0};
 }
 
 const char* fwd_variant(int hidden) {
@@ -1610,11 +1617,11 @@ hipError_t launch_bwd(const BwdArgs& a, bool dx, bool dw, hipStream_t st, bool r
     const BwdShape s = split_shape(a.hidden);
     switch (s.v * 16 + s.tw) {
       case 1 * 16 + 2: bwd_split_go<1, 2>(a, dx, dw, st); break;
-      case 1 * 16 + 4: bwd_split_go<1, 4>(a, dx, dw, st); break;
-      case 2 * 16 + 4: bwd_split_go<2, 4>(a, dx, dw, st); break;
-      case 3 * 16 + 4: bwd_split_go<3, 4>(a, dx, dw, st); break;
-      case 4 * 16 + 4: bwd_split_go<4, 4>(a, dx, dw, st); break;
-      case 5 * 16 + 4: bwd_split_go<5, 4>(a, dx, dw, st); break;
+      case 2 * 16 + 2: bwd_split_go<2, 2>(a, dx, dw, st); break;
+      case 4 * 16 + 2: bwd_split_go<4, 2>(a, dx, dw, st); break;
+      case 5 * 16 + 2: bwd_split_go<5, 2>(a, dx, dw, st); break;
+      case 8 * 16 + 2: bwd_split_go<8, 2>(a, dx, dw, st); break;
+      case 10 * 16 + 2: bwd_split_go<10, 2>(a, dx, dw, st); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

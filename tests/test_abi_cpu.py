@@ -147,7 +147,7 @@ def test_stream_threshold_knob():
     try:
         assert binding.rmsnorm_set_stream_threshold(0) == 7
         assert binding.rmsnorm_set_stream_threshold(-1) == 0     # negative: back to the default
-        assert binding.rmsnorm_set_stream_threshold(prev) == 48
+        assert binding.rmsnorm_set_stream_threshold(prev) == 32
     finally:
         binding.rmsnorm_set_stream_threshold(prev)
 
