@@ -388,6 +388,71 @@ def measure_cell(args, torch, np, binding, inputs, layouts):
     value = (fb + bb) / (ms_step * 1e-3) / 1e9
     achieved = bb / (med["bwd"] * 1e-3) / 1e9
     n_calls = sum(len(n["calls"]) for n in norms)
+    # The per-head pair: the same calls with Q and K of each call in one launch
+    # per phase (rmsnorm_fwd_packed_pair / rmsnorm_bwd_dx_packed_pair), when
+    # every call holds whole tokens of both.
+    pair = None
+    if args.workload == QK_PAIR:
+        nq, nk = norms
+        hq, hk, d = nq["wl"].heads, nk["wl"].heads, nq["H"]
+        if all(cq["rows"] % hq == 0 and ck["rows"] % hk == 0 and cq["rows"] // hq == ck["rows"] // hk
+               for cq, ck in zip(nq["calls"], nk["calls"])):
+            lay = lambda c: None if c["layout"] is None else c["layout"].handle
+
+            def pair_fwd(i):
+                sq, sk = nq["sets"][i % len(nq["sets"])], nk["sets"][i % len(nk["sets"])]
+                for cq, ck, bq, bk in zip(nq["calls"], nk["calls"], sq, sk):
+                    binding.rmsnorm_fwd_packed_pair(
+                        (bq["x"].data_ptr(), nq["w"].data_ptr(), bq["y"].data_ptr(), bq["rstd"].data_ptr(),
+                         hq, hq * d, lay(cq)),
+                        (bk["x"].data_ptr(), nk["w"].data_ptr(), bk["y"].data_ptr(), bk["rstd"].data_ptr(),
+                         hk, hk * d, lay(ck)), cq["rows"] // hq, d, nq["wl"].eps, sh)
+
+            def pair_bwd(i):
+                sq, sk = nq["sets"][i % len(nq["sets"])], nk["sets"][i % len(nk["sets"])]
+                for cq, ck, bq, bk in zip(nq["calls"], nk["calls"], sq, sk):
+                    binding.rmsnorm_bwd_dx_packed_pair(
+                        (bq["x"].data_ptr(), nq["w"].data_ptr(), bq["dy"].data_ptr(), bq["rstd"].data_ptr(),
+                         bq["dx"].data_ptr(), hq, hq * d, lay(cq), nq["acc"].handle),
+                        (bk["x"].data_ptr(), nk["w"].data_ptr(), bk["dy"].data_ptr(), bk["rstd"].data_ptr(),
+                         bk["dx"].data_ptr(), hk, hk * d, lay(ck), nk["acc"].handle), cq["rows"] // hq, d, sh)
+
+            def pair_step(i):
+                pair_fwd(i)
+                pair_bwd(i)
+                run_fin(nq)
+                run_fin(nk)
+
+            pair_step(0)
+            torch.cuda.synchronize()
+            pair_ok = all(torch.equal(n["dw"].view(torch.int32), n["dw_ref"].view(torch.int32)) for n in norms)
+            for i in range(args.warmup):
+                pair_step(i)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(K):
+                pair_step(i)
+            torch.cuda.synchronize()
+            pair_ms = (time.perf_counter() - t0) / K * 1e3
+            pev = []
+            for i in range(K):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                e[0].record(stream)
+                pair_fwd(i)
+                e[1].record(stream)
+                pair_bwd(i)
+                e[2].record(stream)
+                run_fin(nq)
+                run_fin(nk)
+                e[3].record(stream)
+                pev.append(e)
+            torch.cuda.synchronize()
+            pm = {k: float(np.median([e[j].elapsed_time(e[j + 1]) for e in pev]))
+                  for j, k in enumerate(("fwd", "bwd", "finalize"))}
+            pair = {"ms_per_step": round(pair_ms, 4), "phases_ms": {k: round(v, 5) for k, v in pm.items()},
+                    "dweight_bitwise_equal_to_bn_full": pair_ok,
+                    "launches": "one rmsnorm_fwd_packed_pair and one rmsnorm_bwd_dx_packed_pair per call"}
+
     # One call over every row (BN/full): the rstd-recompute backward on the
     # same rows, back to back, checked bit for bit against the saved-rstd one.
     recompute = None
@@ -460,6 +525,11 @@ def measure_cell(args, torch, np, binding, inputs, layouts):
         out["launch_floor"] = floor
     if recompute is not None:
         out["bwd_rstd_recompute"] = recompute
+    if pair is not None:
+        pair["value"] = round((fb + bb) / (pair["ms_per_step"] * 1e-3) / 1e9, 2)
+        pair["frac_of_peak"] = round(pair["value"] / PEAK_GBPS, 4)
+        pair["bwd_gbps"] = round(bb / (pair["phases_ms"]["bwd"] * 1e-3) / 1e9, 1)
+        out["qk_pair_launch"] = pair
     if graph is not None:
         if "ms_per_step" in graph:
             graph["value"] = round((fb + bb) / (graph["ms_per_step"] * 1e-3) / 1e9, 2)

@@ -129,6 +129,38 @@ int rmsnorm_bwd_dx_packed(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rm
                           int64_t head_dim, int64_t token_stride, const rmsnorm_layout* layout,
                           rmsnorm_dw_acc* acc, void* stream);
 
+/* Two per-head norms of one step in one launch -- typically the Q heads and
+ * the K heads of a fused QKV projection output (the qk_norm operator of
+ * "WS1 C4 (#270) closeout evidence", runtime verification status table).
+ * Every output bit, and what each accumulator receives, is that of
+ * rmsnorm_fwd_packed / rmsnorm_bwd_dx_packed called on norm a and then on
+ * norm b; the pair only saves a launch, which matters because a K norm is
+ * short enough (a quarter of the Q bytes at 32 Q and 8 K heads) to lose a
+ * sixth of its time to a launch's ramp and drain.  Each norm has its own
+ * x, w, y / dy, dx, rstd, head count, token stride, layout and
+ * accumulator; tokens and head_dim are shared.  Arguments and errors as
+ * the single calls, plus: the two norms' outputs must not share an element
+ * with each other or with the other norm's inputs (their per-token column
+ * windows may interleave, as Q and K heads of one tensor do), and two
+ * non-NULL accumulators must differ (RMSNORM_EINVAL).  Nothing is enqueued
+ * or recorded unless both norms pass their checks. */
+int rmsnorm_fwd_packed_pair(const rmsnorm_bf16* x_a, const rmsnorm_bf16* w_a, rmsnorm_bf16* y_a,
+                            float* rstd_a, int64_t heads_a, int64_t token_stride_a,
+                            const rmsnorm_layout* layout_a, const rmsnorm_bf16* x_b,
+                            const rmsnorm_bf16* w_b, rmsnorm_bf16* y_b, float* rstd_b,
+                            int64_t heads_b, int64_t token_stride_b,
+                            const rmsnorm_layout* layout_b, int64_t tokens, int64_t head_dim,
+                            float eps, void* stream);
+int rmsnorm_bwd_dx_packed_pair(const rmsnorm_bf16* x_a, const rmsnorm_bf16* w_a,
+                               const rmsnorm_bf16* dy_a, const float* rstd_a, rmsnorm_bf16* dx_a,
+                               int64_t heads_a, int64_t token_stride_a,
+                               const rmsnorm_layout* layout_a, rmsnorm_dw_acc* acc_a,
+                               const rmsnorm_bf16* x_b, const rmsnorm_bf16* w_b,
+                               const rmsnorm_bf16* dy_b, const float* rstd_b, rmsnorm_bf16* dx_b,
+                               int64_t heads_b, int64_t token_stride_b,
+                               const rmsnorm_layout* layout_b, rmsnorm_dw_acc* acc_b,
+                               int64_t tokens, int64_t head_dim, void* stream);
+
 /* dweight contributions only (no dx): same accumulation as rmsnorm_bwd_dx
  * with an accumulator; rstd is an input (any FP32 values).  Defined by the
  * opening note of "WS1 C4 (#270) closeout evidence" (parameter gradients

@@ -30,7 +30,7 @@ EXPORTED = ("rmsnorm_max_hidden", "rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_c
             "rmsnorm_dw_acc_destroy", "rmsnorm_last_error", "rmsnorm_backend_info",
             "rmsnorm_set_split_threshold", "rmsnorm_set_stream_threshold",
             "rmsnorm_set_workgroup_cap", "rmsnorm_stream_copy",
-            "rmsnorm_fwd_packed",
+            "rmsnorm_fwd_packed", "rmsnorm_fwd_packed_pair", "rmsnorm_bwd_dx_packed_pair",
             "rmsnorm_bwd_dx_packed", "rmsnorm_bwd_dx_recompute", "rmsnorm_bwd_noalloc",
             "rmsnorm_bwd_noalloc_max_scratch",
             "det_gemm_fwd", "det_gemm_bwd_dx", "det_gemm_dw_acc_create", "det_gemm_dw_contrib",
@@ -90,6 +90,10 @@ def load() -> ctypes.CDLL:
         "rmsnorm_stream_copy": ([P, P, I64, P], I32),
         "rmsnorm_fwd_packed": ([P, P, P, P, I64, I64, I64, I64, ctypes.c_float, P, P], I32),
         "rmsnorm_bwd_dx_packed": ([P, P, P, P, P, I64, I64, I64, I64, P, P, P], I32),
+        "rmsnorm_fwd_packed_pair": ([P, P, P, P, I64, I64, P, P, P, P, P, I64, I64, P, I64, I64,
+                                     ctypes.c_float, P], I32),
+        "rmsnorm_bwd_dx_packed_pair": ([P, P, P, P, P, I64, I64, P, P, P, P, P, P, P, I64, I64, P,
+                                        P, I64, I64, P], I32),
         "det_gemm_fwd": ([P, P, P, I64, I64, I64, P, P], I32),
         "det_gemm_bwd_dx": ([P, P, P, I64, I64, I64, P, P], I32),
         "det_gemm_dw_acc_create": ([PP, I64, I64, I64, P], I32),
@@ -228,6 +232,20 @@ def rmsnorm_bwd_dx_packed(x: int, w: int, dy: int, rstd: int, dx: int, tokens: i
                           acc: Optional[int], stream: Optional[int]) -> None:
     _check(load().rmsnorm_bwd_dx_packed(x, w, dy, rstd, dx, tokens, heads, head_dim, token_stride,
                                         layout, acc, stream), "rmsnorm_bwd_dx_packed")
+
+
+def rmsnorm_fwd_packed_pair(a: tuple, b: tuple, tokens: int, head_dim: int, eps: float,
+                            stream: Optional[int]) -> None:
+    """a, b = (x, w, y, rstd, heads, token_stride, layout) of each norm (pointers)."""
+    _check(load().rmsnorm_fwd_packed_pair(*a, *b, tokens, head_dim, eps, stream),
+           "rmsnorm_fwd_packed_pair")
+
+
+def rmsnorm_bwd_dx_packed_pair(a: tuple, b: tuple, tokens: int, head_dim: int,
+                               stream: Optional[int]) -> None:
+    """a, b = (x, w, dy, rstd, dx, heads, token_stride, layout, acc) of each norm."""
+    _check(load().rmsnorm_bwd_dx_packed_pair(*a, *b, tokens, head_dim, stream),
+           "rmsnorm_bwd_dx_packed_pair")
 
 
 def rmsnorm_set_split_threshold(blocks: int) -> int:

@@ -143,10 +143,13 @@ int rmsnorm_set_workgroup_cap(int64_t groups, int64_t* previous) {
   return RMSNORM_OK;
 }
 
-static int fwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y, float* rstd,
-                      int64_t rows, int64_t hidden, float eps, const rmsnorm_layout* layout,
-                      void* stream, const rbi::RowPacking& pk, int64_t extent) {
+// Checks one forward call and fills *out; *launch is false when there is
+// nothing to enqueue (rows == 0).
+static int fwd_prepare(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y, float* rstd,
+                       int64_t rows, int64_t hidden, float eps, const rmsnorm_layout* layout,
+                       const rbi::RowPacking& pk, int64_t extent, rbi::FwdArgs* out, bool* launch) {
   int rc;
+  *launch = false;
   if ((rc = check_rows(rows)) || (rc = check_hidden(hidden))) return rc;
   if (!(eps >= 0.0f) || std::isinf(eps)) return fail(RMSNORM_EINVAL, "eps must be finite and >= 0");
   if (layout != nullptr && layout->host.rows != rows)
@@ -161,8 +164,19 @@ static int fwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16
   if (overlaps(y, nbytes, x, nbytes) || overlaps(y, nbytes, w, hidden * 2) ||
       (rstd != nullptr && (overlaps(rstd, rows * 4, x, nbytes) || overlaps(rstd, rows * 4, y, nbytes))))
     return fail(RMSNORM_EINVAL, "outputs must not alias inputs or each other");
-  rbi::FwdArgs a{x, w, y, rstd, rows, static_cast<int32_t>(hidden), eps,
-                 layout ? layout->dev.row_logical : nullptr, pk};
+  *out = rbi::FwdArgs{x, w, y, rstd, rows, static_cast<int32_t>(hidden), eps,
+                      layout ? layout->dev.row_logical : nullptr, pk};
+  *launch = true;
+  return RMSNORM_OK;
+}
+
+static int fwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y, float* rstd,
+                      int64_t rows, int64_t hidden, float eps, const rmsnorm_layout* layout,
+                      void* stream, const rbi::RowPacking& pk, int64_t extent) {
+  rbi::FwdArgs a{};
+  bool launch = false;
+  int rc = fwd_prepare(x, w, y, rstd, rows, hidden, eps, layout, pk, extent, &a, &launch);
+  if (rc != RMSNORM_OK || !launch) return rc;
   hipError_t e = rbi::launch_fwd(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "rmsnorm_fwd launch");
   return RMSNORM_OK;
@@ -186,12 +200,23 @@ static int check_packing(int64_t tokens, int64_t heads, int64_t head_dim, int64_
   return RMSNORM_OK;
 }
 
+// One backward call, checked and turned into kernel arguments; nothing is
+// recorded in the accumulator until bwd_commit (after the launch).
+struct BwdCall {
+  rbi::BwdArgs a{};
+  const rbi::PlanHost* plan_host = nullptr;
+  rmsnorm_dw_acc* acc = nullptr;
+  bool launch = false;   // rows > 0
+  bool with_dx = true;
+  bool recompute = false;
+};
+
 // recompute: rstd is not read (NULL) but rebuilt from x with eps.
-static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
-                      const float* rstd, rmsnorm_bf16* dx, int64_t rows, int64_t hidden,
-                      const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, void* stream,
-                      bool with_dx, const rbi::RowPacking& pk, int64_t extent,
-                      bool recompute = false, float eps = 0.0f) {
+static int bwd_prepare(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
+                       const float* rstd, rmsnorm_bf16* dx, int64_t rows, int64_t hidden,
+                       const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, bool with_dx,
+                       const rbi::RowPacking& pk, int64_t extent, bool recompute, float eps,
+                       BwdCall* c) {
   int rc;
   if ((rc = check_rows(rows)) || (rc = check_hidden(hidden))) return rc;
   if (recompute && (!(eps >= 0.0f) || std::isinf(eps)))
@@ -218,19 +243,18 @@ static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnor
         return fail(RMSNORM_EINVAL, "dx must not alias an input");
     }
   }
-  const rbi::PlanHost* plan_host = layout ? &layout->host : nullptr;
+  c->plan_host = layout ? &layout->host : nullptr;
+  c->acc = acc;
+  c->with_dx = with_dx;
+  c->recompute = recompute;
   rbi::SpillTable spill;
   if (acc != nullptr) {
     std::string err;
-    rc = acc->host.check_call(plan_host, rows, &err, &spill);
+    rc = acc->host.check_call(c->plan_host, rows, &err, &spill);
     if (rc != RMSNORM_OK) return fail(rc, err);
   }
-  if (rows == 0) {
-    if (acc != nullptr) acc->host.commit_call(plan_host);
-    return RMSNORM_OK;
-  }
-
-  rbi::BwdArgs a{};
+  c->launch = rows > 0;
+  rbi::BwdArgs& a = c->a;
   a.x = x;
   a.w = w;
   a.dy = dy;
@@ -251,17 +275,47 @@ static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnor
     a.plan.n_items = static_cast<int32_t>(rbi::num_blocks(rows));
     a.plan.n_pad = 0;
   }
-  const bool stream_path =
-      rbi::bwd_path(a, with_dx, acc != nullptr, recompute) == rbi::BwdPath::kStream;
-  hipError_t e = rbi::launch_bwd(a, with_dx, acc != nullptr, reinterpret_cast<hipStream_t>(stream),
-                                 recompute);
-  if (e != hipSuccess) return hip_fail(e, "rmsnorm backward launch");
-  // the rows count as contributed only once their kernels are enqueued
-  if (acc != nullptr) {
-    acc->host.commit_call(plan_host);
-    if (stream_path) acc->stream_form = true;
-  }
   return RMSNORM_OK;
+}
+
+// The rows count as contributed only once their kernels are enqueued.
+static void bwd_commit(const BwdCall& c) {
+  if (c.acc == nullptr) return;
+  c.acc->host.commit_call(c.plan_host);
+  if (c.launch && rbi::bwd_path(c.a, c.with_dx, true, c.recompute) == rbi::BwdPath::kStream)
+    c.acc->stream_form = true;
+}
+
+static int bwd_common(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsnorm_bf16* dy,
+                      const float* rstd, rmsnorm_bf16* dx, int64_t rows, int64_t hidden,
+                      const rmsnorm_layout* layout, rmsnorm_dw_acc* acc, void* stream,
+                      bool with_dx, const rbi::RowPacking& pk, int64_t extent,
+                      bool recompute = false, float eps = 0.0f) {
+  BwdCall c;
+  int rc = bwd_prepare(x, w, dy, rstd, dx, rows, hidden, layout, acc, with_dx, pk, extent,
+                       recompute, eps, &c);
+  if (rc != RMSNORM_OK) return rc;
+  if (c.launch) {
+    hipError_t e = rbi::launch_bwd(c.a, with_dx, acc != nullptr,
+                                   reinterpret_cast<hipStream_t>(stream), recompute);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm backward launch");
+  }
+  bwd_commit(c);
+  return RMSNORM_OK;
+}
+
+// Two packed norms in one launch: the per-token column windows of two
+// outputs may interleave (Q and K heads of one tensor) but must not share
+// an element.
+static bool windows_disjoint(const void* a, int64_t cols_a, int64_t stride_a, int64_t extent_a,
+                             const void* b, int64_t cols_b, int64_t stride_b, int64_t extent_b) {
+  if (extent_a == 0 || extent_b == 0) return true;
+  if (!overlaps(a, static_cast<size_t>(extent_a) * 2, b, static_cast<size_t>(extent_b) * 2))
+    return true;
+  if (stride_a != stride_b) return false;
+  const int64_t d = (reinterpret_cast<intptr_t>(b) - reinterpret_cast<intptr_t>(a)) / 2;
+  if (d >= 0) return d >= cols_a && d + cols_b <= stride_a;
+  return -d >= cols_b && -d + cols_a <= stride_a;
 }
 
 int rmsnorm_fwd(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf16* y, float* rstd,
@@ -305,6 +359,81 @@ int rmsnorm_bwd_dx_packed(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rm
   int rc = check_packing(tokens, heads, head_dim, token_stride, &pk, &rows, &extent);
   if (rc != RMSNORM_OK) return rc;
   return bwd_common(x, w, dy, rstd, dx, rows, head_dim, layout, acc, stream, true, pk, extent);
+}
+
+int rmsnorm_fwd_packed_pair(const rmsnorm_bf16* x_a, const rmsnorm_bf16* w_a, rmsnorm_bf16* y_a,
+                            float* rstd_a, int64_t heads_a, int64_t token_stride_a,
+                            const rmsnorm_layout* layout_a, const rmsnorm_bf16* x_b,
+                            const rmsnorm_bf16* w_b, rmsnorm_bf16* y_b, float* rstd_b,
+                            int64_t heads_b, int64_t token_stride_b,
+                            const rmsnorm_layout* layout_b, int64_t tokens, int64_t head_dim,
+                            float eps, void* stream) {
+  rbi::RowPacking pa, pb;
+  int64_t rows_a = 0, rows_b = 0, ext_a = 0, ext_b = 0;
+  int rc;
+  if ((rc = check_packing(tokens, heads_a, head_dim, token_stride_a, &pa, &rows_a, &ext_a)) ||
+      (rc = check_packing(tokens, heads_b, head_dim, token_stride_b, &pb, &rows_b, &ext_b)))
+    return rc;
+  rbi::FwdArgs a{}, b{};
+  bool la = false, lb = false;
+  if ((rc = fwd_prepare(x_a, w_a, y_a, rstd_a, rows_a, head_dim, eps, layout_a, pa, ext_a, &a, &la)) ||
+      (rc = fwd_prepare(x_b, w_b, y_b, rstd_b, rows_b, head_dim, eps, layout_b, pb, ext_b, &b, &lb)))
+    return rc;
+  if (!la) return RMSNORM_OK;   // tokens == 0
+  const size_t ea = static_cast<size_t>(ext_a) * 2, eb = static_cast<size_t>(ext_b) * 2;
+  // each norm's outputs against the other norm's inputs and outputs
+  if (overlaps(y_a, ea, x_b, eb) || overlaps(y_b, eb, x_a, ea) ||
+      overlaps(y_a, ea, w_b, head_dim * 2) || overlaps(y_b, eb, w_a, head_dim * 2) ||
+      !windows_disjoint(y_a, heads_a * head_dim, token_stride_a, ext_a, y_b, heads_b * head_dim,
+                        token_stride_b, ext_b) ||
+      (rstd_a != nullptr && (overlaps(rstd_a, rows_a * 4, x_b, eb) || overlaps(rstd_a, rows_a * 4, y_b, eb) ||
+                             (rstd_b != nullptr && overlaps(rstd_a, rows_a * 4, rstd_b, rows_b * 4)))) ||
+      (rstd_b != nullptr && (overlaps(rstd_b, rows_b * 4, x_a, ea) || overlaps(rstd_b, rows_b * 4, y_a, ea))))
+    return fail(RMSNORM_EINVAL, "the pair's outputs must not alias its inputs or each other");
+  hipError_t e = rbi::launch_fwd_pair(a, b, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rmsnorm_fwd_packed_pair launch");
+  return RMSNORM_OK;
+}
+
+int rmsnorm_bwd_dx_packed_pair(const rmsnorm_bf16* x_a, const rmsnorm_bf16* w_a,
+                               const rmsnorm_bf16* dy_a, const float* rstd_a, rmsnorm_bf16* dx_a,
+                               int64_t heads_a, int64_t token_stride_a,
+                               const rmsnorm_layout* layout_a, rmsnorm_dw_acc* acc_a,
+                               const rmsnorm_bf16* x_b, const rmsnorm_bf16* w_b,
+                               const rmsnorm_bf16* dy_b, const float* rstd_b, rmsnorm_bf16* dx_b,
+                               int64_t heads_b, int64_t token_stride_b,
+                               const rmsnorm_layout* layout_b, rmsnorm_dw_acc* acc_b,
+                               int64_t tokens, int64_t head_dim, void* stream) {
+  rbi::RowPacking pa, pb;
+  int64_t rows_a = 0, rows_b = 0, ext_a = 0, ext_b = 0;
+  int rc;
+  if ((rc = check_packing(tokens, heads_a, head_dim, token_stride_a, &pa, &rows_a, &ext_a)) ||
+      (rc = check_packing(tokens, heads_b, head_dim, token_stride_b, &pb, &rows_b, &ext_b)))
+    return rc;
+  if (acc_a != nullptr && acc_a == acc_b)
+    return fail(RMSNORM_EINVAL, "the two norms of a pair need accumulators of their own");
+  BwdCall ca, cb;
+  if ((rc = bwd_prepare(x_a, w_a, dy_a, rstd_a, dx_a, rows_a, head_dim, layout_a, acc_a, true, pa,
+                        ext_a, false, 0.0f, &ca)) ||
+      (rc = bwd_prepare(x_b, w_b, dy_b, rstd_b, dx_b, rows_b, head_dim, layout_b, acc_b, true, pb,
+                        ext_b, false, 0.0f, &cb)))
+    return rc;
+  if (ca.launch) {
+    const size_t ea = static_cast<size_t>(ext_a) * 2, eb = static_cast<size_t>(ext_b) * 2;
+    if (overlaps(dx_a, ea, x_b, eb) || overlaps(dx_a, ea, dy_b, eb) ||
+        overlaps(dx_a, ea, w_b, head_dim * 2) || overlaps(dx_a, ea, rstd_b, rows_b * 4) ||
+        overlaps(dx_b, eb, x_a, ea) || overlaps(dx_b, eb, dy_a, ea) ||
+        overlaps(dx_b, eb, w_a, head_dim * 2) || overlaps(dx_b, eb, rstd_a, rows_a * 4) ||
+        !windows_disjoint(dx_a, heads_a * head_dim, token_stride_a, ext_a, dx_b,
+                          heads_b * head_dim, token_stride_b, ext_b))
+      return fail(RMSNORM_EINVAL, "the pair's dx must not alias its inputs or each other");
+    hipError_t e = rbi::launch_bwd_pair(ca.a, acc_a != nullptr, cb.a, acc_b != nullptr,
+                                        reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm_bwd_dx_packed_pair launch");
+  }
+  bwd_commit(ca);
+  bwd_commit(cb);
+  return RMSNORM_OK;
 }
 
 int rmsnorm_dw_contrib(const rmsnorm_bf16* x, const rmsnorm_bf16* dy, const float* rstd,

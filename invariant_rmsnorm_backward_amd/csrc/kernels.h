@@ -101,6 +101,12 @@ enum class BwdPath { kSmall, kSplit, kStream, kFused };
 BwdPath bwd_path(const BwdArgs& a, bool with_dx, bool with_dw, bool recompute);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// Two per-head norms (hidden <= 256, row placement given by each one's
+// RowPacking) in one launch, every bit as in two launch_fwd calls.
+hipError_t launch_fwd_pair(const FwdArgs& a, const FwdArgs& b, hipStream_t stream);
+// The same for the backward with dx; dw_a / dw_b: fold into a.P / b.P.
+hipError_t launch_bwd_pair(const BwdArgs& a, bool dw_a, const BwdArgs& b, bool dw_b,
+                           hipStream_t stream);
 // dst[0..n16) = src[0..n16) in 16-byte units with the kernels' streaming
 // access policy, one unit per thread (a practical bandwidth ceiling).
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t n16, hipStream_t stream);

@@ -172,17 +172,17 @@ __global__ __launch_bounds__(256) void fwd_row_kernel(FwdArgs a) {
   if (half == 0 && lane == 0 && a.rstd != nullptr) a.rstd[row] = r;
 }
 
-// hidden = 8L with L lanes per row (L in 1..32, a power of two).
+// hidden = 8L with L lanes per row (L in 1..32, a power of two); workgroup
+// wg of n_wg walks row groups wg, wg + n_wg, ...
 template <int L, bool PACKED>
-__global__ __launch_bounds__(256) void fwd_small_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_small_rows(const FwdArgs& a, int64_t wg, int64_t n_wg) {
   constexpr int H = 8 * L;
   constexpr int GROUPS = 256 / L;
   const int g = threadIdx.x / L;
   const int sub = threadIdx.x % L;
   float wf[8];
   unpack8(load16(a.w + sub * 8), wf);
-  for (int64_t base = (int64_t)blockIdx.x * GROUPS; base < a.rows;
-       base += (int64_t)gridDim.x * GROUPS) {
+  for (int64_t base = wg * GROUPS; base < a.rows; base += n_wg * GROUPS) {
     const int64_t row = base + g;
     const bool valid = row < a.rows;
     const bool pad = valid && a.row_logical != nullptr && a.row_logical[row] < 0;
@@ -204,6 +204,18 @@ __global__ __launch_bounds__(256) void fwd_small_kernel(FwdArgs a) {
       if (sub == 0 && a.rstd != nullptr) a.rstd[row] = pad ? 0.0f : r;
     }
   }
+}
+template <int L, bool PACKED>
+__global__ __launch_bounds__(256) void fwd_small_kernel(FwdArgs a) {
+  fwd_small_rows<L, PACKED>(a, blockIdx.x, gridDim.x);
+}
+// Two per-head norms (the Q and K heads of a packed tensor) in one launch:
+// workgroups 0 .. wg_a-1 run norm a, the rest norm b, each exactly as in its
+// own launch.
+template <int L>
+__global__ __launch_bounds__(256) void fwd_small_pair_kernel(FwdArgs a, FwdArgs b, int wg_a) {
+  if ((int)blockIdx.x < wg_a) fwd_small_rows<L, true>(a, blockIdx.x, wg_a);
+  else fwd_small_rows<L, true>(b, (int)blockIdx.x - wg_a, (int)gridDim.x - wg_a);
 }
 
 // ----------------------------------------------------------------- backward
@@ -1015,7 +1027,7 @@ __global__ __launch_bounds__(128 * TW) void bwd_split_kernel(BwdArgs a, SplitMap
 // RC: rstd rebuilt from the row in the forward's order (the same lanes, the
 // same chain and group sum), so its bits are the saved rstd's.
 template <int L, bool DX, bool DW, bool PACKED, bool RC>
-__global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_small_block(const BwdArgs& a, int item) {
   constexpr int H = 8 * L;
   constexpr int GROUPS = 256 / L;
   constexpr int ITERS = (kBlockRows + GROUPS - 1) / GROUPS;
@@ -1024,7 +1036,6 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int g = tid / L;
   const int sub = tid % L;
-  const int item = blockIdx.x;
 
   if (item >= a.plan.n_items) {
     if (DX) {
@@ -1129,6 +1140,18 @@ __global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
       a.P[(int64_t)blk * H + j] = stream_tree4(q_s[j], q_s[H + j], q_s[2 * H + j], q_s[3 * H + j]);
     if (a.form != nullptr && tid == 0) a.form[blk] = 0;
   }
+}
+template <int L, bool DX, bool DW, bool PACKED, bool RC>
+__global__ __launch_bounds__(256) void bwd_small_kernel(BwdArgs a) {
+  bwd_small_block<L, DX, DW, PACKED, RC>(a, blockIdx.x);
+}
+// Two per-head norms in one launch (dx, and dweight into their own
+// accumulators or none): workgroups 0 .. wg_a-1 run norm a's items and
+// padding rows, the rest norm b's, each exactly as in its own launch.
+template <int L, bool DW>
+__global__ __launch_bounds__(256) void bwd_small_pair_kernel(BwdArgs a, BwdArgs b, int wg_a) {
+  if ((int)blockIdx.x < wg_a) bwd_small_block<L, true, DW, true, false>(a, blockIdx.x);
+  else bwd_small_block<L, true, DW, true, false>(b, (int)blockIdx.x - wg_a);
 }
 
 // ----------------------------------------------------------------- finalize
@@ -1362,6 +1385,32 @@ static void fwd_small_go(const FwdArgs& a, hipStream_t st) {
     fwd_small_kernel<L, false><<<dim3((unsigned)g), dim3(256), 0, st>>>(a);
 }
 
+template <int L>
+static void fwd_small_pair_go(const FwdArgs& a, const FwdArgs& b, hipStream_t st) {
+  constexpr int GROUPS = 256 / L;
+  auto groups = [](const FwdArgs& x) {
+    const int64_t g = (x.rows + GROUPS - 1) / GROUPS;
+    return g > grid_cap() ? (int64_t)grid_cap() : g;
+  };
+  const int64_t ga = groups(a), gb = groups(b);
+  if (ga + gb == 0) return;
+  fwd_small_pair_kernel<L><<<dim3((unsigned)(ga + gb)), dim3(256), 0, st>>>(a, b, (int)ga);
+}
+
+hipError_t launch_fwd_pair(const FwdArgs& a, const FwdArgs& b, hipStream_t st) {
+  if (a.hidden != b.hidden) return hipErrorInvalidValue;
+  switch (small_lanes(a.hidden)) {
+    case 1: fwd_small_pair_go<1>(a, b, st); break;
+    case 2: fwd_small_pair_go<2>(a, b, st); break;
+    case 4: fwd_small_pair_go<4>(a, b, st); break;
+    case 8: fwd_small_pair_go<8>(a, b, st); break;
+    case 16: fwd_small_pair_go<16>(a, b, st); break;
+    case 32: fwd_small_pair_go<32>(a, b, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
   if (is_packed(a.pack, a.hidden) && !packed_hidden_supported(a.hidden)) return hipErrorInvalidValue;
@@ -1582,6 +1631,37 @@ static void bwd_small_go(const BwdArgs& a, bool dx, bool dw, bool rc, hipStream_
     else if (dx) bwd_small_kernel<L, true, false, false, false><<<grid, block, 0, st>>>(a);
     else bwd_small_kernel<L, false, true, false, false><<<grid, block, 0, st>>>(a);
   }
+}
+
+template <int L>
+static void bwd_small_pair_go(const BwdArgs& a, const BwdArgs& b, bool dw, hipStream_t st) {
+  constexpr int GROUPS = 256 / L;
+  const int wa = a.plan.n_items + (a.plan.n_pad + GROUPS - 1) / GROUPS;
+  const int wb = b.plan.n_items + (b.plan.n_pad + GROUPS - 1) / GROUPS;
+  if (wa + wb == 0) return;
+  const dim3 grid((unsigned)(wa + wb)), block(256);
+  if (dw) bwd_small_pair_kernel<L, true><<<grid, block, 0, st>>>(a, b, wa);
+  else bwd_small_pair_kernel<L, false><<<grid, block, 0, st>>>(a, b, wa);
+}
+
+hipError_t launch_bwd_pair(const BwdArgs& a, bool dw_a, const BwdArgs& b, bool dw_b,
+                           hipStream_t st) {
+  if (a.hidden != b.hidden || small_lanes(a.hidden) == 0) return hipErrorInvalidValue;
+  if (dw_a != dw_b) {
+    // one norm with an accumulator and one without: two launches
+    hipError_t e = launch_bwd(a, true, dw_a, st);
+    return e != hipSuccess ? e : launch_bwd(b, true, dw_b, st);
+  }
+  switch (small_lanes(a.hidden)) {
+    case 1: bwd_small_pair_go<1>(a, b, dw_a, st); break;
+    case 2: bwd_small_pair_go<2>(a, b, dw_a, st); break;
+    case 4: bwd_small_pair_go<4>(a, b, dw_a, st); break;
+    case 8: bwd_small_pair_go<8>(a, b, dw_a, st); break;
+    case 16: bwd_small_pair_go<16>(a, b, dw_a, st); break;
+    case 32: bwd_small_pair_go<32>(a, b, dw_a, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdArgs& a, bool dx, bool dw, hipStream_t st, bool rc) {

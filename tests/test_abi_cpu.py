@@ -217,3 +217,37 @@ def test_noalloc_refusals_before_any_launch(lib):
         with pytest.raises(binding.RmsNormError) as ei:
             binding.rmsnorm_bwd_noalloc(*args, None)
         assert ei.value.code == code, (args, ei.value)
+
+
+def test_packed_pair_checks_its_arguments(lib):
+    """The one-launch Q/K pair refuses, before any launch, what either single
+    call would refuse, outputs that share elements, and one accumulator for
+    both norms; zero tokens is a no-op."""
+    A = 1 << 24
+    hd, hq, hk = 128, 4, 2
+    ts = (hq + 2 * hk) * hd                      # elements per token
+    tok = 4
+    ext = ((tok - 1) * ts + hq * hd) * 2         # bytes a norm's rows span
+    X, Y, DY, DX, W, R = A, A + (1 << 22), A + (2 << 22), A + (3 << 22), A + (4 << 22), A + (5 << 22)
+    kcol = hq * hd * 2                           # byte offset of the K heads in a token
+
+    def fwd(yk=Y + kcol, head_dim=hd, tokens=tok, stride_k=ts):
+        a = (X, W, Y, R, hq, ts, None)
+        b = (X + kcol, W + 4096, yk, R + 65536, hk, stride_k, None)
+        binding.rmsnorm_fwd_packed_pair(a, b, tokens, head_dim, 1e-6, None)
+
+    for kw, code in ((dict(head_dim=96), binding.EUNSUPPORTED),
+                     (dict(yk=Y + 128), binding.EINVAL),          # K outputs inside the Q windows
+                     (dict(yk=X + kcol), binding.EINVAL),         # K output on the pair's input
+                     (dict(stride_k=100), binding.EINVAL)):       # not a multiple of 8
+        with pytest.raises(binding.RmsNormError) as ei:
+            fwd(**kw)
+        assert ei.value.code == code, (kw, ei.value)
+    fwd(tokens=0)                                # nothing to do
+    ACC = 1 << 30                                # never dereferenced: refused first
+    a = (X, W, DY, R, DX, hq, ts, None, ACC)
+    b = (X + kcol, W + 4096, DY + kcol, R + 65536, DX + kcol, hk, ts, None, ACC)
+    with pytest.raises(binding.RmsNormError) as ei:
+        binding.rmsnorm_bwd_dx_packed_pair(a, b, tok, hd, None)
+    assert ei.value.code == binding.EINVAL and "accumulators" in ei.value.message
+    assert ext > 0

@@ -213,3 +213,103 @@ def test_packed_qk_norm_matches_the_oracle(lengths, layout):
     v0 = (hq + hk) * d
     for t in (y, dx):
         assert bool((t.view(torch.int16)[:, v0:] == SENTINEL).all())   # V never written
+
+
+@pytest.mark.parametrize("lengths,layout", [([100, 37, 64], "identity"), ([70, 3, 41], "padded_permuted")])
+def test_packed_pair_launch_equals_two_calls_and_the_oracle(lengths, layout):
+    """rmsnorm_fwd_packed_pair / rmsnorm_bwd_dx_packed_pair run Q and K in one
+    launch each: y, rstd, dx and both dweights bit for bit those of the two
+    single packed calls, V never written, and the pair's outputs against the
+    FP64 oracle (tolerance contract and the one-ulp gate)."""
+    from tests import parity_utils as pu
+    from invariant_rmsnorm_backward_amd import contract
+    con = contract.load_contract()
+    wq, wk = _side("q", lengths), _side("k", lengths)
+    d, T = wq.hidden, wq.n_tokens
+    hq, hk = wq.heads, wk.heads
+    if layout == "identity":
+        tok = np.arange(T)
+    else:
+        perm = np.random.default_rng(12).permutation(T)
+        tok = np.concatenate([[-1] * 3, perm[: T // 3], [-1] * 4, perm[T // 3:], [-1] * 2])
+    P = len(tok)
+    real = tok >= 0
+    ts = (hq + 2 * hk) * d
+    st = binding.current_stream()
+    phys = torch.from_numpy(np.nonzero(real)[0]).cuda()
+    logi = torch.from_numpy(tok[real]).cuda()
+
+    def packed(q, k):
+        t = torch.zeros((P, ts), dtype=torch.bfloat16, device="cuda")
+        t[phys, : hq * d] = q.view(T, hq * d)[logi]
+        t[phys, hq * d: (hq + hk) * d] = k.view(T, hk * d)[logi]
+        return t
+
+    x = packed(inputs.gen_x(wq, device="cuda"), inputs.gen_x(wk, device="cuda"))
+    dy = packed(inputs.gen_dy(wq, device="cuda"), inputs.gen_dy(wk, device="cuda"))
+    sides = (("q", wq, hq, 0), ("k", wk, hk, hq * d))
+    ws = {s: inputs.gen_w(wl, device="cuda") for s, wl, _, _ in sides}
+    lays = {}
+    for s, wl, heads, _ in sides:
+        rl = np.where(tok[:, None] < 0, -1, tok[:, None] * heads + np.arange(heads)[None, :]).reshape(-1)
+        lays[s] = None if layout == "identity" else binding.Layout(rl.astype(np.int32), T * heads)
+    lh = {s: (None if lays[s] is None else lays[s].handle) for s in lays}
+    col = lambda t, c0: t.view(torch.int16)[:, c0:].view(torch.bfloat16)
+    out = {}
+    for mode in ("single", "pair"):
+        y = torch.full((P, ts), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        dx = y.clone()
+        r = {s: torch.empty(P * h, dtype=torch.float32, device="cuda") for s, _, h, _ in sides}
+        acc = {s: binding.DwAccumulator(T * h, d) for s, _, h, _ in sides}
+        if mode == "single":
+            for s, wl, heads, c0 in sides:
+                binding.rmsnorm_fwd_packed(col(x, c0).data_ptr(), ws[s].data_ptr(), col(y, c0).data_ptr(),
+                                           r[s].data_ptr(), P, heads, d, ts, wl.eps, lh[s], st)
+                binding.rmsnorm_bwd_dx_packed(col(x, c0).data_ptr(), ws[s].data_ptr(),
+                                              col(dy, c0).data_ptr(), r[s].data_ptr(),
+                                              col(dx, c0).data_ptr(), P, heads, d, ts, lh[s],
+                                              acc[s].handle, st)
+        else:
+            fa = [(col(x, c0).data_ptr(), ws[s].data_ptr(), col(y, c0).data_ptr(), r[s].data_ptr(),
+                   heads, ts, lh[s]) for s, _, heads, c0 in sides]
+            binding.rmsnorm_fwd_packed_pair(fa[0], fa[1], P, d, wq.eps, st)
+            ba = [(col(x, c0).data_ptr(), ws[s].data_ptr(), col(dy, c0).data_ptr(), r[s].data_ptr(),
+                   col(dx, c0).data_ptr(), heads, ts, lh[s], acc[s].handle) for s, _, heads, c0 in sides]
+            binding.rmsnorm_bwd_dx_packed_pair(ba[0], ba[1], P, d, st)
+        dw = {s: acc[s].finalize() for s in acc}
+        torch.cuda.synchronize()
+        out[mode] = (y, dx, r, dw)
+        for a in acc.values():
+            a.close()
+    (y1, dx1, r1, dw1), (y2, dx2, r2, dw2) = out["single"], out["pair"]
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(dx1.view(torch.int16), dx2.view(torch.int16))
+    for s in ("q", "k"):
+        assert torch.equal(r1[s].view(torch.int32), r2[s].view(torch.int32)), s
+        assert torch.equal(dw1[s].view(torch.int32), dw2[s].view(torch.int32)), s
+    v0 = (hq + hk) * d
+    for t in (y2, dx2):
+        assert bool((t.view(torch.int16)[:, v0:] == SENTINEL).all())   # V never written
+    # the pair against the oracle, in logical row order t * heads + h
+    inv = np.empty(T, dtype=np.int64)
+    inv[tok[real]] = np.nonzero(real)[0]
+    order = torch.from_numpy(inv).cuda()
+    for s, wl, heads, c0 in sides:
+        ref = _oracle_side(wl)
+        rows_log = T * heads
+        sl = slice(c0, c0 + heads * d)
+        y_log = y2.view(torch.int16)[:, sl][order].reshape(rows_log, d).cpu().numpy().view(np.uint16)
+        dx_log = dx2.view(torch.int16)[:, sl][order].reshape(rows_log, d).cpu().numpy().view(np.uint16)
+        got = {"y": (y_log.astype(np.uint32) << 16).view(np.float32).astype(np.float64),
+               "dx": (dx_log.astype(np.uint32) << 16).view(np.float32).astype(np.float64),
+               "rstd": r2[s].view(P, heads)[order].reshape(rows_log).cpu().numpy().astype(np.float64),
+               "dweight": dw2[s].cpu().numpy().astype(np.float64)}
+        names = {"y": f"y{s}", "dx": f"d{s}", "rstd": f"rstd_{s}", "dweight": f"dweight_{s}"}
+        for t in ("y", "dx", "rstd", "dweight"):
+            assert con.accuracy_passes(got[t], ref[t], names[t]), (s, layout, t)
+        for t, bits in (("y", y_log), ("dx", dx_log)):
+            assert pu.bf16_ulp_fraction(bits, ref[t]) > 0.99, (s, layout, t)
+    print(f"[packed-pair] {layout}: pair launch == two calls bitwise, oracle within contract", flush=True)
+    for lay in lays.values():
+        if lay is not None:
+            lay.close()

@@ -50,7 +50,8 @@ def _same(a, b):
 
 
 @pytest.mark.parametrize("first,second", [
-    ((8192, 4096), (3000, 4096)),      # fused, then two-pass (47 blocks) over the same scratch
+    ((8192, 4096), (3000, 4096)),      # fused, then 47 blocks over the same scratch (two-pass
+                                       # here, stream-owner in the accumulator reference)
     ((6400, 8192), (700, 1024)),       # wide fused, then a narrower shape
     ((20000, 128), (333, 64)),         # small-hidden kernel
 ])
