@@ -207,6 +207,86 @@ class QkNormAdapter(RmsNormAdapter):
                 "pad_rows_clean": np.array([bool(q["pad_rows_clean"][0] and k["pad_rows_clean"][0])])}
 
 
+class QkPairAdapter(QkNormAdapter):
+    """qk_norm with the Q and K norms of every call in one launch per phase
+    (rmsnorm_fwd_packed_pair / rmsnorm_bwd_dx_packed_pair, each norm's rows
+    contiguous: token stride = heads * head_dim).  Same gradient names and,
+    by the entry points' contract, the same bits as qk_norm."""
+    name = "qk_norm_pair"
+
+    def run_cell(self, cell: PairCell, data: QkInputs) -> Dict[str, np.ndarray]:
+        sides = (("q", cell.q, data.q), ("k", cell.k, data.k))
+        d = data.q.x.shape[1]
+        dev = data.q.x.device
+        heads = {s: nd.workload.heads for s, _, nd in sides}
+        st = binding.current_stream()
+        accs, outs, layouts_ = {}, {}, []
+        for s, c, nd in sides:
+            T = nd.x.shape[0]
+            accs[s] = binding.DwAccumulator(T, d, max_spill_rows=spill_bound(c, T))
+            outs[s] = {"y": torch.zeros_like(nd.x), "dx": torch.zeros_like(nd.x),
+                       "rstd": torch.zeros(T, dtype=torch.float32, device=dev)}
+        pads_clean = True
+        for j, (cq, ck) in enumerate(zip(cell.q.calls, cell.k.calls)):
+            self.call_log.append((cell.name, cq.name, cq.rows))
+            per = {}
+            for s, call, nd in (("q", cq, data.q), ("k", ck, data.k)):
+                T = nd.x.shape[0]
+                if call.row_logical is None:
+                    per[s] = dict(x=nd.x, dy=nd.dy, lay=None, rl=None, rows=T)
+                else:
+                    rl = torch.from_numpy(call.row_logical.astype(np.int64)).to(dev)
+                    real = rl >= 0
+                    xc, dyc = _poisoned(call.rows, d, dev), _poisoned(call.rows, d, dev)
+                    xc[real] = nd.x[rl[real]]
+                    dyc[real] = nd.dy[rl[real]]
+                    lay = binding.Layout(call.row_logical, T)
+                    layouts_.append(lay)
+                    per[s] = dict(x=xc, dy=dyc, lay=lay, rl=rl, rows=call.rows)
+                p = per[s]
+                p["y"] = torch.empty_like(p["x"])
+                p["dx"] = torch.empty_like(p["x"])
+                p["rstd"] = torch.empty(p["rows"], dtype=torch.float32, device=dev)
+            tokens = per["q"]["rows"] // heads["q"]
+            assert tokens * heads["q"] == per["q"]["rows"] and tokens * heads["k"] == per["k"]["rows"]
+            lh = lambda p: None if p["lay"] is None else p["lay"].handle
+            fa = [(per[s]["x"].data_ptr(), nd.w.data_ptr(), per[s]["y"].data_ptr(),
+                   per[s]["rstd"].data_ptr(), heads[s], heads[s] * d, lh(per[s])) for s, _, nd in sides]
+            binding.rmsnorm_fwd_packed_pair(fa[0], fa[1], tokens, d, data.q.eps, st)
+            ba = [(per[s]["x"].data_ptr(), nd.w.data_ptr(), per[s]["dy"].data_ptr(),
+                   per[s]["rstd"].data_ptr(), per[s]["dx"].data_ptr(), heads[s], heads[s] * d,
+                   lh(per[s]), accs[s].handle) for s, _, nd in sides]
+            binding.rmsnorm_bwd_dx_packed_pair(ba[0], ba[1], tokens, d, st)
+            for s in ("q", "k"):
+                p, o = per[s], outs[s]
+                if p["rl"] is None:
+                    o["y"].copy_(p["y"])
+                    o["dx"].copy_(p["dx"])
+                    o["rstd"].copy_(p["rstd"])
+                    continue
+                real = p["rl"] >= 0
+                for t in ("y", "dx", "rstd"):
+                    o[t][p["rl"][real]] = p[t][real]
+                if bool((~real).any()):
+                    pad = ~real
+                    pads_clean &= bool((p["y"][pad].view(torch.int16) == 0).all())
+                    pads_clean &= bool((p["dx"][pad].view(torch.int16) == 0).all())
+                    pads_clean &= bool((p["rstd"][pad] == 0).all())
+        dw = {s: accs[s].finalize() for s in accs}
+        torch.cuda.synchronize()
+        bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+        res = {"dq": bits(outs["q"]["dx"]), "dk": bits(outs["k"]["dx"]),
+               "dweight_q": dw["q"].cpu().numpy(), "dweight_k": dw["k"].cpu().numpy(),
+               "yq": bits(outs["q"]["y"]), "yk": bits(outs["k"]["y"]),
+               "rstd_q": outs["q"]["rstd"].cpu().numpy(), "rstd_k": outs["k"]["rstd"].cpu().numpy(),
+               "pad_rows_clean": np.array([pads_clean])}
+        for lay in layouts_:
+            lay.close()
+        for a in accs.values():
+            a.close()
+        return res
+
+
 @dataclasses.dataclass
 class LinearInputs:
     """Logical inputs of a linear layer: x[n_logical, k], W[n, k], dY[n_logical, n]."""
@@ -460,6 +540,7 @@ GRADIENT_ADAPTERS = {
     "rms_norm": RmsNormAdapter,
     "rms_norm_recompute": RmsNormRecomputeAdapter,
     "qk_norm": QkNormAdapter,
+    "qk_norm_pair": QkPairAdapter,
     "det_gemm": LinearAdapter,
     "rms_norm+det_gemm": NormLinearChainAdapter,
     "embedding": EmbeddingAdapter,

@@ -36,6 +36,8 @@ CHAINS = {"chain_rmsnorm_linear_h4096_o4096_t32768": "linear_h4096_o4096_t32768"
 CHUNK = {"rmsnorm_h8_t59": 7, "qknorm": 512}
 # An RMSNorm workload name with this suffix runs the rstd-recompute backward.
 RECOMPUTE = "+recompute"
+# The per-head workload with this suffix runs Q and K in one launch per phase.
+PAIR = "+pair"
 
 
 def _workload(name: str, small: bool) -> inputs.Workload:
@@ -60,7 +62,7 @@ def _run(op_name: str, wls, cells_by_side, names=None):
     """Runs one op over its cells; returns the report (or a blocked one)."""
     from . import adapters
     c = contract.load_contract()
-    if op_name == "qk_norm":
+    if op_name in ("qk_norm", "qk_norm_pair"):
         wq, wk = wls
         cq, ck = cells_by_side
         cells = [adapters.PairCell(a.name, a, b) for a, b in zip(cq, ck)]
@@ -70,7 +72,7 @@ def _run(op_name: str, wls, cells_by_side, names=None):
         cells = [x for x in cells if x.name in names or x.name == "BN/full"]
     if not _gpu():
         return None, cells
-    if op_name == "qk_norm":
+    if op_name in ("qk_norm", "qk_norm_pair"):
         data = adapters.QkInputs(wls[0].name.rsplit("_", 1)[0], adapters.make_inputs(wls[0]),
                                  adapters.make_inputs(wls[1]))
     elif op_name == "det_gemm":
@@ -100,9 +102,11 @@ def _targets(names, small):
             wl = _workload(base, small)
             out.append(("rms_norm_recompute", n, (wl,), (_cells(wl),)))
         elif n.startswith("qknorm"):
+            # "+pair": Q and K of every call in one launch per phase
             base = "qknorm_d128_t16384"
             wq, wk = _workload(base + "_q", small), _workload(base + "_k", small)
-            out.append(("qk_norm", base, (wq, wk), (_cells(wq), _cells(wk))))
+            op = "qk_norm_pair" if n.endswith(PAIR) else "qk_norm"
+            out.append((op, n, (wq, wk), (_cells(wq), _cells(wk))))
         else:
             wl = _workload(n, small)
             out.append(("rms_norm", n, (wl,), (_cells(wl),)))

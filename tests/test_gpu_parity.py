@@ -109,6 +109,8 @@ def test_qk_norm_parity_and_invariance():
     ref = {"dq": rq["dx"], "dk": rk["dx"], "dweight_q": rq["dweight"], "dweight_k": rk["dweight"],
            "yq": rq["y"], "yk": rk["y"], "rstd_q": rq["rstd"], "rstd_k": rk["rstd"]}
     _run("qk_norm", pu.qk_cells(wq, wk, 16), data, ref, "qk_norm")
+    # the same cells with Q and K of every call in one launch per phase
+    _run("qk_norm_pair", pu.qk_cells(wq, wk, 16), data, ref, "qk_norm_pair")
 
 
 def test_masked_padded_permuted_packing_h5120():

@@ -177,8 +177,9 @@ def test_adapter_without_backward_is_red_no_backward():
 
 def test_required_ops_are_enumerable():
     from invariant_rmsnorm_backward_amd import adapters
-    assert set(adapters.GRADIENT_ADAPTERS) == {"rms_norm", "rms_norm_recompute", "qk_norm", "det_gemm",
-                                              "rms_norm+det_gemm", "embedding"}
+    assert set(adapters.GRADIENT_ADAPTERS) == {"rms_norm", "rms_norm_recompute", "qk_norm",
+                                              "qk_norm_pair", "det_gemm", "rms_norm+det_gemm",
+                                              "embedding"}
     for name, cls in adapters.GRADIENT_ADAPTERS.items():
         a = cls()
         assert a.name == name and len(a.grad_names) >= 1 and len(a.forward_names) >= 1
