@@ -524,3 +524,64 @@ def test_a_per_call_dweight_fold_on_the_gpu_is_red():
     rep_ok = harness.assert_gradient_batch_invariant(adapters.RmsNormAdapter(), cells, CONTRACT,
                                                      data=data, raise_on_red=False)
     assert rep_ok.strict
+
+
+def test_bounded_spill_area_refuses_when_full_and_matches_unbounded():
+    """rmsnorm_dw_acc_create_bounded: a call that needs a spill slot beyond the
+    bound is refused with RMSNORM_ESPILL before anything is enqueued and
+    leaves the accumulator as it was; with room for exactly the blocks the
+    calls split, dweight is bit for bit the unbounded accumulator's, on each
+    backward path."""
+    H = 1024
+    wl = inputs.scaled(inputs.workload_h4096(), "spill_bound_h1024", hidden=H, lengths=[700, 311])
+    data = pu.make_data(wl)
+    T = wl.n_logical
+    x, w, dy = data.x, data.w, data.dy
+    _, rstd = binding.fwd(x, w, data.eps)
+    # 100-row pieces: blocks 1, 3, 4, 6, ... straddle piece boundaries
+    pieces = [(a, min(a + 100, T)) for a in range(0, T, 100)]
+    need = {a // 64 for a, b in pieces if a % 64} | {(b - 1) // 64 for a, b in pieces if b % 64 and b < T}
+    assert len(need) > 2
+
+    def run(acc, pieces_):
+        lays = []
+        for a, b in pieces_:
+            lay = binding.Layout(np.arange(a, b, dtype=np.int32), T)
+            lays.append(lay)
+            binding.bwd(x[a:b].contiguous(), w, dy[a:b].contiguous(), rstd[a:b].contiguous(), lay, acc)
+        return lays
+
+    for path in pu.BWD_PATHS:
+        with pu.forced_path(path):
+            ref = binding.DwAccumulator(T, H)
+            lays = run(ref, pieces)
+            dw_ref = ref.finalize().view(torch.int32).cpu()
+            exact = binding.DwAccumulator(T, H, max_spill_rows=64 * len(need))
+            lays += run(exact, pieces)
+            dw_exact = exact.finalize().view(torch.int32).cpu()
+            assert torch.equal(dw_ref, dw_exact), path
+            # one slot short: the call that needs the missing slot is refused
+            short = binding.DwAccumulator(T, H, max_spill_rows=64 * (len(need) - 1))
+            refused_at = None
+            for i, (a, b) in enumerate(pieces):
+                lay = binding.Layout(np.arange(a, b, dtype=np.int32), T)
+                lays.append(lay)
+                try:
+                    binding.bwd(x[a:b].contiguous(), w, dy[a:b].contiguous(), rstd[a:b].contiguous(),
+                                lay, short)
+                except binding.RmsNormError as e:
+                    assert e.code == binding.ESPILL, e
+                    refused_at = i
+                    break
+            assert refused_at is not None
+            # nothing of the refused call was recorded: finalize reports its rows missing
+            with pytest.raises(binding.RmsNormError) as ei:
+                short.finalize()
+            assert ei.value.code == binding.ECOVERAGE
+            torch.cuda.synchronize()
+            for acc in (ref, exact, short):
+                acc.close()
+            for lay in lays:
+                lay.close()
+    print(f"[spill bound] {len(need)} slots: exact bound == unbounded on every path, one short refused",
+          flush=True)
