@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "RMSNorm fwd+bwd achieved HBM GB/s (% of peak) with bitwise B1/BN/chunk invariance"
 PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_traffic_rmsnorm_h4096_t32768.json")
+EMB_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_traffic_det_embedding_v32000_d4096_t32768.json")
 
 
 def algorithmic_bytes(rows_real: int, rows_phys: int, H: int):
@@ -54,14 +55,16 @@ def kernel_source_hash(names=NORM_KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(bwd_bytes: int):
-    """HBM bytes per backward launch from committed rocprofv3 counters, or
-    None when the kernels changed since they were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(bwd_bytes: int, path: str = TRAFFIC_FILE, sources=None):
+    """HBM bytes per backward launch (or per backward call, summed over its
+    launches) from committed rocprofv3 counters, or None when the kernels
+    changed since they were taken."""
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    h = kernel_source_hash() if sources is None else kernel_source_hash(sources)
+    if t.get("kernel_source_hash") != h:
         return None
     return t.get("bytes_per_launch")
 
@@ -765,8 +768,9 @@ def measure_det_embedding(args, torch, np, binding, inputs):
                    "layout": "BN/full (one call)", "step": "fwd + det_embedding_bwd"},
         "roofline": {"bound": "hbm", "achieved": round(bb / (ph["bwd"] * 1e-3) / 1e9, 2),
                      "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(bb / (ph["bwd"] * 1e-3) / 1e9 / PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "block_kernel (multi-block tokens) + finalize_direct_kernel (dE)",
+                     "frac": round(bb / (ph["bwd"] * 1e-3) / 1e9 / PEAK_GBPS, 4),
+                     "traffic": measured_traffic(bb, EMB_TRAFFIC_FILE, EMB_KERNEL_SOURCES),
+                     "kernel": "bwd_head_kernel (multi-block token folds, zero rows) + bwd_tail_kernel (trees, single-block tokens)",
                      "algorithmic_bytes_per_launch": bb, "avg_launch_ms": round(ph["bwd"], 5)},
         "cpu_baseline": cpu,
         "phases_ms": {k: round(v, 5) for k, v in ph.items()},

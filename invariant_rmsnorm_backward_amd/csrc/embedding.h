@@ -22,8 +22,8 @@ struct PlanView {
   const int32_t* tok_nblk;     // [vocab] number of blocks of the token
   const int32_t* blk_order;    // [n_blocks] block ids by decreasing length (work order only)
   const int32_t* mb_blocks;    // [n_mb_blocks] blocks of tokens with two or more blocks
-  const int32_t* mb_tokens;    // [n_mb_tokens] tokens with two or more blocks
-  const int32_t* single_tokens;  // [n_single_tokens] tokens with one block
+  const int32_t* mb_tokens;    // [n_mb_tokens] tokens with two or more blocks, most blocks first
+  const int32_t* single_tokens;  // [n_single_tokens] tokens with one block, longest first
   const int32_t* zero_tokens;    // [n_zero_tokens] tokens that do not occur
   int64_t n_blocks;
   int64_t n_mb_blocks;
@@ -41,9 +41,10 @@ hipError_t launch_blocks(const uint16_t* dy, const PlanView& plan, int64_t dim, 
 // dE[vocab][dim]: each token's tree over its block partials, 0 for absent tokens.
 hipError_t launch_finalize(const float* P, const PlanView& plan, int64_t dim, float* dE,
                            hipStream_t stream);
-// The one-call backward: dE[vocab][dim] from dY rows in logical order --
-// block partials into P only for tokens with two or more blocks, single-block
-// tokens folded straight into dE, absent tokens 0 -- then those tokens' trees.
+// The one-call backward: dE[vocab][dim] from dY rows in logical order, in two
+// launches -- block partials into P only for tokens with two or more blocks,
+// absent tokens 0; then those tokens' trees beside the single-block tokens,
+// which are folded straight into dE.
 hipError_t launch_bwd_one_call(const uint16_t* dy, float* P, const PlanView& plan, int64_t dim,
                                float* dE, hipStream_t stream);
 

@@ -76,9 +76,11 @@ __global__ __launch_bounds__(64) void block_kernel(const uint16_t* __restrict__ 
     u32x4e_t v[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const int i = i0 + u < len ? i0 + u : len - 1;       // in bounds; extra loads unused
-      const int64_t l = __builtin_amdgcn_readlane(my_row, i);
-      v[u] = on ? *reinterpret_cast<const u32x4e_t*>(dy + l * dim + 8 * q) : u32x4e_t{0u, 0u, 0u, 0u};
+      v[u] = u32x4e_t{0u, 0u, 0u, 0u};
+      if (i0 + u < len) {                                   // rows past the block's end are not loaded
+        const int64_t l = __builtin_amdgcn_readlane(my_row, i0 + u);
+        if (on) v[u] = *reinterpret_cast<const u32x4e_t*>(dy + l * dim + 8 * q);
+      }
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -164,85 +166,107 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
                               reinterpret_cast<f32x4e_t*>(dE + v * dim + c0));
 }
 
-// The one-call backward in one launch; each workgroup takes one item of a
-// three-part work list (its order is only a schedule, no result depends on it):
-//   [0, n_mb_blocks)          a block of a token with two or more blocks:
-//                             its fold over every column -> P[b];
-//   [.., + n_single_tokens)   a token with a single block: the same fold,
-//                             written straight to its dE row (the tree of one
-//                             leaf is that leaf), so no partial exists for it;
-//   [.., + ceil(n_zero / 4))  up to 4 absent tokens: their dE rows are 0.
-// Folds run over 2048 columns at a time, 8 per thread, with the rows loaded 8
-// at a time ahead of the adds, in occurrence order from +0.0: the additions of
-// block_kernel, in the same order.
+// The one-call backward in two launches.  Each workgroup takes one item of a
+// work list; the lists' order is only a schedule (longest items first), no
+// result depends on it, and every dE row and partial has one writer.
+//   head: [0, n_mb_blocks)        a block of a token with two or more blocks:
+//                                 its fold over every column -> P[b];
+//         [.., + ceil(n_zero/4))  up to 4 absent tokens: their dE rows are 0;
+//   tail: [0, n_mb_tokens x TS)   the tree of a token with two or more blocks
+//                                 over one slice of 1024 columns (TS slices);
+//         [.., + n_single_tokens) a token with a single block: the same fold,
+//                                 written straight to its dE row (the tree of
+//                                 one leaf is that leaf), so no partial exists.
+// The trees need only the head's partials, so they run beside the
+// single-block folds instead of after every other item.  Folds run over 4096
+// columns at a time, 8 + 8 per thread, with the rows loaded 8 at a time ahead
+// of the adds, in occurrence order from +0.0: the additions of block_kernel,
+// in the same order.
 constexpr int kZeroRowsPerGroup = 4;
+constexpr int kTreeCols = 1024;   // columns of one tree item (256 threads x 4)
 
-__global__ __launch_bounds__(256) void fused_bwd_kernel(const uint16_t* __restrict__ dy,
-                                                        PlanView p, int64_t dim,
-                                                        float* __restrict__ P,
-                                                        float* __restrict__ dE) {
-  const int64_t g = blockIdx.x;
-  const int t = threadIdx.x;
-  if (g >= p.n_mb_blocks + p.n_single_tokens) {
-    const int64_t z0 = (g - p.n_mb_blocks - p.n_single_tokens) * kZeroRowsPerGroup;
-    const f32x4e_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t z = z0; z < z0 + kZeroRowsPerGroup && z < p.n_zero_tokens; ++z) {
-      f32x4e_t* row = reinterpret_cast<f32x4e_t*>(dE + (int64_t)p.zero_tokens[z] * dim);
-      for (int64_t q = t; q < dim / 4; q += 256) __builtin_nontemporal_store(zero, row + q);
-    }
-    return;
-  }
-  int start, len;
-  float* out;
-  if (g < p.n_mb_blocks) {
-    const int64_t b = p.mb_blocks[g];
-    start = p.blk_start[b];
-    len = p.blk_len[b];
-    out = P + b * dim;
-  } else {
-    const int64_t v = p.single_tokens[g - p.n_mb_blocks];
-    const int b = p.tok_first[v];
-    start = p.blk_start[b];
-    len = p.blk_len[b];
-    out = dE + v * dim;
-  }
-  for (int64_t c0 = (int64_t)t * 8; c0 < dim; c0 += 256 * 8) {
-    float r[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+__device__ __forceinline__ void fold_to(const uint16_t* __restrict__ dy, const int32_t* __restrict__ occ,
+                                        int start, int len, int64_t dim, float* __restrict__ out, int t) {
+  // two 2048-column passes at a time, so that a short block's loads for both
+  // are in flight together; rows past the block's end are not loaded
+  for (int64_t c0 = (int64_t)t * 8; c0 < dim; c0 += 2 * 256 * 8) {
+    const int64_t c1 = c0 + 256 * 8;
+    const bool two = c1 < dim;
+    float r0[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    float r1[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     for (int i0 = 0; i0 < len; i0 += 8) {
-      u32x4e_t q[8];
+      u32x4e_t q0[8], q1[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u < len ? i0 + u : len - 1;       // in bounds; extra loads unused
-        const int64_t l = p.occ[start + i];
-        q[u] = *reinterpret_cast<const u32x4e_t*>(dy + l * dim + c0);
+        if (i0 + u < len) {
+          const uint16_t* row = dy + (int64_t)occ[start + i0 + u] * dim;
+          q0[u] = *reinterpret_cast<const u32x4e_t*>(row + c0);
+          if (two) q1[u] = *reinterpret_cast<const u32x4e_t*>(row + c1);
+        }
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (i0 + u < len) {
           float f[8];
-          widen8(q[u], f);
+          widen8(q0[u], f);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) r[e] = r[e] + f[e];
+          for (int e = 0; e < 8; ++e) r0[e] = r0[e] + f[e];
+          if (two) {
+            widen8(q1[u], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r1[e] = r1[e] + f[e];
+          }
         }
       }
     }
     f32x4e_t* dst = reinterpret_cast<f32x4e_t*>(out + c0);
-    __builtin_nontemporal_store(f32x4e_t{r[0], r[1], r[2], r[3]}, dst);
-    __builtin_nontemporal_store(f32x4e_t{r[4], r[5], r[6], r[7]}, dst + 1);
+    __builtin_nontemporal_store(f32x4e_t{r0[0], r0[1], r0[2], r0[3]}, dst);
+    __builtin_nontemporal_store(f32x4e_t{r0[4], r0[5], r0[6], r0[7]}, dst + 1);
+    if (two) {
+      dst = reinterpret_cast<f32x4e_t*>(out + c1);
+      __builtin_nontemporal_store(f32x4e_t{r1[0], r1[1], r1[2], r1[3]}, dst);
+      __builtin_nontemporal_store(f32x4e_t{r1[4], r1[5], r1[6], r1[7]}, dst + 1);
+    }
   }
 }
 
-// The trees of the tokens with two or more blocks (the plan's list), 4
-// columns per thread.
-__global__ __launch_bounds__(256) void tree_list_kernel(const float* __restrict__ P, PlanView p,
-                                                        int64_t dim, float* __restrict__ dE) {
-  const int64_t v = p.mb_tokens[blockIdx.x];
-  const int64_t c0 = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
-  if (c0 >= dim) return;
-  float r[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  token_tree(P, p.tok_first[v], p.tok_nblk[v], dim, c0, r);
-  __builtin_nontemporal_store(f32x4e_t{r[0], r[1], r[2], r[3]},
-                              reinterpret_cast<f32x4e_t*>(dE + v * dim + c0));
+__global__ __launch_bounds__(256) void bwd_head_kernel(const uint16_t* __restrict__ dy, PlanView p,
+                                                       int64_t dim, float* __restrict__ P,
+                                                       float* __restrict__ dE) {
+  const int64_t g = blockIdx.x;
+  const int t = threadIdx.x;
+  if (g < p.n_mb_blocks) {
+    const int64_t b = p.mb_blocks[g];
+    fold_to(dy, p.occ, p.blk_start[b], p.blk_len[b], dim, P + b * dim, t);
+    return;
+  }
+  const int64_t z0 = (g - p.n_mb_blocks) * kZeroRowsPerGroup;
+  const f32x4e_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t z = z0; z < z0 + kZeroRowsPerGroup && z < p.n_zero_tokens; ++z) {
+    f32x4e_t* row = reinterpret_cast<f32x4e_t*>(dE + (int64_t)p.zero_tokens[z] * dim);
+    for (int64_t q = t; q < dim / 4; q += 256) __builtin_nontemporal_store(zero, row + q);
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_tail_kernel(const uint16_t* __restrict__ dy, PlanView p,
+                                                       int64_t dim, const float* __restrict__ P,
+                                                       float* __restrict__ dE) {
+  const int64_t g = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t ts = (dim + kTreeCols - 1) / kTreeCols;
+  if (g < p.n_mb_tokens * ts) {
+    const int64_t v = p.mb_tokens[g / ts];
+    const int64_t c0 = (g % ts) * kTreeCols + (int64_t)t * 4;
+    if (c0 >= dim) return;
+    float r[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    token_tree(P, p.tok_first[v], p.tok_nblk[v], dim, c0, r);
+    __builtin_nontemporal_store(f32x4e_t{r[0], r[1], r[2], r[3]},
+                                reinterpret_cast<f32x4e_t*>(dE + v * dim + c0));
+    return;
+  }
+  const int64_t v = p.single_tokens[g - p.n_mb_tokens * ts];
+  const int b = p.tok_first[v];
+  fold_to(dy, p.occ, p.blk_start[b], p.blk_len[b], dim, dE + v * dim, t);
 }
 
 hipError_t launch_fwd(const int32_t* ids, const uint16_t* table, uint16_t* y, int64_t rows,
@@ -272,13 +296,10 @@ hipError_t launch_finalize(const float* P, const PlanView& plan, int64_t dim, fl
 
 hipError_t launch_bwd_one_call(const uint16_t* dy, float* P, const PlanView& plan, int64_t dim,
                                float* dE, hipStream_t st) {
-  const int64_t groups = plan.n_mb_blocks + plan.n_single_tokens +
-                         (plan.n_zero_tokens + kZeroRowsPerGroup - 1) / kZeroRowsPerGroup;
-  if (groups > 0) fused_bwd_kernel<<<dim3((unsigned)groups), dim3(256), 0, st>>>(dy, plan, dim, P, dE);
-  if (plan.n_mb_tokens > 0) {
-    const dim3 tg((unsigned)plan.n_mb_tokens, (unsigned)((dim / 4 + 255) / 256));
-    tree_list_kernel<<<tg, dim3(256), 0, st>>>(P, plan, dim, dE);
-  }
+  const int64_t head = plan.n_mb_blocks + (plan.n_zero_tokens + kZeroRowsPerGroup - 1) / kZeroRowsPerGroup;
+  const int64_t tail = plan.n_mb_tokens * ((dim + kTreeCols - 1) / kTreeCols) + plan.n_single_tokens;
+  if (head > 0) bwd_head_kernel<<<dim3((unsigned)head), dim3(256), 0, st>>>(dy, plan, dim, P, dE);
+  if (tail > 0) bwd_tail_kernel<<<dim3((unsigned)tail), dim3(256), 0, st>>>(dy, plan, dim, P, dE);
   return hipGetLastError();
 }
 

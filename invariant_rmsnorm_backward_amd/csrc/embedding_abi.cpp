@@ -88,6 +88,12 @@ int build_plan(const int32_t* ids, int64_t T, int64_t vocab, HostPlan* P) {
     const int32_t n = P->tok_nblk[v];
     (n > 1 ? P->mb_tokens : n == 1 ? P->single_tokens : P->zero_tokens).push_back(static_cast<int32_t>(v));
   }
+  // work order of the one-call backward's items: the longest trees and folds first
+  std::stable_sort(P->mb_tokens.begin(), P->mb_tokens.end(),
+                   [&](int32_t a, int32_t b) { return P->tok_nblk[a] > P->tok_nblk[b]; });
+  std::stable_sort(P->single_tokens.begin(), P->single_tokens.end(), [&](int32_t a, int32_t b) {
+    return P->blk_len[P->tok_first[a]] > P->blk_len[P->tok_first[b]];
+  });
   return RMSNORM_OK;
 }
 
@@ -279,11 +285,15 @@ int det_embedding_dw_finalize(det_embedding_dw_acc* acc, float* dE, void* stream
   if (rc != RMSNORM_OK) return fail(rc, err);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  if (acc->mode == kStaged &&
-      (e = rbi::emb::launch_blocks(acc->d_dy, acc->view, acc->dim, acc->d_P, st)) != hipSuccess)
-    return hip_fail(e, "embedding block folds");
-  if ((e = rbi::emb::launch_finalize(acc->d_P, acc->view, acc->dim, dE, st)) != hipSuccess)
+  if (acc->mode == kStaged) {
+    // every row is staged in logical order: the one-call backward's kernels
+    // (no partials for single-block tokens) give the same bits
+    if ((e = rbi::emb::launch_bwd_one_call(acc->d_dy, acc->d_P, acc->view, acc->dim, dE, st)) !=
+        hipSuccess)
+      return hip_fail(e, "embedding folds and token trees");
+  } else if ((e = rbi::emb::launch_finalize(acc->d_P, acc->view, acc->dim, dE, st)) != hipSuccess) {
     return hip_fail(e, "embedding token trees");
+  }
   acc->host.finalized = true;
   return RMSNORM_OK;
 }
