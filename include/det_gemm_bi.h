@@ -8,8 +8,8 @@
  * harness and operator adapters", section "Required adapters", lists GEMM
  * dX/dW; "WS1 C4 (#270) closeout evidence" (status table and the note on
  * the reds) places the deterministic GEMM's dW in the same failure class as
- * RMSNorm's dweight and states that parameter VJPs are built from
- * logical-row FP32 contributions.  With x[rows][K], W[N][K], dY[rows][N]:
+ * RMSNorm's dweight, fixed by building parameter gradients from one FP32
+ * contribution per logical row.  With x[rows][K], W[N][K], dY[rows][N]:
  *     y[r][n]  = sum_k x[r][k] W[n][k]                (bf16 out, FP32 accumulate)
  *     dX[r][k] = sum_n dY[r][n] W[n][k]               (bf16 out, FP32 accumulate)
  *     dW[n][k] = sum over logical rows l of dY[l][n] X[l][k]    (FP32)

@@ -8,7 +8,7 @@ so that every physical layout of the same logical multiset sees the same
 bits ("[WS1 Closeout][Backward] Reusable gradient-invariance harness and
 operator adapters", section Scope: the upstream gradient and active-token
 denominator are fixed across configs; "WS1 C4 (#270) closeout evidence",
-"Acceptance map": the upstream is a pure function of logical identity).
+Acceptance map: dy depends on nothing but the logical identity of the row).
 
 Generator: the SplitMix64 output function (Steele, Lea, Flood, "Fast
 splittable pseudorandom number generators", OOPSLA 2014) applied to a packed

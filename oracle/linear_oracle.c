@@ -10,8 +10,8 @@
  * and operator adapters", section "Required adapters", lists GEMM dX/dW
  * among the required gradients; "WS1 C4 (#270) closeout evidence" (status
  * table and the note on the reds) puts the deterministic GEMM's dW in the
- * same failure class as RMSNorm's dweight and states that parameter VJPs are
- * now built from logical-row FP32 contributions.  The pages print no
+ * same failure class as RMSNorm's dweight; its fix builds parameter
+ * gradients from one FP32 contribution per logical row.  The pages print no
  * formula; the reading used is the standard linear layer
  *     y[r][n]  = sum_k x[r][k] * W[n][k]          (y = x W^T)
  * with x[rows][K], W[N][K], y[rows][N], and its VJP

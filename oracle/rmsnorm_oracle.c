@@ -170,9 +170,9 @@ int oracle_rmsnorm_bwd(const double* x, const double* w, const double* dy, int64
 
 /* ------------------------------------------------------------------------
  * CDO-v2: the canonical FP32 order in which dweight is reduced.  The pages
- * fix only that parameter gradients come from "logical-row FP32
- * contributions" reduced in a "fixed aggregation order" ("WS1 C4 (#270)
- * closeout evidence", opening note and "Acceptance map"); the order below is
+ * fix only that parameter gradients are built from one FP32 contribution per
+ * logical row and reduced in an order that never changes ("WS1 C4 (#270)
+ * closeout evidence", opening note and Acceptance map); the order below is
  * this project's reading of that, written out plainly:
  *   c[l][j] = fl32(fl32(dy * x) * rstd)    one value per logical row; dy*x
  *       of two bf16 values is exact in FP32, so c is dy*x*rstd rounded once
