@@ -67,16 +67,12 @@ __device__ __forceinline__ void wait_vm_lgkm() {
 // Workgroup barrier without a memory fence: the engine waits for its own loads
 // explicitly (a fenced barrier would wait for every load still in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-// 16 bytes per lane from global memory into LDS at lds + 16 * lane (the LDS
-// base goes through m0, which is saved and restored around the load).  The
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane.  The LDS
+// base is an input bound to m0, so the compiler sets m0 itself; the s_nop is
+// the wait state between an m0 write and the load that reads it.  The
 // compiler does not track this load; the engine waits for it with vmcnt.
 __device__ __forceinline__ void load_to_lds(uint64_t src, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds));
 }
 #define RBI_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
@@ -101,7 +97,9 @@ struct Acc {
 //      values of one k, chunk c at position c ^ swk(kr).
 // Thread t loads the chunks P = NT i + t of the tile (i < NI); a wavefront's
 // 64 loads fill 1 KB of LDS contiguously.
-template <bool KM, int ROWS, int BK, int NT>
+// INNER: every tile row is in range and every stage is either wholly inside
+// [0, k_lim) or wholly past it, so a load needs no per-lane range test.
+template <bool KM, int ROWS, int BK, int NT, bool INNER = false>
 struct Operand {
   static constexpr int CHUNKS = ROWS * BK / 8;
   static constexpr int NI = CHUNKS / NT;
@@ -159,6 +157,15 @@ struct Operand {
 
   template <int I>
   __device__ __forceinline__ void issue_one(uint32_t tile, int64_t k0, int w) const {
+    const uint32_t dst = tile + (uint32_t)((NT * I + 64 * w) * 16);
+    if constexpr (INNER) {
+      // k0 is the same in every lane: a stage past the end reads zeros
+      const uint64_t a = !KM ? base + (uint64_t)(((int64_t)RSTEP * I * ld + k0) * 2)
+                             : base + (uint64_t)((k0 + (int64_t)RSTEP * I) * ld * 2);
+      if (k0 + BK <= k_lim) load_to_lds(a, dst);
+      else load_to_lds(zp, dst);
+      return;
+    }
     bool v;
     uint64_t a;
     if (!KM) {
@@ -168,7 +175,7 @@ struct Operand {
       v = (bool)ok & (k0 + kc + RSTEP * I < k_lim);
       a = base + (uint64_t)((k0 + (int64_t)RSTEP * I) * ld * 2);
     }
-    load_to_lds(v ? a : zp, tile + (uint32_t)((NT * I + 64 * w) * 16));
+    load_to_lds(v ? a : zp, dst);
   }
   template <int I = 0>
   __device__ __forceinline__ void issue_all(uint32_t tile, int64_t k0, int w) const {
@@ -205,12 +212,13 @@ struct Operand {
 
 // BM x BN output tile, K stages of BK in an LDS ring of NS stages, WGM x WGN
 // wavefronts (each owning a (BM / WGM) x (BN / WGN) share of 32 x 32 blocks).
-// AKM / BKM: the operand's K index is the slow one in memory.
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool AKM, bool BKM>
+// AKM / BKM: the operand's K index is the slow one in memory.  INNER: the
+// operands' loads need no range test (see Operand).
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool AKM, bool BKM, bool INNER = false>
 struct Engine {
   static constexpr int NT = 64 * WGM * WGN;
-  using OA = Operand<AKM, BM, BK, NT>;
-  using OB = Operand<BKM, BN, BK, NT>;
+  using OA = Operand<AKM, BM, BK, NT, INNER>;
+  using OB = Operand<BKM, BN, BK, NT, INNER>;
   static constexpr int STAGE = OA::BYTES + OB::BYTES;
   static constexpr int L = OA::NI + OB::NI;                  // loads per thread per stage
   static constexpr int LDS_BYTES = NS * STAGE;
@@ -398,6 +406,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void rowwise_kernel(RowwiseArgs p) 
 template <int BM, int BN, int BK, int NS, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void dw_group_kernel(DwArgs p) {
   using E = Engine<BM, BN, BK, NS, WGM, WGN, true, true>;
+  using EI = Engine<BM, BN, BK, NS, WGM, WGN, true, true, true>;
+  static_assert(kGroupRows % BK == 0, "a group holds whole stages");
   __shared__ __align__(16) uint8_t smem[E::LDS_BYTES];
   const int tmc = (int)((p.n + BM - 1) / BM), tnc = (int)((p.k + BN - 1) / BN);
   const int per_group = tmc * tnc;
@@ -408,14 +418,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void dw_group_kernel(DwArgs p) {
   const int64_t r0 = (int64_t)g * kGroupRows;
   int64_t r1 = r0 + kGroupRows;
   if (r1 > p.T) r1 = (p.T + BK - 1) / BK * BK;   // the rest of the group is zero rows
+  // Rows at or past the group's end read as zero: the ring's loads for the
+  // stages after the last one must not reach past the group, whose rows may
+  // be all a caller's buffer holds (a call that holds the group whole).
+  const int64_t row_end = r0 + kGroupRows < p.T ? r0 + kGroupRows : p.T;
   const int t = threadIdx.x;
-  typename E::OA oa;
-  typename E::OB ob;
-  oa.init(p.dy, p.n, n0, p.n, p.T, nullptr, t);
-  ob.init(p.x, p.k, k0, p.k, p.T, nullptr, t);
   typename E::AccT acc;
   acc.zero();
-  E::run(lds_addr((RBI_LDS uint8_t*)smem), acc, oa, ob, r0, (int)((r1 - r0) / BK));
+  const uint32_t sm = lds_addr((RBI_LDS uint8_t*)smem);
+  if (n0 + BM <= p.n && k0 + BN <= p.k && r0 + kGroupRows <= p.T) {
+    // a whole tile of a whole group: no load needs a range test (the same
+    // loads into the same LDS places, so the same chain)
+    typename EI::OA oa;
+    typename EI::OB ob;
+    oa.init(p.dy, p.n, n0, p.n, row_end, nullptr, t);
+    ob.init(p.x, p.k, k0, p.k, row_end, nullptr, t);
+    EI::run(sm, acc, oa, ob, r0, (int)((r1 - r0) / BK));
+  } else {
+    typename E::OA oa;
+    typename E::OB ob;
+    oa.init(p.dy, p.n, n0, p.n, row_end, nullptr, t);
+    ob.init(p.x, p.k, k0, p.k, row_end, nullptr, t);
+    E::run(sm, acc, oa, ob, r0, (int)((r1 - r0) / BK));
+  }
   float* out = p.out + (int64_t)g * p.n * p.k;
   E::for_each(acc, [&](int mi, int ni, float v) {
     const int64_t n = n0 + mi, k = k0 + ni;

@@ -63,12 +63,15 @@ def test_det_gemm_parity_and_invariance(case):
 
 def test_det_gemm_two_groups_and_the_group_tree():
     """More than 16384 logical rows: two dW groups joined by the tree, for one
-    call and for staged chunks."""
+    call, for staged chunks, and for a first call that holds group 0 whole and
+    ends at its last row (its chain runs from the call's own buffer, whose
+    rows end where the group does)."""
     wl = _wl("lin_two_groups", 64, 72, [9000, 7384, 700])
     data = adapters.make_linear_inputs(wl, device="cuda", gen_device="cpu")
     ref, dwa = _reference(wl)
     cells = [layouts.full(wl), layouts.chunked_packed(wl, chunk=4000),
-             layouts.permuted(wl)]
+             layouts.permuted(wl),
+             layouts.chunked_packed(wl, sizes=[16384, 700], name="BN/chunked_group_whole")]
     rep = harness.assert_gradient_batch_invariant("det_gemm", cells, CONTRACT, data=data,
                                                   reference=ref, raise_on_red=False)
     assert rep.strict, rep.first_failure
