@@ -248,13 +248,18 @@ struct Engine {
   }
 
   // The MI x NJ MFMAs of one step; with LOADS, load Q of the next stage after MFMA Q.
+  // Each block is computed transposed (B's fragment as the instruction's
+  // first operand), so that a lane's results lie along a tile row (see
+  // for_each4).  The instruction forms the same products and sums them in the
+  // same order either way: the results are bit for bit those of the
+  // untransposed product.
   template <bool LOADS, int Q = 0>
   __device__ static __forceinline__ void mma(AccT& acc, const bf16x8_t* a, const bf16x8_t* b,
                                              const OA& oa, const OB& ob, uint32_t tile, int64_t k0,
                                              int w) {
     if constexpr (Q < MI * NJ) {
       acc.c[Q / NJ][Q % NJ] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[Q / NJ], b[Q % NJ], acc.c[Q / NJ][Q % NJ], 0, 0, 0);
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[Q % NJ], a[Q / NJ], acc.c[Q / NJ][Q % NJ], 0, 0, 0);
       if constexpr (LOADS && Q < L) {
         RBI_SCHED_FENCE();
         load_q<Q>(oa, ob, tile, k0, w);
@@ -327,10 +332,11 @@ struct Engine {
     wait_vm_lgkm<0>();
   }
 
-  // Result (block i, j; register e) of wavefront w: tile row
-  // wm + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, tile column wn + 32 j + lane % 32.
+  // Results of wavefront w, four consecutive columns at a time: block (i, j),
+  // registers 4q .. 4q + 3 of a lane hold tile row wm + 32 i + lane % 32,
+  // tile columns wn + 32 j + 8 q + 4 (lane / 32) + 0 .. 3.
   template <typename F>
-  __device__ static __forceinline__ void for_each(const AccT& acc, F&& f) {
+  __device__ static __forceinline__ void for_each4(const AccT& acc, F&& f) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int mb = wm(w), nb = wn(w);
 #pragma unroll
@@ -338,9 +344,9 @@ struct Engine {
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          f(mb + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3), nb + 32 * j + (lane & 31),
-            acc.c[i][j][e]);
+        for (int q = 0; q < 4; ++q)
+          f(mb + 32 * i + (lane & 31), nb + 32 * j + 8 * q + 4 * (lane >> 5), acc.c[i][j][4 * q],
+            acc.c[i][j][4 * q + 1], acc.c[i][j][4 * q + 2], acc.c[i][j][4 * q + 3]);
   }
 };
 
@@ -392,11 +398,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void rowwise_kernel(RowwiseArgs p) 
   acc.zero();
   E::run(lds_addr((RBI_LDS uint8_t*)smem), acc, oa, ob, 0, (int)((p.k + BK - 1) / BK));
   // padding rows were loaded as zeros; they are written as 0 explicitly
-  E::for_each(acc, [&](int mi, int ni, float v) {
+  // four bf16 results per 8-byte store (n is a multiple of 8, a column
+  // group is wholly inside or outside the output)
+  E::for_each4(acc, [&](int mi, int ni, float v0, float v1, float v2, float v3) {
     const int64_t m = m0 + mi, n = n0 + ni;
     if (m < p.rows && n < p.n) {
       const bool pad = p.row_logical != nullptr && p.row_logical[m] < 0;
-      p.out[m * p.n + n] = pad ? (uint16_t)0 : to_bf16_rne(v);
+      uint2 o = make_uint2(0u, 0u);
+      if (!pad) {
+        o.x = (uint32_t)to_bf16_rne(v0) | ((uint32_t)to_bf16_rne(v1) << 16);
+        o.y = (uint32_t)to_bf16_rne(v2) | ((uint32_t)to_bf16_rne(v3) << 16);
+      }
+      *reinterpret_cast<uint2*>(p.out + m * p.n + n) = o;
     }
   });
 }
@@ -442,9 +455,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void dw_group_kernel(DwArgs p) {
     E::run(sm, acc, oa, ob, r0, (int)((r1 - r0) / BK));
   }
   float* out = p.out + (int64_t)g * p.n * p.k;
-  E::for_each(acc, [&](int mi, int ni, float v) {
+  E::for_each4(acc, [&](int mi, int ni, float v0, float v1, float v2, float v3) {
     const int64_t n = n0 + mi, k = k0 + ni;
-    if (n < p.n && k < p.k) out[n * p.k + k] = v;
+    if (n < p.n && k < p.k) *reinterpret_cast<float4*>(out + n * p.k + k) = make_float4(v0, v1, v2, v3);
   });
 }
 
