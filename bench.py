@@ -183,6 +183,29 @@ def stream_2to1(torch, nbytes: int, iters: int = 20):
     return gbps
 
 
+def stream_2r1w(binding, torch, nbytes: int, iters: int = 20):
+    """The same mix with the library's two-read probe (c = a XOR b, 16-byte
+    non-temporal accesses, four units per thread per pass), GB/s of the
+    three nbytes buffers: the practical ceiling for the backward's traffic."""
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.int32, device="cuda")
+    b = torch.ones_like(a)
+    c = torch.empty_like(a)
+    sh = binding.current_stream()
+    for _ in range(3):
+        binding.rmsnorm_stream_2r1w(a.data_ptr(), b.data_ptr(), c.data_ptr(), nbytes, sh)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        binding.rmsnorm_stream_2r1w(a.data_ptr(), b.data_ptr(), c.data_ptr(), nbytes, sh)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 3.0 * nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b, c
+    return gbps
+
+
 QK_PAIR = "qknorm_d128_t16384"
 
 
@@ -1050,6 +1073,8 @@ def main():
 
     copy_gbps, torch_copy_gbps = (None, None) if args.no_copy else copy_ceiling(torch, 1 << 30)
     s21_gbps = None if args.no_copy else stream_2to1(torch, 1 << 29)
+    # the probe on buffers of the backward's tensor size (x, dy, dx: 32768 x 4096 bf16)
+    s2p_gbps = None if args.no_copy else stream_2r1w(binding, torch, 1 << 28)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
 
     # host-side setup, timed on its own: a layout plan for the packed, padded,
@@ -1098,6 +1123,8 @@ def main():
         "torch_copy_gbps": None if torch_copy_gbps is None else round(torch_copy_gbps, 1),
         "stream_2to1_gbps": None if s21_gbps is None else round(s21_gbps, 1),
         "bwd_frac_of_stream_2to1": None if s21_gbps is None else round(achieved / s21_gbps, 4),
+        "stream_2r1w_gbps": None if s2p_gbps is None else round(s2p_gbps, 1),
+        "bwd_frac_of_stream_2r1w": None if s2p_gbps is None else round(achieved / s2p_gbps, 4),
         "invariance_bn_vs_8xb1_bitwise": inv_ok,
         "bwd_rstd_recompute": {"avg_launch_ms": round(rc_ms, 5),
                                "gbps": round((bb - 4 * T) / (rc_ms * 1e-3) / 1e9, 1),

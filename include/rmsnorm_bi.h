@@ -324,6 +324,17 @@ int64_t rmsnorm_bwd_noalloc_max_scratch(void);
  * a no-op.  Caller-owned memory; nothing is allocated. */
 int rmsnorm_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
+/* c = a XOR b over `bytes` bytes of device buffers on `stream`: two reads for
+ * each write, the backward's traffic mix (x and dy read, dx written), with
+ * 16-byte non-temporal accesses, four units per thread per pass.  Not part of
+ * the method: it measures the practical HBM rate of that mix on the GPU the
+ * library runs on, the ceiling the backward is compared with.  bytes must be
+ * a multiple of 16, the three pointers 16-byte aligned and c disjoint from a
+ * and b (RMSNORM_EUNSUPPORTED / RMSNORM_EINVAL otherwise; a and b may be the
+ * same buffer); bytes == 0 is a no-op.  Caller-owned memory; nothing is
+ * allocated. */
+int rmsnorm_stream_2r1w(const void* a, const void* b, void* c, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ EXPORTED = ("rmsnorm_max_hidden", "rmsnorm_fwd", "rmsnorm_bwd_dx", "rmsnorm_dw_c
             "rmsnorm_dw_acc_reset",
             "rmsnorm_dw_acc_destroy", "rmsnorm_last_error", "rmsnorm_backend_info",
             "rmsnorm_set_split_threshold", "rmsnorm_set_stream_threshold",
-            "rmsnorm_set_workgroup_cap", "rmsnorm_stream_copy",
+            "rmsnorm_set_workgroup_cap", "rmsnorm_stream_copy", "rmsnorm_stream_2r1w",
             "rmsnorm_fwd_packed", "rmsnorm_fwd_packed_pair", "rmsnorm_bwd_dx_packed_pair",
             "rmsnorm_bwd_dx_packed", "rmsnorm_bwd_dx_recompute", "rmsnorm_bwd_noalloc",
             "rmsnorm_bwd_noalloc_max_scratch",
@@ -88,6 +88,7 @@ def load() -> ctypes.CDLL:
         "rmsnorm_set_stream_threshold": ([I64, ctypes.POINTER(ctypes.c_int64)], I32),
         "rmsnorm_set_workgroup_cap": ([I64, ctypes.POINTER(ctypes.c_int64)], I32),
         "rmsnorm_stream_copy": ([P, P, I64, P], I32),
+        "rmsnorm_stream_2r1w": ([P, P, P, I64, P], I32),
         "rmsnorm_fwd_packed": ([P, P, P, P, I64, I64, I64, I64, ctypes.c_float, P, P], I32),
         "rmsnorm_bwd_dx_packed": ([P, P, P, P, P, I64, I64, I64, I64, P, P, P], I32),
         "rmsnorm_fwd_packed_pair": ([P, P, P, P, I64, I64, P, P, P, P, P, I64, I64, P, I64, I64,
@@ -279,6 +280,11 @@ def rmsnorm_set_workgroup_cap(groups: int) -> int:
 def rmsnorm_stream_copy(src: int, dst: int, nbytes: int, stream: Optional[int]) -> None:
     """Streaming device copy with the kernels' access policy (bandwidth ceiling probe)."""
     _check(load().rmsnorm_stream_copy(src, dst, int(nbytes), stream), "rmsnorm_stream_copy")
+
+
+def rmsnorm_stream_2r1w(a: int, b: int, c: int, nbytes: int, stream: Optional[int]) -> None:
+    """c = a XOR b: two reads per write, the backward's traffic mix (ceiling probe)."""
+    _check(load().rmsnorm_stream_2r1w(a, b, c, int(nbytes), stream), "rmsnorm_stream_2r1w")
 
 
 # ---------------------------------------------------------------- det_gemm

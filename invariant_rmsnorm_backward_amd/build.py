@@ -29,7 +29,7 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contr
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", f"-I{CSRC}"]
 
 SOURCES_HIP = ["kernels.hip", "abi.cpp", "linear.hip", "linear_abi.cpp", "embedding.hip",
-               "embedding_abi.cpp"]
+               "embedding_abi.cpp", "ceiling.hip"]
 SOURCES_CXX = ["plan.cpp"]
 
 

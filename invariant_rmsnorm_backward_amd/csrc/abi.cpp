@@ -12,6 +12,7 @@
 
 #include "../../include/rmsnorm_bi.h"
 #include "abi_internal.h"
+#include "ceiling.h"
 #include "kernels.h"
 #include "plan.h"
 
@@ -134,6 +135,21 @@ int rmsnorm_stream_copy(const void* src, void* dst, int64_t bytes, void* stream)
     return fail(RMSNORM_EINVAL, "src and dst must not overlap");
   const hipError_t e = rbi::launch_stream_copy(src, dst, bytes / 16, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "stream copy launch");
+  return RMSNORM_OK;
+}
+
+int rmsnorm_stream_2r1w(const void* a, const void* b, void* c, int64_t bytes, void* stream) {
+  if (bytes < 0) return fail(RMSNORM_EINVAL, "bytes must be non-negative");
+  if (bytes == 0) return RMSNORM_OK;
+  if (a == nullptr || b == nullptr || c == nullptr) return fail(RMSNORM_EINVAL, "a, b and c must be non-NULL");
+  if (bytes % 16 != 0) return fail(RMSNORM_EUNSUPPORTED, "bytes must be a multiple of 16");
+  if (reinterpret_cast<uintptr_t>(a) % 16 != 0 || reinterpret_cast<uintptr_t>(b) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(c) % 16 != 0)
+    return fail(RMSNORM_EUNSUPPORTED, "a, b and c must be 16-byte aligned");
+  const size_t n = static_cast<size_t>(bytes);
+  if (overlaps(a, n, c, n) || overlaps(b, n, c, n)) return fail(RMSNORM_EINVAL, "c must not overlap a or b");
+  const hipError_t e = rbi::launch_stream_2r1w(a, b, c, bytes / 16, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "two-read stream launch");
   return RMSNORM_OK;
 }
 

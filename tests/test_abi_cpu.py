@@ -167,6 +167,21 @@ def test_stream_copy_checks_its_arguments(lib):
     binding.rmsnorm_stream_copy(A, A + 4096, 0, None)       # zero bytes: a no-op
 
 
+def test_stream_2r1w_checks_its_arguments(lib):
+    """The two-read probe refuses bad arguments before touching the GPU."""
+    A = 1 << 12
+    cases = [((A, A + 4096, A + 8192, -16), binding.EINVAL),           # negative size
+             ((A, 0, A + 8192, 64), binding.EINVAL),                   # NULL input
+             ((A, A + 4096, A + 8192, 40), binding.EUNSUPPORTED),      # not a multiple of 16
+             ((A, A + 4096, A + 8200, 64), binding.EUNSUPPORTED),      # misaligned output
+             ((A, A + 4096, A + 4096 + 32, 64), binding.EINVAL)]       # output overlaps b
+    for (a, b, c, n), code in cases:
+        with pytest.raises(binding.RmsNormError) as ei:
+            binding.rmsnorm_stream_2r1w(a, b, c, n, None)
+        assert ei.value.code == code, (a, b, c, n)
+    binding.rmsnorm_stream_2r1w(A, A, A + 4096, 0, None)      # zero bytes: a no-op
+
+
 def test_workgroup_cap_knob():
     """The fused backward's workgroup cap: set, read back, restore."""
     prev = binding.rmsnorm_set_workgroup_cap(3)

@@ -221,6 +221,18 @@ def test_stream_copy_copies_every_byte(nbytes):
     assert not dst[nbytes // 4:].any()            # nothing past the end is written
 
 
+# the last size needs two grid-stride passes (16,384 workgroups x 1024 units each)
+@pytest.mark.parametrize("nbytes", [16, 4096, 3 * (1 << 20) + 16 * 37, 16 * (16384 * 1024 + 37)])
+def test_stream_2r1w_writes_the_xor_of_every_unit(nbytes):
+    a = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    b = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    c = torch.zeros(nbytes // 4 + 8, dtype=torch.int32, device="cuda")
+    binding.rmsnorm_stream_2r1w(a.data_ptr(), b.data_ptr(), c.data_ptr(), nbytes, binding.current_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(c[: nbytes // 4], a ^ b)
+    assert not c[nbytes // 4:].any()              # nothing past the end is written
+
+
 def _bf16_scaled(bits: np.ndarray, log2: int) -> np.ndarray:
     """bf16 bit patterns times 2**log2, exactly (exponent field shifted);
     zeros stay zero and a value that would leave the normal range becomes a
