@@ -53,6 +53,10 @@ hipError_t launch_group_tree(const float* q, int64_t G, int64_t nk, float* dw, h
 hipError_t launch_stage_rows(const uint16_t* src, int64_t rows, int64_t cols,
                              const int32_t* row_logical, uint16_t* dst, hipStream_t stream,
                              uint64_t skip_groups = 0);
+// The same for two tensors of one call at once (x[rows][ca] -> da, dY[rows][cb] -> db).
+hipError_t launch_stage_rows2(const uint16_t* a, int64_t ca, uint16_t* da, const uint16_t* b,
+                              int64_t cb, uint16_t* db, int64_t rows, const int32_t* row_logical,
+                              hipStream_t stream, uint64_t skip_groups = 0);
 hipError_t launch_zero(uint16_t* dst, int64_t n_elems, hipStream_t stream);
 hipError_t launch_zero_f32(float* dst, int64_t n, hipStream_t stream);
 

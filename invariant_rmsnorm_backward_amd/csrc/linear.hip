@@ -497,6 +497,32 @@ __global__ __launch_bounds__(256) void stage_rows_kernel(const uint16_t* __restr
   }
 }
 
+// The same for the rows of two tensors of one call (x and dY) in one launch:
+// unit i < rows * (ca + cb) / 8 of the call is chunk i % per of row i / per,
+// from the first tensor below ca / 8 chunks, else from the second.
+__global__ __launch_bounds__(256) void stage_rows2_kernel(const uint16_t* __restrict__ a, int64_t ca,
+                                                          uint16_t* __restrict__ da,
+                                                          const uint16_t* __restrict__ b, int64_t cb,
+                                                          uint16_t* __restrict__ db, int64_t rows,
+                                                          const int32_t* __restrict__ row_logical,
+                                                          uint64_t skip_groups) {
+  const int64_t na = ca / 8, per = na + cb / 8;
+  const int64_t total = rows * per;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t p = i / per, c = i % per;
+    const int32_t l = row_logical[p];
+    const int64_t g = l / kGroupRows;
+    if (l >= 0 && !(skip_groups != 0 && g < 64 && ((skip_groups >> g) & 1u))) {
+      if (c < na)
+        *reinterpret_cast<u32x4v_t*>(da + (int64_t)l * ca + 8 * c) = ld16_nt(a + p * ca + 8 * c);
+      else
+        *reinterpret_cast<u32x4v_t*>(db + (int64_t)l * cb + 8 * (c - na)) =
+            ld16_nt(b + p * cb + 8 * (c - na));
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void zero_rows_kernel(uint16_t* __restrict__ dst, int64_t n16) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
     *reinterpret_cast<u32x4v_t*>(dst + 8 * i) = u32x4v_t{0u, 0u, 0u, 0u};
@@ -576,6 +602,17 @@ hipError_t launch_stage_rows(const uint16_t* src, int64_t rows, int64_t cols,
   if (g > 4096) g = 4096;
   stage_rows_kernel<<<dim3((unsigned)g), dim3(256), 0, st>>>(src, rows, cols, row_logical, dst,
                                                               skip_groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_rows2(const uint16_t* a, int64_t ca, uint16_t* da, const uint16_t* b,
+                              int64_t cb, uint16_t* db, int64_t rows, const int32_t* row_logical,
+                              hipStream_t st, uint64_t skip_groups) {
+  if (rows == 0) return hipSuccess;
+  int64_t g = (rows * ((ca + cb) / 8) + 255) / 256;
+  if (g > 4096) g = 4096;
+  stage_rows2_kernel<<<dim3((unsigned)g), dim3(256), 0, st>>>(a, ca, da, b, cb, db, rows, row_logical,
+                                                               skip_groups);
   return hipGetLastError();
 }
 

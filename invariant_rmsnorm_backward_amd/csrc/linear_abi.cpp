@@ -203,10 +203,8 @@ int det_gemm_dw_contrib(const rmsnorm_bf16* x, const rmsnorm_bf16* dy, int64_t r
     }
   }
   if (any_staged &&
-      ((e = rbi::lin::launch_stage_rows(x, rows, k, layout->dev.row_logical, acc->d_x, st,
-                                        direct_mask)) != hipSuccess ||
-       (e = rbi::lin::launch_stage_rows(dy, rows, n, layout->dev.row_logical, acc->d_dy, st,
-                                        direct_mask)) != hipSuccess))
+      (e = rbi::lin::launch_stage_rows2(x, k, acc->d_x, dy, n, acc->d_dy, rows,
+                                        layout->dev.row_logical, st, direct_mask)) != hipSuccess)
     return hip_fail(e, "dW staging");
   acc->host.commit_call(plan_host);
   // a group touched by this call is either whole here (computed) or split
