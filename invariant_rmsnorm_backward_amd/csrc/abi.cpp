@@ -180,8 +180,12 @@ static int fwd_prepare(const rmsnorm_bf16* x, const rmsnorm_bf16* w, rmsnorm_bf1
   if (overlaps(y, nbytes, x, nbytes) || overlaps(y, nbytes, w, hidden * 2) ||
       (rstd != nullptr && (overlaps(rstd, rows * 4, x, nbytes) || overlaps(rstd, rows * 4, y, nbytes))))
     return fail(RMSNORM_EINVAL, "outputs must not alias inputs or each other");
+  // The forward is row-local: the map matters only for padding rows (not
+  // read, written as 0).  A layout without padding rows runs as the identity,
+  // so no row waits for its map entry before its loads.
+  const bool pads = layout != nullptr && !layout->host.pad_rows.empty();
   *out = rbi::FwdArgs{x, w, y, rstd, rows, static_cast<int32_t>(hidden), eps,
-                      layout ? layout->dev.row_logical : nullptr, pk};
+                      pads ? layout->dev.row_logical : nullptr, pk};
   *launch = true;
   return RMSNORM_OK;
 }
@@ -285,11 +289,26 @@ static int bwd_prepare(const rmsnorm_bf16* x, const rmsnorm_bf16* w, const rmsno
   a.rows = rows;
   a.hidden = static_cast<int32_t>(hidden);
   a.pack = pk;
-  if (layout != nullptr) {
+  // A call whose rows are whole canonical blocks in logical order (no padding,
+  // the first row on a block boundary, every block held completely: a B=1
+  // sample or a chunked-prefill piece that starts on a block boundary) is the
+  // identity map on blocks first/64 onwards: it runs the kernels without a
+  // plan (no per-block lookups before the loads), with the block outputs
+  // addressed from that block.  Same rows, same operations, same bits.
+  const rbi::PlanHost* ph = layout ? &layout->host : nullptr;
+  const bool whole_blocks = ph != nullptr && ph->contig_first >= 0 &&
+                            ph->contig_first % rbi::kBlockRows == 0 && ph->n_partial == 0;
+  if (layout != nullptr && !whole_blocks) {
     a.plan = layout->dev;
   } else {
     a.plan.n_items = static_cast<int32_t>(rbi::num_blocks(rows));
     a.plan.n_pad = 0;
+    if (whole_blocks) {
+      const int64_t b0 = ph->contig_first / rbi::kBlockRows;
+      if (a.P != nullptr) a.P += b0 * hidden;
+      if (a.Q != nullptr) a.Q += b0 * 3 * hidden;
+      if (a.form != nullptr) a.form += b0;
+    }
   }
   return RMSNORM_OK;
 }

@@ -70,6 +70,11 @@ int build_plan(const int32_t* row_logical, int64_t rows, int64_t n_logical, Plan
     P.slot_phys[static_cast<size_t>(item) * kBlockRows + (l % kBlockRows)] = static_cast<int32_t>(p);
     if (P.item_info[static_cast<size_t>(item)] < 0) P.partial_rows.push_back(l);
   }
+  if (rows > 0 && P.pad_rows.empty()) {
+    bool contig = true;
+    for (int64_t p = 1; p < rows && contig; ++p) contig = row_logical[p] == row_logical[0] + p;
+    if (contig) P.contig_first = row_logical[0];
+  }
   return kOk;
 }
 

@@ -56,6 +56,8 @@ struct PlanHost {
   std::vector<int32_t> partial_rows; // logical ids of the rows of partial items (the only
                                      // rows whose coverage is tracked one by one)
   int64_t n_real = 0;                // rows with a logical id
+  int64_t contig_first = -1;         // the rows are logical rows contig_first, +1, ... in
+                                     // order with no padding row; else -1
   int64_t n_complete = 0;
   int64_t n_partial = 0;
   int64_t n_items() const { return static_cast<int64_t>(item_info.size()); }
