@@ -55,6 +55,11 @@ int main() {
     }
     for (int32_t p : P.pad_rows) { CHECK(rl[p] == -1); seen[p]++; }
     for (size_t p = 0; p < rl.size(); ++p) CHECK(seen[p] == 1);
+    {
+      bool contig = !rl.empty();
+      for (size_t p = 0; p < rl.size() && contig; ++p) contig = rl[p] >= 0 && rl[p] == rl[0] + (int32_t)p;
+      CHECK(P.contig_first == (contig ? rl[0] : -1));
+    }
     // accumulator: one call then finalize must report missing rows unless all held
     AccHost A;
     A.init(T, 8);
@@ -177,6 +182,36 @@ int main() {
     CHECK(A.prepare_finalize(&spilled, &err) == kOk && spilled.empty());
   }
   // identity accumulator path and state machine
+  // Contiguous runs of logical rows: contig_first, and the whole-block case
+  // the backward runs without a device plan (items are the consecutive
+  // blocks from contig_first / 64, all complete, slot s of item i at
+  // physical row 64 i + s).
+  for (int iter = 0; iter < 2000; ++iter) {
+    const int64_t T = 1 + rng() % 900;
+    int64_t a = rng() % T;
+    if (rng() % 2) a -= a % kBlockRows;
+    int64_t len = 1 + rng() % (T - a);
+    if (rng() % 2) len = std::min<int64_t>(T - a, (len + kBlockRows - 1) / kBlockRows * kBlockRows);
+    std::vector<int32_t> rl;
+    for (int64_t l = a; l < a + len; ++l) rl.push_back((int32_t)l);
+    const bool pad = rng() % 5 == 0;
+    if (pad) rl.push_back(-1);
+    PlanHost P;
+    std::string err;
+    CHECK(build_plan(rl.data(), (int64_t)rl.size(), T, &P, &err) == kOk);
+    CHECK(P.contig_first == (pad ? -1 : a));
+    const bool whole = P.contig_first >= 0 && P.contig_first % kBlockRows == 0 && P.n_partial == 0;
+    CHECK(whole == (!pad && a % kBlockRows == 0 && (len % kBlockRows == 0 || a + len == T)));
+    if (whole) {
+      for (size_t it = 0; it < P.item_info.size(); ++it) {
+        CHECK(P.item_info[it] == (int32_t)(a / kBlockRows + (int64_t)it));
+        for (int s = 0; s < kBlockRows; ++s) {
+          const int64_t p = (int64_t)it * kBlockRows + s;
+          CHECK(P.slot_phys[it * kBlockRows + s] == (p < len ? (int32_t)p : -1));
+        }
+      }
+    }
+  }
   AccHost A;
   std::string err;
   A.init(100, 16);
