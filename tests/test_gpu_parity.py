@@ -597,3 +597,56 @@ def test_bounded_spill_area_refuses_when_full_and_matches_unbounded():
                 lay.close()
     print(f"[spill bound] {len(need)} slots: exact bound == unbounded on every path, one short refused",
           flush=True)
+
+
+def test_whole_block_calls_equal_the_planned_path():
+    """A call whose rows are whole canonical blocks in logical order runs the
+    forward without the map and the backward without a device plan; the same
+    rows with one padding row appended take the planned path.  Both give the
+    same y, rstd, dx and dweight bits on every backward path, and the same
+    dweight as one identity call."""
+    H = 1024
+    wl = inputs.scaled(inputs.workload_h4096(), "whole_blocks_h1024", hidden=H, lengths=[400, 300])
+    data = pu.make_data(wl)
+    T = wl.n_logical
+    x, w, dy = data.x, data.w, data.dy
+    pieces = [(0, 128), (128, 384), (384, T)]          # block-aligned starts; the last ends at T
+    nan_row = torch.full((1, H), float("nan"), dtype=x.dtype, device=x.device)
+    _, rstd_all = binding.fwd(x, w, data.eps)
+    one = binding.DwAccumulator(T, H)
+    binding.bwd(x, w, dy, rstd_all, None, one)
+    dw_one = one.finalize().view(torch.int32).cpu()
+    one.close()
+    lays = []
+    for path in pu.BWD_PATHS:
+        with pu.forced_path(path):
+            dws = []
+            for padded in (False, True):
+                acc = binding.DwAccumulator(T, H)
+                outs = []
+                for a, b in pieces:
+                    rl = np.arange(a, b, dtype=np.int32)
+                    xc, dyc = x[a:b].contiguous(), dy[a:b].contiguous()
+                    if padded:
+                        rl = np.concatenate([rl, np.array([-1], dtype=np.int32)])
+                        xc, dyc = torch.cat([xc, nan_row]), torch.cat([dyc, nan_row])
+                    lay = binding.Layout(rl, T)
+                    y, rstd = binding.fwd(xc, w, data.eps, lay)
+                    dx = binding.bwd(xc, w, dyc, rstd, lay, acc)
+                    n = b - a
+                    outs.append((y[:n].view(torch.int16).cpu(), rstd[:n].view(torch.int32).cpu(),
+                                 dx[:n].view(torch.int16).cpu()))
+                    if padded:
+                        assert not bool(dx[n:].view(torch.int16).any()), path
+                    lays.append(lay)
+                dws.append((acc.finalize().view(torch.int32).cpu(), outs))
+                torch.cuda.synchronize()
+                acc.close()
+            (dw_w, out_w), (dw_p, out_p) = dws
+            assert torch.equal(dw_w, dw_p), path
+            assert torch.equal(dw_w, dw_one), path
+            for (yw, rw, dxw), (yp, rp, dxp) in zip(out_w, out_p):
+                assert torch.equal(yw, yp) and torch.equal(rw, rp) and torch.equal(dxw, dxp), path
+    for lay in lays:
+        lay.close()
+    print("[whole blocks] planned and plan-free calls bitwise equal on every path", flush=True)
