@@ -599,14 +599,14 @@ def test_bounded_spill_area_refuses_when_full_and_matches_unbounded():
           flush=True)
 
 
-def test_whole_block_calls_equal_the_planned_path():
+@pytest.mark.parametrize("H", [128, 1000, 1024, 4096, 5120, 8192])
+def test_whole_block_calls_equal_the_planned_path(H):
     """A call whose rows are whole canonical blocks in logical order runs the
     forward without the map and the backward without a device plan; the same
     rows with one padding row appended take the planned path.  Both give the
     same y, rstd, dx and dweight bits on every backward path, and the same
     dweight as one identity call."""
-    H = 1024
-    wl = inputs.scaled(inputs.workload_h4096(), "whole_blocks_h1024", hidden=H, lengths=[400, 300])
+    wl = inputs.scaled(inputs.workload_h4096(), f"whole_blocks_h{H}", hidden=H, lengths=[400, 300])
     data = pu.make_data(wl)
     T = wl.n_logical
     x, w, dy = data.x, data.w, data.dy
@@ -649,4 +649,4 @@ def test_whole_block_calls_equal_the_planned_path():
                 assert torch.equal(yw, yp) and torch.equal(rw, rp) and torch.equal(dxw, dxp), path
     for lay in lays:
         lay.close()
-    print("[whole blocks] planned and plan-free calls bitwise equal on every path", flush=True)
+    print(f"[whole blocks] hidden {H}: planned and plan-free calls bitwise equal on every path", flush=True)
