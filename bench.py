@@ -43,7 +43,7 @@ def algorithmic_bytes(rows_real: int, rows_phys: int, H: int):
 # Sources that define the RMSNorm kernels (the linear-layer kernels and the
 # C-ABI glue do not change them).
 NORM_KERNEL_SOURCES = ("kernels.hip", "kernels.h", "device_math.h", "plan.h")
-GEMM_KERNEL_SOURCES = ("linear.hip", "linear.h")
+GEMM_KERNEL_SOURCES = ("linear.hip", "linear.h", "tile_map.h")
 
 
 def kernel_source_hash(names=NORM_KERNEL_SOURCES) -> str:

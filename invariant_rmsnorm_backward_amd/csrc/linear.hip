@@ -38,8 +38,10 @@
 //     it + NS are issued one after each MFMA of the last step of stage it;
 //   * tiles are mapped to workgroups so that the 32 workgroups one XCD runs
 //     at a time share 4 row blocks and 8 column blocks (the round-robin
-//     dispatch puts workgroup id on XCD id % 8).
+//     dispatch puts workgroup id on XCD id % 8), also on grids that 4 x 8
+//     super-blocks do not tile (the vocabulary side of an LM head).
 #include "linear.h"
+#include "tile_map.h"
 
 #include <hip/hip_runtime.h>
 
@@ -350,24 +352,6 @@ struct Engine {
   }
 };
 
-// Tile (tm, tn) of workgroup id in a tmc x tnc grid: the tiles are cut into
-// 4 x 8 super-blocks; XCD x (id % 8) takes super-blocks x, x + 8, ... so its
-// 32 concurrent workgroups share 4 row blocks and 8 column blocks.  Grids the
-// super-blocks do not tile fall back to column-major order.
-__device__ __forceinline__ void xcd_tile(int id, int tmc, int tnc, int& tm, int& tn) {
-  constexpr int GM = 4, GN = 8;
-  if (tmc % GM || tnc % GN || ((tmc / GM) * (tnc / GN)) % 8) {
-    tm = id % tmc;
-    tn = id / tmc;
-    return;
-  }
-  const int sbm = tmc / GM;
-  const int xcd = id & 7, slot = id >> 3;
-  const int sb = (slot >> 5) * 8 + xcd, w = slot & 31;
-  tm = (sb % sbm) * GM + w % GM;
-  tn = (sb / sbm) * GN + w / GM;
-}
-
 __device__ __forceinline__ uint16_t to_bf16_rne(float f) {
   const unsigned u = __float_as_uint(f);
   if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);
@@ -387,7 +371,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void rowwise_kernel(RowwiseArgs p) 
   using E = Engine<BM, BN, BK, NS, WGM, WGN, false, BT>;
   __shared__ __align__(16) uint8_t smem[E::LDS_BYTES];
   int tm, tn;
-  xcd_tile((int)blockIdx.x, (int)((p.rows + BM - 1) / BM), (int)((p.n + BN - 1) / BN), tm, tn);
+  if (!xcd_tile((int)blockIdx.x, (int)((p.rows + BM - 1) / BM), (int)((p.n + BN - 1) / BN), tm, tn)) return;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int t = threadIdx.x;
   typename E::OA oa;
@@ -423,10 +407,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void dw_group_kernel(DwArgs p) {
   static_assert(kGroupRows % BK == 0, "a group holds whole stages");
   __shared__ __align__(16) uint8_t smem[E::LDS_BYTES];
   const int tmc = (int)((p.n + BM - 1) / BM), tnc = (int)((p.k + BN - 1) / BN);
-  const int per_group = tmc * tnc;
+  const int per_group = (int)tile_slots(tmc, tnc);
   const int g = (int)p.g_first + (int)blockIdx.x / per_group;
   int tm, tn;
-  xcd_tile((int)blockIdx.x % per_group, tmc, tnc, tm, tn);
+  if (!xcd_tile((int)blockIdx.x % per_group, tmc, tnc, tm, tn)) return;
   const int64_t n0 = (int64_t)tm * BM, k0 = (int64_t)tn * BN;
   const int64_t r0 = (int64_t)g * kGroupRows;
   int64_t r1 = r0 + kGroupRows;
@@ -540,7 +524,7 @@ static bool big_tiles(int64_t m, int64_t n) { return m >= 256 && n >= 256; }
 
 template <int BM, int BN, int BK, int NS, int WGM, int WGN>
 static hipError_t rowwise_go(const RowwiseArgs& a, bool bt, hipStream_t st) {
-  const int64_t tiles = ((a.rows + BM - 1) / BM) * ((a.n + BN - 1) / BN);
+  const int64_t tiles = tile_slots((a.rows + BM - 1) / BM, (a.n + BN - 1) / BN);
   if (tiles > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)tiles), block(64 * WGM * WGN);
   if (bt) rowwise_kernel<BM, BN, BK, NS, WGM, WGN, true><<<grid, block, 0, st>>>(a);
@@ -558,7 +542,7 @@ int64_t num_groups(int64_t T) { return (T + kGroupRows - 1) / kGroupRows; }
 
 template <int BM, int BN, int BK, int NS, int WGM, int WGN>
 static hipError_t dw_go(const DwArgs& a, int64_t G, hipStream_t st) {
-  const int64_t tiles = ((a.n + BM - 1) / BM) * ((a.k + BN - 1) / BN) * G;
+  const int64_t tiles = tile_slots((a.n + BM - 1) / BM, (a.k + BN - 1) / BN) * G;
   if (tiles > INT32_MAX) return hipErrorInvalidValue;
   dw_group_kernel<BM, BN, BK, NS, WGM, WGN><<<dim3((unsigned)tiles), dim3(64 * WGM * WGN), 0, st>>>(a);
   return hipGetLastError();

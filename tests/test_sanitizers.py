@@ -1,6 +1,7 @@
 """Host code under AddressSanitizer + UndefinedBehaviorSanitizer (CPU only):
 the plan/accumulator bookkeeping of the HIP library (fuzzed with random and
-invalid layouts) and the C oracle (driven through its pins)."""
+invalid layouts), the matrix-core kernels' workgroup-to-tile map, and the C
+oracle (driven through its pins)."""
 import os
 import shutil
 import subprocess
@@ -23,6 +24,17 @@ def test_plan_bookkeeping_under_asan_ubsan(tmp_path):
                        env={**os.environ, "ASAN_OPTIONS": "detect_leaks=1"})
     assert r.returncode == 0, r.stdout + r.stderr
     assert "plan fuzz: ok" in r.stdout
+
+
+def test_gemm_tile_map_takes_every_tile_once(tmp_path):
+    """The constexpr tile map that linear.hip launches with, run on the host."""
+    exe = str(tmp_path / "tile_map_check")
+    subprocess.run(["g++", "-std=c++17", *SAN, f"-I{CSRC}",
+                    os.path.join(ROOT, "tests", "native", "tile_map_check.cpp"), "-o", exe],
+                   check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "tile map: ok" in r.stdout
 
 
 def test_oracle_under_asan_ubsan(tmp_path):
