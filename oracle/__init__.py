@@ -214,7 +214,7 @@ class Oracle:
 
     def linear_sample_bf16(self, x_bits, w_bits, dy_bits, kind, ia, ib) -> np.ndarray:
         """Single outputs of an identity-layout call: kind 0 = dX[ia][ib],
-        1 = dW[ia][ib], 2 = |dW|[ia][ib]."""
+        1 = dW[ia][ib], 2 = |dW|[ia][ib], 3 = y[ia][ib]."""
         x = _c(x_bits, np.uint16)
         w = _c(w_bits, np.uint16)
         dy = _c(dy_bits, np.uint16)

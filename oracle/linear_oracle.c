@@ -117,7 +117,8 @@ int oracle_linear_bwd(const uint16_t* x, const uint16_t* w, const uint16_t* dy, 
 
 /* Single outputs of an identity-layout call, one at a time (for sizes whose
  * full products are too slow here): kind 0 = dX[a][b], kind 1 = dW[a][b]
- * (summed over all rows in ascending order), kind 2 = |dW|[a][b]. */
+ * (summed over all rows in ascending order), kind 2 = |dW|[a][b], kind 3 =
+ * y[a][b] (row a of x against row b of W, the forward y = x W^T). */
 int oracle_linear_sample(const uint16_t* x, const uint16_t* w, const uint16_t* dy, int64_t rows,
                          int64_t n, int64_t k, int64_t count, const int32_t* kind,
                          const int64_t* ia, const int64_t* ib, double* out) {
@@ -134,6 +135,10 @@ int oracle_linear_sample(const uint16_t* x, const uint16_t* w, const uint16_t* d
                 const double c = lin_widen(dy[r * n + o]) * lin_widen(x[r * k + i]);
                 acc += kind[s] == 1 ? c : fabs(c);
             }
+        } else if (kind[s] == 3) {
+            const int64_t r = ia[s], o = ib[s];
+            if (r < 0 || r >= rows || o < 0 || o >= n) return LIN_EINVAL;
+            for (int64_t i = 0; i < k; ++i) acc += lin_widen(x[r * k + i]) * lin_widen(w[o * k + i]);
         } else {
             return LIN_EINVAL;
         }

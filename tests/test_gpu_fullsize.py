@@ -169,16 +169,23 @@ def test_linear_h4096_o4096_t32768_sampled():
     kk = np.concatenate([[0, K - 1, 255, 256], rng.integers(0, K, n_s)])
     nn = np.concatenate([[0, N - 1, 127, 128], rng.integers(0, N, n_s)])
     m = len(r)
-    kind = np.concatenate([np.zeros(m, np.int32), np.ones(m, np.int32), np.full(m, 2, np.int32)])
-    ia = np.concatenate([r, nn, nn]).astype(np.int64)
-    ib = np.concatenate([kk, kk, kk]).astype(np.int64)
-    _log(f"{wl.name}: {3 * m} oracle samples")
+    # y over the vocabulary side: the corners of the grid and the tiles on its
+    # last row and column of 256 x 256 tiles, plus random entries
+    ry = np.concatenate([[0, T - 1, T - 1, 0, T - 256, 255], rng.integers(0, T, n_s)])
+    ny = np.concatenate([[0, N - 1, 0, N - 1, N - 256, N - 257], rng.integers(0, N, n_s)])
+    kind = np.concatenate([np.zeros(m, np.int32), np.ones(m, np.int32), np.full(m, 2, np.int32),
+                           np.full(len(ry), 3, np.int32)])
+    ia = np.concatenate([r, nn, nn, ry]).astype(np.int64)
+    ib = np.concatenate([kk, kk, kk, ny]).astype(np.int64)
+    _log(f"{wl.name}: {len(kind)} oracle samples")
     ref = oracle.linear_sample_bf16(xb, wb, dyb, kind, ia, ib)
-    dx_ref, dw_ref, dwa = ref[:m], ref[m:2 * m], ref[2 * m:]
+    dx_ref, dw_ref, dwa, y_ref = ref[:m], ref[m:2 * m], ref[2 * m:3 * m], ref[3 * m:]
     dx_got = harness.bf16_bits_to_f32(out["dX"][r, kk]).astype(np.float64)
     dw_got = out["dW"][nn, kk].astype(np.float64)
+    y_got = harness.bf16_bits_to_f32(out["y"][ry, ny]).astype(np.float64)
     assert CONTRACT.accuracy_passes(dx_got, dx_ref, "dX")
     assert CONTRACT.accuracy_passes(dw_got, dw_ref, "dW")
+    assert CONTRACT.accuracy_passes(y_got, y_ref, "y")
     # one rounding per 16-row step of a group chain (1024 steps) plus the tree
     assert np.all(np.abs(dw_got - dw_ref) <= (1024 + 2) * 2.0 ** -24 * dwa + 1e-30)
     _log(f"{wl.name}: sampled dX/dW match the oracle; max |dW err| / |dW| scale "
@@ -190,8 +197,9 @@ def test_lmhead_v32000_h4096_t32768_sampled():
     32,000-token vocabulary, K = 4096, on 32768 rows (two dW groups).  dX and
     dW bitwise across B=N, 8 x B=1 and chunked-512 calls (the B=N call runs
     both group chains at once, the others stage the rows of the groups they
-    split); sampled dX and dW entries against the FP64 oracle and within the
-    error bound of the canonical order."""
+    split); sampled y, dX and dW entries against the FP64 oracle (y on every
+    edge of the vocabulary-wide tile grid), dW within the error bound of the
+    canonical order."""
     wl = inputs.workload_lmhead()
     data = adapters.make_linear_inputs(wl, device="cuda")
     cells = [layouts.full(wl), layouts.singleton_aggregate(wl),

@@ -61,6 +61,51 @@ def test_det_gemm_parity_and_invariance(case):
     assert all(v.max_abs == 0.0 for v in rep.invariance_reports)
 
 
+def test_det_gemm_edge_tiles_of_a_padded_tile_grid():
+    """Output grids that 4 x 8 super-blocks of 256 x 256 tiles do not tile are
+    launched as whole super-blocks, with the workgroups past the grid's edge
+    exiting at once: y (64 x 31 tiles) and dW (31 x 8 tiles) here, with a
+    ragged last tile column.  y and dX on the first and last tile rows and
+    columns and at random entries, and dW (within the canonical order's error
+    bound), against single FP64 oracle outputs; a layout with padding rows in
+    front (another row grid) gives the same bits."""
+    T, N, K = 16384, 7928, 2048
+    wl = _wl("lin_padded_grid", K, N, [T])
+    data = adapters.make_linear_inputs(wl, device="cuda", gen_device="cpu")
+    out = adapters.LinearAdapter().run_cell(layouts.full(wl), data)
+    # 37 padding rows first, every real row 37 places down (another row grid):
+    # the same bits
+    out_p = adapters.LinearAdapter().run_cell(layouts.padded(wl, T + 37, "left"), data)
+    for name in ("y", "dX", "dW"):
+        assert np.array_equal(out[name].view(np.uint8), out_p[name].view(np.uint8)), name
+    assert bool(out_p["pad_rows_clean"][0])
+    xb, wb, dyb = (inputs.bf16_bits(t) for t in (data.x, data.w, data.dy))
+    rng = np.random.default_rng(31)
+    n_s = 64
+    edge_r = np.array([0, 255, 256, T - 256, T - 1, 0, T - 1, 7000])
+    edge_n = np.array([0, N - 1, N - 120, N - 1, 0, 31 * 256 - 257, N - 256, 4000])
+    ry = np.concatenate([edge_r, rng.integers(0, T, n_s)])
+    ny = np.concatenate([edge_n, rng.integers(0, N, n_s)])
+    rx = np.concatenate([edge_r, rng.integers(0, T, n_s)])
+    kx = np.concatenate([[0, K - 1, 255, 256, K - 256, 1024, 0, K - 1], rng.integers(0, K, n_s)])
+    nw = np.concatenate([edge_n, rng.integers(0, N, n_s)])
+    kw = np.concatenate([[0, K - 1, 255, 256, K - 256, 1024, K - 1, 0], rng.integers(0, K, n_s)])
+    m = len(ry)
+    kind = np.concatenate([np.full(m, 3, np.int32), np.zeros(m, np.int32), np.ones(m, np.int32),
+                           np.full(m, 2, np.int32)])
+    ia = np.concatenate([ry, rx, nw, nw]).astype(np.int64)
+    ib = np.concatenate([ny, kx, kw, kw]).astype(np.int64)
+    ref = oracle.linear_sample_bf16(xb, wb, dyb, kind, ia, ib)
+    y_ref, dx_ref, dw_ref, dwa = ref[:m], ref[m:2 * m], ref[2 * m:3 * m], ref[3 * m:]
+    y_got = harness.bf16_bits_to_f32(out["y"][ry, ny]).astype(np.float64)
+    dx_got = harness.bf16_bits_to_f32(out["dX"][rx, kx]).astype(np.float64)
+    dw_got = out["dW"][nw, kw].astype(np.float64)
+    assert CONTRACT.accuracy_passes(y_got, y_ref, "y")
+    assert CONTRACT.accuracy_passes(dx_got, dx_ref, "dX")
+    assert CONTRACT.accuracy_passes(dw_got, dw_ref, "dW")
+    assert np.all(np.abs(dw_got - dw_ref) <= (1024 + 2) * 2.0 ** -24 * dwa + 1e-30)
+
+
 def test_det_gemm_two_groups_and_the_group_tree():
     """More than 16384 logical rows: two dW groups joined by the tree, for one
     call, for staged chunks, and for a first call that holds group 0 whole and

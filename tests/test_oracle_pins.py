@@ -475,11 +475,16 @@ def pin_linear_samples_match_the_full_products(orc):
     R, N, K = 31, 7, 9
     x, w, dy = _rand_bf16(rng, (R, K)), _rand_bf16(rng, (N, K)), _rand_bf16(rng, (R, N))
     dx, dw, dwa = orc.linear_bwd_bf16(x, w, dy)
-    kind = np.array([0, 0, 1, 1, 2], np.int32)
-    ia = np.array([3, 30, 0, 6, 4], np.int64)
-    ib = np.array([8, 0, 5, 8, 2], np.int64)
+    y = orc.linear_fwd_bf16(x, w)
+    kind = np.array([0, 0, 1, 1, 2, 3, 3], np.int32)
+    ia = np.array([3, 30, 0, 6, 4, 0, 30], np.int64)
+    ib = np.array([8, 0, 5, 8, 2, 6, 0], np.int64)
     got = orc.linear_sample_bf16(x, w, dy, kind, ia, ib)
-    np.testing.assert_array_equal(got, [dx[3, 8], dx[30, 0], dw[0, 5], dw[6, 8], dwa[4, 2]])
+    np.testing.assert_array_equal(got, [dx[3, 8], dx[30, 0], dw[0, 5], dw[6, 8], dwa[4, 2],
+                                        y[0, 6], y[30, 0]])
+    with pytest.raises(oracle.OracleError):
+        orc.linear_sample_bf16(x, w, dy, np.array([3], np.int32), np.array([R], np.int64),
+                               np.array([0], np.int64))
 
 
 def pin_round_bf16(orc):
