@@ -179,6 +179,41 @@ def test_dweight_is_the_canonical_order_bit_for_bit(H, lengths, bwd_path):
     print(f"[cdo] H={H} ({bwd_path}): GPU dweight == CDO-v2 emulation bit for bit", flush=True)
 
 
+@pytest.mark.parametrize("H,T,chunk", [(8, 40000, 8192), (16, 131000, 30000), (8, 262000, 65536),
+                                         (8, 524288, 131072), (8, 524352, 131072),
+                                         (1024, 70000, 16384)])
+def test_block_tree_over_many_blocks_is_the_canonical_tree(H, T, chunk):
+    """The cross-block tree over more than 512 block partials runs level by
+    level (512 leaves per workgroup, then the tree over their roots padded
+    with +0.0): dweight equals the oracle's FP32 emulation of CDO-v2 bit for
+    bit at 625, 2047, 4094, 8192 and 8193 blocks (two levels) and
+    at 1094 blocks of hidden 1024, for one call and for large chunks."""
+    wl = inputs.scaled(inputs.workload_h4096(), f"tree_h{H}_t{T}", hidden=H, lengths=[T])
+    xb = inputs.bf16_bits(inputs.gen_x(wl))
+    wb = inputs.bf16_bits(inputs.gen_w(wl))
+    dyb = inputs.bf16_bits(inputs.gen_dy(wl))
+    _, rstd64 = oracle.rmsnorm_fwd_bf16(xb, wb, wl.eps)
+    rstd32 = rstd64.astype(np.float32)
+    want = oracle.cdo_v2_dweight_f32(xb, dyb, rstd32)
+    data = pu.make_data(wl)
+    rstd_d = torch.from_numpy(rstd32).cuda()
+    print(f"[tree] H={H} T={T}: {(T + 63) // 64} blocks", flush=True)
+    for cell in (layouts.full(wl), layouts.chunked_packed(wl, chunk=chunk)):
+        acc = binding.DwAccumulator(T, H)
+        for call in cell.calls:
+            if call.row_logical is None:
+                binding.dw_contrib(data.x, data.dy, rstd_d, acc)
+            else:
+                rl = torch.from_numpy(call.row_logical.astype(np.int64)).cuda()
+                lay = binding.Layout(call.row_logical, T)
+                binding.dw_contrib(data.x[rl].contiguous(), data.dy[rl].contiguous(),
+                                   rstd_d[rl].contiguous(), acc, lay)
+        got = acc.finalize().cpu().numpy()
+        torch.cuda.synchronize()
+        acc.close()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (H, T, cell.name)
+
+
 @pytest.mark.parametrize("H", [24, 128, 520, 1024, 1032, 4096, 5120, 9000])
 def test_padding_rows_are_written_as_positive_zero(H):
     """Padding rows are never read (they hold NaN here) and come out as +0.0
